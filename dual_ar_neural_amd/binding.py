@@ -1,0 +1,239 @@
+"""ctypes binding of libs2fast (include/s2fast.h).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every computation runs in the library's kernels.  The
+binding raises if the library is missing — there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libs2fast.so")
+MAX_LAYERS = 8
+BF16, F32 = 0, 1
+
+ERRORS = {
+    0: "OK", 1: "ERR_ARG", 2: "ERR_NO_FAST_DECODER", 3: "ERR_HIDDEN_DIM", 4: "ERR_PREFIX_LEN",
+    5: "ERR_BATCH", 6: "ERR_HIP", 7: "ERR_NOMEM", 8: "ERR_DEVICE",
+}
+
+
+class S2FastError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({_strerror(code)})")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "in_dim", "dim", "n_layer", "n_head", "n_head_kv", "head_dim", "ffn_dim",
+        "codebook_size", "num_codebooks", "context")] + [
+        ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float),
+        ("has_project_in", ctypes.c_int32), ("has_qk_norm", ctypes.c_int32),
+        ("weight_dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32)]
+
+
+LAYER_FIELDS = ("attention_norm", "wqkv", "q_norm", "k_norm", "wo", "ffn_norm", "w1", "w3", "w2")
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("project_in", ctypes.c_void_p), ("embeddings", ctypes.c_void_p),
+                ("norm", ctypes.c_void_p), ("output", ctypes.c_void_p),
+                ("layers", LayerWeights * MAX_LAYERS)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libs2fast.so (built in-tree by dual_ar_neural_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m dual_ar_neural_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, F, V = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+        lib.s2fast_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), ctypes.POINTER(ctypes.c_void_p)]
+        lib.s2fast_create.restype = ctypes.c_int
+        lib.s2fast_destroy.argtypes = [P]
+        lib.s2fast_destroy.restype = None
+        lib.s2fast_strerror.argtypes = [ctypes.c_int]
+        lib.s2fast_strerror.restype = ctypes.c_char_p
+        lib.s2fast_decode_frame.argtypes = [P, I, P, P, P, P, P, P, P, V]
+        lib.s2fast_decode_frame.restype = ctypes.c_int
+        lib.s2fast_forward_logits.argtypes = [P, I, P, P, P, V]
+        lib.s2fast_forward_logits.restype = ctypes.c_int
+        lib.s2fast_test_rope_table.argtypes = [I, I, F, P, P]
+        lib.s2fast_test_rope_table.restype = ctypes.c_int
+        lib.s2fast_test_sample.argtypes = [I, I, P, P, P, P, P, P, V]
+        lib.s2fast_test_sample.restype = ctypes.c_int
+        lib.s2fast_syncs_per_frame.argtypes = [P, I]
+        lib.s2fast_syncs_per_frame.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_frame",
+           "s2fast_forward_logits", "s2fast_test_rope_table", "s2fast_test_sample",
+           "s2fast_syncs_per_frame")
+
+
+def _strerror(code: int) -> str:
+    try:
+        return library().s2fast_strerror(code).decode()
+    except Exception:
+        return "?"
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise S2FastError(rc, what)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, shape: Sequence[int], name: str) -> torch.Tensor:
+    if not (t.is_cuda and t.dtype == dtype and tuple(t.shape) == tuple(shape) and t.is_contiguous()):
+        raise ValueError(f"{name}: expected contiguous {dtype} CUDA tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
+def make_config(shape, max_batch: int) -> Config:
+    return Config(in_dim=shape.in_dim, dim=shape.dim, n_layer=shape.n_layer, n_head=shape.n_head,
+                  n_head_kv=shape.n_head_kv, head_dim=shape.head_dim, ffn_dim=shape.ffn_dim,
+                  codebook_size=shape.codebook_size, num_codebooks=shape.num_codebooks,
+                  context=shape.context, rope_base=shape.rope_base, norm_eps=shape.norm_eps,
+                  has_project_in=int(shape.has_project_in), has_qk_norm=int(shape.has_qk_norm),
+                  weight_dtype=BF16 if shape.weight_dtype == "bf16" else F32, max_batch=max_batch)
+
+
+def device_weights(shape, weights: Dict[str, "object"], device="cuda") -> Dict[str, torch.Tensor]:
+    """Copy host weights (numpy: uint16 bf16 bits or float32) to device tensors."""
+    import numpy as np
+    out = {}
+    for k, v in weights.items():
+        if isinstance(v, torch.Tensor):
+            out[k] = v.to(device).contiguous()
+        elif v.dtype == np.uint16:
+            out[k] = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(device).contiguous()
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(device)
+    return out
+
+
+class FastAR:
+    """One s2fast context over device-resident weights."""
+
+    def __init__(self, shape, weights: Dict[str, torch.Tensor], max_batch: int = 1):
+        self.shape = shape
+        self.weights = weights           # keep the device tensors alive
+        self.max_batch = max_batch
+        lib = library()
+        cfg = make_config(shape, max_batch)
+        w = Weights()
+        g = lambda n: _ptr(weights.get(n))
+        w.project_in = g("fast_project_in")
+        w.embeddings = g("fast_embeddings")
+        w.norm = g("fast_norm")
+        w.output = g("fast_output")
+        for i in range(shape.n_layer):
+            p = f"fast_layers.{i}."
+            L = w.layers[i]
+            L.attention_norm = g(p + "attention_norm")
+            L.wqkv = g(p + "attention.wqkv")
+            L.q_norm = g(p + "attention.q_norm")
+            L.k_norm = g(p + "attention.k_norm")
+            L.wo = g(p + "attention.wo")
+            L.ffn_norm = g(p + "ffn_norm")
+            L.w1 = g(p + "feed_forward.w1")
+            L.w3 = g(p + "feed_forward.w3")
+            L.w2 = g(p + "feed_forward.w2")
+        ctx = ctypes.c_void_p()
+        _check(lib.s2fast_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ctx)), "s2fast_create")
+        self._ctx = ctx
+
+    def close(self) -> None:
+        if getattr(self, "_ctx", None):
+            library().s2fast_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def syncs_per_frame(self, B: int) -> int:
+        return library().s2fast_syncs_per_frame(self._ctx, B)
+
+    def decode_frame(self, hidden, sem_code, uniforms, temperature, top_p, top_k, codes=None, stream=None):
+        s = self.shape
+        B = hidden.shape[0]
+        _dev(hidden, torch.float32, (B, s.in_dim), "hidden")
+        _dev(sem_code, torch.int32, (B,), "sem_code")
+        _dev(uniforms, torch.float32, (B, s.n_steps), "uniforms")
+        _dev(temperature, torch.float32, (B,), "temperature")
+        _dev(top_p, torch.float32, (B,), "top_p")
+        _dev(top_k, torch.int32, (B,), "top_k")
+        if codes is None:
+            codes = torch.empty((B, s.num_codebooks), dtype=torch.int32, device=hidden.device)
+        _dev(codes, torch.int32, (B, s.num_codebooks), "codes")
+        rc = library().s2fast_decode_frame(self._ctx, B, _ptr(hidden), _ptr(sem_code), _ptr(uniforms),
+                                           _ptr(temperature), _ptr(top_p), _ptr(top_k), _ptr(codes),
+                                           _stream(stream))
+        _check(rc, "s2fast_decode_frame")
+        return codes
+
+    def forward_logits(self, hidden, codes, logits=None, stream=None):
+        s = self.shape
+        B = hidden.shape[0]
+        _dev(hidden, torch.float32, (B, s.in_dim), "hidden")
+        _dev(codes, torch.int32, (B, s.num_codebooks), "codes")
+        if logits is None:
+            logits = torch.empty((B, s.n_steps, s.codebook_size), dtype=torch.float32, device=hidden.device)
+        _dev(logits, torch.float32, (B, s.n_steps, s.codebook_size), "logits")
+        rc = library().s2fast_forward_logits(self._ctx, B, _ptr(hidden), _ptr(codes), _ptr(logits), _stream(stream))
+        _check(rc, "s2fast_forward_logits")
+        return logits
+
+
+def rope_table(head_dim: int, context: int, base: float):
+    """The library's host-built RoPE table (cos, sin) as numpy [context, head_dim/2]."""
+    import numpy as np
+    c = np.zeros((context, head_dim // 2), np.float32)
+    s = np.zeros((context, head_dim // 2), np.float32)
+    _check(library().s2fast_test_rope_table(head_dim, context, base, c.ctypes.data, s.ctypes.data),
+           "s2fast_test_rope_table")
+    return c, s
+
+
+def sample(logits, temperature, top_p, top_k, u, stream=None):
+    """The device sampler on given logits [B, V] (test export)."""
+    B, V = logits.shape
+    _dev(logits, torch.float32, (B, V), "logits")
+    _dev(temperature, torch.float32, (B,), "temperature")
+    _dev(top_p, torch.float32, (B,), "top_p")
+    _dev(top_k, torch.int32, (B,), "top_k")
+    _dev(u, torch.float32, (B,), "u")
+    codes = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _check(library().s2fast_test_sample(B, V, _ptr(logits), _ptr(temperature), _ptr(top_p), _ptr(top_k),
+                                        _ptr(u), _ptr(codes), _stream(stream)), "s2fast_test_sample")
+    return codes

@@ -1,0 +1,125 @@
+// Device helpers shared by the frame kernel and the sampler kernel.
+//
+// Cross-block communication inside one kernel launch uses only device-scope
+// relaxed atomics: on gfx950 they compile to global loads/stores with the
+// sc1 cache-policy bit, which are coherent across the eight XCDs without the
+// L2 write-back/invalidate that device-scope fences cost.  Ordering between a
+// block's data stores and its arrival flag comes from s_waitcnt vmcnt(0)
+// (stores are counted by vmcnt on gfx9-family parts) plus a workgroup
+// barrier; readers only touch the data after observing every flag, and read
+// it with sc1 loads, so no stale L2/L1 line can be returned.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s2f {
+
+typedef unsigned int u32;
+typedef unsigned long long u64;
+
+constexpr int NWAVE = 8;             // waves per block
+constexpr int NTHREADS = NWAVE * 64; // threads per block
+constexpr int MMAX = 2;              // activation rows one launch processes per phase
+constexpr int TOPK_MAX = 64;         // sampler candidate limit (one per lane)
+constexpr u32 SPIN_LIMIT = 1u << 22; // bounded waits: far longer than any phase
+
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coh(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32 ld_coh(const u32* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ long long ld_coh(const long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(u32* p, u32 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(long long* p, long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_add_coh(long long* p, long long v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): this wave's vector memory
+// operations (loads and stores) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((u32)b) << 16); }
+
+// 16 bytes of weights -> float values (8 bf16 or 4 f32)
+template <typename WT> struct WTraits;
+template <> struct WTraits<uint16_t> {
+  static constexpr int EPL = 8;
+  __device__ __forceinline__ static void unpack(const uint4& q, float* f) {
+    f[0] = __uint_as_float(q.x << 16); f[1] = __uint_as_float(q.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(q.y << 16); f[3] = __uint_as_float(q.y & 0xFFFF0000u);
+    f[4] = __uint_as_float(q.z << 16); f[5] = __uint_as_float(q.z & 0xFFFF0000u);
+    f[6] = __uint_as_float(q.w << 16); f[7] = __uint_as_float(q.w & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ static float one(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
+};
+template <> struct WTraits<float> {
+  static constexpr int EPL = 4;
+  __device__ __forceinline__ static void unpack(const uint4& q, float* f) {
+    f[0] = __uint_as_float(q.x); f[1] = __uint_as_float(q.y);
+    f[2] = __uint_as_float(q.z); f[3] = __uint_as_float(q.w);
+  }
+  __device__ __forceinline__ static float one(const float* p, int i) { return p[i]; }
+};
+
+// Weights are read exactly once per decode step and never reused inside it:
+// stream them with the non-temporal hint.
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint4 r;
+  r.x = __builtin_nontemporal_load(&q->x);
+  r.y = __builtin_nontemporal_load(&q->y);
+  r.z = __builtin_nontemporal_load(&q->z);
+  r.w = __builtin_nontemporal_load(&q->w);
+  return r;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): add the golden gamma, then
+// two xor-shift-multiply rounds and a final xor-shift, all modulo 2^64.
+__device__ __forceinline__ u64 splitmix64(u64 x) {
+  u64 z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Fixed-point accumulation of split-K partial sums: integer addition is
+// associative, so the reduced value does not depend on the arrival order.
+constexpr double FX_SCALE = 4294967296.0;          // 2^32
+constexpr double FX_INV = 1.0 / 4294967296.0;
+__device__ __forceinline__ long long to_fx(float v) { return __double2ll_rn((double)v * FX_SCALE); }
+__device__ __forceinline__ float from_fx(long long a) { return (float)((double)a * FX_INV); }
+
+}  // namespace s2f

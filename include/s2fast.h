@@ -1,0 +1,186 @@
+/*
+ * s2fast — the Fast-AR codebook decoder of the Dual-AR (Fish Audio S2 Pro)
+ * text-to-speech model, as one HIP library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes ("Fast-AR codebook decoding and the generation main loop",
+ * s2.cpp analysis pages, sections 1-5; Mizuoto "Fish Speech" engine page,
+ * "as upstream"):
+ *   For every frame, codebook 0 is the semantic code (the Slow-AR main token
+ *   minus semantic_begin, clamped into the codebook).  Then, for k = 1..9, a
+ *   4-layer causal GQA transformer runs over the window
+ *       [hidden, fast_embeddings[c_0], ..., fast_embeddings[c_{k-1}]]
+ *   (positions restart at 0 on every call, causal mask offset 0, no KV cache
+ *   in the method's definition), its last position goes through fast_norm
+ *   and the untied fast_output matrix to give codebook_size logits, and a
+ *   sampler turns the logits into c_k.  Output: 10 codes per frame.
+ *
+ * Conventions used by every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors) unless stated otherwise.  The caller owns them.
+ *   - Matrices are row-major [out, in]; vectors are contiguous.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Entry points only enqueue work on it; nothing blocks the host except
+ *     where stated.  The caller synchronises before reading outputs.
+ *   - Return value: S2FAST_OK (0) or a positive S2FAST_ERR_* code.  Argument
+ *     errors are detected on the host before anything is enqueued, and then
+ *     no output is touched.
+ *   - One context may be used by one host thread and one stream at a time;
+ *     calls that overlap on one context race.
+ */
+#ifndef S2FAST_H
+#define S2FAST_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  S2FAST_OK = 0,
+  S2FAST_ERR_ARG = 1,              /* NULL pointer, bad size or unsupported shape */
+  S2FAST_ERR_NO_FAST_DECODER = 2,  /* a required Fast-AR weight pointer is NULL
+                                      (the pages' "model has no fast decoder") */
+  S2FAST_ERR_HIDDEN_DIM = 3,       /* hidden width differs from the model's in_dim */
+  S2FAST_ERR_PREFIX_LEN = 4,       /* prefix would be >= num_codebooks codes */
+  S2FAST_ERR_BATCH = 5,            /* B < 1 or B > max_batch */
+  S2FAST_ERR_HIP = 6,              /* a HIP runtime call failed */
+  S2FAST_ERR_NOMEM = 7,            /* device or host allocation failed */
+  S2FAST_ERR_DEVICE = 8            /* device not supported (not gfx950, or the
+                                      grid cannot be co-resident) */
+};
+
+enum { S2FAST_BF16 = 0, S2FAST_F32 = 1 };
+
+/* Model shape ("Overall architecture & Dual-AR data flow", section 2;
+ * "Model loading and GGUF", section 2.2).  S2 Pro: in_dim 2560, dim 2560,
+ * 4 layers, 32 query / 8 KV heads, head_dim 128, ffn 9728, codebook 4096,
+ * 10 codebooks, context 11, RoPE base 1e6, eps 1e-6. */
+typedef struct s2fast_config {
+  int32_t in_dim;          /* width of the Slow-AR hidden state */
+  int32_t dim;             /* fast_dim */
+  int32_t n_layer;         /* <= S2FAST_MAX_LAYERS */
+  int32_t n_head;          /* query heads */
+  int32_t n_head_kv;       /* key/value heads; n_head % n_head_kv == 0 */
+  int32_t head_dim;        /* even, <= 128 */
+  int32_t ffn_dim;         /* SwiGLU hidden width */
+  int32_t codebook_size;   /* V: logits per call, <= 8192 */
+  int32_t num_codebooks;   /* codes per frame (10): num_codebooks-1 decode steps */
+  int32_t context;         /* RoPE positions (11); must be >= num_codebooks */
+  float rope_base;         /* 1e6 */
+  float norm_eps;          /* 1e-6, also used by the per-head q/k norms */
+  int32_t has_project_in;  /* fast_project_in [dim, in_dim] present */
+  int32_t has_qk_norm;     /* per-head q_norm / k_norm present */
+  int32_t weight_dtype;    /* S2FAST_BF16 or S2FAST_F32; all matrices and norm
+                              weights share it */
+  int32_t max_batch;       /* largest B passed to the decode calls */
+} s2fast_config;
+
+#define S2FAST_MAX_LAYERS 8
+
+/* Tensor names follow the GGUF Fast-AR set ("Model loading and GGUF",
+ * section 3).  All pointers are device pointers of `weight_dtype`, row-major
+ * [out, in].  They must stay valid and unchanged for the context's life;
+ * the library reads them in place and keeps no copy. */
+typedef struct s2fast_layer_weights {
+  const void* attention_norm;  /* [dim] */
+  const void* wqkv;            /* [(n_head + 2 n_head_kv) head_dim, dim]; rows are
+                                  Q heads, then K heads, then V heads */
+  const void* q_norm;          /* [head_dim], NULL iff !has_qk_norm */
+  const void* k_norm;          /* [head_dim], NULL iff !has_qk_norm */
+  const void* wo;              /* [dim, n_head head_dim] */
+  const void* ffn_norm;        /* [dim] */
+  const void* w1;              /* [ffn_dim, dim] gate */
+  const void* w3;              /* [ffn_dim, dim] up */
+  const void* w2;              /* [dim, ffn_dim] down */
+} s2fast_layer_weights;
+
+typedef struct s2fast_weights {
+  const void* project_in;      /* fast_project_in [dim, in_dim], NULL iff !has_project_in */
+  const void* embeddings;      /* fast_embeddings [codebook_size, dim] */
+  const void* norm;            /* fast_norm [dim] */
+  const void* output;          /* fast_output [codebook_size, dim] (untied) */
+  s2fast_layer_weights layers[S2FAST_MAX_LAYERS];
+} s2fast_weights;
+
+typedef struct s2fast_ctx s2fast_ctx;
+
+/* Validate the shape and the weight pointers, allocate the context's device
+ * scratch for max_batch requests and build the bf16-rounded RoPE table.
+ * Uses the current HIP device.  On success *out owns the scratch; release
+ * it with s2fast_destroy.  Shape limits (else S2FAST_ERR_ARG): dim, in_dim,
+ * ffn_dim and the per-KV-group width (n_head/n_head_kv)*head_dim are
+ * multiples of 8 (bf16) or 4 (f32) elements; dim, in_dim, ffn_dim <= 16384;
+ * head_dim even and <= 128; context <= 16; 2 <= num_codebooks <= context;
+ * codebook_size <= 8192; n_head_kv <= 64.
+ * Missing required weight pointers give S2FAST_ERR_NO_FAST_DECODER. */
+int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx** out);
+
+void s2fast_destroy(s2fast_ctx* ctx);
+
+const char* s2fast_strerror(int code);
+
+/* Decode one frame for B requests ("Fast-AR codebook decoding ...", section
+ * 5.1, step 3).
+ *   hidden      [B, in_dim]  f32  Slow-AR hidden state (already normalised)
+ *   sem_code    [B]          i32  main_token - semantic_begin; clamped on the
+ *                                 device to [0, codebook_size-1] (section 5.2)
+ *   uniforms    [B, num_codebooks-1] f32  one uniform in (0,1) per draw;
+ *                                 column k-1 drives codebook k.  Each draw
+ *                                 expands it into one exponential per top-k
+ *                                 candidate with SplitMix64 (see the sampler
+ *                                 below)
+ *   temperature [B] f32  <= 0 (or NaN) decodes greedily
+ *   top_p       [B] f32  nucleus mass; the smallest prefix of the sorted
+ *                        top-k set with cumulative probability >= top_p
+ *   top_k       [B] i32  clamped on the device to [1, min(V, 64)]
+ *   codes       [B, num_codebooks] i32 OUT  [sem_code, c_1, ..., c_9]
+ * Sampler (Mizuoto page, "as upstream": argmax(probs / -log u), top-k 30):
+ *   candidates = the top_k largest logits (value desc, index asc);
+ *   z = l / T; e_j = f32(exp(f64(z_j - z_0))); p_j = e_j / sum (f32, rank
+ *   order); keep ranks 0..m, m = first j with cumulative p >= top_p;
+ *   u_j = (floor(splitmix64(bits(u) * 2^32 + j) / 2^40) + 0.5) * 2^-24;
+ *   code = kept candidate maximising p_j / f32(-log(f64(u_j))).
+ * Errors: S2FAST_ERR_BATCH for B outside [1, max_batch]; S2FAST_ERR_ARG for
+ * NULL pointers.  If a launch fails after validation, codes[:, 1:] are
+ * zero-filled on `stream` (the main loop's "failed fast_decode fills the rest
+ * of the frame with 0" convention, section 5.2) and S2FAST_ERR_HIP is
+ * returned. */
+int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
+                        const float* uniforms, const float* temperature, const float* top_p,
+                        const int32_t* top_k, int32_t* codes, void* stream);
+
+/* Teacher-forced logits: for k = 1..num_codebooks-1 the prefix is
+ * codes[:, 0..k-1] (codes[:, 0] is clamped like sem_code; the last column
+ * is not read) and logits[:, k-1, :] receives the codebook_size logits of
+ * that call.
+ *   hidden [B, in_dim] f32; codes [B, num_codebooks] i32 (each in [0, V));
+ *   logits [B, num_codebooks-1, codebook_size] f32 OUT.
+ * Out-of-range prefix codes are clamped to [0, V-1] on the device. */
+int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* codes,
+                          float* logits, void* stream);
+
+/* ---- test exports (used by the test suite; not part of the hot path) ---- */
+
+/* Host-side: the RoPE table the context uses, [context, head_dim/2] cos and
+ * sin as float32 holding bf16-rounded values of cos/sin(p * base^(-2i/hd))
+ * (Mizuoto page, "as upstream").  cos_out / sin_out are HOST pointers. */
+int s2fast_test_rope_table(int32_t head_dim, int32_t context, float rope_base,
+                           float* cos_out, float* sin_out);
+
+/* Device sampler on caller-supplied logits [B, V] (device), with the same
+ * settings layout as s2fast_decode_frame but one uniform per request
+ * (u [B]).  Writes codes [B] (device).  V <= 8192. */
+int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* temperature,
+                       const float* top_p, const int32_t* top_k, const float* u, int32_t* codes,
+                       void* stream);
+
+/* Number of grid-wide synchronisation points one frame of B requests
+ * takes on this context, or -1 on error (for measurement reports). */
+int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S2FAST_H */

@@ -1,0 +1,115 @@
+"""The C-ABI library: loads, exports what include/s2fast.h declares, validates
+arguments on the host, and builds the same RoPE table as the oracle.
+CPU only: nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dual_ar_neural_amd import binding as bd
+from oracle import fast_ar as fa
+from synth import inputs as si
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s2fast.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s2fast_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bd.library()
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bd.EXPORTS)
+
+
+def test_strerror():
+    lib = bd.library()
+    assert lib.s2fast_strerror(0) == b"ok"
+    for code in range(1, 9):
+        assert len(lib.s2fast_strerror(code)) > 5
+    assert lib.s2fast_strerror(99) == b"unknown error"
+
+
+@pytest.mark.parametrize("hd,ctx,base", [(128, 11, 1e6), (64, 11, 1e6), (40, 11, 1e6), (128, 16, 1e4)])
+def test_rope_table_bit_exact_with_oracle(hd, ctx, base):
+    c, s = bd.rope_table(hd, ctx, base)
+    oc, os_ = fa.rope_table(hd, ctx, base)
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32))
+
+
+def _fake_weights(shape, with_layers=True):
+    """Distinct aligned fake addresses: enough for host-side validation,
+    which never dereferences them."""
+    w = bd.Weights()
+    addr = [0x100000]
+
+    def nxt():
+        addr[0] += 0x1000
+        return addr[0]
+    w.embeddings, w.norm, w.output = nxt(), nxt(), nxt()
+    if shape.has_project_in:
+        w.project_in = nxt()
+    if with_layers:
+        for i in range(shape.n_layer):
+            for f in bd.LAYER_FIELDS:
+                setattr(w.layers[i], f, nxt())
+    return w
+
+
+def _create(cfg, w):
+    ctx = ctypes.c_void_p()
+    rc = bd.library().s2fast_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ctx))
+    return rc, ctx
+
+
+def test_create_rejects_missing_fast_decoder():
+    cfg = bd.make_config(si.S2PRO, 1)
+    w = _fake_weights(si.S2PRO, with_layers=False)
+    rc, ctx = _create(cfg, w)
+    assert rc == 2 and not ctx.value          # S2FAST_ERR_NO_FAST_DECODER
+    w = _fake_weights(si.S2PRO)
+    w.output = None
+    assert _create(cfg, w)[0] == 2
+    w = _fake_weights(si.S2PRO)
+    w.layers[3].k_norm = None                 # q/k norm declared but missing
+    assert _create(cfg, w)[0] == 2
+    cfg_p = bd.make_config(si.S2PRO_PROJ, 1)
+    w = _fake_weights(si.S2PRO)               # no project_in pointer
+    assert _create(cfg_p, w)[0] == 2
+
+
+@pytest.mark.parametrize("field,value", [
+    ("head_dim", 130), ("head_dim", 63), ("n_head_kv", 3), ("dim", 2564), ("ffn_dim", 9730),
+    ("codebook_size", 9000), ("num_codebooks", 12), ("context", 17), ("n_layer", 9), ("n_layer", 0),
+    ("max_batch", 0), ("weight_dtype", 7), ("in_dim", 2048)])
+def test_create_rejects_bad_shapes(field, value):
+    cfg = bd.make_config(si.S2PRO, 1)
+    setattr(cfg, field, value)
+    assert _create(cfg, _fake_weights(si.S2PRO))[0] == 1      # S2FAST_ERR_ARG
+
+
+def test_create_rejects_misaligned_weights():
+    cfg = bd.make_config(si.S2PRO, 1)
+    w = _fake_weights(si.S2PRO)
+    w.layers[1].wo = w.layers[1].wo + 2
+    assert _create(cfg, w)[0] == 1
+
+
+def test_null_arguments():
+    lib = bd.library()
+    assert lib.s2fast_create(None, None, None) == 1
+    assert lib.s2fast_decode_frame(None, 1, None, None, None, None, None, None, None, None) == 1
+    assert lib.s2fast_forward_logits(None, 1, None, None, None, None) == 1
+    assert lib.s2fast_test_sample(0, 10, None, None, None, None, None, None, None) == 1
+    assert lib.s2fast_syncs_per_frame(None, 1) == -1
+    lib.s2fast_destroy(None)

@@ -1,0 +1,187 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Logits: |delta| <= 1e-2 * max|logit| + 1e-3 under teacher-forced prefixes.
+Codes: bit-exact except at decisions the oracle reports as knife-edges
+(greedy top-2 gap < 1e-3; sampled top-k boundary, nucleus boundary or race
+within the sampler's margins)."""
+import numpy as np
+import pytest
+import torch
+
+from dual_ar_neural_amd import binding as bd
+from oracle import sampler as sm
+from synth import inputs as si
+from tests import parity as pr
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    _announce("tiny model")
+    return pr.make_pair(si.TINY, si.WORKLOADS["tiny"].seed(0), max_batch=4)
+
+
+@pytest.fixture(scope="module")
+def ragged():
+    _announce("ragged model")
+    return pr.make_pair(si.RAGGED, si.WORKLOADS["ragged"].seed(0), max_batch=4)
+
+
+@pytest.fixture(scope="module")
+def s2pro():
+    _announce("s2pro model (bf16, 828 MB)")
+    return pr.make_pair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0), max_batch=2)
+
+
+# ------------------------------------------------------------------ sampler
+
+def _sampler_cases():
+    rng = np.random.default_rng(123)
+    cases = []
+    for V in (4096, 256, 300, 50, 8192, 64, 2):
+        for T, tp, tk in ((0.8, 0.8, 30), (1.0, 0.9, 30), (0.0, 0.8, 30), (-1.0, 0.5, 30), (0.05, 0.95, 64),
+                          (3.0, 1.0, 100), (0.7, 0.0, 30), (0.9, 1e-9, 1), (1.2, 0.99, 0), (0.6, 0.7, 13)):
+            for kind in ("normal", "ties", "flat", "spiky"):
+                if kind == "normal":
+                    l = rng.standard_normal(V).astype(np.float32) * rng.uniform(0.5, 4)
+                elif kind == "ties":
+                    l = (np.round(rng.standard_normal(V) * 2) / 2).astype(np.float32)
+                elif kind == "flat":
+                    l = np.full(V, 0.25, np.float32)
+                else:
+                    l = rng.standard_normal(V).astype(np.float32)
+                    l[rng.integers(0, V, size=3)] += 8.0
+                u = np.float32((rng.integers(0, 1 << 23) + 0.5) * 2.0 ** -23)
+                cases.append((l, np.float32(T), np.float32(tp), np.int32(tk), u))
+    return cases
+
+
+def test_sampler_bit_exact_with_oracle():
+    cases = _sampler_cases()
+    by_v = {}
+    for c in cases:
+        by_v.setdefault(c[0].size, []).append(c)
+    n = 0
+    for V, cs in by_v.items():
+        logits = pr.to_dev(np.stack([c[0] for c in cs]))
+        T = pr.to_dev(np.array([c[1] for c in cs], np.float32))
+        tp = pr.to_dev(np.array([c[2] for c in cs], np.float32))
+        tk = pr.to_dev(np.array([c[3] for c in cs], np.int32))
+        u = pr.to_dev(np.array([c[4] for c in cs], np.float32))
+        got = bd.sample(logits, T, tp, tk, u).cpu().numpy()
+        for i, c in enumerate(cs):
+            want = sm.sample(*c).code
+            assert got[i] == want, (V, i, c[1:], got[i], want)
+            n += 1
+    _announce(f"sampler: {n} cases bit-exact")
+
+
+def test_sampler_many_uniforms_one_logit_vector():
+    rng = np.random.default_rng(7)
+    V, B = 4096, 512
+    l = rng.standard_normal(V).astype(np.float32) * 2
+    us = ((rng.integers(0, 1 << 23, size=B) + 0.5) * 2.0 ** -23).astype(np.float32)
+    got = bd.sample(pr.to_dev(np.tile(l, (B, 1))), pr.to_dev(np.full(B, 0.8, np.float32)),
+                    pr.to_dev(np.full(B, 0.8, np.float32)), pr.to_dev(np.full(B, 30, np.int32)),
+                    pr.to_dev(us)).cpu().numpy()
+    want = [sm.sample(l, 0.8, 0.8, 30, u).code for u in us]
+    assert list(got) == want
+
+
+# ------------------------------------------------------------------ model parity
+
+def _frames(w, n, B):
+    fr = si.make_frames(w, n_frames=n, batch=B)
+    return fr
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sampled"])
+def test_tiny_codes_and_logits(tiny, mode):
+    w = si.WORKLOADS["tiny"]
+    fr = _frames(w, 6, 1)
+    temp = np.zeros(1, np.float32) if mode == "greedy" else fr["temperature"]
+    excused = 0
+    for f in range(6):
+        codes = pr.gpu_decode(tiny, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], temp,
+                              fr["top_p"], fr["top_k"])
+        excused += pr.check_codes(tiny, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], temp,
+                                  fr["top_p"], fr["top_k"], codes)
+        worst, rel, _, _ = pr.check_logits(tiny, fr["hidden"][f], codes)
+        assert worst <= 1.0, worst
+        assert rel < 1e-4, rel   # far inside the bar: float32 accumulation on both sides
+    _announce(f"tiny {mode}: 6 frames, excused knife-edges {excused}")
+
+
+def test_ragged_batch(ragged):
+    w = si.WORKLOADS["ragged"]
+    fr = _frames(w, 3, 3)
+    excused = 0
+    for f in range(3):
+        codes = pr.gpu_decode(ragged, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], fr["temperature"],
+                              fr["top_p"], fr["top_k"])
+        excused += pr.check_codes(ragged, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f],
+                                  fr["temperature"], fr["top_p"], fr["top_k"], codes)
+        worst, rel, _, _ = pr.check_logits(ragged, fr["hidden"][f], codes)
+        assert worst <= 1.0 and rel < 1e-4, (worst, rel)
+    _announce(f"ragged B=3: excused {excused}")
+
+
+def test_s2pro_b1(s2pro):
+    w = si.WORKLOADS["s2pro_b1"]
+    fr = _frames(w, 3, 1)
+    excused = 0
+    for f in range(3):
+        codes = pr.gpu_decode(s2pro, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], fr["temperature"],
+                              fr["top_p"], fr["top_k"])
+        excused += pr.check_codes(s2pro, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f],
+                                  fr["temperature"], fr["top_p"], fr["top_k"], codes)
+        worst, rel, _, _ = pr.check_logits(s2pro, fr["hidden"][f], codes)
+        _announce(f"s2pro frame {f}: worst |d|/tol {worst:.2e}, |d|/max {rel:.2e}")
+        assert worst <= 1.0 and rel < 1e-4, (worst, rel)
+    _announce(f"s2pro B=1: excused {excused}")
+
+
+def test_s2pro_greedy_b2(s2pro):
+    w = si.WORKLOADS["s2pro_b1"]
+    fr = _frames(w, 1, 2)
+    T = np.zeros(2, np.float32)
+    codes = pr.gpu_decode(s2pro, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], T, fr["top_p"], fr["top_k"])
+    pr.check_codes(s2pro, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], T, fr["top_p"], fr["top_k"], codes)
+
+
+# ------------------------------------------------------------------ behaviour
+
+def test_deterministic(tiny):
+    fr = _frames(si.WORKLOADS["tiny"], 1, 2)
+    a = pr.gpu_decode(tiny, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
+                      fr["top_p"], fr["top_k"])
+    b = pr.gpu_decode(tiny, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
+                      fr["top_p"], fr["top_k"])
+    assert np.array_equal(a, b)
+    la = pr.gpu_forward_logits(tiny, fr["hidden"][0], a)
+    lb = pr.gpu_forward_logits(tiny, fr["hidden"][0], a)
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+
+
+def test_sem_code_is_clamped(tiny):
+    fr = _frames(si.WORKLOADS["tiny"], 1, 2)
+    V = si.TINY.codebook_size
+    sem = np.array([-5, V + 10], np.int32)
+    codes = pr.gpu_decode(tiny, fr["hidden"][0], sem, fr["uniforms"][0], np.zeros(2, np.float32),
+                          fr["top_p"], fr["top_k"])
+    assert list(codes[:, 0]) == [0, V - 1]
+    pr.check_codes(tiny, fr["hidden"][0], sem, fr["uniforms"][0], np.zeros(2, np.float32), fr["top_p"],
+                   fr["top_k"], codes)
+
+
+def test_batch_limits(tiny):
+    fr = _frames(si.WORKLOADS["tiny"], 1, 5)
+    with pytest.raises(bd.S2FastError) as e:
+        pr.gpu_decode(tiny, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
+                      fr["top_p"], fr["top_k"])
+    assert e.value.code == 5
