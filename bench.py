@@ -1,0 +1,204 @@
+"""Benchmark of the Fast-AR frame decoder on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A "step" is one s2fast_decode_frame call: the nine decode calls of one frame
+for a batch of requests.  The measured workload is the S2 Pro-shaped Fast-AR
+(4 layers, dim 2560, 32/8 heads, head_dim 128, ffn 9728, 4096 codes, bf16
+weights, float32 arithmetic) at batch 1 with independent synthetic frames
+(temperature 0.8, top_p 0.8, top_k 30).  All inputs are on the device before
+the timed region; HIP events on the launch stream bracket exactly K frames.
+
+Prints one JSON line: frames/s, per-frame time, the decoder kernel's
+achieved algorithmic HBM bandwidth against the 8 TB/s peak, the float32
+oracle timed on this host's cores on a few frames, and a batch 16/64 sweep.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "Fast-AR frames/sec (9 codebooks) at batch 1/16/64; achieved HBM GB/s"
+
+
+def algorithmic_bytes_per_frame(shape, batch: int) -> int:
+    """Bytes a frame of `batch` requests must move at minimum: every weight
+    read once per decode step (matrices, norm vectors and one embedding row
+    per request), plus each request's inputs and codes."""
+    s = shape
+    wb = 2 if s.weight_dtype == "bf16" else 4
+    per_layer = (s.qkv_dim * s.dim + s.dim * s.attn_dim + 2 * s.ffn_dim * s.dim + s.dim * s.ffn_dim
+                 + 2 * s.dim + (2 * s.head_dim if s.has_qk_norm else 0)) * wb
+    per_step = s.n_layer * per_layer + (s.codebook_size * s.dim + s.dim) * wb + batch * s.dim * wb
+    per_frame = s.n_steps * per_step
+    if s.has_project_in:
+        per_frame += s.dim * s.in_dim * wb
+    io = batch * (s.in_dim * 4 + 4 + s.n_steps * 4 + 3 * 4 + s.num_codebooks * 4)
+    return per_frame + io
+
+
+def time_frames(torch, ctx, dev_in, B, frames, warmup):
+    """Decode `warmup` then `frames` frames; returns seconds for the timed ones."""
+    hidden, sem, uni, temp, tp, tk, out = dev_in
+    F = hidden.shape[0]
+    for i in range(warmup):
+        f = i % F
+        ctx.decode_frame(hidden[f], sem[f], uni[f], temp, tp, tk, codes=out[f])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(frames):
+        f = i % F
+        ctx.decode_frame(hidden[f], sem[f], uni[f], temp, tp, tk, codes=out[f])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3
+
+
+def upload(torch, fr):
+    d = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
+    hidden = d(fr["hidden"], torch.float32)
+    F, B = hidden.shape[:2]
+    return (hidden, d(fr["sem_code"], torch.int32), d(fr["uniforms"], torch.float32),
+            d(fr["temperature"], torch.float32), d(fr["top_p"], torch.float32), d(fr["top_k"], torch.int32),
+            torch.empty((F, B, 10), dtype=torch.int32, device="cuda"))
+
+
+def cpu_baseline(workload, frames: int):
+    """The oracle as it stands, on this host: literal recompute of every
+    window, float32 numpy, BLAS on all the cores the process may use."""
+    from oracle import fast_ar as fa
+    from synth import inputs as si
+    w = workload
+    model = fa.Model.from_weights(w.shape, si.make_weights(w.shape, w.seed(0)))
+    fr = si.make_frames(w, n_frames=frames + 1)
+    fa.decode_frame(model, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
+                    fr["top_p"], fr["top_k"])
+    t0 = time.perf_counter()
+    for f in range(1, frames + 1):
+        fa.decode_frame(model, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], fr["temperature"],
+                        fr["top_p"], fr["top_k"])
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    threads = os.environ.get("OMP_NUM_THREADS")
+    if threads and threads.isdigit():
+        cores = min(cores, int(threads))
+    return {"value": round(w.batch * frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
+            "sample": f"{frames} frames of {w.name} (batch {w.batch}) after one warm-up frame, "
+                      f"{dt:.1f} s wall clock"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256, help="timed frames")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the batch 16/64 lines")
+    ap.add_argument("--cpu-frames", type=int, default=24)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the decoder runs on a single MI355X; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dual_ar_neural_amd import binding as bd
+    from synth import inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = si.WORKLOADS["s2pro_b1"]
+    shape = w.shape
+    print(f"[bench] generating {w.name} weights", file=sys.stderr, flush=True)
+    host = si.make_weights(shape, w.seed(0))
+    dev = bd.device_weights(shape, host)
+    del host
+    ctx = bd.FastAR(shape, dev, max_batch=64)
+    fr = si.make_frames(w, n_frames=min(w.frames, max(args.steps, 1)))
+    dev_in = upload(torch, fr)
+
+    # a plain device copy of known size, so counter runs can calibrate bytes
+    cal = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} frames at batch 1", file=sys.stderr, flush=True)
+    secs = time_frames(torch, ctx, dev_in, 1, args.steps, args.warmup)
+    B = 1
+    frames_per_s = B * args.steps / secs
+    ms = secs * 1e3 / args.steps
+    launches = args.steps * B
+    bytes_frame = algorithmic_bytes_per_frame(shape, B)
+    kern_s = secs / launches
+    achieved = bytes_frame / kern_s / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(frames_per_s, 3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "S2 Pro-shaped Fast-AR frame decode, batch 1, independent frames",
+                   "batch": 1, "weights": "bf16", "dim": shape.dim, "layers": shape.n_layer,
+                   "heads": f"{shape.n_head}/{shape.n_head_kv}", "head_dim": shape.head_dim,
+                   "ffn": shape.ffn_dim, "codebook": shape.codebook_size, "codebooks": shape.num_codebooks,
+                   "sampling": "T 0.8, top_p 0.8, top_k 30"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "frame_kernel<bf16>", "bytes_per_launch": bytes_frame,
+                     "avg_launch_us": round(kern_s * 1e6, 2)},
+        "syncs_per_frame": ctx.syncs_per_frame(1),
+    }
+    if not args.no_sweep:
+        sweep = {}
+        for Bs, wname, nf in ((16, "s2pro_b16", 4), (64, "s2pro_b64", 2)):
+            ws = si.WORKLOADS[wname]
+            if ws.shape is not shape:
+                hs = si.make_weights(ws.shape, ws.seed(0))
+                ds = bd.device_weights(ws.shape, hs)
+                del hs
+                cs = bd.FastAR(ws.shape, ds, max_batch=Bs)
+            else:
+                ds, cs = None, ctx
+            frs = si.make_frames(ws, n_frames=nf)
+            di = upload(torch, frs)
+            print(f"[bench] timing {nf} frames at batch {Bs}", file=sys.stderr, flush=True)
+            sec = time_frames(torch, cs, di, Bs, nf, 1)
+            fb = algorithmic_bytes_per_frame(ws.shape, Bs)
+            sweep[f"b{Bs}"] = {"frames_per_s": round(Bs * nf / sec, 2), "ms_per_frame": round(sec * 1e3 / nf, 3),
+                               "hbm_gbs": round(fb * nf / sec / 1e9, 1),
+                               "frac": round(fb * nf / sec / 1e9 / PEAK_HBM_GBS, 4), "frames": nf,
+                               "workload": ws.name}
+            if cs is not ctx:
+                cs.close()
+                del ds
+            torch.cuda.empty_cache()
+        result["batch_sweep"] = sweep
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_frames)
+    print(json.dumps(result), flush=True)
+    ctx.close()
+
+
+if __name__ == "__main__":
+    main()

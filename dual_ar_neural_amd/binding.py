@@ -76,6 +76,8 @@ def library() -> ctypes.CDLL:
         lib.s2fast_test_rope_table.restype = ctypes.c_int
         lib.s2fast_test_sample.argtypes = [I, I, P, P, P, P, P, P, V]
         lib.s2fast_test_sample.restype = ctypes.c_int
+        lib.s2fast_test_timeline.argtypes = [P, I, P, I]
+        lib.s2fast_test_timeline.restype = ctypes.c_int
         lib.s2fast_syncs_per_frame.argtypes = [P, I]
         lib.s2fast_syncs_per_frame.restype = ctypes.c_int
         _lib = lib
@@ -84,7 +86,7 @@ def library() -> ctypes.CDLL:
 
 EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_frame",
            "s2fast_forward_logits", "s2fast_test_rope_table", "s2fast_test_sample",
-           "s2fast_syncs_per_frame")
+           "s2fast_syncs_per_frame", "s2fast_test_timeline")
 
 
 def _strerror(code: int) -> str:
@@ -180,6 +182,20 @@ class FastAR:
             self.close()
         except Exception:
             pass
+
+    def timeline(self, enable: bool = True, fetch: bool = False):
+        """Turn per-block phase timing on/off; with fetch, return the last
+        frame's marks as numpy [blocks, 256, 8] (100 MHz ticks): per sync
+        point, phase done, released, then in-phase marks."""
+        import numpy as np
+        out = None
+        if fetch:
+            import torch as _t
+            nb = _t.cuda.get_device_properties(0).multi_processor_count
+            out = np.zeros((nb, 256, 8), np.uint32)
+        _check(library().s2fast_test_timeline(self._ctx, int(enable), None if out is None else out.ctypes.data,
+                                              0 if out is None else out.size), "s2fast_test_timeline")
+        return out
 
     def syncs_per_frame(self, B: int) -> int:
         return library().s2fast_syncs_per_frame(self._ctx, B)

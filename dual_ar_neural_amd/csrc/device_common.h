@@ -35,6 +35,11 @@ __device__ __forceinline__ u32 ld_coh(const u32* p) {
 __device__ __forceinline__ long long ld_coh(const long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ u64 ld_coh64(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<const u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float lo_f32(u64 v) { return __uint_as_float((u32)v); }
+__device__ __forceinline__ float hi_f32(u64 v) { return __uint_as_float((u32)(v >> 32)); }
 __device__ __forceinline__ void st_coh(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

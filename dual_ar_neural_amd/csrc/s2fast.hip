@@ -67,41 +67,57 @@ struct FrameArgs {
   const int* forced;       // [ncb] teacher-forced codes, or nullptr
   int* codes_out;          // [ncb] or nullptr
   float* logits_out;       // [ncb-1][V] or nullptr
-  // scratch (device; cross-block traffic only through sc1 accesses)
+  // Per-frame arena.  Every (step, layer) output has its own 256-byte
+  // aligned region, written once per frame (write-through sc1 stores or
+  // device atomics) and read only after the grid sync that follows its
+  // writes, so readers may use ordinary L2-cacheable loads: no stale copy of
+  // a region can exist in any L2 (the kernel starts with an acquire that
+  // invalidates lines cached by earlier frames).
   float* xin0;             // [dim] fast_project_in(hidden)
-  float* x;                // [MMAX][dim] residual stream of the new rows
-  float* qkv;              // [MMAX][qkv_dim]
-  long long* acc;          // [MMAX][dim] fixed-point attention output (0 at entry and exit)
-  float* g;                // [MMAX][ffn]
+  float* x;                // [slot][MMAX][dim] residual stream after each layer
+  float* qkv;              // [slot][MMAX][qkv_dim]
+  long long* acc;          // [slot][MMAX][dim] fixed-point attention output (zero between frames)
+  float* g;                // [slot][MMAX][ffn]
   float* kv;               // [n_layer][ctx][n_kv][2][hd] this frame's keys/values
-  float* logits;           // [V]
+  float* logits;           // [step][V]
+  long long x_slot, qkv_slot, acc_slot, g_slot, logits_slot;  // region strides (elements)
   u32* flags;              // [P][64] per-block barrier epochs
   u32 epoch0;              // epoch reached before this launch
   u32* err;                // watchdog word
+  u32* tlog;               // optional [P][TLOG_MAX][TLOG_W] wall-clock marks
+  u32 tlog_epoch;          // scratch for the marks: epoch at the phase start
 };
+constexpr int TLOG_MAX = 256;
+constexpr int TLOG_W = 8;   // per sync point: phase done, released, then in-phase marks 2..7
+constexpr int GEMV_RING = 8;   // weight chunks in flight per wave
 
 // ---------------------------------------------------------------- LDS map
 struct Lds {
-  float* act;    // [MMAX][kmax]; also the sampler's logits
+  float* act;    // [MMAX][kmax] GEMV activations (see phys()); also the sampler's logits
   float* red;    // [rmax][NWAVE][MMAX]
   float* small;  // [64]: rms scratch, epilogue temporaries
   float* q;      // [MMAX][gheads][hd]
   float* kc;     // [ctx][hd]
   float* vc;     // [ctx][hd]
   float* sc;     // [MMAX][gheads][ctx] attention probabilities
-  float* a1;     // [rmax][MMAX] w1 outputs before SwiGLU
   float* cval;   // [64]
   int* cidx;     // [64]
   u32* mark;     // [256]
   int* codes;    // [16]
   int* flag;     // [4]
+  float* nw;     // [dim] RMSNorm weight of the current layer phase
+  float* fnw;    // [dim] fast_norm weight (loaded once per frame)
+  float* qkn;    // [n_layer][2][hd] q_norm and k_norm weights (loaded once per frame)
+  float* rope;   // [2][ctx][hd/2] cos and sin (loaded once per frame)
 };
 
-__host__ __device__ inline size_t lds_floats(int kmax, int rmax, int gheads, int hd, int ctx, int V) {
+__host__ __device__ inline size_t lds_floats(int kmax, int rmax, int gheads, int hd, int ctx, int V, int dim,
+                                             int n_layer) {
   size_t act = (size_t)MMAX * kmax;
   if ((size_t)V > act) act = V;
   return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)MMAX * gheads * hd + 2 * (size_t)ctx * hd +
-         (size_t)MMAX * gheads * ctx + (size_t)rmax * MMAX + 64 + 64 + 256 + 16 + 4;
+         (size_t)MMAX * gheads * ctx + 64 + 64 + 256 + 16 + 4 + 2 * (size_t)dim + (size_t)n_layer * 2 * hd +
+         (size_t)ctx * hd;
 }
 
 __device__ inline Lds carve(float* base, const FrameArgs& a) {
@@ -116,14 +132,31 @@ __device__ inline Lds carve(float* base, const FrameArgs& a) {
   s.kc = p; p += (size_t)a.ctx_len * a.hd;
   s.vc = p; p += (size_t)a.ctx_len * a.hd;
   s.sc = p; p += (size_t)MMAX * a.gheads * a.ctx_len;
-  s.a1 = p; p += (size_t)a.rmax * MMAX;
   s.cval = p; p += 64;
   s.cidx = reinterpret_cast<int*>(p); p += 64;
   s.mark = reinterpret_cast<u32*>(p); p += 256;
   s.codes = reinterpret_cast<int*>(p); p += 16;
-  s.flag = reinterpret_cast<int*>(p);
+  s.flag = reinterpret_cast<int*>(p); p += 4;
+  s.nw = p; p += a.dim;
+  s.fnw = p; p += a.dim;
+  s.qkn = p; p += (size_t)a.n_layer * 2 * a.hd;
+  s.rope = p;
   return s;
 }
+
+// window position of new row m at decode step `step`: rows 0 and 1 at step 1, row `step` after
+__device__ __forceinline__ int row_pos(int step, int m) { return step == 1 ? m : step; }
+
+// per-(step, layer) regions of the frame arena
+__device__ __forceinline__ size_t slot_of(const FrameArgs& a, int step, int l) { return (size_t)(step - 1) * a.n_layer + l; }
+__device__ __forceinline__ float* xb(const FrameArgs& a, int step, int l) { return a.x + slot_of(a, step, l) * a.x_slot; }
+__device__ __forceinline__ float* qkvb(const FrameArgs& a, int step, int l) { return a.qkv + slot_of(a, step, l) * a.qkv_slot; }
+__device__ __forceinline__ float* gb(const FrameArgs& a, int step, int l) { return a.g + slot_of(a, step, l) * a.g_slot; }
+__device__ __forceinline__ long long* accb(const FrameArgs& a, int step, int l) { return a.acc + slot_of(a, step, l) * a.acc_slot; }
+__device__ __forceinline__ float* logitsb(const FrameArgs& a, int step) { return a.logits + (size_t)(step - 1) * a.logits_slot; }
+
+// plain (L2-cacheable) loads of arena data
+__device__ __forceinline__ u64 ld64(const void* p) { return *reinterpret_cast<const u64*>(p); }
 
 // rows [r0, r1) of an n-row matrix owned by part `j` of `parts`
 __device__ __forceinline__ void split_rows(int n, int j, int parts, int& r0, int& r1) {
@@ -133,13 +166,19 @@ __device__ __forceinline__ void split_rows(int n, int j, int parts, int& r0, int
 
 // --------------------------------------------------------------- grid sync
 // Device-wide barrier.  Every thread first waits for its own stores (vmcnt),
+// issued before the GEMV_RING-1 prologue loads of the next phase,
 // the block meets at s_barrier, then wave 0 publishes the block's epoch and
 // polls every block's flag with coherent loads.  Returns false (after
 // raising the watchdog word) if a flag does not arrive within SPIN_LIMIT
 // polls; the caller then leaves the kernel.
-__device__ bool grid_sync(const FrameArgs& a, u32& epoch, const Lds& s) {
-  wait_vmem();
+__device__ __forceinline__ bool grid_sync(const FrameArgs& a, u32& epoch, const Lds& s) {
+  // vmcnt(GEMV_RING-1): everything but the next phase's prologue loads has
+  // completed, in particular this thread's output stores
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (GEMV_RING - 1));
   __syncthreads();
+  const u32 idx = epoch - a.epoch0;
+  if (a.tlog && threadIdx.x == 0 && idx < TLOG_MAX)
+    a.tlog[((size_t)blockIdx.x * TLOG_MAX + idx) * TLOG_W] = (u32)wall_clock64();
   ++epoch;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -156,77 +195,300 @@ __device__ bool grid_sync(const FrameArgs& a, u32& epoch, const Lds& s) {
     if (lane == 0) {
       if (!ok) atomicOr(a.err, 1u);
       s.flag[0] = ok ? 0 : 1;
+      if (a.tlog && idx < TLOG_MAX) a.tlog[((size_t)blockIdx.x * TLOG_MAX + idx) * TLOG_W + 1] = (u32)wall_clock64();
     }
   }
   __syncthreads();
   return s.flag[0] == 0;
 }
 
-// --------------------------------------------------------------- GEMV
-// Rows [row0, row0+nrows) of W (row stride ldw elements), columns
-// [col0, col0+K), against M activation rows in LDS (row stride act_ld).
-// Each wave takes a contiguous range of 64-segment chunks (16 bytes per
-// lane) of the block's rows and leaves per-(row, wave, m) partial sums in
-// red, which the caller zeroes beforehand and reduces in wave order.
+
+// in-phase timeline mark (instrumented runs only): word w of the current
+// phase's record, by thread 0
+__device__ __forceinline__ void mark(const FrameArgs& a, u32 phase, int w) {
+  if (a.tlog && threadIdx.x == 0 && phase < TLOG_MAX)
+    a.tlog[((size_t)blockIdx.x * TLOG_MAX + phase) * TLOG_W + w] = (u32)wall_clock64();
+}
+
+// --------------------------------------------------------------- staging
+// Cross-block inputs (arena regions) are read with plain 8-byte loads.  Every
+// helper issues a batch of independent loads per thread before using any of
+// them, so a phase pays about one memory round trip for its activations.
+constexpr int SB = 8;   // loads in flight per thread per batch
+
+// Position of natural element k of a GEMV activation row of width K in LDS.
+// For bf16 weights a lane consumes 8 columns (16 bytes of weights) per load;
+// its 8 activation floats are kept as two 16-byte halves in two separate
+// half-rows, so each half is one conflict-free ds_read_b128 across the wave
+// (lane-consecutive 16-byte addresses).  f32 weights consume 4 columns, which
+// is already one lane-consecutive 16-byte read: identity.
 template <typename WT>
-__device__ __forceinline__ void gemv(const WT* __restrict__ W, long long ldw, int col0, int K, int row0,
-                                     int nrows, const float* act, int act_ld, int M, float* red) {
-  constexpr int EPL = WTraits<WT>::EPL;
-  constexpr int U = 4;
-  const int S = K / EPL;
-  const int C = (S + 63) >> 6;
-  const int T = nrows * C;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = (int)(((long long)T * wave) / NWAVE);
-  const int t1 = (int)(((long long)T * (wave + 1)) / NWAVE);
-  if (t0 >= t1) return;
-  float acc[MMAX];
+__device__ __forceinline__ int phys(int k, int K) {
+  if (WTraits<WT>::EPL == 8) return ((k >> 3) << 2) + (k & 3) + ((k & 4) ? (K >> 1) : 0);
+  return k;
+}
+
+// n floats (n even, src 8-byte aligned) of arena data into LDS; PERM places
+// them for a GEMV over K = n columns.
+template <typename WT, bool PERM>
+__device__ __forceinline__ void stage_arena(float* dst, const float* src, int n) {
+  const int np = n >> 1;
+  for (int base = 0; base < np; base += NTHREADS * SB) {
+    u64 v[SB];
 #pragma unroll
-  for (int m = 0; m < MMAX; ++m) acc[m] = 0.0f;
-  int cur = t0 / C;
-  auto flush = [&](int r) {
-#pragma unroll
-    for (int m = 0; m < MMAX; ++m) {
-      if (m < M) {
-        float v = wave_sum(acc[m]);
-        if (lane == 0) red[((size_t)r * NWAVE + wave) * MMAX + m] = v;
-      }
-      acc[m] = 0.0f;
-    }
-  };
-  for (int t = t0; t < t1; t += U) {
-    uint4 q[U];
-    int seg[U], rr[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tt = t + u;
-      rr[u] = tt / C;
-      seg[u] = (tt - rr[u] * C) * 64 + lane;
-      ok[u] = (tt < t1) && (seg[u] < S);
-      if (ok[u]) q[u] = ld_stream(W + (long long)(row0 + rr[u]) * ldw + col0 + (long long)seg[u] * EPL);
-      else q[u] = make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < SB; ++j) {
+      const int i = base + j * NTHREADS + threadIdx.x;
+      v[j] = i < np ? ld64(src + 2 * i) : 0ull;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (t + u < t1) {
-        if (rr[u] != cur) { flush(cur); cur = rr[u]; }
-        if (ok[u]) {
-          float w[EPL];
-          WTraits<WT>::unpack(q[u], w);
-#pragma unroll
-          for (int m = 0; m < MMAX; ++m) {
-            if (m < M) {
-              const float* ap = act + (size_t)m * act_ld + (size_t)seg[u] * EPL;
-#pragma unroll
-              for (int e = 0; e < EPL; ++e) acc[m] = fmaf(w[e], ap[e], acc[m]);
-            }
-          }
-        }
+    for (int j = 0; j < SB; ++j) {
+      const int i = base + j * NTHREADS + threadIdx.x;
+      if (i < np) {
+        float* d = dst + (PERM ? phys<WT>(2 * i, n) : 2 * i);
+        d[0] = lo_f32(v[j]);
+        d[1] = hi_f32(v[j]);
       }
     }
   }
-  flush(cur);
+}
+
+// Two consecutive layer-0 input values (elements 2p, 2p+1) of the row at
+// window position pos: position 0 is the hidden state (through
+// fast_project_in when present), position j >= 1 is fast_embeddings[c_{j-1}]
+// ("Fast-AR codebook decoding ...", section 2).  Packed as two float32 bit
+// patterns.
+template <typename WT>
+__device__ __forceinline__ u64 input_pair(const FrameArgs& a, const Lds& s, int pos, int p) {
+  if (pos == 0) {
+    if (a.has_proj) return ld64(a.xin0 + 2 * p);
+    return *reinterpret_cast<const u64*>(a.hidden + 2 * p);
+  }
+  const WT* e = reinterpret_cast<const WT*>(a.emb) + (size_t)s.codes[pos - 1] * a.dim + 2 * p;
+  const float f0 = WTraits<WT>::one(e, 0), f1 = WTraits<WT>::one(e, 1);
+  return (u64)__float_as_uint(f0) | ((u64)__float_as_uint(f1) << 32);
+}
+
+// Two consecutive weights w[2p], w[2p+1] in their storage format: one dword
+// for bf16, two for f32 (keeps the staging batches' register footprint low).
+template <typename WT> struct WPair;
+template <> struct WPair<uint16_t> {
+  using type = u32;
+  __device__ static __forceinline__ type load(const uint16_t* w, int p) {
+    return *reinterpret_cast<const u32*>(w + 2 * p);
+  }
+  __device__ static __forceinline__ float lo(type b) { return __uint_as_float(b << 16); }
+  __device__ static __forceinline__ float hi(type b) { return __uint_as_float(b & 0xFFFF0000u); }
+};
+template <> struct WPair<float> {
+  using type = u64;
+  __device__ static __forceinline__ type load(const float* w, int p) {
+    return *reinterpret_cast<const u64*>(w + 2 * p);
+  }
+  __device__ static __forceinline__ float lo(type b) { return lo_f32(b); }
+  __device__ static __forceinline__ float hi(type b) { return hi_f32(b); }
+};
+
+// Layer input x of the M new rows into LDS act rows (GEMV layout over dim
+// columns); with ADD_ACC also adds the fixed-point attention accumulator
+// (x_mid = x + attention output).
+template <typename WT, bool ADD_ACC>
+__device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds& s, int l, int step, int M,
+                                                  const WT* normw) {
+  const int hp = a.dim >> 1;
+  const int np = M * hp;
+  for (int base = 0; base < np; base += NTHREADS * SB) {
+    u64 xv[SB], a0[SB], a1[SB];
+    typename WPair<WT>::type wv[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int i = base + j * NTHREADS + threadIdx.x;
+      xv[j] = 0ull; a0[j] = 0ull; a1[j] = 0ull; wv[j] = 0;
+      if (i < hp) wv[j] = WPair<WT>::load(normw, i);   // this phase's RMSNorm weight, same round trip
+      if (i < np) {
+        const int m = i / hp, p = i - m * hp;
+        xv[j] = (l == 0) ? input_pair<WT>(a, s, row_pos(step, m), p) : ld64(xb(a, step, l - 1) + (size_t)m * a.dim + 2 * p);
+        if (ADD_ACC) {
+          const long long* ac = accb(a, step, l) + (size_t)m * a.dim + 2 * p;
+          a0[j] = ld64(ac);
+          a1[j] = ld64(ac + 1);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int i = base + j * NTHREADS + threadIdx.x;
+      if (i < np) {
+        const int m = i / hp, p = i - m * hp;
+        float v0 = lo_f32(xv[j]), v1 = hi_f32(xv[j]);
+        if (ADD_ACC) { v0 += from_fx((long long)a0[j]); v1 += from_fx((long long)a1[j]); }
+        float* d = s.act + (size_t)m * a.kmax + phys<WT>(2 * p, a.dim);
+        d[0] = v0; d[1] = v1;
+      }
+      if (i < hp) { s.nw[2 * i] = WPair<WT>::lo(wv[j]); s.nw[2 * i + 1] = WPair<WT>::hi(wv[j]); }
+    }
+  }
+}
+
+// --------------------------------------------------------------- GEMV
+// A "chunk" is 64 consecutive 16-byte segments of one weight row (one load
+// per lane, 1 KB per wave).  A block's GEMV covers virtual rows [0, nrows)
+// of up to two matrices with the same column range (rows < nr_a from
+// matrix a, the rest from matrix b: w1 and w3 of the SwiGLU run as one
+// GEMV).  Each wave takes a contiguous range of the block's chunks and
+// leaves per-(row, wave, m) partial sums in red, which the caller zeroes
+// beforehand and reduces in wave order.
+//
+// Weight loads are issued with inline assembly into a ring of RING register
+// slots and retired with explicit s_waitcnt vmcnt(RING-1): RING-1 chunks stay
+// in flight while one is consumed.  vmcnt retires in issue order, so any
+// other memory operation issued in between only makes these waits stricter.
+// The compiler does not see the loads; from issue to the wait that retires
+// it each slot is kept live by an asm operand tie, and a GEMV body ends with
+// vmcnt(0).  Every issue step loads exactly one 16-byte value per lane (a
+// valid dummy address past the wave's range), so the fixed count is exact.
+//
+// The first RING-1 loads of a phase (its "prologue") are issued at the end
+// of the previous phase, before the grid sync, which therefore waits only
+// for vmcnt(RING-1): the block's output stores are done while the next
+// phase's weights are already streaming in.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int RING = GEMV_RING;
+
+__device__ __forceinline__ void asm_load16(u32x4& d, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(d) : "v"(p));
+}
+
+struct Plan {
+  const char* base_a;   // block's first row in matrix a (bytes)
+  const char* base_b;   // block's first row in matrix b
+  const char* dummy;    // always-valid address for loads past the range
+  long long row_bytes;
+  int nr_a, nrows, K, S, C, t0, t1;
+  int it, ir, ic;       // issue cursor
+  const char* irow;
+};
+
+template <typename WT>
+__device__ __forceinline__ Plan make_plan(const WT* Wa, const WT* Wb, long long ldw, int col0, int K, int row0,
+                                          int nr_a, int nrows) {
+  constexpr int EPL = WTraits<WT>::EPL;
+  Plan p;
+  p.row_bytes = ldw * (long long)sizeof(WT);
+  p.base_a = reinterpret_cast<const char*>(Wa + (long long)row0 * ldw + col0);
+  p.base_b = Wb ? reinterpret_cast<const char*>(Wb + (long long)row0 * ldw + col0) : p.base_a;
+  p.dummy = reinterpret_cast<const char*>(Wa);
+  p.nr_a = nr_a;
+  p.nrows = nrows;
+  p.K = K;
+  p.S = K / EPL;
+  p.C = (p.S + 63) >> 6;
+  const int T = nrows * p.C;
+  const int wave = threadIdx.x >> 6;
+  p.t0 = (int)(((long long)T * wave) / NWAVE);
+  p.t1 = (int)(((long long)T * (wave + 1)) / NWAVE);
+  p.it = p.t0;
+  p.ir = p.C ? p.t0 / p.C : 0;
+  p.ic = p.t0 - p.ir * p.C;
+  p.irow = (p.ir < nr_a) ? p.base_a + (long long)p.ir * p.row_bytes : p.base_b + (long long)(p.ir - nr_a) * p.row_bytes;
+  return p;
+}
+
+__device__ __forceinline__ Plan null_plan(const void* W) {
+  Plan p;
+  p.base_a = p.base_b = p.dummy = p.irow = reinterpret_cast<const char*>(W);
+  p.row_bytes = 0;
+  p.nr_a = p.nrows = p.K = p.S = p.C = p.t0 = p.t1 = p.it = p.ir = p.ic = 0;
+  return p;
+}
+
+__device__ __forceinline__ void plan_issue(Plan& p, u32x4& d) {
+  const int lane = threadIdx.x & 63;
+  const char* addr = p.dummy;
+  if (p.it < p.t1) {
+    const int seg = p.ic * 64 + lane;
+    addr = (seg < p.S) ? p.irow + (long long)seg * 16 : p.irow;
+    ++p.it;
+    if (++p.ic == p.C) {
+      p.ic = 0;
+      ++p.ir;
+      p.irow = (p.ir < p.nr_a) ? p.base_a + (long long)p.ir * p.row_bytes
+                               : p.base_b + (long long)(p.ir - p.nr_a) * p.row_bytes;
+    }
+  }
+  asm_load16(d, addr);
+}
+
+__device__ __forceinline__ void gemv_prologue(Plan& p, u32x4 (&slot)[RING]) {
+#pragma unroll
+  for (int j = 0; j < RING - 1; ++j) plan_issue(p, slot[j]);
+}
+
+// Body: consume the wave's chunks against M activation rows in LDS (GEMV
+// layout, row stride act_ld).
+template <typename WT>
+__device__ __forceinline__ void gemv_body(Plan& p, u32x4 (&slot)[RING], const float* act, int act_ld, int M,
+                                          float* red) {
+  constexpr int EPL = WTraits<WT>::EPL;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = p.t0, t1 = p.t1;
+  if (t0 < t1) {
+    const int C = p.C, S = p.S, Kh = p.K >> 1;
+    int cr = t0 / C, cc = t0 - cr * C;
+    float acc[MMAX];
+#pragma unroll
+    for (int m = 0; m < MMAX; ++m) acc[m] = 0.0f;
+    auto flush = [&](int r) {
+#pragma unroll
+      for (int m = 0; m < MMAX; ++m) {
+        if (m < M) {
+          float v = wave_sum(acc[m]);
+          if (lane == 0) red[((size_t)r * NWAVE + wave) * MMAX + m] = v;
+        }
+        acc[m] = 0.0f;
+      }
+    };
+    auto consume = [&](const u32x4& q) {
+      const int seg = cc * 64 + lane;
+      if (seg < S) {
+        float w[EPL];
+        WTraits<WT>::unpack(make_uint4(q.x, q.y, q.z, q.w), w);
+#pragma unroll
+        for (int m = 0; m < MMAX; ++m) {
+          if (m < M) {
+            const float* row = act + (size_t)m * act_ld;
+            const float4 x0 = *reinterpret_cast<const float4*>(row + (size_t)seg * 4);
+            float s0 = acc[m];
+            s0 = fmaf(w[0], x0.x, s0); s0 = fmaf(w[1], x0.y, s0);
+            s0 = fmaf(w[2], x0.z, s0); s0 = fmaf(w[3], x0.w, s0);
+            if (EPL == 8) {
+              const float4 x1 = *reinterpret_cast<const float4*>(row + Kh + (size_t)seg * 4);
+              s0 = fmaf(w[4 % EPL], x1.x, s0); s0 = fmaf(w[5 % EPL], x1.y, s0);
+              s0 = fmaf(w[6 % EPL], x1.z, s0); s0 = fmaf(w[7 % EPL], x1.w, s0);
+            }
+            acc[m] = s0;
+          }
+        }
+      }
+      if (++cc == C) { cc = 0; flush(cr); ++cr; }
+    };
+    for (int t = t0; t < t1; t += RING) {
+#pragma unroll
+      for (int r = 0; r < RING; ++r) {
+        plan_issue(p, slot[(r + RING - 1) % RING]);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - 1));
+        asm volatile("" : "+v"(slot[r]));
+        if (t + r < t1) consume(slot[r]);
+      }
+    }
+    if (cc != 0) flush(cr);   // the wave's range ended inside a row
+  } else {
+    // no chunks: retire the prologue's dummies like the loop would
+#pragma unroll
+    for (int r = 0; r < RING; ++r) asm volatile("" : "+v"(slot[r]));
+  }
+  asm volatile("s_waitcnt vmcnt(0)");
+#pragma unroll
+  for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
 }
 
 __device__ __forceinline__ void zero_lds(float* p, int n) {
@@ -241,10 +503,11 @@ __device__ __forceinline__ float red_sum(const float* red, int r, int m) {
   return v;
 }
 
-// RMSNorm of M rows of length K held in LDS, in place: x / sqrt(mean(x^2) + eps) * w
-// ("Model loading and GGUF", section 2.2: eps 1e-6; Mizuoto page: float32).
+// RMSNorm of M rows of K values held in LDS in GEMV layout, in place:
+// x / sqrt(mean(x^2) + eps) * w ("Model loading and GGUF", section 2.2:
+// eps 1e-6; Mizuoto page: computed in float32).
 template <typename WT>
-__device__ void rms_norm_rows(float* act, int act_ld, int M, int K, const WT* w, float eps, float* small) {
+__device__ __forceinline__ void rms_norm_rows(float* act, int act_ld, int M, int K, const float* w, float eps, float* small) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int m = 0; m < M; ++m) {
     float ss = 0.0f;
@@ -264,40 +527,37 @@ __device__ void rms_norm_rows(float* act, int act_ld, int M, int K, const WT* w,
   __syncthreads();
   for (int m = 0; m < M; ++m) {
     const float den = small[32 + m];
-    for (int k = threadIdx.x; k < K; k += NTHREADS)
-      act[(size_t)m * act_ld + k] = act[(size_t)m * act_ld + k] / den * WTraits<WT>::one(w, k);
+    for (int k = threadIdx.x; k < K; k += NTHREADS) {
+      float* v = act + (size_t)m * act_ld + phys<WT>(k, K);
+      *v = *v / den * w[k];
+    }
   }
   __syncthreads();
 }
 
-// Layer input of new row m at window position pos, element k: position 0 is
-// the hidden state (through fast_project_in when present), position j >= 1
-// is fast_embeddings[c_{j-1}] ("Fast-AR codebook decoding ...", section 2).
+// Layer-0 input of new row m at window position pos, one element (used for
+// the few rows a block owns in the w2 phase).
 template <typename WT>
 __device__ __forceinline__ float layer0_input(const FrameArgs& a, const Lds& s, int pos, int k) {
-  if (pos == 0) return a.has_proj ? ld_coh(a.xin0 + k) : a.hidden[k];
+  if (pos == 0) return a.has_proj ? a.xin0[k] : a.hidden[k];
   const WT* e = reinterpret_cast<const WT*>(a.emb) + (size_t)s.codes[pos - 1] * a.dim;
   return WTraits<WT>::one(e, k);
 }
 
-__device__ __forceinline__ int row_pos(int step, int m) { return step == 1 ? m : step; }
-
-// one 128-wide (or narrower) head vector per wave: RMSNorm with weight w, then
-// pair RoPE at position pos; in place in LDS.
-template <typename WT>
-__device__ __forceinline__ void head_norm_rope(float* v, int hd, const WT* w, bool do_norm, float eps,
+// One head vector per wave: RMSNorm with weight w (optional), then pair RoPE
+// at position pos; in place in LDS.
+__device__ __forceinline__ void head_norm_rope(float* v, int hd, const float* w, bool do_norm, float eps,
                                                const float* rope, int ctx, int pos) {
   const int lane = threadIdx.x & 63;
-  // lane owns the pair (2*lane, 2*lane+1) when 2*lane < hd
-  const bool own = 2 * lane < hd;
+  const bool own = 2 * lane < hd;   // lane owns the pair (2*lane, 2*lane+1)
   float x0 = own ? v[2 * lane] : 0.0f;
   float x1 = own ? v[2 * lane + 1] : 0.0f;
   if (do_norm) {
     float ss = wave_sum(fmaf(x0, x0, x1 * x1));
     const float den = sqrtf(ss / (float)hd + eps);
     if (own) {
-      x0 = x0 / den * WTraits<WT>::one(w, 2 * lane);
-      x1 = x1 / den * WTraits<WT>::one(w, 2 * lane + 1);
+      x0 = x0 / den * w[2 * lane];
+      x1 = x1 / den * w[2 * lane + 1];
     }
   }
   if (own) {
@@ -308,73 +568,172 @@ __device__ __forceinline__ void head_norm_rope(float* v, int hd, const WT* w, bo
   }
 }
 
-// --------------------------------------------------------------- phases
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// x_mid of one element (the rows a block owns in the w2 phase)
 template <typename WT>
-__device__ void phase_qkv(const FrameArgs& a, const Lds& s, int l, int step, int M) {
-  const int D = a.dim;
-  for (int m = 0; m < M; ++m) {
-    const int pos = row_pos(step, m);
-    for (int k = threadIdx.x; k < D; k += NTHREADS)
-      s.act[(size_t)m * a.kmax + k] = (l == 0) ? layer0_input<WT>(a, s, pos, k) : ld_coh(a.x + (size_t)m * D + k);
+__device__ __forceinline__ float x_mid_of(const FrameArgs& a, const Lds& s, int l, int step, int m, int k) {
+  const float xin = (l == 0) ? layer0_input<WT>(a, s, row_pos(step, m), k) : xb(a, step, l - 1)[(size_t)m * a.dim + k];
+  return xin + from_fx(accb(a, step, l)[(size_t)m * a.dim + k]);
+}
+
+// --------------------------------------------------------------- phases
+enum PhaseKind { PH_PROJ = 0, PH_QKV, PH_WO, PH_FFN_UP, PH_FFN_DOWN, PH_HEAD };
+
+struct PhaseId { int step, layer, kind; };
+
+__device__ __forceinline__ PhaseId phase_id(const FrameArgs& a, int ph) {
+  PhaseId id;
+  if (a.has_proj) {
+    if (ph == 0) { id.step = 0; id.layer = 0; id.kind = PH_PROJ; return id; }
+    --ph;
   }
+  const int per = 4 * a.n_layer + 1;
+  id.step = 1 + ph / per;
+  const int r = ph % per;
+  if (r == 4 * a.n_layer) { id.layer = 0; id.kind = PH_HEAD; }
+  else { id.layer = r >> 2; id.kind = PH_QKV + (r & 3); }
+  return id;
+}
+
+__device__ __forceinline__ int phase_count(const FrameArgs& a) {
+  return (a.has_proj ? 1 : 0) + (a.ncb - 1) * (4 * a.n_layer + 1);
+}
+
+// rows of the wo phase: KV group g of this block and its share of the rows
+__device__ __forceinline__ void wo_rows(const FrameArgs& a, int& g, int& r0, int& r1) {
+  const int P = gridDim.x;
+  g = blockIdx.x % a.n_kv;
+  const int rg = blockIdx.x / a.n_kv;
+  const int Pg = (P - g + a.n_kv - 1) / a.n_kv;
+  split_rows(a.dim, rg, Pg, r0, r1);
+}
+
+template <typename WT>
+__device__ __forceinline__ Plan plan_for(const FrameArgs& a, int ph) {
+  const PhaseId id = phase_id(a, ph);
+  const int P = gridDim.x, b = blockIdx.x;
   int r0, r1;
-  split_rows(a.qkv_dim, blockIdx.x, gridDim.x, r0, r1);
-  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
-  __syncthreads();
-  rms_norm_rows<WT>(s.act, a.kmax, M, D, reinterpret_cast<const WT*>(a.L[l].attn_norm), a.eps, s.small);
-  gemv<WT>(reinterpret_cast<const WT*>(a.L[l].wqkv), D, 0, D, r0, r1 - r0, s.act, a.kmax, M, s.red);
-  __syncthreads();
-  for (int i = threadIdx.x; i < (r1 - r0) * M; i += NTHREADS) {
-    const int r = i / M, m = i % M;
-    st_coh(a.qkv + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m));
+  const LayerPtr& L = a.L[id.layer];
+  switch (id.kind) {
+    case PH_PROJ:
+      split_rows(a.dim, b, P, r0, r1);
+      return make_plan<WT>((const WT*)a.proj, nullptr, a.in_dim, 0, a.in_dim, r0, r1 - r0, r1 - r0);
+    case PH_QKV:
+      split_rows(a.qkv_dim, b, P, r0, r1);
+      return make_plan<WT>((const WT*)L.wqkv, nullptr, a.dim, 0, a.dim, r0, r1 - r0, r1 - r0);
+    case PH_WO: {
+      int g;
+      wo_rows(a, g, r0, r1);
+      return make_plan<WT>((const WT*)L.wo, nullptr, a.attn_dim, g * a.gw, a.gw, r0, r1 - r0, r1 - r0);
+    }
+    case PH_FFN_UP:
+      split_rows(a.ffn, b, P, r0, r1);
+      return make_plan<WT>((const WT*)L.w1, (const WT*)L.w3, a.dim, 0, a.dim, r0, r1 - r0, 2 * (r1 - r0));
+    case PH_FFN_DOWN:
+      split_rows(a.dim, b, P, r0, r1);
+      return make_plan<WT>((const WT*)L.w2, nullptr, a.ffn, 0, a.ffn, r0, r1 - r0, r1 - r0);
+    default:
+      split_rows(a.V, b, P, r0, r1);
+      return make_plan<WT>((const WT*)a.outw, nullptr, a.dim, 0, a.dim, r0, r1 - r0, r1 - r0);
   }
 }
 
 template <typename WT>
-__device__ void phase_attn_wo(const FrameArgs& a, const Lds& s, int l, int step, int M) {
-  const int P = gridDim.x;
-  const int g = blockIdx.x % a.n_kv;              // KV group of this block
-  const int rg = blockIdx.x / a.n_kv;             // rank inside the group
-  const int Pg = (P - g + a.n_kv - 1) / a.n_kv;   // blocks in the group
+__device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl,
+                                          u32x4 (&slot)[RING]) {
+  const int D = a.dim;
   int r0, r1;
-  split_rows(a.dim, rg, Pg, r0, r1);
+  split_rows(a.qkv_dim, blockIdx.x, gridDim.x, r0, r1);
+  stage_layer_input<WT, false>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].attn_norm));
+  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
+  __syncthreads();
+  mark(a, s.flag[1], 4);
+  rms_norm_rows<WT>(s.act, a.kmax, M, D, s.nw, a.eps, s.small);
+  mark(a, s.flag[1], 2);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
+  __syncthreads();
+  mark(a, s.flag[1], 3);
+  for (int i = threadIdx.x; i < (r1 - r0) * M; i += NTHREADS) {
+    const int r = i / M, m = i % M;
+    st_coh(qkvb(a, step, l) + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m));
+  }
+}
+
+template <typename WT>
+__device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl,
+                                              u32x4 (&slot)[RING]) {
+  int g, r0, r1;
+  wo_rows(a, g, r0, r1);
+  const int rg = blockIdx.x / a.n_kv;
   const int hd = a.hd, H = a.n_head, G = a.n_kv, gh = a.gheads;
   const int first_new = (step == 1) ? 0 : step;   // positions < first_new come from this frame's cache
-  const int last_pos = (step == 1) ? 1 : step;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const WT* qn = reinterpret_cast<const WT*>(a.L[l].q_norm);
-  const WT* kn = reinterpret_cast<const WT*>(a.L[l].k_norm);
+  const float* qn = s.qkn + (size_t)l * 2 * hd;
+  const float* kn = qn + hd;
   float* kvl = a.kv + (size_t)l * a.ctx_len * G * 2 * hd;   // [ctx][G][2][hd]
   const bool need_attn = (r1 > r0) || rg == 0;
   if (need_attn) {
-    // cached keys/values of positions < first_new
-    for (int i = threadIdx.x; i < first_new * hd; i += NTHREADS) {
-      const int j = i / hd, d = i % hd;
-      s.kc[(size_t)j * hd + d] = ld_coh(kvl + (((size_t)j * G + g) * 2 + 0) * hd + d);
-      s.vc[(size_t)j * hd + d] = ld_coh(kvl + (((size_t)j * G + g) * 2 + 1) * hd + d);
-    }
-    // new rows: raw q (the group's heads), k, v
-    for (int m = 0; m < M; ++m) {
-      const int pos = row_pos(step, m);
-      const float* src = a.qkv + (size_t)m * a.qkv_dim;
-      for (int i = threadIdx.x; i < gh * hd; i += NTHREADS)
-        s.q[(size_t)m * gh * hd + i] = ld_coh(src + (size_t)g * gh * hd + i);
-      for (int d = threadIdx.x; d < hd; d += NTHREADS) {
-        s.kc[(size_t)pos * hd + d] = ld_coh(src + (size_t)H * hd + (size_t)g * hd + d);
-        s.vc[(size_t)pos * hd + d] = ld_coh(src + (size_t)(H + G) * hd + (size_t)g * hd + d);
+    // one batched gather: cached keys/values of positions < first_new, then
+    // the new rows' raw q (this group's heads), k and v
+    {
+      const int hp = hd >> 1;
+      const int n_cache = first_new * 2 * hp;
+      const int n_row = (gh + 2) * hp;
+      const int total = n_cache + M * n_row;
+      for (int base = 0; base < total; base += NTHREADS * SB) {
+        u64 v[SB];
+        float* dst[SB];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const int i = base + j * NTHREADS + threadIdx.x;
+          v[j] = 0ull;
+          dst[j] = nullptr;
+          if (i < total) {
+            const float* src;
+            if (i < n_cache) {
+              const int jpos = i / (2 * hp), r = i - jpos * 2 * hp;     // r: pair inside [K | V]
+              const int kvsel = r / hp, pp = r - kvsel * hp;
+              src = kvl + (((size_t)jpos * G + g) * 2 + kvsel) * hd + 2 * pp;
+              dst[j] = (kvsel == 0 ? s.kc : s.vc) + (size_t)jpos * hd + 2 * pp;
+            } else {
+              const int t = i - n_cache;
+              const int m = t / n_row, r = t - m * n_row;
+              const float* row = qkvb(a, step, l) + (size_t)m * a.qkv_dim;
+              const int pos = row_pos(step, m);
+              if (r < gh * hp) {
+                src = row + (size_t)g * gh * hd + 2 * r;
+                dst[j] = s.q + (size_t)m * gh * hd + 2 * r;
+              } else if (r < (gh + 1) * hp) {
+                const int pp = r - gh * hp;
+                src = row + (size_t)H * hd + (size_t)g * hd + 2 * pp;
+                dst[j] = s.kc + (size_t)pos * hd + 2 * pp;
+              } else {
+                const int pp = r - (gh + 1) * hp;
+                src = row + (size_t)(H + G) * hd + (size_t)g * hd + 2 * pp;
+                dst[j] = s.vc + (size_t)pos * hd + 2 * pp;
+              }
+            }
+            v[j] = ld64(src);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+          if (dst[j]) { dst[j][0] = lo_f32(v[j]); dst[j][1] = hi_f32(v[j]); }
       }
     }
     __syncthreads();
+    mark(a, s.flag[1], 4);
     // q/k RMSNorm + RoPE: one wave per head vector
     const int nvec = M * gh + M;
     for (int v = wave; v < nvec; v += NWAVE) {
       if (v < M * gh) {
         const int m = v / gh;
-        head_norm_rope<WT>(s.q + (size_t)v * hd, hd, qn, a.has_qkn, a.eps, a.rope, a.ctx_len, row_pos(step, m));
+        head_norm_rope(s.q + (size_t)v * hd, hd, qn, a.has_qkn, a.eps, s.rope, a.ctx_len, row_pos(step, m));
       } else {
         const int m = v - M * gh;
         const int pos = row_pos(step, m);
-        head_norm_rope<WT>(s.kc + (size_t)pos * hd, hd, kn, a.has_qkn, a.eps, a.rope, a.ctx_len, pos);
+        head_norm_rope(s.kc + (size_t)pos * hd, hd, kn, a.has_qkn, a.eps, s.rope, a.ctx_len, pos);
       }
     }
     __syncthreads();
@@ -388,8 +747,10 @@ __device__ void phase_attn_wo(const FrameArgs& a, const Lds& s, int l, int step,
         }
       }
     }
-    // scaled dot-product attention, causal with offset 0: row at position p
-    // sees positions 0..p.  One wave per (row, head).
+    // scaled dot-product attention, causal with offset 0: the row at
+    // position p sees positions 0..p ("Fast-AR codebook decoding ...",
+    // section 3).  One wave per (row, head); the output goes to LDS in the
+    // wo GEMV layout (columns of this KV group).
     const float scale = 1.0f / sqrtf((float)hd);
     for (int pr = wave; pr < M * gh; pr += NWAVE) {
       const int m = pr / gh, hh = pr % gh;
@@ -415,102 +776,97 @@ __device__ void phase_attn_wo(const FrameArgs& a, const Lds& s, int l, int step,
         if (lane < hd) o0 = fmaf(pj, s.vc[(size_t)j * hd + lane], o0);
         if (lane + 64 < hd) o1 = fmaf(pj, s.vc[(size_t)j * hd + lane + 64], o1);
       }
-      float* o = s.act + (size_t)m * a.kmax + (size_t)hh * hd;
-      if (lane < hd) o[lane] = o0;
-      if (lane + 64 < hd) o[lane + 64] = o1;
+      float* o = s.act + (size_t)m * a.kmax;
+      if (lane < hd) o[phys<WT>(hh * hd + lane, a.gw)] = o0;
+      if (lane + 64 < hd) o[phys<WT>(hh * hd + lane + 64, a.gw)] = o1;
     }
-    (void)last_pos;
   }
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
-  // wo restricted to this group's columns [g*gw, (g+1)*gw)
-  gemv<WT>(reinterpret_cast<const WT*>(a.L[l].wo), a.attn_dim, g * a.gw, a.gw, r0, r1 - r0, s.act, a.kmax, M, s.red);
+  mark(a, s.flag[1], 2);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
+  mark(a, s.flag[1], 3);
   for (int i = threadIdx.x; i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
-    atomic_add_coh(a.acc + (size_t)m * a.dim + r0 + r, to_fx(red_sum(s.red, r, m)));
+    atomic_add_coh(accb(a, step, l) + (size_t)m * a.dim + r0 + r, to_fx(red_sum(s.red, r, m)));
   }
 }
 
 template <typename WT>
-__device__ __forceinline__ float x_mid_of(const FrameArgs& a, const Lds& s, int l, int step, int m, int k) {
-  const float xin = (l == 0) ? layer0_input<WT>(a, s, row_pos(step, m), k) : ld_coh(a.x + (size_t)m * a.dim + k);
-  return xin + from_fx(ld_coh(a.acc + (size_t)m * a.dim + k));
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-template <typename WT>
-__device__ void phase_ffn_up(const FrameArgs& a, const Lds& s, int l, int step, int M) {
+__device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl,
+                                             u32x4 (&slot)[RING]) {
   const int D = a.dim;
-  for (int m = 0; m < M; ++m)
-    for (int k = threadIdx.x; k < D; k += NTHREADS) s.act[(size_t)m * a.kmax + k] = x_mid_of<WT>(a, s, l, step, m, k);
   int r0, r1;
   split_rows(a.ffn, blockIdx.x, gridDim.x, r0, r1);
   const int nr = r1 - r0;
-  zero_lds(s.red, nr * NWAVE * MMAX);
+  stage_layer_input<WT, true>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm));
+  zero_lds(s.red, 2 * nr * NWAVE * MMAX);
   __syncthreads();
-  rms_norm_rows<WT>(s.act, a.kmax, M, D, reinterpret_cast<const WT*>(a.L[l].ffn_norm), a.eps, s.small);
-  gemv<WT>(reinterpret_cast<const WT*>(a.L[l].w1), D, 0, D, r0, nr, s.act, a.kmax, M, s.red);
+  rms_norm_rows<WT>(s.act, a.kmax, M, D, s.nw, a.eps, s.small);
+  mark(a, s.flag[1], 2);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);   // rows [0, nr): w1, [nr, 2nr): w3
   __syncthreads();
-  for (int i = threadIdx.x; i < nr * M; i += NTHREADS) s.a1[i] = red_sum(s.red, i / M, i % M);
-  __syncthreads();
-  zero_lds(s.red, nr * NWAVE * MMAX);
-  __syncthreads();
-  gemv<WT>(reinterpret_cast<const WT*>(a.L[l].w3), D, 0, D, r0, nr, s.act, a.kmax, M, s.red);
-  __syncthreads();
+  mark(a, s.flag[1], 3);
   for (int i = threadIdx.x; i < nr * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
-    st_coh(a.g + (size_t)m * a.ffn + r0 + r, silu(s.a1[i]) * red_sum(s.red, r, m));
+    st_coh(gb(a, step, l) + (size_t)m * a.ffn + r0 + r, silu(red_sum(s.red, r, m)) * red_sum(s.red, nr + r, m));
   }
 }
 
 template <typename WT>
-__device__ void phase_ffn_down(const FrameArgs& a, const Lds& s, int l, int step, int M) {
-  for (int m = 0; m < M; ++m)
-    for (int k = threadIdx.x; k < a.ffn; k += NTHREADS) s.act[(size_t)m * a.kmax + k] = ld_coh(a.g + (size_t)m * a.ffn + k);
+__device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl,
+                                               u32x4 (&slot)[RING]) {
   int r0, r1;
   split_rows(a.dim, blockIdx.x, gridDim.x, r0, r1);
+  for (int m = 0; m < M; ++m) stage_arena<WT, true>(s.act + (size_t)m * a.kmax, gb(a, step, l) + (size_t)m * a.ffn, a.ffn);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
-  gemv<WT>(reinterpret_cast<const WT*>(a.L[l].w2), a.ffn, 0, a.ffn, r0, r1 - r0, s.act, a.kmax, M, s.red);
+  mark(a, s.flag[1], 2);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
+  mark(a, s.flag[1], 3);
   for (int i = threadIdx.x; i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
     const int k = r0 + r;
     const float xm = x_mid_of<WT>(a, s, l, step, m, k);
-    st_coh(a.x + (size_t)m * a.dim + k, xm + red_sum(s.red, r, m));
-    st_coh(a.acc + (size_t)m * a.dim + k, 0ll);
+    st_coh(xb(a, step, l) + (size_t)m * a.dim + k, xm + red_sum(s.red, r, m));
+    st_coh(accb(a, step, l) + (size_t)m * a.dim + k, 0ll);   // ready for the next frame
   }
 }
 
 template <typename WT>
-__device__ void phase_head(const FrameArgs& a, const Lds& s, int step, int M) {
+__device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int step, int M, Plan& pl,
+                                           u32x4 (&slot)[RING]) {
   const int D = a.dim;
-  for (int k = threadIdx.x; k < D; k += NTHREADS) s.act[k] = ld_coh(a.x + (size_t)(M - 1) * D + k);
   int r0, r1;
   split_rows(a.V, blockIdx.x, gridDim.x, r0, r1);
+  stage_arena<WT, true>(s.act, xb(a, step, a.n_layer - 1) + (size_t)(M - 1) * D, D);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
-  rms_norm_rows<WT>(s.act, a.kmax, 1, D, reinterpret_cast<const WT*>(a.fnorm), a.eps, s.small);
-  gemv<WT>(reinterpret_cast<const WT*>(a.outw), D, 0, D, r0, r1 - r0, s.act, a.kmax, 1, s.red);
+  rms_norm_rows<WT>(s.act, a.kmax, 1, D, s.fnw, a.eps, s.small);
+  mark(a, s.flag[1], 2);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
+  mark(a, s.flag[1], 3);
   for (int r = threadIdx.x; r < r1 - r0; r += NTHREADS) {
     const float v = red_sum(s.red, r, 0);
-    st_coh(a.logits + r0 + r, v);
+    st_coh(logitsb(a, step) + r0 + r, v);
     if (a.logits_out) a.logits_out[(size_t)(step - 1) * a.V + r0 + r] = v;
   }
 }
 
 template <typename WT>
-__device__ void phase_project_in(const FrameArgs& a, const Lds& s) {
-  for (int k = threadIdx.x; k < a.in_dim; k += NTHREADS) s.act[k] = a.hidden[k];
+__device__ __forceinline__ void phase_project_in(const FrameArgs& a, const Lds& s, Plan& pl, u32x4 (&slot)[RING]) {
   int r0, r1;
   split_rows(a.dim, blockIdx.x, gridDim.x, r0, r1);
+  for (int k = threadIdx.x; k < a.in_dim; k += NTHREADS) s.act[phys<WT>(k, a.in_dim)] = a.hidden[k];
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
-  gemv<WT>(reinterpret_cast<const WT*>(a.proj), a.in_dim, 0, a.in_dim, r0, r1 - r0, s.act, a.kmax, 1, s.red);
+  mark(a, s.flag[1], 2);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
+  mark(a, s.flag[1], 3);
   for (int r = threadIdx.x; r < r1 - r0; r += NTHREADS) st_coh(a.xin0 + r0 + r, red_sum(s.red, r, 0));
 }
 
@@ -518,6 +874,8 @@ template <typename WT>
 __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
   extern __shared__ float lds_base[];
   const Lds s = carve(lds_base, a);
+  // drop any L2/L1 line a previous frame left for the arena's addresses
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   u32 epoch = a.epoch0;
   const int V = a.V;
   if (threadIdx.x == 0) {
@@ -526,35 +884,64 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
     if (a.forced)
       for (int j = 1; j < a.ncb; ++j) s.codes[j] = min(max(a.forced[j], 0), V - 1);
   }
+  // per-frame constants into LDS: q/k norm weights of every layer, RoPE table
+  if (a.has_qkn) {
+    for (int i = threadIdx.x; i < a.n_layer * 2 * a.hd; i += NTHREADS) {
+      const int l = i / (2 * a.hd), r = i - l * 2 * a.hd;
+      const WT* w = reinterpret_cast<const WT*>(r < a.hd ? a.L[l].q_norm : a.L[l].k_norm);
+      s.qkn[i] = WTraits<WT>::one(w, r < a.hd ? r : r - a.hd);
+    }
+  }
+  for (int i = threadIdx.x; i < a.ctx_len * a.hd; i += NTHREADS) s.rope[i] = a.rope[i];
+  for (int i = threadIdx.x; i < a.dim; i += NTHREADS) s.fnw[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(a.fnorm), i);
   __syncthreads();
-  if (a.has_proj) {
-    phase_project_in<WT>(a, s);
-    if (!grid_sync(a, epoch, s)) return;
-  }
-  for (int step = 1; step < a.ncb; ++step) {
+  u32x4 slot[RING];
+  const int nph = phase_count(a);
+  Plan pl = plan_for<WT>(a, 0);
+  gemv_prologue(pl, slot);
+  for (int ph = 0; ph < nph; ++ph) {
+    const PhaseId id = phase_id(a, ph);
+    const int step = id.step, l = id.layer;
     const int M = (step == 1) ? 2 : 1;
-    for (int l = 0; l < a.n_layer; ++l) {
-      phase_qkv<WT>(a, s, l, step, M);
-      if (!grid_sync(a, epoch, s)) return;
-      phase_attn_wo<WT>(a, s, l, step, M);
-      if (!grid_sync(a, epoch, s)) return;
-      phase_ffn_up<WT>(a, s, l, step, M);
-      if (!grid_sync(a, epoch, s)) return;
-      phase_ffn_down<WT>(a, s, l, step, M);
-      if (!grid_sync(a, epoch, s)) return;
+    if (a.tlog && threadIdx.x == 0) s.flag[1] = (int)(epoch - a.epoch0);
+    mark(a, epoch - a.epoch0, 5);
+    switch (id.kind) {
+      case PH_PROJ: phase_project_in<WT>(a, s, pl, slot); break;
+      case PH_QKV: phase_qkv<WT>(a, s, l, step, M, pl, slot); break;
+      case PH_WO: phase_attn_wo<WT>(a, s, l, step, M, pl, slot); break;
+      case PH_FFN_UP: phase_ffn_up<WT>(a, s, l, step, M, pl, slot); break;
+      case PH_FFN_DOWN: phase_ffn_down<WT>(a, s, l, step, M, pl, slot); break;
+      default: phase_head<WT>(a, s, step, M, pl, slot); break;
     }
-    phase_head<WT>(a, s, step, M);
-    if (a.forced) continue;            // teacher forcing: the next prefix is known
-    if (!grid_sync(a, epoch, s)) return;
-    for (int v = threadIdx.x; v < V; v += NTHREADS) s.act[v] = ld_coh(a.logits + v);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const int code = sample_wave(s.act, V, a.temp[0], a.top_p[0], a.top_k[0], a.uniforms[step - 1],
-                                   s.cval, s.cidx, s.mark);
-      if (threadIdx.x == 0) s.codes[step] = min(max(code, 0), V - 1);
+    // start streaming the next phase's weights before meeting the grid; the
+    // compiler barrier keeps this phase's output stores ahead of those loads,
+    // which is what the sync's vmcnt(RING-1) relies on
+    pl = (ph + 1 < nph) ? plan_for<WT>(a, ph + 1) : null_plan(a.outw);
+    asm volatile("" ::: "memory");
+    gemv_prologue(pl, slot);
+    if (id.kind == PH_HEAD && a.forced) continue;   // teacher forcing: the next prefix is known
+    if (!grid_sync(a, epoch, s)) {
+      asm volatile("s_waitcnt vmcnt(0)");
+#pragma unroll
+      for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
+      return;
     }
-    __syncthreads();
+    if (id.kind == PH_HEAD) {
+      stage_arena<WT, false>(s.act, logitsb(a, step), V & ~1);
+      if ((V & 1) && threadIdx.x == 0) s.act[V - 1] = logitsb(a, step)[V - 1];
+      __syncthreads();
+      if (threadIdx.x < 64) {
+        const int code = sample_wave(s.act, V, a.temp[0], a.top_p[0], a.top_k[0], a.uniforms[step - 1],
+                                     s.cval, s.cidx, s.mark);
+        if (threadIdx.x == 0) s.codes[step] = min(max(code, 0), V - 1);
+      }
+      __syncthreads();
+    }
   }
+  // the final prologue only loaded dummies
+  asm volatile("s_waitcnt vmcnt(0)");
+#pragma unroll
+  for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
   if (blockIdx.x == 0 && a.codes_out && threadIdx.x < a.ncb) a.codes_out[threadIdx.x] = s.codes[threadIdx.x];
 }
 
@@ -583,6 +970,7 @@ struct s2fast_ctx {
   int ncu = 0;
   size_t lds_bytes = 0;
   int kmax = 0, rmax = 0;
+  long long x_slot = 0, qkv_slot = 0, acc_slot = 0, g_slot = 0, logits_slot = 0;
   float* rope = nullptr;
   float* xin0 = nullptr;
   float* x = nullptr;
@@ -593,6 +981,8 @@ struct s2fast_ctx {
   float* logits = nullptr;
   u32* flags = nullptr;
   u32* err = nullptr;
+  u32* tlog = nullptr;     // allocated on first s2fast_test_timeline call
+  bool tlog_on = false;
   u32 epoch = 0;
 };
 
@@ -627,7 +1017,7 @@ int syncs_for(const s2fast_config& c, bool forced) {
 
 void free_ctx(s2fast_ctx* c) {
   if (!c) return;
-  void* ptrs[] = {c->rope, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err};
+  void* ptrs[] = {c->rope, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -673,7 +1063,10 @@ void fill_shape(const s2fast_ctx* c, FrameArgs& fa) {
   }
   fa.rope = c->rope;
   fa.xin0 = c->xin0; fa.x = c->x; fa.qkv = c->qkv; fa.acc = c->acc; fa.g = c->g; fa.kv = c->kv;
+  fa.x_slot = c->x_slot; fa.qkv_slot = c->qkv_slot; fa.acc_slot = c->acc_slot; fa.g_slot = c->g_slot;
+  fa.logits_slot = c->logits_slot;
   fa.logits = c->logits; fa.flags = c->flags; fa.err = c->err;
+  fa.tlog = c->tlog_on ? c->tlog : nullptr;
 }
 
 }  // namespace
@@ -756,11 +1149,13 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   const int per_group = (P + k.n_head_kv - 1) / k.n_head_kv;
   const int groups_min = P / k.n_head_kv;
   int rmax = 0;
-  for (int n : {qkv_dim, k.ffn_dim, k.dim, k.codebook_size}) rmax = std::max(rmax, (n + P - 1) / P);
+  for (int n : {qkv_dim, 2 * k.ffn_dim, k.dim, k.codebook_size}) rmax = std::max(rmax, (n + P - 1) / P);
+  rmax = std::max(rmax, 2 * ((k.ffn_dim + P - 1) / P));   // w1 and w3 rows of one block
   rmax = std::max(rmax, (k.dim + groups_min - 1) / std::max(groups_min, 1));
   (void)per_group;
   c->rmax = rmax + 1;
-  size_t lds = lds_floats(c->kmax, c->rmax, gheads, k.head_dim, k.context, k.codebook_size) * sizeof(float);
+  size_t lds = lds_floats(c->kmax, c->rmax, gheads, k.head_dim, k.context, k.codebook_size, k.dim, k.n_layer) *
+               sizeof(float);
   // more than half of the CU's 160 KB: exactly one block per CU
   const size_t one_per_cu = 84 * 1024;
   if (lds < one_per_cu) lds = one_per_cu;
@@ -778,15 +1173,25 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   const int half = k.head_dim / 2;
   std::vector<float> rope((size_t)2 * k.context * half);
   rope_table_host(k.head_dim, k.context, k.rope_base, rope.data(), rope.data() + (size_t)k.context * half);
-  bool ok = dalloc(&c->rope, rope.size()) == hipSuccess && dalloc(&c->xin0, (size_t)k.dim) == hipSuccess &&
-            dalloc(&c->x, (size_t)MMAX * k.dim) == hipSuccess && dalloc(&c->qkv, (size_t)MMAX * qkv_dim) == hipSuccess &&
-            dalloc(&c->acc, (size_t)MMAX * k.dim) == hipSuccess && dalloc(&c->g, (size_t)MMAX * k.ffn_dim) == hipSuccess &&
+  // frame arena: one 256-byte aligned region per (decode step, layer)
+  auto rup = [](long long n, long long q) { return (n + q - 1) / q * q; };
+  const long long slots = (long long)(k.num_codebooks - 1) * k.n_layer;
+  c->x_slot = rup((long long)MMAX * k.dim, 64);
+  c->qkv_slot = rup((long long)MMAX * qkv_dim, 64);
+  c->acc_slot = rup((long long)MMAX * k.dim, 32);
+  c->g_slot = rup((long long)MMAX * k.ffn_dim, 64);
+  c->logits_slot = rup(k.codebook_size, 64);
+  bool ok = dalloc(&c->rope, rope.size()) == hipSuccess && dalloc(&c->xin0, (size_t)rup(k.dim, 64)) == hipSuccess &&
+            dalloc(&c->x, (size_t)(slots * c->x_slot)) == hipSuccess &&
+            dalloc(&c->qkv, (size_t)(slots * c->qkv_slot)) == hipSuccess &&
+            dalloc(&c->acc, (size_t)(slots * c->acc_slot)) == hipSuccess &&
+            dalloc(&c->g, (size_t)(slots * c->g_slot)) == hipSuccess &&
             dalloc(&c->kv, (size_t)k.n_layer * k.context * k.n_head_kv * 2 * k.head_dim) == hipSuccess &&
-            dalloc(&c->logits, (size_t)k.codebook_size) == hipSuccess && dalloc(&c->flags, (size_t)P * 64) == hipSuccess &&
-            dalloc(&c->err, 64) == hipSuccess;
+            dalloc(&c->logits, (size_t)((k.num_codebooks - 1) * c->logits_slot)) == hipSuccess &&
+            dalloc(&c->flags, (size_t)P * 64) == hipSuccess && dalloc(&c->err, 64) == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
   ok = hipMemcpy(c->rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice) == hipSuccess &&
-       hipMemset(c->acc, 0, (size_t)MMAX * k.dim * sizeof(long long)) == hipSuccess &&
+       hipMemset(c->acc, 0, (size_t)(slots * c->acc_slot) * sizeof(long long)) == hipSuccess &&
        hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
        hipMemset(c->err, 0, 64 * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_HIP; }
@@ -853,6 +1258,22 @@ int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const
     fa.logits_out = logits + (size_t)b * (k.num_codebooks - 1) * k.codebook_size;
     const int rc = launch_frame(ctx, fa, st);
     if (rc != S2FAST_OK) return rc;
+  }
+  return S2FAST_OK;
+}
+
+int s2fast_test_timeline(s2fast_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  const size_t n = (size_t)ctx->ncu * TLOG_MAX * TLOG_W;
+  if (!ctx->tlog) {
+    if (hipMalloc(reinterpret_cast<void**>(&ctx->tlog), n * sizeof(u32)) != hipSuccess) return S2FAST_ERR_NOMEM;
+    if (hipMemset(ctx->tlog, 0, n * sizeof(u32)) != hipSuccess) return S2FAST_ERR_HIP;
+  }
+  ctx->tlog_on = enable != 0;
+  if (host_out) {
+    if (capacity < (int64_t)n) return S2FAST_ERR_ARG;
+    if (hipDeviceSynchronize() != hipSuccess) return S2FAST_ERR_HIP;
+    if (hipMemcpy(host_out, ctx->tlog, n * sizeof(u32), hipMemcpyDeviceToHost) != hipSuccess) return S2FAST_ERR_HIP;
   }
   return S2FAST_OK;
 }

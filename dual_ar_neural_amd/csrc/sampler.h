@@ -87,16 +87,34 @@ __device__ int sample_wave(const float* L, int V, float T, float top_p, int top_
   float sv = mv; int si = mi;
   wave_sort_desc(sv, si);
   const float t = __shfl(sv, n - 1, 64);
-  // 2. candidates: every value >= t (a superset of the top n)
+  // 2. candidates: every value >= t (a superset of the top n).  While more
+  //    than 64 values pass, raise t by bisection between t and the maximum,
+  //    keeping at least n values at or above it.
+  float t_lo = t;
+  int total = 0;
+  {
+    int cnt = 0;
+    for (int i = lane; i < V; i += 64) cnt += (L[i] >= t_lo) ? 1 : 0;
+    total = wave_sum_i(cnt);
+    float t_hi = __shfl(sv, 0, 64);          // the maximum
+    for (int round = 0; round < 32 && total > 64; ++round) {
+      const float mid = t_lo + 0.5f * (t_hi - t_lo);
+      if (!(mid > t_lo) || !(mid < t_hi)) break;   // no representable value in between
+      int c2 = 0;
+      for (int i = lane; i < V; i += 64) c2 += (L[i] >= mid) ? 1 : 0;
+      const int tot2 = wave_sum_i(c2);
+      if (tot2 >= n) { t_lo = mid; total = tot2; }
+      else t_hi = mid;
+    }
+  }
   int cnt = 0;
-  for (int i = lane; i < V; i += 64) cnt += (L[i] >= t) ? 1 : 0;
-  const int total = wave_sum_i(cnt);
+  for (int i = lane; i < V; i += 64) cnt += (L[i] >= t_lo) ? 1 : 0;
   float cv; int ci;
   if (total <= 64) {
     int off = wave_excl_scan(cnt);
     for (int i = lane; i < V; i += 64) {
       float x = L[i];
-      if (x >= t) { cval[off] = x; cidx[off] = i; ++off; }
+      if (x >= t_lo) { cval[off] = x; cidx[off] = i; ++off; }
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

@@ -175,6 +175,17 @@ int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* t
                        const float* top_p, const int32_t* top_k, const float* u, int32_t* codes,
                        void* stream);
 
+/* Timeline instrumentation (blocking; for measurement only).  enable != 0
+ * makes later launches on this context record, for every block and every
+ * grid-wide synchronisation point i < 256 of a frame, the 100 MHz wall clock
+ * when the block finished the phase before i (word 0) and when it left
+ * synchronisation i (word 1); words 2..7 hold in-phase marks (2: before the
+ * GEMV, 3: after it, 4: input staged, 5: phase start), 0 where a phase sets
+ * none.  If host_out is not NULL (HOST pointer, capacity >= n_blocks*256*8
+ * words) the device is synchronised and the last frame's record is copied
+ * out as [block][i][8].  The buffer is allocated on the first call. */
+int s2fast_test_timeline(s2fast_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity);
+
 /* Number of grid-wide synchronisation points one frame of B requests
  * takes on this context, or -1 on error (for measurement reports). */
 int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B);
