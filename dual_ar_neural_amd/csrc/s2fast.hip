@@ -91,6 +91,7 @@ constexpr int TLOG_MAX = 256;
 constexpr int TLOG_W = 8;   // per sync point: phase done, released, then in-phase marks 2..7
 constexpr int GEMV_RING = 8;   // weight chunks in flight per wave
 
+
 // ---------------------------------------------------------------- LDS map
 struct Lds {
   float* act;    // [MMAX][kmax] GEMV activations (see phys()); also the sampler's logits
@@ -100,9 +101,9 @@ struct Lds {
   float* kc;     // [ctx][hd]
   float* vc;     // [ctx][hd]
   float* sc;     // [MMAX][gheads][ctx] attention probabilities
-  float* cval;   // [64]
+  float* cval;   // [64] sampler candidates
   int* cidx;     // [64]
-  u32* mark;     // [256]
+  u32* mark;     // [256] sampler cross-wave scratch
   int* codes;    // [16]
   int* flag;     // [4]
   float* nw;     // [dim] RMSNorm weight of the current layer phase
@@ -116,7 +117,7 @@ __host__ __device__ inline size_t lds_floats(int kmax, int rmax, int gheads, int
   size_t act = (size_t)MMAX * kmax;
   if ((size_t)V > act) act = V;
   return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)MMAX * gheads * hd + 2 * (size_t)ctx * hd +
-         (size_t)MMAX * gheads * ctx + 64 + 64 + 256 + 16 + 4 + 2 * (size_t)dim + (size_t)n_layer * 2 * hd +
+         (size_t)MMAX * gheads * ctx + 2 * TOPK_MAX + 256 + 16 + 4 + 2 * (size_t)dim + (size_t)n_layer * 2 * hd +
          (size_t)ctx * hd;
 }
 
@@ -132,8 +133,8 @@ __device__ inline Lds carve(float* base, const FrameArgs& a) {
   s.kc = p; p += (size_t)a.ctx_len * a.hd;
   s.vc = p; p += (size_t)a.ctx_len * a.hd;
   s.sc = p; p += (size_t)MMAX * a.gheads * a.ctx_len;
-  s.cval = p; p += 64;
-  s.cidx = reinterpret_cast<int*>(p); p += 64;
+  s.cval = p; p += TOPK_MAX;
+  s.cidx = reinterpret_cast<int*>(p); p += TOPK_MAX;
   s.mark = reinterpret_cast<u32*>(p); p += 256;
   s.codes = reinterpret_cast<int*>(p); p += 16;
   s.flag = reinterpret_cast<int*>(p); p += 4;
@@ -158,6 +159,15 @@ __device__ __forceinline__ float* logitsb(const FrameArgs& a, int step) { return
 // plain (L2-cacheable) loads of arena data
 __device__ __forceinline__ u64 ld64(const void* p) { return *reinterpret_cast<const u64*>(p); }
 
+// The thread index through an opaque move: values derived from it are then
+// computed where they are used instead of being hoisted out of the frame's
+// phase loop, where they would stay live (and spill) across every phase.
+__device__ __forceinline__ int tidx() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
+
 // rows [r0, r1) of an n-row matrix owned by part `j` of `parts`
 __device__ __forceinline__ void split_rows(int n, int j, int parts, int& r0, int& r1) {
   r0 = (int)(((long long)n * j) / parts);
@@ -165,23 +175,21 @@ __device__ __forceinline__ void split_rows(int n, int j, int parts, int& r0, int
 }
 
 // --------------------------------------------------------------- grid sync
-// Device-wide barrier.  Every thread first waits for its own stores (vmcnt),
-// issued before the GEMV_RING-1 prologue loads of the next phase,
-// the block meets at s_barrier, then wave 0 publishes the block's epoch and
-// polls every block's flag with coherent loads.  Returns false (after
-// raising the watchdog word) if a flag does not arrive within SPIN_LIMIT
-// polls; the caller then leaves the kernel.
+// Device-wide barrier.  Every thread first waits for its own stores
+// (vmcnt(0); no weight loads are in flight here), the block meets at
+// s_barrier, then wave 0 publishes the block's epoch and polls every block's
+// flag with coherent loads.  Returns false (after raising the watchdog word)
+// if a flag does not arrive within SPIN_LIMIT polls; the caller then leaves
+// the kernel.
 __device__ __forceinline__ bool grid_sync(const FrameArgs& a, u32& epoch, const Lds& s) {
-  // vmcnt(GEMV_RING-1): everything but the next phase's prologue loads has
-  // completed, in particular this thread's output stores
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (GEMV_RING - 1));
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's output stores are done
   __syncthreads();
   const u32 idx = epoch - a.epoch0;
-  if (a.tlog && threadIdx.x == 0 && idx < TLOG_MAX)
+  if (a.tlog && tidx() == 0 && idx < TLOG_MAX)
     a.tlog[((size_t)blockIdx.x * TLOG_MAX + idx) * TLOG_W] = (u32)wall_clock64();
   ++epoch;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
+  if (tidx() < 64) {
+    const int lane = tidx();
     const int P = gridDim.x;
     if (lane == 0) st_coh(a.flags + 64 * blockIdx.x, epoch);
     u32 spins = 0;
@@ -206,7 +214,7 @@ __device__ __forceinline__ bool grid_sync(const FrameArgs& a, u32& epoch, const 
 // in-phase timeline mark (instrumented runs only): word w of the current
 // phase's record, by thread 0
 __device__ __forceinline__ void mark(const FrameArgs& a, u32 phase, int w) {
-  if (a.tlog && threadIdx.x == 0 && phase < TLOG_MAX)
+  if (a.tlog && tidx() == 0 && phase < TLOG_MAX)
     a.tlog[((size_t)blockIdx.x * TLOG_MAX + phase) * TLOG_W + w] = (u32)wall_clock64();
 }
 
@@ -237,12 +245,12 @@ __device__ __forceinline__ void stage_arena(float* dst, const float* src, int n)
     u64 v[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      const int i = base + j * NTHREADS + threadIdx.x;
+      const int i = base + j * NTHREADS + tidx();
       v[j] = i < np ? ld64(src + 2 * i) : 0ull;
     }
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      const int i = base + j * NTHREADS + threadIdx.x;
+      const int i = base + j * NTHREADS + tidx();
       if (i < np) {
         float* d = dst + (PERM ? phys<WT>(2 * i, n) : 2 * i);
         d[0] = lo_f32(v[j]);
@@ -301,7 +309,7 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
     typename WPair<WT>::type wv[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      const int i = base + j * NTHREADS + threadIdx.x;
+      const int i = base + j * NTHREADS + tidx();
       xv[j] = 0ull; a0[j] = 0ull; a1[j] = 0ull; wv[j] = 0;
       if (i < hp) wv[j] = WPair<WT>::load(normw, i);   // this phase's RMSNorm weight, same round trip
       if (i < np) {
@@ -316,7 +324,7 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
     }
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
-      const int i = base + j * NTHREADS + threadIdx.x;
+      const int i = base + j * NTHREADS + tidx();
       if (i < np) {
         const int m = i / hp, p = i - m * hp;
         float v0 = lo_f32(xv[j]), v1 = hi_f32(xv[j]);
@@ -347,10 +355,9 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
 // vmcnt(0).  Every issue step loads exactly one 16-byte value per lane (a
 // valid dummy address past the wave's range), so the fixed count is exact.
 //
-// The first RING-1 loads of a phase (its "prologue") are issued at the end
-// of the previous phase, before the grid sync, which therefore waits only
-// for vmcnt(RING-1): the block's output stores are done while the next
-// phase's weights are already streaming in.
+// The first RING-1 loads of a phase (its "prologue") are issued right after
+// the grid barrier that precedes it, so that they overlap the phase's
+// activation staging and normalisation.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int RING = GEMV_RING;
 
@@ -383,7 +390,7 @@ __device__ __forceinline__ Plan make_plan(const WT* Wa, const WT* Wb, long long 
   p.S = K / EPL;
   p.C = (p.S + 63) >> 6;
   const int T = nrows * p.C;
-  const int wave = threadIdx.x >> 6;
+  const int wave = tidx() >> 6;
   p.t0 = (int)(((long long)T * wave) / NWAVE);
   p.t1 = (int)(((long long)T * (wave + 1)) / NWAVE);
   p.it = p.t0;
@@ -402,7 +409,7 @@ __device__ __forceinline__ Plan null_plan(const void* W) {
 }
 
 __device__ __forceinline__ void plan_issue(Plan& p, u32x4& d) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tidx() & 63;
   const char* addr = p.dummy;
   if (p.it < p.t1) {
     const int seg = p.ic * 64 + lane;
@@ -429,7 +436,7 @@ template <typename WT>
 __device__ __forceinline__ void gemv_body(Plan& p, u32x4 (&slot)[RING], const float* act, int act_ld, int M,
                                           float* red) {
   constexpr int EPL = WTraits<WT>::EPL;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   const int t0 = p.t0, t1 = p.t1;
   if (t0 < t1) {
     const int C = p.C, S = p.S, Kh = p.K >> 1;
@@ -492,7 +499,7 @@ __device__ __forceinline__ void gemv_body(Plan& p, u32x4 (&slot)[RING], const fl
 }
 
 __device__ __forceinline__ void zero_lds(float* p, int n) {
-  for (int i = threadIdx.x; i < n; i += NTHREADS) p[i] = 0.0f;
+  for (int i = tidx(); i < n; i += NTHREADS) p[i] = 0.0f;
 }
 
 // sum of the per-wave partials of row r, activation row m
@@ -508,10 +515,10 @@ __device__ __forceinline__ float red_sum(const float* red, int r, int m) {
 // eps 1e-6; Mizuoto page: computed in float32).
 template <typename WT>
 __device__ __forceinline__ void rms_norm_rows(float* act, int act_ld, int M, int K, const float* w, float eps, float* small) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   for (int m = 0; m < M; ++m) {
     float ss = 0.0f;
-    for (int k = threadIdx.x; k < K; k += NTHREADS) {
+    for (int k = tidx(); k < K; k += NTHREADS) {
       float v = act[(size_t)m * act_ld + k];
       ss = fmaf(v, v, ss);
     }
@@ -519,15 +526,15 @@ __device__ __forceinline__ void rms_norm_rows(float* act, int act_ld, int M, int
     if (lane == 0) small[m * NWAVE + wave] = ss;
   }
   __syncthreads();
-  if (threadIdx.x < M) {
+  if (tidx() < M) {
     float t = 0.0f;
-    for (int w2 = 0; w2 < NWAVE; ++w2) t += small[threadIdx.x * NWAVE + w2];
-    small[32 + threadIdx.x] = sqrtf(t / (float)K + eps);
+    for (int w2 = 0; w2 < NWAVE; ++w2) t += small[tidx() * NWAVE + w2];
+    small[32 + tidx()] = sqrtf(t / (float)K + eps);
   }
   __syncthreads();
   for (int m = 0; m < M; ++m) {
     const float den = small[32 + m];
-    for (int k = threadIdx.x; k < K; k += NTHREADS) {
+    for (int k = tidx(); k < K; k += NTHREADS) {
       float* v = act + (size_t)m * act_ld + phys<WT>(k, K);
       *v = *v / den * w[k];
     }
@@ -548,7 +555,7 @@ __device__ __forceinline__ float layer0_input(const FrameArgs& a, const Lds& s, 
 // at position pos; in place in LDS.
 __device__ __forceinline__ void head_norm_rope(float* v, int hd, const float* w, bool do_norm, float eps,
                                                const float* rope, int ctx, int pos) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tidx() & 63;
   const bool own = 2 * lane < hd;   // lane owns the pair (2*lane, 2*lane+1)
   float x0 = own ? v[2 * lane] : 0.0f;
   float x1 = own ? v[2 * lane + 1] : 0.0f;
@@ -654,7 +661,7 @@ __device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int 
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  for (int i = threadIdx.x; i < (r1 - r0) * M; i += NTHREADS) {
+  for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
     st_coh(qkvb(a, step, l) + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m));
   }
@@ -668,7 +675,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
   const int rg = blockIdx.x / a.n_kv;
   const int hd = a.hd, H = a.n_head, G = a.n_kv, gh = a.gheads;
   const int first_new = (step == 1) ? 0 : step;   // positions < first_new come from this frame's cache
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
   const float* qn = s.qkn + (size_t)l * 2 * hd;
   const float* kn = qn + hd;
   float* kvl = a.kv + (size_t)l * a.ctx_len * G * 2 * hd;   // [ctx][G][2][hd]
@@ -686,7 +693,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
         float* dst[SB];
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-          const int i = base + j * NTHREADS + threadIdx.x;
+          const int i = base + j * NTHREADS + tidx();
           v[j] = 0ull;
           dst[j] = nullptr;
           if (i < total) {
@@ -724,7 +731,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
     }
     __syncthreads();
     mark(a, s.flag[1], 4);
-    // q/k RMSNorm + RoPE: one wave per head vector
+      // q/k RMSNorm + RoPE: one wave per head vector
     const int nvec = M * gh + M;
     for (int v = wave; v < nvec; v += NWAVE) {
       if (v < M * gh) {
@@ -741,7 +748,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
     if (rg == 0) {
       for (int m = 0; m < M; ++m) {
         const int pos = row_pos(step, m);
-        for (int d = threadIdx.x; d < hd; d += NTHREADS) {
+        for (int d = tidx(); d < hd; d += NTHREADS) {
           st_coh(kvl + (((size_t)pos * G + g) * 2 + 0) * hd + d, s.kc[(size_t)pos * hd + d]);
           st_coh(kvl + (((size_t)pos * G + g) * 2 + 1) * hd + d, s.vc[(size_t)pos * hd + d]);
         }
@@ -787,7 +794,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  for (int i = threadIdx.x; i < (r1 - r0) * M; i += NTHREADS) {
+  for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
     atomic_add_coh(accb(a, step, l) + (size_t)m * a.dim + r0 + r, to_fx(red_sum(s.red, r, m)));
   }
@@ -808,7 +815,7 @@ __device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, i
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);   // rows [0, nr): w1, [nr, 2nr): w3
   __syncthreads();
   mark(a, s.flag[1], 3);
-  for (int i = threadIdx.x; i < nr * M; i += NTHREADS) {
+  for (int i = tidx(); i < nr * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
     st_coh(gb(a, step, l) + (size_t)m * a.ffn + r0 + r, silu(red_sum(s.red, r, m)) * red_sum(s.red, nr + r, m));
   }
@@ -826,7 +833,7 @@ __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s,
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  for (int i = threadIdx.x; i < (r1 - r0) * M; i += NTHREADS) {
+  for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
     const int k = r0 + r;
     const float xm = x_mid_of<WT>(a, s, l, step, m, k);
@@ -849,7 +856,7 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  for (int r = threadIdx.x; r < r1 - r0; r += NTHREADS) {
+  for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
     const float v = red_sum(s.red, r, 0);
     st_coh(logitsb(a, step) + r0 + r, v);
     if (a.logits_out) a.logits_out[(size_t)(step - 1) * a.V + r0 + r] = v;
@@ -860,14 +867,14 @@ template <typename WT>
 __device__ __forceinline__ void phase_project_in(const FrameArgs& a, const Lds& s, Plan& pl, u32x4 (&slot)[RING]) {
   int r0, r1;
   split_rows(a.dim, blockIdx.x, gridDim.x, r0, r1);
-  for (int k = threadIdx.x; k < a.in_dim; k += NTHREADS) s.act[phys<WT>(k, a.in_dim)] = a.hidden[k];
+  for (int k = tidx(); k < a.in_dim; k += NTHREADS) s.act[phys<WT>(k, a.in_dim)] = a.hidden[k];
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  for (int r = threadIdx.x; r < r1 - r0; r += NTHREADS) st_coh(a.xin0 + r0 + r, red_sum(s.red, r, 0));
+  for (int r = tidx(); r < r1 - r0; r += NTHREADS) st_coh(a.xin0 + r0 + r, red_sum(s.red, r, 0));
 }
 
 template <typename WT>
@@ -878,7 +885,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   u32 epoch = a.epoch0;
   const int V = a.V;
-  if (threadIdx.x == 0) {
+  if (tidx() == 0) {
     const int c0 = a.forced ? a.forced[0] : a.sem_code[0];
     s.codes[0] = min(max(c0, 0), V - 1);     // clamp both ways (main loop, section 5.2)
     if (a.forced)
@@ -886,14 +893,14 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
   }
   // per-frame constants into LDS: q/k norm weights of every layer, RoPE table
   if (a.has_qkn) {
-    for (int i = threadIdx.x; i < a.n_layer * 2 * a.hd; i += NTHREADS) {
+    for (int i = tidx(); i < a.n_layer * 2 * a.hd; i += NTHREADS) {
       const int l = i / (2 * a.hd), r = i - l * 2 * a.hd;
       const WT* w = reinterpret_cast<const WT*>(r < a.hd ? a.L[l].q_norm : a.L[l].k_norm);
       s.qkn[i] = WTraits<WT>::one(w, r < a.hd ? r : r - a.hd);
     }
   }
-  for (int i = threadIdx.x; i < a.ctx_len * a.hd; i += NTHREADS) s.rope[i] = a.rope[i];
-  for (int i = threadIdx.x; i < a.dim; i += NTHREADS) s.fnw[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(a.fnorm), i);
+  for (int i = tidx(); i < a.ctx_len * a.hd; i += NTHREADS) s.rope[i] = a.rope[i];
+  for (int i = tidx(); i < a.dim; i += NTHREADS) s.fnw[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(a.fnorm), i);
   __syncthreads();
   u32x4 slot[RING];
   const int nph = phase_count(a);
@@ -903,7 +910,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
     const PhaseId id = phase_id(a, ph);
     const int step = id.step, l = id.layer;
     const int M = (step == 1) ? 2 : 1;
-    if (a.tlog && threadIdx.x == 0) s.flag[1] = (int)(epoch - a.epoch0);
+    if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     mark(a, epoch - a.epoch0, 5);
     switch (id.kind) {
       case PH_PROJ: phase_project_in<WT>(a, s, pl, slot); break;
@@ -913,13 +920,16 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
       case PH_FFN_DOWN: phase_ffn_down<WT>(a, s, l, step, M, pl, slot); break;
       default: phase_head<WT>(a, s, step, M, pl, slot); break;
     }
-    // start streaming the next phase's weights before meeting the grid; the
-    // compiler barrier keeps this phase's output stores ahead of those loads,
-    // which is what the sync's vmcnt(RING-1) relies on
+    // The next phase's weight loads are issued only after the grid barrier:
+    // vmcnt retires in order, so loads issued before it would hold up the
+    // barrier's flag polls and the next phase's activation loads behind a
+    // full HBM round trip (measured slower than this order).
     pl = (ph + 1 < nph) ? plan_for<WT>(a, ph + 1) : null_plan(a.outw);
     asm volatile("" ::: "memory");
-    gemv_prologue(pl, slot);
-    if (id.kind == PH_HEAD && a.forced) continue;   // teacher forcing: the next prefix is known
+    if (id.kind == PH_HEAD && a.forced) {           // teacher forcing: the next prefix is known
+      gemv_prologue(pl, slot);
+      continue;
+    }
     if (!grid_sync(a, epoch, s)) {
       asm volatile("s_waitcnt vmcnt(0)");
 #pragma unroll
@@ -927,36 +937,31 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
       return;
     }
     if (id.kind == PH_HEAD) {
-      stage_arena<WT, false>(s.act, logitsb(a, step), V & ~1);
-      if ((V & 1) && threadIdx.x == 0) s.act[V - 1] = logitsb(a, step)[V - 1];
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        const int code = sample_wave(s.act, V, a.temp[0], a.top_p[0], a.top_k[0], a.uniforms[step - 1],
-                                     s.cval, s.cidx, s.mark);
-        if (threadIdx.x == 0) s.codes[step] = min(max(code, 0), V - 1);
-      }
+      const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
+      const int code = sample_request(logitsb(a, step), V, a.temp[0], a.top_p[0], a.top_k[0],
+                                      a.uniforms[step - 1], sc);
+      if (tidx() == 0) s.codes[step] = min(max(code, 0), V - 1);
       __syncthreads();
     }
+    gemv_prologue(pl, slot);
   }
   // the final prologue only loaded dummies
   asm volatile("s_waitcnt vmcnt(0)");
 #pragma unroll
   for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
-  if (blockIdx.x == 0 && a.codes_out && threadIdx.x < a.ncb) a.codes_out[threadIdx.x] = s.codes[threadIdx.x];
+  if (blockIdx.x == 0 && a.codes_out && tidx() < a.ncb) a.codes_out[tidx()] = s.codes[tidx()];
 }
 
-__global__ void __launch_bounds__(64) sample_kernel(int V, const float* logits, const float* temp, const float* top_p,
-                                                    const int* top_k, const float* u, int* codes) {
-  extern __shared__ float lds_base[];
-  float* L = lds_base;
-  float* cval = L + V;
-  int* cidx = reinterpret_cast<int*>(cval + 64);
-  u32* mark = reinterpret_cast<u32*>(cidx + 64);
+__global__ void __launch_bounds__(NTHREADS) sample_kernel(int V, const float* logits, const float* temp,
+                                                          const float* top_p, const int* top_k, const float* u,
+                                                          int* codes) {
+  __shared__ float cval[TOPK_MAX];
+  __shared__ int cidx[TOPK_MAX];
+  __shared__ int red[2 * NWAVE * SAMP_TAU];
   const int b = blockIdx.x;
-  for (int i = threadIdx.x; i < V; i += 64) L[i] = logits[(size_t)b * V + i];
-  __syncthreads();
-  const int c = sample_wave(L, V, temp[b], top_p[b], top_k[b], u[b], cval, cidx, mark);
-  if (threadIdx.x == 0) codes[b] = c;
+  const SampScratch sc{cval, cidx, red};
+  const int c = sample_request(logits + (size_t)b * V, V, temp[b], top_p[b], top_k[b], u[b], sc);
+  if (tidx() == 0) codes[b] = c;
 }
 
 }  // namespace
@@ -1291,8 +1296,7 @@ int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* t
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return S2FAST_ERR_HIP;
   if (!is_gfx950(dev)) return S2FAST_ERR_DEVICE;
-  const size_t lds = ((size_t)V + 64 + 64 + 256) * sizeof(float);
-  hipLaunchKernelGGL(sample_kernel, dim3(B), dim3(64), lds, reinterpret_cast<hipStream_t>(stream), V, logits,
+  hipLaunchKernelGGL(sample_kernel, dim3(B), dim3(NTHREADS), 0, reinterpret_cast<hipStream_t>(stream), V, logits,
                      temperature, top_p, top_k, u, codes);
   return hipGetLastError() == hipSuccess ? S2FAST_OK : S2FAST_ERR_HIP;
 }

@@ -1,5 +1,4 @@
-// Sampler run by one wavefront: turns one request's logits (in LDS) into a
-// code.  Mizuoto "Fish Speech" engine page, "as upstream": a draw is
+// Sampler: turns one request's logits into a code.  Mizuoto "Fish Speech" engine page, "as upstream": a draw is
 // argmax(probs / -log u) and top-k is fixed at 30; the order of the steps,
 // tie rules and float formats are the reading documented with the oracle:
 //   greedy when T <= 0 (or NaN): argmax, lowest index on ties;
@@ -22,8 +21,7 @@ __device__ __forceinline__ bool key_before(float v, int i, float w, int k) {
 
 // Bitonic sort of one (value, index) pair per lane into rank order
 // (lane 0 = first).
-__device__ __forceinline__ void wave_sort_desc(float& v, int& i) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void wave_sort_desc(float& v, int& i, int lane) {
 #pragma unroll
   for (int k = 2; k <= 64; k <<= 1) {
 #pragma unroll
@@ -49,123 +47,213 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
   }
 }
 
-// Exclusive prefix sum across the wave.
-__device__ __forceinline__ int wave_excl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-  int incl = x;
+// ----------------------------------------------------------------- block
+// The whole block (NTHREADS threads) samples one request.  Thread t holds
+// logits t, t + NTHREADS, ... in registers (VPT of them, V <= VPT * NTHREADS).
+constexpr int SAMP_TAU = 16;       // thresholds per search round: lo + (hi - lo) j / 16
+constexpr int SAMP_ROUNDS = 8;     // search rounds before the exact fallback
+
+// LDS scratch: cval/cidx [TOPK_MAX] candidates, red [2][NWAVE][SAMP_TAU]
+// words for the cross-wave counts (two buffers, so one barrier per round).
+struct SampScratch {
+  float* cval;
+  int* cidx;
+  int* red;
+};
+
+__device__ __forceinline__ float wave_min_f(float v) {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  return incl - x;
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
 }
 
-// L: logits in LDS [V].  cval/cidx: LDS scratch [64]; mark: LDS scratch
-// [ceil(V/32)] words (used only when more than 64 values tie around the
-// top-k threshold).  Must be called by all 64 lanes of one wave.
-__device__ int sample_wave(const float* L, int V, float T, float top_p, int top_k, float u,
-                           float* cval, int* cidx, u32* mark) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ float readlane_f(float v, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
+// Threshold j of a search round over [lo, lo + d]; one explicit fma so that
+// the counting pass and the decision after it agree on every bit.
+__device__ __forceinline__ float samp_tau(float lo, float d, int j) {
+  return __builtin_fmaf(d, (float)j * (1.0f / SAMP_TAU), lo);
+}
+
+// Block-wide best (value desc, index asc); every thread gets the winner.
+// buf: NWAVE floats + NWAVE ints of LDS, not touched again before the next
+// barrier by any thread.
+__device__ __forceinline__ void block_best(float& v, int& i, int* buf, int tid) {
+  const int w = tid >> 6, lane = tid & 63;
+  wave_best(v, i);
+  float* bf = reinterpret_cast<float*>(buf);
+  if (lane == 0) { bf[w] = v; buf[NWAVE + w] = i; }
+  __syncthreads();
+  v = bf[0]; i = buf[NWAVE];
+#pragma unroll
+  for (int k = 1; k < NWAVE; ++k) {
+    const float ov = bf[k];
+    const int oi = buf[NWAVE + k];
+    if (key_before(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+}
+
+// Returns the sampled code in every lane of wave 0 (other waves: undefined).
+// L: the request's V logits (device memory, finite values).
+template <int VPT>
+__device__ __forceinline__ int sample_block(const float* L, int V, float T, float top_p, int top_k, float u, const SampScratch& sc) {
+  // The thread index goes through an opaque move so that nothing derived
+  // from it (sort masks, hash offsets) is hoisted out of the caller's loops,
+  // where it would stay live in registers across every other phase.
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+  const int lane = tid & 63, w = tid >> 6;
   constexpr int BIG = 0x7FFFFFFF;
-  if (!(T > 0.0f)) {
+  float x[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int i = tid + j * NTHREADS;
+    x[j] = (i < V) ? L[i] : -INFINITY;
+  }
+  int buf = 0;
+  if (!(T > 0.0f)) {                                   // greedy: argmax, lowest index on ties
     float bv = -INFINITY; int bi = BIG;
-    for (int i = lane; i < V; i += 64) {
-      float x = L[i];
-      if (key_before(x, i, bv, bi)) { bv = x; bi = i; }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int i = tid + j * NTHREADS;
+      if (i < V && key_before(x[j], i, bv, bi)) { bv = x[j]; bi = i; }
     }
-    wave_best(bv, bi);
+    block_best(bv, bi, sc.red, tid);
     return bi < V ? bi : 0;
   }
   const int n = max(1, min(top_k, min(V, TOPK_MAX)));
-  // 1. each lane's best element; the n-th best lane maximum bounds the top-n from below
-  float mv = -INFINITY; int mi = BIG;
-  for (int i = lane; i < V; i += 64) {
-    float x = L[i];
-    if (key_before(x, i, mv, mi)) { mv = x; mi = i; }
-  }
-  float sv = mv; int si = mi;
-  wave_sort_desc(sv, si);
-  const float t = __shfl(sv, n - 1, 64);
-  // 2. candidates: every value >= t (a superset of the top n).  While more
-  //    than 64 values pass, raise t by bisection between t and the maximum,
-  //    keeping at least n values at or above it.
-  float t_lo = t;
-  int total = 0;
+
+  // 1. range of the logits
+  float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+  for (int j = 0; j < VPT; ++j)
+    if (tid + j * NTHREADS < V) { mx = fmaxf(mx, x[j]); mn = fminf(mn, x[j]); }
+  mx = wave_max(mx);
+  mn = wave_min_f(mn);
   {
-    int cnt = 0;
-    for (int i = lane; i < V; i += 64) cnt += (L[i] >= t_lo) ? 1 : 0;
-    total = wave_sum_i(cnt);
-    float t_hi = __shfl(sv, 0, 64);          // the maximum
-    for (int round = 0; round < 32 && total > 64; ++round) {
-      const float mid = t_lo + 0.5f * (t_hi - t_lo);
-      if (!(mid > t_lo) || !(mid < t_hi)) break;   // no representable value in between
-      int c2 = 0;
-      for (int i = lane; i < V; i += 64) c2 += (L[i] >= mid) ? 1 : 0;
-      const int tot2 = wave_sum_i(c2);
-      if (tot2 >= n) { t_lo = mid; total = tot2; }
-      else t_hi = mid;
-    }
+    float* bf = reinterpret_cast<float*>(sc.red);
+    if (lane == 0) { bf[w] = mx; bf[NWAVE + w] = mn; }
+    __syncthreads();
+    mx = bf[0]; mn = bf[NWAVE];
+#pragma unroll
+    for (int k = 1; k < NWAVE; ++k) { mx = fmaxf(mx, bf[k]); mn = fminf(mn, bf[NWAVE + k]); }
+    buf = 1;
   }
-  int cnt = 0;
-  for (int i = lane; i < V; i += 64) cnt += (L[i] >= t_lo) ? 1 : 0;
-  float cv; int ci;
-  if (total <= 64) {
-    int off = wave_excl_scan(cnt);
-    for (int i = lane; i < V; i += 64) {
-      float x = L[i];
-      if (x >= t_lo) { cval[off] = x; cidx[off] = i; ++off; }
+
+  // 2. threshold search.  Invariant: cnt = #{x >= lo} >= n.  Each round counts
+  //    the values at or above 15 evenly spaced thresholds in [lo, hi] and
+  //    keeps the highest one that still passes n values, until at most
+  //    TOPK_MAX values pass: those are a superset of the top n.
+  float lo = mn, hi = mx;
+  int cnt = V;
+  const bool finite = __builtin_isfinite(lo) && __builtin_isfinite(hi);
+  for (int r = 0; r < SAMP_ROUNDS && finite && cnt > TOPK_MAX; ++r) {
+    const float d = hi - lo;
+    int* rb = sc.red + buf * (NWAVE * SAMP_TAU);
+#pragma unroll
+    for (int jt = 1; jt < SAMP_TAU; ++jt) {
+      const float tau = samp_tau(lo, d, jt);
+      int cj = 0;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) cj += __popcll(__ballot(x[j] >= tau));
+      if (lane == 0) rb[w * SAMP_TAU + jt] = cj;      // wave-uniform count
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    cv = lane < total ? cval[lane] : -INFINITY;
-    ci = lane < total ? cidx[lane] : BIG;
-    wave_sort_desc(cv, ci);
+    __syncthreads();
+    buf ^= 1;
+    int tot = 0;
+    if (lane < SAMP_TAU) {
+#pragma unroll
+      for (int k = 0; k < NWAVE; ++k) tot += rb[k * SAMP_TAU + lane];
+    }
+    const u64 ge = __ballot(lane >= 1 && lane < SAMP_TAU && tot >= n);
+    const int jb = ge ? 63 - __clzll((long long)ge) : 0;   // counts fall with j: ge is 1..jb
+    const float nlo = jb ? samp_tau(lo, d, jb) : lo;
+    const float nhi = (jb + 1 < SAMP_TAU) ? samp_tau(lo, d, jb + 1) : hi;
+    const int ncnt = jb ? __builtin_amdgcn_readlane(tot, jb) : cnt;
+    if (!(nlo > lo) && !(nhi < hi)) break;                 // the interval no longer shrinks
+    lo = nlo; hi = nhi; cnt = ncnt;
+  }
+
+  float cv = -INFINITY; int ci = BIG;                   // wave 0: lane j = rank j
+  if (cnt <= TOPK_MAX) {
+    // 3a. compact the cnt values >= lo into LDS, then sort them in wave 0
+    int* rb = sc.red + buf * (NWAVE * SAMP_TAU);
+    int wc = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) wc += __popcll(__ballot(x[j] >= lo));
+    if (lane == 0) rb[w] = wc;
+    __syncthreads();
+    int off = 0;
+    for (int k = 0; k < w; ++k) off += rb[k];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const u64 b = __ballot(x[j] >= lo);
+      if (x[j] >= lo) {
+        const int pos = off + (int)__builtin_amdgcn_mbcnt_hi((u32)(b >> 32), __builtin_amdgcn_mbcnt_lo((u32)b, 0u));
+        sc.cval[pos] = x[j];
+        sc.cidx[pos] = tid + j * NTHREADS;
+      }
+      off += __popcll(b);
+    }
+    __syncthreads();
+    if (w == 0) {
+      cv = lane < cnt ? sc.cval[lane] : -INFINITY;
+      ci = lane < cnt ? sc.cidx[lane] : BIG;
+      wave_sort_desc(cv, ci, lane);
+    }
   } else {
-    // many ties around the threshold: n rounds of exact selection
-    const int words = (V + 31) >> 5;
-    for (int w = lane; w < words; w += 64) mark[w] = 0u;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    cv = -INFINITY; ci = BIG;
+    // 3b. many ties around the threshold: n rounds of exact block-wide selection
+    u32 taken = 0u;
     for (int r = 0; r < n; ++r) {
       float bv = -INFINITY; int bi = BIG;
-      for (int i = lane; i < V; i += 64) {
-        if ((mark[i >> 5] >> (i & 31)) & 1u) continue;
-        float x = L[i];
-        if (key_before(x, i, bv, bi)) { bv = x; bi = i; }
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int i = tid + j * NTHREADS;
+        if (i < V && !((taken >> j) & 1u) && key_before(x[j], i, bv, bi)) { bv = x[j]; bi = i; }
       }
-      wave_best(bv, bi);
-      if (lane == r) { cv = bv; ci = bi; }
-      if (lane == 0 && bi < V) mark[bi >> 5] |= 1u << (bi & 31);
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      block_best(bv, bi, sc.red + buf * (NWAVE * SAMP_TAU), tid);
+      buf ^= 1;
+      if (w == 0 && lane == r) { cv = bv; ci = bi; }
+#pragma unroll
+      for (int j = 0; j < VPT; ++j)
+        if (tid + j * NTHREADS == bi) taken |= 1u << j;
     }
   }
-  // 3. lane j < n holds the rank-j candidate
+  if (w != 0) return 0;
+
+  // 4. lane j < n holds the rank-j candidate: tempered softmax over them
   const bool act = lane < n;
   const float z = act ? cv / T : 0.0f;
-  const float z0 = __shfl(z, 0, 64);
-  const float d = z - z0;
-  const float e = act ? (float)exp((double)d) : 0.0f;
+  const float z0 = readlane_f(z, 0);
+  const float dz = z - z0;
+  const float e = act ? (float)exp((double)dz) : 0.0f;
   float S = 0.0f;
-  for (int j = 0; j < n; ++j) S += __shfl(e, j, 64);
+  for (int j = 0; j < n; ++j) S += readlane_f(e, j);
   const float p = act ? e / S : 0.0f;
   float c = 0.0f, my_c = 0.0f;
   for (int j = 0; j < n; ++j) {
-    c += __shfl(p, j, 64);
+    c += readlane_f(p, j);
     if (lane == j) my_c = c;
   }
   const u64 ge = __ballot(act && my_c >= top_p);
   const int m = ge ? (__ffsll((long long)ge) - 1) : (n - 1);
-  // 4. exponential race over the kept ranks 0..m
+  // 5. exponential race over the kept ranks 0..m
   const u64 h = splitmix64(((u64)__float_as_uint(u) << 32) + (u64)lane);
   const double uj = ((double)(h >> 40) + 0.5) * (1.0 / 16777216.0);
   const float E = (float)(-log(uj));
   float key = (lane <= m) ? p / E : -INFINITY;
   int kl = lane;
   wave_best(key, kl);
-  return __shfl(ci, kl, 64);
+  return __builtin_amdgcn_readlane(ci, kl);
+}
+
+// Sampler entry for any V <= 2 * 8 * NTHREADS.
+__device__ __forceinline__ int sample_request(const float* L, int V, float T, float top_p, int top_k, float u,
+                                              const SampScratch& sc) {
+  if (V <= 8 * NTHREADS) return sample_block<8>(L, V, T, top_p, top_k, u, sc);
+  return sample_block<16>(L, V, T, top_p, top_k, u, sc);
 }
 
 }  // namespace s2f

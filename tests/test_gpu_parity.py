@@ -46,16 +46,23 @@ def _sampler_cases():
     for V in (4096, 256, 300, 50, 8192, 64, 2):
         for T, tp, tk in ((0.8, 0.8, 30), (1.0, 0.9, 30), (0.0, 0.8, 30), (-1.0, 0.5, 30), (0.05, 0.95, 64),
                           (3.0, 1.0, 100), (0.7, 0.0, 30), (0.9, 1e-9, 1), (1.2, 0.99, 0), (0.6, 0.7, 13)):
-            for kind in ("normal", "ties", "flat", "spiky"):
+            for kind in ("normal", "ties", "flat", "spiky", "outlier", "bf16"):
                 if kind == "normal":
                     l = rng.standard_normal(V).astype(np.float32) * rng.uniform(0.5, 4)
                 elif kind == "ties":
                     l = (np.round(rng.standard_normal(V) * 2) / 2).astype(np.float32)
                 elif kind == "flat":
                     l = np.full(V, 0.25, np.float32)
-                else:
+                elif kind == "spiky":
                     l = rng.standard_normal(V).astype(np.float32)
                     l[rng.integers(0, V, size=3)] += 8.0
+                elif kind == "outlier":      # a huge range: many threshold-search rounds
+                    l = rng.standard_normal(V).astype(np.float32)
+                    l[rng.integers(0, V)] = 1e6
+                    l[rng.integers(0, V)] = -1e6
+                else:                        # bf16-quantised logits: near-ties at every scale
+                    l = (rng.standard_normal(V) * 3).astype(np.float32)
+                    l = (l.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
                 u = np.float32((rng.integers(0, 1 << 23) + 0.5) * 2.0 ** -23)
                 cases.append((l, np.float32(T), np.float32(tp), np.int32(tk), u))
     return cases
