@@ -48,7 +48,10 @@ def algorithmic_bytes_per_frame(shape, batch: int) -> int:
 
 
 def time_frames(torch, ctx, dev_in, B, frames, warmup):
-    """Decode `warmup` then `frames` frames; returns seconds for the timed ones."""
+    """Decode `warmup` then `frames` frames on the current stream.  Returns
+    (seconds over the timed region, mean seconds per decode call): every call
+    is bracketed by its own pair of HIP events on that stream, so the second
+    figure excludes the host's gaps between launches."""
     hidden, sem, uni, temp, tp, tk, out = dev_in
     F = hidden.shape[0]
     for i in range(warmup):
@@ -56,15 +59,16 @@ def time_frames(torch, ctx, dev_in, B, frames, warmup):
         ctx.decode_frame(hidden[f], sem[f], uni[f], temp, tp, tk, codes=out[f])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(frames)]
     for i in range(frames):
         f = i % F
-        ctx.decode_frame(hidden[f], sem[f], uni[f], temp, tp, tk, codes=out[f])
-    e1.record(stream)
+        ev[i][0].record(stream)
+        ctx.decode_frame(hidden[f], sem[f], uni[f], temp, tp, tk, codes=out[f], stream=stream)
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1e3
+    total = ev[0][0].elapsed_time(ev[-1][1]) / 1e3
+    per_call = sum(a.elapsed_time(b) for a, b in ev) / 1e3 / frames
+    return total, per_call
 
 
 def upload(torch, fr):
@@ -76,13 +80,34 @@ def upload(torch, fr):
             torch.empty((F, B, 10), dtype=torch.int32, device="cuda"))
 
 
-def cpu_baseline(workload, frames: int):
+def traffic_from_profile(path: str, source_files) -> dict | None:
+    """HBM bytes per launch of the frame kernel from the committed counter
+    summary, if it was taken on the current kernel sources (else None)."""
+    import hashlib
+    import re
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for f in source_files:
+        h.update(open(f, "rb").read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec
+
+
+def cpu_baseline(workload, frames: int, host_weights):
     """The oracle as it stands, on this host: literal recompute of every
     window, float32 numpy, BLAS on all the cores the process may use."""
     from oracle import fast_ar as fa
     from synth import inputs as si
     w = workload
-    model = fa.Model.from_weights(w.shape, si.make_weights(w.shape, w.seed(0)))
+    model = fa.Model.from_weights(w.shape, host_weights)
     fr = si.make_frames(w, n_frames=frames + 1)
     fa.decode_frame(model, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
                     fr["top_p"], fr["top_k"])
@@ -124,7 +149,8 @@ def main():
     print(f"[bench] generating {w.name} weights", file=sys.stderr, flush=True)
     host = si.make_weights(shape, w.seed(0))
     dev = bd.device_weights(shape, host)
-    del host
+    if args.no_cpu_baseline:
+        del host
     ctx = bd.FastAR(shape, dev, max_batch=64)
     fr = si.make_frames(w, n_frames=min(w.frames, max(args.steps, 1)))
     dev_in = upload(torch, fr)
@@ -136,14 +162,16 @@ def main():
     torch.cuda.synchronize()
 
     print(f"[bench] timing {args.steps} frames at batch 1", file=sys.stderr, flush=True)
-    secs = time_frames(torch, ctx, dev_in, 1, args.steps, args.warmup)
+    secs, kern_s = time_frames(torch, ctx, dev_in, 1, args.steps, args.warmup)
     B = 1
     frames_per_s = B * args.steps / secs
     ms = secs * 1e3 / args.steps
-    launches = args.steps * B
-    bytes_frame = algorithmic_bytes_per_frame(shape, B)
-    kern_s = secs / launches
+    bytes_frame = algorithmic_bytes_per_frame(shape, B)   # one launch is one frame at batch 1
     achieved = bytes_frame / kern_s / 1e9
+    csrc = os.path.join(ROOT, "dual_ar_neural_amd", "csrc")
+    prof = traffic_from_profile(os.path.join(ROOT, "profiles", "frame_kernel_s2pro_b1_hbm_traffic.md"),
+                                [os.path.join(csrc, f) for f in ("s2fast.hip", "device_common.h", "sampler.h")])
+    traffic = prof["hbm_bytes_per_launch"] if prof else None
     result = {
         "metric": METRIC,
         "value": round(frames_per_s, 3),
@@ -163,7 +191,7 @@ def main():
                    "ffn": shape.ffn_dim, "codebook": shape.codebook_size, "codebooks": shape.num_codebooks,
                    "sampling": "T 0.8, top_p 0.8, top_k 30"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "frame_kernel<bf16>", "bytes_per_launch": bytes_frame,
                      "avg_launch_us": round(kern_s * 1e6, 2)},
         "syncs_per_frame": ctx.syncs_per_frame(1),
@@ -182,7 +210,7 @@ def main():
             frs = si.make_frames(ws, n_frames=nf)
             di = upload(torch, frs)
             print(f"[bench] timing {nf} frames at batch {Bs}", file=sys.stderr, flush=True)
-            sec = time_frames(torch, cs, di, Bs, nf, 1)
+            sec, _ = time_frames(torch, cs, di, Bs, nf, 1)
             fb = algorithmic_bytes_per_frame(ws.shape, Bs)
             sweep[f"b{Bs}"] = {"frames_per_s": round(Bs * nf / sec, 2), "ms_per_frame": round(sec * 1e3 / nf, 3),
                                "hbm_gbs": round(fb * nf / sec / 1e9, 1),
@@ -195,7 +223,7 @@ def main():
         result["batch_sweep"] = sweep
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_frames)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_frames, host)
     print(json.dumps(result), flush=True)
     ctx.close()
 

@@ -95,20 +95,49 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
   return r;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Wave reductions.  Within each 16-lane row, DPP moves (quad permutations,
+// then the half-row and row mirrors) combine values in registers; the four
+// row results are then read out with readlane.  Every lane of the wave must
+// be active.  Each combining step is commutative between the two lanes it
+// pairs, so all lanes of a row hold bit-identical partial results and the
+// returned value is the same in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_QUAD_1032 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+__device__ __forceinline__ float readlane_f(float v, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<DPP_QUAD_1032>(v);
+  v += dpp_f<DPP_QUAD_2301>(v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f<DPP_ROW_MIRROR>(v);
   return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+__device__ __forceinline__ float wave_min(float v) {
+  v = fminf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fminf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fminf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = fminf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  return fminf(fminf(readlane_f(v, 0), readlane_f(v, 16)), fminf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 // SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): add the golden gamma, then

@@ -89,7 +89,7 @@ struct FrameArgs {
 };
 constexpr int TLOG_MAX = 256;
 constexpr int TLOG_W = 8;   // per sync point: phase done, released, then in-phase marks 2..7
-constexpr int GEMV_RING = 8;   // weight chunks in flight per wave
+constexpr int GEMV_RING = 4;   // weight chunks in flight per wave
 
 
 // ---------------------------------------------------------------- LDS map

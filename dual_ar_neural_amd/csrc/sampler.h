@@ -61,15 +61,6 @@ struct SampScratch {
   int* red;
 };
 
-__device__ __forceinline__ float wave_min_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ __forceinline__ float readlane_f(float v, int j) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
-}
 
 // Threshold j of a search round over [lo, lo + d]; one explicit fma so that
 // the counting pass and the decision after it agree on every bit.
@@ -131,7 +122,7 @@ __device__ __forceinline__ int sample_block(const float* L, int V, float T, floa
   for (int j = 0; j < VPT; ++j)
     if (tid + j * NTHREADS < V) { mx = fmaxf(mx, x[j]); mn = fminf(mn, x[j]); }
   mx = wave_max(mx);
-  mn = wave_min_f(mn);
+  mn = wave_min(mn);
   {
     float* bf = reinterpret_cast<float*>(sc.red);
     if (lane == 0) { bf[w] = mx; bf[NWAVE + w] = mn; }

@@ -114,9 +114,19 @@ def is_norm(name: str) -> bool:
     return name.endswith("norm")
 
 
-def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+def bf16_bits_from_f32(x: np.ndarray, inplace: bool = False) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even); returns the uint16
-    bit patterns.  Inputs here are always finite."""
+    bit patterns.  Inputs here are always finite.  With inplace, x (float32,
+    contiguous) is used as scratch and destroyed."""
+    if inplace:
+        b = x.view(np.uint32)
+        t = b >> np.uint32(16)
+        t &= np.uint32(1)
+        b += t
+        del t
+        b += np.uint32(0x7FFF)
+        b >>= np.uint32(16)
+        return b.astype(np.uint16)
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
@@ -136,12 +146,13 @@ def make_weights(shape: ModelShape, seed: int) -> Dict[str, np.ndarray]:
     out: Dict[str, np.ndarray] = {}
     for name in weight_names(shape):
         shp = weight_shape(shape, name)
-        z = rng.standard_normal(size=shp, dtype=np.float32)
-        if is_norm(name):
-            w = np.float32(1.0) + np.float32(0.05) * z
-        else:
-            w = np.float32(0.02) * z
-        out[name] = bf16_bits_from_f32(w) if shape.weight_dtype == "bf16" else w.astype(np.float32)
+        w = rng.standard_normal(size=shp, dtype=np.float32)
+        if is_norm(name):            # 1 + 0.05 z, float32
+            w *= np.float32(0.05)
+            w += np.float32(1.0)
+        else:                        # 0.02 z, float32
+            w *= np.float32(0.02)
+        out[name] = bf16_bits_from_f32(w, inplace=True) if shape.weight_dtype == "bf16" else w
     return out
 
 
