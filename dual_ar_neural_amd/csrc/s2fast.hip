@@ -94,13 +94,12 @@ constexpr int GEMV_RING = 4;   // weight chunks in flight per wave
 
 // ---------------------------------------------------------------- LDS map
 struct Lds {
-  float* act;    // [MMAX][kmax] GEMV activations (see phys()); also the sampler's logits
+  float* act;    // [MMAX][kmax] GEMV activations (see phys())
   float* red;    // [rmax][NWAVE][MMAX]
   float* small;  // [64]: rms scratch, epilogue temporaries
   float* q;      // [MMAX][gheads][hd]
   float* kc;     // [ctx][hd]
   float* vc;     // [ctx][hd]
-  float* sc;     // [MMAX][gheads][ctx] attention probabilities
   float* cval;   // [64] sampler candidates
   int* cidx;     // [64]
   u32* mark;     // [256] sampler cross-wave scratch
@@ -114,17 +113,15 @@ struct Lds {
 
 __host__ __device__ inline size_t lds_floats(int kmax, int rmax, int gheads, int hd, int ctx, int V, int dim,
                                              int n_layer) {
-  size_t act = (size_t)MMAX * kmax;
-  if ((size_t)V > act) act = V;
+  const size_t act = ((size_t)MMAX * kmax + 3) & ~(size_t)3;   // keeps the regions after it 16-byte aligned
   return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)MMAX * gheads * hd + 2 * (size_t)ctx * hd +
-         (size_t)MMAX * gheads * ctx + 2 * TOPK_MAX + 256 + 16 + 4 + 2 * (size_t)dim + (size_t)n_layer * 2 * hd +
+         2 * TOPK_MAX + 256 + 16 + 4 + 2 * (size_t)dim + (size_t)n_layer * 2 * hd +
          (size_t)ctx * hd;
 }
 
 __device__ inline Lds carve(float* base, const FrameArgs& a) {
   Lds s;
-  size_t act = (size_t)MMAX * a.kmax;
-  if ((size_t)a.V > act) act = a.V;
+  const size_t act = ((size_t)MMAX * a.kmax + 3) & ~(size_t)3;
   float* p = base;
   s.act = p; p += act;
   s.red = p; p += (size_t)a.rmax * NWAVE * MMAX;
@@ -132,7 +129,6 @@ __device__ inline Lds carve(float* base, const FrameArgs& a) {
   s.q = p; p += (size_t)MMAX * a.gheads * a.hd;
   s.kc = p; p += (size_t)a.ctx_len * a.hd;
   s.vc = p; p += (size_t)a.ctx_len * a.hd;
-  s.sc = p; p += (size_t)MMAX * a.gheads * a.ctx_len;
   s.cval = p; p += TOPK_MAX;
   s.cidx = reinterpret_cast<int*>(p); p += TOPK_MAX;
   s.mark = reinterpret_cast<u32*>(p); p += 256;
@@ -557,19 +553,19 @@ __device__ __forceinline__ void head_norm_rope(float* v, int hd, const float* w,
                                                const float* rope, int ctx, int pos) {
   const int lane = tidx() & 63;
   const bool own = 2 * lane < hd;   // lane owns the pair (2*lane, 2*lane+1)
-  float x0 = own ? v[2 * lane] : 0.0f;
-  float x1 = own ? v[2 * lane + 1] : 0.0f;
+  const int pl = own ? lane : 0;    // loads stay unconditional (see the attention scores)
+  float x0 = v[2 * pl], x1 = v[2 * pl + 1];
+  const float w0 = w[2 * pl], w1 = w[2 * pl + 1];
+  const float c = rope[(size_t)pos * (hd / 2) + pl];
+  const float sn = rope[(size_t)ctx * (hd / 2) + (size_t)pos * (hd / 2) + pl];
+  if (!own) { x0 = 0.0f; x1 = 0.0f; }
   if (do_norm) {
     float ss = wave_sum(fmaf(x0, x0, x1 * x1));
     const float den = sqrtf(ss / (float)hd + eps);
-    if (own) {
-      x0 = x0 / den * w[2 * lane];
-      x1 = x1 / den * w[2 * lane + 1];
-    }
+    x0 = x0 / den * w0;
+    x1 = x1 / den * w1;
   }
   if (own) {
-    const float c = rope[(size_t)pos * (hd / 2) + lane];
-    const float sn = rope[(size_t)ctx * (hd / 2) + (size_t)pos * (hd / 2) + lane];
     v[2 * lane] = x0 * c - x1 * sn;
     v[2 * lane + 1] = x0 * sn + x1 * c;
   }
@@ -688,21 +684,24 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
       const int n_cache = first_new * 2 * hp;
       const int n_row = (gh + 2) * hp;
       const int total = n_cache + M * n_row;
+      // destinations as float offsets from s.q (q, kc and vc are carved
+      // in that order), so that the stores stay plain LDS stores
+      const int kc_off = (int)(s.kc - s.q), vc_off = (int)(s.vc - s.q);
       for (int base = 0; base < total; base += NTHREADS * SB) {
         u64 v[SB];
-        float* dst[SB];
+        int dst[SB];
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
           const int i = base + j * NTHREADS + tidx();
           v[j] = 0ull;
-          dst[j] = nullptr;
+          dst[j] = -1;
           if (i < total) {
             const float* src;
             if (i < n_cache) {
               const int jpos = i / (2 * hp), r = i - jpos * 2 * hp;     // r: pair inside [K | V]
               const int kvsel = r / hp, pp = r - kvsel * hp;
               src = kvl + (((size_t)jpos * G + g) * 2 + kvsel) * hd + 2 * pp;
-              dst[j] = (kvsel == 0 ? s.kc : s.vc) + (size_t)jpos * hd + 2 * pp;
+              dst[j] = (kvsel == 0 ? kc_off : vc_off) + jpos * hd + 2 * pp;
             } else {
               const int t = i - n_cache;
               const int m = t / n_row, r = t - m * n_row;
@@ -710,15 +709,15 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
               const int pos = row_pos(step, m);
               if (r < gh * hp) {
                 src = row + (size_t)g * gh * hd + 2 * r;
-                dst[j] = s.q + (size_t)m * gh * hd + 2 * r;
+                dst[j] = m * gh * hd + 2 * r;
               } else if (r < (gh + 1) * hp) {
                 const int pp = r - gh * hp;
                 src = row + (size_t)H * hd + (size_t)g * hd + 2 * pp;
-                dst[j] = s.kc + (size_t)pos * hd + 2 * pp;
+                dst[j] = kc_off + pos * hd + 2 * pp;
               } else {
                 const int pp = r - (gh + 1) * hp;
                 src = row + (size_t)(H + G) * hd + (size_t)g * hd + 2 * pp;
-                dst[j] = s.vc + (size_t)pos * hd + 2 * pp;
+                dst[j] = vc_off + pos * hd + 2 * pp;
               }
             }
             v[j] = ld64(src);
@@ -726,7 +725,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
         }
 #pragma unroll
         for (int j = 0; j < SB; ++j)
-          if (dst[j]) { dst[j][0] = lo_f32(v[j]); dst[j][1] = hi_f32(v[j]); }
+          if (dst[j] >= 0) { s.q[dst[j]] = lo_f32(v[j]); s.q[dst[j] + 1] = hi_f32(v[j]); }
       }
     }
     __syncthreads();
@@ -744,6 +743,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
       }
     }
     __syncthreads();
+    mark(a, s.flag[1], 6);
     // keep this step's keys/values for later steps of the frame
     if (rg == 0) {
       for (int m = 0; m < M; ++m) {
@@ -758,35 +758,61 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
     // position p sees positions 0..p ("Fast-AR codebook decoding ...",
     // section 3).  One wave per (row, head); the output goes to LDS in the
     // wo GEMV layout (columns of this KV group).
+    // Straight-line code: every LDS read is unconditional (clamped
+    // addresses) and masking is done on values, so the reads issue back to
+    // back; guarded reads would each become a branch with its own wait.
     const float scale = 1.0f / sqrtf((float)hd);
+    const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane row of the wave, lane in it
+    const int d8 = min(8 * l16, hd - 8);          // lane's 8 head dims in the score pass (hd % 8 == 0)
+    const bool dlive = 8 * l16 < hd;
     for (int pr = wave; pr < M * gh; pr += NWAVE) {
       const int m = pr / gh, hh = pr % gh;
       const int pos = row_pos(step, m);
       const float* qv = s.q + (size_t)pr * hd;
-      float* sc = s.sc + (size_t)pr * a.ctx_len;
-      const float q0 = lane < hd ? qv[lane] : 0.0f;
-      const float q1 = lane + 64 < hd ? qv[lane + 64] : 0.0f;
-      float mx = -INFINITY;
-      for (int j = 0; j <= pos; ++j) {
-        const float k0 = lane < hd ? s.kc[(size_t)j * hd + lane] : 0.0f;
-        const float k1 = lane + 64 < hd ? s.kc[(size_t)j * hd + lane + 64] : 0.0f;
-        const float dot = wave_sum(fmaf(q0, k0, q1 * k1)) * scale;
-        if (lane == 0) sc[j] = dot;
-        mx = fmaxf(mx, dot);
+      const float4 qa = *reinterpret_cast<const float4*>(qv + d8);
+      const float4 qb = *reinterpret_cast<const float4*>(qv + d8 + 4);
+      // scores: row g16 of the wave takes positions g16, g16+4, g16+8,
+      // g16+12 (context <= 16)
+      float sc4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * r + g16;
+        const float* kr = s.kc + (size_t)min(j, pos) * hd + d8;
+        const float4 ka = *reinterpret_cast<const float4*>(kr);
+        const float4 kb = *reinterpret_cast<const float4*>(kr + 4);
+        float part = qa.x * ka.x;
+        part = fmaf(qa.y, ka.y, part); part = fmaf(qa.z, ka.z, part); part = fmaf(qa.w, ka.w, part);
+        part = fmaf(qb.x, kb.x, part); part = fmaf(qb.y, kb.y, part);
+        part = fmaf(qb.z, kb.z, part); part = fmaf(qb.w, kb.w, part);
+        part = row16_sum(dlive ? part : 0.0f);
+        sc4[r] = (j <= pos) ? part * scale : -INFINITY;
       }
-      __builtin_amdgcn_wave_barrier();
-      float den = 0.0f;
-      for (int j = 0; j <= pos; ++j) den += expf(sc[j] - mx);
+      // softmax over positions 0..pos: exp(s - max) / sum
+      float mx = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
+      mx = fmaxf(fmaxf(readlane_f(mx, 0), readlane_f(mx, 16)), fmaxf(readlane_f(mx, 32), readlane_f(mx, 48)));
+      float e4[4], es = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e4[r] = expf(sc4[r] - mx);    // exp(-inf) = 0 for masked positions
+        es += e4[r];
+      }
+      const float den = (readlane_f(es, 0) + readlane_f(es, 16)) + (readlane_f(es, 32) + readlane_f(es, 48));
+      // output: lanes over head dims; all 16 positions are read, masked
+      // ones with weight 0
+      const int c0 = min(lane, hd - 1), c1 = min(lane + 64, hd - 1);
       float o0 = 0.0f, o1 = 0.0f;
-      for (int j = 0; j <= pos; ++j) {
-        const float pj = expf(sc[j] - mx) / den;
-        if (lane < hd) o0 = fmaf(pj, s.vc[(size_t)j * hd + lane], o0);
-        if (lane + 64 < hd) o1 = fmaf(pj, s.vc[(size_t)j * hd + lane + 64], o1);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float* vr = s.vc + (size_t)min(j, pos) * hd;
+        const float pj = readlane_f(e4[j >> 2], (j & 3) * 16) / den;   // 0 past pos
+        o0 = fmaf(pj, vr[c0], o0);
+        o1 = fmaf(pj, vr[c1], o1);
       }
       float* o = s.act + (size_t)m * a.kmax;
       if (lane < hd) o[phys<WT>(hh * hd + lane, a.gw)] = o0;
       if (lane + 64 < hd) o[phys<WT>(hh * hd + lane + 64, a.gw)] = o1;
     }
+    mark(a, s.flag[1], 7);
   }
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
@@ -1101,7 +1127,7 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   if (k.weight_dtype != S2FAST_BF16 && k.weight_dtype != S2FAST_F32) return S2FAST_ERR_ARG;
   if (k.n_layer < 1 || k.n_layer > S2FAST_MAX_LAYERS) return S2FAST_ERR_ARG;
   if (k.n_head < 1 || k.n_head_kv < 1 || k.n_head % k.n_head_kv != 0 || k.n_head_kv > 64) return S2FAST_ERR_ARG;
-  if (k.head_dim < 2 || k.head_dim > 128 || (k.head_dim & 1)) return S2FAST_ERR_ARG;
+  if (k.head_dim < 8 || k.head_dim > 128 || (k.head_dim % 8)) return S2FAST_ERR_ARG;
   if (k.dim < epl || k.in_dim < epl || k.ffn_dim < epl || k.dim > 16384 || k.in_dim > 16384 || k.ffn_dim > 16384)
     return S2FAST_ERR_ARG;
   if (k.dim % epl || k.in_dim % epl || k.ffn_dim % epl) return S2FAST_ERR_ARG;

@@ -62,7 +62,7 @@ typedef struct s2fast_config {
   int32_t n_layer;         /* <= S2FAST_MAX_LAYERS */
   int32_t n_head;          /* query heads */
   int32_t n_head_kv;       /* key/value heads; n_head % n_head_kv == 0 */
-  int32_t head_dim;        /* even, <= 128 */
+  int32_t head_dim;        /* multiple of 8, <= 128 */
   int32_t ffn_dim;         /* SwiGLU hidden width */
   int32_t codebook_size;   /* V: logits per call, <= 8192 */
   int32_t num_codebooks;   /* codes per frame (10): num_codebooks-1 decode steps */
@@ -111,7 +111,7 @@ typedef struct s2fast_ctx s2fast_ctx;
  * it with s2fast_destroy.  Shape limits (else S2FAST_ERR_ARG): dim, in_dim,
  * ffn_dim and the per-KV-group width (n_head/n_head_kv)*head_dim are
  * multiples of 8 (bf16) or 4 (f32) elements; dim, in_dim, ffn_dim <= 16384;
- * head_dim even and <= 128; context <= 16; 2 <= num_codebooks <= context;
+ * head_dim a multiple of 8 and <= 128; context <= 16; 2 <= num_codebooks <= context;
  * codebook_size <= 8192; n_head_kv <= 64.
  * Missing required weight pointers give S2FAST_ERR_NO_FAST_DECODER. */
 int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx** out);
@@ -180,8 +180,9 @@ int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* t
  * grid-wide synchronisation point i < 256 of a frame, the 100 MHz wall clock
  * when the block finished the phase before i (word 0) and when it left
  * synchronisation i (word 1); words 2..7 hold in-phase marks (2: before the
- * GEMV, 3: after it, 4: input staged, 5: phase start), 0 where a phase sets
- * none.  If host_out is not NULL (HOST pointer, capacity >= n_blocks*256*8
+ * GEMV, 3: after it, 4: input staged, 5: phase start, 6 and 7: after the
+ * q/k norms and after the attention scores in the attention phase), 0 where
+ * a phase sets none.  If host_out is not NULL (HOST pointer, capacity >= n_blocks*256*8
  * words) the device is synchronised and the last frame's record is copied
  * out as [block][i][8].  The buffer is allocated on the first call. */
 int s2fast_test_timeline(s2fast_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity);

@@ -89,7 +89,7 @@ def test_create_rejects_missing_fast_decoder():
 
 
 @pytest.mark.parametrize("field,value", [
-    ("head_dim", 130), ("head_dim", 63), ("n_head_kv", 3), ("dim", 2564), ("ffn_dim", 9730),
+    ("head_dim", 130), ("head_dim", 63), ("head_dim", 60), ("n_head_kv", 3), ("dim", 2564), ("ffn_dim", 9730),
     ("codebook_size", 9000), ("num_codebooks", 12), ("context", 17), ("n_layer", 9), ("n_layer", 0),
     ("max_batch", 0), ("weight_dtype", 7), ("in_dim", 2048)])
 def test_create_rejects_bad_shapes(field, value):
