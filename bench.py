@@ -132,7 +132,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch 16/64 lines")
-    ap.add_argument("--cpu-frames", type=int, default=24)
+    ap.add_argument("--cpu-frames", type=int, default=96)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decoder runs on a single MI355X; "
@@ -155,11 +155,13 @@ def main():
     fr = si.make_frames(w, n_frames=min(w.frames, max(args.steps, 1)))
     dev_in = upload(torch, fr)
 
-    # a plain device copy of known size, so counter runs can calibrate bytes
-    cal = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    # one elementwise kernel of known traffic (reads 256 MiB, writes 256 MiB),
+    # so that counter runs can calibrate their byte counts
+    cal = torch.zeros(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
     cal2 = torch.empty_like(cal)
-    cal2.copy_(cal)
+    torch.add(cal, 1.0, out=cal2)
     torch.cuda.synchronize()
+    del cal, cal2
 
     print(f"[bench] timing {args.steps} frames at batch 1", file=sys.stderr, flush=True)
     secs, kern_s = time_frames(torch, ctx, dev_in, 1, args.steps, args.warmup)

@@ -1,6 +1,7 @@
-// Sampler: turns one request's logits into a code.  Mizuoto "Fish Speech" engine page, "as upstream": a draw is
-// argmax(probs / -log u) and top-k is fixed at 30; the order of the steps,
-// tie rules and float formats are the reading documented with the oracle:
+// Sampler: turns one request's logits into a code.  Mizuoto "Fish Speech"
+// engine page, section "What matches upstream": a draw is argmax(probs /
+// -log u) and top-k is fixed at 30; the order of the steps, tie rules and
+// float formats are the reading documented with the oracle:
 //   greedy when T <= 0 (or NaN): argmax, lowest index on ties;
 //   candidates: the n = clamp(top_k, 1, min(V, 64)) largest logits ordered by
 //   (value desc, index asc); z = l / T; e_j = f32(exp(f64(z_j - z_0)));

@@ -4,7 +4,7 @@
  *
  * What it computes ("Fast-AR codebook decoding and the generation main loop",
  * s2.cpp analysis pages, sections 1-5; Mizuoto "Fish Speech" engine page,
- * "as upstream"):
+ * section "What matches upstream"):
  *   For every frame, codebook 0 is the semantic code (the Slow-AR main token
  *   minus semantic_begin, clamped into the codebook).  Then, for k = 1..9, a
  *   4-layer causal GQA transformer runs over the window
@@ -135,7 +135,7 @@ const char* s2fast_strerror(int code);
  *                        top-k set with cumulative probability >= top_p
  *   top_k       [B] i32  clamped on the device to [1, min(V, 64)]
  *   codes       [B, num_codebooks] i32 OUT  [sem_code, c_1, ..., c_9]
- * Sampler (Mizuoto page, "as upstream": argmax(probs / -log u), top-k 30):
+ * Sampler (Mizuoto page, "What matches upstream": argmax(probs / -log u), top-k 30):
  *   candidates = the top_k largest logits (value desc, index asc);
  *   z = l / T; e_j = f32(exp(f64(z_j - z_0))); p_j = e_j / sum (f32, rank
  *   order); keep ranks 0..m, m = first j with cumulative p >= top_p;
@@ -164,7 +164,7 @@ int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const
 
 /* Host-side: the RoPE table the context uses, [context, head_dim/2] cos and
  * sin as float32 holding bf16-rounded values of cos/sin(p * base^(-2i/hd))
- * (Mizuoto page, "as upstream").  cos_out / sin_out are HOST pointers. */
+ * (Mizuoto page, "What matches upstream").  cos_out / sin_out are HOST pointers. */
 int s2fast_test_rope_table(int32_t head_dim, int32_t context, float rope_base,
                            float* cos_out, float* sin_out);
 

@@ -4,7 +4,7 @@ A plain, slow, literal CPU implementation of what the Fast-AR decoder
 computes, written from the s2.cpp analysis pages ("Fast-AR codebook decoding
 and the generation main loop", sections 1-5; "Overall architecture & Dual-AR
 data flow", sections 2-3) and the Mizuoto "Fish Speech" engine page
-("as upstream": float32 RMSNorm, adjacent-pair RoPE with a bf16-rounded
+(section "What matches upstream": float32 RMSNorm, adjacent-pair RoPE with a bf16-rounded
 table, the draw argmax(probs / -log u), top-k fixed at 30).
 
 Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline``

@@ -7,7 +7,7 @@ position at a time, one head at a time, in float64, with the rotary
 embedding done as complex multiplication and attention as explicit loops
 over the visible keys.  It follows the same reading of the pages as
 ``fast_ar`` ("Fast-AR codebook decoding and the generation main loop",
-sections 1-4; Mizuoto "Fish Speech" page, "as upstream"), but shares no
+sections 1-4; Mizuoto "Fish Speech" page, section "What matches upstream"), but shares no
 code with it.  Slow: meant for the tiny and ragged shapes only.
 """
 from __future__ import annotations

@@ -69,7 +69,7 @@ class Model:
 def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis in float32: x / sqrt(mean(x^2) + eps) * w.
     ("Model loading and GGUF" section 2.2 gives eps 1e-6; the Mizuoto page,
-    "as upstream", computes it in float32.)"""
+    section "What matches upstream", computes it in float32.)"""
     x = np.asarray(x, dtype=F32)
     ms = np.mean(x * x, axis=-1, keepdims=True, dtype=F32)
     return (x / np.sqrt(ms + F32(eps))) * weight
@@ -86,7 +86,7 @@ def rope_table(head_dim: int, context: int, base: float, bf16: bool = True):
     """cos/sin table [context, head_dim/2] for positions 0..context-1.
 
     theta(p, i) = p * base^(-2i/head_dim), evaluated in float64; the Mizuoto
-    page ("as upstream") rounds the frequency table to bfloat16.  Returns
+    page (section "What matches upstream") rounds the frequency table to bfloat16.  Returns
     float32 arrays holding the (bf16-rounded) values."""
     i = np.arange(head_dim // 2, dtype=np.float64)
     inv_freq = base ** (-2.0 * i / head_dim)

@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY (see the package header).
 
-What the pages fix (Mizuoto "Fish Speech" page, "as upstream" and
-"limitations"): a draw is argmax(probs / -log(u)); top-k is fixed at 30;
+What the pages fix (Mizuoto "Fish Speech" engine page, sections
+"What matches upstream" and "Limitations"): a draw is argmax(probs / -log(u)); top-k is fixed at 30;
 temperature and top-p are per request.  The s2.cpp sampler chapter is not
 among the pages, so the order and the tie/rounding details below are this
 oracle's stated reading:
