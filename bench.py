@@ -80,10 +80,23 @@ def upload(torch, fr):
             torch.empty((F, B, 10), dtype=torch.int32, device="cuda"))
 
 
+def code_digest(source_files) -> str:
+    """sha256 of the kernel sources with comments and whitespace removed, so
+    that only code changes count as a kernel change."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in source_files:
+        text = open(f).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def traffic_from_profile(path: str, source_files) -> dict | None:
     """HBM bytes per launch of the frame kernel from the committed counter
-    summary, if it was taken on the current kernel sources (else None)."""
-    import hashlib
+    summary, if it was taken on the current kernel code (else None)."""
     import re
     try:
         text = open(path).read()
@@ -93,10 +106,7 @@ def traffic_from_profile(path: str, source_files) -> dict | None:
     if not m:
         return None
     rec = json.loads(m.group(1))
-    h = hashlib.sha256()
-    for f in source_files:
-        h.update(open(f, "rb").read())
-    if rec.get("source_sha256") != h.hexdigest():
+    if rec.get("code_sha256") != code_digest(source_files):
         return None
     return rec
 
