@@ -1,0 +1,719 @@
+// Batched frame decode: one cooperative launch decodes one frame for up to
+// BQ_MAX requests in lockstep, streaming every weight matrix once per decode
+// step for all of them.
+//
+// Per decode step the rows are the requests' new window positions (two per
+// request at step 1: positions 0 and 1; one after), M <= 2 * BQ_MAX.  Every
+// linear layer is a skinny GEMM Y[M x N] = X[M x K] W^T run on the matrix
+// cores: each workgroup owns a range of W's rows (all of K); W (bf16) is the
+// MFMA A operand, streamed from HBM with 16-byte loads; X is staged in LDS,
+// K-tile by K-tile, as the B operand split into bf16 high and low halves
+// (x = hi + lo exactly to about 2^-16 relative), so that the products keep
+// float32-level accuracy; accumulation is float32.  f32 weights use the
+// float32 MFMA with float32 X instead.
+//
+// Phases per step and layer (grid barrier after each):
+//   QKV   x_in * attention_norm -> wqkv; the RMS divides the outputs
+//   ATTN  one workgroup per (request, KV group): q/k RMSNorm, pair RoPE,
+//         causal attention over the request's window (mask offset 0)
+//   WO    x_mid = x_in + wo(attn)
+//   UP    x_mid * ffn_norm -> w1, w3; g = silu(a1) * a3
+//   DOWN  x = x_mid + w2(g)
+// then HEAD (fast_norm, untied output) and SAMPLE (workgroup b draws request
+// b's code).  ("Fast-AR codebook decoding and the generation main loop",
+// sections 2-4.)
+//
+// Included by s2fast.hip inside its anonymous namespace.
+
+constexpr int BQ_MAX = 16;               // requests per batched launch
+constexpr int MP_MAX = 2 * BQ_MAX;       // rows per decode step at most
+constexpr int XF_BYTES = 96 * 1024;      // LDS for the X operand (and the reduction)
+constexpr int TMAX = 6;                  // 16-row tiles of W per workgroup and phase
+constexpr int RED_TILES = 12;            // tiles x M-tiles the reduction buffer holds
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct BatchArgs {
+  int in_dim, dim, n_layer, n_head, n_kv, hd, ffn, V, ncb, ctx_len;
+  float eps;
+  int has_proj, has_qkn;
+  int qkv_dim, attn_dim, gheads, gw;
+  const void* proj;
+  const void* emb;
+  const void* fnorm;
+  const void* outw;
+  LayerPtr L[S2FAST_MAX_LAYERS];
+  const float* rope;        // [2][ctx_len][hd/2]
+  int Bq;                   // requests in this launch, 1..BQ_MAX
+  const float* hidden;      // [Bq][in_dim]
+  const int* sem_code;      // [Bq]
+  const float* uniforms;    // [Bq][ncb-1]
+  const float* temp;        // [Bq]
+  const float* top_p;       // [Bq]
+  const int* top_k;         // [Bq]
+  const int* forced;        // [Bq][ncb] or nullptr
+  int* codes_out;           // [Bq][ncb] or nullptr
+  float* logits_out;        // [Bq][ncb-1][V] or nullptr
+  // arena: every (step, layer) region written once per frame (see FrameArgs)
+  float* xin0;              // [BQ_MAX][dim]
+  float* x;                 // [slot][MP_MAX][dim] residual after the layer
+  float* xmid;              // [slot][MP_MAX][dim] residual after attention
+  float* qkv;               // [slot][MP_MAX][qkv_dim]
+  float* att;               // [slot][MP_MAX][attn_dim]
+  float* g;                 // [slot][MP_MAX][ffn]
+  float* logits;            // [step][BQ_MAX][V]
+  float* kv;                // [BQ_MAX][n_layer][ctx][n_kv][2][hd]
+  int* codes;               // [BQ_MAX][16] sampled codes
+  long long x_slot, qkv_slot, att_slot, g_slot, logits_slot;
+  u32* flags;
+  u32 epoch0;
+  u32* err;
+  u32* tlog;
+};
+
+struct BLds {
+  char* xf;      // XF_BYTES: X fragments; reduction buffer; attention scratch
+  float* ssp;    // [NTHREADS] per-thread sums of squares
+  float* rms;    // [MP_MAX]
+  float* qkn;    // [n_layer][2][hd]
+  float* rope;   // [2][ctx][hd/2]
+  float* cval;   // [TOPK_MAX]
+  int* cidx;     // [TOPK_MAX]
+  int* sred;     // [2 * NWAVE * SAMP_TAU]
+  int* rcode;    // [MP_MAX] embedding row of each row's layer-0 input (-1: hidden state)
+  int* flag;     // [4]
+};
+
+__host__ __device__ inline size_t b_lds_bytes(int n_layer, int hd, int ctx) {
+  return (size_t)XF_BYTES + sizeof(float) * ((size_t)NTHREADS + MP_MAX + (size_t)n_layer * 2 * hd + (size_t)ctx * hd +
+                                             TOPK_MAX) +
+         sizeof(int) * ((size_t)TOPK_MAX + 2 * NWAVE * SAMP_TAU + MP_MAX + 4);
+}
+
+__device__ inline BLds b_carve(char* base, const BatchArgs& a) {
+  BLds s;
+  char* p = base;
+  s.xf = p; p += XF_BYTES;
+  s.ssp = reinterpret_cast<float*>(p); p += sizeof(float) * NTHREADS;
+  s.rms = reinterpret_cast<float*>(p); p += sizeof(float) * MP_MAX;
+  s.qkn = reinterpret_cast<float*>(p); p += sizeof(float) * (size_t)a.n_layer * 2 * a.hd;
+  s.rope = reinterpret_cast<float*>(p); p += sizeof(float) * (size_t)a.ctx_len * a.hd;
+  s.cval = reinterpret_cast<float*>(p); p += sizeof(float) * TOPK_MAX;
+  s.cidx = reinterpret_cast<int*>(p); p += sizeof(int) * TOPK_MAX;
+  s.sred = reinterpret_cast<int*>(p); p += sizeof(int) * 2 * NWAVE * SAMP_TAU;
+  s.rcode = reinterpret_cast<int*>(p); p += sizeof(int) * MP_MAX;
+  s.flag = reinterpret_cast<int*>(p);
+  return s;
+}
+
+// rows of decode step `step`: request b's positions 0 and 1 are rows b and
+// Bq + b at step 1; position `step` is row b afterwards
+__device__ __forceinline__ int b_rows(const BatchArgs& a, int step) { return step == 1 ? 2 * a.Bq : a.Bq; }
+__device__ __forceinline__ int b_pos(const BatchArgs& a, int step, int m) { return step == 1 ? m / a.Bq : step; }
+__device__ __forceinline__ int b_last_row(const BatchArgs& a, int step, int b) { return step == 1 ? a.Bq + b : b; }
+
+__device__ __forceinline__ size_t b_slot(const BatchArgs& a, int step, int l) { return (size_t)(step - 1) * a.n_layer + l; }
+__device__ __forceinline__ float* bx(const BatchArgs& a, int step, int l) { return a.x + b_slot(a, step, l) * a.x_slot; }
+__device__ __forceinline__ float* bxmid(const BatchArgs& a, int step, int l) { return a.xmid + b_slot(a, step, l) * a.x_slot; }
+__device__ __forceinline__ float* bqkv(const BatchArgs& a, int step, int l) { return a.qkv + b_slot(a, step, l) * a.qkv_slot; }
+__device__ __forceinline__ float* batt(const BatchArgs& a, int step, int l) { return a.att + b_slot(a, step, l) * a.att_slot; }
+__device__ __forceinline__ float* bg(const BatchArgs& a, int step, int l) { return a.g + b_slot(a, step, l) * a.g_slot; }
+__device__ __forceinline__ float* blogits(const BatchArgs& a, int step) { return a.logits + (size_t)(step - 1) * a.logits_slot; }
+__device__ __forceinline__ float* bkv(const BatchArgs& a, int b, int l, int pos, int g) {
+  return a.kv + ((((size_t)b * a.n_layer + l) * a.ctx_len + pos) * a.n_kv + g) * 2 * a.hd;
+}
+
+// code c_j of request b: the (clamped) semantic code for j = 0, later the
+// teacher-forced input or the code sampled at step j
+__device__ __forceinline__ int b_code(const BatchArgs& a, int b, int j) {
+  int c;
+  if (a.forced) c = a.forced[(size_t)b * a.ncb + j];
+  else if (j == 0) c = a.sem_code[b];
+  else c = a.codes[b * 16 + j];
+  return min(max(c, 0), a.V - 1);
+}
+
+// ------------------------------------------------------------ skinny GEMM
+enum BKind { BK_PROJ = 0, BK_QKV, BK_WO, BK_UP, BK_DOWN, BK_HEAD };
+
+struct GemmDesc {
+  const char* wa;      // virtual rows v < R1: wa + v * ldb
+  const char* wb;      // virtual rows v >= R1: wb + (v - R1) * ldb
+  long long ldb;       // row stride in bytes
+  int R1, R;           // rows from wa, all rows
+  int K;               // columns
+  int M;               // rows of X (<= MP_MAX)
+  int kind, step, l;
+  const void* normw;   // RMSNorm weight over K, or nullptr
+  const char* dummy;   // always-valid address (the matrix base) for padding loads
+};
+
+template <typename WT> struct MF;
+template <> struct MF<uint16_t> {
+  static constexpr int KSZ = 32;      // K per k-step (one 16x16x32 MFMA per X half)
+  static constexpr int GE = 8;        // K per lane per k-step
+  static constexpr int FRAG = 2048;   // LDS bytes per k-step and M-tile (hi + lo)
+};
+template <> struct MF<float> {
+  static constexpr int KSZ = 16;      // four 16x16x4 MFMAs
+  static constexpr int GE = 4;
+  static constexpr int FRAG = 1024;
+};
+
+// round-to-nearest-even float -> bf16 bits, and the exact float of a bf16
+__device__ __forceinline__ u32 bf16_rne(float f) {
+  const u32 u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// GE source values of row m at column k (k a multiple of GE, in range)
+template <typename WT>
+__device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int m, int k,
+                                        float (&v)[8]) {
+  constexpr int GE = MF<WT>::GE;
+  const float* src = nullptr;
+  const WT* esrc = nullptr;
+  switch (gd.kind) {
+    case BK_PROJ: src = a.hidden + (size_t)m * a.in_dim; break;
+    case BK_QKV:
+      if (gd.l > 0) src = bx(a, gd.step, gd.l - 1) + (size_t)m * a.dim;
+      else if (s.rcode[m] < 0) src = a.has_proj ? a.xin0 + (size_t)(m % a.Bq) * a.dim : a.hidden + (size_t)(m % a.Bq) * a.in_dim;
+      else esrc = reinterpret_cast<const WT*>(a.emb) + (size_t)s.rcode[m] * a.dim;
+      break;
+    case BK_WO: src = batt(a, gd.step, gd.l) + (size_t)m * a.attn_dim; break;
+    case BK_UP: src = bxmid(a, gd.step, gd.l) + (size_t)m * a.dim; break;
+    case BK_DOWN: src = bg(a, gd.step, gd.l) + (size_t)m * a.ffn; break;
+    default: src = bx(a, gd.step, a.n_layer - 1) + (size_t)b_last_row(a, gd.step, m) * a.dim; break;
+  }
+  if (esrc) {
+    if (GE == 8) {
+      const uint4 q = *reinterpret_cast<const uint4*>(esrc + k);
+      v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+      v[4] = __uint_as_float(q.z << 16); v[5] = __uint_as_float(q.z & 0xFFFF0000u);
+      v[6] = __uint_as_float(q.w << 16); v[7] = __uint_as_float(q.w & 0xFFFF0000u);
+    } else {
+      const float4 q = *reinterpret_cast<const float4*>(esrc + k);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+  } else {
+    const float4 q0 = *reinterpret_cast<const float4*>(src + k);
+    v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+    if (GE == 8) {
+      const float4 q1 = *reinterpret_cast<const float4*>(src + k + 4);
+      v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+    }
+  }
+}
+
+// GE weights of the RMSNorm vector at column k
+template <typename WT>
+__device__ __forceinline__ void b_fetch_w(const void* w, int k, float (&v)[8]) {
+  if (MF<WT>::GE == 8) {
+    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(w) + k);
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+    v[4] = __uint_as_float(q.z << 16); v[5] = __uint_as_float(q.z & 0xFFFF0000u);
+    v[6] = __uint_as_float(q.w << 16); v[7] = __uint_as_float(q.w & 0xFFFF0000u);
+  } else {
+    const float4 q = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + k);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+}
+
+// Stage K-tile `tau` of X (columns [tau*KSM*KSZ, ...)) into LDS as MFMA B
+// fragments: lane (q, j) of k-step s and M-tile mt holds X[16 mt + j][k0 + s KSZ
+// + GE q .. + GE).  Thread t always handles row m = t % Mp, so its running sum
+// of squares (normed phases) covers one row in a fixed order.
+template <typename WT>
+__device__ __forceinline__ void b_stage(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int tau, int KSM,
+                                        int Mp, int MT, float& ss) {
+  constexpr int GE = MF<WT>::GE, KSZ = MF<WT>::KSZ;
+  constexpr int SBX = 2;                       // items in flight per thread
+  const int tid = tidx();
+  const int m = tid % Mp;
+  const int k0 = tau * KSM * KSZ;
+  const int n_items = Mp * KSM * 4;            // multiple of NTHREADS (Mp * KSM * 4 = 3072 or 6144)
+  const int lo_off = KSM * MT * 1024;          // bf16: low halves after the high halves
+  for (int base = 0; base < n_items; base += NTHREADS * SBX) {
+    float v[SBX][8], w[SBX][8];
+    bool ok[SBX];
+#pragma unroll
+    for (int j = 0; j < SBX; ++j) {
+      const int i = base + j * NTHREADS + tid;
+      const int kg = i / Mp;
+      const int k = k0 + kg * GE;
+      ok[j] = i < n_items && m < gd.M && k < gd.K;
+      if (ok[j]) {
+        b_fetch<WT>(a, s, gd, m, k, v[j]);
+        if (gd.normw) b_fetch_w<WT>(gd.normw, k, w[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SBX; ++j) {
+      const int i = base + j * NTHREADS + tid;
+      if (i >= n_items) continue;
+      const int kg = i / Mp;
+      const int sl = kg >> 2, q = kg & 3;
+      const int idx = ((sl * MT + (m >> 4)) * 64 + q * 16 + (m & 15)) * 16;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = 0.0f;
+        if (e < GE && ok[j]) {
+          if (gd.normw) { ss = fmaf(v[j][e], v[j][e], ss); x[e] = v[j][e] * w[j][e]; }
+          else x[e] = v[j][e];
+        }
+      }
+      if (GE == 8) {
+        u32 h[8], lw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          h[e] = bf16_rne(x[e]);
+          lw[e] = bf16_rne(x[e] - __uint_as_float(h[e] << 16));
+        }
+        *reinterpret_cast<uint4*>(s.xf + idx) =
+            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        *reinterpret_cast<uint4*>(s.xf + lo_off + idx) =
+            make_uint4(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16), lw[4] | (lw[5] << 16), lw[6] | (lw[7] << 16));
+      } else {
+        *reinterpret_cast<float4*>(s.xf + idx) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+    }
+  }
+}
+
+// Per-wave walk over its weight chunks: in K-tile tau the wave takes k-steps
+// ks0 + wave, ks0 + wave + 8, ... and, for each, the T row tiles; the list of
+// a tile is padded to a multiple of RING (padding issues dummy loads) so that
+// the register ring is in phase at every K-tile boundary.
+struct BIter {
+  int tau, j;
+};
+
+struct BGeom {
+  int T, KST, KSM, NT;
+  __device__ __forceinline__ int nks(int tau, int wave) const {
+    const int ks0 = tau * KSM, ks1 = min(KST, ks0 + KSM);
+    const int n = ks1 - ks0 - wave;
+    return n > 0 ? (n + NWAVE - 1) / NWAVE : 0;
+  }
+  __device__ __forceinline__ int n_real(int tau, int wave) const { return T * nks(tau, wave); }
+  __device__ __forceinline__ int n_pad(int tau, int wave) const { return (n_real(tau, wave) + RING - 1) / RING * RING; }
+};
+
+template <typename WT>
+__device__ __forceinline__ void b_issue(const GemmDesc& gd, const BGeom& G, BIter& it, int wave, int lane,
+                                        u32x4& slot) {
+  constexpr int KSZ = MF<WT>::KSZ, GE = MF<WT>::GE;
+  const char* addr = gd.dummy;
+  if (it.tau < G.NT) {
+    if (it.j < G.n_real(it.tau, wave)) {
+      const int s = it.tau * G.KSM + wave + NWAVE * (it.j / G.T);
+      const int t = it.j % G.T;
+      int v = 16 * t + (lane & 15);
+      v = min(v, gd.R - 1);
+      int col = s * KSZ + GE * (lane >> 4);
+      if (col >= gd.K) col = 0;      // past the last column: X is zero there
+      const char* row = v < gd.R1 ? gd.wa + (long long)v * gd.ldb : gd.wb + (long long)(v - gd.R1) * gd.ldb;
+      addr = row + (long long)col * sizeof(WT);
+    }
+    if (++it.j >= G.n_pad(it.tau, wave)) {
+      it.j = 0;
+      ++it.tau;
+      while (it.tau < G.NT && G.n_pad(it.tau, wave) == 0) ++it.tau;
+    }
+  }
+  asm_load16(slot, addr);
+}
+
+template <typename WT>
+__device__ __forceinline__ void b_mfma(f32x4 (&D)[TMAX][2], int t, int MT, const u32x4& w, const char* xf, int sl,
+                                       int lane, int lo_off) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    if (mt >= MT) break;
+    const int idx = ((sl * MT + mt) * 64 + lane) * 16;
+    if (sizeof(WT) == 2) {
+      const uint4 bh = *reinterpret_cast<const uint4*>(xf + idx);
+      const uint4 bl = *reinterpret_cast<const uint4*>(xf + lo_off + idx);
+      bf16x8 av, hv, lv;
+      __builtin_memcpy(&av, &w, 16);
+      __builtin_memcpy(&hv, &bh, 16);
+      __builtin_memcpy(&lv, &bl, 16);
+#pragma unroll
+      for (int tt = 0; tt < TMAX; ++tt) {
+        if (tt == t) {
+          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, D[tt][mt], 0, 0, 0);
+          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lv, D[tt][mt], 0, 0, 0);
+        }
+      }
+    } else {
+      const float4 bx = *reinterpret_cast<const float4*>(xf + idx);
+      const float a0 = __uint_as_float(w.x), a1 = __uint_as_float(w.y), a2 = __uint_as_float(w.z),
+                  a3 = __uint_as_float(w.w);
+#pragma unroll
+      for (int tt = 0; tt < TMAX; ++tt) {
+        if (tt == t) {
+          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bx.x, D[tt][mt], 0, 0, 0);
+          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bx.y, D[tt][mt], 0, 0, 0);
+          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, bx.z, D[tt][mt], 0, 0, 0);
+          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, bx.w, D[tt][mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Per-wave partial products of one GEMM phase, summed in wave order.
+struct RedView {
+  const float* red;
+  int T, MT;
+  __device__ __forceinline__ float sum(int v, int m) const {
+    // element (v = 16 t + 4 qd + r, m = 16 mt + j) sits in lane qd * 16 + j, slot r
+    const int t = v >> 4, i = v & 15, mt = m >> 4;
+    const int ln = (i >> 2) * 16 + (m & 15), r = i & 3;
+    float acc = 0.0f;
+    for (int w = 0; w < NWAVE; ++w) acc += red[(((size_t)w * T + t) * MT + mt) * 256 + ln * 4 + r];
+    return acc;
+  }
+};
+
+// Run one GEMM phase on this workgroup.  On return (after a barrier) the
+// view holds the per-wave partial sums and, with a norm weight, rms[m] holds
+// sqrt(mean(x_m^2) + eps) over the K columns.
+template <typename WT>
+__device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, const GemmDesc& gd) {
+  constexpr int KSZ = MF<WT>::KSZ;
+  const int tid = tidx();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int Mp = gd.M <= 16 ? 16 : 32, MT = Mp >> 4;
+  BGeom G;
+  G.T = (gd.R + 15) >> 4;
+  G.KST = (gd.K + KSZ - 1) / KSZ;
+  G.KSM = XF_BYTES / (MT * MF<WT>::FRAG);
+  G.NT = (G.KST + G.KSM - 1) / G.KSM;
+  const int lo_off = G.KSM * MT * 1024;
+  f32x4 D[TMAX][2];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) D[t][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float ss = 0.0f;
+  const bool has_rows = gd.R > 0;
+  BIter it{0, 0};
+  while (it.tau < G.NT && G.n_pad(it.tau, wave) == 0) ++it.tau;
+  if (!has_rows) it.tau = G.NT;
+  u32x4 slot[RING];
+#pragma unroll
+  for (int j = 0; j < RING - 1; ++j) b_issue<WT>(gd, G, it, wave, lane, slot[j]);
+  for (int tau = 0; tau < G.NT; ++tau) {
+    if (tau > 0) __syncthreads();                  // every wave is done with the previous K-tile
+    b_stage<WT>(a, s, gd, tau, G.KSM, Mp, MT, ss);
+    __syncthreads();
+    const int nr = has_rows ? G.n_real(tau, wave) : 0;
+    const int np = has_rows ? G.n_pad(tau, wave) : 0;
+    for (int j = 0; j < np; j += RING) {
+#pragma unroll
+      for (int r = 0; r < RING; ++r) {
+        b_issue<WT>(gd, G, it, wave, lane, slot[(r + RING - 1) % RING]);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - 1));
+        asm volatile("" : "+v"(slot[r]));
+        if (j + r < nr) {
+          const int jj = j + r;
+          const int sl = wave + NWAVE * (jj / G.T);   // k-step within the K-tile
+          b_mfma<WT>(D, jj % G.T, MT, slot[r], s.xf, sl, lane, lo_off);
+        }
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)");
+#pragma unroll
+  for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
+  // cross-wave reduction through LDS (the X fragments are dead now)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(s.xf);
+  for (int t = 0; t < G.T && t < TMAX; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      if (mt >= MT) break;
+      f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int tt = 0; tt < TMAX; ++tt)
+        if (tt == t) d = D[tt][mt];
+      *reinterpret_cast<float4*>(red + (((size_t)wave * G.T + t) * MT + mt) * 256 + lane * 4) =
+          make_float4(d[0], d[1], d[2], d[3]);
+    }
+  if (gd.normw) s.ssp[tid] = ss;
+  __syncthreads();
+  if (gd.normw && tid < gd.M) {
+    float t2 = 0.0f;
+    for (int q = tid; q < NTHREADS; q += Mp) t2 += s.ssp[q];
+    s.rms[tid] = sqrtf(t2 / (float)gd.K + a.eps);
+  }
+  __syncthreads();
+  return RedView{red, G.T, MT};
+}
+
+// ------------------------------------------------------------ phases
+template <typename WT>
+__device__ __forceinline__ float b_layer0_elem(const BatchArgs& a, const BLds& s, int m, int k) {
+  const int c = s.rcode[m];
+  if (c < 0) return a.has_proj ? a.xin0[(size_t)(m % a.Bq) * a.dim + k] : a.hidden[(size_t)(m % a.Bq) * a.in_dim + k];
+  return WTraits<WT>::one(reinterpret_cast<const WT*>(a.emb) + (size_t)c * a.dim, k);
+}
+
+template <typename WT>
+__device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, int kind, int step, int l) {
+  const int P = gridDim.x, blk = blockIdx.x;
+  GemmDesc gd;
+  gd.kind = kind; gd.step = step; gd.l = l;
+  gd.normw = nullptr;
+  gd.wb = nullptr;
+  int r0 = 0, r1 = 0;
+  const LayerPtr& L = a.L[l];
+  switch (kind) {
+    case BK_PROJ:
+      split_rows(a.dim, blk, P, r0, r1);
+      gd.wa = (const char*)a.proj; gd.ldb = (long long)a.in_dim * sizeof(WT); gd.K = a.in_dim; gd.M = a.Bq;
+      break;
+    case BK_QKV:
+      split_rows(a.qkv_dim, blk, P, r0, r1);
+      gd.wa = (const char*)L.wqkv; gd.ldb = (long long)a.dim * sizeof(WT); gd.K = a.dim; gd.M = b_rows(a, step);
+      gd.normw = L.attn_norm;
+      break;
+    case BK_WO:
+      split_rows(a.dim, blk, P, r0, r1);
+      gd.wa = (const char*)L.wo; gd.ldb = (long long)a.attn_dim * sizeof(WT); gd.K = a.attn_dim; gd.M = b_rows(a, step);
+      break;
+    case BK_UP:
+      split_rows(a.ffn, blk, P, r0, r1);
+      gd.wa = (const char*)L.w1; gd.wb = (const char*)L.w3; gd.ldb = (long long)a.dim * sizeof(WT); gd.K = a.dim;
+      gd.M = b_rows(a, step);
+      gd.normw = L.ffn_norm;
+      break;
+    case BK_DOWN:
+      split_rows(a.dim, blk, P, r0, r1);
+      gd.wa = (const char*)L.w2; gd.ldb = (long long)a.ffn * sizeof(WT); gd.K = a.ffn; gd.M = b_rows(a, step);
+      break;
+    default:
+      split_rows(a.V, blk, P, r0, r1);
+      gd.wa = (const char*)a.outw; gd.ldb = (long long)a.dim * sizeof(WT); gd.K = a.dim; gd.M = a.Bq;
+      gd.normw = a.fnorm;
+      break;
+  }
+  const int nr = r1 - r0;
+  gd.dummy = gd.wa;
+  gd.wa += (long long)r0 * gd.ldb;
+  if (gd.wb) gd.wb += (long long)r0 * gd.ldb;
+  gd.R1 = nr;
+  gd.R = kind == BK_UP ? 2 * nr : nr;
+  if (!gd.wb) gd.wb = gd.wa;
+  const RedView rv = b_gemm<WT>(a, s, gd);
+  const int M = gd.M;
+  const int nv = kind == BK_UP ? nr : gd.R;
+  for (int o = tidx(); o < nv * M; o += NTHREADS) {
+    const int m = o % M, v = o / M;
+    const float d = rv.sum(v, m);
+    switch (kind) {
+      case BK_PROJ: st_coh(a.xin0 + (size_t)m * a.dim + r0 + v, d); break;
+      case BK_QKV: st_coh(bqkv(a, step, l) + (size_t)m * a.qkv_dim + r0 + v, d / s.rms[m]); break;
+      case BK_WO: {
+        const int k = r0 + v;
+        const float xin = l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[(size_t)m * a.dim + k];
+        st_coh(bxmid(a, step, l) + (size_t)m * a.dim + k, xin + d);
+        break;
+      }
+      case BK_UP: {
+        // rows v < nr are w1 (gate), rows nr + v are w3 (up) of column r0 + v
+        const float a1 = d / s.rms[m], a3 = rv.sum(nr + v, m) / s.rms[m];
+        st_coh(bg(a, step, l) + (size_t)m * a.ffn + r0 + v, silu(a1) * a3);
+        break;
+      }
+      case BK_DOWN: {
+        const int k = r0 + v;
+        st_coh(bx(a, step, l) + (size_t)m * a.dim + k, bxmid(a, step, l)[(size_t)m * a.dim + k] + d);
+        break;
+      }
+      default: {
+        const float y = d / s.rms[m];
+        st_coh(blogits(a, step) + (size_t)m * a.V + r0 + v, y);
+        if (a.logits_out) a.logits_out[((size_t)m * (a.ncb - 1) + (step - 1)) * a.V + r0 + v] = y;
+        break;
+      }
+    }
+  }
+}
+
+// One workgroup per (request b, KV group g): the request's new rows' q (the
+// group's heads), k and v from the wqkv outputs, its cached keys/values of
+// earlier positions, q/k RMSNorm + pair RoPE, then causal attention with
+// offset 0; the new keys/values are kept for the frame's later steps.
+template <typename WT>
+__device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, int step, int l) {
+  const int j = blockIdx.x;
+  if (j >= a.Bq * a.n_kv) return;
+  const int b = j / a.n_kv, g = j % a.n_kv;
+  const int hd = a.hd, gh = a.gheads, H = a.n_head, G = a.n_kv;
+  const int n_new = step == 1 ? 2 : 1;
+  const int first_new = step == 1 ? 0 : step;
+  const int tid = tidx(), wave = tid >> 6, lane = tid & 63;
+  float* q = reinterpret_cast<float*>(s.xf);                 // [n_new][gh][hd]
+  float* kc = q + (size_t)2 * gh * hd;                       // [ctx][hd]
+  float* vc = kc + (size_t)a.ctx_len * hd;                   // [ctx][hd]
+  // gather: cached keys/values, then the new rows' raw q, k, v
+  const int n_cache = first_new * 2 * hd;
+  const int n_row = (gh + 2) * hd;
+  for (int i = tid; i < n_cache + n_new * n_row; i += NTHREADS) {
+    if (i < n_cache) {
+      const int pos = i / (2 * hd), r = i - pos * 2 * hd;
+      const float v = bkv(a, b, l, pos, g)[r];
+      (r < hd ? kc : vc)[(size_t)pos * hd + (r % hd)] = v;
+    } else {
+      const int t = i - n_cache;
+      const int nr = t / n_row, r = t - nr * n_row;
+      const int m = step == 1 ? nr * a.Bq + b : b;
+      const int pos = step == 1 ? nr : step;
+      const float* row = bqkv(a, step, l) + (size_t)m * a.qkv_dim;
+      if (r < gh * hd) q[(size_t)nr * gh * hd + r] = row[(size_t)g * gh * hd + r];
+      else if (r < (gh + 1) * hd) kc[(size_t)pos * hd + (r - gh * hd)] = row[(size_t)H * hd + (size_t)g * hd + (r - gh * hd)];
+      else vc[(size_t)pos * hd + (r - (gh + 1) * hd)] = row[(size_t)(H + G) * hd + (size_t)g * hd + (r - (gh + 1) * hd)];
+    }
+  }
+  __syncthreads();
+  const float* qn = s.qkn + (size_t)l * 2 * hd;
+  const float* kn = qn + hd;
+  for (int v = wave; v < n_new * gh + n_new; v += NWAVE) {
+    if (v < n_new * gh) {
+      head_norm_rope(q + (size_t)v * hd, hd, qn, a.has_qkn, a.eps, s.rope, a.ctx_len, first_new + v / gh);
+    } else {
+      const int pos = first_new + (v - n_new * gh);
+      head_norm_rope(kc + (size_t)pos * hd, hd, kn, a.has_qkn, a.eps, s.rope, a.ctx_len, pos);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_new * 2 * hd; i += NTHREADS) {
+    const int nr = i / (2 * hd), r = i - nr * 2 * hd;
+    const int pos = first_new + nr;
+    st_coh(bkv(a, b, l, pos, g) + r, r < hd ? kc[(size_t)pos * hd + r] : vc[(size_t)pos * hd + r - hd]);
+  }
+  // one wave per (row, head); same straight-line scheme as the batch-1 kernel
+  const float scale = 1.0f / sqrtf((float)hd);
+  const int g16 = lane >> 4, l16 = lane & 15;
+  const int d8 = min(8 * l16, hd - 8);
+  const bool dlive = 8 * l16 < hd;
+  const int c0 = min(lane, hd - 1), c1 = min(lane + 64, hd - 1);
+  for (int pr = wave; pr < n_new * gh; pr += NWAVE) {
+    const int nr = pr / gh, hh = pr % gh;
+    const int pos = first_new + nr;
+    const int m = step == 1 ? nr * a.Bq + b : b;
+    const float* qv = q + (size_t)pr * hd;
+    const float4 qa = *reinterpret_cast<const float4*>(qv + d8);
+    const float4 qb = *reinterpret_cast<const float4*>(qv + d8 + 4);
+    float sc4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int jp = 4 * r + g16;
+      const float* kr = kc + (size_t)min(jp, pos) * hd + d8;
+      const float4 ka = *reinterpret_cast<const float4*>(kr);
+      const float4 kb = *reinterpret_cast<const float4*>(kr + 4);
+      float part = qa.x * ka.x;
+      part = fmaf(qa.y, ka.y, part); part = fmaf(qa.z, ka.z, part); part = fmaf(qa.w, ka.w, part);
+      part = fmaf(qb.x, kb.x, part); part = fmaf(qb.y, kb.y, part);
+      part = fmaf(qb.z, kb.z, part); part = fmaf(qb.w, kb.w, part);
+      part = row16_sum(dlive ? part : 0.0f);
+      sc4[r] = (jp <= pos) ? part * scale : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
+    mx = fmaxf(fmaxf(readlane_f(mx, 0), readlane_f(mx, 16)), fmaxf(readlane_f(mx, 32), readlane_f(mx, 48)));
+    float e4[4], es = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      e4[r] = expf(sc4[r] - mx);
+      es += e4[r];
+    }
+    const float den = (readlane_f(es, 0) + readlane_f(es, 16)) + (readlane_f(es, 32) + readlane_f(es, 48));
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int jp = 0; jp < 16; ++jp) {
+      const float* vr = vc + (size_t)min(jp, pos) * hd;
+      const float pj = readlane_f(e4[jp >> 2], (jp & 3) * 16) / den;
+      o0 = fmaf(pj, vr[c0], o0);
+      o1 = fmaf(pj, vr[c1], o1);
+    }
+    float* o = batt(a, step, l) + (size_t)m * a.attn_dim + (size_t)g * a.gw + (size_t)hh * hd;
+    if (lane < hd) st_coh(o + lane, o0);
+    if (lane + 64 < hd) st_coh(o + lane + 64, o1);
+  }
+}
+
+// Workgroup b < Bq draws request b's code of step `step` from its logits.
+__device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s, int step) {
+  const int b = blockIdx.x;
+  if (b >= a.Bq) return;
+  const SampScratch sc{s.cval, s.cidx, s.sred};
+  const int code = sample_request(blogits(a, step) + (size_t)b * a.V, a.V, a.temp[b], a.top_p[b], a.top_k[b],
+                                  a.uniforms[(size_t)b * (a.ncb - 1) + (step - 1)], sc);
+  if (tidx() == 0) {
+    const int c = min(max(code, 0), a.V - 1);
+    st_coh(a.codes + b * 16 + step, c);
+    if (a.codes_out) a.codes_out[(size_t)b * a.ncb + step] = c;
+  }
+}
+
+__host__ __device__ inline int b_syncs(int has_proj, int ncb, int n_layer, bool forced) {
+  return (has_proj ? 1 : 0) + (ncb - 1) * (5 * n_layer + (forced ? 0 : 2));
+}
+
+template <typename WT>
+__global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
+  extern __shared__ float lds_base[];
+  const BLds s = b_carve(reinterpret_cast<char*>(lds_base), a);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  u32 epoch = a.epoch0;
+  if (a.has_qkn) {
+    for (int i = tidx(); i < a.n_layer * 2 * a.hd; i += NTHREADS) {
+      const int l = i / (2 * a.hd), r = i - l * 2 * a.hd;
+      const WT* w = reinterpret_cast<const WT*>(r < a.hd ? a.L[l].q_norm : a.L[l].k_norm);
+      s.qkn[i] = WTraits<WT>::one(w, r < a.hd ? r : r - a.hd);
+    }
+  }
+  for (int i = tidx(); i < a.ctx_len * a.hd; i += NTHREADS) s.rope[i] = a.rope[i];
+  if (blockIdx.x == 0 && a.codes_out)
+    for (int b = tidx(); b < a.Bq; b += NTHREADS) a.codes_out[(size_t)b * a.ncb] = b_code(a, b, 0);
+  __syncthreads();
+  if (a.has_proj) {
+    b_phase_gemm<WT>(a, s, BK_PROJ, 0, 0);
+    if (!grid_sync(a, epoch, s.flag)) return;
+  }
+  for (int step = 1; step < a.ncb; ++step) {
+    const int M = b_rows(a, step);
+    for (int l = 0; l < a.n_layer; ++l) {
+      if (l == 0) {
+        // layer-0 input of every row: the hidden state at position 0, else
+        // fast_embeddings[c_{pos-1}] ("Fast-AR codebook decoding ...", section 2)
+        for (int m = tidx(); m < M; m += NTHREADS) {
+          const int pos = b_pos(a, step, m);
+          s.rcode[m] = pos == 0 ? -1 : b_code(a, m % a.Bq, pos - 1);
+        }
+        __syncthreads();
+      }
+      b_phase_gemm<WT>(a, s, BK_QKV, step, l);
+      if (!grid_sync(a, epoch, s.flag)) return;
+      b_phase_attn<WT>(a, s, step, l);
+      if (!grid_sync(a, epoch, s.flag)) return;
+      b_phase_gemm<WT>(a, s, BK_WO, step, l);
+      if (!grid_sync(a, epoch, s.flag)) return;
+      b_phase_gemm<WT>(a, s, BK_UP, step, l);
+      if (!grid_sync(a, epoch, s.flag)) return;
+      b_phase_gemm<WT>(a, s, BK_DOWN, step, l);
+      if (!grid_sync(a, epoch, s.flag)) return;
+    }
+    b_phase_gemm<WT>(a, s, BK_HEAD, step, 0);
+    if (a.forced) continue;          // teacher forcing: the next prefix is known
+    if (!grid_sync(a, epoch, s.flag)) return;
+    b_phase_sample(a, s, step);
+    if (!grid_sync(a, epoch, s.flag)) return;
+  }
+}

@@ -177,7 +177,8 @@ __device__ __forceinline__ void split_rows(int n, int j, int parts, int& r0, int
 // flag with coherent loads.  Returns false (after raising the watchdog word)
 // if a flag does not arrive within SPIN_LIMIT polls; the caller then leaves
 // the kernel.
-__device__ __forceinline__ bool grid_sync(const FrameArgs& a, u32& epoch, const Lds& s) {
+template <typename Args>
+__device__ __forceinline__ bool grid_sync(const Args& a, u32& epoch, int* lds_flag) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's output stores are done
   __syncthreads();
   const u32 idx = epoch - a.epoch0;
@@ -198,18 +199,19 @@ __device__ __forceinline__ bool grid_sync(const FrameArgs& a, u32& epoch, const 
     }
     if (lane == 0) {
       if (!ok) atomicOr(a.err, 1u);
-      s.flag[0] = ok ? 0 : 1;
+      lds_flag[0] = ok ? 0 : 1;
       if (a.tlog && idx < TLOG_MAX) a.tlog[((size_t)blockIdx.x * TLOG_MAX + idx) * TLOG_W + 1] = (u32)wall_clock64();
     }
   }
   __syncthreads();
-  return s.flag[0] == 0;
+  return lds_flag[0] == 0;
 }
 
 
 // in-phase timeline mark (instrumented runs only): word w of the current
 // phase's record, by thread 0
-__device__ __forceinline__ void mark(const FrameArgs& a, u32 phase, int w) {
+template <typename Args>
+__device__ __forceinline__ void mark(const Args& a, u32 phase, int w) {
   if (a.tlog && tidx() == 0 && phase < TLOG_MAX)
     a.tlog[((size_t)blockIdx.x * TLOG_MAX + phase) * TLOG_W + w] = (u32)wall_clock64();
 }
@@ -956,7 +958,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
       gemv_prologue(pl, slot);
       continue;
     }
-    if (!grid_sync(a, epoch, s)) {
+    if (!grid_sync(a, epoch, s.flag)) {
       asm volatile("s_waitcnt vmcnt(0)");
 #pragma unroll
       for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
@@ -990,6 +992,8 @@ __global__ void __launch_bounds__(NTHREADS) sample_kernel(int V, const float* lo
   if (tidx() == 0) codes[b] = c;
 }
 
+#include "batched.h"
+
 }  // namespace
 
 // =================================================================== host
@@ -1015,6 +1019,20 @@ struct s2fast_ctx {
   u32* tlog = nullptr;     // allocated on first s2fast_test_timeline call
   bool tlog_on = false;
   u32 epoch = 0;
+  // batched decoding (batch >= 2): requests per launch (0: every request is
+  // decoded by its own launch) and the batched arena
+  int bq = 0;
+  size_t b_lds = 0;
+  long long bx_slot = 0, bqkv_slot = 0, batt_slot = 0, bg_slot = 0, blogits_slot = 0;
+  float* b_xin0 = nullptr;
+  float* b_x = nullptr;
+  float* b_xmid = nullptr;
+  float* b_qkv = nullptr;
+  float* b_att = nullptr;
+  float* b_g = nullptr;
+  float* b_logits = nullptr;
+  float* b_kv = nullptr;
+  int* b_codes = nullptr;
 };
 
 namespace {
@@ -1048,7 +1066,8 @@ int syncs_for(const s2fast_config& c, bool forced) {
 
 void free_ctx(s2fast_ctx* c) {
   if (!c) return;
-  void* ptrs[] = {c->rope, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog};
+  void* ptrs[] = {c->rope, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog,
+                  c->b_xin0, c->b_x, c->b_xmid, c->b_qkv, c->b_att, c->b_g, c->b_logits, c->b_kv, c->b_codes};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -1074,6 +1093,61 @@ int launch_frame(s2fast_ctx* c, const FrameArgs& fa_in, hipStream_t stream) {
   if (e != hipSuccess) return S2FAST_ERR_HIP;
   c->epoch += n;
   return S2FAST_OK;
+}
+
+int launch_batched(s2fast_ctx* c, const BatchArgs& ba_in, hipStream_t stream) {
+  BatchArgs ba = ba_in;
+  const u32 n = (u32)b_syncs(c->cfg.has_project_in, c->cfg.num_codebooks, c->cfg.n_layer, ba.forced != nullptr);
+  if (c->epoch > 0xF0000000u) {
+    if (hipMemsetAsync(c->flags, 0, (size_t)c->ncu * 64 * sizeof(u32), stream) != hipSuccess) return S2FAST_ERR_HIP;
+    c->epoch = 0;
+  }
+  ba.epoch0 = c->epoch;
+  void* args[] = {&ba};
+  const void* fn = c->cfg.weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&frame_kernel_b<uint16_t>)
+                                                       : reinterpret_cast<const void*>(&frame_kernel_b<float>);
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(c->ncu), dim3(NTHREADS), args, c->b_lds, stream);
+  if (e != hipSuccess) return S2FAST_ERR_HIP;
+  c->epoch += n;
+  return S2FAST_OK;
+}
+
+void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
+  const s2fast_config& k = c->cfg;
+  std::memset(&ba, 0, sizeof(ba));
+  ba.in_dim = k.in_dim; ba.dim = k.dim; ba.n_layer = k.n_layer; ba.n_head = k.n_head; ba.n_kv = k.n_head_kv;
+  ba.hd = k.head_dim; ba.ffn = k.ffn_dim; ba.V = k.codebook_size; ba.ncb = k.num_codebooks; ba.ctx_len = k.context;
+  ba.eps = k.norm_eps; ba.has_proj = k.has_project_in; ba.has_qkn = k.has_qk_norm;
+  ba.qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim;
+  ba.attn_dim = k.n_head * k.head_dim;
+  ba.gheads = k.n_head / k.n_head_kv;
+  ba.gw = ba.gheads * k.head_dim;
+  ba.proj = c->w.project_in; ba.emb = c->w.embeddings; ba.fnorm = c->w.norm; ba.outw = c->w.output;
+  for (int l = 0; l < k.n_layer; ++l) {
+    const s2fast_layer_weights& L = c->w.layers[l];
+    ba.L[l] = LayerPtr{L.attention_norm, L.wqkv, L.q_norm, L.k_norm, L.wo, L.ffn_norm, L.w1, L.w3, L.w2};
+  }
+  ba.rope = c->rope;
+  ba.xin0 = c->b_xin0; ba.x = c->b_x; ba.xmid = c->b_xmid; ba.qkv = c->b_qkv; ba.att = c->b_att; ba.g = c->b_g;
+  ba.logits = c->b_logits; ba.kv = c->b_kv; ba.codes = c->b_codes;
+  ba.x_slot = c->bx_slot; ba.qkv_slot = c->bqkv_slot; ba.att_slot = c->batt_slot; ba.g_slot = c->bg_slot;
+  ba.logits_slot = c->blogits_slot;
+  ba.flags = c->flags; ba.err = c->err;
+  ba.tlog = c->tlog_on ? c->tlog : nullptr;
+}
+
+// Can this shape run the batched kernel, and with how many requests per
+// launch?  0 when it cannot (then every request gets its own launch).
+int batched_group(const s2fast_config& k, int P) {
+  const int qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim;
+  const int gh = k.n_head / k.n_head_kv;
+  int tmax = 0;
+  for (int n : {qkv_dim, k.dim, k.codebook_size}) tmax = std::max(tmax, ((n + P - 1) / P + 15) / 16);
+  tmax = std::max(tmax, (2 * ((k.ffn_dim + P - 1) / P) + 15) / 16);
+  if (tmax > TMAX || 2 * tmax > RED_TILES) return 0;
+  if ((size_t)(2 * gh * k.head_dim + 2 * k.context * k.head_dim) * sizeof(float) > (size_t)XF_BYTES) return 0;
+  const int bq = std::min(BQ_MAX, P / k.n_head_kv);
+  return bq >= 2 ? bq : 0;
 }
 
 void fill_shape(const s2fast_ctx* c, FrameArgs& fa) {
@@ -1226,6 +1300,37 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
        hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
        hipMemset(c->err, 0, 64 * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_HIP; }
+  if (k.max_batch >= 2) {
+    c->bq = batched_group(k, P);
+    if (c->bq > 0) {
+      c->b_lds = b_lds_bytes(k.n_layer, k.head_dim, k.context);
+      const void* fb = k.weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&frame_kernel_b<uint16_t>)
+                                                     : reinterpret_cast<const void*>(&frame_kernel_b<float>);
+      int nbb = 0;
+      if (c->b_lds > (size_t)prop.sharedMemPerBlock ||
+          hipFuncSetAttribute(fb, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c->b_lds) != hipSuccess ||
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&nbb, fb, NTHREADS, c->b_lds) != hipSuccess || nbb < 1) {
+        c->bq = 0;   // batches then run one launch per request
+      }
+    }
+    if (c->bq > 0) {
+      c->bx_slot = rup((long long)MP_MAX * k.dim, 64);
+      c->bqkv_slot = rup((long long)MP_MAX * qkv_dim, 64);
+      c->batt_slot = rup((long long)MP_MAX * k.n_head * k.head_dim, 64);
+      c->bg_slot = rup((long long)MP_MAX * k.ffn_dim, 64);
+      c->blogits_slot = rup((long long)BQ_MAX * k.codebook_size, 64);
+      ok = dalloc(&c->b_xin0, (size_t)BQ_MAX * k.dim) == hipSuccess &&
+           dalloc(&c->b_x, (size_t)(slots * c->bx_slot)) == hipSuccess &&
+           dalloc(&c->b_xmid, (size_t)(slots * c->bx_slot)) == hipSuccess &&
+           dalloc(&c->b_qkv, (size_t)(slots * c->bqkv_slot)) == hipSuccess &&
+           dalloc(&c->b_att, (size_t)(slots * c->batt_slot)) == hipSuccess &&
+           dalloc(&c->b_g, (size_t)(slots * c->bg_slot)) == hipSuccess &&
+           dalloc(&c->b_logits, (size_t)((k.num_codebooks - 1) * c->blogits_slot)) == hipSuccess &&
+           dalloc(&c->b_kv, (size_t)BQ_MAX * k.n_layer * k.context * k.n_head_kv * 2 * k.head_dim) == hipSuccess &&
+           dalloc(&c->b_codes, (size_t)BQ_MAX * 16) == hipSuccess;
+      if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
+    }
+  }
   *out = c;
   return S2FAST_OK;
 }
@@ -1238,7 +1343,9 @@ void s2fast_destroy(s2fast_ctx* ctx) {
 
 int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B) {
   if (!ctx || B < 1) return -1;
-  return B * syncs_for(ctx->cfg, false);
+  if (B == 1 || ctx->bq == 0) return B * syncs_for(ctx->cfg, false);
+  const int groups = (B + ctx->bq - 1) / ctx->bq;
+  return groups * b_syncs(ctx->cfg.has_project_in, ctx->cfg.num_codebooks, ctx->cfg.n_layer, false);
 }
 
 int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
@@ -1249,10 +1356,27 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
   if (!hidden || !sem_code || !uniforms || !temperature || !top_p || !top_k || !codes) return S2FAST_ERR_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const s2fast_config& k = ctx->cfg;
+  int rc = S2FAST_OK;
+  if (B >= 2 && ctx->bq > 0) {
+    BatchArgs ba;
+    fill_batch_shape(ctx, ba);
+    for (int b0 = 0; b0 < B && rc == S2FAST_OK; b0 += ctx->bq) {
+      ba.Bq = std::min(ctx->bq, B - b0);
+      ba.hidden = hidden + (size_t)b0 * k.in_dim;
+      ba.sem_code = sem_code + b0;
+      ba.uniforms = uniforms + (size_t)b0 * (k.num_codebooks - 1);
+      ba.temp = temperature + b0;
+      ba.top_p = top_p + b0;
+      ba.top_k = top_k + b0;
+      ba.forced = nullptr;
+      ba.codes_out = codes + (size_t)b0 * k.num_codebooks;
+      ba.logits_out = nullptr;
+      rc = launch_batched(ctx, ba, st);
+    }
+  }
   FrameArgs fa;
   fill_shape(ctx, fa);
-  int rc = S2FAST_OK;
-  for (int b = 0; b < B && rc == S2FAST_OK; ++b) {
+  for (int b = 0; b < B && rc == S2FAST_OK && !(B >= 2 && ctx->bq > 0); ++b) {
     fa.hidden = hidden + (size_t)b * k.in_dim;
     fa.sem_code = sem_code + b;
     fa.uniforms = uniforms + (size_t)b * (k.num_codebooks - 1);
@@ -1279,6 +1403,21 @@ int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const
   if (!hidden || !codes || !logits) return S2FAST_ERR_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const s2fast_config& k = ctx->cfg;
+  if (B >= 2 && ctx->bq > 0) {
+    BatchArgs ba;
+    fill_batch_shape(ctx, ba);
+    for (int b0 = 0; b0 < B; b0 += ctx->bq) {
+      ba.Bq = std::min(ctx->bq, B - b0);
+      ba.hidden = hidden + (size_t)b0 * k.in_dim;
+      ba.sem_code = codes + (size_t)b0 * k.num_codebooks;
+      ba.forced = codes + (size_t)b0 * k.num_codebooks;
+      ba.codes_out = nullptr;
+      ba.logits_out = logits + (size_t)b0 * (k.num_codebooks - 1) * k.codebook_size;
+      const int rc = launch_batched(ctx, ba, st);
+      if (rc != S2FAST_OK) return rc;
+    }
+    return S2FAST_OK;
+  }
   FrameArgs fa;
   fill_shape(ctx, fa);
   for (int b = 0; b < B; ++b) {
