@@ -27,9 +27,9 @@
 
 constexpr int BQ_MAX = 16;               // requests per batched launch
 constexpr int MP_MAX = 2 * BQ_MAX;       // rows per decode step at most
-constexpr int XF_BYTES = 96 * 1024;      // LDS for the X operand (and the reduction)
-constexpr int TMAX = 6;                  // 16-row tiles of W per workgroup and phase
-constexpr int RED_TILES = 12;            // tiles x M-tiles the reduction buffer holds
+constexpr int XF_BYTES = 128 * 1024;     // LDS for the X operand (two buffers; also the reduction)
+constexpr int TMAX = 5;                  // 16-row tiles of W per workgroup and phase
+constexpr int RED_TILES = 10;            // tiles x M-tiles the reduction buffer holds
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -83,12 +83,13 @@ struct BLds {
   int* sred;     // [2 * NWAVE * SAMP_TAU]
   int* rcode;    // [MP_MAX] embedding row of each row's layer-0 input (-1: hidden state)
   int* flag;     // [4]
+  float* nw;     // [dim] the current phase's RMSNorm weight
 };
 
-__host__ __device__ inline size_t b_lds_bytes(int n_layer, int hd, int ctx) {
+__host__ __device__ inline size_t b_lds_bytes(int n_layer, int hd, int ctx, int dim) {
   return (size_t)XF_BYTES + sizeof(float) * ((size_t)NTHREADS + MP_MAX + (size_t)n_layer * 2 * hd + (size_t)ctx * hd +
                                              TOPK_MAX) +
-         sizeof(int) * ((size_t)TOPK_MAX + 2 * NWAVE * SAMP_TAU + MP_MAX + 4);
+         sizeof(int) * ((size_t)TOPK_MAX + 2 * NWAVE * SAMP_TAU + MP_MAX + 4) + sizeof(float) * (size_t)dim;
 }
 
 __device__ inline BLds b_carve(char* base, const BatchArgs& a) {
@@ -103,7 +104,8 @@ __device__ inline BLds b_carve(char* base, const BatchArgs& a) {
   s.cidx = reinterpret_cast<int*>(p); p += sizeof(int) * TOPK_MAX;
   s.sred = reinterpret_cast<int*>(p); p += sizeof(int) * 2 * NWAVE * SAMP_TAU;
   s.rcode = reinterpret_cast<int*>(p); p += sizeof(int) * MP_MAX;
-  s.flag = reinterpret_cast<int*>(p);
+  s.flag = reinterpret_cast<int*>(p); p += sizeof(int) * 4;
+  s.nw = reinterpret_cast<float*>(p);
   return s;
 }
 
@@ -207,62 +209,57 @@ __device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const
   }
 }
 
-// GE weights of the RMSNorm vector at column k
-template <typename WT>
-__device__ __forceinline__ void b_fetch_w(const void* w, int k, float (&v)[8]) {
-  if (MF<WT>::GE == 8) {
-    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(w) + k);
-    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
-    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
-    v[4] = __uint_as_float(q.z << 16); v[5] = __uint_as_float(q.z & 0xFFFF0000u);
-    v[6] = __uint_as_float(q.w << 16); v[7] = __uint_as_float(q.w & 0xFFFF0000u);
-  } else {
-    const float4 q = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(w) + k);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-  }
-}
+// All eight waves stage a K-tile of X, then all eight stream the weights
+// against it.  (Staging on a few dedicated waves while the others stream was
+// measured slower: with the weight streams running, the staging loads -- data
+// written by other XCDs, so L2 misses -- wait much longer in the memory
+// queues.)
+constexpr int NWC = NWAVE;                      // waves running the MFMAs
+constexpr int NSTAGE = NTHREADS;                // threads staging X
+constexpr int XBUF = XF_BYTES;                  // one X buffer
+// staging items in flight per thread (bf16: 4 items of 8 columns; more
+// spills registers next to the MFMA accumulators)
+template <typename WT> constexpr int sbs() { return MF<WT>::GE == 8 ? 4 : 8; }
 
-// Stage K-tile `tau` of X (columns [tau*KSM*KSZ, ...)) into LDS as MFMA B
-// fragments: lane (q, j) of k-step s and M-tile mt holds X[16 mt + j][k0 + s KSZ
-// + GE q .. + GE).  Thread t always handles row m = t % Mp, so its running sum
-// of squares (normed phases) covers one row in a fixed order.
+// Stage K-tile `tau` of X (columns [tau*KSM*KSZ, ...)) into buffer `buf` as
+// MFMA B fragments: lane (q, j) of k-step s and M-tile mt holds
+// X[16 mt + j][k0 + s KSZ + GE q .. + GE) (bf16: high halves, then low halves
+// in the second half of the buffer).  Staging thread st always handles row
+// m = st % Mp, so its running sum of squares (normed phases) covers one row
+// in a fixed order.
 template <typename WT>
 __device__ __forceinline__ void b_stage(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int tau, int KSM,
-                                        int Mp, int MT, float& ss) {
+                                        int Mp, int MT, char* buf, int st, float& ss) {
   constexpr int GE = MF<WT>::GE, KSZ = MF<WT>::KSZ;
-  constexpr int SBX = 2;                       // items in flight per thread
-  const int tid = tidx();
-  const int m = tid % Mp;
+  const int m = st % Mp;
   const int k0 = tau * KSM * KSZ;
-  const int n_items = Mp * KSM * 4;            // multiple of NTHREADS (Mp * KSM * 4 = 3072 or 6144)
-  const int lo_off = KSM * MT * 1024;          // bf16: low halves after the high halves
-  for (int base = 0; base < n_items; base += NTHREADS * SBX) {
-    float v[SBX][8], w[SBX][8];
-    bool ok[SBX];
+  constexpr int SBS = sbs<WT>();
+  const int n_items = Mp * KSM * 4;            // multiple of NSTAGE * SBS
+  const int lo_off = KSM * MT * 1024;
+  for (int base = 0; base < n_items; base += NSTAGE * SBS) {
+    float v[SBS][8];
+    bool ok[SBS];
 #pragma unroll
-    for (int j = 0; j < SBX; ++j) {
-      const int i = base + j * NTHREADS + tid;
-      const int kg = i / Mp;
-      const int k = k0 + kg * GE;
+    for (int j = 0; j < SBS; ++j) {
+      const int i = base + j * NSTAGE + st;
+      const int k = k0 + (i / Mp) * GE;
       ok[j] = i < n_items && m < gd.M && k < gd.K;
-      if (ok[j]) {
-        b_fetch<WT>(a, s, gd, m, k, v[j]);
-        if (gd.normw) b_fetch_w<WT>(gd.normw, k, w[j]);
-      }
+      if (ok[j]) b_fetch<WT>(a, s, gd, m, k, v[j]);
     }
 #pragma unroll
-    for (int j = 0; j < SBX; ++j) {
-      const int i = base + j * NTHREADS + tid;
+    for (int j = 0; j < SBS; ++j) {
+      const int i = base + j * NSTAGE + st;
       if (i >= n_items) continue;
       const int kg = i / Mp;
       const int sl = kg >> 2, q = kg & 3;
       const int idx = ((sl * MT + (m >> 4)) * 64 + q * 16 + (m & 15)) * 16;
+      const int k = k0 + kg * GE;
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[e] = 0.0f;
         if (e < GE && ok[j]) {
-          if (gd.normw) { ss = fmaf(v[j][e], v[j][e], ss); x[e] = v[j][e] * w[j][e]; }
+          if (gd.normw) { ss = fmaf(v[j][e], v[j][e], ss); x[e] = v[j][e] * s.nw[k + e]; }
           else x[e] = v[j][e];
         }
       }
@@ -273,34 +270,33 @@ __device__ __forceinline__ void b_stage(const BatchArgs& a, const BLds& s, const
           h[e] = bf16_rne(x[e]);
           lw[e] = bf16_rne(x[e] - __uint_as_float(h[e] << 16));
         }
-        *reinterpret_cast<uint4*>(s.xf + idx) =
+        *reinterpret_cast<uint4*>(buf + idx) =
             make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-        *reinterpret_cast<uint4*>(s.xf + lo_off + idx) =
+        *reinterpret_cast<uint4*>(buf + lo_off + idx) =
             make_uint4(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16), lw[4] | (lw[5] << 16), lw[6] | (lw[7] << 16));
       } else {
-        *reinterpret_cast<float4*>(s.xf + idx) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(buf + idx) = make_float4(x[0], x[1], x[2], x[3]);
       }
     }
   }
 }
 
-// Per-wave walk over its weight chunks: in K-tile tau the wave takes k-steps
-// ks0 + wave, ks0 + wave + 8, ... and, for each, the T row tiles; the list of
-// a tile is padded to a multiple of RING (padding issues dummy loads) so that
-// the register ring is in phase at every K-tile boundary.
+// Work of compute wave w in K-tile tau: the tile's (k-step, row tile) pairs
+// i = sl * T + t taken round robin, i = w, w + NWC, ...; the list is padded to
+// a multiple of RING (padding issues dummy loads) so that the register ring
+// is in phase at every K-tile boundary.
 struct BIter {
   int tau, j;
 };
 
 struct BGeom {
   int T, KST, KSM, NT;
-  __device__ __forceinline__ int nks(int tau, int wave) const {
-    const int ks0 = tau * KSM, ks1 = min(KST, ks0 + KSM);
-    const int n = ks1 - ks0 - wave;
-    return n > 0 ? (n + NWAVE - 1) / NWAVE : 0;
+  __device__ __forceinline__ int n_real(int tau, int w) const {
+    const int ks = min(KST - tau * KSM, KSM);
+    const int n = T * ks - w;
+    return n > 0 ? (n + NWC - 1) / NWC : 0;
   }
-  __device__ __forceinline__ int n_real(int tau, int wave) const { return T * nks(tau, wave); }
-  __device__ __forceinline__ int n_pad(int tau, int wave) const { return (n_real(tau, wave) + RING - 1) / RING * RING; }
+  __device__ __forceinline__ int n_pad(int tau, int w) const { return (n_real(tau, w) + RING - 1) / RING * RING; }
 };
 
 template <typename WT>
@@ -310,10 +306,10 @@ __device__ __forceinline__ void b_issue(const GemmDesc& gd, const BGeom& G, BIte
   const char* addr = gd.dummy;
   if (it.tau < G.NT) {
     if (it.j < G.n_real(it.tau, wave)) {
-      const int s = it.tau * G.KSM + wave + NWAVE * (it.j / G.T);
-      const int t = it.j % G.T;
-      int v = 16 * t + (lane & 15);
-      v = min(v, gd.R - 1);
+      const int i = wave + NWC * it.j;
+      const int s = it.tau * G.KSM + i / G.T;
+      const int t = i % G.T;
+      const int v = min(16 * t + (lane & 15), gd.R - 1);
       int col = s * KSZ + GE * (lane >> 4);
       if (col >= gd.K) col = 0;      // past the last column: X is zero there
       const char* row = v < gd.R1 ? gd.wa + (long long)v * gd.ldb : gd.wb + (long long)(v - gd.R1) * gd.ldb;
@@ -375,32 +371,21 @@ struct RedView {
     const int t = v >> 4, i = v & 15, mt = m >> 4;
     const int ln = (i >> 2) * 16 + (m & 15), r = i & 3;
     float acc = 0.0f;
-    for (int w = 0; w < NWAVE; ++w) acc += red[(((size_t)w * T + t) * MT + mt) * 256 + ln * 4 + r];
+    for (int w = 0; w < NWC; ++w) acc += red[(((size_t)w * T + t) * MT + mt) * 256 + ln * 4 + r];
     return acc;
   }
 };
 
-// Run one GEMM phase on this workgroup.  On return (after a barrier) the
-// view holds the per-wave partial sums and, with a norm weight, rms[m] holds
-// sqrt(mean(x_m^2) + eps) over the K columns.
+// Compute-wave side of one GEMM phase.
 template <typename WT>
-__device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, const GemmDesc& gd) {
-  constexpr int KSZ = MF<WT>::KSZ;
-  const int tid = tidx();
-  const int wave = tid >> 6, lane = tid & 63;
-  const int Mp = gd.M <= 16 ? 16 : 32, MT = Mp >> 4;
-  BGeom G;
-  G.T = (gd.R + 15) >> 4;
-  G.KST = (gd.K + KSZ - 1) / KSZ;
-  G.KSM = XF_BYTES / (MT * MF<WT>::FRAG);
-  G.NT = (G.KST + G.KSM - 1) / G.KSM;
+__device__ __forceinline__ void b_compute(const BatchArgs& a, const BLds& s, const GemmDesc& gd, const BGeom& G, int Mp,
+                                          int MT, int wave, int lane, float& ss) {
   const int lo_off = G.KSM * MT * 1024;
   f32x4 D[TMAX][2];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t)
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) D[t][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float ss = 0.0f;
   const bool has_rows = gd.R > 0;
   BIter it{0, 0};
   while (it.tau < G.NT && G.n_pad(it.tau, wave) == 0) ++it.tau;
@@ -408,10 +393,13 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
   u32x4 slot[RING];
 #pragma unroll
   for (int j = 0; j < RING - 1; ++j) b_issue<WT>(gd, G, it, wave, lane, slot[j]);
+  mark(a, s.flag[1], 2);
   for (int tau = 0; tau < G.NT; ++tau) {
-    if (tau > 0) __syncthreads();                  // every wave is done with the previous K-tile
-    b_stage<WT>(a, s, gd, tau, G.KSM, Mp, MT, ss);
+    if (tau > 0) __syncthreads();                       // every wave is done with tile tau-1
+    b_stage<WT>(a, s, gd, tau, G.KSM, Mp, MT, s.xf, tidx(), ss);
     __syncthreads();
+    if (tau == 0) mark(a, s.flag[1], 3);
+    const char* xb = s.xf;
     const int nr = has_rows ? G.n_real(tau, wave) : 0;
     const int np = has_rows ? G.n_pad(tau, wave) : 0;
     for (int j = 0; j < np; j += RING) {
@@ -421,18 +409,17 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - 1));
         asm volatile("" : "+v"(slot[r]));
         if (j + r < nr) {
-          const int jj = j + r;
-          const int sl = wave + NWAVE * (jj / G.T);   // k-step within the K-tile
-          b_mfma<WT>(D, jj % G.T, MT, slot[r], s.xf, sl, lane, lo_off);
+          const int i = wave + NWC * (j + r);
+          b_mfma<WT>(D, i % G.T, MT, slot[r], xb, i / G.T, lane, lo_off);
         }
       }
     }
+    if (tau < 2 || tau == G.NT - 1) mark(a, s.flag[1], tau < 2 ? 4 + tau : 6);
   }
+  __syncthreads();                                      // X is dead: the reduction may overwrite it
   asm volatile("s_waitcnt vmcnt(0)");
 #pragma unroll
   for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
-  // cross-wave reduction through LDS (the X fragments are dead now)
-  __syncthreads();
   float* red = reinterpret_cast<float*>(s.xf);
   for (int t = 0; t < G.T && t < TMAX; ++t)
 #pragma unroll
@@ -445,15 +432,37 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
       *reinterpret_cast<float4*>(red + (((size_t)wave * G.T + t) * MT + mt) * 256 + lane * 4) =
           make_float4(d[0], d[1], d[2], d[3]);
     }
+}
+
+// Run one GEMM phase on this workgroup.  On return (after a barrier) the
+// view holds the compute waves' partial sums and, with a norm weight,
+// rms[m] holds sqrt(mean(x_m^2) + eps) over the K columns.
+template <typename WT>
+__device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, const GemmDesc& gd) {
+  constexpr int KSZ = MF<WT>::KSZ;
+  const int tid = tidx();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int Mp = gd.M <= 16 ? 16 : 32, MT = Mp >> 4;
+  BGeom G;
+  G.T = (gd.R + 15) >> 4;
+  G.KST = (gd.K + KSZ - 1) / KSZ;
+  G.KSM = XBUF / (MT * MF<WT>::FRAG);
+  G.NT = (G.KST + G.KSM - 1) / G.KSM;
+  if (gd.normw) {
+    for (int k = tid; k < gd.K; k += NTHREADS) s.nw[k] = WTraits<WT>::one(reinterpret_cast<const WT*>(gd.normw), k);
+    __syncthreads();
+  }
+  float ss = 0.0f;
+  b_compute<WT>(a, s, gd, G, Mp, MT, wave, lane, ss);
   if (gd.normw) s.ssp[tid] = ss;
   __syncthreads();
   if (gd.normw && tid < gd.M) {
     float t2 = 0.0f;
-    for (int q = tid; q < NTHREADS; q += Mp) t2 += s.ssp[q];
+    for (int q = tid; q < NSTAGE; q += Mp) t2 += s.ssp[q];
     s.rms[tid] = sqrtf(t2 / (float)gd.K + a.eps);
   }
   __syncthreads();
-  return RedView{red, G.T, MT};
+  return RedView{reinterpret_cast<const float*>(s.xf), G.T, MT};
 }
 
 // ------------------------------------------------------------ phases
@@ -689,6 +698,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
   }
   for (int step = 1; step < a.ncb; ++step) {
     const int M = b_rows(a, step);
+    if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     for (int l = 0; l < a.n_layer; ++l) {
       if (l == 0) {
         // layer-0 input of every row: the hidden state at position 0, else
@@ -701,14 +711,19 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
       }
       b_phase_gemm<WT>(a, s, BK_QKV, step, l);
       if (!grid_sync(a, epoch, s.flag)) return;
+      if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       b_phase_attn<WT>(a, s, step, l);
       if (!grid_sync(a, epoch, s.flag)) return;
+      if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       b_phase_gemm<WT>(a, s, BK_WO, step, l);
       if (!grid_sync(a, epoch, s.flag)) return;
+      if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       b_phase_gemm<WT>(a, s, BK_UP, step, l);
       if (!grid_sync(a, epoch, s.flag)) return;
+      if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       b_phase_gemm<WT>(a, s, BK_DOWN, step, l);
       if (!grid_sync(a, epoch, s.flag)) return;
+      if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     }
     b_phase_gemm<WT>(a, s, BK_HEAD, step, 0);
     if (a.forced) continue;          // teacher forcing: the next prefix is known

@@ -35,7 +35,7 @@ def ragged():
 @pytest.fixture(scope="module")
 def s2pro():
     _announce("s2pro model (bf16, 828 MB)")
-    return pr.make_pair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0), max_batch=2)
+    return pr.make_pair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0), max_batch=20)
 
 
 # ------------------------------------------------------------------ sampler
@@ -159,6 +159,72 @@ def test_s2pro_greedy_b2(s2pro):
     T = np.zeros(2, np.float32)
     codes = pr.gpu_decode(s2pro, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], T, fr["top_p"], fr["top_k"])
     pr.check_codes(s2pro, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], T, fr["top_p"], fr["top_k"], codes)
+
+
+# ------------------------------------------------------------------ batched decoding
+# Batches of 2..16 requests share one launch (skinny GEMMs on the matrix
+# cores); larger batches run in groups of 16.
+
+def test_s2pro_b16_batched(s2pro):
+    w = si.WORKLOADS["s2pro_b16"]          # per-request temperature / top_p, Zipf semantic codes
+    fr = _frames(w, 1, 16)
+    codes = pr.gpu_decode(s2pro, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
+                          fr["top_p"], fr["top_k"])
+    excused = pr.check_codes(s2pro, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
+                             fr["top_p"], fr["top_k"], codes)
+    worst, rel, _, _ = pr.check_logits(s2pro, fr["hidden"][0][:4], codes[:4])
+    _announce(f"s2pro B=16: excused {excused}; logits worst |d|/tol {worst:.2e}, |d|/max {rel:.2e}")
+    assert worst <= 1.0 and rel < 1e-3, (worst, rel)
+
+
+def test_s2pro_batched_teacher_forced_all_rows(s2pro):
+    """Teacher-forced logits of a full group of 16 (every row of the skinny
+    GEMMs, both M-tiles at step 1)."""
+    w = si.WORKLOADS["s2pro_b16"]
+    fr = _frames(w, 1, 16)
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, w.shape.codebook_size, size=(16, w.shape.num_codebooks)).astype(np.int32)
+    worst, rel, _, _ = pr.check_logits(s2pro, fr["hidden"][0], codes)
+    _announce(f"s2pro B=16 teacher-forced: worst |d|/tol {worst:.2e}, |d|/max {rel:.2e}")
+    assert worst <= 1.0 and rel < 1e-3, (worst, rel)
+
+
+def test_two_groups_with_project_in():
+    """B = 18 runs as 16 + 2; project_in shape, first half greedy."""
+    w = si.WORKLOADS["s2pro_b64"]
+    pair = pr.make_pair(w.shape, w.seed(0), max_batch=18)
+    fr = _frames(w, 1, 18)
+    assert (fr["temperature"][:9] == 0).all() and (fr["temperature"][9:] > 0).all()
+    codes = pr.gpu_decode(pair, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
+                          fr["top_p"], fr["top_k"])
+    pick = [0, 8, 9, 15, 16, 17]
+    excused = pr.check_codes(pair, fr["hidden"][0][pick], fr["sem_code"][0][pick], fr["uniforms"][0][pick],
+                             fr["temperature"][pick], fr["top_p"][pick], fr["top_k"][pick], codes[pick])
+    worst, rel, _, _ = pr.check_logits(pair, fr["hidden"][0][[0, 17]], codes[[0, 17]])
+    _announce(f"project_in B=18: excused {excused}; logits worst {worst:.2e}, rel {rel:.2e}")
+    assert worst <= 1.0 and rel < 1e-3, (worst, rel)
+    pair.ctx.close()
+
+
+def test_tiny_f32_batched_groups():
+    """float32 weights (float32 MFMA path), B = 20 = 16 + 4, mixed settings."""
+    w = si.WORKLOADS["tiny"]
+    pair = pr.make_pair(w.shape, w.seed(0), max_batch=20)
+    fr = _frames(w, 2, 20)
+    rng = np.random.default_rng(11)
+    temp = rng.uniform(0.5, 1.2, size=20).astype(np.float32)
+    temp[::3] = 0.0
+    top_p = rng.uniform(0.5, 1.0, size=20).astype(np.float32)
+    top_k = rng.integers(1, 80, size=20).astype(np.int32)
+    excused = 0
+    for f in range(2):
+        codes = pr.gpu_decode(pair, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], temp, top_p, top_k)
+        excused += pr.check_codes(pair, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], temp, top_p, top_k,
+                                  codes)
+        worst, rel, _, _ = pr.check_logits(pair, fr["hidden"][f], codes)
+        assert worst <= 1.0 and rel < 1e-4, (worst, rel)
+    _announce(f"tiny f32 B=20: excused {excused}")
+    pair.ctx.close()
 
 
 # ------------------------------------------------------------------ behaviour
