@@ -105,7 +105,6 @@ struct Lds {
   u32* mark;     // [256] sampler cross-wave scratch
   int* codes;    // [16]
   int* flag;     // [4]
-  float* nw;     // [dim] RMSNorm weight of the current layer phase
   float* fnw;    // [dim] fast_norm weight (loaded once per frame)
   float* qkn;    // [n_layer][2][hd] q_norm and k_norm weights (loaded once per frame)
   float* rope;   // [2][ctx][hd/2] cos and sin (loaded once per frame)
@@ -115,7 +114,7 @@ __host__ __device__ inline size_t lds_floats(int kmax, int rmax, int gheads, int
                                              int n_layer) {
   const size_t act = ((size_t)MMAX * kmax + 3) & ~(size_t)3;   // keeps the regions after it 16-byte aligned
   return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)MMAX * gheads * hd + 2 * (size_t)ctx * hd +
-         2 * TOPK_MAX + 256 + 16 + 4 + 2 * (size_t)dim + (size_t)n_layer * 2 * hd +
+         2 * TOPK_MAX + 256 + 16 + 4 + (size_t)dim + (size_t)n_layer * 2 * hd +
          (size_t)ctx * hd;
 }
 
@@ -134,7 +133,6 @@ __device__ inline Lds carve(float* base, const FrameArgs& a) {
   s.mark = reinterpret_cast<u32*>(p); p += 256;
   s.codes = reinterpret_cast<int*>(p); p += 16;
   s.flag = reinterpret_cast<int*>(p); p += 4;
-  s.nw = p; p += a.dim;
   s.fnw = p; p += a.dim;
   s.qkn = p; p += (size_t)a.n_layer * 2 * a.hd;
   s.rope = p;
@@ -294,14 +292,36 @@ template <> struct WPair<float> {
   __device__ static __forceinline__ float hi(type b) { return hi_f32(b); }
 };
 
+// Per-wave partial sums of squares of rows 0 and 1 into small[m * NWAVE + wave].
+__device__ __forceinline__ void store_ss(float* small, int M, float ss0, float ss1) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const float t0 = wave_sum(ss0);
+  const float t1 = wave_sum(ss1);
+  if (lane == 0) {
+    small[wave] = t0;
+    if (M > 1) small[NWAVE + wave] = t1;
+  }
+}
+
+// sqrt(mean(x_m^2) + eps) of row m over K columns from the per-wave partials
+__device__ __forceinline__ float norm_den(const float* small, int m, int K, float eps) {
+  float t = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) t += small[m * NWAVE + w];
+  return sqrtf(t / (float)K + eps);
+}
+
 // Layer input x of the M new rows into LDS act rows (GEMV layout over dim
-// columns); with ADD_ACC also adds the fixed-point attention accumulator
-// (x_mid = x + attention output).
+// columns), already multiplied by this phase's RMSNorm weight; with ADD_ACC
+// the fixed-point attention accumulator is added first (x_mid = x + attention
+// output).  The RMS itself divides the GEMV outputs (norm_den): the row
+// sums of squares are left as per-wave partials in small[m * NWAVE + wave].
 template <typename WT, bool ADD_ACC>
 __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds& s, int l, int step, int M,
                                                   const WT* normw) {
   const int hp = a.dim >> 1;
   const int np = M * hp;
+  float ss0 = 0.0f, ss1 = 0.0f;
   for (int base = 0; base < np; base += NTHREADS * SB) {
     u64 xv[SB], a0[SB], a1[SB];
     typename WPair<WT>::type wv[SB];
@@ -309,9 +329,9 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
     for (int j = 0; j < SB; ++j) {
       const int i = base + j * NTHREADS + tidx();
       xv[j] = 0ull; a0[j] = 0ull; a1[j] = 0ull; wv[j] = 0;
-      if (i < hp) wv[j] = WPair<WT>::load(normw, i);   // this phase's RMSNorm weight, same round trip
       if (i < np) {
         const int m = i / hp, p = i - m * hp;
+        wv[j] = WPair<WT>::load(normw, p);   // the RMSNorm weight, same round trip
         xv[j] = (l == 0) ? input_pair<WT>(a, s, row_pos(step, m), p) : ld64(xb(a, step, l - 1) + (size_t)m * a.dim + 2 * p);
         if (ADD_ACC) {
           const long long* ac = accb(a, step, l) + (size_t)m * a.dim + 2 * p;
@@ -327,12 +347,15 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
         const int m = i / hp, p = i - m * hp;
         float v0 = lo_f32(xv[j]), v1 = hi_f32(xv[j]);
         if (ADD_ACC) { v0 += from_fx((long long)a0[j]); v1 += from_fx((long long)a1[j]); }
+        if (m == 0) ss0 = fmaf(v0, v0, fmaf(v1, v1, ss0));
+        else ss1 = fmaf(v0, v0, fmaf(v1, v1, ss1));
         float* d = s.act + (size_t)m * a.kmax + phys<WT>(2 * p, a.dim);
-        d[0] = v0; d[1] = v1;
+        d[0] = v0 * WPair<WT>::lo(wv[j]);
+        d[1] = v1 * WPair<WT>::hi(wv[j]);
       }
-      if (i < hp) { s.nw[2 * i] = WPair<WT>::lo(wv[j]); s.nw[2 * i + 1] = WPair<WT>::hi(wv[j]); }
     }
   }
+  store_ss(s.small, M, ss0, ss1);
 }
 
 // --------------------------------------------------------------- GEMV
@@ -511,34 +534,6 @@ __device__ __forceinline__ float red_sum(const float* red, int r, int m) {
 // RMSNorm of M rows of K values held in LDS in GEMV layout, in place:
 // x / sqrt(mean(x^2) + eps) * w ("Model loading and GGUF", section 2.2:
 // eps 1e-6; Mizuoto page: computed in float32).
-template <typename WT>
-__device__ __forceinline__ void rms_norm_rows(float* act, int act_ld, int M, int K, const float* w, float eps, float* small) {
-  const int wave = tidx() >> 6, lane = tidx() & 63;
-  for (int m = 0; m < M; ++m) {
-    float ss = 0.0f;
-    for (int k = tidx(); k < K; k += NTHREADS) {
-      float v = act[(size_t)m * act_ld + k];
-      ss = fmaf(v, v, ss);
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) small[m * NWAVE + wave] = ss;
-  }
-  __syncthreads();
-  if (tidx() < M) {
-    float t = 0.0f;
-    for (int w2 = 0; w2 < NWAVE; ++w2) t += small[tidx() * NWAVE + w2];
-    small[32 + tidx()] = sqrtf(t / (float)K + eps);
-  }
-  __syncthreads();
-  for (int m = 0; m < M; ++m) {
-    const float den = small[32 + m];
-    for (int k = tidx(); k < K; k += NTHREADS) {
-      float* v = act + (size_t)m * act_ld + phys<WT>(k, K);
-      *v = *v / den * w[k];
-    }
-  }
-  __syncthreads();
-}
 
 // Layer-0 input of new row m at window position pos, one element (used for
 // the few rows a block owns in the w2 phase).
@@ -654,14 +649,13 @@ __device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int 
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 4);
-  rms_norm_rows<WT>(s.act, a.kmax, M, D, s.nw, a.eps, s.small);
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
   for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
-    st_coh(qkvb(a, step, l) + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m));
+    st_coh(qkvb(a, step, l) + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m) / norm_den(s.small, m, D, a.eps));
   }
 }
 
@@ -838,14 +832,14 @@ __device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, i
   stage_layer_input<WT, true>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm));
   zero_lds(s.red, 2 * nr * NWAVE * MMAX);
   __syncthreads();
-  rms_norm_rows<WT>(s.act, a.kmax, M, D, s.nw, a.eps, s.small);
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);   // rows [0, nr): w1, [nr, 2nr): w3
   __syncthreads();
   mark(a, s.flag[1], 3);
   for (int i = tidx(); i < nr * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
-    st_coh(gb(a, step, l) + (size_t)m * a.ffn + r0 + r, silu(red_sum(s.red, r, m)) * red_sum(s.red, nr + r, m));
+    const float den = norm_den(s.small, m, D, a.eps);
+    st_coh(gb(a, step, l) + (size_t)m * a.ffn + r0 + r, silu(red_sum(s.red, r, m) / den) * (red_sum(s.red, nr + r, m) / den));
   }
 }
 
@@ -876,16 +870,41 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
   const int D = a.dim;
   int r0, r1;
   split_rows(a.V, blockIdx.x, gridDim.x, r0, r1);
-  stage_arena<WT, true>(s.act, xb(a, step, a.n_layer - 1) + (size_t)(M - 1) * D, D);
+  {
+    // last row of the final layer, times fast_norm (in LDS); the RMS divides the logits
+    const float* src = xb(a, step, a.n_layer - 1) + (size_t)(M - 1) * D;
+    const int np = D >> 1;
+    float ss = 0.0f;
+    for (int base = 0; base < np; base += NTHREADS * SB) {
+      u64 v[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const int i = base + j * NTHREADS + tidx();
+        v[j] = i < np ? ld64(src + 2 * i) : 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const int i = base + j * NTHREADS + tidx();
+        if (i < np) {
+          const float v0 = lo_f32(v[j]), v1 = hi_f32(v[j]);
+          ss = fmaf(v0, v0, fmaf(v1, v1, ss));
+          float* d = s.act + phys<WT>(2 * i, D);
+          d[0] = v0 * s.fnw[2 * i];
+          d[1] = v1 * s.fnw[2 * i + 1];
+        }
+      }
+    }
+    store_ss(s.small, 1, ss, 0.0f);
+  }
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
-  rms_norm_rows<WT>(s.act, a.kmax, 1, D, s.fnw, a.eps, s.small);
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
+  const float hden = norm_den(s.small, 0, D, a.eps);
   for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
-    const float v = red_sum(s.red, r, 0);
+    const float v = red_sum(s.red, r, 0) / hden;
     st_coh(logitsb(a, step) + r0 + r, v);
     if (a.logits_out) a.logits_out[(size_t)(step - 1) * a.V + r0 + r] = v;
   }
