@@ -190,8 +190,14 @@ __device__ __forceinline__ bool grid_sync(const Args& a, u32& epoch, int* lds_fl
     u32 spins = 0;
     bool ok = true;
     while (true) {
-      bool done = true;
-      for (int b = lane; b < P; b += 64) done = done && (ld_coh(a.flags + 64 * b) >= epoch);
+      // the first four flags of a lane are loaded unconditionally, so all four
+      // are in flight together (guarded or short-circuit loads would cost one
+      // memory round trip each); blocks beyond 256 are polled after them
+      u32 f[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = ld_coh(a.flags + 64 * min(lane + 64 * q, P - 1));
+      bool done = (f[0] >= epoch) & (f[1] >= epoch) & (f[2] >= epoch) & (f[3] >= epoch);
+      for (int b = lane + 256; b < P; b += 64) done &= ld_coh(a.flags + 64 * b) >= epoch;
       if (__ballot(done) == ~0ull) break;
       if (++spins > SPIN_LIMIT) { ok = false; break; }
     }
@@ -232,26 +238,23 @@ __device__ __forceinline__ int phys(int k, int K) {
   return k;
 }
 
-// n floats (n even, src 8-byte aligned) of arena data into LDS; PERM places
-// them for a GEMV over K = n columns.
+// n floats (n a multiple of 4, src 16-byte aligned) of arena data into LDS
+// with 16-byte loads; PERM places them for a GEMV over K = n columns (four
+// consecutive columns stay consecutive in that layout).
 template <typename WT, bool PERM>
 __device__ __forceinline__ void stage_arena(float* dst, const float* src, int n) {
-  const int np = n >> 1;
-  for (int base = 0; base < np; base += NTHREADS * SB) {
-    u64 v[SB];
+  const int nq = n >> 2;
+  for (int base = 0; base < nq; base += NTHREADS * SB) {
+    float4 v[SB];
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
       const int i = base + j * NTHREADS + tidx();
-      v[j] = i < np ? ld64(src + 2 * i) : 0ull;
+      v[j] = i < nq ? *reinterpret_cast<const float4*>(src + 4 * i) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
       const int i = base + j * NTHREADS + tidx();
-      if (i < np) {
-        float* d = dst + (PERM ? phys<WT>(2 * i, n) : 2 * i);
-        d[0] = lo_f32(v[j]);
-        d[1] = hi_f32(v[j]);
-      }
+      if (i < nq) *reinterpret_cast<float4*>(dst + (PERM ? phys<WT>(4 * i, n) : 4 * i)) = v[j];
     }
   }
 }
