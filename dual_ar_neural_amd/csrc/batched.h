@@ -321,7 +321,7 @@ __device__ __forceinline__ void b_issue(const GemmDesc& gd, const BGeom& G, BIte
       while (it.tau < G.NT && G.n_pad(it.tau, wave) == 0) ++it.tau;
     }
   }
-  asm_load16(slot, addr);
+  load16_nt(slot, addr);
 }
 
 template <typename WT>
@@ -406,8 +406,6 @@ __device__ __forceinline__ void b_compute(const BatchArgs& a, const BLds& s, con
 #pragma unroll
       for (int r = 0; r < RING; ++r) {
         b_issue<WT>(gd, G, it, wave, lane, slot[(r + RING - 1) % RING]);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - 1));
-        asm volatile("" : "+v"(slot[r]));
         if (j + r < nr) {
           const int i = wave + NWC * (j + r);
           b_mfma<WT>(D, i % G.T, MT, slot[r], xb, i / G.T, lane, lo_off);
@@ -417,9 +415,6 @@ __device__ __forceinline__ void b_compute(const BatchArgs& a, const BLds& s, con
     if (tau < 2 || tau == G.NT - 1) mark(a, s.flag[1], tau < 2 ? 4 + tau : 6);
   }
   __syncthreads();                                      // X is dead: the reduction may overwrite it
-  asm volatile("s_waitcnt vmcnt(0)");
-#pragma unroll
-  for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
   float* red = reinterpret_cast<float*>(s.xf);
   for (int t = 0; t < G.T && t < TMAX; ++t)
 #pragma unroll

@@ -162,6 +162,19 @@ __device__ __forceinline__ int tidx() {
   return t;
 }
 
+// Number of `width`-item steps of a staging batch at `base` over n items, through
+// an opaque scalar move.  The consuming half of a batch bounds its loop with
+// this value instead of repeating the loading half's test: the compiler can
+// then not treat the two halves as control-equivalent and hoist conversions
+// of loaded values (each with a wait on its load) above the weight prologue
+// issued between them.
+__device__ __forceinline__ int steps_opaque(int n, int base, int width = NTHREADS) {
+  const int k = (n - base + width - 1) / width;
+  int r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "s"(k));
+  return r;
+}
+
 // rows [r0, r1) of an n-row matrix owned by part `j` of `parts`
 __device__ __forceinline__ void split_rows(int n, int j, int parts, int& r0, int& r1) {
   r0 = (int)(((long long)n * j) / parts);
@@ -224,8 +237,6 @@ __device__ __forceinline__ void mark(const Args& a, u32 phase, int w) {
 // Cross-block inputs (arena regions) are read with plain 8-byte loads.  Every
 // helper issues a batch of independent loads per thread before using any of
 // them, so a phase pays about one memory round trip for its activations.
-constexpr int SB = 8;   // loads in flight per thread per batch
-
 // Position of natural element k of a GEMV activation row of width K in LDS.
 // For bf16 weights a lane consumes 8 columns (16 bytes of weights) per load;
 // its 8 activation floats are kept as two 16-byte halves in two separate
@@ -238,62 +249,67 @@ __device__ __forceinline__ int phys(int k, int K) {
   return k;
 }
 
-// n floats (n a multiple of 4, src 16-byte aligned) of arena data into LDS
-// with 16-byte loads; PERM places them for a GEMV over K = n columns (four
-// consecutive columns stay consecutive in that layout).
-template <typename WT, bool PERM>
-__device__ __forceinline__ void stage_arena(float* dst, const float* src, int n) {
-  const int nq = n >> 2;
-  for (int base = 0; base < nq; base += NTHREADS * SB) {
-    float4 v[SB];
-#pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const int i = base + j * NTHREADS + tidx();
-      v[j] = i < nq ? *reinterpret_cast<const float4*>(src + 4 * i) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
-#pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const int i = base + j * NTHREADS + tidx();
-      if (i < nq) *reinterpret_cast<float4*>(dst + (PERM ? phys<WT>(4 * i, n) : 4 * i)) = v[j];
-    }
-  }
-}
+typedef float v4f __attribute__((ext_vector_type(4)));         // native vectors stay in registers
+typedef long long v2ll __attribute__((ext_vector_type(2)));
 
-// Two consecutive layer-0 input values (elements 2p, 2p+1) of the row at
-// window position pos: position 0 is the hidden state (through
-// fast_project_in when present), position j >= 1 is fast_embeddings[c_{j-1}]
-// ("Fast-AR codebook decoding ...", section 2).  Packed as two float32 bit
-// patterns.
-template <typename WT>
-__device__ __forceinline__ u64 input_pair(const FrameArgs& a, const Lds& s, int pos, int p) {
-  if (pos == 0) {
-    if (a.has_proj) return ld64(a.xin0 + 2 * p);
-    return *reinterpret_cast<const u64*>(a.hidden + 2 * p);
-  }
-  const WT* e = reinterpret_cast<const WT*>(a.emb) + (size_t)s.codes[pos - 1] * a.dim + 2 * p;
-  const float f0 = WTraits<WT>::one(e, 0), f1 = WTraits<WT>::one(e, 1);
-  return (u64)__float_as_uint(f0) | ((u64)__float_as_uint(f1) << 32);
-}
-
-// Two consecutive weights w[2p], w[2p+1] in their storage format: one dword
-// for bf16, two for f32 (keeps the staging batches' register footprint low).
-template <typename WT> struct WPair;
-template <> struct WPair<uint16_t> {
-  using type = u32;
-  __device__ static __forceinline__ type load(const uint16_t* w, int p) {
-    return *reinterpret_cast<const u32*>(w + 2 * p);
-  }
-  __device__ static __forceinline__ float lo(type b) { return __uint_as_float(b << 16); }
-  __device__ static __forceinline__ float hi(type b) { return __uint_as_float(b & 0xFFFF0000u); }
+// Activation staging.  A batch covers NS steps of NTHREADS 16-byte quads
+// (four consecutive floats); step j of thread t takes quad base + j*NTHREADS
+// + t.  All loads of a batch are issued before any is used and none is
+// guarded: a step past the end re-reads the thread's first quad of the
+// batch (the cache lines its first load fetched), so every address stays in
+// bounds.  The first batch takes a hook that runs right after its loads are
+// issued; the phase issues its weight prologue there, so the activation
+// loads it waits on are not queued behind a chip-wide burst of weight loads.
+// The consuming half of a batch is bounded by the opaque step count.
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
 };
-template <> struct WPair<float> {
+
+__device__ __forceinline__ int quad_of(int base, int j, int nq) {
+  const int q = base + j * NTHREADS + tidx();
+  return q < nq ? q : min(base + tidx(), nq - 1);
+}
+
+// Four consecutive weights w[4c..4c+3] in their storage format: 8 bytes for
+// bf16, 16 for f32.
+template <typename WT> struct WQuad;
+template <> struct WQuad<uint16_t> {
   using type = u64;
-  __device__ static __forceinline__ type load(const float* w, int p) {
-    return *reinterpret_cast<const u64*>(w + 2 * p);
+  __device__ static __forceinline__ type load(const uint16_t* w, int c) {
+    return *reinterpret_cast<const u64*>(w + 4 * c);
   }
-  __device__ static __forceinline__ float lo(type b) { return lo_f32(b); }
-  __device__ static __forceinline__ float hi(type b) { return hi_f32(b); }
+  __device__ static __forceinline__ float get(type b, int e) { return __uint_as_float((u32)(b >> (16 * e)) << 16); }
 };
+template <> struct WQuad<float> {
+  using type = v4f;
+  __device__ static __forceinline__ type load(const float* w, int c) {
+    return *reinterpret_cast<const v4f*>(w + 4 * c);
+  }
+  __device__ static __forceinline__ float get(type b, int e) { return b[e]; }
+};
+
+// n floats (n a multiple of 4, src 16-byte aligned) of arena data into LDS;
+// PERM places them for a GEMV over K = n columns (four consecutive columns
+// stay consecutive in that layout).
+template <typename WT, bool PERM, int NS, typename Hook>
+__device__ __forceinline__ void stage_arena(float* dst, const float* src, int n, const Hook& hook) {
+  const int nq = n >> 2;
+  auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
+    v4f v[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) v[j] = *reinterpret_cast<const v4f*>(src + 4 * quad_of(base, j, nq));
+    after();
+    const int nj = steps_opaque(nq, base);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (j >= nj) break;
+      const int q = base + j * NTHREADS + tidx();
+      if (q < nq) *reinterpret_cast<v4f*>(dst + (PERM ? phys<WT>(4 * q, n) : 4 * q)) = v[j];
+    }
+  };
+  batch(0, hook);
+  for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
+}
 
 // Per-wave partial sums of squares of rows 0 and 1 into small[m * NWAVE + wave].
 __device__ __forceinline__ void store_ss(float* small, int M, float ss0, float ss1) {
@@ -319,45 +335,70 @@ __device__ __forceinline__ float norm_den(const float* small, int m, int K, floa
 // the fixed-point attention accumulator is added first (x_mid = x + attention
 // output).  The RMS itself divides the GEMV outputs (norm_den): the row
 // sums of squares are left as per-wave partials in small[m * NWAVE + wave].
-template <typename WT, bool ADD_ACC>
+template <typename WT, bool ADD_ACC, typename Hook>
 __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds& s, int l, int step, int M,
-                                                  const WT* normw) {
-  const int hp = a.dim >> 1;
-  const int np = M * hp;
+                                                  const WT* normw, const Hook& hook) {
+  constexpr int NS = 3;
+  const int hq = a.dim >> 2;
+  const int nq = M * hq;
+  // float32 source rows: the previous layer's output, or at layer 0 the
+  // hidden state (through fast_project_in when present) at window position 0;
+  // layer 0 at positions j >= 1 takes fast_embeddings[c_{j-1}]
+  // ("Fast-AR codebook decoding ...", section 2)
+  const float* fsrc = (l > 0) ? xb(a, step, l - 1) : (a.has_proj ? a.xin0 : a.hidden);
+  const size_t fstride = (l > 0) ? (size_t)a.dim : 0;
   float ss0 = 0.0f, ss1 = 0.0f;
-  for (int base = 0; base < np; base += NTHREADS * SB) {
-    u64 xv[SB], a0[SB], a1[SB];
-    typename WPair<WT>::type wv[SB];
+  auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
+    v4f xv[NS];
+    v2ll a0[NS], a1[NS];
+    typename WQuad<WT>::type wv[NS], ev[NS];
 #pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const int i = base + j * NTHREADS + tidx();
-      xv[j] = 0ull; a0[j] = 0ull; a1[j] = 0ull; wv[j] = 0;
-      if (i < np) {
-        const int m = i / hp, p = i - m * hp;
-        wv[j] = WPair<WT>::load(normw, p);   // the RMSNorm weight, same round trip
-        xv[j] = (l == 0) ? input_pair<WT>(a, s, row_pos(step, m), p) : ld64(xb(a, step, l - 1) + (size_t)m * a.dim + 2 * p);
-        if (ADD_ACC) {
-          const long long* ac = accb(a, step, l) + (size_t)m * a.dim + 2 * p;
-          a0[j] = ld64(ac);
-          a1[j] = ld64(ac + 1);
-        }
+    for (int j = 0; j < NS; ++j) {
+      const int q = quad_of(base, j, nq);
+      const int m = q / hq, c = q - m * hq;
+      const int pos = row_pos(step, m);
+      wv[j] = WQuad<WT>::load(normw, c);   // the RMSNorm weight, same round trip
+      xv[j] = *reinterpret_cast<const v4f*>(fsrc + (size_t)m * fstride + 4 * c);
+      // layer 0, position >= 1: the embedding row of the previous code
+      // (otherwise row 0, loaded and not used, so that the load needs no branch)
+      const int code = (l == 0 && pos > 0) ? s.codes[max(pos - 1, 0)] : 0;
+      ev[j] = WQuad<WT>::load(reinterpret_cast<const WT*>(a.emb) + (size_t)code * a.dim, c);
+      if (ADD_ACC) {
+        const long long* ac = accb(a, step, l) + (size_t)m * a.dim + 4 * c;
+        a0[j] = *reinterpret_cast<const v2ll*>(ac);
+        a1[j] = *reinterpret_cast<const v2ll*>(ac + 2);
       }
     }
+    after();
+    const int nj = steps_opaque(nq, base);
 #pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const int i = base + j * NTHREADS + tidx();
-      if (i < np) {
-        const int m = i / hp, p = i - m * hp;
-        float v0 = lo_f32(xv[j]), v1 = hi_f32(xv[j]);
-        if (ADD_ACC) { v0 += from_fx((long long)a0[j]); v1 += from_fx((long long)a1[j]); }
-        if (m == 0) ss0 = fmaf(v0, v0, fmaf(v1, v1, ss0));
-        else ss1 = fmaf(v0, v0, fmaf(v1, v1, ss1));
-        float* d = s.act + (size_t)m * a.kmax + phys<WT>(2 * p, a.dim);
-        d[0] = v0 * WPair<WT>::lo(wv[j]);
-        d[1] = v1 * WPair<WT>::hi(wv[j]);
+    for (int j = 0; j < NS; ++j) {
+      if (j >= nj) break;
+      const int qu = base + j * NTHREADS + tidx();
+      const int q = min(qu, nq - 1);
+      const int m = q / hq, c = q - m * hq;
+      const bool emb = (l == 0 && row_pos(step, m) > 0);
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = emb ? WQuad<WT>::get(ev[j], e) : xv[j][e];
+      if (ADD_ACC) {
+        v[0] += from_fx(a0[j][0]); v[1] += from_fx(a0[j][1]);
+        v[2] += from_fx(a1[j][0]); v[3] += from_fx(a1[j][1]);
+      }
+      if (qu < nq) {
+        float t = (m == 0) ? ss0 : ss1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t = fmaf(v[e], v[e], t);
+        if (m == 0) ss0 = t; else ss1 = t;
+        v4f o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = v[e] * WQuad<WT>::get(wv[j], e);
+        *reinterpret_cast<v4f*>(s.act + (size_t)m * a.kmax + phys<WT>(4 * c, a.dim)) = o;
       }
     }
-  }
+  };
+  batch(0, hook);
+  for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
   store_ss(s.small, M, ss0, ss1);
 }
 
@@ -370,23 +411,22 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
 // leaves per-(row, wave, m) partial sums in red, which the caller zeroes
 // beforehand and reduces in wave order.
 //
-// Weight loads are issued with inline assembly into a ring of RING register
-// slots and retired with explicit s_waitcnt vmcnt(RING-1): RING-1 chunks stay
-// in flight while one is consumed.  vmcnt retires in issue order, so any
-// other memory operation issued in between only makes these waits stricter.
-// The compiler does not see the loads; from issue to the wait that retires
-// it each slot is kept live by an asm operand tie, and a GEMV body ends with
-// vmcnt(0).  Every issue step loads exactly one 16-byte value per lane (a
-// valid dummy address past the wave's range), so the fixed count is exact.
+// Weight loads go into a ring of RING register slots: each step issues the
+// load RING-1 chunks ahead and consumes the oldest, so RING-1 chunks stay in
+// flight while one is multiplied.  The loads are ordinary non-temporal loads
+// the compiler sees, so it places the vmcnt waits itself (in-order retirement
+// lets it wait for exactly the slot being consumed).  Every issue step loads
+// one 16-byte value per lane, a valid dummy address past the wave's range.
 //
-// The first RING-1 loads of a phase (its "prologue") are issued right after
-// the grid barrier that precedes it, so that they overlap the phase's
-// activation staging and normalisation.
+// The first RING-1 loads of a phase (its "prologue") are issued when the
+// phase starts, before its activation staging and normalisation, which they
+// overlap.  A phase's slots never outlive the phase: nothing in flight is
+// carried across the grid barrier or the phase loop.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int RING = GEMV_RING;
 
-__device__ __forceinline__ void asm_load16(u32x4& d, const void* p) {
-  asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(d) : "v"(p));
+__device__ __forceinline__ void load16_nt(u32x4& d, const void* p) {
+  d = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 struct Plan {
@@ -414,21 +454,13 @@ __device__ __forceinline__ Plan make_plan(const WT* Wa, const WT* Wb, long long 
   p.S = K / EPL;
   p.C = (p.S + 63) >> 6;
   const int T = nrows * p.C;
-  const int wave = tidx() >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tidx() >> 6);   // the plan is wave-uniform
   p.t0 = (int)(((long long)T * wave) / NWAVE);
   p.t1 = (int)(((long long)T * (wave + 1)) / NWAVE);
   p.it = p.t0;
   p.ir = p.C ? p.t0 / p.C : 0;
   p.ic = p.t0 - p.ir * p.C;
   p.irow = (p.ir < nr_a) ? p.base_a + (long long)p.ir * p.row_bytes : p.base_b + (long long)(p.ir - nr_a) * p.row_bytes;
-  return p;
-}
-
-__device__ __forceinline__ Plan null_plan(const void* W) {
-  Plan p;
-  p.base_a = p.base_b = p.dummy = p.irow = reinterpret_cast<const char*>(W);
-  p.row_bytes = 0;
-  p.nr_a = p.nrows = p.K = p.S = p.C = p.t0 = p.t1 = p.it = p.ir = p.ic = 0;
   return p;
 }
 
@@ -446,80 +478,82 @@ __device__ __forceinline__ void plan_issue(Plan& p, u32x4& d) {
                                : p.base_b + (long long)(p.ir - p.nr_a) * p.row_bytes;
     }
   }
-  asm_load16(d, addr);
+  load16_nt(d, addr);
 }
 
+// The scheduling fences keep the prologue's loads together where the phase
+// places them: the scheduler would otherwise interleave the consumers of the
+// staging loads issued just before, each with a wait on those loads, between
+// the weight loads.
 __device__ __forceinline__ void gemv_prologue(Plan& p, u32x4 (&slot)[RING]) {
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < RING - 1; ++j) plan_issue(p, slot[j]);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Body: consume the wave's chunks against M activation rows in LDS (GEMV
-// layout, row stride act_ld).
+// Body: consume the wave's chunks against MM activation rows in LDS (GEMV
+// layout, row stride act_ld).  The chunk cursor is wave-uniform, so every
+// branch here is a scalar branch; the per-lane tail of a row (segments past
+// K) is handled by zeroing the lane's weights, not by a branch.
+template <typename WT, int MM>
+__device__ __forceinline__ void gemv_rows(Plan& p, u32x4 (&slot)[RING], const float* act, int act_ld, float* red) {
+  constexpr int EPL = WTraits<WT>::EPL;
+  const int wave = __builtin_amdgcn_readfirstlane(tidx() >> 6), lane = tidx() & 63;
+  const int t0 = p.t0, t1 = p.t1;
+  if (t0 >= t1) return;
+  const int C = p.C, S = p.S, Kh = p.K >> 1;
+  int cr = t0 / C, cc = t0 - cr * C;
+  float acc[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) acc[m] = 0.0f;
+  auto flush = [&](int r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const float v = wave_sum(acc[m]);
+      if (lane == 0) red[((size_t)r * NWAVE + wave) * MMAX + m] = v;
+      acc[m] = 0.0f;
+    }
+  };
+  auto consume = [&](const u32x4& q) __attribute__((always_inline)) {
+    const int seg = cc * 64 + lane;
+    const bool live = seg < S;
+    const int sg = live ? seg : 0;
+    float w[EPL];
+    WTraits<WT>::unpack(make_uint4(q.x, q.y, q.z, q.w), w);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) w[e] = live ? w[e] : 0.0f;
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      const float* row = act + (size_t)m * act_ld;
+      const float4 x0 = *reinterpret_cast<const float4*>(row + (size_t)sg * 4);
+      float s0 = acc[m];
+      s0 = fmaf(w[0], x0.x, s0); s0 = fmaf(w[1], x0.y, s0);
+      s0 = fmaf(w[2], x0.z, s0); s0 = fmaf(w[3], x0.w, s0);
+      if (EPL == 8) {
+        const float4 x1 = *reinterpret_cast<const float4*>(row + Kh + (size_t)sg * 4);
+        s0 = fmaf(w[4 % EPL], x1.x, s0); s0 = fmaf(w[5 % EPL], x1.y, s0);
+        s0 = fmaf(w[6 % EPL], x1.z, s0); s0 = fmaf(w[7 % EPL], x1.w, s0);
+      }
+      acc[m] = s0;
+    }
+    if (++cc == C) { cc = 0; flush(cr); ++cr; }
+  };
+  for (int t = t0; t < t1; t += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      plan_issue(p, slot[(r + RING - 1) % RING]);
+      if (t + r < t1) consume(slot[r]);
+    }
+  }
+  if (cc != 0) flush(cr);   // the wave's range ended inside a row
+}
+
 template <typename WT>
 __device__ __forceinline__ void gemv_body(Plan& p, u32x4 (&slot)[RING], const float* act, int act_ld, int M,
                                           float* red) {
-  constexpr int EPL = WTraits<WT>::EPL;
-  const int wave = tidx() >> 6, lane = tidx() & 63;
-  const int t0 = p.t0, t1 = p.t1;
-  if (t0 < t1) {
-    const int C = p.C, S = p.S, Kh = p.K >> 1;
-    int cr = t0 / C, cc = t0 - cr * C;
-    float acc[MMAX];
-#pragma unroll
-    for (int m = 0; m < MMAX; ++m) acc[m] = 0.0f;
-    auto flush = [&](int r) {
-#pragma unroll
-      for (int m = 0; m < MMAX; ++m) {
-        if (m < M) {
-          float v = wave_sum(acc[m]);
-          if (lane == 0) red[((size_t)r * NWAVE + wave) * MMAX + m] = v;
-        }
-        acc[m] = 0.0f;
-      }
-    };
-    auto consume = [&](const u32x4& q) {
-      const int seg = cc * 64 + lane;
-      if (seg < S) {
-        float w[EPL];
-        WTraits<WT>::unpack(make_uint4(q.x, q.y, q.z, q.w), w);
-#pragma unroll
-        for (int m = 0; m < MMAX; ++m) {
-          if (m < M) {
-            const float* row = act + (size_t)m * act_ld;
-            const float4 x0 = *reinterpret_cast<const float4*>(row + (size_t)seg * 4);
-            float s0 = acc[m];
-            s0 = fmaf(w[0], x0.x, s0); s0 = fmaf(w[1], x0.y, s0);
-            s0 = fmaf(w[2], x0.z, s0); s0 = fmaf(w[3], x0.w, s0);
-            if (EPL == 8) {
-              const float4 x1 = *reinterpret_cast<const float4*>(row + Kh + (size_t)seg * 4);
-              s0 = fmaf(w[4 % EPL], x1.x, s0); s0 = fmaf(w[5 % EPL], x1.y, s0);
-              s0 = fmaf(w[6 % EPL], x1.z, s0); s0 = fmaf(w[7 % EPL], x1.w, s0);
-            }
-            acc[m] = s0;
-          }
-        }
-      }
-      if (++cc == C) { cc = 0; flush(cr); ++cr; }
-    };
-    for (int t = t0; t < t1; t += RING) {
-#pragma unroll
-      for (int r = 0; r < RING; ++r) {
-        plan_issue(p, slot[(r + RING - 1) % RING]);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - 1));
-        asm volatile("" : "+v"(slot[r]));
-        if (t + r < t1) consume(slot[r]);
-      }
-    }
-    if (cc != 0) flush(cr);   // the wave's range ended inside a row
-  } else {
-    // no chunks: retire the prologue's dummies like the loop would
-#pragma unroll
-    for (int r = 0; r < RING; ++r) asm volatile("" : "+v"(slot[r]));
-  }
-  asm volatile("s_waitcnt vmcnt(0)");
-#pragma unroll
-  for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
+  if (M == 1) gemv_rows<WT, 1>(p, slot, act, act_ld, red);
+  else gemv_rows<WT, 2>(p, slot, act, act_ld, red);
 }
 
 __device__ __forceinline__ void zero_lds(float* p, int n) {
@@ -643,12 +677,13 @@ __device__ __forceinline__ Plan plan_for(const FrameArgs& a, int ph) {
 }
 
 template <typename WT>
-__device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl,
-                                          u32x4 (&slot)[RING]) {
+__device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
   const int D = a.dim;
   int r0, r1;
   split_rows(a.qkv_dim, blockIdx.x, gridDim.x, r0, r1);
-  stage_layer_input<WT, false>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].attn_norm));
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  stage_layer_input<WT, false>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].attn_norm), pro);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 4);
@@ -663,8 +698,7 @@ __device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int 
 }
 
 template <typename WT>
-__device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl,
-                                              u32x4 (&slot)[RING]) {
+__device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
   int g, r0, r1;
   wo_rows(a, g, r0, r1);
   const int rg = blockIdx.x / a.n_kv;
@@ -675,58 +709,70 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
   const float* kn = qn + hd;
   float* kvl = a.kv + (size_t)l * a.ctx_len * G * 2 * hd;   // [ctx][G][2][hd]
   const bool need_attn = (r1 > r0) || rg == 0;
-  if (need_attn) {
-    // one batched gather: cached keys/values of positions < first_new, then
-    // the new rows' raw q (this group's heads), k and v
-    {
-      const int hp = hd >> 1;
-      const int n_cache = first_new * 2 * hp;
-      const int n_row = (gh + 2) * hp;
-      const int total = n_cache + M * n_row;
-      // destinations as float offsets from s.q (q, kc and vc are carved
-      // in that order), so that the stores stay plain LDS stores
-      const int kc_off = (int)(s.kc - s.q), vc_off = (int)(s.vc - s.q);
-      for (int base = 0; base < total; base += NTHREADS * SB) {
-        u64 v[SB];
-        int dst[SB];
-#pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          const int i = base + j * NTHREADS + tidx();
-          v[j] = 0ull;
-          dst[j] = -1;
-          if (i < total) {
-            const float* src;
-            if (i < n_cache) {
-              const int jpos = i / (2 * hp), r = i - jpos * 2 * hp;     // r: pair inside [K | V]
-              const int kvsel = r / hp, pp = r - kvsel * hp;
-              src = kvl + (((size_t)jpos * G + g) * 2 + kvsel) * hd + 2 * pp;
-              dst[j] = (kvsel == 0 ? kc_off : vc_off) + jpos * hd + 2 * pp;
-            } else {
-              const int t = i - n_cache;
-              const int m = t / n_row, r = t - m * n_row;
-              const float* row = qkvb(a, step, l) + (size_t)m * a.qkv_dim;
-              const int pos = row_pos(step, m);
-              if (r < gh * hp) {
-                src = row + (size_t)g * gh * hd + 2 * r;
-                dst[j] = m * gh * hd + 2 * r;
-              } else if (r < (gh + 1) * hp) {
-                const int pp = r - gh * hp;
-                src = row + (size_t)H * hd + (size_t)g * hd + 2 * pp;
-                dst[j] = kc_off + pos * hd + 2 * pp;
-              } else {
-                const int pp = r - (gh + 1) * hp;
-                src = row + (size_t)(H + G) * hd + (size_t)g * hd + 2 * pp;
-                dst[j] = vc_off + pos * hd + 2 * pp;
-              }
-            }
-            v[j] = ld64(src);
-          }
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  {
+    // One gather of head vectors (segments of hd floats) into LDS: the cached
+    // keys of positions < first_new, their values, then per new row its gh
+    // raw query heads (this group's), its key and its value.  Nothing for a
+    // block without wo rows outside the first row group.  A wave takes
+    // segments wave, wave + NWAVE, ...; the segment arithmetic is
+    // wave-uniform and a lane moves one pair of floats.
+    constexpr int NS = 4;
+    const int F = first_new, hp = hd >> 1;
+    const int nseg = need_attn ? 2 * F + M * (gh + 2) : 0;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int lp = min(lane, hp - 1);
+    auto seg = [&](int sg, const float*& src, float*& dst) __attribute__((always_inline)) {
+      if (sg < F) {
+        src = kvl + ((size_t)(sg * G + g) * 2 + 0) * hd;
+        dst = s.kc + (size_t)sg * hd;
+      } else if (sg < 2 * F) {
+        src = kvl + ((size_t)((sg - F) * G + g) * 2 + 1) * hd;
+        dst = s.vc + (size_t)(sg - F) * hd;
+      } else {
+        const int t = sg - 2 * F;
+        const int m = t / (gh + 2), r = t - m * (gh + 2);
+        const float* row = qkvb(a, step, l) + (size_t)m * a.qkv_dim;
+        const int pos = row_pos(step, m);
+        if (r < gh) {
+          src = row + (size_t)(g * gh + r) * hd;
+          dst = s.q + (size_t)(m * gh + r) * hd;
+        } else if (r == gh) {
+          src = row + (size_t)(H + g) * hd;
+          dst = s.kc + (size_t)pos * hd;
+        } else {
+          src = row + (size_t)(H + G + g) * hd;
+          dst = s.vc + (size_t)pos * hd;
         }
-#pragma unroll
-        for (int j = 0; j < SB; ++j)
-          if (dst[j] >= 0) { s.q[dst[j]] = lo_f32(v[j]); s.q[dst[j] + 1] = hi_f32(v[j]); }
       }
-    }
+    };
+    auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
+      u64 v[NS];
+      float* dst[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        // a step past the end re-reads segment 0 (a valid row when nseg is 0)
+        const int sg = base + wv + NWAVE * j;
+        const float* src;
+        seg(sg < nseg ? sg : 0, src, dst[j]);
+        v[j] = ld64(src + 2 * lp);
+      }
+      after();
+      const int nj = steps_opaque(nseg, base, NWAVE);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        if (j >= nj) break;
+        if (base + wv + NWAVE * j < nseg && lane < hp) {
+          dst[j][2 * lane] = lo_f32(v[j]);
+          dst[j][2 * lane + 1] = hi_f32(v[j]);
+        }
+      }
+    };
+    batch(0, pro);
+    for (int base = NWAVE * NS; base < nseg; base += NWAVE * NS) batch(base, NoHook{});
+  }
+  if (need_attn) {
     __syncthreads();
     mark(a, s.flag[1], 4);
       // q/k RMSNorm + RoPE: one wave per head vector
@@ -826,13 +872,14 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
 }
 
 template <typename WT>
-__device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl,
-                                             u32x4 (&slot)[RING]) {
+__device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
   const int D = a.dim;
   int r0, r1;
   split_rows(a.ffn, blockIdx.x, gridDim.x, r0, r1);
   const int nr = r1 - r0;
-  stage_layer_input<WT, true>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm));
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  stage_layer_input<WT, true>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
   zero_lds(s.red, 2 * nr * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
@@ -847,11 +894,14 @@ __device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, i
 }
 
 template <typename WT>
-__device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl,
-                                               u32x4 (&slot)[RING]) {
+__device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
   int r0, r1;
   split_rows(a.dim, blockIdx.x, gridDim.x, r0, r1);
-  for (int m = 0; m < M; ++m) stage_arena<WT, true>(s.act + (size_t)m * a.kmax, gb(a, step, l) + (size_t)m * a.ffn, a.ffn);
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  stage_arena<WT, true, 5>(s.act, gb(a, step, l), a.ffn, pro);
+  for (int m = 1; m < M; ++m)
+    stage_arena<WT, true, 5>(s.act + (size_t)m * a.kmax, gb(a, step, l) + (size_t)m * a.ffn, a.ffn, NoHook{});
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
@@ -868,35 +918,41 @@ __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s,
 }
 
 template <typename WT>
-__device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int step, int M, Plan& pl,
-                                           u32x4 (&slot)[RING]) {
+__device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int step, int M, Plan& pl) {
   const int D = a.dim;
   int r0, r1;
   split_rows(a.V, blockIdx.x, gridDim.x, r0, r1);
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   {
     // last row of the final layer, times fast_norm (in LDS); the RMS divides the logits
+    constexpr int NS = 2;
     const float* src = xb(a, step, a.n_layer - 1) + (size_t)(M - 1) * D;
-    const int np = D >> 1;
+    const int nq = D >> 2;
     float ss = 0.0f;
-    for (int base = 0; base < np; base += NTHREADS * SB) {
-      u64 v[SB];
+    auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
+      v4f v[NS];
 #pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        const int i = base + j * NTHREADS + tidx();
-        v[j] = i < np ? ld64(src + 2 * i) : 0ull;
-      }
+      for (int j = 0; j < NS; ++j) v[j] = *reinterpret_cast<const v4f*>(src + 4 * quad_of(base, j, nq));
+      after();
+      const int nj = steps_opaque(nq, base);
 #pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        const int i = base + j * NTHREADS + tidx();
-        if (i < np) {
-          const float v0 = lo_f32(v[j]), v1 = hi_f32(v[j]);
-          ss = fmaf(v0, v0, fmaf(v1, v1, ss));
-          float* d = s.act + phys<WT>(2 * i, D);
-          d[0] = v0 * s.fnw[2 * i];
-          d[1] = v1 * s.fnw[2 * i + 1];
+      for (int j = 0; j < NS; ++j) {
+        if (j >= nj) break;
+        const int q = base + j * NTHREADS + tidx();
+        if (q < nq) {
+          v4f o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ss = fmaf(v[j][e], v[j][e], ss);
+            o[e] = v[j][e] * s.fnw[4 * q + e];
+          }
+          *reinterpret_cast<v4f*>(s.act + phys<WT>(4 * q, D)) = o;
         }
       }
-    }
+    };
+    batch(0, pro);
+    for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
     store_ss(s.small, 1, ss, 0.0f);
   }
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
@@ -914,9 +970,11 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
 }
 
 template <typename WT>
-__device__ __forceinline__ void phase_project_in(const FrameArgs& a, const Lds& s, Plan& pl, u32x4 (&slot)[RING]) {
+__device__ __forceinline__ void phase_project_in(const FrameArgs& a, const Lds& s, Plan& pl) {
   int r0, r1;
   split_rows(a.dim, blockIdx.x, gridDim.x, r0, r1);
+  u32x4 slot[RING];
+  gemv_prologue(pl, slot);
   for (int k = tidx(); k < a.in_dim; k += NTHREADS) s.act[phys<WT>(k, a.in_dim)] = a.hidden[k];
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
@@ -952,10 +1010,11 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
   for (int i = tidx(); i < a.ctx_len * a.hd; i += NTHREADS) s.rope[i] = a.rope[i];
   for (int i = tidx(); i < a.dim; i += NTHREADS) s.fnw[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(a.fnorm), i);
   __syncthreads();
-  u32x4 slot[RING];
   const int nph = phase_count(a);
+  // A phase's plan (row range and chunk split) is plain integers and is
+  // computed before the barrier that precedes the phase; its loads are
+  // issued only inside the phase.
   Plan pl = plan_for<WT>(a, 0);
-  gemv_prologue(pl, slot);
   for (int ph = 0; ph < nph; ++ph) {
     const PhaseId id = phase_id(a, ph);
     const int step = id.step, l = id.layer;
@@ -963,29 +1022,16 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
     if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     mark(a, epoch - a.epoch0, 5);
     switch (id.kind) {
-      case PH_PROJ: phase_project_in<WT>(a, s, pl, slot); break;
-      case PH_QKV: phase_qkv<WT>(a, s, l, step, M, pl, slot); break;
-      case PH_WO: phase_attn_wo<WT>(a, s, l, step, M, pl, slot); break;
-      case PH_FFN_UP: phase_ffn_up<WT>(a, s, l, step, M, pl, slot); break;
-      case PH_FFN_DOWN: phase_ffn_down<WT>(a, s, l, step, M, pl, slot); break;
-      default: phase_head<WT>(a, s, step, M, pl, slot); break;
+      case PH_PROJ: phase_project_in<WT>(a, s, pl); break;
+      case PH_QKV: phase_qkv<WT>(a, s, l, step, M, pl); break;
+      case PH_WO: phase_attn_wo<WT>(a, s, l, step, M, pl); break;
+      case PH_FFN_UP: phase_ffn_up<WT>(a, s, l, step, M, pl); break;
+      case PH_FFN_DOWN: phase_ffn_down<WT>(a, s, l, step, M, pl); break;
+      default: phase_head<WT>(a, s, step, M, pl); break;
     }
-    // The next phase's weight loads are issued only after the grid barrier:
-    // vmcnt retires in order, so loads issued before it would hold up the
-    // barrier's flag polls and the next phase's activation loads behind a
-    // full HBM round trip (measured slower than this order).
-    pl = (ph + 1 < nph) ? plan_for<WT>(a, ph + 1) : null_plan(a.outw);
-    asm volatile("" ::: "memory");
-    if (id.kind == PH_HEAD && a.forced) {           // teacher forcing: the next prefix is known
-      gemv_prologue(pl, slot);
-      continue;
-    }
-    if (!grid_sync(a, epoch, s.flag)) {
-      asm volatile("s_waitcnt vmcnt(0)");
-#pragma unroll
-      for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
-      return;
-    }
+    pl = plan_for<WT>(a, min(ph + 1, nph - 1));
+    if (id.kind == PH_HEAD && a.forced) continue;   // teacher forcing: the next prefix is known
+    if (!grid_sync(a, epoch, s.flag)) return;
     if (id.kind == PH_HEAD) {
       const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
       const int code = sample_request(logitsb(a, step), V, a.temp[0], a.top_p[0], a.top_k[0],
@@ -993,12 +1039,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
       if (tidx() == 0) s.codes[step] = min(max(code, 0), V - 1);
       __syncthreads();
     }
-    gemv_prologue(pl, slot);
   }
-  // the final prologue only loaded dummies
-  asm volatile("s_waitcnt vmcnt(0)");
-#pragma unroll
-  for (int j = 0; j < RING; ++j) asm volatile("" : "+v"(slot[j]));
   if (blockIdx.x == 0 && a.codes_out && tidx() < a.ncb) a.codes_out[tidx()] = s.codes[tidx()];
 }
 
@@ -1376,6 +1417,7 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
   if (!ctx) return S2FAST_ERR_ARG;
   if (B < 1 || B > ctx->cfg.max_batch) return S2FAST_ERR_BATCH;
   if (!hidden || !sem_code || !uniforms || !temperature || !top_p || !top_k || !codes) return S2FAST_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(hidden) & 15u) return S2FAST_ERR_ARG;   // read in 16-byte quads
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const s2fast_config& k = ctx->cfg;
   int rc = S2FAST_OK;
@@ -1423,6 +1465,7 @@ int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const
   if (!ctx) return S2FAST_ERR_ARG;
   if (B < 1 || B > ctx->cfg.max_batch) return S2FAST_ERR_BATCH;
   if (!hidden || !codes || !logits) return S2FAST_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(hidden) & 15u) return S2FAST_ERR_ARG;   // read in 16-byte quads
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const s2fast_config& k = ctx->cfg;
   if (B >= 2 && ctx->bq > 0) {

@@ -122,7 +122,8 @@ const char* s2fast_strerror(int code);
 
 /* Decode one frame for B requests ("Fast-AR codebook decoding ...", section
  * 5.1, step 3).
- *   hidden      [B, in_dim]  f32  Slow-AR hidden state (already normalised)
+ *   hidden      [B, in_dim]  f32  Slow-AR hidden state (already normalised);
+ *                                 16-byte aligned device memory
  *   sem_code    [B]          i32  main_token - semantic_begin; clamped on the
  *                                 device to [0, codebook_size-1] (section 5.2)
  *   uniforms    [B, num_codebooks-1] f32  one uniform in (0,1) per draw;
@@ -142,7 +143,7 @@ const char* s2fast_strerror(int code);
  *   u_j = (floor(splitmix64(bits(u) * 2^32 + j) / 2^40) + 0.5) * 2^-24;
  *   code = kept candidate maximising p_j / f32(-log(f64(u_j))).
  * Errors: S2FAST_ERR_BATCH for B outside [1, max_batch]; S2FAST_ERR_ARG for
- * NULL pointers.  If a launch fails after validation, codes[:, 1:] are
+ * NULL pointers or a hidden pointer that is not 16-byte aligned.  If a launch fails after validation, codes[:, 1:] are
  * zero-filled on `stream` (the main loop's "failed fast_decode fills the rest
  * of the frame with 0" convention, section 5.2) and S2FAST_ERR_HIP is
  * returned. */
@@ -154,7 +155,8 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
  * codes[:, 0..k-1] (codes[:, 0] is clamped like sem_code; the last column
  * is not read) and logits[:, k-1, :] receives the codebook_size logits of
  * that call.
- *   hidden [B, in_dim] f32; codes [B, num_codebooks] i32 (each in [0, V));
+ *   hidden [B, in_dim] f32, 16-byte aligned; codes [B, num_codebooks] i32
+ *   (each in [0, V));
  *   logits [B, num_codebooks-1, codebook_size] f32 OUT.
  * Out-of-range prefix codes are clamped to [0, V-1] on the device. */
 int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* codes,
