@@ -95,7 +95,7 @@ constexpr int GEMV_RING = 4;   // weight chunks in flight per wave
 // ---------------------------------------------------------------- LDS map
 struct Lds {
   float* act;    // [MMAX][kmax] GEMV activations (see phys())
-  float* red;    // [rmax][NWAVE][MMAX]
+  float* red;    // [rmax][MMAX][NWAVE] per-wave GEMV partials
   float* small;  // [64]: rms scratch, epilogue temporaries
   float* q;      // [MMAX][gheads][hd]
   float* kc;     // [ctx][hd]
@@ -176,9 +176,10 @@ __device__ __forceinline__ int steps_opaque(int n, int base, int width = NTHREAD
 }
 
 // rows [r0, r1) of an n-row matrix owned by part `j` of `parts`
+// (n * parts stays far below 2^32 for every matrix here)
 __device__ __forceinline__ void split_rows(int n, int j, int parts, int& r0, int& r1) {
-  r0 = (int)(((long long)n * j) / parts);
-  r1 = (int)(((long long)n * (j + 1)) / parts);
+  r0 = (int)(((unsigned)n * (unsigned)j) / (unsigned)parts);
+  r1 = (int)(((unsigned)n * (unsigned)(j + 1)) / (unsigned)parts);
 }
 
 // --------------------------------------------------------------- grid sync
@@ -355,7 +356,7 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int q = quad_of(base, j, nq);
-      const int m = q / hq, c = q - m * hq;
+      const int m = q >= hq ? 1 : 0, c = q - m * hq;   // M <= 2
       const int pos = row_pos(step, m);
       wv[j] = WQuad<WT>::load(normw, c);   // the RMSNorm weight, same round trip
       xv[j] = *reinterpret_cast<const v4f*>(fsrc + (size_t)m * fstride + 4 * c);
@@ -376,7 +377,7 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
       if (j >= nj) break;
       const int qu = base + j * NTHREADS + tidx();
       const int q = min(qu, nq - 1);
-      const int m = q / hq, c = q - m * hq;
+      const int m = q >= hq ? 1 : 0, c = q - m * hq;
       const bool emb = (l == 0 && row_pos(step, m) > 0);
       float v[4];
 #pragma unroll
@@ -437,6 +438,7 @@ struct Plan {
   int nr_a, nrows, K, S, C, t0, t1;
   int it, ir, ic;       // issue cursor
   const char* irow;
+  int r0, r1, g;        // the block's output rows [r0, r1) (and KV group for wo)
 };
 
 template <typename WT>
@@ -511,7 +513,7 @@ __device__ __forceinline__ void gemv_rows(Plan& p, u32x4 (&slot)[RING], const fl
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
       const float v = wave_sum(acc[m]);
-      if (lane == 0) red[((size_t)r * NWAVE + wave) * MMAX + m] = v;
+      if (lane == 0) red[((size_t)r * MMAX + m) * NWAVE + wave] = v;
       acc[m] = 0.0f;
     }
   };
@@ -561,11 +563,12 @@ __device__ __forceinline__ void zero_lds(float* p, int n) {
 }
 
 // sum of the per-wave partials of row r, activation row m
+static_assert(NWAVE == 8, "red_sum reads the wave partials as two float4");
 __device__ __forceinline__ float red_sum(const float* red, int r, int m) {
-  float v = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) v += red[((size_t)r * NWAVE + w) * MMAX + m];
-  return v;
+  // the NWAVE partials of (r, m) are contiguous: two 16-byte LDS reads
+  const float4* q = reinterpret_cast<const float4*>(red + ((size_t)r * MMAX + m) * NWAVE);
+  const float4 a = q[0], b = q[1];
+  return ((((((a.x + a.y) + a.z) + a.w) + b.x) + b.y) + b.z) + b.w;
 }
 
 // RMSNorm of M rows of K values held in LDS in GEMV layout, in place:
@@ -619,17 +622,28 @@ enum PhaseKind { PH_PROJ = 0, PH_QKV, PH_WO, PH_FFN_UP, PH_FFN_DOWN, PH_HEAD };
 
 struct PhaseId { int step, layer, kind; };
 
-__device__ __forceinline__ PhaseId phase_id(const FrameArgs& a, int ph) {
+// Phase order of a frame: [fast_project_in], then per decode step 1..ncb-1
+// the four phases of every layer and the output head.
+__device__ __forceinline__ PhaseId first_phase(const FrameArgs& a) {
   PhaseId id;
-  if (a.has_proj) {
-    if (ph == 0) { id.step = 0; id.layer = 0; id.kind = PH_PROJ; return id; }
-    --ph;
+  id.step = a.has_proj ? 0 : 1;
+  id.layer = 0;
+  id.kind = a.has_proj ? PH_PROJ : PH_QKV;
+  return id;
+}
+
+__device__ __forceinline__ PhaseId next_phase(const FrameArgs& a, PhaseId id) {
+  if (id.kind == PH_PROJ || id.kind == PH_HEAD) {
+    ++id.step;
+    id.layer = 0;
+    id.kind = PH_QKV;
+  } else if (id.kind == PH_FFN_DOWN) {
+    ++id.layer;
+    id.kind = (id.layer == a.n_layer) ? PH_HEAD : PH_QKV;
+    if (id.kind == PH_HEAD) id.layer = 0;
+  } else {
+    ++id.kind;
   }
-  const int per = 4 * a.n_layer + 1;
-  id.step = 1 + ph / per;
-  const int r = ph % per;
-  if (r == 4 * a.n_layer) { id.layer = 0; id.kind = PH_HEAD; }
-  else { id.layer = r >> 2; id.kind = PH_QKV + (r & 3); }
   return id;
 }
 
@@ -647,40 +661,47 @@ __device__ __forceinline__ void wo_rows(const FrameArgs& a, int& g, int& r0, int
 }
 
 template <typename WT>
-__device__ __forceinline__ Plan plan_for(const FrameArgs& a, int ph) {
-  const PhaseId id = phase_id(a, ph);
+__device__ __forceinline__ Plan plan_for(const FrameArgs& a, PhaseId id) {
   const int P = gridDim.x, b = blockIdx.x;
-  int r0, r1;
+  int r0, r1, g = 0;
   const LayerPtr& L = a.L[id.layer];
+  Plan p;
   switch (id.kind) {
     case PH_PROJ:
       split_rows(a.dim, b, P, r0, r1);
-      return make_plan<WT>((const WT*)a.proj, nullptr, a.in_dim, 0, a.in_dim, r0, r1 - r0, r1 - r0);
+      p = make_plan<WT>((const WT*)a.proj, nullptr, a.in_dim, 0, a.in_dim, r0, r1 - r0, r1 - r0);
+      break;
     case PH_QKV:
       split_rows(a.qkv_dim, b, P, r0, r1);
-      return make_plan<WT>((const WT*)L.wqkv, nullptr, a.dim, 0, a.dim, r0, r1 - r0, r1 - r0);
-    case PH_WO: {
-      int g;
+      p = make_plan<WT>((const WT*)L.wqkv, nullptr, a.dim, 0, a.dim, r0, r1 - r0, r1 - r0);
+      break;
+    case PH_WO:
       wo_rows(a, g, r0, r1);
-      return make_plan<WT>((const WT*)L.wo, nullptr, a.attn_dim, g * a.gw, a.gw, r0, r1 - r0, r1 - r0);
-    }
+      p = make_plan<WT>((const WT*)L.wo, nullptr, a.attn_dim, g * a.gw, a.gw, r0, r1 - r0, r1 - r0);
+      break;
     case PH_FFN_UP:
       split_rows(a.ffn, b, P, r0, r1);
-      return make_plan<WT>((const WT*)L.w1, (const WT*)L.w3, a.dim, 0, a.dim, r0, r1 - r0, 2 * (r1 - r0));
+      p = make_plan<WT>((const WT*)L.w1, (const WT*)L.w3, a.dim, 0, a.dim, r0, r1 - r0, 2 * (r1 - r0));
+      break;
     case PH_FFN_DOWN:
       split_rows(a.dim, b, P, r0, r1);
-      return make_plan<WT>((const WT*)L.w2, nullptr, a.ffn, 0, a.ffn, r0, r1 - r0, r1 - r0);
+      p = make_plan<WT>((const WT*)L.w2, nullptr, a.ffn, 0, a.ffn, r0, r1 - r0, r1 - r0);
+      break;
     default:
       split_rows(a.V, b, P, r0, r1);
-      return make_plan<WT>((const WT*)a.outw, nullptr, a.dim, 0, a.dim, r0, r1 - r0, r1 - r0);
+      p = make_plan<WT>((const WT*)a.outw, nullptr, a.dim, 0, a.dim, r0, r1 - r0, r1 - r0);
+      break;
   }
+  p.r0 = r0;
+  p.r1 = r1;
+  p.g = g;
+  return p;
 }
 
 template <typename WT>
 __device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
   const int D = a.dim;
-  int r0, r1;
-  split_rows(a.qkv_dim, blockIdx.x, gridDim.x, r0, r1);
+  const int r0 = pl.r0, r1 = pl.r1;
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   stage_layer_input<WT, false>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].attn_norm), pro);
@@ -699,8 +720,7 @@ __device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int 
 
 template <typename WT>
 __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
-  int g, r0, r1;
-  wo_rows(a, g, r0, r1);
+  const int g = pl.g, r0 = pl.r0, r1 = pl.r1;
   const int rg = blockIdx.x / a.n_kv;
   const int hd = a.hd, H = a.n_head, G = a.n_kv, gh = a.gheads;
   const int first_new = (step == 1) ? 0 : step;   // positions < first_new come from this frame's cache
@@ -732,7 +752,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
         dst = s.vc + (size_t)(sg - F) * hd;
       } else {
         const int t = sg - 2 * F;
-        const int m = t / (gh + 2), r = t - m * (gh + 2);
+        const int m = t >= gh + 2 ? 1 : 0, r = t - m * (gh + 2);   // M <= 2
         const float* row = qkvb(a, step, l) + (size_t)m * a.qkv_dim;
         const int pos = row_pos(step, m);
         if (r < gh) {
@@ -874,8 +894,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
 template <typename WT>
 __device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
   const int D = a.dim;
-  int r0, r1;
-  split_rows(a.ffn, blockIdx.x, gridDim.x, r0, r1);
+  const int r0 = pl.r0, r1 = pl.r1;
   const int nr = r1 - r0;
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
@@ -895,8 +914,7 @@ __device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, i
 
 template <typename WT>
 __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
-  int r0, r1;
-  split_rows(a.dim, blockIdx.x, gridDim.x, r0, r1);
+  const int r0 = pl.r0, r1 = pl.r1;
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   stage_arena<WT, true, 5>(s.act, gb(a, step, l), a.ffn, pro);
@@ -920,8 +938,7 @@ __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s,
 template <typename WT>
 __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int step, int M, Plan& pl) {
   const int D = a.dim;
-  int r0, r1;
-  split_rows(a.V, blockIdx.x, gridDim.x, r0, r1);
+  const int r0 = pl.r0, r1 = pl.r1;
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   {
@@ -971,8 +988,7 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
 
 template <typename WT>
 __device__ __forceinline__ void phase_project_in(const FrameArgs& a, const Lds& s, Plan& pl) {
-  int r0, r1;
-  split_rows(a.dim, blockIdx.x, gridDim.x, r0, r1);
+  const int r0 = pl.r0, r1 = pl.r1;
   u32x4 slot[RING];
   gemv_prologue(pl, slot);
   for (int k = tidx(); k < a.in_dim; k += NTHREADS) s.act[phys<WT>(k, a.in_dim)] = a.hidden[k];
@@ -1014,9 +1030,9 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
   // A phase's plan (row range and chunk split) is plain integers and is
   // computed before the barrier that precedes the phase; its loads are
   // issued only inside the phase.
-  Plan pl = plan_for<WT>(a, 0);
+  PhaseId id = first_phase(a);
+  Plan pl = plan_for<WT>(a, id);
   for (int ph = 0; ph < nph; ++ph) {
-    const PhaseId id = phase_id(a, ph);
     const int step = id.step, l = id.layer;
     const int M = (step == 1) ? 2 : 1;
     if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
@@ -1029,10 +1045,12 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
       case PH_FFN_DOWN: phase_ffn_down<WT>(a, s, l, step, M, pl); break;
       default: phase_head<WT>(a, s, step, M, pl); break;
     }
-    pl = plan_for<WT>(a, min(ph + 1, nph - 1));
-    if (id.kind == PH_HEAD && a.forced) continue;   // teacher forcing: the next prefix is known
+    const PhaseId done = id;
+    id = next_phase(a, id);
+    pl = plan_for<WT>(a, id);   // past the last phase: a plan that is never used
+    if (done.kind == PH_HEAD && a.forced) continue;   // teacher forcing: the next prefix is known
     if (!grid_sync(a, epoch, s.flag)) return;
-    if (id.kind == PH_HEAD) {
+    if (done.kind == PH_HEAD) {
       const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
       const int code = sample_request(logitsb(a, step), V, a.temp[0], a.top_p[0], a.top_k[0],
                                       a.uniforms[step - 1], sc);
