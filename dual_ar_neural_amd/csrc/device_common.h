@@ -110,6 +110,32 @@ constexpr int DPP_QUAD_2301 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 constexpr int DPP_ROW_MIRROR = 0x140;
 
+// Value of lane (lane ^ J) for a constant J, without the LDS crossbar where
+// the lane pattern allows: J = 1, 2 are quad permutations; J = 4, 8 stay
+// inside a 16-lane row, so the lane takes the row shift by J in the direction
+// of its partner (row_shl: lane + J, row_shr: lane - J); J = 16 is a swizzle
+// (xor mask inside 32-lane halves); J = 32 goes through ds_bpermute.
+template <int J>
+__device__ __forceinline__ int xor_lane(int v, int lane) {
+  if constexpr (J == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);
+  } else if constexpr (J == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);
+  } else if constexpr (J == 4 || J == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x100 + J, 0xF, 0xF, true);   // row_shl:J
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x110 + J, 0xF, 0xF, true);   // row_shr:J
+    return (lane & J) ? dn : up;
+  } else if constexpr (J == 16) {
+    return __builtin_amdgcn_ds_swizzle(v, (0x10 << 10) | 0x1F);   // bitmask mode: xor 16, and 31
+  } else {
+    return __shfl_xor(v, J, 64);
+  }
+}
+template <int J>
+__device__ __forceinline__ float xor_lane_f(float v, int lane) {
+  return __int_as_float(xor_lane<J>(__float_as_int(v), lane));
+}
+
 __device__ __forceinline__ float readlane_f(float v, int j) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
 }

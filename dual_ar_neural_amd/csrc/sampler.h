@@ -20,32 +20,49 @@ __device__ __forceinline__ bool key_before(float v, int i, float w, int k) {
   return v > w || (v == w && i < k);
 }
 
+// One compare-exchange step of the bitonic network: partner lane ^ J,
+// this lane's k-block sorted first to last when (lane & K) == 0.
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step(float& v, int& i, int lane) {
+  const float ov = xor_lane_f<J>(v, lane);
+  const int oi = xor_lane<J>(i, lane);
+  const bool up = (lane & K) == 0;
+  const bool lower = (lane & J) == 0;     // this lane holds the lower position of the pair
+  const bool mine_first = key_before(v, i, ov, oi);
+  const bool keep_mine = (lower == up) ? mine_first : !mine_first;
+  v = keep_mine ? v : ov;
+  i = keep_mine ? i : oi;
+}
+
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge(float& v, int& i, int lane) {
+  bitonic_step<K, J>(v, i, lane);
+  if constexpr (J > 1) bitonic_merge<K, J / 2>(v, i, lane);
+}
+
+template <int K>
+__device__ __forceinline__ void bitonic_sort(float& v, int& i, int lane) {
+  if constexpr (K > 2) bitonic_sort<K / 2>(v, i, lane);
+  bitonic_merge<K, K / 2>(v, i, lane);
+}
+
 // Bitonic sort of one (value, index) pair per lane into rank order
 // (lane 0 = first).
-__device__ __forceinline__ void wave_sort_desc(float& v, int& i, int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      float ov = __shfl_xor(v, j, 64);
-      int oi = __shfl_xor(i, j, 64);
-      bool up = (lane & k) == 0;          // this k-block is sorted "first to last"
-      bool lower = (lane & j) == 0;       // this lane holds the lower position of the pair
-      bool mine_first = key_before(v, i, ov, oi);
-      bool keep_mine = (lower == up) ? mine_first : !mine_first;
-      if (!keep_mine) { v = ov; i = oi; }
-    }
-  }
+__device__ __forceinline__ void wave_sort_desc(float& v, int& i, int lane) { bitonic_sort<64>(v, i, lane); }
+
+template <int O>
+__device__ __forceinline__ void best_step(float& v, int& i, int lane) {
+  const float ov = xor_lane_f<O>(v, lane);
+  const int oi = xor_lane<O>(i, lane);
+  if (key_before(ov, oi, v, i)) { v = ov; i = oi; }
+  if constexpr (O > 1) best_step<O / 2>(v, i, lane);
 }
 
 // Wave-wide argmax by (value desc, index asc); returns the winner in all lanes.
 __device__ __forceinline__ void wave_best(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o, 64);
-    int oi = __shfl_xor(i, o, 64);
-    if (key_before(ov, oi, v, i)) { v = ov; i = oi; }
-  }
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  best_step<32>(v, i, lane);
 }
 
 // ----------------------------------------------------------------- block
@@ -141,7 +158,13 @@ __device__ __forceinline__ int sample_block(const float* L, int V, float T, floa
   float lo = mn, hi = mx;
   int cnt = V;
   const bool finite = __builtin_isfinite(lo) && __builtin_isfinite(hi);
+  // Per-wave counts of the values >= lo, when the round that set lo left
+  // them in a buffer no later round has overwritten (rounds alternate two
+  // buffers): the compaction below then needs no counting pass of its own.
+  const int* lo_counts = nullptr;
+  int lo_j = 0, lo_round = -2, last_round = -1;
   for (int r = 0; r < SAMP_ROUNDS && finite && cnt > TOPK_MAX; ++r) {
+    last_round = r;
     const float d = hi - lo;
     int* rb = sc.red + buf * (NWAVE * SAMP_TAU);
 #pragma unroll
@@ -165,20 +188,26 @@ __device__ __forceinline__ int sample_block(const float* L, int V, float T, floa
     const float nhi = (jb + 1 < SAMP_TAU) ? samp_tau(lo, d, jb + 1) : hi;
     const int ncnt = jb ? __builtin_amdgcn_readlane(tot, jb) : cnt;
     if (!(nlo > lo) && !(nhi < hi)) break;                 // the interval no longer shrinks
+    if (jb) { lo_counts = rb; lo_j = jb; lo_round = r; }
     lo = nlo; hi = nhi; cnt = ncnt;
   }
+  if (last_round - lo_round > 1) lo_counts = nullptr;
 
   float cv = -INFINITY; int ci = BIG;                   // wave 0: lane j = rank j
   if (cnt <= TOPK_MAX) {
     // 3a. compact the cnt values >= lo into LDS, then sort them in wave 0
-    int* rb = sc.red + buf * (NWAVE * SAMP_TAU);
-    int wc = 0;
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) wc += __popcll(__ballot(x[j] >= lo));
-    if (lane == 0) rb[w] = wc;
-    __syncthreads();
     int off = 0;
-    for (int k = 0; k < w; ++k) off += rb[k];
+    if (lo_counts) {
+      for (int k = 0; k < w; ++k) off += lo_counts[k * SAMP_TAU + lo_j];
+    } else {
+      int* rb = sc.red + buf * (NWAVE * SAMP_TAU);
+      int wc = 0;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) wc += __popcll(__ballot(x[j] >= lo));
+      if (lane == 0) rb[w] = wc;
+      __syncthreads();
+      for (int k = 0; k < w; ++k) off += rb[k];
+    }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const u64 b = __ballot(x[j] >= lo);
@@ -221,13 +250,18 @@ __device__ __forceinline__ int sample_block(const float* L, int V, float T, floa
   const float z0 = readlane_f(z, 0);
   const float dz = z - z0;
   const float e = act ? (float)exp((double)dz) : 0.0f;
+  // Sequential f32 sums in rank order, unrolled over all 64 lanes: e and p
+  // are exactly 0 past rank n-1, and adding +0 to a non-negative sum leaves
+  // it bit-identical, so the chains equal the n-term ones.
   float S = 0.0f;
-  for (int j = 0; j < n; ++j) S += readlane_f(e, j);
+#pragma unroll
+  for (int j = 0; j < TOPK_MAX; ++j) S += readlane_f(e, j);
   const float p = act ? e / S : 0.0f;
   float c = 0.0f, my_c = 0.0f;
-  for (int j = 0; j < n; ++j) {
+#pragma unroll
+  for (int j = 0; j < TOPK_MAX; ++j) {
     c += readlane_f(p, j);
-    if (lane == j) my_c = c;
+    my_c = (lane == j) ? c : my_c;
   }
   const u64 ge = __ballot(act && my_c >= top_p);
   const int m = ge ? (__ffsll((long long)ge) - 1) : (n - 1);
