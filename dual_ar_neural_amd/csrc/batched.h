@@ -163,49 +163,59 @@ template <> struct MF<float> {
   static constexpr int FRAG = 1024;
 };
 
-// round-to-nearest-even float -> bf16 bits, and the exact float of a bf16
-__device__ __forceinline__ u32 bf16_rne(float f) {
-  const u32 u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// two floats -> two bf16 (round to nearest even), a in the low half
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32 bf16_pair(float a, float b) {
+  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  u32 u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
 }
 
-// GE source values of row m at column k (k a multiple of GE, in range)
+// GE source values of row m at column k (k a multiple of GE; row and column
+// in range).  The loads are unconditional: the phase kind is uniform (scalar
+// branches), and at layer 0 the float32 row and the embedding row are both
+// read and one is selected, so no load sits behind a per-lane branch.
 template <typename WT>
 __device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int m, int k,
                                         float (&v)[8]) {
   constexpr int GE = MF<WT>::GE;
-  const float* src = nullptr;
-  const WT* esrc = nullptr;
+  const float* src;
   switch (gd.kind) {
     case BK_PROJ: src = a.hidden + (size_t)m * a.in_dim; break;
     case BK_QKV:
       if (gd.l > 0) src = bx(a, gd.step, gd.l - 1) + (size_t)m * a.dim;
-      else if (s.rcode[m] < 0) src = a.has_proj ? a.xin0 + (size_t)(m % a.Bq) * a.dim : a.hidden + (size_t)(m % a.Bq) * a.in_dim;
-      else esrc = reinterpret_cast<const WT*>(a.emb) + (size_t)s.rcode[m] * a.dim;
+      else src = a.has_proj ? a.xin0 + (size_t)(m % a.Bq) * a.dim : a.hidden + (size_t)(m % a.Bq) * a.in_dim;
       break;
     case BK_WO: src = batt(a, gd.step, gd.l) + (size_t)m * a.attn_dim; break;
     case BK_UP: src = bxmid(a, gd.step, gd.l) + (size_t)m * a.dim; break;
     case BK_DOWN: src = bg(a, gd.step, gd.l) + (size_t)m * a.ffn; break;
     default: src = bx(a, gd.step, a.n_layer - 1) + (size_t)b_last_row(a, gd.step, m) * a.dim; break;
   }
-  if (esrc) {
+  const float4 q0 = *reinterpret_cast<const float4*>(src + k);
+  v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+  if (GE == 8) {
+    const float4 q1 = *reinterpret_cast<const float4*>(src + k + 4);
+    v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+  }
+  if (gd.kind == BK_QKV && gd.l == 0) {
+    // rows at window positions >= 1 take fast_embeddings[code] instead
+    const int c = s.rcode[m];
+    const WT* e = reinterpret_cast<const WT*>(a.emb) + (size_t)max(c, 0) * a.dim;
+    float ev[8];
     if (GE == 8) {
-      const uint4 q = *reinterpret_cast<const uint4*>(esrc + k);
-      v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
-      v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
-      v[4] = __uint_as_float(q.z << 16); v[5] = __uint_as_float(q.z & 0xFFFF0000u);
-      v[6] = __uint_as_float(q.w << 16); v[7] = __uint_as_float(q.w & 0xFFFF0000u);
+      const uint4 q = *reinterpret_cast<const uint4*>(e + k);
+      ev[0] = __uint_as_float(q.x << 16); ev[1] = __uint_as_float(q.x & 0xFFFF0000u);
+      ev[2] = __uint_as_float(q.y << 16); ev[3] = __uint_as_float(q.y & 0xFFFF0000u);
+      ev[4] = __uint_as_float(q.z << 16); ev[5] = __uint_as_float(q.z & 0xFFFF0000u);
+      ev[6] = __uint_as_float(q.w << 16); ev[7] = __uint_as_float(q.w & 0xFFFF0000u);
     } else {
-      const float4 q = *reinterpret_cast<const float4*>(esrc + k);
-      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+      const float4 q = *reinterpret_cast<const float4*>(e + k);
+      ev[0] = q.x; ev[1] = q.y; ev[2] = q.z; ev[3] = q.w;
     }
-  } else {
-    const float4 q0 = *reinterpret_cast<const float4*>(src + k);
-    v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
-    if (GE == 8) {
-      const float4 q1 = *reinterpret_cast<const float4*>(src + k + 4);
-      v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
-    }
+#pragma unroll
+    for (int t = 0; t < GE; ++t) v[t] = c >= 0 ? ev[t] : v[t];
   }
 }
 
@@ -236,44 +246,56 @@ __device__ __forceinline__ void b_stage(const BatchArgs& a, const BLds& s, const
   constexpr int SBS = sbs<WT>();
   const int n_items = Mp * KSM * 4;            // multiple of NSTAGE * SBS
   const int lo_off = KSM * MT * 1024;
+  const int msh = Mp == 16 ? 4 : 5;             // i / Mp
   for (int base = 0; base < n_items; base += NSTAGE * SBS) {
     float v[SBS][8];
     bool ok[SBS];
 #pragma unroll
     for (int j = 0; j < SBS; ++j) {
       const int i = base + j * NSTAGE + st;
-      const int k = k0 + (i / Mp) * GE;
+      const int k = k0 + (i >> msh) * GE;
       ok[j] = i < n_items && m < gd.M && k < gd.K;
-      if (ok[j]) b_fetch<WT>(a, s, gd, m, k, v[j]);
+      b_fetch<WT>(a, s, gd, m < gd.M ? m : 0, ok[j] ? k : 0, v[j]);   // in bounds; zeroed below if not ok
     }
 #pragma unroll
     for (int j = 0; j < SBS; ++j) {
       const int i = base + j * NSTAGE + st;
       if (i >= n_items) continue;
-      const int kg = i / Mp;
+      const int kg = i >> msh;
       const int sl = kg >> 2, q = kg & 3;
       const int idx = ((sl * MT + (m >> 4)) * 64 + q * 16 + (m & 15)) * 16;
       const int k = k0 + kg * GE;
       float x[8];
+      float w[8];
+      if (gd.normw) {                              // uniform: the phase's RMSNorm weight, from LDS
+        const int kk = ok[j] ? k : 0;
+        const float4 w0 = *reinterpret_cast<const float4*>(s.nw + kk);
+        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+        if (GE == 8) {
+          const float4 w1 = *reinterpret_cast<const float4*>(s.nw + kk + 4);
+          w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[e] = 0.0f;
         if (e < GE && ok[j]) {
-          if (gd.normw) { ss = fmaf(v[j][e], v[j][e], ss); x[e] = v[j][e] * s.nw[k + e]; }
+          if (gd.normw) { ss = fmaf(v[j][e], v[j][e], ss); x[e] = v[j][e] * w[e]; }
           else x[e] = v[j][e];
         }
       }
       if (GE == 8) {
-        u32 h[8], lw[8];
+        // x = hi + lo with hi = bf16(x), lo = bf16(x - hi), both round to
+        // nearest even (the packed hardware conversion)
+        u32 h[4], lw[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          h[e] = bf16_rne(x[e]);
-          lw[e] = bf16_rne(x[e] - __uint_as_float(h[e] << 16));
+        for (int p = 0; p < 4; ++p) {
+          h[p] = bf16_pair(x[2 * p], x[2 * p + 1]);
+          lw[p] = bf16_pair(x[2 * p] - __uint_as_float(h[p] << 16),
+                            x[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u));
         }
-        *reinterpret_cast<uint4*>(buf + idx) =
-            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-        *reinterpret_cast<uint4*>(buf + lo_off + idx) =
-            make_uint4(lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16), lw[4] | (lw[5] << 16), lw[6] | (lw[7] << 16));
+        *reinterpret_cast<uint4*>(buf + idx) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(buf + lo_off + idx) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       } else {
         *reinterpret_cast<float4*>(buf + idx) = make_float4(x[0], x[1], x[2], x[3]);
       }
