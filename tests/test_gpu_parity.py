@@ -206,6 +206,25 @@ def test_two_groups_with_project_in():
     pair.ctx.close()
 
 
+def test_s2pro_b64_bench_config():
+    """The batch-64 workload as bench.py times it (four launches of 16, with
+    fast_project_in, half greedy): codes of one request at each group edge
+    and teacher-forced logits of two requests against the oracle."""
+    w = si.WORKLOADS["s2pro_b64"]
+    pair = pr.make_pair(w.shape, w.seed(0), max_batch=64)
+    fr = _frames(w, 1, 64)
+    codes = pr.gpu_decode(pair, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
+                          fr["top_p"], fr["top_k"])
+    assert codes.shape == (64, w.shape.num_codebooks)
+    pick = [0, 15, 16, 31, 32, 47, 48, 63]
+    excused = pr.check_codes(pair, fr["hidden"][0][pick], fr["sem_code"][0][pick], fr["uniforms"][0][pick],
+                             fr["temperature"][pick], fr["top_p"][pick], fr["top_k"][pick], codes[pick])
+    worst, rel, _, _ = pr.check_logits(pair, fr["hidden"][0][[31, 48]], codes[[31, 48]])
+    _announce(f"s2pro B=64: excused {excused}; logits worst {worst:.2e}, rel {rel:.2e}")
+    assert worst <= 1.0 and rel < 1e-3, (worst, rel)
+    pair.ctx.close()
+
+
 def test_tiny_f32_batched_groups():
     """float32 weights (float32 MFMA path), B = 20 = 16 + 4, mixed settings."""
     w = si.WORKLOADS["tiny"]
