@@ -229,7 +229,7 @@ constexpr int NSTAGE = NTHREADS;                // threads staging X
 constexpr int XBUF = XF_BYTES;                  // one X buffer
 // staging items in flight per thread (bf16: 4 items of 8 columns; more
 // spills registers next to the MFMA accumulators)
-template <typename WT> constexpr int sbs() { return MF<WT>::GE == 8 ? 4 : 8; }
+template <typename WT> constexpr int sbs() { return MF<WT>::GE == 8 ? 8 : 8; }
 
 // Stage K-tile `tau` of X (columns [tau*KSM*KSZ, ...)) into buffer `buf` as
 // MFMA B fragments: lane (q, j) of k-step s and M-tile mt holds
@@ -458,7 +458,7 @@ template <typename WT>
 __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, const GemmDesc& gd) {
   constexpr int KSZ = MF<WT>::KSZ;
   const int tid = tidx();
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave-uniform work split
   const int Mp = gd.M <= 16 ? 16 : 32, MT = Mp >> 4;
   BGeom G;
   G.T = (gd.R + 15) >> 4;

@@ -729,6 +729,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
   const float* kn = qn + hd;
   float* kvl = a.kv + (size_t)l * a.ctx_len * G * 2 * hd;   // [ctx][G][2][hd]
   const bool need_attn = (r1 > r0) || rg == 0;
+  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);   // the GEMV's partial sums (read after the barriers below)
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   {
@@ -864,22 +865,24 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
       const float den = (readlane_f(es, 0) + readlane_f(es, 16)) + (readlane_f(es, 32) + readlane_f(es, 48));
       // output: lanes over head dims; all 16 positions are read, masked
       // ones with weight 0
+      // (the weights' normalisation is applied once to the output)
       const int c0 = min(lane, hd - 1), c1 = min(lane + 64, hd - 1);
       float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float* vr = s.vc + (size_t)min(j, pos) * hd;
-        const float pj = readlane_f(e4[j >> 2], (j & 3) * 16) / den;   // 0 past pos
-        o0 = fmaf(pj, vr[c0], o0);
-        o1 = fmaf(pj, vr[c1], o1);
+        const float ej = readlane_f(e4[j >> 2], (j & 3) * 16);   // 0 past pos
+        o0 = fmaf(ej, vr[c0], o0);
+        o1 = fmaf(ej, vr[c1], o1);
       }
+      o0 /= den;
+      o1 /= den;
       float* o = s.act + (size_t)m * a.kmax;
       if (lane < hd) o[phys<WT>(hh * hd + lane, a.gw)] = o0;
       if (lane + 64 < hd) o[phys<WT>(hh * hd + lane + 64, a.gw)] = o1;
     }
     mark(a, s.flag[1], 7);
   }
-  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
