@@ -219,93 +219,108 @@ __device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const
   }
 }
 
-// All eight waves stage a K-tile of X, then all eight stream the weights
-// against it.  (Staging on a few dedicated waves while the others stream was
-// measured slower: with the weight streams running, the staging loads -- data
-// written by other XCDs, so L2 misses -- wait much longer in the memory
-// queues.)
+// X is staged K-tile by K-tile into two alternating LDS buffers.  Every
+// thread stages the same share of each tile; the loads of tile tau+1 are
+// issued before tile tau's weight stream starts and converted into the other
+// buffer after it, so only the first tile's staging is exposed.  (Staging on
+// a few dedicated waves while the others stream was measured slower: with
+// the weight streams running, the staging loads -- data written by other
+// XCDs, so L2 misses -- wait much longer in the memory queues.)
 constexpr int NWC = NWAVE;                      // waves running the MFMAs
 constexpr int NSTAGE = NTHREADS;                // threads staging X
-constexpr int XBUF = XF_BYTES;                  // one X buffer
-// staging items in flight per thread (bf16: 4 items of 8 columns; more
-// spills registers next to the MFMA accumulators)
-template <typename WT> constexpr int sbs() { return MF<WT>::GE == 8 ? 8 : 8; }
+constexpr int XBUF = XF_BYTES / 2;              // one of the two X buffers
+// staging items per thread and K-tile (a buffer holds 2048 (bf16 hi + lo) or
+// 4096 (f32) items of GE columns at either M-tile count)
+template <typename WT> constexpr int sbs() { return MF<WT>::GE == 8 ? 4 : 8; }
 
-// Stage K-tile `tau` of X (columns [tau*KSM*KSZ, ...)) into buffer `buf` as
-// MFMA B fragments: lane (q, j) of k-step s and M-tile mt holds
-// X[16 mt + j][k0 + s KSZ + GE q .. + GE) (bf16: high halves, then low halves
-// in the second half of the buffer).  Staging thread st always handles row
-// m = st % Mp, so its running sum of squares (normed phases) covers one row
-// in a fixed order.
+// One thread's share of K-tile `tau` of X (columns [tau*KSM*KSZ, ...)):
+// items i = j * NSTAGE + st of GE columns of row m = st % Mp, so that a
+// thread's running sum of squares (normed phases) covers one row in a fixed
+// order.
 template <typename WT>
-__device__ __forceinline__ void b_stage(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int tau, int KSM,
-                                        int Mp, int MT, char* buf, int st, float& ss) {
-  constexpr int GE = MF<WT>::GE, KSZ = MF<WT>::KSZ;
+struct StageRegs {
+  float v[sbs<WT>()][8];
+  bool ok[sbs<WT>()];
+};
+
+template <typename WT>
+__device__ __forceinline__ void b_stage_load(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int tau, int KSM,
+                                             int Mp, int st, StageRegs<WT>& r) {
+  constexpr int GE = MF<WT>::GE, KSZ = MF<WT>::KSZ, SBS = sbs<WT>();
   const int m = st % Mp;
   const int k0 = tau * KSM * KSZ;
-  constexpr int SBS = sbs<WT>();
-  const int n_items = Mp * KSM * 4;            // multiple of NSTAGE * SBS
-  const int lo_off = KSM * MT * 1024;
   const int msh = Mp == 16 ? 4 : 5;             // i / Mp
-  for (int base = 0; base < n_items; base += NSTAGE * SBS) {
-    float v[SBS][8];
-    bool ok[SBS];
 #pragma unroll
-    for (int j = 0; j < SBS; ++j) {
-      const int i = base + j * NSTAGE + st;
-      const int k = k0 + (i >> msh) * GE;
-      ok[j] = i < n_items && m < gd.M && k < gd.K;
-      b_fetch<WT>(a, s, gd, m < gd.M ? m : 0, ok[j] ? k : 0, v[j]);   // in bounds; zeroed below if not ok
+  for (int j = 0; j < SBS; ++j) {
+    const int i = j * NSTAGE + st;
+    const int k = k0 + (i >> msh) * GE;
+    r.ok[j] = m < gd.M && k < gd.K;
+    b_fetch<WT>(a, s, gd, m < gd.M ? m : 0, r.ok[j] ? k : 0, r.v[j]);   // in bounds; zeroed below if not ok
+  }
+}
+
+// ... and its conversion into buffer `buf` as MFMA B fragments: lane (q, j)
+// of k-step s and M-tile mt holds X[16 mt + j][k0 + s KSZ + GE q .. + GE)
+// (bf16: high halves, then low halves in the second half of the buffer).
+template <typename WT>
+__device__ __forceinline__ void b_stage_store(const BLds& s, const GemmDesc& gd, int tau, int KSM, int Mp, int MT,
+                                              char* buf, int st, const StageRegs<WT>& r, float& ss) {
+  constexpr int GE = MF<WT>::GE, KSZ = MF<WT>::KSZ, SBS = sbs<WT>();
+  const int m = st % Mp;
+  const int k0 = tau * KSM * KSZ;
+  const int lo_off = KSM * MT * 1024;
+  const int msh = Mp == 16 ? 4 : 5;
+#pragma unroll
+  for (int j = 0; j < SBS; ++j) {
+    const int i = j * NSTAGE + st;
+    const int kg = i >> msh;
+    const int sl = kg >> 2, q = kg & 3;
+    const int idx = ((sl * MT + (m >> 4)) * 64 + q * 16 + (m & 15)) * 16;
+    const int k = k0 + kg * GE;
+    float x[8];
+    float w[8];
+    if (gd.normw) {                              // uniform: the phase's RMSNorm weight, from LDS
+      const int kk = r.ok[j] ? k : 0;
+      const float4 w0 = *reinterpret_cast<const float4*>(s.nw + kk);
+      w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+      if (GE == 8) {
+        const float4 w1 = *reinterpret_cast<const float4*>(s.nw + kk + 4);
+        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+      }
     }
 #pragma unroll
-    for (int j = 0; j < SBS; ++j) {
-      const int i = base + j * NSTAGE + st;
-      if (i >= n_items) continue;
-      const int kg = i >> msh;
-      const int sl = kg >> 2, q = kg & 3;
-      const int idx = ((sl * MT + (m >> 4)) * 64 + q * 16 + (m & 15)) * 16;
-      const int k = k0 + kg * GE;
-      float x[8];
-      float w[8];
-      if (gd.normw) {                              // uniform: the phase's RMSNorm weight, from LDS
-        const int kk = ok[j] ? k : 0;
-        const float4 w0 = *reinterpret_cast<const float4*>(s.nw + kk);
-        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-        if (GE == 8) {
-          const float4 w1 = *reinterpret_cast<const float4*>(s.nw + kk + 4);
-          w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
-        }
+    for (int e = 0; e < 8; ++e) {
+      x[e] = 0.0f;
+      if (e < GE && r.ok[j]) {
+        if (gd.normw) { ss = fmaf(r.v[j][e], r.v[j][e], ss); x[e] = r.v[j][e] * w[e]; }
+        else x[e] = r.v[j][e];
       }
+    }
+    if (GE == 8) {
+      // x = hi + lo with hi = bf16(x), lo = bf16(x - hi), both round to
+      // nearest even (the packed hardware conversion)
+      u32 h[4], lw[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = 0.0f;
-        if (e < GE && ok[j]) {
-          if (gd.normw) { ss = fmaf(v[j][e], v[j][e], ss); x[e] = v[j][e] * w[e]; }
-          else x[e] = v[j][e];
-        }
+      for (int p = 0; p < 4; ++p) {
+        h[p] = bf16_pair(x[2 * p], x[2 * p + 1]);
+        lw[p] = bf16_pair(x[2 * p] - __uint_as_float(h[p] << 16), x[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u));
       }
-      if (GE == 8) {
-        // x = hi + lo with hi = bf16(x), lo = bf16(x - hi), both round to
-        // nearest even (the packed hardware conversion)
-        u32 h[4], lw[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          h[p] = bf16_pair(x[2 * p], x[2 * p + 1]);
-          lw[p] = bf16_pair(x[2 * p] - __uint_as_float(h[p] << 16),
-                            x[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u));
-        }
-        *reinterpret_cast<uint4*>(buf + idx) = make_uint4(h[0], h[1], h[2], h[3]);
-        *reinterpret_cast<uint4*>(buf + lo_off + idx) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      } else {
-        *reinterpret_cast<float4*>(buf + idx) = make_float4(x[0], x[1], x[2], x[3]);
-      }
+      *reinterpret_cast<uint4*>(buf + idx) = make_uint4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<uint4*>(buf + lo_off + idx) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else {
+      *reinterpret_cast<float4*>(buf + idx) = make_float4(x[0], x[1], x[2], x[3]);
     }
   }
 }
 
+// Weight fragments in flight per compute wave (a deeper ring measured
+// slower: the K-tile time is set by the tile's staging and barrier, not by
+// the weight stream's latency).
+constexpr int BRING = RING;
+
 // Work of compute wave w in K-tile tau: the tile's (k-step, row tile) pairs
 // i = sl * T + t taken round robin, i = w, w + NWC, ...; the list is padded to
-// a multiple of RING (padding issues dummy loads) so that the register ring
+// a multiple of BRING (padding issues dummy loads) so that the register ring
 // is in phase at every K-tile boundary.
 struct BIter {
   int tau, j;
@@ -318,7 +333,7 @@ struct BGeom {
     const int n = T * ks - w;
     return n > 0 ? (n + NWC - 1) / NWC : 0;
   }
-  __device__ __forceinline__ int n_pad(int tau, int w) const { return (n_real(tau, w) + RING - 1) / RING * RING; }
+  __device__ __forceinline__ int n_pad(int tau, int w) const { return (n_real(tau, w) + BRING - 1) / BRING * BRING; }
 };
 
 template <typename WT>
@@ -412,31 +427,37 @@ __device__ __forceinline__ void b_compute(const BatchArgs& a, const BLds& s, con
   BIter it{0, 0};
   while (it.tau < G.NT && G.n_pad(it.tau, wave) == 0) ++it.tau;
   if (!has_rows) it.tau = G.NT;
-  u32x4 slot[RING];
+  u32x4 slot[BRING];
 #pragma unroll
-  for (int j = 0; j < RING - 1; ++j) b_issue<WT>(gd, G, it, wave, lane, slot[j]);
+  for (int j = 0; j < BRING - 1; ++j) b_issue<WT>(gd, G, it, wave, lane, slot[j]);
   mark(a, s.flag[1], 2);
+  StageRegs<WT> sr;
+  b_stage_load<WT>(a, s, gd, 0, G.KSM, Mp, tidx(), sr);
+  b_stage_store<WT>(s, gd, 0, G.KSM, Mp, MT, s.xf, tidx(), sr, ss);
+  __syncthreads();
+  mark(a, s.flag[1], 3);
   for (int tau = 0; tau < G.NT; ++tau) {
-    if (tau > 0) __syncthreads();                       // every wave is done with tile tau-1
-    b_stage<WT>(a, s, gd, tau, G.KSM, Mp, MT, s.xf, tidx(), ss);
-    __syncthreads();
-    if (tau == 0) mark(a, s.flag[1], 3);
-    const char* xb = s.xf;
+    const bool more = tau + 1 < G.NT;
+    if (more) b_stage_load<WT>(a, s, gd, tau + 1, G.KSM, Mp, tidx(), sr);
+    const char* xb = s.xf + (tau & 1) * XBUF;
     const int nr = has_rows ? G.n_real(tau, wave) : 0;
     const int np = has_rows ? G.n_pad(tau, wave) : 0;
-    for (int j = 0; j < np; j += RING) {
+    for (int j = 0; j < np; j += BRING) {
 #pragma unroll
-      for (int r = 0; r < RING; ++r) {
-        b_issue<WT>(gd, G, it, wave, lane, slot[(r + RING - 1) % RING]);
+      for (int r = 0; r < BRING; ++r) {
+        b_issue<WT>(gd, G, it, wave, lane, slot[(r + BRING - 1) % BRING]);
         if (j + r < nr) {
           const int i = wave + NWC * (j + r);
           b_mfma<WT>(D, i % G.T, MT, slot[r], xb, i / G.T, lane, lo_off);
         }
       }
     }
+    // the next tile goes into the other buffer: every wave finished reading
+    // it (tile tau-1) before the barrier that ended that tile
+    if (more) b_stage_store<WT>(s, gd, tau + 1, G.KSM, Mp, MT, s.xf + ((tau + 1) & 1) * XBUF, tidx(), sr, ss);
+    __syncthreads();
     if (tau < 2 || tau == G.NT - 1) mark(a, s.flag[1], tau < 2 ? 4 + tau : 6);
   }
-  __syncthreads();                                      // X is dead: the reduction may overwrite it
   float* red = reinterpret_cast<float*>(s.xf);
   for (int t = 0; t < G.T && t < TMAX; ++t)
 #pragma unroll
@@ -664,10 +685,12 @@ __device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, 
 #pragma unroll
     for (int jp = 0; jp < 16; ++jp) {
       const float* vr = vc + (size_t)min(jp, pos) * hd;
-      const float pj = readlane_f(e4[jp >> 2], (jp & 3) * 16) / den;
-      o0 = fmaf(pj, vr[c0], o0);
-      o1 = fmaf(pj, vr[c1], o1);
+      const float ej = readlane_f(e4[jp >> 2], (jp & 3) * 16);   // 0 past pos
+      o0 = fmaf(ej, vr[c0], o0);
+      o1 = fmaf(ej, vr[c1], o1);
     }
+    o0 /= den;   // the weights' normalisation, once per output
+    o1 /= den;
     float* o = batt(a, step, l) + (size_t)m * a.attn_dim + (size_t)g * a.gw + (size_t)hh * hd;
     if (lane < hd) st_coh(o + lane, o0);
     if (lane + 64 < hd) st_coh(o + lane + 64, o1);
