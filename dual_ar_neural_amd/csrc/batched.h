@@ -6,9 +6,9 @@
 // request at step 1: positions 0 and 1; one after), M <= 2 * BQ_MAX.  Every
 // linear layer is a skinny GEMM Y[M x N] = X[M x K] W^T run on the matrix
 // cores: each workgroup owns a range of W's rows (all of K); W (bf16) is the
-// MFMA A operand, streamed from HBM with 16-byte loads; X is staged in LDS,
-// K-tile by K-tile, as the B operand split into bf16 high and low halves
-// (x = hi + lo exactly to about 2^-16 relative), so that the products keep
+// MFMA A operand, streamed from HBM with 16-byte loads; X, read from the
+// arena by the wave that uses it, is the B operand split into bf16 high and
+// low halves (x = hi + lo to about 2^-16 relative), so that the products keep
 // float32-level accuracy; accumulation is float32.  f32 weights use the
 // float32 MFMA with float32 X instead.
 //
@@ -27,7 +27,7 @@
 
 constexpr int BQ_MAX = 16;               // requests per batched launch
 constexpr int MP_MAX = 2 * BQ_MAX;       // rows per decode step at most
-constexpr int XF_BYTES = 128 * 1024;     // LDS for the X operand (two buffers; also the reduction)
+constexpr int XF_BYTES = 128 * 1024;     // LDS for the GEMM partial sums and the attention scratch
 constexpr int TMAX = 5;                  // 16-row tiles of W per workgroup and phase
 constexpr int RED_TILES = 10;            // tiles x M-tiles the reduction buffer holds
 
@@ -73,8 +73,8 @@ struct BatchArgs {
 };
 
 struct BLds {
-  char* xf;      // XF_BYTES: X fragments; reduction buffer; attention scratch
-  float* ssp;    // [NTHREADS] per-thread sums of squares
+  char* xf;      // XF_BYTES: GEMM partial sums; attention scratch
+  float* ssp;    // [NTHREADS] per-wave row sums of squares ([NWAVE][MP_MAX] used)
   float* rms;    // [MP_MAX]
   float* qkn;    // [n_layer][2][hd]
   float* rope;   // [2][ctx][hd/2]
@@ -155,12 +155,10 @@ template <typename WT> struct MF;
 template <> struct MF<uint16_t> {
   static constexpr int KSZ = 32;      // K per k-step (one 16x16x32 MFMA per X half)
   static constexpr int GE = 8;        // K per lane per k-step
-  static constexpr int FRAG = 2048;   // LDS bytes per k-step and M-tile (hi + lo)
 };
 template <> struct MF<float> {
   static constexpr int KSZ = 16;      // four 16x16x4 MFMAs
   static constexpr int GE = 4;
-  static constexpr int FRAG = 1024;
 };
 
 // two floats -> two bf16 (round to nearest even), a in the low half
@@ -219,68 +217,61 @@ __device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const
   }
 }
 
-// X is staged K-tile by K-tile into two alternating LDS buffers.  Every
-// thread stages the same share of each tile; the loads of tile tau+1 are
-// issued before tile tau's weight stream starts and converted into the other
-// buffer after it, so only the first tile's staging is exposed.  (Staging on
-// a few dedicated waves while the others stream was measured slower: with
-// the weight streams running, the staging loads -- data written by other
-// XCDs, so L2 misses -- wait much longer in the memory queues.)
-constexpr int NWC = NWAVE;                      // waves running the MFMAs
-constexpr int NSTAGE = NTHREADS;                // threads staging X
-constexpr int XBUF = XF_BYTES / 2;              // one of the two X buffers
-// staging items per thread and K-tile (a buffer holds 2048 (bf16 hi + lo) or
-// 4096 (f32) items of GE columns at either M-tile count)
-template <typename WT> constexpr int sbs() { return MF<WT>::GE == 8 ? 4 : 8; }
+// ------------------------------------------------------------ GEMM core
+// Work split: wave w takes the k-steps s = w, w + NWAVE, ... (KSZ columns
+// each) for every row tile of the workgroup, so each X fragment is read and
+// converted by exactly one wave, straight into MFMA B operands: no staging
+// in LDS and no barrier inside the phase.  Per k-step a wave loads the
+// weight fragment of each row tile (A operand: lane -> row 16 t + lane % 16,
+// columns s KSZ + GE (lane / 16) ..) and the X fragment of each M-tile (B
+// operand: lane -> row 16 mt + lane % 16, the same columns), applies the
+// phase's RMSNorm weight, splits X into bf16 high and low halves (x = hi + lo
+// to about 2^-16 relative) and accumulates D[t][mt] in float32.  The loads of
+// a k-step are issued PD k-steps before it is used (more when a k-step has
+// few row tiles; deeper pipelines measured slower).
+template <int TT, int MTT> constexpr int bpd() { return TT == 1 ? 4 : (TT == 2 ? 3 : 2); }
 
-// One thread's share of K-tile `tau` of X (columns [tau*KSM*KSZ, ...)):
-// items i = j * NSTAGE + st of GE columns of row m = st % Mp, so that a
-// thread's running sum of squares (normed phases) covers one row in a fixed
-// order.
-template <typename WT>
-struct StageRegs {
-  float v[sbs<WT>()][8];
-  bool ok[sbs<WT>()];
+template <typename WT, int TT, int MTT>
+struct BUnit {
+  u32x4 w[TT];
+  float x[MTT][8];
+  bool ok[MTT];
 };
 
-template <typename WT>
-__device__ __forceinline__ void b_stage_load(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int tau, int KSM,
-                                             int Mp, int st, StageRegs<WT>& r) {
-  constexpr int GE = MF<WT>::GE, KSZ = MF<WT>::KSZ, SBS = sbs<WT>();
-  const int m = st % Mp;
-  const int k0 = tau * KSM * KSZ;
-  const int msh = Mp == 16 ? 4 : 5;             // i / Mp
+// Loads of k-step st (past the wave's last k-step: loads of k-step 0, unused)
+template <typename WT, int TT, int MTT>
+__device__ __forceinline__ void b_load(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int st, int KST,
+                                       int lane, BUnit<WT, TT, MTT>& u) {
+  constexpr int KSZ = MF<WT>::KSZ, GE = MF<WT>::GE;
+  const bool live = st < KST;
+  const int col = (live ? st : 0) * KSZ + GE * (lane >> 4);
+  const bool colok = col < gd.K;              // past the last column X is zero (weights: column 0)
+  const int c = colok ? col : 0;
 #pragma unroll
-  for (int j = 0; j < SBS; ++j) {
-    const int i = j * NSTAGE + st;
-    const int k = k0 + (i >> msh) * GE;
-    r.ok[j] = m < gd.M && k < gd.K;
-    b_fetch<WT>(a, s, gd, m < gd.M ? m : 0, r.ok[j] ? k : 0, r.v[j]);   // in bounds; zeroed below if not ok
+  for (int t = 0; t < TT; ++t) {
+    const int v = min(16 * t + (lane & 15), gd.R - 1);
+    const char* row = v < gd.R1 ? gd.wa + (long long)v * gd.ldb : gd.wb + (long long)(v - gd.R1) * gd.ldb;
+    load16_nt(u.w[t], row + (long long)c * sizeof(WT));
+  }
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt) {
+    const int m = 16 * mt + (lane & 15);
+    u.ok[mt] = live && colok && m < gd.M;
+    b_fetch<WT>(a, s, gd, m < gd.M ? m : 0, c, u.x[mt]);
   }
 }
 
-// ... and its conversion into buffer `buf` as MFMA B fragments: lane (q, j)
-// of k-step s and M-tile mt holds X[16 mt + j][k0 + s KSZ + GE q .. + GE)
-// (bf16: high halves, then low halves in the second half of the buffer).
-template <typename WT>
-__device__ __forceinline__ void b_stage_store(const BLds& s, const GemmDesc& gd, int tau, int KSM, int Mp, int MT,
-                                              char* buf, int st, const StageRegs<WT>& r, float& ss) {
-  constexpr int GE = MF<WT>::GE, KSZ = MF<WT>::KSZ, SBS = sbs<WT>();
-  const int m = st % Mp;
-  const int k0 = tau * KSM * KSZ;
-  const int lo_off = KSM * MT * 1024;
-  const int msh = Mp == 16 ? 4 : 5;
+template <typename WT, int TT, int MTT>
+__device__ __forceinline__ void b_use(const BLds& s, const GemmDesc& gd, int st, int lane, const BUnit<WT, TT, MTT>& u,
+                                      f32x4 (&D)[TT][MTT], float (&ss)[MTT]) {
+  constexpr int KSZ = MF<WT>::KSZ, GE = MF<WT>::GE;
+  const int col = st * KSZ + GE * (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < SBS; ++j) {
-    const int i = j * NSTAGE + st;
-    const int kg = i >> msh;
-    const int sl = kg >> 2, q = kg & 3;
-    const int idx = ((sl * MT + (m >> 4)) * 64 + q * 16 + (m & 15)) * 16;
-    const int k = k0 + kg * GE;
+  for (int mt = 0; mt < MTT; ++mt) {
     float x[8];
     float w[8];
     if (gd.normw) {                              // uniform: the phase's RMSNorm weight, from LDS
-      const int kk = r.ok[j] ? k : 0;
+      const int kk = u.ok[mt] ? col : 0;
       const float4 w0 = *reinterpret_cast<const float4*>(s.nw + kk);
       w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
       if (GE == 8) {
@@ -291,111 +282,75 @@ __device__ __forceinline__ void b_stage_store(const BLds& s, const GemmDesc& gd,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x[e] = 0.0f;
-      if (e < GE && r.ok[j]) {
-        if (gd.normw) { ss = fmaf(r.v[j][e], r.v[j][e], ss); x[e] = r.v[j][e] * w[e]; }
-        else x[e] = r.v[j][e];
+      if (e < GE && u.ok[mt]) {
+        if (gd.normw) { ss[mt] = fmaf(u.x[mt][e], u.x[mt][e], ss[mt]); x[e] = u.x[mt][e] * w[e]; }
+        else x[e] = u.x[mt][e];
       }
     }
     if (GE == 8) {
-      // x = hi + lo with hi = bf16(x), lo = bf16(x - hi), both round to
-      // nearest even (the packed hardware conversion)
       u32 h[4], lw[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         h[p] = bf16_pair(x[2 * p], x[2 * p + 1]);
         lw[p] = bf16_pair(x[2 * p] - __uint_as_float(h[p] << 16), x[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u));
       }
-      *reinterpret_cast<uint4*>(buf + idx) = make_uint4(h[0], h[1], h[2], h[3]);
-      *reinterpret_cast<uint4*>(buf + lo_off + idx) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      bf16x8 hv, lv;
+      __builtin_memcpy(&hv, h, 16);
+      __builtin_memcpy(&lv, lw, 16);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        bf16x8 av;
+        __builtin_memcpy(&av, &u.w[t], 16);
+        D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, D[t][mt], 0, 0, 0);
+        D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lv, D[t][mt], 0, 0, 0);
+      }
     } else {
-      *reinterpret_cast<float4*>(buf + idx) = make_float4(x[0], x[1], x[2], x[3]);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const u32x4 q = u.w[t];
+        D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q.x), x[0], D[t][mt], 0, 0, 0);
+        D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q.y), x[1], D[t][mt], 0, 0, 0);
+        D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q.z), x[2], D[t][mt], 0, 0, 0);
+        D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(q.w), x[3], D[t][mt], 0, 0, 0);
+      }
     }
   }
 }
 
-// Weight fragments in flight per compute wave (a deeper ring measured
-// slower: the K-tile time is set by the tile's staging and barrier, not by
-// the weight stream's latency).
-constexpr int BRING = RING;
-
-// Work of compute wave w in K-tile tau: the tile's (k-step, row tile) pairs
-// i = sl * T + t taken round robin, i = w, w + NWC, ...; the list is padded to
-// a multiple of BRING (padding issues dummy loads) so that the register ring
-// is in phase at every K-tile boundary.
-struct BIter {
-  int tau, j;
-};
-
-struct BGeom {
-  int T, KST, KSM, NT;
-  __device__ __forceinline__ int n_real(int tau, int w) const {
-    const int ks = min(KST - tau * KSM, KSM);
-    const int n = T * ks - w;
-    return n > 0 ? (n + NWC - 1) / NWC : 0;
+// One wave's share of a GEMM phase with TT row tiles and MTT M-tiles: its
+// partial sums go to red[((wave * TT + t) * MTT + mt) * 256 + lane * 4 ..],
+// its per-lane sums of squares of X to ssm[mt] (row 16 mt + lane % 16).
+template <typename WT, int TT, int MTT>
+__device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int wave, int lane,
+                                       float* red, float (&ssm)[2]) {
+  constexpr int KSZ = MF<WT>::KSZ, PD = bpd<TT, MTT>();
+  const int KST = (gd.K + KSZ - 1) / KSZ;
+  const int ns = wave < KST ? (KST - wave + NWAVE - 1) / NWAVE : 0;   // this wave's k-steps
+  f32x4 D[TT][MTT];
+  float ss[MTT];
+#pragma unroll
+  for (int mt = 0; mt < MTT; ++mt) {
+    ss[mt] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) D[t][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  __device__ __forceinline__ int n_pad(int tau, int w) const { return (n_real(tau, w) + BRING - 1) / BRING * BRING; }
-};
-
-template <typename WT>
-__device__ __forceinline__ void b_issue(const GemmDesc& gd, const BGeom& G, BIter& it, int wave, int lane,
-                                        u32x4& slot) {
-  constexpr int KSZ = MF<WT>::KSZ, GE = MF<WT>::GE;
-  const char* addr = gd.dummy;
-  if (it.tau < G.NT) {
-    if (it.j < G.n_real(it.tau, wave)) {
-      const int i = wave + NWC * it.j;
-      const int s = it.tau * G.KSM + i / G.T;
-      const int t = i % G.T;
-      const int v = min(16 * t + (lane & 15), gd.R - 1);
-      int col = s * KSZ + GE * (lane >> 4);
-      if (col >= gd.K) col = 0;      // past the last column: X is zero there
-      const char* row = v < gd.R1 ? gd.wa + (long long)v * gd.ldb : gd.wb + (long long)(v - gd.R1) * gd.ldb;
-      addr = row + (long long)col * sizeof(WT);
-    }
-    if (++it.j >= G.n_pad(it.tau, wave)) {
-      it.j = 0;
-      ++it.tau;
-      while (it.tau < G.NT && G.n_pad(it.tau, wave) == 0) ++it.tau;
+  BUnit<WT, TT, MTT> u[PD];
+#pragma unroll
+  for (int p = 0; p < PD - 1; ++p) b_load<WT, TT, MTT>(a, s, gd, wave + NWAVE * p, KST, lane, u[p]);
+  for (int i = 0; i < ns; i += PD) {
+#pragma unroll
+    for (int r = 0; r < PD; ++r) {
+      b_load<WT, TT, MTT>(a, s, gd, wave + NWAVE * (i + r + PD - 1), KST, lane, u[(r + PD - 1) % PD]);
+      if (i + r < ns) b_use<WT, TT, MTT>(s, gd, wave + NWAVE * (i + r), lane, u[r], D, ss);
     }
   }
-  load16_nt(slot, addr);
-}
-
-template <typename WT>
-__device__ __forceinline__ void b_mfma(f32x4 (&D)[TMAX][2], int t, int MT, const u32x4& w, const char* xf, int sl,
-                                       int lane, int lo_off) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    if (mt >= MT) break;
-    const int idx = ((sl * MT + mt) * 64 + lane) * 16;
-    if (sizeof(WT) == 2) {
-      const uint4 bh = *reinterpret_cast<const uint4*>(xf + idx);
-      const uint4 bl = *reinterpret_cast<const uint4*>(xf + lo_off + idx);
-      bf16x8 av, hv, lv;
-      __builtin_memcpy(&av, &w, 16);
-      __builtin_memcpy(&hv, &bh, 16);
-      __builtin_memcpy(&lv, &bl, 16);
+  for (int mt = 0; mt < MTT; ++mt) {
+    ssm[mt] = ss[mt];
 #pragma unroll
-      for (int tt = 0; tt < TMAX; ++tt) {
-        if (tt == t) {
-          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, D[tt][mt], 0, 0, 0);
-          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lv, D[tt][mt], 0, 0, 0);
-        }
-      }
-    } else {
-      const float4 bx = *reinterpret_cast<const float4*>(xf + idx);
-      const float a0 = __uint_as_float(w.x), a1 = __uint_as_float(w.y), a2 = __uint_as_float(w.z),
-                  a3 = __uint_as_float(w.w);
-#pragma unroll
-      for (int tt = 0; tt < TMAX; ++tt) {
-        if (tt == t) {
-          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bx.x, D[tt][mt], 0, 0, 0);
-          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bx.y, D[tt][mt], 0, 0, 0);
-          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, bx.z, D[tt][mt], 0, 0, 0);
-          D[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, bx.w, D[tt][mt], 0, 0, 0);
-        }
-      }
-    }
+    for (int t = 0; t < TT; ++t)
+      *reinterpret_cast<float4*>(red + (((size_t)wave * TT + t) * MTT + mt) * 256 + lane * 4) =
+          make_float4(D[t][mt][0], D[t][mt][1], D[t][mt][2], D[t][mt][3]);
   }
 }
 
@@ -408,99 +363,63 @@ struct RedView {
     const int t = v >> 4, i = v & 15, mt = m >> 4;
     const int ln = (i >> 2) * 16 + (m & 15), r = i & 3;
     float acc = 0.0f;
-    for (int w = 0; w < NWC; ++w) acc += red[(((size_t)w * T + t) * MT + mt) * 256 + ln * 4 + r];
+    for (int w = 0; w < NWAVE; ++w) acc += red[(((size_t)w * T + t) * MT + mt) * 256 + ln * 4 + r];
     return acc;
   }
 };
 
-// Compute-wave side of one GEMM phase.
-template <typename WT>
-__device__ __forceinline__ void b_compute(const BatchArgs& a, const BLds& s, const GemmDesc& gd, const BGeom& G, int Mp,
-                                          int MT, int wave, int lane, float& ss) {
-  const int lo_off = G.KSM * MT * 1024;
-  f32x4 D[TMAX][2];
-#pragma unroll
-  for (int t = 0; t < TMAX; ++t)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) D[t][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const bool has_rows = gd.R > 0;
-  BIter it{0, 0};
-  while (it.tau < G.NT && G.n_pad(it.tau, wave) == 0) ++it.tau;
-  if (!has_rows) it.tau = G.NT;
-  u32x4 slot[BRING];
-#pragma unroll
-  for (int j = 0; j < BRING - 1; ++j) b_issue<WT>(gd, G, it, wave, lane, slot[j]);
-  mark(a, s.flag[1], 2);
-  StageRegs<WT> sr;
-  b_stage_load<WT>(a, s, gd, 0, G.KSM, Mp, tidx(), sr);
-  b_stage_store<WT>(s, gd, 0, G.KSM, Mp, MT, s.xf, tidx(), sr, ss);
-  __syncthreads();
-  mark(a, s.flag[1], 3);
-  for (int tau = 0; tau < G.NT; ++tau) {
-    const bool more = tau + 1 < G.NT;
-    if (more) b_stage_load<WT>(a, s, gd, tau + 1, G.KSM, Mp, tidx(), sr);
-    const char* xb = s.xf + (tau & 1) * XBUF;
-    const int nr = has_rows ? G.n_real(tau, wave) : 0;
-    const int np = has_rows ? G.n_pad(tau, wave) : 0;
-    for (int j = 0; j < np; j += BRING) {
-#pragma unroll
-      for (int r = 0; r < BRING; ++r) {
-        b_issue<WT>(gd, G, it, wave, lane, slot[(r + BRING - 1) % BRING]);
-        if (j + r < nr) {
-          const int i = wave + NWC * (j + r);
-          b_mfma<WT>(D, i % G.T, MT, slot[r], xb, i / G.T, lane, lo_off);
-        }
-      }
-    }
-    // the next tile goes into the other buffer: every wave finished reading
-    // it (tile tau-1) before the barrier that ended that tile
-    if (more) b_stage_store<WT>(s, gd, tau + 1, G.KSM, Mp, MT, s.xf + ((tau + 1) & 1) * XBUF, tidx(), sr, ss);
-    __syncthreads();
-    if (tau < 2 || tau == G.NT - 1) mark(a, s.flag[1], tau < 2 ? 4 + tau : 6);
-  }
-  float* red = reinterpret_cast<float*>(s.xf);
-  for (int t = 0; t < G.T && t < TMAX; ++t)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      if (mt >= MT) break;
-      f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int tt = 0; tt < TMAX; ++tt)
-        if (tt == t) d = D[tt][mt];
-      *reinterpret_cast<float4*>(red + (((size_t)wave * G.T + t) * MT + mt) * 256 + lane * 4) =
-          make_float4(d[0], d[1], d[2], d[3]);
-    }
-}
-
 // Run one GEMM phase on this workgroup.  On return (after a barrier) the
-// view holds the compute waves' partial sums and, with a norm weight,
-// rms[m] holds sqrt(mean(x_m^2) + eps) over the K columns.
+// view holds the waves' partial sums and, with a norm weight, rms[m] holds
+// sqrt(mean(x_m^2) + eps) over the K columns.
 template <typename WT>
 __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, const GemmDesc& gd) {
-  constexpr int KSZ = MF<WT>::KSZ;
   const int tid = tidx();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave-uniform work split
-  const int Mp = gd.M <= 16 ? 16 : 32, MT = Mp >> 4;
-  BGeom G;
-  G.T = (gd.R + 15) >> 4;
-  G.KST = (gd.K + KSZ - 1) / KSZ;
-  G.KSM = XBUF / (MT * MF<WT>::FRAG);
-  G.NT = (G.KST + G.KSM - 1) / G.KSM;
+  const int MT = gd.M <= 16 ? 1 : 2;
+  const int T = (gd.R + 15) >> 4;
   if (gd.normw) {
     for (int k = tid; k < gd.K; k += NTHREADS) s.nw[k] = WTraits<WT>::one(reinterpret_cast<const WT*>(gd.normw), k);
     __syncthreads();
   }
-  float ss = 0.0f;
-  b_compute<WT>(a, s, gd, G, Mp, MT, wave, lane, ss);
-  if (gd.normw) s.ssp[tid] = ss;
+  float* red = reinterpret_cast<float*>(s.xf);
+  float ssm[2] = {0.0f, 0.0f};
+  mark(a, s.flag[1], 2);
+#define B_CORE(TT_)                                                         \
+  case TT_:                                                                 \
+    if (MT == 1) b_core<WT, TT_, 1>(a, s, gd, wave, lane, red, ssm);        \
+    else b_core<WT, TT_, 2>(a, s, gd, wave, lane, red, ssm);                \
+    break;
+  switch (T) {
+    B_CORE(1)
+    B_CORE(2)
+    B_CORE(3)
+    B_CORE(4)
+    B_CORE(5)
+    default: break;   // no rows in this workgroup
+  }
+#undef B_CORE
+  static_assert(TMAX == 5, "b_gemm dispatches row-tile counts 1..5");
+  mark(a, s.flag[1], 3);
+  if (gd.normw) {
+    // a row's sum of squares: its four lanes (lane % 16 = row) in each wave,
+    // then the waves
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      if (mt >= MT) break;
+      float v = ssm[mt];
+      v += xor_lane_f<16>(v, lane);
+      v += xor_lane_f<32>(v, lane);
+      if (lane < 16) s.ssp[wave * MP_MAX + 16 * mt + lane] = v;
+    }
+  }
   __syncthreads();
   if (gd.normw && tid < gd.M) {
     float t2 = 0.0f;
-    for (int q = tid; q < NSTAGE; q += Mp) t2 += s.ssp[q];
+    for (int w = 0; w < NWAVE; ++w) t2 += s.ssp[w * MP_MAX + tid];
     s.rms[tid] = sqrtf(t2 / (float)gd.K + a.eps);
   }
   __syncthreads();
-  return RedView{reinterpret_cast<const float*>(s.xf), G.T, MT};
+  return RedView{red, T, MT};
 }
 
 // ------------------------------------------------------------ phases
