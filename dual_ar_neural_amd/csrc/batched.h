@@ -219,9 +219,9 @@ __device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const
 
 // ------------------------------------------------------------ GEMM core
 // Work split: wave w takes the k-steps s = w, w + NWAVE, ... (KSZ columns
-// each) for every row tile of the workgroup, so each X fragment is read and
-// converted by exactly one wave, straight into MFMA B operands: no staging
-// in LDS and no barrier inside the phase.  Per k-step a wave loads the
+// each) for every row tile of the workgroup, so each X
+// fragment is read and converted by exactly one wave, straight into MFMA B
+// operands: no staging in LDS and no barrier inside the phase.  Per k-step a wave loads the
 // weight fragment of each row tile (A operand: lane -> row 16 t + lane % 16,
 // columns s KSZ + GE (lane / 16) ..) and the X fragment of each M-tile (B
 // operand: lane -> row 16 mt + lane % 16, the same columns), applies the
@@ -326,6 +326,7 @@ __device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const 
   constexpr int KSZ = MF<WT>::KSZ, PD = bpd<TT, MTT>();
   const int KST = (gd.K + KSZ - 1) / KSZ;
   const int ns = wave < KST ? (KST - wave + NWAVE - 1) / NWAVE : 0;   // this wave's k-steps
+  const auto kstep = [&](int j) __attribute__((always_inline)) { return j < ns ? wave + NWAVE * j : KST; };
   f32x4 D[TT][MTT];
   float ss[MTT];
 #pragma unroll
@@ -336,12 +337,12 @@ __device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const 
   }
   BUnit<WT, TT, MTT> u[PD];
 #pragma unroll
-  for (int p = 0; p < PD - 1; ++p) b_load<WT, TT, MTT>(a, s, gd, wave + NWAVE * p, KST, lane, u[p]);
+  for (int p = 0; p < PD - 1; ++p) b_load<WT, TT, MTT>(a, s, gd, kstep(p), KST, lane, u[p]);
   for (int i = 0; i < ns; i += PD) {
 #pragma unroll
     for (int r = 0; r < PD; ++r) {
-      b_load<WT, TT, MTT>(a, s, gd, wave + NWAVE * (i + r + PD - 1), KST, lane, u[(r + PD - 1) % PD]);
-      if (i + r < ns) b_use<WT, TT, MTT>(s, gd, wave + NWAVE * (i + r), lane, u[r], D, ss);
+      b_load<WT, TT, MTT>(a, s, gd, kstep(i + r + PD - 1), KST, lane, u[(r + PD - 1) % PD]);
+      if (i + r < ns) b_use<WT, TT, MTT>(s, gd, kstep(i + r), lane, u[r], D, ss);
     }
   }
 #pragma unroll
@@ -477,6 +478,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   gd.R = kind == BK_UP ? 2 * nr : nr;
   if (!gd.wb) gd.wb = gd.wa;
   const RedView rv = b_gemm<WT>(a, s, gd);
+  mark(a, s.flag[1], 4);
   const int M = gd.M;
   const int nv = kind == BK_UP ? nr : gd.R;
   for (int o = tidx(); o < nv * M; o += NTHREADS) {
@@ -510,6 +512,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       }
     }
   }
+  mark(a, s.flag[1], 5);
 }
 
 // One workgroup per (request b, KV group g): the request's new rows' q (the
