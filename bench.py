@@ -31,16 +31,21 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "Fast-AR frames/sec (9 codebooks) at batch 1/16/64; achieved HBM GB/s"
 
 
-def algorithmic_bytes_per_frame(shape, batch: int) -> int:
+def algorithmic_bytes_per_frame(shape, batch: int, qkv0_table: bool) -> int:
     """Bytes a frame of `batch` requests must move at minimum: every weight
     read once per decode step (matrices, norm vectors and one embedding row
-    per request), plus each request's inputs and codes."""
+    per request), plus each request's inputs and codes.  With qkv0_table the
+    steps after the first take their one new row's layer-0 q/k/v from the
+    context's precomputed table (one float32 row of qkv_dim per request)
+    instead of streaming layer 0's wqkv and attention_norm."""
     s = shape
     wb = 2 if s.weight_dtype == "bf16" else 4
     per_layer = (s.qkv_dim * s.dim + s.dim * s.attn_dim + 2 * s.ffn_dim * s.dim + s.dim * s.ffn_dim
                  + 2 * s.dim + (2 * s.head_dim if s.has_qk_norm else 0)) * wb
     per_step = s.n_layer * per_layer + (s.codebook_size * s.dim + s.dim) * wb + batch * s.dim * wb
     per_frame = s.n_steps * per_step
+    if qkv0_table:
+        per_frame -= (s.n_steps - 1) * ((s.qkv_dim * s.dim + s.dim) * wb - batch * s.qkv_dim * 4)
     if s.has_project_in:
         per_frame += s.dim * s.in_dim * wb
     io = batch * (s.in_dim * 4 + 4 + s.n_steps * 4 + 3 * 4 + s.num_codebooks * 4)
@@ -178,7 +183,7 @@ def main():
     B = 1
     frames_per_s = B * args.steps / secs
     ms = secs * 1e3 / args.steps
-    bytes_frame = algorithmic_bytes_per_frame(shape, B)   # one launch is one frame at batch 1
+    bytes_frame = algorithmic_bytes_per_frame(shape, B, True)   # one launch is one frame at batch 1
     achieved = bytes_frame / kern_s / 1e9
     csrc = os.path.join(ROOT, "dual_ar_neural_amd", "csrc")
     prof = traffic_from_profile(os.path.join(ROOT, "profiles", "frame_kernel_s2pro_b1_hbm_traffic.md"),
@@ -223,7 +228,7 @@ def main():
             di = upload(torch, frs)
             print(f"[bench] timing {nf} frames at batch {Bs}", file=sys.stderr, flush=True)
             sec, _ = time_frames(torch, cs, di, Bs, nf, 1)
-            fb = algorithmic_bytes_per_frame(ws.shape, Bs)
+            fb = algorithmic_bytes_per_frame(ws.shape, Bs, False)   # the batched kernel streams layer-0 wqkv every step
             sweep[f"b{Bs}"] = {"frames_per_s": round(Bs * nf / sec, 2), "ms_per_frame": round(sec * 1e3 / nf, 3),
                                "hbm_gbs": round(fb * nf / sec / 1e9, 1),
                                "frac": round(fb * nf / sec / 1e9 / PEAK_HBM_GBS, 4), "frames": nf,

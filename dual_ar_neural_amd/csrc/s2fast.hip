@@ -57,6 +57,11 @@ struct FrameArgs {
   const void* outw;
   LayerPtr L[S2FAST_MAX_LAYERS];
   const float* rope;  // [2][ctx_len][hd/2]: cos then sin
+  // Layer-0 q/k/v of every embedding row, [V][qkv_dim]:
+  // wqkv . (attention_norm * e_c) / rms(e_c).  A new row at position >= 2
+  // is fast_embeddings[c] of a code this block already knows, so its
+  // layer-0 projection is a row of this table (built once per context).
+  const float* qkv0;
   // the request this launch decodes
   const float* hidden;     // [in_dim]
   const int* sem_code;     // [1]
@@ -487,10 +492,11 @@ __device__ __forceinline__ void plan_issue(Plan& p, u32x4& d) {
 // places them: the scheduler would otherwise interleave the consumers of the
 // staging loads issued just before, each with a wait on those loads, between
 // the weight loads.
-__device__ __forceinline__ void gemv_prologue(Plan& p, u32x4 (&slot)[RING]) {
+template <int R>
+__device__ __forceinline__ void gemv_prologue(Plan& p, u32x4 (&slot)[R]) {
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < RING - 1; ++j) plan_issue(p, slot[j]);
+  for (int j = 0; j < R - 1; ++j) plan_issue(p, slot[j]);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -498,8 +504,8 @@ __device__ __forceinline__ void gemv_prologue(Plan& p, u32x4 (&slot)[RING]) {
 // layout, row stride act_ld).  The chunk cursor is wave-uniform, so every
 // branch here is a scalar branch; the per-lane tail of a row (segments past
 // K) is handled by zeroing the lane's weights, not by a branch.
-template <typename WT, int MM>
-__device__ __forceinline__ void gemv_rows(Plan& p, u32x4 (&slot)[RING], const float* act, int act_ld, float* red) {
+template <typename WT, int MM, int R>
+__device__ __forceinline__ void gemv_rows(Plan& p, u32x4 (&slot)[R], const float* act, int act_ld, float* red) {
   constexpr int EPL = WTraits<WT>::EPL;
   const int wave = __builtin_amdgcn_readfirstlane(tidx() >> 6), lane = tidx() & 63;
   const int t0 = p.t0, t1 = p.t1;
@@ -541,18 +547,18 @@ __device__ __forceinline__ void gemv_rows(Plan& p, u32x4 (&slot)[RING], const fl
     }
     if (++cc == C) { cc = 0; flush(cr); ++cr; }
   };
-  for (int t = t0; t < t1; t += RING) {
+  for (int t = t0; t < t1; t += R) {
 #pragma unroll
-    for (int r = 0; r < RING; ++r) {
-      plan_issue(p, slot[(r + RING - 1) % RING]);
+    for (int r = 0; r < R; ++r) {
+      plan_issue(p, slot[(r + R - 1) % R]);
       if (t + r < t1) consume(slot[r]);
     }
   }
   if (cc != 0) flush(cr);   // the wave's range ended inside a row
 }
 
-template <typename WT>
-__device__ __forceinline__ void gemv_body(Plan& p, u32x4 (&slot)[RING], const float* act, int act_ld, int M,
+template <typename WT, int R>
+__device__ __forceinline__ void gemv_body(Plan& p, u32x4 (&slot)[R], const float* act, int act_ld, int M,
                                           float* red) {
   if (M == 1) gemv_rows<WT, 1>(p, slot, act, act_ld, red);
   else gemv_rows<WT, 2>(p, slot, act, act_ld, red);
@@ -623,7 +629,9 @@ enum PhaseKind { PH_PROJ = 0, PH_QKV, PH_WO, PH_FFN_UP, PH_FFN_DOWN, PH_HEAD };
 struct PhaseId { int step, layer, kind; };
 
 // Phase order of a frame: [fast_project_in], then per decode step 1..ncb-1
-// the four phases of every layer and the output head.
+// the four phases of every layer and the output head, except that steps
+// >= 2 start at layer 0's attention (their one new row's layer-0 q/k/v is a
+// row of the qkv0 table).
 __device__ __forceinline__ PhaseId first_phase(const FrameArgs& a) {
   PhaseId id;
   id.step = a.has_proj ? 0 : 1;
@@ -636,7 +644,7 @@ __device__ __forceinline__ PhaseId next_phase(const FrameArgs& a, PhaseId id) {
   if (id.kind == PH_PROJ || id.kind == PH_HEAD) {
     ++id.step;
     id.layer = 0;
-    id.kind = PH_QKV;
+    id.kind = (id.step >= 2) ? PH_WO : PH_QKV;   // layer-0 q/k/v of later steps: the qkv0 table
   } else if (id.kind == PH_FFN_DOWN) {
     ++id.layer;
     id.kind = (id.layer == a.n_layer) ? PH_HEAD : PH_QKV;
@@ -648,7 +656,7 @@ __device__ __forceinline__ PhaseId next_phase(const FrameArgs& a, PhaseId id) {
 }
 
 __device__ __forceinline__ int phase_count(const FrameArgs& a) {
-  return (a.has_proj ? 1 : 0) + (a.ncb - 1) * (4 * a.n_layer + 1);
+  return (a.has_proj ? 1 : 0) + (a.ncb - 1) * (4 * a.n_layer + 1) - (a.ncb - 2);
 }
 
 // rows of the wo phase: KV group g of this block and its share of the rows
@@ -741,6 +749,9 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
     // wave-uniform and a lane moves one pair of floats.
     constexpr int NS = 4;
     const int F = first_new, hp = hd >> 1;
+    // new rows' q/k/v: this step's wqkv phase output, or at layer 0 of steps
+    // >= 2 the qkv0 row of the code that produced the row
+    const float* qkv_new = (l == 0 && step >= 2) ? a.qkv0 + (size_t)s.codes[step - 1] * a.qkv_dim : qkvb(a, step, l);
     const int nseg = need_attn ? 2 * F + M * (gh + 2) : 0;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int lp = min(lane, hp - 1);
@@ -754,7 +765,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
       } else {
         const int t = sg - 2 * F;
         const int m = t >= gh + 2 ? 1 : 0, r = t - m * (gh + 2);   // M <= 2
-        const float* row = qkvb(a, step, l) + (size_t)m * a.qkv_dim;
+        const float* row = qkv_new + (size_t)m * a.qkv_dim;
         const int pos = row_pos(step, m);
         if (r < gh) {
           src = row + (size_t)(g * gh + r) * hd;
@@ -1051,7 +1062,10 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
     const PhaseId done = id;
     id = next_phase(a, id);
     pl = plan_for<WT>(a, id);   // past the last phase: a plan that is never used
-    if (done.kind == PH_HEAD && a.forced) continue;   // teacher forcing: the next prefix is known
+    if (done.kind == PH_HEAD && a.forced) {   // teacher forcing: the next prefix is known
+      __syncthreads();   // the head's epilogue still reads red and small
+      continue;
+    }
     if (!grid_sync(a, epoch, s.flag)) return;
     if (done.kind == PH_HEAD) {
       const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
@@ -1076,6 +1090,74 @@ __global__ void __launch_bounds__(NTHREADS) sample_kernel(int V, const float* lo
   if (tidx() == 0) codes[b] = c;
 }
 
+// ------------------------------------------------------ qkv0 table build
+// Run once when a context is created.  den[c] = sqrt(mean_k e_c[k]^2 + eps)
+// of every embedding row (the layer-0 attention_norm RMS, "Model loading and
+// GGUF", section 2.2).
+template <typename WT>
+__global__ void __launch_bounds__(256) qkv0_den_kernel(const WT* emb, int D, float eps, float* den) {
+  __shared__ float red[4];
+  const WT* e = emb + (size_t)blockIdx.x * D;
+  float ss = 0.0f;
+  for (int k = threadIdx.x; k < D; k += 256) {
+    const float v = WTraits<WT>::one(e, k);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) den[blockIdx.x] = sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)D + eps);
+}
+
+// out[c][r] = (sum_k W[r][k] * (g[k] * e_c[k])) / den[c]: the layer-0 wqkv
+// output of embedding row c, a float32 GEMM in 64 x 64 tiles (16 outputs a
+// thread).
+template <typename WT>
+__global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const WT* emb, const WT* g, const float* den,
+                                                        int V, int R, int D, float* out) {
+  constexpr int TK = 32;
+  __shared__ float Es[TK][65];   // [k][c]: g * e
+  __shared__ float Ws[TK][65];   // [k][r]
+  const int c0 = blockIdx.y * 64, r0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < D; k0 += TK) {
+    for (int i = threadIdx.x; i < 64 * TK; i += 256) {
+      const int row = i / TK, k = i % TK, kk = k0 + k;
+      const int c = c0 + row, r = r0 + row;
+      Es[k][row] = (c < V && kk < D) ? WTraits<WT>::one(g, kk) * WTraits<WT>::one(emb + (size_t)c * D, kk) : 0.0f;
+      Ws[k][row] = (r < R && kk < D) ? WTraits<WT>::one(W + (size_t)r * D, kk) : 0.0f;
+    }
+    __syncthreads();
+    for (int k = 0; k < TK; ++k) {
+      float ev[4], wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ev[i] = Es[k][ty * 4 + i];
+        wv[i] = Ws[k][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(wv[j], ev[i], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = c0 + ty * 4 + i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + tx * 4 + j;
+      if (c < V && r < R) out[(size_t)c * R + r] = acc[i][j] / den[c];
+    }
+  }
+}
+
 #include "batched.h"
 
 }  // namespace
@@ -1091,6 +1173,7 @@ struct s2fast_ctx {
   int kmax = 0, rmax = 0;
   long long x_slot = 0, qkv_slot = 0, acc_slot = 0, g_slot = 0, logits_slot = 0;
   float* rope = nullptr;
+  float* qkv0 = nullptr;   // [V][qkv_dim] layer-0 q/k/v of every embedding row
   float* xin0 = nullptr;
   float* x = nullptr;
   float* qkv = nullptr;
@@ -1143,14 +1226,16 @@ void rope_table_host(int hd, int ctx, float base, float* c, float* s) {
     }
 }
 
+// grid syncs of one launch: one per phase (the frame kernel's phase_count),
+// less the head's when the prefix is teacher-forced
 int syncs_for(const s2fast_config& c, bool forced) {
   const int per_step = 4 * c.n_layer + (forced ? 0 : 1);
-  return (c.has_project_in ? 1 : 0) + (c.num_codebooks - 1) * per_step;
+  return (c.has_project_in ? 1 : 0) + (c.num_codebooks - 1) * per_step - (c.num_codebooks - 2);
 }
 
 void free_ctx(s2fast_ctx* c) {
   if (!c) return;
-  void* ptrs[] = {c->rope, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog,
+  void* ptrs[] = {c->rope, c->qkv0, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog,
                   c->b_xin0, c->b_x, c->b_xmid, c->b_qkv, c->b_att, c->b_g, c->b_logits, c->b_kv, c->b_codes};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
@@ -1160,6 +1245,35 @@ void free_ctx(s2fast_ctx* c) {
 template <typename T>
 hipError_t dalloc(T** p, size_t n) {
   return hipMalloc(reinterpret_cast<void**>(p), n * sizeof(T) > 0 ? n * sizeof(T) : 16);
+}
+
+// The qkv0 table from the weights the context was created with (they stay
+// unchanged for its life).
+int build_qkv0(s2fast_ctx* c) {
+  const s2fast_config& k = c->cfg;
+  const int R = (k.n_head + 2 * k.n_head_kv) * k.head_dim, V = k.codebook_size, D = k.dim;
+  float* den = nullptr;
+  if (dalloc(&c->qkv0, (size_t)V * R) != hipSuccess || dalloc(&den, (size_t)V) != hipSuccess) {
+    if (den) (void)hipFree(den);
+    return S2FAST_ERR_NOMEM;
+  }
+  const dim3 grid((R + 63) / 64, (V + 63) / 64);
+  if (k.weight_dtype == S2FAST_BF16) {
+    const uint16_t* e = static_cast<const uint16_t*>(c->w.embeddings);
+    hipLaunchKernelGGL(qkv0_den_kernel<uint16_t>, dim3(V), dim3(256), 0, 0, e, D, k.norm_eps, den);
+    hipLaunchKernelGGL(qkv0_gemm_kernel<uint16_t>, grid, dim3(256), 0, 0,
+                       static_cast<const uint16_t*>(c->w.layers[0].wqkv), e,
+                       static_cast<const uint16_t*>(c->w.layers[0].attention_norm), den, V, R, D, c->qkv0);
+  } else {
+    const float* e = static_cast<const float*>(c->w.embeddings);
+    hipLaunchKernelGGL(qkv0_den_kernel<float>, dim3(V), dim3(256), 0, 0, e, D, k.norm_eps, den);
+    hipLaunchKernelGGL(qkv0_gemm_kernel<float>, grid, dim3(256), 0, 0,
+                       static_cast<const float*>(c->w.layers[0].wqkv), e,
+                       static_cast<const float*>(c->w.layers[0].attention_norm), den, V, R, D, c->qkv0);
+  }
+  const bool ok = hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+  (void)hipFree(den);
+  return ok ? S2FAST_OK : S2FAST_ERR_HIP;
 }
 
 int launch_frame(s2fast_ctx* c, const FrameArgs& fa_in, hipStream_t stream) {
@@ -1251,6 +1365,7 @@ void fill_shape(const s2fast_ctx* c, FrameArgs& fa) {
     fa.L[l] = LayerPtr{L.attention_norm, L.wqkv, L.q_norm, L.k_norm, L.wo, L.ffn_norm, L.w1, L.w3, L.w2};
   }
   fa.rope = c->rope;
+  fa.qkv0 = c->qkv0;
   fa.xin0 = c->xin0; fa.x = c->x; fa.qkv = c->qkv; fa.acc = c->acc; fa.g = c->g; fa.kv = c->kv;
   fa.x_slot = c->x_slot; fa.qkv_slot = c->qkv_slot; fa.acc_slot = c->acc_slot; fa.g_slot = c->g_slot;
   fa.logits_slot = c->logits_slot;
@@ -1384,6 +1499,7 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
        hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
        hipMemset(c->err, 0, 64 * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_HIP; }
+  if (build_qkv0(c) != S2FAST_OK) { free_ctx(c); return S2FAST_ERR_HIP; }
   if (k.max_batch >= 2) {
     c->bq = batched_group(k, P);
     if (c->bq > 0) {

@@ -81,7 +81,12 @@ typedef struct s2fast_config {
 /* Tensor names follow the GGUF Fast-AR set ("Model loading and GGUF",
  * section 3).  All pointers are device pointers of `weight_dtype`, row-major
  * [out, in].  They must stay valid and unchanged for the context's life;
- * the library reads them in place and keeps no copy. */
+ * the library reads them in place.  At creation it also derives one table
+ * from them: the layer-0 q/k/v of every embedding row,
+ * wqkv . (attention_norm * e_c) / rms(e_c) for c < codebook_size, float32
+ * [codebook_size, qkv width] (100 MB at the S2 Pro shape).  A decode step
+ * after the first adds one embedding row, so its layer-0 projection is a
+ * row of this table instead of a pass over wqkv. */
 typedef struct s2fast_layer_weights {
   const void* attention_norm;  /* [dim] */
   const void* wqkv;            /* [(n_head + 2 n_head_kv) head_dim, dim]; rows are
@@ -106,7 +111,9 @@ typedef struct s2fast_weights {
 typedef struct s2fast_ctx s2fast_ctx;
 
 /* Validate the shape and the weight pointers, allocate the context's device
- * scratch for max_batch requests and build the bf16-rounded RoPE table.
+ * scratch for max_batch requests, build the bf16-rounded RoPE table and the
+ * layer-0 q/k/v table above (one GEMM on the current stream's device,
+ * synchronised before returning).
  * Uses the current HIP device.  On success *out owns the scratch; release
  * it with s2fast_destroy.  Shape limits (else S2FAST_ERR_ARG): dim, in_dim,
  * ffn_dim and the per-KV-group width (n_head/n_head_kv)*head_dim are
