@@ -228,7 +228,7 @@ def main():
             di = upload(torch, frs)
             print(f"[bench] timing {nf} frames at batch {Bs}", file=sys.stderr, flush=True)
             sec, _ = time_frames(torch, cs, di, Bs, nf, 1)
-            fb = algorithmic_bytes_per_frame(ws.shape, Bs, False)   # the batched kernel streams layer-0 wqkv every step
+            fb = algorithmic_bytes_per_frame(ws.shape, Bs, True)
             sweep[f"b{Bs}"] = {"frames_per_s": round(Bs * nf / sec, 2), "ms_per_frame": round(sec * 1e3 / nf, 3),
                                "hbm_gbs": round(fb * nf / sec / 1e9, 1),
                                "frac": round(fb * nf / sec / 1e9 / PEAK_HBM_GBS, 4), "frames": nf,

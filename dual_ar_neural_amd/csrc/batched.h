@@ -45,6 +45,7 @@ struct BatchArgs {
   const void* outw;
   LayerPtr L[S2FAST_MAX_LAYERS];
   const float* rope;        // [2][ctx_len][hd/2]
+  const float* qkv0;        // [V][qkv_dim] layer-0 q/k/v of every embedding row (see FrameArgs)
   int Bq;                   // requests in this launch, 1..BQ_MAX
   const float* hidden;      // [Bq][in_dim]
   const int* sem_code;      // [Bq]
@@ -132,7 +133,7 @@ __device__ __forceinline__ int b_code(const BatchArgs& a, int b, int j) {
   int c;
   if (a.forced) c = a.forced[(size_t)b * a.ncb + j];
   else if (j == 0) c = a.sem_code[b];
-  else c = a.codes[b * 16 + j];
+  else c = ld_coh(a.codes + b * 16 + j);   // one line holds codes written at different steps
   return min(max(c, 0), a.V - 1);
 }
 
@@ -531,7 +532,9 @@ __device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, 
   float* q = reinterpret_cast<float*>(s.xf);                 // [n_new][gh][hd]
   float* kc = q + (size_t)2 * gh * hd;                       // [ctx][hd]
   float* vc = kc + (size_t)a.ctx_len * hd;                   // [ctx][hd]
-  // gather: cached keys/values, then the new rows' raw q, k, v
+  // gather: cached keys/values, then the new rows' raw q, k, v (layer 0 of
+  // steps >= 2: the qkv0 row of the code that produced the row)
+  const float* row0 = (l == 0 && step >= 2) ? a.qkv0 + (size_t)b_code(a, b, step - 1) * a.qkv_dim : nullptr;
   const int n_cache = first_new * 2 * hd;
   const int n_row = (gh + 2) * hd;
   for (int i = tid; i < n_cache + n_new * n_row; i += NTHREADS) {
@@ -544,7 +547,7 @@ __device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, 
       const int nr = t / n_row, r = t - nr * n_row;
       const int m = step == 1 ? nr * a.Bq + b : b;
       const int pos = step == 1 ? nr : step;
-      const float* row = bqkv(a, step, l) + (size_t)m * a.qkv_dim;
+      const float* row = row0 ? row0 : bqkv(a, step, l) + (size_t)m * a.qkv_dim;
       if (r < gh * hd) q[(size_t)nr * gh * hd + r] = row[(size_t)g * gh * hd + r];
       else if (r < (gh + 1) * hd) kc[(size_t)pos * hd + (r - gh * hd)] = row[(size_t)H * hd + (size_t)g * hd + (r - gh * hd)];
       else vc[(size_t)pos * hd + (r - (gh + 1) * hd)] = row[(size_t)(H + G) * hd + (size_t)g * hd + (r - (gh + 1) * hd)];
@@ -633,8 +636,9 @@ __device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s
   }
 }
 
+// grid syncs of one launch; steps >= 2 have no layer-0 wqkv phase
 __host__ __device__ inline int b_syncs(int has_proj, int ncb, int n_layer, bool forced) {
-  return (has_proj ? 1 : 0) + (ncb - 1) * (5 * n_layer + (forced ? 0 : 2));
+  return (has_proj ? 1 : 0) + (ncb - 1) * (5 * n_layer + (forced ? 0 : 2)) - (ncb - 2);
 }
 
 template <typename WT>
@@ -671,9 +675,11 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
         }
         __syncthreads();
       }
-      b_phase_gemm<WT>(a, s, BK_QKV, step, l);
-      if (!grid_sync(a, epoch, s.flag)) return;
-      if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
+      if (l > 0 || step == 1) {   // layer 0 of later steps reads the qkv0 table in the attention phase
+        b_phase_gemm<WT>(a, s, BK_QKV, step, l);
+        if (!grid_sync(a, epoch, s.flag)) return;
+        if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
+      }
       b_phase_attn<WT>(a, s, step, l);
       if (!grid_sync(a, epoch, s.flag)) return;
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);

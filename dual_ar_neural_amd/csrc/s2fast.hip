@@ -83,7 +83,9 @@ struct FrameArgs {
   float* qkv;              // [slot][MMAX][qkv_dim]
   long long* acc;          // [slot][MMAX][dim] fixed-point attention output (zero between frames)
   float* g;                // [slot][MMAX][ffn]
-  float* kv;               // [n_layer][ctx][n_kv][2][hd] this frame's keys/values
+  float* kv;               // [n_layer][ctx][kv_pos] this frame's keys/values ([n_kv][2][hd] per position)
+  int kv_pos;              // floats per position: n_kv * 2 * hd rounded up to a 128-byte line, so
+                           // positions written at different steps never share a cache line
   float* logits;           // [step][V]
   long long x_slot, qkv_slot, acc_slot, g_slot, logits_slot;  // region strides (elements)
   u32* flags;              // [P][64] per-block barrier epochs
@@ -735,7 +737,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const float* qn = s.qkn + (size_t)l * 2 * hd;
   const float* kn = qn + hd;
-  float* kvl = a.kv + (size_t)l * a.ctx_len * G * 2 * hd;   // [ctx][G][2][hd]
+  float* kvl = a.kv + (size_t)l * a.ctx_len * a.kv_pos;   // [ctx][kv_pos]
   const bool need_attn = (r1 > r0) || rg == 0;
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);   // the GEMV's partial sums (read after the barriers below)
   u32x4 slot[RING];
@@ -757,10 +759,10 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
     const int lp = min(lane, hp - 1);
     auto seg = [&](int sg, const float*& src, float*& dst) __attribute__((always_inline)) {
       if (sg < F) {
-        src = kvl + ((size_t)(sg * G + g) * 2 + 0) * hd;
+        src = kvl + (sg * a.kv_pos + (g * 2 + 0) * hd);
         dst = s.kc + (size_t)sg * hd;
       } else if (sg < 2 * F) {
-        src = kvl + ((size_t)((sg - F) * G + g) * 2 + 1) * hd;
+        src = kvl + ((sg - F) * a.kv_pos + (g * 2 + 1) * hd);
         dst = s.vc + (size_t)(sg - F) * hd;
       } else {
         const int t = sg - 2 * F;
@@ -826,8 +828,8 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
       for (int m = 0; m < M; ++m) {
         const int pos = row_pos(step, m);
         for (int d = tidx(); d < hd; d += NTHREADS) {
-          st_coh(kvl + (((size_t)pos * G + g) * 2 + 0) * hd + d, s.kc[(size_t)pos * hd + d]);
-          st_coh(kvl + (((size_t)pos * G + g) * 2 + 1) * hd + d, s.vc[(size_t)pos * hd + d]);
+          st_coh(kvl + (pos * a.kv_pos + (g * 2 + 0) * hd + d), s.kc[(size_t)pos * hd + d]);
+          st_coh(kvl + (pos * a.kv_pos + (g * 2 + 1) * hd + d), s.vc[(size_t)pos * hd + d]);
         }
       }
     }
@@ -1171,7 +1173,7 @@ struct s2fast_ctx {
   int ncu = 0;
   size_t lds_bytes = 0;
   int kmax = 0, rmax = 0;
-  long long x_slot = 0, qkv_slot = 0, acc_slot = 0, g_slot = 0, logits_slot = 0;
+  long long x_slot = 0, qkv_slot = 0, acc_slot = 0, g_slot = 0, logits_slot = 0, kv_pos = 0;
   float* rope = nullptr;
   float* qkv0 = nullptr;   // [V][qkv_dim] layer-0 q/k/v of every embedding row
   float* xin0 = nullptr;
@@ -1326,6 +1328,7 @@ void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
     ba.L[l] = LayerPtr{L.attention_norm, L.wqkv, L.q_norm, L.k_norm, L.wo, L.ffn_norm, L.w1, L.w3, L.w2};
   }
   ba.rope = c->rope;
+  ba.qkv0 = c->qkv0;
   ba.xin0 = c->b_xin0; ba.x = c->b_x; ba.xmid = c->b_xmid; ba.qkv = c->b_qkv; ba.att = c->b_att; ba.g = c->b_g;
   ba.logits = c->b_logits; ba.kv = c->b_kv; ba.codes = c->b_codes;
   ba.x_slot = c->bx_slot; ba.qkv_slot = c->bqkv_slot; ba.att_slot = c->batt_slot; ba.g_slot = c->bg_slot;
@@ -1367,6 +1370,7 @@ void fill_shape(const s2fast_ctx* c, FrameArgs& fa) {
   fa.rope = c->rope;
   fa.qkv0 = c->qkv0;
   fa.xin0 = c->xin0; fa.x = c->x; fa.qkv = c->qkv; fa.acc = c->acc; fa.g = c->g; fa.kv = c->kv;
+  fa.kv_pos = (int)c->kv_pos;
   fa.x_slot = c->x_slot; fa.qkv_slot = c->qkv_slot; fa.acc_slot = c->acc_slot; fa.g_slot = c->g_slot;
   fa.logits_slot = c->logits_slot;
   fa.logits = c->logits; fa.flags = c->flags; fa.err = c->err;
@@ -1485,12 +1489,13 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   c->acc_slot = rup((long long)MMAX * k.dim, 32);
   c->g_slot = rup((long long)MMAX * k.ffn_dim, 64);
   c->logits_slot = rup(k.codebook_size, 64);
+  c->kv_pos = rup((long long)k.n_head_kv * 2 * k.head_dim, 32);
   bool ok = dalloc(&c->rope, rope.size()) == hipSuccess && dalloc(&c->xin0, (size_t)rup(k.dim, 64)) == hipSuccess &&
             dalloc(&c->x, (size_t)(slots * c->x_slot)) == hipSuccess &&
             dalloc(&c->qkv, (size_t)(slots * c->qkv_slot)) == hipSuccess &&
             dalloc(&c->acc, (size_t)(slots * c->acc_slot)) == hipSuccess &&
             dalloc(&c->g, (size_t)(slots * c->g_slot)) == hipSuccess &&
-            dalloc(&c->kv, (size_t)k.n_layer * k.context * k.n_head_kv * 2 * k.head_dim) == hipSuccess &&
+            dalloc(&c->kv, (size_t)(k.n_layer * k.context * c->kv_pos)) == hipSuccess &&
             dalloc(&c->logits, (size_t)((k.num_codebooks - 1) * c->logits_slot)) == hipSuccess &&
             dalloc(&c->flags, (size_t)P * 64) == hipSuccess && dalloc(&c->err, 64) == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
