@@ -46,6 +46,9 @@ struct BatchArgs {
   LayerPtr L[S2FAST_MAX_LAYERS];
   const float* rope;        // [2][ctx_len][hd/2]
   const float* qkv0;        // [V][qkv_dim] layer-0 q/k/v of every embedding row (see FrameArgs)
+  // each GEMM's weights repacked into one contiguous stream per workgroup
+  // (b_pack_kernel), indexed by pk_index(kind, layer)
+  const char* pk[2 + 4 * S2FAST_MAX_LAYERS];
   int Bq;                   // requests in this launch, 1..BQ_MAX
   const float* hidden;      // [Bq][in_dim]
   const int* sem_code;      // [Bq]
@@ -141,15 +144,13 @@ __device__ __forceinline__ int b_code(const BatchArgs& a, int b, int j) {
 enum BKind { BK_PROJ = 0, BK_QKV, BK_WO, BK_UP, BK_DOWN, BK_HEAD };
 
 struct GemmDesc {
-  const char* wa;      // virtual rows v < R1: wa + v * ldb
-  const char* wb;      // virtual rows v >= R1: wb + (v - R1) * ldb
-  long long ldb;       // row stride in bytes
-  int R1, R;           // rows from wa, all rows
+  const char* pk;      // this workgroup's packed weight stream (b_pack_kernel layout)
+  long long kp;        // bytes of one packed row: k-steps * 64
+  int R;               // rows (for the SwiGLU phase: w1 rows, then the same w3 rows)
   int K;               // columns
   int M;               // rows of X (<= MP_MAX)
   int kind, step, l;
   const void* normw;   // RMSNorm weight over K, or nullptr
-  const char* dummy;   // always-valid address (the matrix base) for padding loads
 };
 
 template <typename WT> struct MF;
@@ -161,6 +162,45 @@ template <> struct MF<float> {
   static constexpr int KSZ = 16;      // four 16x16x4 MFMAs
   static constexpr int GE = 4;
 };
+
+// Slot of a GEMM's packed stream in BatchArgs::pk.
+__host__ __device__ inline int pk_index(int kind, int l) {
+  return kind == BK_PROJ ? 0 : (kind == BK_HEAD ? 1 : 2 + 4 * l + (kind - BK_QKV));
+}
+
+// Packed weight streams.  Rows are split over the workgroups exactly as the
+// GEMM phase splits them (split_rows); the SwiGLU phase's rows are the
+// workgroup's w1 rows followed by the same w3 rows.  A workgroup's rows are
+// cut into tiles of 16 (the last one may be shorter, rt rows) and each tile
+// into k-steps of KSZ columns; the k-step of a tile is rt * 64 contiguous
+// bytes, row after row, each row's 64 bytes being the four GE-element pieces
+// the MFMA lane groups 0..3 read.  So every weight load of a wave is one
+// contiguous run (16 rows x 64 bytes), and a workgroup's whole phase is one
+// contiguous stream.  Columns past K are zero.  Workgroup b's stream starts
+// at row (or for SwiGLU, 2 x row) r0 of a matrix of k-steps * 64-byte rows.
+template <typename WT>
+__global__ void __launch_bounds__(256) b_pack_kernel(const WT* wa, const WT* wb, int R, int K, char* dst) {
+  constexpr int KSZ = MF<WT>::KSZ, GE = MF<WT>::GE, NG = KSZ / GE;
+  int r0, r1;
+  split_rows(R, blockIdx.x, gridDim.x, r0, r1);
+  const int nr = r1 - r0;
+  const int NR = wb ? 2 * nr : nr;
+  const int KST = (K + KSZ - 1) / KSZ;
+  const long long kp = (long long)KST * 64;
+  char* base = dst + (long long)(wb ? 2 * r0 : r0) * kp;
+  const long long n = (long long)NR * KST * NG;
+  for (long long idx = threadIdx.x; idx < n; idx += 256) {
+    const int i = (int)(idx / (KST * NG));
+    const int q = (int)(idx - (long long)i * KST * NG);
+    const int st = q / NG, kg = q - st * NG;
+    const int c = st * KSZ + kg * GE;
+    const WT* src = (wb && i >= nr) ? wb + (long long)(r0 + i - nr) * K : wa + (long long)(r0 + i) * K;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (c < K) v = *reinterpret_cast<const uint4*>(src + c);   // K is a multiple of GE
+    const int t = i >> 4, ii = i & 15, rt = min(16, NR - 16 * t);
+    *reinterpret_cast<uint4*>(base + (long long)16 * t * kp + (long long)st * rt * 64 + ii * 64 + kg * 16) = v;
+  }
+}
 
 // two floats -> two bf16 (round to nearest even), a in the low half
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -248,11 +288,14 @@ __device__ __forceinline__ void b_load(const BatchArgs& a, const BLds& s, const 
   const int col = (live ? st : 0) * KSZ + GE * (lane >> 4);
   const bool colok = col < gd.K;              // past the last column X is zero (weights: column 0)
   const int c = colok ? col : 0;
+  // weights from the packed stream: tile t's k-step is rt rows of 64 bytes
+  // (lanes past a short tile's rows re-read its last row)
+  const int sp = live ? st : 0;
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
-    const int v = min(16 * t + (lane & 15), gd.R - 1);
-    const char* row = v < gd.R1 ? gd.wa + (long long)v * gd.ldb : gd.wb + (long long)(v - gd.R1) * gd.ldb;
-    load16_nt(u.w[t], row + (long long)c * sizeof(WT));
+    const int rt = min(16, gd.R - 16 * t);
+    const int i = min(lane & 15, rt - 1);
+    load16_nt(u.w[t], gd.pk + (long long)16 * t * gd.kp + (long long)sp * rt * 64 + i * 64 + (lane >> 4) * 16);
   }
 #pragma unroll
   for (int mt = 0; mt < MTT; ++mt) {
@@ -438,46 +481,41 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   GemmDesc gd;
   gd.kind = kind; gd.step = step; gd.l = l;
   gd.normw = nullptr;
-  gd.wb = nullptr;
   int r0 = 0, r1 = 0;
   const LayerPtr& L = a.L[l];
   switch (kind) {
     case BK_PROJ:
       split_rows(a.dim, blk, P, r0, r1);
-      gd.wa = (const char*)a.proj; gd.ldb = (long long)a.in_dim * sizeof(WT); gd.K = a.in_dim; gd.M = a.Bq;
+      gd.K = a.in_dim; gd.M = a.Bq;
       break;
     case BK_QKV:
       split_rows(a.qkv_dim, blk, P, r0, r1);
-      gd.wa = (const char*)L.wqkv; gd.ldb = (long long)a.dim * sizeof(WT); gd.K = a.dim; gd.M = b_rows(a, step);
+      gd.K = a.dim; gd.M = b_rows(a, step);
       gd.normw = L.attn_norm;
       break;
     case BK_WO:
       split_rows(a.dim, blk, P, r0, r1);
-      gd.wa = (const char*)L.wo; gd.ldb = (long long)a.attn_dim * sizeof(WT); gd.K = a.attn_dim; gd.M = b_rows(a, step);
+      gd.K = a.attn_dim; gd.M = b_rows(a, step);
       break;
     case BK_UP:
       split_rows(a.ffn, blk, P, r0, r1);
-      gd.wa = (const char*)L.w1; gd.wb = (const char*)L.w3; gd.ldb = (long long)a.dim * sizeof(WT); gd.K = a.dim;
-      gd.M = b_rows(a, step);
+      gd.K = a.dim; gd.M = b_rows(a, step);
       gd.normw = L.ffn_norm;
       break;
     case BK_DOWN:
       split_rows(a.dim, blk, P, r0, r1);
-      gd.wa = (const char*)L.w2; gd.ldb = (long long)a.ffn * sizeof(WT); gd.K = a.ffn; gd.M = b_rows(a, step);
+      gd.K = a.ffn; gd.M = b_rows(a, step);
       break;
     default:
       split_rows(a.V, blk, P, r0, r1);
-      gd.wa = (const char*)a.outw; gd.ldb = (long long)a.dim * sizeof(WT); gd.K = a.dim; gd.M = a.Bq;
+      gd.K = a.dim; gd.M = a.Bq;
       gd.normw = a.fnorm;
       break;
   }
   const int nr = r1 - r0;
-  gd.dummy = gd.wa;
-  gd.wa += (long long)r0 * gd.ldb;
-  if (gd.wb) gd.wb += (long long)r0 * gd.ldb;
-  gd.R1 = nr;
   gd.R = kind == BK_UP ? 2 * nr : nr;
-  if (!gd.wb) gd.wb = gd.wa;
+  gd.kp = (long long)((gd.K + MF<WT>::KSZ - 1) / MF<WT>::KSZ) * 64;
+  gd.pk = a.pk[pk_index(kind, l)] + (long long)(kind == BK_UP ? 2 * r0 : r0) * gd.kp;
   const RedView rv = b_gemm<WT>(a, s, gd);
   mark(a, s.flag[1], 4);
   const int M = gd.M;
