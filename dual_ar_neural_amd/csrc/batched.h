@@ -49,6 +49,12 @@ struct BatchArgs {
   // each GEMM's weights repacked into one contiguous stream per workgroup
   // (b_pack_kernel), indexed by pk_index(kind, layer)
   const char* pk[2 + 4 * S2FAST_MAX_LAYERS];
+  // w2 split over its K columns: ks_down workgroups share a row group, each
+  // adds its partial sums into dacc (fixed point) and the last of them (by
+  // the dcnt count) writes x = x_mid + sum and clears both for the next frame
+  int ks_down;
+  long long* dacc;          // [slot][MP_MAX][dim]
+  int* dcnt;                // [slot][P / ks_down]
   int Bq;                   // requests in this launch, 1..BQ_MAX
   const float* hidden;      // [Bq][in_dim]
   const int* sem_code;      // [Bq]
@@ -125,6 +131,7 @@ __device__ __forceinline__ float* bxmid(const BatchArgs& a, int step, int l) { r
 __device__ __forceinline__ float* bqkv(const BatchArgs& a, int step, int l) { return a.qkv + b_slot(a, step, l) * a.qkv_slot; }
 __device__ __forceinline__ float* batt(const BatchArgs& a, int step, int l) { return a.att + b_slot(a, step, l) * a.att_slot; }
 __device__ __forceinline__ float* bg(const BatchArgs& a, int step, int l) { return a.g + b_slot(a, step, l) * a.g_slot; }
+__device__ __forceinline__ long long* bdacc(const BatchArgs& a, int step, int l) { return a.dacc + b_slot(a, step, l) * a.x_slot; }
 __device__ __forceinline__ float* blogits(const BatchArgs& a, int step) { return a.logits + (size_t)(step - 1) * a.logits_slot; }
 __device__ __forceinline__ float* bkv(const BatchArgs& a, int b, int l, int pos, int g) {
   return a.kv + ((((size_t)b * a.n_layer + l) * a.ctx_len + pos) * a.n_kv + g) * 2 * a.hd;
@@ -147,7 +154,8 @@ struct GemmDesc {
   const char* pk;      // this workgroup's packed weight stream (b_pack_kernel layout)
   long long kp;        // bytes of one packed row: k-steps * 64
   int R;               // rows (for the SwiGLU phase: w1 rows, then the same w3 rows)
-  int K;               // columns
+  int K;               // columns (of this workgroup's K slice)
+  int k0;              // first column of the slice
   int M;               // rows of X (<= MP_MAX)
   int kind, step, l;
   const void* normw;   // RMSNorm weight over K, or nullptr
@@ -178,16 +186,23 @@ __host__ __device__ inline int pk_index(int kind, int l) {
 // contiguous run (16 rows x 64 bytes), and a workgroup's whole phase is one
 // contiguous stream.  Columns past K are zero.  Workgroup b's stream starts
 // at row (or for SwiGLU, 2 x row) r0 of a matrix of k-steps * 64-byte rows.
+//
+// With a K split S (gridDim.x a multiple of S), workgroup b packs row group
+// b / S of gridDim.x / S and the columns [ks Ks, (ks + 1) Ks) of its slice
+// ks = b % S, Ks = K / S; the S slices of a row group follow each other, so
+// the stream starts at row r0 S + ks nr of a matrix of Ks-column rows.
 template <typename WT>
-__global__ void __launch_bounds__(256) b_pack_kernel(const WT* wa, const WT* wb, int R, int K, char* dst) {
+__global__ void __launch_bounds__(256) b_pack_kernel(const WT* wa, const WT* wb, int R, int K, int S, char* dst) {
   constexpr int KSZ = MF<WT>::KSZ, GE = MF<WT>::GE, NG = KSZ / GE;
+  const int rg = blockIdx.x / S, ks = blockIdx.x - rg * S;
   int r0, r1;
-  split_rows(R, blockIdx.x, gridDim.x, r0, r1);
+  split_rows(R, rg, gridDim.x / S, r0, r1);
   const int nr = r1 - r0;
   const int NR = wb ? 2 * nr : nr;
-  const int KST = (K + KSZ - 1) / KSZ;
+  const int Ks = K / S, c0 = ks * Ks;
+  const int KST = (Ks + KSZ - 1) / KSZ;
   const long long kp = (long long)KST * 64;
-  char* base = dst + (long long)(wb ? 2 * r0 : r0) * kp;
+  char* base = dst + (long long)(wb ? 2 * r0 : r0 * S + ks * nr) * kp;
   const long long n = (long long)NR * KST * NG;
   for (long long idx = threadIdx.x; idx < n; idx += 256) {
     const int i = (int)(idx / (KST * NG));
@@ -196,7 +211,7 @@ __global__ void __launch_bounds__(256) b_pack_kernel(const WT* wa, const WT* wb,
     const int c = st * KSZ + kg * GE;
     const WT* src = (wb && i >= nr) ? wb + (long long)(r0 + i - nr) * K : wa + (long long)(r0 + i) * K;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (c < K) v = *reinterpret_cast<const uint4*>(src + c);   // K is a multiple of GE
+    if (c < Ks) v = *reinterpret_cast<const uint4*>(src + c0 + c);   // Ks is a multiple of GE
     const int t = i >> 4, ii = i & 15, rt = min(16, NR - 16 * t);
     *reinterpret_cast<uint4*>(base + (long long)16 * t * kp + (long long)st * rt * 64 + ii * 64 + kg * 16) = v;
   }
@@ -301,7 +316,7 @@ __device__ __forceinline__ void b_load(const BatchArgs& a, const BLds& s, const 
   for (int mt = 0; mt < MTT; ++mt) {
     const int m = 16 * mt + (lane & 15);
     u.ok[mt] = live && colok && m < gd.M;
-    b_fetch<WT>(a, s, gd, m < gd.M ? m : 0, c, u.x[mt]);
+    b_fetch<WT>(a, s, gd, m < gd.M ? m : 0, gd.k0 + c, u.x[mt]);
   }
 }
 
@@ -481,7 +496,9 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   GemmDesc gd;
   gd.kind = kind; gd.step = step; gd.l = l;
   gd.normw = nullptr;
-  int r0 = 0, r1 = 0;
+  gd.k0 = 0;
+  int r0 = 0, r1 = 0, ks = 0;
+  const int S = kind == BK_DOWN ? a.ks_down : 1;
   const LayerPtr& L = a.L[l];
   switch (kind) {
     case BK_PROJ:
@@ -503,8 +520,9 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       gd.normw = L.ffn_norm;
       break;
     case BK_DOWN:
-      split_rows(a.dim, blk, P, r0, r1);
-      gd.K = a.ffn; gd.M = b_rows(a, step);
+      ks = blk % S;
+      split_rows(a.dim, blk / S, P / S, r0, r1);
+      gd.K = a.ffn / S; gd.k0 = ks * gd.K; gd.M = b_rows(a, step);
       break;
     default:
       split_rows(a.V, blk, P, r0, r1);
@@ -515,7 +533,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   const int nr = r1 - r0;
   gd.R = kind == BK_UP ? 2 * nr : nr;
   gd.kp = (long long)((gd.K + MF<WT>::KSZ - 1) / MF<WT>::KSZ) * 64;
-  gd.pk = a.pk[pk_index(kind, l)] + (long long)(kind == BK_UP ? 2 * r0 : r0) * gd.kp;
+  gd.pk = a.pk[pk_index(kind, l)] + (long long)(kind == BK_UP ? 2 * r0 : r0 * S + ks * nr) * gd.kp;
   const RedView rv = b_gemm<WT>(a, s, gd);
   mark(a, s.flag[1], 4);
   const int M = gd.M;
@@ -540,7 +558,8 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       }
       case BK_DOWN: {
         const int k = r0 + v;
-        st_coh(bx(a, step, l) + (size_t)m * a.dim + k, bxmid(a, step, l)[(size_t)m * a.dim + k] + d);
+        if (S > 1) atomic_add_coh(bdacc(a, step, l) + (size_t)m * a.dim + k, to_fx(d));
+        else st_coh(bx(a, step, l) + (size_t)m * a.dim + k, bxmid(a, step, l)[(size_t)m * a.dim + k] + d);
         break;
       }
       default: {
@@ -549,6 +568,25 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
         if (a.logits_out) a.logits_out[((size_t)m * (a.ncb - 1) + (step - 1)) * a.V + r0 + v] = y;
         break;
       }
+    }
+  }
+  if (kind == BK_DOWN && S > 1) {
+    // the row group's last contributor: x = x_mid + sum of the K slices, and
+    // the accumulator and count cleared for the next frame
+    long long* acc = bdacc(a, step, l);
+    int* cnt = a.dcnt + b_slot(a, step, l) * (P / S) + blk / S;
+    wait_vmem();        // this workgroup's additions have completed
+    __syncthreads();
+    if (tidx() == 0) s.flag[3] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    __syncthreads();
+    if (s.flag[3]) {
+      for (int o = tidx(); o < nr * M; o += NTHREADS) {
+        const int m = o % M, k = r0 + o / M;
+        const size_t e = (size_t)m * a.dim + k;
+        st_coh(bx(a, step, l) + e, bxmid(a, step, l)[e] + from_fx(ld_coh(acc + e)));
+        st_coh(acc + e, 0ll);
+      }
+      if (tidx() == 0) st_coh(cnt, 0);
     }
   }
   mark(a, s.flag[1], 5);

@@ -1203,6 +1203,9 @@ struct s2fast_ctx {
   float* b_kv = nullptr;
   int* b_codes = nullptr;
   char* b_pk = nullptr;                          // packed weight streams of the batched GEMMs
+  long long* b_dacc = nullptr;                   // w2 K-split accumulators [slot][x_slot]
+  int* b_dcnt = nullptr;                         // and their per-row-group counts [slot][P]
+  int b_ks_down = 1;
   long long b_pk_off[2 + 4 * S2FAST_MAX_LAYERS] = {};
 };
 
@@ -1241,7 +1244,7 @@ void free_ctx(s2fast_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->rope, c->qkv0, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog,
                   c->b_xin0, c->b_x, c->b_xmid, c->b_qkv, c->b_att, c->b_g, c->b_logits, c->b_kv, c->b_codes,
-                  c->b_pk};
+                  c->b_pk, c->b_dacc, c->b_dcnt};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -1258,23 +1261,23 @@ int pack_batched(s2fast_ctx* c) {
   const s2fast_config& k = c->cfg;
   const int qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim, attn_dim = k.n_head * k.head_dim;
   const int ksz = k.weight_dtype == S2FAST_BF16 ? 32 : 16;
-  struct Job { int idx; const void* wa; const void* wb; int R, K; };
+  struct Job { int idx; const void* wa; const void* wb; int R, K, S; };
   Job jobs[2 + 4 * S2FAST_MAX_LAYERS];
   int nj = 0;
-  if (k.has_project_in) jobs[nj++] = {0, c->w.project_in, nullptr, k.dim, k.in_dim};
-  jobs[nj++] = {1, c->w.output, nullptr, k.codebook_size, k.dim};
+  if (k.has_project_in) jobs[nj++] = {0, c->w.project_in, nullptr, k.dim, k.in_dim, 1};
+  jobs[nj++] = {1, c->w.output, nullptr, k.codebook_size, k.dim, 1};
   for (int l = 0; l < k.n_layer; ++l) {
     const s2fast_layer_weights& L = c->w.layers[l];
-    jobs[nj++] = {2 + 4 * l + 0, L.wqkv, nullptr, qkv_dim, k.dim};
-    jobs[nj++] = {2 + 4 * l + 1, L.wo, nullptr, k.dim, attn_dim};
-    jobs[nj++] = {2 + 4 * l + 2, L.w1, L.w3, k.ffn_dim, k.dim};
-    jobs[nj++] = {2 + 4 * l + 3, L.w2, nullptr, k.dim, k.ffn_dim};
+    jobs[nj++] = {2 + 4 * l + 0, L.wqkv, nullptr, qkv_dim, k.dim, 1};
+    jobs[nj++] = {2 + 4 * l + 1, L.wo, nullptr, k.dim, attn_dim, 1};
+    jobs[nj++] = {2 + 4 * l + 2, L.w1, L.w3, k.ffn_dim, k.dim, 1};
+    jobs[nj++] = {2 + 4 * l + 3, L.w2, nullptr, k.dim, k.ffn_dim, c->b_ks_down};
   }
   long long total = 0;
   for (int j = 0; j < nj; ++j) {
     c->b_pk_off[jobs[j].idx] = total;
-    const long long rows = (long long)jobs[j].R * (jobs[j].wb ? 2 : 1);
-    total += rows * ((jobs[j].K + ksz - 1) / ksz) * 64;
+    const long long rows = (long long)jobs[j].R * (jobs[j].wb ? 2 : 1) * jobs[j].S;
+    total += rows * ((jobs[j].K / jobs[j].S + ksz - 1) / ksz) * 64;
     total = (total + 255) / 256 * 256;
   }
   if (dalloc(&c->b_pk, (size_t)total) != hipSuccess) return S2FAST_ERR_NOMEM;
@@ -1283,10 +1286,10 @@ int pack_batched(s2fast_ctx* c) {
     if (k.weight_dtype == S2FAST_BF16)
       hipLaunchKernelGGL(b_pack_kernel<uint16_t>, dim3(c->ncu), dim3(256), 0, 0,
                          static_cast<const uint16_t*>(jobs[j].wa), static_cast<const uint16_t*>(jobs[j].wb),
-                         jobs[j].R, jobs[j].K, dst);
+                         jobs[j].R, jobs[j].K, jobs[j].S, dst);
     else
       hipLaunchKernelGGL(b_pack_kernel<float>, dim3(c->ncu), dim3(256), 0, 0, static_cast<const float*>(jobs[j].wa),
-                         static_cast<const float*>(jobs[j].wb), jobs[j].R, jobs[j].K, dst);
+                         static_cast<const float*>(jobs[j].wb), jobs[j].R, jobs[j].K, jobs[j].S, dst);
   }
   return (hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess) ? S2FAST_OK : S2FAST_ERR_HIP;
 }
@@ -1372,6 +1375,7 @@ void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
   ba.rope = c->rope;
   ba.qkv0 = c->qkv0;
   for (int i = 0; i < 2 + 4 * S2FAST_MAX_LAYERS; ++i) ba.pk[i] = c->b_pk + c->b_pk_off[i];
+  ba.ks_down = c->b_ks_down; ba.dacc = c->b_dacc; ba.dcnt = c->b_dcnt;
   ba.xin0 = c->b_xin0; ba.x = c->b_x; ba.xmid = c->b_xmid; ba.qkv = c->b_qkv; ba.att = c->b_att; ba.g = c->b_g;
   ba.logits = c->b_logits; ba.kv = c->b_kv; ba.codes = c->b_codes;
   ba.x_slot = c->bx_slot; ba.qkv_slot = c->bqkv_slot; ba.att_slot = c->batt_slot; ba.g_slot = c->bg_slot;
@@ -1576,6 +1580,16 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
            dalloc(&c->b_logits, (size_t)((k.num_codebooks - 1) * c->blogits_slot)) == hipSuccess &&
            dalloc(&c->b_kv, (size_t)BQ_MAX * k.n_layer * k.context * k.n_head_kv * 2 * k.head_dim) == hipSuccess &&
            dalloc(&c->b_codes, (size_t)BQ_MAX * 16) == hipSuccess;
+      if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
+      // w2 split four ways over K when the row groups and the slices fit
+      // the GEMM's tiles (at most TMAX x 16 rows, whole k-steps)
+      const int ksz = k.weight_dtype == S2FAST_BF16 ? 32 : 16;
+      const int ks = 4;
+      c->b_ks_down = (P % ks == 0 && k.ffn_dim % (ks * ksz) == 0 && (k.dim + P / ks - 1) / (P / ks) <= 16 * TMAX) ? ks : 1;
+      ok = dalloc(&c->b_dacc, (size_t)(slots * c->bx_slot)) == hipSuccess &&
+           dalloc(&c->b_dcnt, (size_t)(slots * P)) == hipSuccess &&
+           hipMemset(c->b_dacc, 0, (size_t)(slots * c->bx_slot) * sizeof(long long)) == hipSuccess &&
+           hipMemset(c->b_dcnt, 0, (size_t)(slots * P) * sizeof(int)) == hipSuccess;
       if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
       const int pst = pack_batched(c);
       if (pst != S2FAST_OK) { free_ctx(c); return pst; }
