@@ -49,12 +49,13 @@ struct BatchArgs {
   // each GEMM's weights repacked into one contiguous stream per workgroup
   // (b_pack_kernel), indexed by pk_index(kind, layer)
   const char* pk[2 + 4 * S2FAST_MAX_LAYERS];
-  // w2 split over its K columns: ks_down workgroups share a row group, each
-  // adds its partial sums into dacc (fixed point) and the last of them (by
-  // the dcnt count) writes x = x_mid + sum and clears both for the next frame
-  int ks_down;
-  long long* dacc;          // [slot][MP_MAX][dim]
-  int* dcnt;                // [slot][P / ks_down]
+  // wo and w2 split over their K columns: ks[kind] workgroups share a row
+  // group, each adds its partial sums into kacc[kind] (fixed point) and the
+  // last of them (by the kcnt[kind] count) writes the phase's output and
+  // clears both for the next frame; ks 1: no split
+  int ks[6];
+  long long* kacc[6];       // [slot][MP_MAX][dim]
+  int* kcnt[6];             // [slot][P / ks]
   int Bq;                   // requests in this launch, 1..BQ_MAX
   const float* hidden;      // [Bq][in_dim]
   const int* sem_code;      // [Bq]
@@ -131,7 +132,9 @@ __device__ __forceinline__ float* bxmid(const BatchArgs& a, int step, int l) { r
 __device__ __forceinline__ float* bqkv(const BatchArgs& a, int step, int l) { return a.qkv + b_slot(a, step, l) * a.qkv_slot; }
 __device__ __forceinline__ float* batt(const BatchArgs& a, int step, int l) { return a.att + b_slot(a, step, l) * a.att_slot; }
 __device__ __forceinline__ float* bg(const BatchArgs& a, int step, int l) { return a.g + b_slot(a, step, l) * a.g_slot; }
-__device__ __forceinline__ long long* bdacc(const BatchArgs& a, int step, int l) { return a.dacc + b_slot(a, step, l) * a.x_slot; }
+__device__ __forceinline__ long long* bkacc(const BatchArgs& a, int kind, int step, int l) {
+  return a.kacc[kind] + b_slot(a, step, l) * a.x_slot;
+}
 __device__ __forceinline__ float* blogits(const BatchArgs& a, int step) { return a.logits + (size_t)(step - 1) * a.logits_slot; }
 __device__ __forceinline__ float* bkv(const BatchArgs& a, int b, int l, int pos, int g) {
   return a.kv + ((((size_t)b * a.n_layer + l) * a.ctx_len + pos) * a.n_kv + g) * 2 * a.hd;
@@ -498,7 +501,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   gd.normw = nullptr;
   gd.k0 = 0;
   int r0 = 0, r1 = 0, ks = 0;
-  const int S = kind == BK_DOWN ? a.ks_down : 1;
+  const int S = a.ks[kind];
   const LayerPtr& L = a.L[l];
   switch (kind) {
     case BK_PROJ:
@@ -511,8 +514,9 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       gd.normw = L.attn_norm;
       break;
     case BK_WO:
-      split_rows(a.dim, blk, P, r0, r1);
-      gd.K = a.attn_dim; gd.M = b_rows(a, step);
+      ks = blk % S;
+      split_rows(a.dim, blk / S, P / S, r0, r1);
+      gd.K = a.attn_dim / S; gd.k0 = ks * gd.K; gd.M = b_rows(a, step);
       break;
     case BK_UP:
       split_rows(a.ffn, blk, P, r0, r1);
@@ -546,8 +550,12 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       case BK_QKV: st_coh(bqkv(a, step, l) + (size_t)m * a.qkv_dim + r0 + v, d / s.rms[m]); break;
       case BK_WO: {
         const int k = r0 + v;
-        const float xin = l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[(size_t)m * a.dim + k];
-        st_coh(bxmid(a, step, l) + (size_t)m * a.dim + k, xin + d);
+        if (S > 1) {
+          atomic_add_coh(bkacc(a, kind, step, l) + (size_t)m * a.dim + k, to_fx(d));
+        } else {
+          const float xin = l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[(size_t)m * a.dim + k];
+          st_coh(bxmid(a, step, l) + (size_t)m * a.dim + k, xin + d);
+        }
         break;
       }
       case BK_UP: {
@@ -558,7 +566,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       }
       case BK_DOWN: {
         const int k = r0 + v;
-        if (S > 1) atomic_add_coh(bdacc(a, step, l) + (size_t)m * a.dim + k, to_fx(d));
+        if (S > 1) atomic_add_coh(bkacc(a, kind, step, l) + (size_t)m * a.dim + k, to_fx(d));
         else st_coh(bx(a, step, l) + (size_t)m * a.dim + k, bxmid(a, step, l)[(size_t)m * a.dim + k] + d);
         break;
       }
@@ -570,11 +578,12 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       }
     }
   }
-  if (kind == BK_DOWN && S > 1) {
-    // the row group's last contributor: x = x_mid + sum of the K slices, and
-    // the accumulator and count cleared for the next frame
-    long long* acc = bdacc(a, step, l);
-    int* cnt = a.dcnt + b_slot(a, step, l) * (P / S) + blk / S;
+  if (S > 1) {
+    // the row group's last contributor: the output from the sum of the K
+    // slices (wo: x_mid = x_in + sum; w2: x = x_mid + sum), and the
+    // accumulator and count cleared for the next frame
+    long long* acc = bkacc(a, kind, step, l);
+    int* cnt = a.kcnt[kind] + b_slot(a, step, l) * (P / S) + blk / S;
     wait_vmem();        // this workgroup's additions have completed
     __syncthreads();
     if (tidx() == 0) s.flag[3] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
@@ -583,7 +592,13 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       for (int o = tidx(); o < nr * M; o += NTHREADS) {
         const int m = o % M, k = r0 + o / M;
         const size_t e = (size_t)m * a.dim + k;
-        st_coh(bx(a, step, l) + e, bxmid(a, step, l)[e] + from_fx(ld_coh(acc + e)));
+        const float sum = from_fx(ld_coh(acc + e));
+        if (kind == BK_WO) {
+          const float xin = l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[e];
+          st_coh(bxmid(a, step, l) + e, xin + sum);
+        } else {
+          st_coh(bx(a, step, l) + e, bxmid(a, step, l)[e] + sum);
+        }
         st_coh(acc + e, 0ll);
       }
       if (tidx() == 0) st_coh(cnt, 0);

@@ -1162,6 +1162,10 @@ __global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const WT* e
 
 #include "batched.h"
 
+#ifndef KS_DOWN
+#define KS_DOWN 4
+#endif
+
 }  // namespace
 
 // =================================================================== host
@@ -1203,9 +1207,9 @@ struct s2fast_ctx {
   float* b_kv = nullptr;
   int* b_codes = nullptr;
   char* b_pk = nullptr;                          // packed weight streams of the batched GEMMs
-  long long* b_dacc = nullptr;                   // w2 K-split accumulators [slot][x_slot]
-  int* b_dcnt = nullptr;                         // and their per-row-group counts [slot][P]
-  int b_ks_down = 1;
+  long long* b_kacc[6] = {};                     // K-split accumulators of wo and w2 [slot][x_slot]
+  int* b_kcnt[6] = {};                           // and their per-row-group counts [slot][P]
+  int b_ks[6] = {1, 1, 1, 1, 1, 1};              // K split of each batched GEMM kind
   long long b_pk_off[2 + 4 * S2FAST_MAX_LAYERS] = {};
 };
 
@@ -1244,7 +1248,7 @@ void free_ctx(s2fast_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->rope, c->qkv0, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog,
                   c->b_xin0, c->b_x, c->b_xmid, c->b_qkv, c->b_att, c->b_g, c->b_logits, c->b_kv, c->b_codes,
-                  c->b_pk, c->b_dacc, c->b_dcnt};
+                  c->b_pk, c->b_kacc[BK_WO], c->b_kcnt[BK_WO], c->b_kacc[BK_DOWN], c->b_kcnt[BK_DOWN]};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -1269,9 +1273,9 @@ int pack_batched(s2fast_ctx* c) {
   for (int l = 0; l < k.n_layer; ++l) {
     const s2fast_layer_weights& L = c->w.layers[l];
     jobs[nj++] = {2 + 4 * l + 0, L.wqkv, nullptr, qkv_dim, k.dim, 1};
-    jobs[nj++] = {2 + 4 * l + 1, L.wo, nullptr, k.dim, attn_dim, 1};
+    jobs[nj++] = {2 + 4 * l + 1, L.wo, nullptr, k.dim, attn_dim, c->b_ks[BK_WO]};
     jobs[nj++] = {2 + 4 * l + 2, L.w1, L.w3, k.ffn_dim, k.dim, 1};
-    jobs[nj++] = {2 + 4 * l + 3, L.w2, nullptr, k.dim, k.ffn_dim, c->b_ks_down};
+    jobs[nj++] = {2 + 4 * l + 3, L.w2, nullptr, k.dim, k.ffn_dim, c->b_ks[BK_DOWN]};
   }
   long long total = 0;
   for (int j = 0; j < nj; ++j) {
@@ -1375,7 +1379,7 @@ void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
   ba.rope = c->rope;
   ba.qkv0 = c->qkv0;
   for (int i = 0; i < 2 + 4 * S2FAST_MAX_LAYERS; ++i) ba.pk[i] = c->b_pk + c->b_pk_off[i];
-  ba.ks_down = c->b_ks_down; ba.dacc = c->b_dacc; ba.dcnt = c->b_dcnt;
+  for (int kd = 0; kd < 6; ++kd) { ba.ks[kd] = c->b_ks[kd]; ba.kacc[kd] = c->b_kacc[kd]; ba.kcnt[kd] = c->b_kcnt[kd]; }
   ba.xin0 = c->b_xin0; ba.x = c->b_x; ba.xmid = c->b_xmid; ba.qkv = c->b_qkv; ba.att = c->b_att; ba.g = c->b_g;
   ba.logits = c->b_logits; ba.kv = c->b_kv; ba.codes = c->b_codes;
   ba.x_slot = c->bx_slot; ba.qkv_slot = c->bqkv_slot; ba.att_slot = c->batt_slot; ba.g_slot = c->bg_slot;
@@ -1581,16 +1585,23 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
            dalloc(&c->b_kv, (size_t)BQ_MAX * k.n_layer * k.context * k.n_head_kv * 2 * k.head_dim) == hipSuccess &&
            dalloc(&c->b_codes, (size_t)BQ_MAX * 16) == hipSuccess;
       if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
-      // w2 split four ways over K when the row groups and the slices fit
-      // the GEMM's tiles (at most TMAX x 16 rows, whole k-steps)
+      // w2 (the widest K) split KS_DOWN ways over K when the row groups and
+      // the slices fit the GEMM's tiles (at most TMAX x 16 rows, whole
+      // k-steps).  wo could split the same way, but with its K of 4096 the
+      // saved activation reads do not pay for the accumulate-and-finalise
+      // round trips.
       const int ksz = k.weight_dtype == S2FAST_BF16 ? 32 : 16;
-      const int ks = 4;
-      c->b_ks_down = (P % ks == 0 && k.ffn_dim % (ks * ksz) == 0 && (k.dim + P / ks - 1) / (P / ks) <= 16 * TMAX) ? ks : 1;
-      ok = dalloc(&c->b_dacc, (size_t)(slots * c->bx_slot)) == hipSuccess &&
-           dalloc(&c->b_dcnt, (size_t)(slots * P)) == hipSuccess &&
-           hipMemset(c->b_dacc, 0, (size_t)(slots * c->bx_slot) * sizeof(long long)) == hipSuccess &&
-           hipMemset(c->b_dcnt, 0, (size_t)(slots * P) * sizeof(int)) == hipSuccess;
-      if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
+      const int ks = KS_DOWN;
+      const bool rows_fit = P % ks == 0 && (k.dim + P / ks - 1) / (P / ks) <= 16 * TMAX;
+      c->b_ks[BK_DOWN] = (rows_fit && k.ffn_dim % (ks * ksz) == 0) ? ks : 1;
+      for (int kd : {(int)BK_WO, (int)BK_DOWN}) {
+        if (c->b_ks[kd] == 1) continue;
+        ok = dalloc(&c->b_kacc[kd], (size_t)(slots * c->bx_slot)) == hipSuccess &&
+             dalloc(&c->b_kcnt[kd], (size_t)(slots * P)) == hipSuccess &&
+             hipMemset(c->b_kacc[kd], 0, (size_t)(slots * c->bx_slot) * sizeof(long long)) == hipSuccess &&
+             hipMemset(c->b_kcnt[kd], 0, (size_t)(slots * P) * sizeof(int)) == hipSuccess;
+        if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
+      }
       const int pst = pack_batched(c);
       if (pst != S2FAST_OK) { free_ctx(c); return pst; }
     }
