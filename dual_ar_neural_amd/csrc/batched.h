@@ -25,8 +25,9 @@
 //
 // Included by s2fast.hip inside its anonymous namespace.
 
-constexpr int BQ_MAX = 16;               // requests per batched launch
+constexpr int BQ_MAX = 32;               // requests per batched launch
 constexpr int MP_MAX = 2 * BQ_MAX;       // rows per decode step at most
+constexpr int GM_MAX = 32;               // rows of one GEMM pass (two 16-row M-tiles)
 constexpr int XF_BYTES = 128 * 1024;     // LDS for the GEMM partial sums and the attention scratch
 constexpr int TMAX = 5;                  // 16-row tiles of W per workgroup and phase
 constexpr int RED_TILES = 10;            // tiles x M-tiles the reduction buffer holds
@@ -159,7 +160,8 @@ struct GemmDesc {
   int R;               // rows (for the SwiGLU phase: w1 rows, then the same w3 rows)
   int K;               // columns (of this workgroup's K slice)
   int k0;              // first column of the slice
-  int M;               // rows of X (<= MP_MAX)
+  int m0;              // first row of X of this pass
+  int M;               // rows of X (<= GM_MAX in a pass)
   int kind, step, l;
   const void* normw;   // RMSNorm weight over K, or nullptr
 };
@@ -319,7 +321,7 @@ __device__ __forceinline__ void b_load(const BatchArgs& a, const BLds& s, const 
   for (int mt = 0; mt < MTT; ++mt) {
     const int m = 16 * mt + (lane & 15);
     u.ok[mt] = live && colok && m < gd.M;
-    b_fetch<WT>(a, s, gd, m < gd.M ? m : 0, gd.k0 + c, u.x[mt]);
+    b_fetch<WT>(a, s, gd, gd.m0 + (m < gd.M ? m : 0), gd.k0 + c, u.x[mt]);
   }
 }
 
@@ -500,6 +502,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   gd.kind = kind; gd.step = step; gd.l = l;
   gd.normw = nullptr;
   gd.k0 = 0;
+  gd.m0 = 0;
   int r0 = 0, r1 = 0, ks = 0;
   const int S = a.ks[kind];
   const LayerPtr& L = a.L[l];
@@ -538,46 +541,56 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   gd.R = kind == BK_UP ? 2 * nr : nr;
   gd.kp = (long long)((gd.K + MF<WT>::KSZ - 1) / MF<WT>::KSZ) * 64;
   gd.pk = a.pk[pk_index(kind, l)] + (long long)(kind == BK_UP ? 2 * r0 : r0 * S + ks * nr) * gd.kp;
-  const RedView rv = b_gemm<WT>(a, s, gd);
-  mark(a, s.flag[1], 4);
-  const int M = gd.M;
-  const int nv = kind == BK_UP ? nr : gd.R;
-  for (int o = tidx(); o < nv * M; o += NTHREADS) {
-    const int m = o % M, v = o / M;
-    const float d = rv.sum(v, m);
-    switch (kind) {
-      case BK_PROJ: st_coh(a.xin0 + (size_t)m * a.dim + r0 + v, d); break;
-      case BK_QKV: st_coh(bqkv(a, step, l) + (size_t)m * a.qkv_dim + r0 + v, d / s.rms[m]); break;
-      case BK_WO: {
-        const int k = r0 + v;
-        if (S > 1) {
-          atomic_add_coh(bkacc(a, kind, step, l) + (size_t)m * a.dim + k, to_fx(d));
-        } else {
-          const float xin = l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[(size_t)m * a.dim + k];
-          st_coh(bxmid(a, step, l) + (size_t)m * a.dim + k, xin + d);
+  // rows in passes of at most GM_MAX (the MFMA core's M-tiles): a pass
+  // streams this workgroup's weights once
+  const int Mt = gd.M;
+  for (int m0 = 0; m0 < Mt; m0 += GM_MAX) {
+    gd.m0 = m0;
+    gd.M = min(GM_MAX, Mt - m0);
+    const RedView rv = b_gemm<WT>(a, s, gd);
+    mark(a, s.flag[1], 4);
+    const int M = gd.M;
+    const int nv = kind == BK_UP ? nr : gd.R;
+    for (int o = tidx(); o < nv * M; o += NTHREADS) {
+      const int mp = o % M, v = o / M;   // row of the pass, output column
+      const int m = m0 + mp;
+      const float d = rv.sum(v, mp);
+      switch (kind) {
+        case BK_PROJ: st_coh(a.xin0 + (size_t)m * a.dim + r0 + v, d); break;
+        case BK_QKV: st_coh(bqkv(a, step, l) + (size_t)m * a.qkv_dim + r0 + v, d / s.rms[mp]); break;
+        case BK_WO: {
+          const int k = r0 + v;
+          if (S > 1) {
+            atomic_add_coh(bkacc(a, kind, step, l) + (size_t)m * a.dim + k, to_fx(d));
+          } else {
+            const float xin = l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[(size_t)m * a.dim + k];
+            st_coh(bxmid(a, step, l) + (size_t)m * a.dim + k, xin + d);
+          }
+          break;
         }
-        break;
-      }
-      case BK_UP: {
-        // rows v < nr are w1 (gate), rows nr + v are w3 (up) of column r0 + v
-        const float a1 = d / s.rms[m], a3 = rv.sum(nr + v, m) / s.rms[m];
-        st_coh(bg(a, step, l) + (size_t)m * a.ffn + r0 + v, silu(a1) * a3);
-        break;
-      }
-      case BK_DOWN: {
-        const int k = r0 + v;
-        if (S > 1) atomic_add_coh(bkacc(a, kind, step, l) + (size_t)m * a.dim + k, to_fx(d));
-        else st_coh(bx(a, step, l) + (size_t)m * a.dim + k, bxmid(a, step, l)[(size_t)m * a.dim + k] + d);
-        break;
-      }
-      default: {
-        const float y = d / s.rms[m];
-        st_coh(blogits(a, step) + (size_t)m * a.V + r0 + v, y);
-        if (a.logits_out) a.logits_out[((size_t)m * (a.ncb - 1) + (step - 1)) * a.V + r0 + v] = y;
-        break;
+        case BK_UP: {
+          // rows v < nr are w1 (gate), rows nr + v are w3 (up) of column r0 + v
+          const float a1 = d / s.rms[mp], a3 = rv.sum(nr + v, mp) / s.rms[mp];
+          st_coh(bg(a, step, l) + (size_t)m * a.ffn + r0 + v, silu(a1) * a3);
+          break;
+        }
+        case BK_DOWN: {
+          const int k = r0 + v;
+          if (S > 1) atomic_add_coh(bkacc(a, kind, step, l) + (size_t)m * a.dim + k, to_fx(d));
+          else st_coh(bx(a, step, l) + (size_t)m * a.dim + k, bxmid(a, step, l)[(size_t)m * a.dim + k] + d);
+          break;
+        }
+        default: {
+          const float y = d / s.rms[mp];
+          st_coh(blogits(a, step) + (size_t)m * a.V + r0 + v, y);
+          if (a.logits_out) a.logits_out[((size_t)m * (a.ncb - 1) + (step - 1)) * a.V + r0 + v] = y;
+          break;
+        }
       }
     }
+    if (m0 + GM_MAX < Mt) __syncthreads();   // the next pass reuses the partial sums and rms in LDS
   }
+  const int M = Mt;
   if (S > 1) {
     // the row group's last contributor: the output from the sum of the K
     // slices (wo: x_mid = x_in + sum; w2: x = x_mid + sum), and the

@@ -35,7 +35,7 @@ def ragged():
 @pytest.fixture(scope="module")
 def s2pro():
     _announce("s2pro model (bf16, 828 MB)")
-    return pr.make_pair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0), max_batch=20)
+    return pr.make_pair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0), max_batch=32)
 
 
 # ------------------------------------------------------------------ sampler
@@ -162,8 +162,9 @@ def test_s2pro_greedy_b2(s2pro):
 
 
 # ------------------------------------------------------------------ batched decoding
-# Batches of 2..16 requests share one launch (skinny GEMMs on the matrix
-# cores); larger batches run in groups of 16.
+# Batches of 2..32 requests share one launch (skinny GEMMs on the matrix
+# cores, rows in passes of 32: step 1 of a group above 16 takes two);
+# larger batches run in groups of 32.
 
 def test_s2pro_b16_batched(s2pro):
     w = si.WORKLOADS["s2pro_b16"]          # per-request temperature / top_p, Zipf semantic codes
@@ -178,36 +179,36 @@ def test_s2pro_b16_batched(s2pro):
 
 
 def test_s2pro_batched_teacher_forced_all_rows(s2pro):
-    """Teacher-forced logits of a full group of 16 (every row of the skinny
-    GEMMs, both M-tiles at step 1)."""
+    """Teacher-forced logits of a full group of 32 (every row of the skinny
+    GEMMs; step 1's 64 rows in two passes)."""
     w = si.WORKLOADS["s2pro_b16"]
-    fr = _frames(w, 1, 16)
+    fr = _frames(w, 1, 32)
     rng = np.random.default_rng(5)
-    codes = rng.integers(0, w.shape.codebook_size, size=(16, w.shape.num_codebooks)).astype(np.int32)
+    codes = rng.integers(0, w.shape.codebook_size, size=(32, w.shape.num_codebooks)).astype(np.int32)
     worst, rel, _, _ = pr.check_logits(s2pro, fr["hidden"][0], codes)
-    _announce(f"s2pro B=16 teacher-forced: worst |d|/tol {worst:.2e}, |d|/max {rel:.2e}")
+    _announce(f"s2pro B=32 teacher-forced: worst |d|/tol {worst:.2e}, |d|/max {rel:.2e}")
     assert worst <= 1.0 and rel < 1e-3, (worst, rel)
 
 
 def test_two_groups_with_project_in():
-    """B = 18 runs as 16 + 2; project_in shape, first half greedy."""
+    """B = 34 runs as 32 + 2; project_in shape, first half greedy."""
     w = si.WORKLOADS["s2pro_b64"]
-    pair = pr.make_pair(w.shape, w.seed(0), max_batch=18)
-    fr = _frames(w, 1, 18)
-    assert (fr["temperature"][:9] == 0).all() and (fr["temperature"][9:] > 0).all()
+    pair = pr.make_pair(w.shape, w.seed(0), max_batch=34)
+    fr = _frames(w, 1, 34)
+    assert (fr["temperature"][:17] == 0).all() and (fr["temperature"][17:] > 0).all()
     codes = pr.gpu_decode(pair, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
                           fr["top_p"], fr["top_k"])
-    pick = [0, 8, 9, 15, 16, 17]
+    pick = [0, 16, 17, 31, 32, 33]
     excused = pr.check_codes(pair, fr["hidden"][0][pick], fr["sem_code"][0][pick], fr["uniforms"][0][pick],
                              fr["temperature"][pick], fr["top_p"][pick], fr["top_k"][pick], codes[pick])
-    worst, rel, _, _ = pr.check_logits(pair, fr["hidden"][0][[0, 17]], codes[[0, 17]])
-    _announce(f"project_in B=18: excused {excused}; logits worst {worst:.2e}, rel {rel:.2e}")
+    worst, rel, _, _ = pr.check_logits(pair, fr["hidden"][0][[0, 33]], codes[[0, 33]])
+    _announce(f"project_in B=34: excused {excused}; logits worst {worst:.2e}, rel {rel:.2e}")
     assert worst <= 1.0 and rel < 1e-3, (worst, rel)
     pair.ctx.close()
 
 
 def test_s2pro_b64_bench_config():
-    """The batch-64 workload as bench.py times it (four launches of 16, with
+    """The batch-64 workload as bench.py times it (two launches of 32, with
     fast_project_in, half greedy): codes of one request at each group edge
     and teacher-forced logits of two requests against the oracle."""
     w = si.WORKLOADS["s2pro_b64"]
@@ -226,15 +227,15 @@ def test_s2pro_b64_bench_config():
 
 
 def test_tiny_f32_batched_groups():
-    """float32 weights (float32 MFMA path), B = 20 = 16 + 4, mixed settings."""
+    """float32 weights (float32 MFMA path), B = 36 = 32 + 4, mixed settings."""
     w = si.WORKLOADS["tiny"]
-    pair = pr.make_pair(w.shape, w.seed(0), max_batch=20)
-    fr = _frames(w, 2, 20)
+    pair = pr.make_pair(w.shape, w.seed(0), max_batch=36)
+    fr = _frames(w, 2, 36)
     rng = np.random.default_rng(11)
-    temp = rng.uniform(0.5, 1.2, size=20).astype(np.float32)
+    temp = rng.uniform(0.5, 1.2, size=36).astype(np.float32)
     temp[::3] = 0.0
-    top_p = rng.uniform(0.5, 1.0, size=20).astype(np.float32)
-    top_k = rng.integers(1, 80, size=20).astype(np.int32)
+    top_p = rng.uniform(0.5, 1.0, size=36).astype(np.float32)
+    top_k = rng.integers(1, 80, size=36).astype(np.int32)
     excused = 0
     for f in range(2):
         codes = pr.gpu_decode(pair, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], temp, top_p, top_k)
@@ -242,7 +243,7 @@ def test_tiny_f32_batched_groups():
                                   codes)
         worst, rel, _, _ = pr.check_logits(pair, fr["hidden"][f], codes)
         assert worst <= 1.0 and rel < 1e-4, (worst, rel)
-    _announce(f"tiny f32 B=20: excused {excused}")
+    _announce(f"tiny f32 B=36: excused {excused}")
     pair.ctx.close()
 
 
