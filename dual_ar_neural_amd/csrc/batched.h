@@ -51,11 +51,12 @@ struct BatchArgs {
   // (b_pack_kernel), indexed by pk_index(kind, layer)
   const char* pk[2 + 4 * S2FAST_MAX_LAYERS];
   // wo and w2 split over their K columns: ks[kind] workgroups share a row
-  // group, each adds its partial sums into kacc[kind] (fixed point) and the
-  // last of them (by the kcnt[kind] count) writes the phase's output and
-  // clears both for the next frame; ks 1: no split
+  // group, each stores its partial sums into its slice of kpart[kind], and
+  // the last of them (by the kcnt[kind] count) adds the slices in slice
+  // order, writes the phase's output and clears the count for the next
+  // frame; ks 1: no split
   int ks[6];
-  long long* kacc[6];       // [slot][MP_MAX][dim]
+  float* kpart[6];          // [slot][ks][MP_MAX][dim]
   int* kcnt[6];             // [slot][P / ks]
   int Bq;                   // requests in this launch, 1..BQ_MAX
   const float* hidden;      // [Bq][in_dim]
@@ -133,8 +134,9 @@ __device__ __forceinline__ float* bxmid(const BatchArgs& a, int step, int l) { r
 __device__ __forceinline__ float* bqkv(const BatchArgs& a, int step, int l) { return a.qkv + b_slot(a, step, l) * a.qkv_slot; }
 __device__ __forceinline__ float* batt(const BatchArgs& a, int step, int l) { return a.att + b_slot(a, step, l) * a.att_slot; }
 __device__ __forceinline__ float* bg(const BatchArgs& a, int step, int l) { return a.g + b_slot(a, step, l) * a.g_slot; }
-__device__ __forceinline__ long long* bkacc(const BatchArgs& a, int kind, int step, int l) {
-  return a.kacc[kind] + b_slot(a, step, l) * a.x_slot;
+// slice j of kind's partial sums at (step, layer)
+__device__ __forceinline__ float* bkpart(const BatchArgs& a, int kind, int step, int l, int j) {
+  return a.kpart[kind] + (b_slot(a, step, l) * a.ks[kind] + j) * a.x_slot;
 }
 __device__ __forceinline__ float* blogits(const BatchArgs& a, int step) { return a.logits + (size_t)(step - 1) * a.logits_slot; }
 __device__ __forceinline__ float* bkv(const BatchArgs& a, int b, int l, int pos, int g) {
@@ -561,7 +563,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
         case BK_WO: {
           const int k = r0 + v;
           if (S > 1) {
-            atomic_add_coh(bkacc(a, kind, step, l) + (size_t)m * a.dim + k, to_fx(d));
+            st_coh(bkpart(a, kind, step, l, ks) + (size_t)m * a.dim + k, d);
           } else {
             const float xin = l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[(size_t)m * a.dim + k];
             st_coh(bxmid(a, step, l) + (size_t)m * a.dim + k, xin + d);
@@ -576,7 +578,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
         }
         case BK_DOWN: {
           const int k = r0 + v;
-          if (S > 1) atomic_add_coh(bkacc(a, kind, step, l) + (size_t)m * a.dim + k, to_fx(d));
+          if (S > 1) st_coh(bkpart(a, kind, step, l, ks) + (size_t)m * a.dim + k, d);
           else st_coh(bx(a, step, l) + (size_t)m * a.dim + k, bxmid(a, step, l)[(size_t)m * a.dim + k] + d);
           break;
         }
@@ -592,27 +594,44 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   }
   const int M = Mt;
   if (S > 1) {
-    // the row group's last contributor: the output from the sum of the K
-    // slices (wo: x_mid = x_in + sum; w2: x = x_mid + sum), and the
-    // accumulator and count cleared for the next frame
-    long long* acc = bkacc(a, kind, step, l);
+    // the row group's last contributor: the output from the K slices'
+    // partial sums added in slice order (wo: x_mid = x_in + sum; w2: x =
+    // x_mid + sum), and the count cleared for the next frame
     int* cnt = a.kcnt[kind] + b_slot(a, step, l) * (P / S) + blk / S;
-    wait_vmem();        // this workgroup's additions have completed
+    wait_vmem();        // this workgroup's partial sums have been stored
     __syncthreads();
     if (tidx() == 0) s.flag[3] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
     __syncthreads();
     if (s.flag[3]) {
-      for (int o = tidx(); o < nr * M; o += NTHREADS) {
-        const int m = o % M, k = r0 + o / M;
-        const size_t e = (size_t)m * a.dim + k;
-        const float sum = from_fx(ld_coh(acc + e));
-        if (kind == BK_WO) {
-          const float xin = l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[e];
-          st_coh(bxmid(a, step, l) + e, xin + sum);
-        } else {
-          st_coh(bx(a, step, l) + e, bxmid(a, step, l)[e] + sum);
+      // FB elements a thread per batch, every load of a batch issued before
+      // any is used (one memory round trip a batch, not one an element)
+      constexpr int FB = 4, SMAX = 4;
+      const int n = nr * M;
+      for (int base = 0; base < n; base += FB * NTHREADS) {
+        float pv[FB][SMAX];
+        float xv[FB];
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+          const int o = min(base + j * NTHREADS + tidx(), n - 1);
+          const int m = o % M, k = r0 + o / M;
+          const size_t e = (size_t)m * a.dim + k;
+#pragma unroll
+          for (int q = 0; q < SMAX; ++q) pv[j][q] = q < S ? ld_coh(bkpart(a, kind, step, l, q) + e) : 0.0f;
+          xv[j] = kind == BK_WO ? (l == 0 ? b_layer0_elem<WT>(a, s, m, k) : bx(a, step, l - 1)[e])
+                                : bxmid(a, step, l)[e];
         }
-        st_coh(acc + e, 0ll);
+#pragma unroll
+        for (int j = 0; j < FB; ++j) {
+          const int o = base + j * NTHREADS + tidx();
+          if (o < n) {
+            const int m = o % M, k = r0 + o / M;
+            float sum = pv[j][0];
+#pragma unroll
+            for (int q = 1; q < SMAX; ++q)
+              if (q < S) sum += pv[j][q];
+            st_coh((kind == BK_WO ? bxmid(a, step, l) : bx(a, step, l)) + (size_t)m * a.dim + k, xv[j] + sum);
+          }
+        }
       }
       if (tidx() == 0) st_coh(cnt, 0);
     }

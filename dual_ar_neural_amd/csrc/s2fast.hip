@@ -1165,6 +1165,7 @@ __global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const WT* e
 #ifndef KS_DOWN
 #define KS_DOWN 4
 #endif
+static_assert(KS_DOWN >= 1 && KS_DOWN <= 4, "the finalising workgroup adds at most four K slices");
 
 }  // namespace
 
@@ -1207,7 +1208,7 @@ struct s2fast_ctx {
   float* b_kv = nullptr;
   int* b_codes = nullptr;
   char* b_pk = nullptr;                          // packed weight streams of the batched GEMMs
-  long long* b_kacc[6] = {};                     // K-split accumulators of wo and w2 [slot][x_slot]
+  float* b_kpart[6] = {};                        // K-split partial sums of wo and w2 [slot][ks][x_slot]
   int* b_kcnt[6] = {};                           // and their per-row-group counts [slot][P]
   int b_ks[6] = {1, 1, 1, 1, 1, 1};              // K split of each batched GEMM kind
   long long b_pk_off[2 + 4 * S2FAST_MAX_LAYERS] = {};
@@ -1248,7 +1249,7 @@ void free_ctx(s2fast_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->rope, c->qkv0, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog,
                   c->b_xin0, c->b_x, c->b_xmid, c->b_qkv, c->b_att, c->b_g, c->b_logits, c->b_kv, c->b_codes,
-                  c->b_pk, c->b_kacc[BK_WO], c->b_kcnt[BK_WO], c->b_kacc[BK_DOWN], c->b_kcnt[BK_DOWN]};
+                  c->b_pk, c->b_kpart[BK_WO], c->b_kcnt[BK_WO], c->b_kpart[BK_DOWN], c->b_kcnt[BK_DOWN]};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -1379,7 +1380,7 @@ void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
   ba.rope = c->rope;
   ba.qkv0 = c->qkv0;
   for (int i = 0; i < 2 + 4 * S2FAST_MAX_LAYERS; ++i) ba.pk[i] = c->b_pk + c->b_pk_off[i];
-  for (int kd = 0; kd < 6; ++kd) { ba.ks[kd] = c->b_ks[kd]; ba.kacc[kd] = c->b_kacc[kd]; ba.kcnt[kd] = c->b_kcnt[kd]; }
+  for (int kd = 0; kd < 6; ++kd) { ba.ks[kd] = c->b_ks[kd]; ba.kpart[kd] = c->b_kpart[kd]; ba.kcnt[kd] = c->b_kcnt[kd]; }
   ba.xin0 = c->b_xin0; ba.x = c->b_x; ba.xmid = c->b_xmid; ba.qkv = c->b_qkv; ba.att = c->b_att; ba.g = c->b_g;
   ba.logits = c->b_logits; ba.kv = c->b_kv; ba.codes = c->b_codes;
   ba.x_slot = c->bx_slot; ba.qkv_slot = c->bqkv_slot; ba.att_slot = c->batt_slot; ba.g_slot = c->bg_slot;
@@ -1596,9 +1597,8 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
       c->b_ks[BK_DOWN] = (rows_fit && k.ffn_dim % (ks * ksz) == 0) ? ks : 1;
       for (int kd : {(int)BK_WO, (int)BK_DOWN}) {
         if (c->b_ks[kd] == 1) continue;
-        ok = dalloc(&c->b_kacc[kd], (size_t)(slots * c->bx_slot)) == hipSuccess &&
+        ok = dalloc(&c->b_kpart[kd], (size_t)(slots * c->b_ks[kd] * c->bx_slot)) == hipSuccess &&
              dalloc(&c->b_kcnt[kd], (size_t)(slots * P)) == hipSuccess &&
-             hipMemset(c->b_kacc[kd], 0, (size_t)(slots * c->bx_slot) * sizeof(long long)) == hipSuccess &&
              hipMemset(c->b_kcnt[kd], 0, (size_t)(slots * P) * sizeof(int)) == hipSuccess;
         if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
       }
