@@ -1586,15 +1586,16 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
            dalloc(&c->b_kv, (size_t)BQ_MAX * k.n_layer * k.context * k.n_head_kv * 2 * k.head_dim) == hipSuccess &&
            dalloc(&c->b_codes, (size_t)BQ_MAX * 16) == hipSuccess;
       if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
-      // w2 (the widest K) split KS_DOWN ways over K when the row groups and
-      // the slices fit the GEMM's tiles (at most TMAX x 16 rows, whole
-      // k-steps).  wo could split the same way, but with its K of 4096 the
-      // saved activation reads do not pay for the accumulate-and-finalise
-      // round trips.
+      // w2 and wo (the widest K: ffn and the attention width) split KS_DOWN
+      // ways over K when the row groups and the slices fit the GEMM's tiles
+      // (at most TMAX x 16 rows, whole k-steps).  The saved activation reads
+      // outweigh the store / count / finalise round trips the split adds
+      // (w2 26.5 -> 14.9 us a phase at batch 16; wo about 1 % of a launch).
       const int ksz = k.weight_dtype == S2FAST_BF16 ? 32 : 16;
       const int ks = KS_DOWN;
       const bool rows_fit = P % ks == 0 && (k.dim + P / ks - 1) / (P / ks) <= 16 * TMAX;
       c->b_ks[BK_DOWN] = (rows_fit && k.ffn_dim % (ks * ksz) == 0) ? ks : 1;
+      c->b_ks[BK_WO] = (rows_fit && (k.n_head * k.head_dim) % (ks * ksz) == 0) ? ks : 1;
       for (int kd : {(int)BK_WO, (int)BK_DOWN}) {
         if (c->b_ks[kd] == 1) continue;
         ok = dalloc(&c->b_kpart[kd], (size_t)(slots * c->b_ks[kd] * c->bx_slot)) == hipSuccess &&
