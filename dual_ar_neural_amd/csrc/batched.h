@@ -55,9 +55,15 @@ struct BatchArgs {
   // the last of them (by the kcnt[kind] count) adds the slices in slice
   // order, writes the phase's output and clears the count for the next
   // frame; ks 1: no split
+  // The wqkv phase may split as well; it needs no finalising step: the
+  // attention workgroups add the two slices' partial sums of the values
+  // they read and divide by the RMS rebuilt from the slices' sums of
+  // squares (kss).
   int ks[6];
-  float* kpart[6];          // [slot][ks][MP_MAX][dim]
+  float* kpart[6];          // [slot][ks][kslot]
+  long long kslot[6];       // elements of one slice: MP_MAX rows of the phase's output width
   int* kcnt[6];             // [slot][P / ks]
+  float* kss[6];            // [slot][ks][MP_MAX] sums of squares of a slice's X rows
   int Bq;                   // requests in this launch, 1..BQ_MAX
   const float* hidden;      // [Bq][in_dim]
   const int* sem_code;      // [Bq]
@@ -136,7 +142,10 @@ __device__ __forceinline__ float* batt(const BatchArgs& a, int step, int l) { re
 __device__ __forceinline__ float* bg(const BatchArgs& a, int step, int l) { return a.g + b_slot(a, step, l) * a.g_slot; }
 // slice j of kind's partial sums at (step, layer)
 __device__ __forceinline__ float* bkpart(const BatchArgs& a, int kind, int step, int l, int j) {
-  return a.kpart[kind] + (b_slot(a, step, l) * a.ks[kind] + j) * a.x_slot;
+  return a.kpart[kind] + (b_slot(a, step, l) * a.ks[kind] + j) * a.kslot[kind];
+}
+__device__ __forceinline__ float* bkss(const BatchArgs& a, int kind, int step, int l, int j) {
+  return a.kss[kind] + (b_slot(a, step, l) * a.ks[kind] + j) * MP_MAX;
 }
 __device__ __forceinline__ float* blogits(const BatchArgs& a, int step) { return a.logits + (size_t)(step - 1) * a.logits_slot; }
 __device__ __forceinline__ float* bkv(const BatchArgs& a, int b, int l, int pos, int g) {
@@ -445,7 +454,8 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
   const int MT = gd.M <= 16 ? 1 : 2;
   const int T = (gd.R + 15) >> 4;
   if (gd.normw) {
-    for (int k = tid; k < gd.K; k += NTHREADS) s.nw[k] = WTraits<WT>::one(reinterpret_cast<const WT*>(gd.normw), k);
+    for (int k = tid; k < gd.K; k += NTHREADS)
+      s.nw[k] = WTraits<WT>::one(reinterpret_cast<const WT*>(gd.normw), gd.k0 + k);
     __syncthreads();
   }
   float* red = reinterpret_cast<float*>(s.xf);
@@ -483,7 +493,8 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
   if (gd.normw && tid < gd.M) {
     float t2 = 0.0f;
     for (int w = 0; w < NWAVE; ++w) t2 += s.ssp[w * MP_MAX + tid];
-    s.rms[tid] = sqrtf(t2 / (float)gd.K + a.eps);
+    // a K slice keeps its raw sum of squares (the consumer adds the slices')
+    s.rms[tid] = a.ks[gd.kind] > 1 ? t2 : sqrtf(t2 / (float)gd.K + a.eps);
   }
   __syncthreads();
   return RedView{red, T, MT};
@@ -514,8 +525,9 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       gd.K = a.in_dim; gd.M = a.Bq;
       break;
     case BK_QKV:
-      split_rows(a.qkv_dim, blk, P, r0, r1);
-      gd.K = a.dim; gd.M = b_rows(a, step);
+      ks = blk % S;
+      split_rows(a.qkv_dim, blk / S, P / S, r0, r1);
+      gd.K = a.dim / S; gd.k0 = ks * gd.K; gd.M = b_rows(a, step);
       gd.normw = L.attn_norm;
       break;
     case BK_WO:
@@ -559,7 +571,10 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       const float d = rv.sum(v, mp);
       switch (kind) {
         case BK_PROJ: st_coh(a.xin0 + (size_t)m * a.dim + r0 + v, d); break;
-        case BK_QKV: st_coh(bqkv(a, step, l) + (size_t)m * a.qkv_dim + r0 + v, d / s.rms[mp]); break;
+        case BK_QKV:
+          if (S > 1) st_coh(bkpart(a, kind, step, l, ks) + (size_t)m * a.qkv_dim + r0 + v, d);
+          else st_coh(bqkv(a, step, l) + (size_t)m * a.qkv_dim + r0 + v, d / s.rms[mp]);
+          break;
         case BK_WO: {
           const int k = r0 + v;
           if (S > 1) {
@@ -590,10 +605,12 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
         }
       }
     }
+    if (kind == BK_QKV && S > 1 && blk / S == 0 && tidx() < M)   // one row group per slice
+      st_coh(bkss(a, kind, step, l, ks) + m0 + tidx(), s.rms[tidx()]);
     if (m0 + GM_MAX < Mt) __syncthreads();   // the next pass reuses the partial sums and rms in LDS
   }
   const int M = Mt;
-  if (S > 1) {
+  if (S > 1 && (kind == BK_WO || kind == BK_DOWN)) {
     // the row group's last contributor: the output from the K slices'
     // partial sums added in slice order (wo: x_mid = x_in + sum; w2: x =
     // x_mid + sum), and the count cleared for the next frame
@@ -658,6 +675,18 @@ __device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, 
   // gather: cached keys/values, then the new rows' raw q, k, v (layer 0 of
   // steps >= 2: the qkv0 row of the code that produced the row)
   const float* row0 = (l == 0 && step >= 2) ? a.qkv0 + (size_t)b_code(a, b, step - 1) * a.qkv_dim : nullptr;
+  // a wqkv split over K: the new rows' values are the slices' partial sums
+  // added in slice order, divided by the RMS of the whole row
+  const int S = row0 ? 1 : a.ks[BK_QKV];
+  float rden[2] = {1.0f, 1.0f};
+  if (S > 1) {
+    for (int nr = 0; nr < n_new; ++nr) {
+      const int m = step == 1 ? nr * a.Bq + b : b;
+      float ss = bkss(a, BK_QKV, step, l, 0)[m];
+      for (int q2 = 1; q2 < S; ++q2) ss += bkss(a, BK_QKV, step, l, q2)[m];
+      rden[nr] = sqrtf(ss / (float)a.dim + a.eps);
+    }
+  }
   const int n_cache = first_new * 2 * hd;
   const int n_row = (gh + 2) * hd;
   for (int i = tid; i < n_cache + n_new * n_row; i += NTHREADS) {
@@ -670,10 +699,22 @@ __device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, 
       const int nr = t / n_row, r = t - nr * n_row;
       const int m = step == 1 ? nr * a.Bq + b : b;
       const int pos = step == 1 ? nr : step;
-      const float* row = row0 ? row0 : bqkv(a, step, l) + (size_t)m * a.qkv_dim;
-      if (r < gh * hd) q[(size_t)nr * gh * hd + r] = row[(size_t)g * gh * hd + r];
-      else if (r < (gh + 1) * hd) kc[(size_t)pos * hd + (r - gh * hd)] = row[(size_t)H * hd + (size_t)g * hd + (r - gh * hd)];
-      else vc[(size_t)pos * hd + (r - (gh + 1) * hd)] = row[(size_t)(H + G) * hd + (size_t)g * hd + (r - (gh + 1) * hd)];
+      int c;          // column of the wqkv output row
+      float* dst;
+      if (r < gh * hd) { c = g * gh * hd + r; dst = q + (size_t)nr * gh * hd + r; }
+      else if (r < (gh + 1) * hd) { c = H * hd + g * hd + (r - gh * hd); dst = kc + (size_t)pos * hd + (r - gh * hd); }
+      else { c = (H + G) * hd + g * hd + (r - (gh + 1) * hd); dst = vc + (size_t)pos * hd + (r - (gh + 1) * hd); }
+      float v;
+      if (row0) {
+        v = row0[c];
+      } else if (S > 1) {
+        v = bkpart(a, BK_QKV, step, l, 0)[(size_t)m * a.qkv_dim + c];
+        for (int q2 = 1; q2 < S; ++q2) v += bkpart(a, BK_QKV, step, l, q2)[(size_t)m * a.qkv_dim + c];
+        v /= rden[nr];
+      } else {
+        v = bqkv(a, step, l)[(size_t)m * a.qkv_dim + c];
+      }
+      *dst = v;
     }
   }
   __syncthreads();

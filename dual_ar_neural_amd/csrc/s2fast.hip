@@ -1208,7 +1208,9 @@ struct s2fast_ctx {
   float* b_kv = nullptr;
   int* b_codes = nullptr;
   char* b_pk = nullptr;                          // packed weight streams of the batched GEMMs
-  float* b_kpart[6] = {};                        // K-split partial sums of wo and w2 [slot][ks][x_slot]
+  float* b_kpart[6] = {};                        // K-split partial sums [slot][ks][kslot]
+  long long b_kslot[6] = {};
+  float* b_kss[6] = {};                          // slice sums of squares (wqkv) [slot][ks][MP_MAX]
   int* b_kcnt[6] = {};                           // and their per-row-group counts [slot][P]
   int b_ks[6] = {1, 1, 1, 1, 1, 1};              // K split of each batched GEMM kind
   long long b_pk_off[2 + 4 * S2FAST_MAX_LAYERS] = {};
@@ -1249,7 +1251,8 @@ void free_ctx(s2fast_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->rope, c->qkv0, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog,
                   c->b_xin0, c->b_x, c->b_xmid, c->b_qkv, c->b_att, c->b_g, c->b_logits, c->b_kv, c->b_codes,
-                  c->b_pk, c->b_kpart[BK_WO], c->b_kcnt[BK_WO], c->b_kpart[BK_DOWN], c->b_kcnt[BK_DOWN]};
+                  c->b_pk, c->b_kpart[BK_WO], c->b_kcnt[BK_WO], c->b_kpart[BK_DOWN], c->b_kcnt[BK_DOWN],
+                  c->b_kpart[BK_QKV], c->b_kcnt[BK_QKV], c->b_kss[BK_QKV]};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -1273,7 +1276,7 @@ int pack_batched(s2fast_ctx* c) {
   jobs[nj++] = {1, c->w.output, nullptr, k.codebook_size, k.dim, 1};
   for (int l = 0; l < k.n_layer; ++l) {
     const s2fast_layer_weights& L = c->w.layers[l];
-    jobs[nj++] = {2 + 4 * l + 0, L.wqkv, nullptr, qkv_dim, k.dim, 1};
+    jobs[nj++] = {2 + 4 * l + 0, L.wqkv, nullptr, qkv_dim, k.dim, c->b_ks[BK_QKV]};
     jobs[nj++] = {2 + 4 * l + 1, L.wo, nullptr, k.dim, attn_dim, c->b_ks[BK_WO]};
     jobs[nj++] = {2 + 4 * l + 2, L.w1, L.w3, k.ffn_dim, k.dim, 1};
     jobs[nj++] = {2 + 4 * l + 3, L.w2, nullptr, k.dim, k.ffn_dim, c->b_ks[BK_DOWN]};
@@ -1380,7 +1383,10 @@ void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
   ba.rope = c->rope;
   ba.qkv0 = c->qkv0;
   for (int i = 0; i < 2 + 4 * S2FAST_MAX_LAYERS; ++i) ba.pk[i] = c->b_pk + c->b_pk_off[i];
-  for (int kd = 0; kd < 6; ++kd) { ba.ks[kd] = c->b_ks[kd]; ba.kpart[kd] = c->b_kpart[kd]; ba.kcnt[kd] = c->b_kcnt[kd]; }
+  for (int kd = 0; kd < 6; ++kd) {
+    ba.ks[kd] = c->b_ks[kd]; ba.kpart[kd] = c->b_kpart[kd]; ba.kslot[kd] = c->b_kslot[kd];
+    ba.kcnt[kd] = c->b_kcnt[kd]; ba.kss[kd] = c->b_kss[kd];
+  }
   ba.xin0 = c->b_xin0; ba.x = c->b_x; ba.xmid = c->b_xmid; ba.qkv = c->b_qkv; ba.att = c->b_att; ba.g = c->b_g;
   ba.logits = c->b_logits; ba.kv = c->b_kv; ba.codes = c->b_codes;
   ba.x_slot = c->bx_slot; ba.qkv_slot = c->bqkv_slot; ba.att_slot = c->batt_slot; ba.g_slot = c->bg_slot;
@@ -1596,10 +1602,18 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
       const bool rows_fit = P % ks == 0 && (k.dim + P / ks - 1) / (P / ks) <= 16 * TMAX;
       c->b_ks[BK_DOWN] = (rows_fit && k.ffn_dim % (ks * ksz) == 0) ? ks : 1;
       c->b_ks[BK_WO] = (rows_fit && (k.n_head * k.head_dim) % (ks * ksz) == 0) ? ks : 1;
-      for (int kd : {(int)BK_WO, (int)BK_DOWN}) {
+      // wqkv splits two ways (its row groups must also fit TMAX tiles); its
+      // consumer, the attention, adds the two slices itself
+      const int kq = 2;
+      c->b_ks[BK_QKV] = (P % kq == 0 && (qkv_dim + P / kq - 1) / (P / kq) <= 16 * TMAX && k.dim % (kq * ksz) == 0)
+                            ? kq : 1;
+      c->b_kslot[BK_WO] = c->b_kslot[BK_DOWN] = c->bx_slot;
+      c->b_kslot[BK_QKV] = c->bqkv_slot;
+      for (int kd : {(int)BK_QKV, (int)BK_WO, (int)BK_DOWN}) {
         if (c->b_ks[kd] == 1) continue;
-        ok = dalloc(&c->b_kpart[kd], (size_t)(slots * c->b_ks[kd] * c->bx_slot)) == hipSuccess &&
+        ok = dalloc(&c->b_kpart[kd], (size_t)(slots * c->b_ks[kd] * c->b_kslot[kd])) == hipSuccess &&
              dalloc(&c->b_kcnt[kd], (size_t)(slots * P)) == hipSuccess &&
+             dalloc(&c->b_kss[kd], (size_t)(slots * c->b_ks[kd] * MP_MAX)) == hipSuccess &&
              hipMemset(c->b_kcnt[kd], 0, (size_t)(slots * P) * sizeof(int)) == hipSuccess;
         if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
       }
