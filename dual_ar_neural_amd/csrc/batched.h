@@ -546,8 +546,9 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
       gd.K = a.ffn / S; gd.k0 = ks * gd.K; gd.M = b_rows(a, step);
       break;
     default:
-      split_rows(a.V, blk, P, r0, r1);
-      gd.K = a.dim; gd.M = a.Bq;
+      ks = blk % S;
+      split_rows(a.V, blk / S, P / S, r0, r1);
+      gd.K = a.dim / S; gd.k0 = ks * gd.K; gd.M = a.Bq;
       gd.normw = a.fnorm;
       break;
   }
@@ -598,14 +599,18 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
           break;
         }
         default: {
-          const float y = d / s.rms[mp];
-          st_coh(blogits(a, step) + (size_t)m * a.V + r0 + v, y);
-          if (a.logits_out) a.logits_out[((size_t)m * (a.ncb - 1) + (step - 1)) * a.V + r0 + v] = y;
+          if (S > 1) {
+            st_coh(bkpart(a, kind, step, l, ks) + (size_t)m * a.V + r0 + v, d);
+          } else {
+            const float y = d / s.rms[mp];
+            st_coh(blogits(a, step) + (size_t)m * a.V + r0 + v, y);
+            if (a.logits_out) a.logits_out[((size_t)m * (a.ncb - 1) + (step - 1)) * a.V + r0 + v] = y;
+          }
           break;
         }
       }
     }
-    if (kind == BK_QKV && S > 1 && blk / S == 0 && tidx() < M)   // one row group per slice
+    if ((kind == BK_QKV || kind == BK_HEAD) && S > 1 && blk / S == 0 && tidx() < M)   // one row group per slice
       st_coh(bkss(a, kind, step, l, ks) + m0 + tidx(), s.rms[tidx()]);
     if (m0 + GM_MAX < Mt) __syncthreads();   // the next pass reuses the partial sums and rms in LDS
   }
@@ -787,11 +792,33 @@ __device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, 
 }
 
 // Workgroup b < Bq draws request b's code of step `step` from its logits.
+// With the head split over K, the workgroup first adds request b's two
+// slices of logits in slice order and divides by the RMS rebuilt from the
+// slices' sums of squares, into LDS (and the caller's logits buffer); with a
+// teacher-forced prefix that is all it does.
 __device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s, int step) {
   const int b = blockIdx.x;
   if (b >= a.Bq) return;
+  const float* L = blogits(a, step) + (size_t)b * a.V;
+  const int S = a.ks[BK_HEAD];
+  if (S > 1) {
+    float ss = bkss(a, BK_HEAD, step, 0, 0)[b];
+    for (int q = 1; q < S; ++q) ss += bkss(a, BK_HEAD, step, 0, q)[b];
+    const float rd = sqrtf(ss / (float)a.dim + a.eps);
+    float* lg = reinterpret_cast<float*>(s.xf);
+    for (int i = tidx(); i < a.V; i += NTHREADS) {
+      float v = bkpart(a, BK_HEAD, step, 0, 0)[(size_t)b * a.V + i];
+      for (int q = 1; q < S; ++q) v += bkpart(a, BK_HEAD, step, 0, q)[(size_t)b * a.V + i];
+      v /= rd;
+      lg[i] = v;
+      if (a.logits_out) a.logits_out[((size_t)b * (a.ncb - 1) + (step - 1)) * a.V + i] = v;
+    }
+    __syncthreads();
+    L = lg;
+  }
+  if (a.forced) return;
   const SampScratch sc{s.cval, s.cidx, s.sred};
-  const int code = sample_request(blogits(a, step) + (size_t)b * a.V, a.V, a.temp[b], a.top_p[b], a.top_k[b],
+  const int code = sample_request(L, a.V, a.temp[b], a.top_p[b], a.top_k[b],
                                   a.uniforms[(size_t)b * (a.ncb - 1) + (step - 1)], sc);
   if (tidx() == 0) {
     const int c = min(max(code, 0), a.V - 1);
@@ -800,9 +827,12 @@ __device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s
   }
 }
 
-// grid syncs of one launch; steps >= 2 have no layer-0 wqkv phase
-__host__ __device__ inline int b_syncs(int has_proj, int ncb, int n_layer, bool forced) {
-  return (has_proj ? 1 : 0) + (ncb - 1) * (5 * n_layer + (forced ? 0 : 2)) - (ncb - 2);
+// grid syncs of one launch; steps >= 2 have no layer-0 wqkv phase.  With
+// a teacher-forced prefix a step ends at the head, unless the head is split
+// over K and the caller wants the logits (head_logits): then one sync lets
+// the sample phase assemble them.
+__host__ __device__ inline int b_syncs(int has_proj, int ncb, int n_layer, bool forced, bool head_logits) {
+  return (has_proj ? 1 : 0) + (ncb - 1) * (5 * n_layer + (forced ? (head_logits ? 1 : 0) : 2)) - (ncb - 2);
 }
 
 template <typename WT>
@@ -858,9 +888,12 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     }
     b_phase_gemm<WT>(a, s, BK_HEAD, step, 0);
-    if (a.forced) continue;          // teacher forcing: the next prefix is known
+    // teacher forcing: the next prefix is known (the sample phase then only
+    // assembles a split head's logits for the caller)
+    if (a.forced && !(a.ks[BK_HEAD] > 1 && a.logits_out)) continue;
     if (!grid_sync(a, epoch, s.flag)) return;
     b_phase_sample(a, s, step);
+    if (a.forced) continue;
     if (!grid_sync(a, epoch, s.flag)) return;
   }
 }

@@ -1252,7 +1252,8 @@ void free_ctx(s2fast_ctx* c) {
   void* ptrs[] = {c->rope, c->qkv0, c->xin0, c->x, c->qkv, c->acc, c->g, c->kv, c->logits, c->flags, c->err, c->tlog,
                   c->b_xin0, c->b_x, c->b_xmid, c->b_qkv, c->b_att, c->b_g, c->b_logits, c->b_kv, c->b_codes,
                   c->b_pk, c->b_kpart[BK_WO], c->b_kcnt[BK_WO], c->b_kpart[BK_DOWN], c->b_kcnt[BK_DOWN],
-                  c->b_kpart[BK_QKV], c->b_kcnt[BK_QKV], c->b_kss[BK_QKV]};
+                  c->b_kpart[BK_QKV], c->b_kcnt[BK_QKV], c->b_kss[BK_QKV],
+                  c->b_kpart[BK_HEAD], c->b_kcnt[BK_HEAD], c->b_kss[BK_HEAD]};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -1273,7 +1274,7 @@ int pack_batched(s2fast_ctx* c) {
   Job jobs[2 + 4 * S2FAST_MAX_LAYERS];
   int nj = 0;
   if (k.has_project_in) jobs[nj++] = {0, c->w.project_in, nullptr, k.dim, k.in_dim, 1};
-  jobs[nj++] = {1, c->w.output, nullptr, k.codebook_size, k.dim, 1};
+  jobs[nj++] = {1, c->w.output, nullptr, k.codebook_size, k.dim, c->b_ks[BK_HEAD]};
   for (int l = 0; l < k.n_layer; ++l) {
     const s2fast_layer_weights& L = c->w.layers[l];
     jobs[nj++] = {2 + 4 * l + 0, L.wqkv, nullptr, qkv_dim, k.dim, c->b_ks[BK_QKV]};
@@ -1350,7 +1351,8 @@ int launch_frame(s2fast_ctx* c, const FrameArgs& fa_in, hipStream_t stream) {
 
 int launch_batched(s2fast_ctx* c, const BatchArgs& ba_in, hipStream_t stream) {
   BatchArgs ba = ba_in;
-  const u32 n = (u32)b_syncs(c->cfg.has_project_in, c->cfg.num_codebooks, c->cfg.n_layer, ba.forced != nullptr);
+  const u32 n = (u32)b_syncs(c->cfg.has_project_in, c->cfg.num_codebooks, c->cfg.n_layer, ba.forced != nullptr,
+                            c->b_ks[BK_HEAD] > 1 && ba.logits_out != nullptr);
   if (c->epoch > 0xF0000000u) {
     if (hipMemsetAsync(c->flags, 0, (size_t)c->ncu * 64 * sizeof(u32), stream) != hipSuccess) return S2FAST_ERR_HIP;
     c->epoch = 0;
@@ -1607,9 +1609,13 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
       const int kq = 2;
       c->b_ks[BK_QKV] = (P % kq == 0 && (qkv_dim + P / kq - 1) / (P / kq) <= 16 * TMAX && k.dim % (kq * ksz) == 0)
                             ? kq : 1;
+      // the head too, its consumer (the sample phase) adding the slices
+      c->b_ks[BK_HEAD] = (P % kq == 0 && (k.codebook_size + P / kq - 1) / (P / kq) <= 16 * TMAX &&
+                          k.dim % (kq * ksz) == 0) ? kq : 1;
       c->b_kslot[BK_WO] = c->b_kslot[BK_DOWN] = c->bx_slot;
       c->b_kslot[BK_QKV] = c->bqkv_slot;
-      for (int kd : {(int)BK_QKV, (int)BK_WO, (int)BK_DOWN}) {
+      c->b_kslot[BK_HEAD] = c->blogits_slot;
+      for (int kd : {(int)BK_QKV, (int)BK_WO, (int)BK_DOWN, (int)BK_HEAD}) {
         if (c->b_ks[kd] == 1) continue;
         ok = dalloc(&c->b_kpart[kd], (size_t)(slots * c->b_ks[kd] * c->b_kslot[kd])) == hipSuccess &&
              dalloc(&c->b_kcnt[kd], (size_t)(slots * P)) == hipSuccess &&
@@ -1635,7 +1641,7 @@ int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B) {
   if (!ctx || B < 1) return -1;
   if (B == 1 || ctx->bq == 0) return B * syncs_for(ctx->cfg, false);
   const int groups = (B + ctx->bq - 1) / ctx->bq;
-  return groups * b_syncs(ctx->cfg.has_project_in, ctx->cfg.num_codebooks, ctx->cfg.n_layer, false);
+  return groups * b_syncs(ctx->cfg.has_project_in, ctx->cfg.num_codebooks, ctx->cfg.n_layer, false, false);
 }
 
 int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
