@@ -28,6 +28,7 @@
 constexpr int BQ_MAX = 32;               // requests per batched launch
 constexpr int MP_MAX = 2 * BQ_MAX;       // rows per decode step at most
 constexpr int GM_MAX = 32;               // rows of one GEMM pass (two 16-row M-tiles)
+constexpr int KCNT_STRIDE = 64;          // ints between K-split counts (each on its own line)
 constexpr int XF_BYTES = 128 * 1024;     // LDS for the GEMM partial sums and the attention scratch
 constexpr int TMAX = 5;                  // 16-row tiles of W per workgroup and phase
 constexpr int RED_TILES = 10;            // tiles x M-tiles the reduction buffer holds
@@ -62,7 +63,7 @@ struct BatchArgs {
   int ks[6];
   float* kpart[6];          // [slot][ks][kslot]
   long long kslot[6];       // elements of one slice: MP_MAX rows of the phase's output width
-  int* kcnt[6];             // [slot][P / ks]
+  int* kcnt[6];             // [slot][P / ks], one count per 256-byte line
   float* kss[6];            // [slot][ks][MP_MAX] sums of squares of a slice's X rows
   int Bq;                   // requests in this launch, 1..BQ_MAX
   const float* hidden;      // [Bq][in_dim]
@@ -619,7 +620,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
     // the row group's last contributor: the output from the K slices'
     // partial sums added in slice order (wo: x_mid = x_in + sum; w2: x =
     // x_mid + sum), and the count cleared for the next frame
-    int* cnt = a.kcnt[kind] + b_slot(a, step, l) * (P / S) + blk / S;
+    int* cnt = a.kcnt[kind] + (b_slot(a, step, l) * (P / S) + blk / S) * KCNT_STRIDE;
     wait_vmem();        // this workgroup's partial sums have been stored
     __syncthreads();
     if (tidx() == 0) s.flag[3] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;

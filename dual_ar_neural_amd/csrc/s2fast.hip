@@ -1618,9 +1618,9 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
       for (int kd : {(int)BK_QKV, (int)BK_WO, (int)BK_DOWN, (int)BK_HEAD}) {
         if (c->b_ks[kd] == 1) continue;
         ok = dalloc(&c->b_kpart[kd], (size_t)(slots * c->b_ks[kd] * c->b_kslot[kd])) == hipSuccess &&
-             dalloc(&c->b_kcnt[kd], (size_t)(slots * P)) == hipSuccess &&
+             dalloc(&c->b_kcnt[kd], (size_t)(slots * P * KCNT_STRIDE)) == hipSuccess &&
              dalloc(&c->b_kss[kd], (size_t)(slots * c->b_ks[kd] * MP_MAX)) == hipSuccess &&
-             hipMemset(c->b_kcnt[kd], 0, (size_t)(slots * P) * sizeof(int)) == hipSuccess;
+             hipMemset(c->b_kcnt[kd], 0, (size_t)(slots * P * KCNT_STRIDE) * sizeof(int)) == hipSuccess;
         if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
       }
       const int pst = pack_batched(c);
