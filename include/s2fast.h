@@ -113,7 +113,11 @@ typedef struct s2fast_ctx s2fast_ctx;
 /* Validate the shape and the weight pointers, allocate the context's device
  * scratch for max_batch requests, build the bf16-rounded RoPE table and the
  * layer-0 q/k/v table above (one GEMM on the current stream's device,
- * synchronised before returning).
+ * synchronised before returning).  With max_batch >= 2 the context also
+ * keeps a repacked copy of every weight matrix for the batched kernel (the
+ * size of the weights: 0.83 GB at the S2 Pro shape), in which each
+ * workgroup's rows form one contiguous stream; batches run 32 requests to a
+ * launch.
  * Uses the current HIP device.  On success *out owns the scratch; release
  * it with s2fast_destroy.  Shape limits (else S2FAST_ERR_ARG): dim, in_dim,
  * ffn_dim and the per-KV-group width (n_head/n_head_kv)*head_dim are
