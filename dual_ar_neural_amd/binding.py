@@ -51,6 +51,23 @@ class Weights(ctypes.Structure):
                 ("layers", LayerWeights * MAX_LAYERS)]
 
 
+SLOW_MAX_LAYERS = 64
+RAS_WINDOW = 10
+
+
+class SlowConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "dim", "n_layer", "n_head", "n_head_kv", "head_dim", "ffn_dim", "vocab", "codebook_size",
+        "num_codebooks", "semantic_begin", "end_id", "max_context")] + [
+        ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float),
+        ("has_qk_norm", ctypes.c_int32), ("weight_dtype", ctypes.c_int32)]
+
+
+class SlowWeights(ctypes.Structure):
+    _fields_ = [("embeddings", ctypes.c_void_p), ("codebook_embeddings", ctypes.c_void_p),
+                ("norm", ctypes.c_void_p), ("layers", LayerWeights * SLOW_MAX_LAYERS)]
+
+
 _lib = None
 
 
@@ -80,13 +97,27 @@ def library() -> ctypes.CDLL:
         lib.s2fast_test_timeline.restype = ctypes.c_int
         lib.s2fast_syncs_per_frame.argtypes = [P, I]
         lib.s2fast_syncs_per_frame.restype = ctypes.c_int
+        lib.s2fast_slow_create.argtypes = [ctypes.POINTER(SlowConfig), ctypes.POINTER(SlowWeights),
+                                           ctypes.POINTER(ctypes.c_void_p)]
+        lib.s2fast_slow_create.restype = ctypes.c_int
+        lib.s2fast_slow_destroy.argtypes = [P]
+        lib.s2fast_slow_destroy.restype = None
+        lib.s2fast_slow_step.argtypes = [P, P, I, P, P, P, P, P, P, P, P, P, P, P, V]
+        lib.s2fast_slow_step.restype = ctypes.c_int
+        lib.s2fast_full_frame.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, V]
+        lib.s2fast_full_frame.restype = ctypes.c_int
+        lib.s2fast_slow_syncs.argtypes = [P]
+        lib.s2fast_slow_syncs.restype = ctypes.c_int
+        lib.s2fast_slow_allowed.argtypes = [P]
+        lib.s2fast_slow_allowed.restype = ctypes.c_int
         _lib = lib
     return _lib
 
 
 EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_frame",
            "s2fast_forward_logits", "s2fast_test_rope_table", "s2fast_test_sample",
-           "s2fast_syncs_per_frame", "s2fast_test_timeline")
+           "s2fast_syncs_per_frame", "s2fast_test_timeline", "s2fast_slow_create", "s2fast_slow_destroy",
+           "s2fast_slow_step", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed")
 
 
 def _strerror(code: int) -> str:
@@ -229,6 +260,112 @@ class FastAR:
         rc = library().s2fast_forward_logits(self._ctx, B, _ptr(hidden), _ptr(codes), _ptr(logits), _stream(stream))
         _check(rc, "s2fast_forward_logits")
         return logits
+
+
+def make_slow_config(shape) -> SlowConfig:
+    return SlowConfig(dim=shape.dim, n_layer=shape.n_layer, n_head=shape.n_head, n_head_kv=shape.n_head_kv,
+                      head_dim=shape.head_dim, ffn_dim=shape.ffn_dim, vocab=shape.vocab,
+                      codebook_size=shape.codebook_size, num_codebooks=shape.num_codebooks,
+                      semantic_begin=shape.sem_begin, end_id=shape.end_id, max_context=shape.max_ctx,
+                      rope_base=shape.rope_base, norm_eps=shape.norm_eps, has_qk_norm=int(shape.has_qk_norm),
+                      weight_dtype=BF16 if shape.weight_dtype == "bf16" else F32)
+
+
+class SlowAR:
+    """One Slow-AR step context over device-resident weights."""
+
+    def __init__(self, shape, weights: Dict[str, torch.Tensor]):
+        self.shape = shape
+        self.weights = weights
+        lib = library()
+        cfg = make_slow_config(shape)
+        w = SlowWeights()
+        g = lambda n: _ptr(weights.get(n))
+        w.embeddings = g("embeddings")
+        w.codebook_embeddings = g("codebook_embeddings")
+        w.norm = g("norm")
+        for i in range(shape.n_layer):
+            p = f"layers.{i}."
+            L = w.layers[i]
+            for f, n in zip(LAYER_FIELDS, ("attention_norm", "attention.wqkv", "attention.q_norm",
+                                           "attention.k_norm", "attention.wo", "ffn_norm", "feed_forward.w1",
+                                           "feed_forward.w3", "feed_forward.w2")):
+                setattr(L, f, g(p + n))
+        ctx = ctypes.c_void_p()
+        _check(lib.s2fast_slow_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ctx)), "s2fast_slow_create")
+        self._ctx = ctx
+        self.n_allowed = lib.s2fast_slow_allowed(ctx)
+
+    def close(self) -> None:
+        if getattr(self, "_ctx", None):
+            library().s2fast_slow_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def syncs(self) -> int:
+        return library().s2fast_slow_syncs(self._ctx)
+
+    def kv_dtype(self):
+        return torch.bfloat16 if self.shape.weight_dtype == "bf16" else torch.float32
+
+    def _common(self, kv, prev_main, prev_codes, window, temperature, top_p, top_k):
+        s = self.shape
+        _dev(kv, self.kv_dtype(), (s.n_layer, s.n_head_kv, s.max_ctx, 2, s.head_dim), "kv_cache")
+        _dev(prev_main, torch.int32, (1,), "prev_main")
+        _dev(prev_codes, torch.int32, (s.num_codebooks,), "prev_codes")
+        _dev(window, torch.int32, (1 + RAS_WINDOW,), "window")
+        _dev(temperature, torch.float32, (1,), "temperature")
+        _dev(top_p, torch.float32, (1,), "top_p")
+        _dev(top_k, torch.int32, (1,), "top_k")
+
+    def step(self, kv, n_past: int, prev_main, prev_codes, window, u, temperature, top_p, top_k,
+             main_out=None, sem_out=None, hidden_out=None, logits_out=None, stream=None):
+        s = self.shape
+        self._common(kv, prev_main, prev_codes, window, temperature, top_p, top_k)
+        _dev(u, torch.float32, (2,), "u")
+        dev = kv.device
+        if main_out is None:
+            main_out = torch.empty(1, dtype=torch.int32, device=dev)
+        if sem_out is None:
+            sem_out = torch.empty(1, dtype=torch.int32, device=dev)
+        if hidden_out is None:
+            hidden_out = torch.empty(s.dim, dtype=torch.float32, device=dev)
+        _dev(hidden_out, torch.float32, (s.dim,), "hidden_out")
+        if logits_out is not None:
+            _dev(logits_out, torch.float32, (self.n_allowed,), "logits_out")
+        rc = library().s2fast_slow_step(self._ctx, _ptr(kv), int(n_past), _ptr(prev_main), _ptr(prev_codes),
+                                        _ptr(window), _ptr(u), _ptr(temperature), _ptr(top_p), _ptr(top_k),
+                                        _ptr(main_out), _ptr(sem_out), _ptr(hidden_out), _ptr(logits_out),
+                                        _stream(stream))
+        _check(rc, "s2fast_slow_step")
+        return main_out, sem_out, hidden_out
+
+    def full_frame(self, fast: "FastAR", kv, n_past: int, prev_main, prev_codes, window, u_slow, u_fast,
+                   temperature, top_p, top_k, main_out=None, hidden_out=None, codes_out=None, stream=None):
+        s = self.shape
+        self._common(kv, prev_main, prev_codes, window, temperature, top_p, top_k)
+        _dev(u_slow, torch.float32, (2,), "u_slow")
+        _dev(u_fast, torch.float32, (s.num_codebooks - 1,), "u_fast")
+        dev = kv.device
+        if main_out is None:
+            main_out = torch.empty(1, dtype=torch.int32, device=dev)
+        if hidden_out is None:
+            hidden_out = torch.empty(s.dim, dtype=torch.float32, device=dev)
+        if codes_out is None:
+            codes_out = torch.empty(s.num_codebooks, dtype=torch.int32, device=dev)
+        _dev(hidden_out, torch.float32, (s.dim,), "hidden_out")
+        _dev(codes_out, torch.int32, (s.num_codebooks,), "codes_out")
+        rc = library().s2fast_full_frame(self._ctx, fast._ctx, _ptr(kv), int(n_past), _ptr(prev_main),
+                                         _ptr(prev_codes), _ptr(window), _ptr(u_slow), _ptr(u_fast),
+                                         _ptr(temperature), _ptr(top_p), _ptr(top_k), _ptr(main_out),
+                                         _ptr(hidden_out), _ptr(codes_out), _stream(stream))
+        _check(rc, "s2fast_full_frame")
+        return main_out, hidden_out, codes_out
 
 
 def rope_table(head_dim: int, context: int, base: float):

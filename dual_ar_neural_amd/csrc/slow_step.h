@@ -1,0 +1,621 @@
+// Slow-AR decode step: one cooperative launch computes one new position of
+// one request and draws its main token.  Included by s2fast.hip inside its
+// anonymous namespace; it uses the GEMV, grid-barrier and sampler helpers
+// defined there.
+//
+// What one step computes ("Overall architecture & Dual-AR data flow",
+// sections 3.2 and 3.4; "Fast-AR codebook decoding and the generation main
+// loop", sections 5 and 6):
+//   x = sem_scale * embeddings[main] + sum_j codebook_embeddings[j*cbs + c_j]
+//   36 x { RMSNorm -> wqkv -> q/k RMSNorm + pair RoPE at position n_past ->
+//          attention over the KV cache (positions 0..n_past, the new key and
+//          value written at n_past in the cache's precision) -> wo -> + x;
+//          RMSNorm -> w1, w3 -> silu * -> w2 -> + x }
+//   hidden = RMSNorm(x, norm); logits = embeddings . hidden (tied);
+//   main token drawn from logits + sem_mask, redrawn at temperature 1.0 /
+//   top_p 0.9 if it is a semantic id already among the last 10 main tokens.
+//
+// Per layer the blocks run five phases, each closed by a grid barrier:
+//   QKV   RMSNorm(x) -> rows of wqkv
+//   ATTN  block (g, c): KV group g, chunk c of the positions.  The group's
+//         query heads and the new key/value are normalised and rotated in
+//         LDS; the chunk's keys/values stream from the cache once for all
+//         the group's query heads; each wave keeps an online softmax over
+//         its positions; the block leaves one (max, sum, output) partial per
+//         head
+//   WO    block (g, row group): merges group g's chunk partials (log-sum-exp
+//         weights) into the group's attention output, then wo rows over the
+//         group's columns, added across groups in an int64 fixed-point
+//         accumulator
+//   UP    RMSNorm(x + attn) -> w1, w3 rows -> silu(a1) * a3
+//   DOWN  w2 rows; x = x + attn + ffn
+// then the head (only the rows sem_mask leaves finite: every other logit is
+// -inf and can never be drawn) and, in block 0, the draw.
+
+constexpr int SLOW_MAX_LAYERS = S2FAST_SLOW_MAX_LAYERS;
+constexpr int RAS_WIN = 10;     // repetition window (main-loop page, section 6)
+constexpr int SPPW = 12;        // attention positions per wave per load batch
+constexpr int GH_MAX = 8;       // query heads per KV group
+constexpr int CMB = 32;         // chunk partials loaded per batch in the merge
+
+struct SlowArgs {
+  int dim, n_layer, n_head, n_kv, hd, ffn, vocab, ncb, cbs;
+  int sem_begin, end_id, nsem, n_allowed, end_first;
+  float eps, sem_scale;
+  int has_qkn, qkv_dim, attn_dim, gheads, gw, kmax, rmax;
+  int max_ctx, n_past, nchunk;
+  const void* emb;    // [vocab][dim]
+  const void* cemb;   // [ncb * cbs][dim]
+  const void* norm;   // [dim]
+  const LayerPtr* L;  // [n_layer] in device memory (the kernel argument stays small)
+  const float* rope;  // [2][max_ctx][hd/2]: cos then sin
+  void* kv;           // [n_layer][n_kv][max_ctx][2][hd] keys then values, weight type
+  // the request
+  const int* prev_main;     // [1] the previous frame's main token
+  const int* prev_codes;    // [ncb] and its codes
+  int* window;              // [1 + RAS_WIN]: count, then main tokens oldest first
+  const float* u;           // [2]: main draw, repetition redraw
+  const float* temp;
+  const float* top_p;
+  const int* top_k;
+  int* main_out;            // [1]
+  int* sem_out;             // [1] clamp(main - sem_begin, 0, cbs - 1)
+  float* hidden_out;        // [dim]
+  float* logits_out;        // [n_allowed] or nullptr
+  // per-launch arena: every region is written once per launch and read only
+  // after the barrier that follows its writes (see FrameArgs)
+  float* x0;                // [dim] the step's input vector
+  float* x;                 // [n_layer][x_slot]
+  float* qkv;               // [n_layer][qkv_slot]
+  long long* acc;           // [n_layer][acc_slot] (zero between launches)
+  float* g;                 // [n_layer][g_slot]
+  float* po;                // [n_layer][n_kv][nchunk][gheads][hd] chunk outputs
+  float* pml;               // [n_layer][n_kv][nchunk][gheads][2] chunk max and sum
+  float* logits;            // [n_allowed]
+  long long x_slot, qkv_slot, acc_slot, g_slot, po_slot, pml_slot;
+  u32* flags;
+  u32 epoch0;
+  u32* err;
+  u32* tlog;
+  u32 tlog_epoch;
+};
+
+struct SlowLds {
+  float* act;    // [kmax] GEMV activation row (phys() layout)
+  float* red;    // [rmax][MMAX][NWAVE]
+  float* small;  // [64]
+  float* q;      // [gheads + 2][hd]: the group's query heads, then the new key and value
+  float* qkn;    // [2][hd] q_norm, k_norm
+  float* ow;     // [NWAVE][gheads][hd + 2] per-wave attention partials
+  float* cval;
+  int* cidx;
+  u32* mark;
+  int* flag;
+  int* tok;      // [32]: previous main token, its codes; then the draw
+};
+
+__host__ __device__ inline size_t slow_lds_floats(int kmax, int rmax, int gheads, int hd) {
+  const size_t act = ((size_t)kmax + 3) & ~(size_t)3;
+  return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)(gheads + 2) * hd + 2 * (size_t)hd +
+         (size_t)NWAVE * gheads * (hd + 2) + 2 * TOPK_MAX + 256 + 4 + 32;
+}
+
+__device__ inline SlowLds slow_carve(float* base, const SlowArgs& a) {
+  SlowLds s;
+  float* p = base;
+  s.act = p; p += ((size_t)a.kmax + 3) & ~(size_t)3;
+  s.red = p; p += (size_t)a.rmax * NWAVE * MMAX;
+  s.small = p; p += 64;
+  s.q = p; p += (size_t)(a.gheads + 2) * a.hd;
+  s.qkn = p; p += 2 * (size_t)a.hd;
+  s.ow = p; p += (size_t)NWAVE * a.gheads * (a.hd + 2);
+  s.cval = p; p += TOPK_MAX;
+  s.cidx = reinterpret_cast<int*>(p); p += TOPK_MAX;
+  s.mark = reinterpret_cast<u32*>(p); p += 256;
+  s.flag = reinterpret_cast<int*>(p); p += 4;
+  s.tok = reinterpret_cast<int*>(p);
+  return s;
+}
+
+__device__ __forceinline__ const float* slow_lin(const SlowArgs& a, int l) {
+  return l == 0 ? a.x0 : a.x + (size_t)(l - 1) * a.x_slot;
+}
+
+// the cache's element type: bf16 (round to nearest even) or f32
+template <typename WT> struct KVElem;
+template <> struct KVElem<uint16_t> {
+  using pair = u32;
+  __device__ static __forceinline__ pair load(const uint16_t* p) { return *reinterpret_cast<const u32*>(p); }
+  __device__ static __forceinline__ float lo(pair v) { return __uint_as_float(v << 16); }
+  __device__ static __forceinline__ float hi(pair v) { return __uint_as_float(v & 0xFFFF0000u); }
+  __device__ static __forceinline__ uint16_t enc(float x) {
+    const u32 b = __float_as_uint(x);
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+  }
+  __device__ static __forceinline__ float round(float x) { return __uint_as_float((u32)enc(x) << 16); }
+};
+template <> struct KVElem<float> {
+  using pair = u64;
+  __device__ static __forceinline__ pair load(const float* p) { return *reinterpret_cast<const u64*>(p); }
+  __device__ static __forceinline__ float lo(pair v) { return lo_f32(v); }
+  __device__ static __forceinline__ float hi(pair v) { return hi_f32(v); }
+  __device__ static __forceinline__ float enc(float x) { return x; }
+  __device__ static __forceinline__ float round(float x) { return x; }
+};
+
+// token id of row i of the head (the ids sem_mask leaves finite, ascending)
+__device__ __forceinline__ int slow_token(const SlowArgs& a, int i) {
+  if (a.end_first) return i == 0 ? a.end_id : a.sem_begin + i - 1;
+  return i < a.nsem ? a.sem_begin + i : a.end_id;
+}
+
+enum SlowPhase { SP_QKV = 0, SP_ATTN, SP_WO, SP_UP, SP_DOWN, SP_HEAD };
+
+__device__ __forceinline__ void slow_wo_rows(const SlowArgs& a, int& g, int& r0, int& r1) {
+  const int P = gridDim.x;
+  g = blockIdx.x % a.n_kv;
+  const int rg = blockIdx.x / a.n_kv;
+  const int Pg = (P - g + a.n_kv - 1) / a.n_kv;
+  split_rows(a.dim, rg, Pg, r0, r1);
+}
+
+template <typename WT>
+__device__ __forceinline__ Plan slow_plan(const SlowArgs& a, int l, int kind) {
+  const int P = gridDim.x, b = blockIdx.x;
+  const WT* emb = reinterpret_cast<const WT*>(a.emb);
+  int r0 = 0, r1 = 0, g = 0;
+  Plan p;
+  if (kind == SP_HEAD) {
+    split_rows(a.n_allowed, b, P, r0, r1);
+    const int n = r1 - r0;
+    const long long D = a.dim;
+    if (a.end_first) {
+      if (r0 == 0) p = make_plan<WT>(emb + (long long)a.end_id * D, emb + (long long)a.sem_begin * D, D, 0, a.dim, 0, min(n, 1), n);
+      else p = make_plan<WT>(emb + (long long)(a.sem_begin + r0 - 1) * D, nullptr, D, 0, a.dim, 0, n, n);
+    } else {
+      const int na = max(0, min(r1, a.nsem) - r0);
+      const WT* wa = na > 0 ? emb + (long long)(a.sem_begin + r0) * D : emb;
+      p = make_plan<WT>(wa, emb + (long long)a.end_id * D, D, 0, a.dim, 0, na, n);
+    }
+  } else {
+    const LayerPtr& L = a.L[l];
+    switch (kind) {
+      case SP_QKV:
+        split_rows(a.qkv_dim, b, P, r0, r1);
+        p = make_plan<WT>((const WT*)L.wqkv, nullptr, a.dim, 0, a.dim, r0, r1 - r0, r1 - r0);
+        break;
+      case SP_WO:
+        slow_wo_rows(a, g, r0, r1);
+        p = make_plan<WT>((const WT*)L.wo, nullptr, a.attn_dim, g * a.gw, a.gw, r0, r1 - r0, r1 - r0);
+        break;
+      case SP_UP:
+        split_rows(a.ffn, b, P, r0, r1);
+        p = make_plan<WT>((const WT*)L.w1, (const WT*)L.w3, a.dim, 0, a.dim, r0, r1 - r0, 2 * (r1 - r0));
+        break;
+      case SP_DOWN:
+        split_rows(a.dim, b, P, r0, r1);
+        p = make_plan<WT>((const WT*)L.w2, nullptr, a.ffn, 0, a.ffn, r0, r1 - r0, r1 - r0);
+        break;
+      default:   // attention: no GEMV
+        p = make_plan<WT>(emb, nullptr, a.dim, 0, a.dim, 0, 0, 0);
+        break;
+    }
+  }
+  p.r0 = r0;
+  p.r1 = r1;
+  p.g = g;
+  return p;
+}
+
+// Layer input into LDS act (GEMV layout over dim columns) times the phase's
+// RMSNorm weight; the per-wave sums of squares go to small.  MODE 0: the
+// step's input vector built from the embedding tables (block 0 also stores
+// it to the arena for the later phases of layer 0); 1: the previous layer's
+// output; 2: layer input + the attention accumulator (x_mid).
+template <typename WT, int MODE, typename Hook>
+__device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, int l, const WT* normw,
+                                           const Hook& hook) {
+  constexpr int NS = MODE == 0 ? 2 : 3;
+  constexpr int NT = 11;                    // main token + at most 10 codebook rows per batch step
+  const int nq = a.dim >> 2;
+  const float* src = slow_lin(a, l);
+  const WT* emb = reinterpret_cast<const WT*>(a.emb);
+  const WT* cemb = reinterpret_cast<const WT*>(a.cemb);
+  float ss = 0.0f;
+  auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
+    v4f xv[NS];
+    v2ll a0[NS], a1[NS];
+    typename WQuad<WT>::type wv[NS], ev[NS][NT];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int c = quad_of(base, j, nq);
+      wv[j] = WQuad<WT>::load(normw, c);
+      if (MODE == 0) {
+        ev[j][0] = WQuad<WT>::load(emb + (size_t)s.tok[0] * a.dim, c);
+#pragma unroll
+        for (int t = 1; t < NT; ++t) {
+          const int jj = min(t - 1, a.ncb - 1);
+          ev[j][t] = WQuad<WT>::load(cemb + ((size_t)jj * a.cbs + s.tok[1 + jj]) * a.dim, c);
+        }
+      } else {
+        xv[j] = *reinterpret_cast<const v4f*>(src + 4 * c);
+        if (MODE == 2) {
+          const long long* ac = a.acc + (size_t)l * a.acc_slot + 4 * c;
+          a0[j] = *reinterpret_cast<const v2ll*>(ac);
+          a1[j] = *reinterpret_cast<const v2ll*>(ac + 2);
+        }
+      }
+    }
+    after();
+    const int nj = steps_opaque(nq, base);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (j >= nj) break;
+      const int cu = base + j * NTHREADS + tidx();
+      const int c = min(cu, nq - 1);
+      float v[4];
+      if (MODE == 0) {
+        // sem_scale * e_main, then the codebook rows added in codebook order
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = a.sem_scale * WQuad<WT>::get(ev[j][0], e);
+#pragma unroll
+        for (int t = 1; t < NT; ++t) {
+          if (t > a.ncb) break;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += WQuad<WT>::get(ev[j][t], e);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = xv[j][e];
+        if (MODE == 2) {
+          v[0] += from_fx(a0[j][0]); v[1] += from_fx(a0[j][1]);
+          v[2] += from_fx(a1[j][0]); v[3] += from_fx(a1[j][1]);
+        }
+      }
+      if (cu < nq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(v[e], v[e], ss);
+        if (MODE == 0 && blockIdx.x == 0)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st_coh(a.x0 + 4 * c + e, v[e]);
+        v4f o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = v[e] * WQuad<WT>::get(wv[j], e);
+        *reinterpret_cast<v4f*>(s.act + phys<WT>(4 * c, a.dim)) = o;
+      }
+    }
+  };
+  batch(0, hook);
+  for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
+  store_ss(s.small, 1, ss, 0.0f);
+}
+
+template <typename WT>
+__device__ __forceinline__ void slow_qkv(const SlowArgs& a, const SlowLds& s, int l, Plan& pl) {
+  const int r0 = pl.r0, r1 = pl.r1;
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  const WT* nw = reinterpret_cast<const WT*>(a.L[l].attn_norm);
+  if (l == 0) slow_stage<WT, 0>(a, s, l, nw, pro);
+  else slow_stage<WT, 1>(a, s, l, nw, pro);
+  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
+  __syncthreads();
+  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
+  __syncthreads();
+  const float den = norm_den(s.small, 0, a.dim, a.eps);
+  float* out = a.qkv + (size_t)l * a.qkv_slot;
+  for (int r = tidx(); r < r1 - r0; r += NTHREADS) st_coh(out + r0 + r, red_sum(s.red, r, 0) / den);
+}
+
+template <typename WT>
+__device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, int l) {
+  using KV = KVElem<WT>;
+  const int G = a.n_kv, gh = a.gheads, hd = a.hd, H = a.n_head;
+  const int g = blockIdx.x % G, c = blockIdx.x / G;
+  if (c >= a.nchunk) return;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int N = a.n_past + 1;
+  const int p0 = (int)(((long long)N * c) / a.nchunk), p1 = (int)(((long long)N * (c + 1)) / a.nchunk);
+  const float* qkv = a.qkv + (size_t)l * a.qkv_slot;
+  // the group's query heads, then the new key and value, and the q/k norm weights
+  for (int i = tidx(); i < (gh + 2) * hd; i += NTHREADS) {
+    const int v = i / hd, d = i - v * hd;
+    const int src = v < gh ? (g * gh + v) * hd : (v == gh ? (H + g) * hd : (H + G + g) * hd);
+    s.q[i] = qkv[src + d];
+  }
+  if (a.has_qkn)
+    for (int i = tidx(); i < 2 * hd; i += NTHREADS)
+      s.qkn[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(i < hd ? a.L[l].q_norm : a.L[l].k_norm), i % hd);
+  __syncthreads();
+  for (int v = wave; v < gh + 1; v += NWAVE)
+    head_norm_rope(s.q + (size_t)v * hd, hd, v < gh ? s.qkn : s.qkn + hd, a.has_qkn, a.eps, a.rope, a.max_ctx,
+                   a.n_past);
+  __syncthreads();
+  float* kn = s.q + (size_t)gh * hd;
+  float* vn = kn + hd;
+  for (int d = tidx(); d < 2 * hd; d += NTHREADS) kn[d] = KV::round(kn[d]);   // the cache's precision
+  __syncthreads();
+
+  const WT* kvg = reinterpret_cast<const WT*>(a.kv) + (size_t)(l * G + g) * a.max_ctx * 2 * hd;
+  const bool own = 2 * lane < hd;
+  const int lp = own ? lane : 0;
+  float qx[GH_MAX][2], m[GH_MAX], ls[GH_MAX], o0[GH_MAX], o1[GH_MAX];
+#pragma unroll
+  for (int hh = 0; hh < GH_MAX; ++hh) {
+    const int h = min(hh, gh - 1);
+    qx[hh][0] = own ? s.q[h * hd + 2 * lp] : 0.0f;
+    qx[hh][1] = own ? s.q[h * hd + 2 * lp + 1] : 0.0f;
+    m[hh] = -INFINITY;
+    ls[hh] = 0.0f;
+    o0[hh] = 0.0f;
+    o1[hh] = 0.0f;
+  }
+  const float scale = 1.0f / sqrtf((float)hd);
+  for (int base = p0 + wave; base < p1; base += NWAVE * SPPW) {
+    typename KV::pair kr[SPPW], vr[SPPW];
+#pragma unroll
+    for (int i = 0; i < SPPW; ++i) {
+      const int j = base + NWAVE * i;
+      const int jc = j < p1 ? j : p0;     // past the chunk: re-read its first row (in bounds)
+      const WT* row = kvg + (size_t)jc * 2 * hd + 2 * lp;
+      kr[i] = KV::load(row);
+      vr[i] = KV::load(row + hd);
+    }
+    float kx[SPPW][2], vx[SPPW][2];
+#pragma unroll
+    for (int i = 0; i < SPPW; ++i) {
+      // the new position comes from LDS; a position past the chunk reads as
+      // zeros, so whatever the cache holds past n_past never enters the sums
+      const int j = base + NWAVE * i;
+      const bool nw = j == a.n_past, live = j < p1;
+      kx[i][0] = nw ? kn[2 * lp] : (live ? KV::lo(kr[i]) : 0.0f);
+      kx[i][1] = nw ? kn[2 * lp + 1] : (live ? KV::hi(kr[i]) : 0.0f);
+      vx[i][0] = nw ? vn[2 * lp] : (live ? KV::lo(vr[i]) : 0.0f);
+      vx[i][1] = nw ? vn[2 * lp + 1] : (live ? KV::hi(vr[i]) : 0.0f);
+    }
+#pragma unroll
+    for (int hh = 0; hh < GH_MAX; ++hh) {
+      if (hh >= gh) break;
+      float sc[SPPW];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < SPPW; ++i) {
+        float part = fmaf(qx[hh][0], kx[i][0], qx[hh][1] * kx[i][1]);
+        part = wave_sum(own ? part : 0.0f);
+        sc[i] = (base + NWAVE * i < p1) ? part * scale : -INFINITY;
+        mb = fmaxf(mb, sc[i]);
+      }
+      const float mn = fmaxf(m[hh], mb);
+      if (mn == -INFINITY) continue;
+      const float r = expf(m[hh] - mn);   // 0 while m is -inf
+      float l_ = ls[hh] * r, a0 = o0[hh] * r, a1 = o1[hh] * r;
+#pragma unroll
+      for (int i = 0; i < SPPW; ++i) {
+        const float e = expf(sc[i] - mn);   // 0 past the chunk
+        l_ += e;
+        a0 = fmaf(e, vx[i][0], a0);
+        a1 = fmaf(e, vx[i][1], a1);
+      }
+      m[hh] = mn;
+      ls[hh] = l_;
+      o0[hh] = a0;
+      o1[hh] = a1;
+    }
+  }
+  // per-wave partials, then the block's partial per head
+  const int ws = hd + 2;
+#pragma unroll
+  for (int hh = 0; hh < GH_MAX; ++hh) {
+    if (hh >= gh) break;
+    float* w = s.ow + ((size_t)wave * gh + hh) * ws;
+    if (own) { w[2 * lane] = o0[hh]; w[2 * lane + 1] = o1[hh]; }
+    if (lane == 0) { w[hd] = m[hh]; w[hd + 1] = ls[hh]; }
+  }
+  __syncthreads();
+  float* po = a.po + (size_t)l * a.po_slot + ((size_t)g * a.nchunk + c) * gh * hd;
+  float* pml = a.pml + (size_t)l * a.pml_slot + ((size_t)g * a.nchunk + c) * gh * 2;
+  for (int t = tidx(); t < gh * hd; t += NTHREADS) {
+    const int hh = t / hd, d = t - hh * hd;
+    float M = -INFINITY;
+    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.ow[((size_t)w * gh + hh) * ws + hd]);
+    float O = 0.0f, Ls = 0.0f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < NWAVE; ++w) {
+        const float* ww = s.ow + ((size_t)w * gh + hh) * ws;
+        const float f = expf(ww[hd] - M);   // 0 for a wave without positions
+        O = fmaf(f, ww[d], O);
+        Ls = fmaf(f, ww[hd + 1], Ls);
+      }
+    }
+    st_coh(po + t, O);
+    if (d == 0) {
+      st_coh(pml + 2 * hh, M);
+      st_coh(pml + 2 * hh + 1, Ls);
+    }
+  }
+  // the new key and value into the cache (the block whose chunk holds n_past)
+  if (c == a.nchunk - 1) {
+    WT* row = reinterpret_cast<WT*>(a.kv) + ((size_t)(l * G + g) * a.max_ctx + a.n_past) * 2 * hd;
+    for (int d = tidx(); d < 2 * hd; d += NTHREADS) row[d] = KV::enc(kn[d]);
+  }
+}
+
+template <typename WT>
+__device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int l, Plan& pl) {
+  const int g = pl.g, r0 = pl.r0, r1 = pl.r1;
+  const int gh = a.gheads, hd = a.hd, nc = a.nchunk, n = gh * hd;
+  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
+  u32x4 slot[RING];
+  const float* pml = a.pml + (size_t)l * a.pml_slot + (size_t)g * nc * gh * 2;
+  const float* po = a.po + (size_t)l * a.po_slot + (size_t)g * nc * gh * hd;
+  // merge the chunk partials of every head of the group: thread t takes
+  // element t of the group's output (head t / hd, dim t % hd)
+  const int iters = (n + NTHREADS - 1) / NTHREADS;
+  for (int it = 0; it < iters; ++it) {
+    const int t = it * NTHREADS + tidx();
+    const int tt = min(t, n - 1);
+    const int hh = tt / hd;
+    float M = -INFINITY, Ls = 0.0f, O = 0.0f;
+    for (int c0 = 0; c0 < nc; c0 += CMB) {
+      u64 ml[CMB];
+      float ov[CMB];
+#pragma unroll
+      for (int j = 0; j < CMB; ++j) {
+        const int cc = min(c0 + j, nc - 1);
+        ml[j] = ld64(pml + ((size_t)cc * gh + hh) * 2);
+        ov[j] = po[(size_t)cc * n + tt];
+      }
+      if (it == 0 && c0 == 0) gemv_prologue(pl, slot);
+      float mb = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < CMB; ++j)
+        if (c0 + j < nc) mb = fmaxf(mb, lo_f32(ml[j]));
+      const float mn = fmaxf(M, mb);
+      if (mn == -INFINITY) continue;
+      const float r = expf(M - mn);
+      Ls *= r;
+      O *= r;
+#pragma unroll
+      for (int j = 0; j < CMB; ++j) {
+        if (c0 + j < nc) {
+          const float f = expf(lo_f32(ml[j]) - mn);   // 0 for an empty chunk
+          Ls = fmaf(f, hi_f32(ml[j]), Ls);
+          O = fmaf(f, ov[j], O);
+        }
+      }
+      M = mn;
+    }
+    if (t < n) s.act[phys<WT>(t, a.gw)] = O / Ls;
+  }
+  __syncthreads();
+  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
+  __syncthreads();
+  long long* acc = a.acc + (size_t)l * a.acc_slot;
+  for (int r = tidx(); r < r1 - r0; r += NTHREADS) atomic_add_coh(acc + r0 + r, to_fx(red_sum(s.red, r, 0)));
+}
+
+template <typename WT>
+__device__ __forceinline__ void slow_up(const SlowArgs& a, const SlowLds& s, int l, Plan& pl) {
+  const int r0 = pl.r0, r1 = pl.r1, nr = r1 - r0;
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  slow_stage<WT, 2>(a, s, l, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
+  zero_lds(s.red, 2 * nr * NWAVE * MMAX);
+  __syncthreads();
+  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);   // rows [0, nr): w1, [nr, 2nr): w3
+  __syncthreads();
+  const float den = norm_den(s.small, 0, a.dim, a.eps);
+  float* out = a.g + (size_t)l * a.g_slot;
+  for (int r = tidx(); r < nr; r += NTHREADS)
+    st_coh(out + r0 + r, silu(red_sum(s.red, r, 0) / den) * (red_sum(s.red, nr + r, 0) / den));
+}
+
+template <typename WT>
+__device__ __forceinline__ void slow_down(const SlowArgs& a, const SlowLds& s, int l, Plan& pl) {
+  const int r0 = pl.r0, r1 = pl.r1;
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  stage_arena<WT, true, 5>(s.act, a.g + (size_t)l * a.g_slot, a.ffn, pro);
+  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
+  __syncthreads();
+  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
+  __syncthreads();
+  const float* xin = slow_lin(a, l);
+  float* xo = a.x + (size_t)l * a.x_slot;
+  long long* acc = a.acc + (size_t)l * a.acc_slot;
+  for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
+    const int k = r0 + r;
+    const float xm = xin[k] + from_fx(acc[k]);
+    st_coh(xo + k, xm + red_sum(s.red, r, 0));
+    st_coh(acc + k, 0ll);   // ready for the next launch
+  }
+}
+
+template <typename WT>
+__device__ __forceinline__ void slow_head(const SlowArgs& a, const SlowLds& s, Plan& pl) {
+  const int r0 = pl.r0, r1 = pl.r1;
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  // the final norm reads the last layer's output: the same staging as a
+  // layer input one past the last layer
+  slow_stage<WT, 1>(a, s, a.n_layer, reinterpret_cast<const WT*>(a.norm), pro);
+  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
+  __syncthreads();
+  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
+  __syncthreads();
+  const float den = norm_den(s.small, 0, a.dim, a.eps);
+  for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
+    const float v = red_sum(s.red, r, 0) / den;
+    st_coh(a.logits + r0 + r, v);
+    if (a.logits_out) a.logits_out[r0 + r] = v;
+  }
+  // hidden = RMSNorm(x, norm): the normalised state handed to Fast-AR
+  if (blockIdx.x == 0)
+    for (int k = tidx(); k < a.dim; k += NTHREADS) a.hidden_out[k] = s.act[phys<WT>(k, a.dim)] / den;
+}
+
+// Block 0, after the head's barrier: the main-token draw, the repetition
+// check against the window, the window update (main-loop page, sections 5
+// and 6).
+__device__ __forceinline__ void slow_draw(const SlowArgs& a, const SlowLds& s) {
+  const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
+  const int i1 = sample_request(a.logits, a.n_allowed, a.temp[0], a.top_p[0], a.top_k[0], a.u[0], sc);
+  if (tidx() == 0) {
+    const int tok = slow_token(a, min(max(i1, 0), a.n_allowed - 1));
+    const int cnt = min(max(a.window[0], 0), RAS_WIN);
+    bool rep = false;
+    for (int j = 0; j < cnt; ++j) rep |= a.window[1 + j] == tok;
+    s.tok[16] = tok;
+    s.tok[17] = (rep && tok >= a.sem_begin && tok < a.sem_begin + a.nsem) ? 1 : 0;
+  }
+  __syncthreads();
+  int tok = s.tok[16];
+  if (s.tok[17]) {
+    const int i2 = sample_request(a.logits, a.n_allowed, 1.0f, 0.9f, a.top_k[0], a.u[1], sc);
+    if (tidx() == 0) s.tok[16] = slow_token(a, min(max(i2, 0), a.n_allowed - 1));
+    __syncthreads();
+    tok = s.tok[16];
+  }
+  if (tidx() == 0) {
+    a.main_out[0] = tok;
+    a.sem_out[0] = min(max(tok - a.sem_begin, 0), a.cbs - 1);
+    int cnt = min(max(a.window[0], 0), RAS_WIN);
+    if (cnt == RAS_WIN) {
+      for (int j = 0; j + 1 < RAS_WIN; ++j) a.window[1 + j] = a.window[2 + j];
+      a.window[RAS_WIN] = tok;
+    } else {
+      a.window[1 + cnt] = tok;
+      ++cnt;
+    }
+    a.window[0] = cnt;
+  }
+}
+
+template <typename WT>
+__global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs a) {
+  extern __shared__ float lds_base[];
+  const SlowLds s = slow_carve(lds_base, a);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  u32 epoch = a.epoch0;
+  if (tidx() <= a.ncb) {
+    const int t = tidx();
+    s.tok[t] = t == 0 ? min(max(a.prev_main[0], 0), a.vocab - 1) : min(max(a.prev_codes[t - 1], 0), a.cbs - 1);
+  }
+  __syncthreads();
+  const int nph = 5 * a.n_layer + 1;
+  for (int ph = 0; ph < nph; ++ph) {
+    const int l = ph / 5;
+    const int kind = ph < 5 * a.n_layer ? ph - 5 * l : (int)SP_HEAD;
+    Plan pl = slow_plan<WT>(a, l, kind);
+    switch (kind) {
+      case SP_QKV: slow_qkv<WT>(a, s, l, pl); break;
+      case SP_ATTN: slow_attn<WT>(a, s, l); break;
+      case SP_WO: slow_wo<WT>(a, s, l, pl); break;
+      case SP_UP: slow_up<WT>(a, s, l, pl); break;
+      case SP_DOWN: slow_down<WT>(a, s, l, pl); break;
+      default: slow_head<WT>(a, s, pl); break;
+    }
+    if (!grid_sync(a, epoch, s.flag)) return;
+  }
+  if (blockIdx.x == 0) slow_draw(a, s);
+}

@@ -173,6 +173,118 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
 int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* codes,
                           float* logits, void* stream);
 
+/* ---- Slow-AR decode step and the full Dual-AR frame ----
+ *
+ * What a step computes ("Overall architecture & Dual-AR data flow", sections
+ * 3.2 and 3.4; "Fast-AR codebook decoding and the generation main loop",
+ * sections 5 and 6): the previous frame's 11 values (main token m and codes
+ * c_0..c_9) give the input
+ *     x = (1/sqrt(num_codebooks+1)) * embeddings[m]
+ *         + sum_j codebook_embeddings[j * codebook_size + c_j],
+ * which runs through n_layer pre-norm layers (RMSNorm, fused wqkv, per-head
+ * q/k RMSNorm, pair RoPE at position n_past, GQA attention over the KV cache
+ * positions 0..n_past, wo, SwiGLU) as position n_past; the layer's new key
+ * and value are written into the cache at n_past.  hidden = RMSNorm(x, norm);
+ * the tied logits embeddings . hidden are masked to the semantic ids
+ * [semantic_begin, semantic_begin + codebook_size) and end_id, and the main
+ * token is drawn from them with the sampler of s2fast_decode_frame.  A
+ * semantic main token already in the window of the last 10 main tokens is
+ * drawn again at temperature 1.0, top_p 0.9 (same top_k) with the second
+ * uniform; the window then receives the main token.
+ * Only the unmasked logits are computed: every other logit is -inf and can
+ * never be drawn. */
+#define S2FAST_SLOW_MAX_LAYERS 64
+#define S2FAST_RAS_WINDOW 10
+
+/* S2 Pro: dim 2560, 36 layers, 32 / 8 heads, head_dim 128, ffn 9728, vocab
+ * 155776, codebook_size 4096, 10 codebooks, semantic ids 151678..155773,
+ * RoPE base 1e6, eps 1e-6 ("Model loading and GGUF", section 2.2). */
+typedef struct s2fast_slow_config {
+  int32_t dim;
+  int32_t n_layer;          /* <= S2FAST_SLOW_MAX_LAYERS */
+  int32_t n_head;
+  int32_t n_head_kv;        /* n_head % n_head_kv == 0, n_head / n_head_kv <= 8 */
+  int32_t head_dim;         /* multiple of 8, <= 128 */
+  int32_t ffn_dim;
+  int32_t vocab;            /* rows of embeddings */
+  int32_t codebook_size;    /* semantic ids and codes per codebook, <= 8191 */
+  int32_t num_codebooks;    /* codes per frame, 1..10 */
+  int32_t semantic_begin;   /* first semantic id */
+  int32_t end_id;           /* the end-of-speech id sem_mask also leaves open */
+  int32_t max_context;      /* positions the KV cache holds */
+  float rope_base;
+  float norm_eps;
+  int32_t has_qk_norm;
+  int32_t weight_dtype;     /* S2FAST_BF16 or S2FAST_F32: weights and KV cache */
+} s2fast_slow_config;
+
+/* Device pointers of weight_dtype, row-major [out, in], valid and unchanged
+ * for the context's life. */
+typedef struct s2fast_slow_weights {
+  const void* embeddings;           /* [vocab, dim], also the tied output matrix */
+  const void* codebook_embeddings;  /* [num_codebooks * codebook_size, dim] */
+  const void* norm;                 /* [dim] final RMSNorm weight */
+  s2fast_layer_weights layers[S2FAST_SLOW_MAX_LAYERS];
+} s2fast_slow_weights;
+
+typedef struct s2fast_slow_ctx s2fast_slow_ctx;
+
+/* Validate, allocate the step's device scratch (one launch's arena, about
+ * n_layer * 0.7 MB at the S2 Pro shape) and the RoPE table for max_context
+ * positions.  Shape limits (else S2FAST_ERR_ARG): dim, ffn_dim and the
+ * per-KV-group width multiples of 8 (bf16) or 4 (f32) elements and <= 16384;
+ * the semantic range inside [0, vocab); end_id in [0, vocab);
+ * max_context >= 1.  Missing weight pointers give S2FAST_ERR_NO_FAST_DECODER.
+ * Release with s2fast_slow_destroy. */
+int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights* w, s2fast_slow_ctx** out);
+
+void s2fast_slow_destroy(s2fast_slow_ctx* ctx);
+
+/* One Slow-AR decode step of one request.
+ *   kv_cache    [n_layer, n_head_kv, max_context, 2, head_dim] weight_dtype,
+ *               keys (after q/k norm and RoPE) then values per position,
+ *               16-byte aligned; positions < n_past are read, position n_past
+ *               is written (new entries are rounded to the cache type)
+ *   n_past      host int in [0, max_context): the new position's index
+ *   prev_main   [1] i32, prev_codes [num_codebooks] i32: the previous
+ *               frame's values (clamped on the device into [0, vocab) and
+ *               [0, codebook_size))
+ *   window      [1 + S2FAST_RAS_WINDOW] i32 IN/OUT: count, then the last
+ *               main tokens oldest first
+ *   u           [2] f32 uniforms in (0,1): the draw and the repetition redraw
+ *   temperature, top_p [1] f32, top_k [1] i32: as s2fast_decode_frame
+ *   main_out    [1] i32 OUT the main token
+ *   sem_code_out [1] i32 OUT main - semantic_begin clamped to [0, codebook_size)
+ *   hidden_out  [dim] f32 OUT RMSNorm(x, norm), 16-byte aligned
+ *   logits_out  [n_allowed] f32 OUT or NULL: the unmasked logits, ids
+ *               ascending (n_allowed = codebook_size, + 1 if end_id is
+ *               outside the semantic range)
+ * Errors: S2FAST_ERR_ARG for NULL pointers (other than logits_out),
+ * misaligned kv_cache / hidden_out or n_past outside [0, max_context). */
+int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const int32_t* prev_main,
+                     const int32_t* prev_codes, int32_t* window, const float* u, const float* temperature,
+                     const float* top_p, const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out,
+                     float* hidden_out, float* logits_out, void* stream);
+
+/* One full frame ("Fast-AR codebook decoding ...", section 5.1): the Slow-AR
+ * step above, then s2fast_decode_frame of one request on its hidden state
+ * and semantic code.  The fast context must have in_dim == dim,
+ * the same codebook_size and num_codebooks.
+ *   u_slow [2], u_fast [num_codebooks-1] f32; main_out [1] i32 OUT;
+ *   hidden_out [dim] f32 OUT (16-byte aligned); codes_out [num_codebooks]
+ *   i32 OUT [sem_code, c_1, ..., c_9].
+ * A following frame passes main_out and codes_out as prev_main and
+ * prev_codes and n_past + 1; the caller stops at end_id. */
+int s2fast_full_frame(s2fast_slow_ctx* slow, s2fast_ctx* fast, void* kv_cache, int32_t n_past,
+                      const int32_t* prev_main, const int32_t* prev_codes, int32_t* window, const float* u_slow,
+                      const float* u_fast, const float* temperature, const float* top_p, const int32_t* top_k,
+                      int32_t* main_out, float* hidden_out, int32_t* codes_out, void* stream);
+
+/* Grid-wide synchronisation points of one Slow-AR step (5 per layer + 1),
+ * and the number of head rows (n_allowed); -1 on error. */
+int s2fast_slow_syncs(const s2fast_slow_ctx* ctx);
+int s2fast_slow_allowed(const s2fast_slow_ctx* ctx);
+
 /* ---- test exports (used by the test suite; not part of the hot path) ---- */
 
 /* Host-side: the RoPE table the context uses, [context, head_dim/2] cos and

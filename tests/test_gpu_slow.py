@@ -1,0 +1,245 @@
+"""Parity of the Slow-AR step and the full frame (HIP path through the C ABI)
+with the oracle, on the GPU.
+
+Tolerances (float32 accumulation in another order than the oracle's):
+  logits: |delta| <= 1e-2 * max|logit| + 1e-3 (the Fast-AR logit bound);
+  hidden: |delta| <= 1e-3 * max|hidden| + 1e-4;
+  new cache entries: rtol 1e-2, atol 1e-3 (a float32 value a few ulps away
+  from the oracle's can round to the neighbouring bf16 value, 2^-8 apart);
+  main token and codes: equal unless the oracle reports a knife-edge draw,
+  and then inside the allowed set."""
+import numpy as np
+import pytest
+import torch
+
+from dual_ar_neural_amd import binding as bd
+from oracle import fast_ar as fa
+from oracle import slow_ar as sa
+from synth import inputs as si
+from synth import slow_inputs as ssi
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def _announce(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+class SlowPair:
+    def __init__(self, shape, seed):
+        self.shape = shape
+        self.host = ssi.make_weights(shape, seed)
+        self.oracle = sa.SlowModel.from_weights(shape, self.host)
+        self.dev = bd.device_weights(shape, self.host)
+        self.gpu = bd.SlowAR(shape, self.dev)
+
+
+@pytest.fixture(scope="module")
+def slow_tiny():
+    _announce("slow tiny model")
+    return SlowPair(ssi.SLOW_TINY, ssi.SLOW_WORKLOADS["slow_tiny"].seed(0))
+
+
+@pytest.fixture(scope="module")
+def slow_ragged():
+    _announce("slow ragged model")
+    return SlowPair(ssi.SLOW_RAGGED, ssi.SLOW_WORKLOADS["slow_ragged"].seed(0))
+
+
+def _host_kv(shape, n_past, seed):
+    """Cache with positions < n_past filled; positions >= n_past hold NaN,
+    which no correct step reads."""
+    kv = ssi.make_kv_cache(shape, n_past, seed)
+    if shape.weight_dtype == "bf16":
+        kv[:, :, n_past:] = 0x7FC0          # bf16 NaN
+        return kv, si.f32_from_bf16_bits(kv)
+    kv[:, :, n_past:] = np.nan
+    return kv, kv.copy()
+
+
+def _dev_kv(kv):
+    if kv.dtype == np.uint16:
+        return torch.from_numpy(kv.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(kv).cuda()
+
+
+def _kv_f32(t):
+    return t.float().cpu().numpy()
+
+
+def _i32(a):
+    return torch.tensor(np.asarray(a, dtype=np.int32).reshape(-1)).cuda()
+
+
+def _f32(a):
+    return torch.tensor(np.asarray(a, dtype=F32).reshape(-1)).cuda()
+
+
+def _window_dev(win):
+    w = np.zeros(1 + bd.RAS_WINDOW, np.int32)
+    w[0] = len(win)
+    w[1:1 + len(win)] = win
+    return _i32(w)
+
+
+def _check_step(p, n_past, main, codes, win, u, T=0.8, top_p=0.8, top_k=30, seed=77):
+    s = p.shape
+    kv_host, kv_f = _host_kv(s, n_past, seed)
+    kv = _dev_kv(kv_host)
+    logits = torch.empty(p.gpu.n_allowed, dtype=torch.float32, device="cuda")
+    window = _window_dev(win)
+    _announce(f"slow step {s.name} n_past={n_past} window={len(win)}")
+    m_out, sem_out, h_out = p.gpu.step(kv, n_past, _i32([main]), _i32(codes), window, _f32(u), _f32([T]),
+                                       _f32([top_p]), _i32([top_k]), logits_out=logits)
+    torch.cuda.synchronize()
+    st = sa.step(p.oracle, sa.combine(p.oracle, main, codes), kv_f, n_past)
+    ids = sa.allowed_ids(s)
+    assert ids.size == p.gpu.n_allowed
+    ref = st.logits[ids]
+    got = logits.cpu().numpy()
+    tol = 1e-2 * np.abs(ref).max() + 1e-3
+    assert np.abs(got - ref).max() <= tol, (np.abs(got - ref).max(), tol)
+    h = h_out.cpu().numpy()
+    assert np.abs(h - st.hidden).max() <= 1e-3 * np.abs(st.hidden).max() + 1e-4
+    kv_after = _kv_f32(kv)
+    np.testing.assert_allclose(kv_after[:, :, n_past], st.kv_new, rtol=1e-2, atol=1e-3)
+    # every other position is untouched
+    assert np.array_equal(np.delete(kv_after, n_past, axis=2), np.delete(kv_f, n_past, axis=2), equal_nan=True)
+    md = sa.draw_main(s, st.logits, list(win), T, top_p, top_k, u[0], u[1])
+    tok = int(m_out.item())
+    if not md.fragile:
+        assert tok == md.token, (tok, md)
+    assert tok in set(ids.tolist())
+    assert int(sem_out.item()) == sa.sem_code(s, tok)
+    w = window.cpu().numpy()
+    want = sa.push_window(list(win), tok)
+    assert w[0] == len(want) and list(w[1:1 + w[0]]) == want
+    return md, tok
+
+
+@pytest.mark.parametrize("n_past", [0, 1, 37, 79])
+def test_slow_step_tiny(slow_tiny, n_past):
+    s = slow_tiny.shape
+    inp = ssi.make_step_inputs(ssi.SLOW_WORKLOADS["slow_tiny"], 1)
+    _check_step(slow_tiny, n_past, inp["main"][0], inp["codes"][0], [], inp["u_slow"][0])
+
+
+@pytest.mark.parametrize("n_past", [0, 5, 130, 299])
+def test_slow_step_ragged(slow_ragged, n_past):
+    inp = ssi.make_step_inputs(ssi.SLOW_WORKLOADS["slow_ragged"], 2)
+    win = [int(x) for x in (inp["main"][1], slow_ragged.shape.sem_begin + 3)]
+    _check_step(slow_ragged, n_past, inp["main"][0], inp["codes"][0], win, inp["u_slow"][0], T=0.9, top_p=0.85)
+
+
+def test_slow_step_greedy_and_full_window(slow_ragged):
+    s = slow_ragged.shape
+    inp = ssi.make_step_inputs(ssi.SLOW_WORKLOADS["slow_ragged"], 1)
+    win = list(range(s.sem_begin, s.sem_begin + bd.RAS_WINDOW))
+    _check_step(slow_ragged, 64, inp["main"][0], inp["codes"][0], win, inp["u_slow"][0], T=0.0)
+
+
+def test_slow_step_repetition_redraw(slow_ragged):
+    """A window holding the oracle's first draw forces the redraw at
+    temperature 1.0 / top_p 0.9 with the second uniform."""
+    s = slow_ragged.shape
+    inp = ssi.make_step_inputs(ssi.SLOW_WORKLOADS["slow_ragged"], 1)
+    main, codes, u = inp["main"][0], inp["codes"][0], inp["u_slow"][0]
+    kv_host, kv_f = _host_kv(s, 40, 77)
+    st = sa.step(slow_ragged.oracle, sa.combine(slow_ragged.oracle, main, codes), kv_f, 40)
+    first = sa.draw_main(s, st.logits, [], 0.9, 0.85, 30, u[0], u[1])
+    assert s.sem_begin <= first.token <= s.sem_end
+    md, tok = _check_step(slow_ragged, 40, main, codes, [s.sem_begin, first.token], u, T=0.9, top_p=0.85)
+    assert md.resampled
+
+
+def test_slow_step_rejects_bad_arguments(slow_tiny):
+    s = slow_tiny.shape
+    kv = torch.zeros((s.n_layer, s.n_head_kv, s.max_ctx, 2, s.head_dim), dtype=torch.float32, device="cuda")
+    args = (_i32([s.sem_begin]), _i32(np.zeros(s.num_codebooks)), _window_dev([]), _f32([0.5, 0.5]),
+            _f32([0.8]), _f32([0.8]), _i32([30]))
+    for n_past in (-1, s.max_ctx):
+        with pytest.raises(bd.S2FastError) as e:
+            slow_tiny.gpu.step(kv, n_past, *args)
+        assert e.value.code == 1
+
+
+def _full_frames(p, fast_pair, n_frames, n_fill, u_slow, u_fast, main0, codes0, T, top_p, top_k=30):
+    """Chained frames on the device (each frame's outputs feed the next)
+    against the oracle's frame loop."""
+    s = p.shape
+    kv_host, kv_f = _host_kv(s, n_fill + n_frames, 91)
+    kv_host[:, :, n_fill:] = 0x7FC0 if s.weight_dtype == "bf16" else np.nan
+    kv_f = si.f32_from_bf16_bits(kv_host) if s.weight_dtype == "bf16" else kv_host.copy()
+    kv = _dev_kv(kv_host)
+    window = _window_dev([])
+    main_d, codes_d = _i32([main0]), _i32(codes0)
+    hid = torch.empty(s.dim, dtype=torch.float32, device="cuda")
+    o_main, o_codes, o_win = int(main0), np.asarray(codes0), []
+    allowed = set(sa.allowed_ids(s).tolist())
+    exact = fragile = 0
+    for f in range(n_frames):
+        _announce(f"full frame {s.name} frame {f}")
+        m_new = torch.empty(1, dtype=torch.int32, device="cuda")
+        c_new = torch.empty(s.num_codebooks, dtype=torch.int32, device="cuda")
+        p.gpu.full_frame(fast_pair.gpu, kv, n_fill + f, main_d, codes_d, window, _f32(u_slow[f]), _f32(u_fast[f]),
+                         _f32([T]), _f32([top_p]), _i32([top_k]), main_out=m_new, hidden_out=hid, codes_out=c_new)
+        torch.cuda.synchronize()
+        r = sa.decode_frame(p.oracle, fast_pair.oracle, kv_f, n_fill + f, o_main, o_codes, o_win, u_slow[f],
+                            u_fast[f], T, top_p, top_k)
+        tok, codes = int(m_new.item()), c_new.cpu().numpy()
+        h = hid.cpu().numpy()
+        assert np.abs(h - r.hidden).max() <= 1e-3 * np.abs(r.hidden).max() + 1e-4
+        assert tok in allowed and codes.min() >= 0 and codes.max() < s.codebook_size
+        if r.main.fragile:
+            fragile += 1              # a knife-edge main draw: the GPU's token is followed below
+        else:
+            assert tok == r.main.token, (f, tok, r.main)
+            # codes up to the first knife-edge Fast-AR draw are exact
+            k = 1 + int(np.argmax(r.fast_fragile)) if r.fast_fragile.any() else s.num_codebooks
+            assert np.array_equal(codes[:k], r.codes[:k]), (f, codes, r.codes, r.fast_fragile)
+            exact += k
+        kv_f[:, :, n_fill + f] = r.kv_new
+        # the next frame starts from the GPU's draws on both sides
+        o_main, o_codes, o_win = tok, codes, sa.push_window(o_win, tok)
+        main_d, codes_d = m_new, c_new
+    assert _kv_f32(kv)[:, :, n_fill:n_fill + n_frames].shape[2] == n_frames
+    return exact, fragile
+
+
+class FastPair:
+    def __init__(self, shape, seed):
+        self.oracle = fa.Model.from_weights(shape, si.make_weights(shape, seed))
+        self.gpu = bd.FastAR(shape, bd.device_weights(shape, si.make_weights(shape, seed)), max_batch=1)
+
+
+def test_full_frame_tiny(slow_tiny):
+    fast = FastPair(si.TINY, si.WORKLOADS["tiny"].seed(0))
+    w = ssi.SLOW_WORKLOADS["slow_tiny"]
+    inp = ssi.make_step_inputs(w, 4)
+    exact, fragile = _full_frames(slow_tiny, fast, 4, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
+                                  inp["codes"][0], 0.8, 0.8)
+    assert exact >= 10 and fragile <= 1
+
+
+def test_full_frame_ragged(slow_ragged):
+    fast = FastPair(si.RAGGED, si.WORKLOADS["ragged"].seed(0))
+    w = ssi.SLOW_WORKLOADS["slow_ragged"]
+    inp = ssi.make_step_inputs(w, 3)
+    exact, fragile = _full_frames(slow_ragged, fast, 3, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
+                                  inp["codes"][0], 0.9, 0.85)
+    assert exact >= 10 and fragile <= 1
+
+
+@pytest.mark.timeout(600)
+def test_slow_step_s2pro_full_size():
+    """The measured shape: 36 layers, 2048 cached positions (N(0,1) bf16),
+    vocabulary 155776; one step at position 2048 against the full oracle
+    step (positions past 2048 hold NaN)."""
+    w = ssi.SLOW_WORKLOADS["full_s2pro"]
+    s = w.shape
+    _announce("slow s2pro weights (7.3 GB bf16)")
+    p = SlowPair(s, w.seed(0))
+    inp = ssi.make_step_inputs(w, 1)
+    _check_step(p, w.n_fill, inp["main"][0], inp["codes"][0], [], inp["u_slow"][0], seed=w.seed(5))
+    p.gpu.close()
