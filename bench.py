@@ -11,7 +11,9 @@ the timed region; HIP events on the launch stream bracket exactly K frames.
 
 Prints one JSON line: frames/s, per-frame time, the decoder kernel's
 achieved algorithmic HBM bandwidth against the 8 TB/s peak, the float32
-oracle timed on this host's cores on a few frames, and a batch 16/64 sweep.
+oracle timed on this host's cores on a few frames, a batch 16/64 sweep, and
+the full frame (Slow-AR step from 2048 cached positions, then the Fast-AR
+frame) with the Slow-AR kernel's own bandwidth.
 """
 from __future__ import annotations
 
@@ -50,6 +52,96 @@ def algorithmic_bytes_per_frame(shape, batch: int, qkv0_table: bool) -> int:
         per_frame += s.dim * s.in_dim * wb
     io = batch * (s.in_dim * 4 + 4 + s.n_steps * 4 + 3 * 4 + s.num_codebooks * 4)
     return per_frame + io
+
+
+def slow_step_bytes(shape, n_past: int) -> int:
+    """Bytes one Slow-AR step must move at minimum at position n_past: every
+    layer matrix and norm vector once, the input rows (one embedding row and
+    one codebook row per codebook), the cache keys/values of positions
+    0..n_past-1 read and the new position's written, and the head rows the
+    mask leaves open (semantic ids and the end id) plus the final norm."""
+    s = shape
+    wb = 2 if s.weight_dtype == "bf16" else 4
+    per_layer = (s.qkv_dim * s.dim + s.dim * s.attn_dim + 3 * s.ffn_dim * s.dim + 2 * s.dim
+                 + (2 * s.head_dim if s.has_qk_norm else 0)) * wb
+    kv_pos = s.n_head_kv * 2 * s.head_dim * wb
+    kv = s.n_layer * (n_past + 1) * kv_pos
+    n_allowed = s.codebook_size + (0 if s.sem_begin <= s.end_id <= s.sem_end else 1)
+    head = (n_allowed + 1) * s.dim * wb
+    inputs = (1 + s.num_codebooks) * s.dim * wb
+    return s.n_layer * per_layer + kv + head + inputs + s.dim * 4
+
+
+def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int):
+    """The full frame (one Slow-AR step, then the Fast-AR frame) at batch 1,
+    chained on the device for `frames` frames from 2048 cached positions;
+    then the Slow-AR step alone with per-call events for its kernel time."""
+    from synth import slow_inputs as ssi
+    w = ssi.SLOW_WORKLOADS["full_s2pro"]
+    s = w.shape
+    frames = max(1, min(frames, s.max_ctx - w.n_fill))
+    print(f"[bench] generating {w.name} Slow-AR weights", file=sys.stderr, flush=True)
+    host = ssi.make_weights(s, w.seed(0), threads=16)
+    dev = bd.device_weights(s, host)
+    del host
+    kvh = ssi.make_kv_cache(s, w.n_fill, w.seed(5))
+    kv = torch.from_numpy(kvh.view(np.int16)).view(torch.bfloat16).cuda()
+    del kvh
+    slow = bd.SlowAR(s, dev)
+    inp = ssi.make_step_inputs(w, frames)
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
+    u_slow, u_fast = t(inp["u_slow"], torch.float32), t(inp["u_fast"], torch.float32)
+    temp, tp, tk = t([inp["temperature"]], torch.float32), t([inp["top_p"]], torch.float32), t([inp["top_k"]], torch.int32)
+    main = t(inp["main"][:1], torch.int32)
+    codes = t(inp["codes"][0], torch.int32)
+    window = torch.zeros(1 + bd.RAS_WINDOW, dtype=torch.int32, device="cuda")
+    hidden = torch.empty(s.dim, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(f, pos):
+        slow.full_frame(fast_ctx, kv, pos, main, codes, window, u_slow[f], u_fast[f], temp, tp, tk,
+                        main_out=main, hidden_out=hidden, codes_out=codes, stream=stream)
+
+    for i in range(warmup):
+        run(i % frames, w.n_fill + i)
+    torch.cuda.synchronize()
+    window.zero_()
+    print(f"[bench] timing {frames} full frames", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for f in range(frames):
+        run(f, w.n_fill + f)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3
+    # the Slow-AR kernel alone, each call between its own events
+    n_slow = min(frames, 64)
+    sem = torch.empty(1, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_slow)]
+    for f in range(n_slow):
+        ev[f][0].record(stream)
+        slow.step(kv, w.n_fill + f, main, codes, window, u_slow[f], temp, tp, tk, main_out=main, sem_out=sem,
+                  hidden_out=hidden, stream=stream)
+        ev[f][1].record(stream)
+    torch.cuda.synchronize()
+    slow_s = sum(a.elapsed_time(b) for a, b in ev) / 1e3 / n_slow
+    slow_b = sum(slow_step_bytes(s, w.n_fill + f) for f in range(n_slow)) / n_slow
+    fast_b = algorithmic_bytes_per_frame(fast_shape, 1, True)
+    frame_b = sum(slow_step_bytes(s, w.n_fill + f) for f in range(frames)) / frames + fast_b
+    out = {"workload": "S2 Pro-shaped full frame: 36-layer Slow-AR step (2048 cached positions, bf16 cache, "
+                       "tied head masked to 4096 semantic ids + end id, repetition window 10) then the "
+                       "9-codebook Fast-AR frame, batch 1, frames chained on the device",
+           "frames": frames, "frames_per_s": round(frames / sec, 2), "ms_per_frame": round(sec * 1e3 / frames, 3),
+           "frame_bytes": int(frame_b), "frame_hbm_gbs": round(frame_b * frames / sec / 1e9, 1),
+           "frame_frac": round(frame_b * frames / sec / 1e9 / PEAK_HBM_GBS, 4),
+           "slow_kernel": {"kernel": "slow_kernel<bf16>", "avg_launch_us": round(slow_s * 1e6, 2),
+                           "bytes_per_launch": int(slow_b), "achieved_gbs": round(slow_b / slow_s / 1e9, 1),
+                           "frac": round(slow_b / slow_s / 1e9 / PEAK_HBM_GBS, 4), "syncs": slow.syncs(),
+                           "launches": n_slow}}
+    slow.close()
+    del dev, kv
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_frames(torch, ctx, dev_in, B, frames, warmup):
@@ -148,6 +240,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch 16/64 lines")
     ap.add_argument("--cpu-frames", type=int, default=96)
+    ap.add_argument("--no-full-frame", action="store_true", help="skip the full-frame (Slow-AR + Fast-AR) line")
+    ap.add_argument("--full-frames", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decoder runs on a single MI355X; "
@@ -238,6 +332,8 @@ def main():
                 del ds
             torch.cuda.empty_cache()
         result["batch_sweep"] = sweep
+    if not args.no_full_frame:
+        result["full_frame"] = full_frame_bench(torch, bd, ctx, shape, args.full_frames, 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_frames, host)
