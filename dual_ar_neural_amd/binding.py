@@ -110,6 +110,8 @@ def library() -> ctypes.CDLL:
         lib.s2fast_slow_syncs.restype = ctypes.c_int
         lib.s2fast_slow_allowed.argtypes = [P]
         lib.s2fast_slow_allowed.restype = ctypes.c_int
+        lib.s2fast_test_slow_timeline.argtypes = [P, I, P, I]
+        lib.s2fast_test_slow_timeline.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -117,7 +119,8 @@ def library() -> ctypes.CDLL:
 EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_frame",
            "s2fast_forward_logits", "s2fast_test_rope_table", "s2fast_test_sample",
            "s2fast_syncs_per_frame", "s2fast_test_timeline", "s2fast_slow_create", "s2fast_slow_destroy",
-           "s2fast_slow_step", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed")
+           "s2fast_slow_step", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed",
+           "s2fast_test_slow_timeline")
 
 
 def _strerror(code: int) -> str:
@@ -309,6 +312,17 @@ class SlowAR:
 
     def syncs(self) -> int:
         return library().s2fast_slow_syncs(self._ctx)
+
+    def timeline(self, enable: bool = True, fetch: bool = False):
+        """Per-block phase timing of later steps (see FastAR.timeline)."""
+        import numpy as np
+        out = None
+        if fetch:
+            nb = torch.cuda.get_device_properties(0).multi_processor_count
+            out = np.zeros((nb, 256, 8), np.uint32)
+        _check(library().s2fast_test_slow_timeline(self._ctx, int(enable), None if out is None else out.ctypes.data,
+                                                   0 if out is None else out.size), "s2fast_test_slow_timeline")
+        return out
 
     def kv_dtype(self):
         return torch.bfloat16 if self.shape.weight_dtype == "bf16" else torch.float32

@@ -1789,6 +1789,8 @@ struct s2fast_slow_ctx {
   int* sem = nullptr;          // the full frame's semantic code, handed to Fast-AR
   u32* flags = nullptr;
   u32* err = nullptr;
+  u32* tlog = nullptr;     // allocated on first s2fast_test_slow_timeline call
+  bool tlog_on = false;
   u32 epoch = 0;
 };
 
@@ -1797,7 +1799,7 @@ namespace {
 void free_slow(s2fast_slow_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->layers, c->rope, c->x0, c->x, c->qkv, c->acc, c->g, c->po, c->pml, c->logits, c->sem,
-                  c->flags, c->err};
+                  c->flags, c->err, c->tlog};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete c;
@@ -1964,7 +1966,7 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
   a.pml = ctx->pml; a.logits = ctx->logits;
   a.x_slot = ctx->x_slot; a.qkv_slot = ctx->qkv_slot; a.acc_slot = ctx->acc_slot; a.g_slot = ctx->g_slot;
   a.po_slot = ctx->po_slot; a.pml_slot = ctx->pml_slot;
-  a.flags = ctx->flags; a.err = ctx->err; a.tlog = nullptr;
+  a.flags = ctx->flags; a.err = ctx->err; a.tlog = ctx->tlog_on ? ctx->tlog : nullptr;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (ctx->epoch > 0xF0000000u) {
     if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
@@ -1976,6 +1978,22 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
                                  ctx->lds_bytes, st) != hipSuccess)
     return S2FAST_ERR_HIP;
   ctx->epoch += (u32)s2fast_slow_syncs(ctx);
+  return S2FAST_OK;
+}
+
+int s2fast_test_slow_timeline(s2fast_slow_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  const size_t n = (size_t)ctx->ncu * TLOG_MAX * TLOG_W;
+  if (!ctx->tlog) {
+    if (hipMalloc(reinterpret_cast<void**>(&ctx->tlog), n * sizeof(u32)) != hipSuccess) return S2FAST_ERR_NOMEM;
+    if (hipMemset(ctx->tlog, 0, n * sizeof(u32)) != hipSuccess) return S2FAST_ERR_HIP;
+  }
+  ctx->tlog_on = enable != 0;
+  if (host_out) {
+    if (capacity < (int64_t)n) return S2FAST_ERR_ARG;
+    if (hipDeviceSynchronize() != hipSuccess) return S2FAST_ERR_HIP;
+    if (hipMemcpy(host_out, ctx->tlog, n * sizeof(u32), hipMemcpyDeviceToHost) != hipSuccess) return S2FAST_ERR_HIP;
+  }
   return S2FAST_OK;
 }
 

@@ -36,7 +36,6 @@ constexpr int SLOW_MAX_LAYERS = S2FAST_SLOW_MAX_LAYERS;
 constexpr int RAS_WIN = 10;     // repetition window (main-loop page, section 6)
 constexpr int SPPW = 12;        // attention positions per wave per load batch
 constexpr int GH_MAX = 8;       // query heads per KV group
-constexpr int CMB = 32;         // chunk partials loaded per batch in the merge
 
 struct SlowArgs {
   int dim, n_layer, n_head, n_kv, hd, ffn, vocab, ncb, cbs;
@@ -87,6 +86,8 @@ struct SlowLds {
   float* q;      // [gheads + 2][hd]: the group's query heads, then the new key and value
   float* qkn;    // [2][hd] q_norm, k_norm
   float* ow;     // [NWAVE][gheads][hd + 2] per-wave attention partials
+  float* mrg;    // [NTHREADS][6] chunk-merge partials (max, sum, 4 outputs)
+  float* rope1;  // [hd]: cos then sin at position n_past
   float* cval;
   int* cidx;
   u32* mark;
@@ -97,7 +98,7 @@ struct SlowLds {
 __host__ __device__ inline size_t slow_lds_floats(int kmax, int rmax, int gheads, int hd) {
   const size_t act = ((size_t)kmax + 3) & ~(size_t)3;
   return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)(gheads + 2) * hd + 2 * (size_t)hd +
-         (size_t)NWAVE * gheads * (hd + 2) + 2 * TOPK_MAX + 256 + 4 + 32;
+         (size_t)NWAVE * gheads * (hd + 2) + 6 * (size_t)NTHREADS + (size_t)hd + 2 * TOPK_MAX + 256 + 4 + 32;
 }
 
 __device__ inline SlowLds slow_carve(float* base, const SlowArgs& a) {
@@ -109,6 +110,8 @@ __device__ inline SlowLds slow_carve(float* base, const SlowArgs& a) {
   s.q = p; p += (size_t)(a.gheads + 2) * a.hd;
   s.qkn = p; p += 2 * (size_t)a.hd;
   s.ow = p; p += (size_t)NWAVE * a.gheads * (a.hd + 2);
+  s.mrg = p; p += 6 * (size_t)NTHREADS;
+  s.rope1 = p; p += a.hd;
   s.cval = p; p += TOPK_MAX;
   s.cidx = reinterpret_cast<int*>(p); p += TOPK_MAX;
   s.mark = reinterpret_cast<u32*>(p); p += 256;
@@ -300,43 +303,25 @@ __device__ __forceinline__ void slow_qkv(const SlowArgs& a, const SlowLds& s, in
   else slow_stage<WT, 1>(a, s, l, nw, pro);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
+  mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
+  mark(a, s.flag[1], 3);
   const float den = norm_den(s.small, 0, a.dim, a.eps);
   float* out = a.qkv + (size_t)l * a.qkv_slot;
   for (int r = tidx(); r < r1 - r0; r += NTHREADS) st_coh(out + r0 + r, red_sum(s.red, r, 0) / den);
 }
 
+// Attention of one block over positions [p0, p1) of its KV group, any
+// head_dim / cache type: lane pairs of head dims, one wave reduction per
+// (position, head).  Leaves each wave's (output, max, sum) per head in s.ow.
 template <typename WT>
-__device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, int l) {
+__device__ __forceinline__ void attn_lanes(const SlowArgs& a, const SlowLds& s, const WT* kvg, int p0, int p1) {
   using KV = KVElem<WT>;
-  const int G = a.n_kv, gh = a.gheads, hd = a.hd, H = a.n_head;
-  const int g = blockIdx.x % G, c = blockIdx.x / G;
-  if (c >= a.nchunk) return;
+  const int gh = a.gheads, hd = a.hd;
   const int wave = tidx() >> 6, lane = tidx() & 63;
-  const int N = a.n_past + 1;
-  const int p0 = (int)(((long long)N * c) / a.nchunk), p1 = (int)(((long long)N * (c + 1)) / a.nchunk);
-  const float* qkv = a.qkv + (size_t)l * a.qkv_slot;
-  // the group's query heads, then the new key and value, and the q/k norm weights
-  for (int i = tidx(); i < (gh + 2) * hd; i += NTHREADS) {
-    const int v = i / hd, d = i - v * hd;
-    const int src = v < gh ? (g * gh + v) * hd : (v == gh ? (H + g) * hd : (H + G + g) * hd);
-    s.q[i] = qkv[src + d];
-  }
-  if (a.has_qkn)
-    for (int i = tidx(); i < 2 * hd; i += NTHREADS)
-      s.qkn[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(i < hd ? a.L[l].q_norm : a.L[l].k_norm), i % hd);
-  __syncthreads();
-  for (int v = wave; v < gh + 1; v += NWAVE)
-    head_norm_rope(s.q + (size_t)v * hd, hd, v < gh ? s.qkn : s.qkn + hd, a.has_qkn, a.eps, a.rope, a.max_ctx,
-                   a.n_past);
-  __syncthreads();
-  float* kn = s.q + (size_t)gh * hd;
-  float* vn = kn + hd;
-  for (int d = tidx(); d < 2 * hd; d += NTHREADS) kn[d] = KV::round(kn[d]);   // the cache's precision
-  __syncthreads();
-
-  const WT* kvg = reinterpret_cast<const WT*>(a.kv) + (size_t)(l * G + g) * a.max_ctx * 2 * hd;
+  const float* kn = s.q + (size_t)gh * hd;
+  const float* vn = kn + hd;
   const bool own = 2 * lane < hd;
   const int lp = own ? lane : 0;
   float qx[GH_MAX][2], m[GH_MAX], ls[GH_MAX], o0[GH_MAX], o1[GH_MAX];
@@ -402,7 +387,7 @@ __device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, i
       o1[hh] = a1;
     }
   }
-  // per-wave partials, then the block's partial per head
+  // per-wave partials
   const int ws = hd + 2;
 #pragma unroll
   for (int hh = 0; hh < GH_MAX; ++hh) {
@@ -411,6 +396,147 @@ __device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, i
     if (own) { w[2 * lane] = o0[hh]; w[2 * lane + 1] = o1[hh]; }
     if (lane == 0) { w[hd] = m[hh]; w[hd + 1] = ls[hh]; }
   }
+}
+
+// The measured shape's attention: bf16 cache, head_dim 128, four query heads
+// per KV group.  A 256-byte key (or value) row is 16 lanes x 16 bytes, so one
+// wave load instruction covers four positions; a score is one 16-lane row
+// reduction.  Each lane keeps the online-softmax state of its row's
+// positions for its 8 head dims; the four rows of a wave are added at the
+// end.  Leaves each wave's (output, max, sum) per head in s.ow.
+template <typename WT>
+__device__ __forceinline__ void attn_rows16(const SlowArgs& a, const SlowLds& s, const WT* kvg, int p0, int p1) {
+  constexpr int NI = 3;      // load instructions (4 positions each) per wave per batch
+  constexpr int GH = 4, HD = 128;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int r = lane >> 4, sg = lane & 15;     // position row of the instruction, dims 8sg..8sg+7
+  const float* kn = s.q + GH * HD;
+  const float* vn = kn + HD;
+  float qv[GH][8], m[GH], ls[GH], o[GH][8];
+#pragma unroll
+  for (int hh = 0; hh < GH; ++hh) {
+    const float4 q0 = *reinterpret_cast<const float4*>(s.q + hh * HD + 8 * sg);
+    const float4 q1 = *reinterpret_cast<const float4*>(s.q + hh * HD + 8 * sg + 4);
+    qv[hh][0] = q0.x; qv[hh][1] = q0.y; qv[hh][2] = q0.z; qv[hh][3] = q0.w;
+    qv[hh][4] = q1.x; qv[hh][5] = q1.y; qv[hh][6] = q1.z; qv[hh][7] = q1.w;
+    m[hh] = -INFINITY;
+    ls[hh] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[hh][k] = 0.0f;
+  }
+  const float scale = 1.0f / sqrtf((float)HD);
+  for (int b0 = p0; b0 < p1; b0 += NWAVE * NI * 4) {
+    u32x4 kr[NI], vr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int j = b0 + (i * NWAVE + wave) * 4 + r;
+      const int jc = j < p1 ? j : p0;     // past the chunk: re-read its first row (in bounds)
+      const WT* row = kvg + (size_t)jc * 2 * HD + 8 * sg;
+      kr[i] = *reinterpret_cast<const u32x4*>(row);
+      vr[i] = *reinterpret_cast<const u32x4*>(row + HD);
+    }
+    float kx[NI][8], vx[NI][8], sc[NI][GH];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      // the new position from LDS; positions past the chunk read as zeros
+      const int j = b0 + (i * NWAVE + wave) * 4 + r;
+      const bool nw = j == a.n_past, live = j < p1;
+      float kf[8], vf[8];
+      WTraits<WT>::unpack(make_uint4(kr[i].x, kr[i].y, kr[i].z, kr[i].w), kf);
+      WTraits<WT>::unpack(make_uint4(vr[i].x, vr[i].y, vr[i].z, vr[i].w), vf);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        kx[i][k] = nw ? kn[8 * sg + k] : (live ? kf[k] : 0.0f);
+        vx[i][k] = nw ? vn[8 * sg + k] : (live ? vf[k] : 0.0f);
+      }
+#pragma unroll
+      for (int hh = 0; hh < GH; ++hh) {
+        float part = qv[hh][0] * kx[i][0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) part = fmaf(qv[hh][k], kx[i][k], part);
+        part = row16_sum(part);
+        sc[i][hh] = live ? part * scale : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh) {
+      float mb = sc[0][hh];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mb = fmaxf(mb, sc[i][hh]);
+      mb = fmaxf(fmaxf(readlane_f(mb, 0), readlane_f(mb, 16)), fmaxf(readlane_f(mb, 32), readlane_f(mb, 48)));
+      const float mn = fmaxf(m[hh], mb);
+      if (mn == -INFINITY) continue;
+      const float rs = expf(m[hh] - mn);   // 0 while m is -inf
+      ls[hh] *= rs;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[hh][k] *= rs;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float e = expf(sc[i][hh] - mn);   // 0 past the chunk
+        ls[hh] += e;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[hh][k] = fmaf(e, vx[i][k], o[hh][k]);
+      }
+      m[hh] = mn;
+    }
+  }
+  // add the four position rows of the wave
+#pragma unroll
+  for (int hh = 0; hh < GH; ++hh) {
+    ls[hh] += xor_lane_f<16>(ls[hh], lane);
+    ls[hh] += xor_lane_f<32>(ls[hh], lane);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o[hh][k] += xor_lane_f<16>(o[hh][k], lane);
+      o[hh][k] += xor_lane_f<32>(o[hh][k], lane);
+    }
+  }
+  const int ws = HD + 2;
+  if (r == 0) {
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh) {
+      float* w = s.ow + ((size_t)wave * GH + hh) * ws;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[8 * sg + k] = o[hh][k];
+      if (sg == 0) { w[HD] = m[hh]; w[HD + 1] = ls[hh]; }
+    }
+  }
+}
+
+template <typename WT>
+__device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, int l) {
+  using KV = KVElem<WT>;
+  const int G = a.n_kv, gh = a.gheads, hd = a.hd, H = a.n_head;
+  const int g = blockIdx.x % G, c = blockIdx.x / G;
+  if (c >= a.nchunk) return;
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const int N = a.n_past + 1;
+  const int p0 = (int)(((long long)N * c) / a.nchunk), p1 = (int)(((long long)N * (c + 1)) / a.nchunk);
+  const float* qkv = a.qkv + (size_t)l * a.qkv_slot;
+  // the group's query heads, then the new key and value, and the q/k norm weights
+  for (int i = tidx(); i < (gh + 2) * hd; i += NTHREADS) {
+    const int v = i / hd, d = i - v * hd;
+    const int src = v < gh ? (g * gh + v) * hd : (v == gh ? (H + g) * hd : (H + G + g) * hd);
+    s.q[i] = qkv[src + d];
+  }
+  if (a.has_qkn)
+    for (int i = tidx(); i < 2 * hd; i += NTHREADS)
+      s.qkn[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(i < hd ? a.L[l].q_norm : a.L[l].k_norm), i % hd);
+  __syncthreads();
+  for (int v = wave; v < gh + 1; v += NWAVE)
+    head_norm_rope(s.q + (size_t)v * hd, hd, v < gh ? s.qkn : s.qkn + hd, a.has_qkn, a.eps, s.rope1, 1, 0);
+  __syncthreads();
+  mark(a, s.flag[1], 6);
+  float* kn = s.q + (size_t)gh * hd;
+  float* vn = kn + hd;
+  for (int d = tidx(); d < 2 * hd; d += NTHREADS) kn[d] = KV::round(kn[d]);   // the cache's precision
+  __syncthreads();
+
+  const WT* kvg = reinterpret_cast<const WT*>(a.kv) + (size_t)(l * G + g) * a.max_ctx * 2 * hd;
+  const int ws = hd + 2;
+  if (sizeof(WT) == 2 && hd == 128 && gh == 4) attn_rows16<WT>(a, s, kvg, p0, p1);
+  else attn_lanes<WT>(a, s, kvg, p0, p1);
+  mark(a, s.flag[1], 7);
   __syncthreads();
   float* po = a.po + (size_t)l * a.po_slot + ((size_t)g * a.nchunk + c) * gh * hd;
   float* pml = a.pml + (size_t)l * a.pml_slot + ((size_t)g * a.nchunk + c) * gh * 2;
@@ -448,48 +574,84 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
   u32x4 slot[RING];
   const float* pml = a.pml + (size_t)l * a.pml_slot + (size_t)g * nc * gh * 2;
   const float* po = a.po + (size_t)l * a.po_slot + (size_t)g * nc * gh * hd;
-  // merge the chunk partials of every head of the group: thread t takes
-  // element t of the group's output (head t / hd, dim t % hd)
-  const int iters = (n + NTHREADS - 1) / NTHREADS;
+  // Merge the chunk partials of every head of the group (log-sum-exp
+  // weights).  A thread takes 4 consecutive output elements (one 16-byte
+  // load per chunk) of the chunks cs, cs + S, ...; the S subsets of a quad
+  // then meet in LDS.
+  const int nq = n >> 2;                          // hd % 8 == 0
+  const int S = max(1, NTHREADS / nq);
+  const int iters = S > 1 ? 1 : (nq + NTHREADS - 1) / NTHREADS;
+  constexpr int CB = 8;
   for (int it = 0; it < iters; ++it) {
-    const int t = it * NTHREADS + tidx();
-    const int tt = min(t, n - 1);
-    const int hh = tt / hd;
-    float M = -INFINITY, Ls = 0.0f, O = 0.0f;
-    for (int c0 = 0; c0 < nc; c0 += CMB) {
-      u64 ml[CMB];
-      float ov[CMB];
+    const int t = tidx();
+    const int q = S > 1 ? t % nq : it * NTHREADS + t;
+    const int cs = S > 1 ? t / nq : 0;
+    const bool live = S > 1 ? cs < S : q < nq;
+    const int qq = min(q, nq - 1), hh = (4 * qq) / hd;
+    float M = -INFINITY, Ls = 0.0f;
+    v4f O = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = cs; c0 < nc + S * CB; c0 += S * CB) {
+      if (c0 >= nc && !(it == 0 && c0 == cs)) break;
+      u64 ml[CB];
+      v4f ov[CB];
 #pragma unroll
-      for (int j = 0; j < CMB; ++j) {
-        const int cc = min(c0 + j, nc - 1);
+      for (int j = 0; j < CB; ++j) {
+        const int cc = min(c0 + j * S, nc - 1);
         ml[j] = ld64(pml + ((size_t)cc * gh + hh) * 2);
-        ov[j] = po[(size_t)cc * n + tt];
+        ov[j] = *reinterpret_cast<const v4f*>(po + (size_t)cc * n + 4 * qq);
       }
-      if (it == 0 && c0 == 0) gemv_prologue(pl, slot);
+      if (it == 0 && c0 == cs) gemv_prologue(pl, slot);
       float mb = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < CMB; ++j)
-        if (c0 + j < nc) mb = fmaxf(mb, lo_f32(ml[j]));
+      for (int j = 0; j < CB; ++j)
+        if (c0 + j * S < nc) mb = fmaxf(mb, lo_f32(ml[j]));
       const float mn = fmaxf(M, mb);
       if (mn == -INFINITY) continue;
-      const float r = expf(M - mn);
-      Ls *= r;
-      O *= r;
+      const float rs = expf(M - mn);
+      Ls *= rs;
+      O *= rs;
 #pragma unroll
-      for (int j = 0; j < CMB; ++j) {
-        if (c0 + j < nc) {
+      for (int j = 0; j < CB; ++j) {
+        if (c0 + j * S < nc) {
           const float f = expf(lo_f32(ml[j]) - mn);   // 0 for an empty chunk
           Ls = fmaf(f, hi_f32(ml[j]), Ls);
-          O = fmaf(f, ov[j], O);
+          O += f * ov[j];
         }
       }
       M = mn;
     }
-    if (t < n) s.act[phys<WT>(t, a.gw)] = O / Ls;
+    if (S > 1) {
+      if (live) {
+        float* w = s.mrg + (size_t)t * 6;
+        w[0] = M; w[1] = Ls; w[2] = O[0]; w[3] = O[1]; w[4] = O[2]; w[5] = O[3];
+      }
+    } else if (live) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s.act[phys<WT>(4 * qq + e, a.gw)] = O[e] / Ls;
+    }
+  }
+  if (S > 1) {
+    __syncthreads();
+    for (int q = tidx(); q < nq; q += NTHREADS) {
+      float M = -INFINITY;
+      for (int j = 0; j < S; ++j) M = fmaxf(M, s.mrg[(size_t)(j * nq + q) * 6]);
+      float Ls = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < S; ++j) {
+        const float* w = s.mrg + (size_t)(j * nq + q) * 6;
+        const float f = expf(w[0] - M);              // 0 for a subset without positions
+        Ls = fmaf(f, w[1], Ls);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] = fmaf(f, w[2 + e], O[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s.act[phys<WT>(4 * q + e, a.gw)] = O[e] / Ls;
+    }
   }
   __syncthreads();
+  mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
+  mark(a, s.flag[1], 3);
   long long* acc = a.acc + (size_t)l * a.acc_slot;
   for (int r = tidx(); r < r1 - r0; r += NTHREADS) atomic_add_coh(acc + r0 + r, to_fx(red_sum(s.red, r, 0)));
 }
@@ -502,8 +664,10 @@ __device__ __forceinline__ void slow_up(const SlowArgs& a, const SlowLds& s, int
   slow_stage<WT, 2>(a, s, l, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
   zero_lds(s.red, 2 * nr * NWAVE * MMAX);
   __syncthreads();
+  mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);   // rows [0, nr): w1, [nr, 2nr): w3
   __syncthreads();
+  mark(a, s.flag[1], 3);
   const float den = norm_den(s.small, 0, a.dim, a.eps);
   float* out = a.g + (size_t)l * a.g_slot;
   for (int r = tidx(); r < nr; r += NTHREADS)
@@ -518,8 +682,10 @@ __device__ __forceinline__ void slow_down(const SlowArgs& a, const SlowLds& s, i
   stage_arena<WT, true, 5>(s.act, a.g + (size_t)l * a.g_slot, a.ffn, pro);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
+  mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
+  mark(a, s.flag[1], 3);
   const float* xin = slow_lin(a, l);
   float* xo = a.x + (size_t)l * a.x_slot;
   long long* acc = a.acc + (size_t)l * a.acc_slot;
@@ -541,8 +707,10 @@ __device__ __forceinline__ void slow_head(const SlowArgs& a, const SlowLds& s, P
   slow_stage<WT, 1>(a, s, a.n_layer, reinterpret_cast<const WT*>(a.norm), pro);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
+  mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
+  mark(a, s.flag[1], 3);
   const float den = norm_den(s.small, 0, a.dim, a.eps);
   for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
     const float v = red_sum(s.red, r, 0) / den;
@@ -601,12 +769,21 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs a) {
     const int t = tidx();
     s.tok[t] = t == 0 ? min(max(a.prev_main[0], 0), a.vocab - 1) : min(max(a.prev_codes[t - 1], 0), a.cbs - 1);
   }
+  // cos and sin of position n_past (the same for every layer)
+  for (int i = tidx(); i < a.hd; i += NTHREADS) {
+    const int h2 = a.hd >> 1, half = i >= h2 ? 1 : 0;
+    s.rope1[i] = a.rope[((size_t)half * a.max_ctx + a.n_past) * h2 + (i - half * h2)];
+  }
   __syncthreads();
   const int nph = 5 * a.n_layer + 1;
+  // A phase's plan (plain integers) is computed before the barrier that
+  // precedes the phase.
+  Plan pl = slow_plan<WT>(a, 0, SP_QKV);
   for (int ph = 0; ph < nph; ++ph) {
     const int l = ph / 5;
     const int kind = ph < 5 * a.n_layer ? ph - 5 * l : (int)SP_HEAD;
-    Plan pl = slow_plan<WT>(a, l, kind);
+    if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
+    mark(a, epoch - a.epoch0, 5);
     switch (kind) {
       case SP_QKV: slow_qkv<WT>(a, s, l, pl); break;
       case SP_ATTN: slow_attn<WT>(a, s, l); break;
@@ -614,6 +791,11 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs a) {
       case SP_UP: slow_up<WT>(a, s, l, pl); break;
       case SP_DOWN: slow_down<WT>(a, s, l, pl); break;
       default: slow_head<WT>(a, s, pl); break;
+    }
+    {
+      const int ln = (ph + 1) / 5;
+      const int kn = ph + 1 < 5 * a.n_layer ? ph + 1 - 5 * ln : (int)SP_HEAD;
+      pl = slow_plan<WT>(a, min(ln, a.n_layer - 1), kn);   // past the last phase: never used
     }
     if (!grid_sync(a, epoch, s.flag)) return;
   }

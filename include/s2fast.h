@@ -312,6 +312,10 @@ int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* t
  * out as [block][i][8].  The buffer is allocated on the first call. */
 int s2fast_test_timeline(s2fast_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity);
 
+/* The same instrumentation for Slow-AR step launches (sync point i < 256 of
+ * a step; in-phase words are 0). */
+int s2fast_test_slow_timeline(s2fast_slow_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity);
+
 /* Number of grid-wide synchronisation points one frame of B requests
  * takes on this context, or -1 on error (for measurement reports). */
 int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B);

@@ -73,6 +73,12 @@ SLOW_TINY = SlowShape("slow_tiny", dim=256, n_layer=2, n_head=4, n_head_kv=2, he
 SLOW_S2PRO = SlowShape("slow_s2pro", dim=2560, n_layer=36, n_head=32, n_head_kv=8, head_dim=128,
                        ffn_dim=9728, vocab=155776, codebook_size=4096, sem_begin=151678,
                        end_id=151645, max_ctx=2560)
+# the measured shape's head layout (bf16, head_dim 128, 4 query heads per KV
+# group) at small widths
+SLOW_MID = SlowShape("slow_mid", dim=512, n_layer=2, n_head=8, n_head_kv=2, head_dim=128, ffn_dim=1024,
+                     vocab=3000, codebook_size=512, sem_begin=2400, end_id=100, max_ctx=700)
+# the same with a cache too long for a chunk to be held in LDS
+SLOW_MID_LONG = replace(SLOW_MID, name="slow_mid_long", max_ctx=13000)
 # awkward sizes: nothing a multiple of the kernels' tiles, end id above the
 # semantic range, bf16 weights and cache
 SLOW_RAGGED = SlowShape("slow_ragged", dim=176, n_layer=3, n_head=6, n_head_kv=2, head_dim=40,
@@ -165,6 +171,8 @@ class SlowWorkload:
 SLOW_WORKLOADS: Dict[str, SlowWorkload] = {
     "full_s2pro": SlowWorkload(5, "full_s2pro", SLOW_S2PRO, n_fill=2048, frames=512),
     "slow_tiny": SlowWorkload(11, "slow_tiny", SLOW_TINY, n_fill=37, frames=4),
+    "slow_mid": SlowWorkload(13, "slow_mid", SLOW_MID, n_fill=333, frames=3),
+    "slow_mid_long": SlowWorkload(14, "slow_mid_long", SLOW_MID_LONG, n_fill=12345, frames=2),
     "slow_ragged": SlowWorkload(12, "slow_ragged", SLOW_RAGGED, n_fill=130, frames=3,
                                 temperature=0.9, top_p=0.85),
 }

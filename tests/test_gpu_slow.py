@@ -125,6 +125,32 @@ def test_slow_step_tiny(slow_tiny, n_past):
     _check_step(slow_tiny, n_past, inp["main"][0], inp["codes"][0], [], inp["u_slow"][0])
 
 
+@pytest.fixture(scope="module")
+def slow_mid():
+    _announce("slow mid model")
+    return SlowPair(ssi.SLOW_MID, ssi.SLOW_WORKLOADS["slow_mid"].seed(0))
+
+
+@pytest.mark.parametrize("n_past", [0, 3, 95, 96, 333, 699])
+def test_slow_step_mid(slow_mid, n_past):
+    """The measured shape's attention path (bf16, head_dim 128, 4 heads per
+    group) at chunk sizes from empty to a few positions."""
+    inp = ssi.make_step_inputs(ssi.SLOW_WORKLOADS["slow_mid"], 2)
+    win = [int(inp["main"][1])]
+    _check_step(slow_mid, n_past, inp["main"][0], inp["codes"][0], win, inp["u_slow"][0])
+
+
+@pytest.mark.parametrize("n_past", [97, 12345, 12999])
+def test_slow_step_mid_long_context(n_past):
+    """The same attention path over a long cache: chunks of up to 102
+    positions, more than one load batch per wave."""
+    w = ssi.SLOW_WORKLOADS["slow_mid_long"]
+    p = SlowPair(w.shape, ssi.SLOW_WORKLOADS["slow_mid"].seed(0))
+    inp = ssi.make_step_inputs(w, 1)
+    _check_step(p, n_past, inp["main"][0], inp["codes"][0], [], inp["u_slow"][0])
+    p.gpu.close()
+
+
 @pytest.mark.parametrize("n_past", [0, 5, 130, 299])
 def test_slow_step_ragged(slow_ragged, n_past):
     inp = ssi.make_step_inputs(ssi.SLOW_WORKLOADS["slow_ragged"], 2)
@@ -234,12 +260,15 @@ def test_full_frame_ragged(slow_ragged):
 @pytest.mark.timeout(600)
 def test_slow_step_s2pro_full_size():
     """The measured shape: 36 layers, 2048 cached positions (N(0,1) bf16),
-    vocabulary 155776; one step at position 2048 against the full oracle
-    step (positions past 2048 hold NaN)."""
+    vocabulary 155776; steps at positions 2048 and 2559 (the last) against
+    the full oracle step (positions past n_past hold NaN)."""
     w = ssi.SLOW_WORKLOADS["full_s2pro"]
     s = w.shape
     _announce("slow s2pro weights (7.3 GB bf16)")
     p = SlowPair(s, w.seed(0))
-    inp = ssi.make_step_inputs(w, 1)
+    inp = ssi.make_step_inputs(w, 2)
     _check_step(p, w.n_fill, inp["main"][0], inp["codes"][0], [], inp["u_slow"][0], seed=w.seed(5))
+    # the cache's last position (chunks of 80 positions)
+    _check_step(p, s.max_ctx - 1, inp["main"][1], inp["codes"][1], [int(inp["main"][0])], inp["u_slow"][1],
+                seed=w.seed(6))
     p.gpu.close()
