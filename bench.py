@@ -72,10 +72,54 @@ def slow_step_bytes(shape, n_past: int) -> int:
     return s.n_layer * per_layer + kv + head + inputs + s.dim * 4
 
 
-def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int):
+def slow_traffic():
+    """HBM bytes per Slow-AR launch from the committed counter summary, if it
+    was taken on the current kernel code (else None)."""
+    csrc = os.path.join(ROOT, "dual_ar_neural_amd", "csrc")
+    rec = traffic_from_profile(os.path.join(ROOT, "profiles", "slow_kernel_s2pro_full_frame_hbm_traffic.md"),
+                               [os.path.join(csrc, f) for f in ("s2fast.hip", "slow_step.h", "device_common.h",
+                                                                "sampler.h")])
+    return rec["hbm_bytes_per_launch"] if rec else None
+
+
+def full_frame_cpu(host_slow, kvh, fast_host, fast_shape, inp, n_fill, frames: int):
+    """The oracle's full frame (Slow-AR step over the cache, masked draw,
+    nine Fast-AR draws) on this host: `frames` chained frames after one
+    warm-up frame."""
+    from oracle import fast_ar as fa
+    from oracle import slow_ar as sa
+    from synth import inputs as si
+    from synth import slow_inputs as ssi
+    s = ssi.SLOW_WORKLOADS["full_s2pro"].shape
+    slow = sa.SlowModel.from_weights(s, host_slow)
+    fast = fa.Model.from_weights(fast_shape, fast_host)
+    kv = si.f32_from_bf16_bits(kvh)
+    main, codes, win = int(inp["main"][0]), inp["codes"][0], []
+    T, tp, tk = inp["temperature"], inp["top_p"], inp["top_k"]
+    t0 = 0.0
+    for f in range(frames + 1):
+        if f == 1:
+            t0 = time.perf_counter()
+        r = sa.decode_frame(slow, fast, kv, n_fill + f, main, codes, win, inp["u_slow"][f], inp["u_fast"][f],
+                            T, tp, tk)
+        kv[:, :, n_fill + f] = r.kv_new
+        main, codes, win = r.main.token, r.codes, r.window
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    threads = os.environ.get("OMP_NUM_THREADS")
+    if threads and threads.isdigit():
+        cores = min(cores, int(threads))
+    return {"value": round(frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
+            "sample": f"{frames} chained full frames from position {n_fill + 1} after one warm-up frame, "
+                      f"{dt:.1f} s wall clock"}
+
+
+def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, fast_host=None, cpu_frames=0):
     """The full frame (one Slow-AR step, then the Fast-AR frame) at batch 1,
     chained on the device for `frames` frames from 2048 cached positions;
-    then the Slow-AR step alone with per-call events for its kernel time."""
+    then the Slow-AR step alone with per-call events for its kernel time.
+    With fast_host and cpu_frames > 0, the oracle's full frame is timed on
+    the host afterwards."""
     from synth import slow_inputs as ssi
     w = ssi.SLOW_WORKLOADS["full_s2pro"]
     s = w.shape
@@ -83,10 +127,13 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int):
     print(f"[bench] generating {w.name} Slow-AR weights", file=sys.stderr, flush=True)
     host = ssi.make_weights(s, w.seed(0), threads=16)
     dev = bd.device_weights(s, host)
-    del host
+    keep_host = fast_host is not None and cpu_frames > 0
+    if not keep_host:
+        del host
     kvh = ssi.make_kv_cache(s, w.n_fill, w.seed(5))
     kv = torch.from_numpy(kvh.view(np.int16)).view(torch.bfloat16).cuda()
-    del kvh
+    if not keep_host:
+        del kvh
     slow = bd.SlowAR(s, dev)
     inp = ssi.make_step_inputs(w, frames)
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
@@ -135,12 +182,17 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int):
            "frame_bytes": int(frame_b), "frame_hbm_gbs": round(frame_b * frames / sec / 1e9, 1),
            "frame_frac": round(frame_b * frames / sec / 1e9 / PEAK_HBM_GBS, 4),
            "slow_kernel": {"kernel": "slow_kernel<bf16>", "avg_launch_us": round(slow_s * 1e6, 2),
+                           "traffic": slow_traffic(),
                            "bytes_per_launch": int(slow_b), "achieved_gbs": round(slow_b / slow_s / 1e9, 1),
                            "frac": round(slow_b / slow_s / 1e9 / PEAK_HBM_GBS, 4), "syncs": slow.syncs(),
                            "launches": n_slow}}
     slow.close()
     del dev, kv
     torch.cuda.empty_cache()
+    if keep_host:
+        print("[bench] timing the oracle's full frame on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = full_frame_cpu(host, kvh, fast_host, fast_shape, ssi.make_step_inputs(w, cpu_frames + 1),
+                                             w.n_fill, cpu_frames)
     return out
 
 
@@ -242,6 +294,7 @@ def main():
     ap.add_argument("--cpu-frames", type=int, default=96)
     ap.add_argument("--no-full-frame", action="store_true", help="skip the full-frame (Slow-AR + Fast-AR) line")
     ap.add_argument("--full-frames", type=int, default=512)
+    ap.add_argument("--cpu-full-frames", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decoder runs on a single MI355X; "
@@ -333,7 +386,8 @@ def main():
             torch.cuda.empty_cache()
         result["batch_sweep"] = sweep
     if not args.no_full_frame:
-        result["full_frame"] = full_frame_bench(torch, bd, ctx, shape, args.full_frames, 4)
+        result["full_frame"] = full_frame_bench(torch, bd, ctx, shape, args.full_frames, 4,
+                                                None if args.no_cpu_baseline else host, args.cpu_full_frames)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_frames, host)
