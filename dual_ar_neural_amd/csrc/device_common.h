@@ -62,6 +62,15 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((u32)b) << 16); }
 
+// A pointer known to address global memory.  Weight pointers that reach a
+// kernel through a table in device memory (rather than as kernel arguments)
+// would otherwise be accessed with flat instructions, which also count
+// against the LDS wait counter.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gbl(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+
 // 16 bytes of weights -> float values (8 bf16 or 4 f32)
 template <typename WT> struct WTraits;
 template <> struct WTraits<uint16_t> {
@@ -72,7 +81,7 @@ template <> struct WTraits<uint16_t> {
     f[4] = __uint_as_float(q.z << 16); f[5] = __uint_as_float(q.z & 0xFFFF0000u);
     f[6] = __uint_as_float(q.w << 16); f[7] = __uint_as_float(q.w & 0xFFFF0000u);
   }
-  __device__ __forceinline__ static float one(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static float one(const uint16_t* p, int i) { return bf16_to_f32(gbl(p)[i]); }
 };
 template <> struct WTraits<float> {
   static constexpr int EPL = 4;
@@ -80,7 +89,7 @@ template <> struct WTraits<float> {
     f[0] = __uint_as_float(q.x); f[1] = __uint_as_float(q.y);
     f[2] = __uint_as_float(q.z); f[3] = __uint_as_float(q.w);
   }
-  __device__ __forceinline__ static float one(const float* p, int i) { return p[i]; }
+  __device__ __forceinline__ static float one(const float* p, int i) { return gbl(p)[i]; }
 };
 
 // Weights are read exactly once per decode step and never reused inside it:

@@ -284,14 +284,14 @@ template <typename WT> struct WQuad;
 template <> struct WQuad<uint16_t> {
   using type = u64;
   __device__ static __forceinline__ type load(const uint16_t* w, int c) {
-    return *reinterpret_cast<const u64*>(w + 4 * c);
+    return *gbl(reinterpret_cast<const u64*>(w + 4 * c));
   }
   __device__ static __forceinline__ float get(type b, int e) { return __uint_as_float((u32)(b >> (16 * e)) << 16); }
 };
 template <> struct WQuad<float> {
   using type = v4f;
   __device__ static __forceinline__ type load(const float* w, int c) {
-    return *reinterpret_cast<const v4f*>(w + 4 * c);
+    return *gbl(reinterpret_cast<const v4f*>(w + 4 * c));
   }
   __device__ static __forceinline__ float get(type b, int e) { return b[e]; }
 };
@@ -434,7 +434,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int RING = GEMV_RING;
 
 __device__ __forceinline__ void load16_nt(u32x4& d, const void* p) {
-  d = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  d = __builtin_nontemporal_load(gbl(reinterpret_cast<const u32x4*>(p)));
 }
 
 struct Plan {
