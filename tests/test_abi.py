@@ -113,3 +113,80 @@ def test_null_arguments():
     assert lib.s2fast_test_sample(0, 10, None, None, None, None, None, None, None) == 1
     assert lib.s2fast_syncs_per_frame(None, 1) == -1
     lib.s2fast_destroy(None)
+
+
+# ---------------------------------------------------------------- Slow-AR
+
+def _fake_slow_weights(shape, with_layers=True):
+    """Distinct 256-byte-aligned fake device addresses (never dereferenced:
+    every case below is rejected before any device call)."""
+    from synth import slow_inputs as ssi  # noqa: F401
+    base = [0x7F0000000000]
+
+    def nxt():
+        base[0] += 1 << 20
+        return base[0]
+    w = bd.SlowWeights()
+    w.embeddings, w.codebook_embeddings, w.norm = nxt(), nxt(), nxt()
+    if with_layers:
+        for i in range(shape.n_layer):
+            for f in bd.LAYER_FIELDS:
+                setattr(w.layers[i], f, nxt())
+    return w
+
+
+def _slow_create(cfg, w):
+    ctx = ctypes.c_void_p()
+    rc = bd.library().s2fast_slow_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ctx))
+    return rc, ctx
+
+
+def test_slow_create_rejects_missing_weights():
+    from synth import slow_inputs as ssi
+    s = ssi.SLOW_S2PRO
+    cfg = bd.make_slow_config(s)
+    rc, ctx = _slow_create(cfg, _fake_slow_weights(s, with_layers=False))
+    assert rc == 2 and not ctx.value
+    w = _fake_slow_weights(s)
+    w.codebook_embeddings = None
+    assert _slow_create(cfg, w)[0] == 2
+    w = _fake_slow_weights(s)
+    w.layers[35].q_norm = None
+    assert _slow_create(cfg, w)[0] == 2
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_codebooks", 11), ("num_codebooks", 0), ("head_dim", 12), ("head_dim", 136), ("n_head_kv", 5),
+    ("n_head", 96), ("n_layer", 65), ("n_layer", 0), ("semantic_begin", 155000), ("semantic_begin", -1),
+    ("end_id", 155776), ("end_id", -3), ("max_context", 0), ("codebook_size", 8192), ("dim", 2564),
+    ("ffn_dim", 9730), ("weight_dtype", 3)])
+def test_slow_create_rejects_bad_shapes(field, value):
+    from synth import slow_inputs as ssi
+    s = ssi.SLOW_S2PRO
+    cfg = bd.make_slow_config(s)
+    setattr(cfg, field, value)
+    assert _slow_create(cfg, _fake_slow_weights(s))[0] == 1
+
+
+def test_slow_create_rejects_misaligned_weights():
+    from synth import slow_inputs as ssi
+    s = ssi.SLOW_S2PRO
+    cfg = bd.make_slow_config(s)
+    w = _fake_slow_weights(s)
+    w.layers[7].w2 = w.layers[7].w2 + 8
+    assert _slow_create(cfg, w)[0] == 1
+    w = _fake_slow_weights(s)
+    w.embeddings = w.embeddings + 4
+    assert _slow_create(cfg, w)[0] == 1
+
+
+def test_slow_null_arguments():
+    lib = bd.library()
+    assert lib.s2fast_slow_create(None, None, None) == 1
+    assert lib.s2fast_slow_step(None, None, 0, None, None, None, None, None, None, None, None, None, None, None,
+                                None) == 1
+    assert lib.s2fast_full_frame(None, None, None, 0, None, None, None, None, None, None, None, None, None, None,
+                                 None, None) == 1
+    assert lib.s2fast_slow_syncs(None) == -1 and lib.s2fast_slow_allowed(None) == -1
+    assert lib.s2fast_test_slow_timeline(None, 1, None, 0) == 1
+    lib.s2fast_slow_destroy(None)
