@@ -30,7 +30,14 @@ Readings of points the pages leave open (each also listed in the design doc):
     architecture page and the measured configuration write it (the engine
     page's remark that inference scales the codebook embeddings is not
     followed);
-  * a generated frame's position always carries codes (mask 1);
+  * a position's codebook terms count exactly when its row-0 token is a
+    semantic id (the mask of the prompt matrix: codes are present only in
+    reference-audio positions; every generated frame's main token is
+    semantic);
+  * prefill runs the prompt's positions through the same cached step one
+    at a time (the engine's CUDA path takes one token per chunk; any chunk
+    size gives the same result), and only the last position's logits feed
+    the first main-token draw;
   * the KV cache stores keys after q/k-norm and RoPE; new entries are
     rounded to the cache type (bf16 for bf16 models) before the attention
     reads them;
@@ -98,17 +105,23 @@ def cache_round(shape, x: np.ndarray) -> np.ndarray:
 # input, mask, head
 # --------------------------------------------------------------------------
 
+def is_semantic(shape, token) -> bool:
+    return shape.sem_begin <= int(token) <= shape.sem_end
+
+
 def combine(model: SlowModel, main_token: int, codes) -> np.ndarray:
-    """Input vector of one generated position [dim] (architecture page,
-    section 3.2)."""
+    """Input vector of one position [dim] (architecture page, section 3.2):
+    the row-0 token's embedding scaled by sem_scale, plus the codebook rows
+    when the position carries codes (its row-0 token is a semantic id)."""
     s = model.shape
     codes = np.asarray(codes, dtype=np.int64)
     assert codes.shape == (s.num_codebooks,)
     scale = F32(1.0 / np.sqrt(np.float64(s.num_codebooks + 1)))
     x = scale * model.row("embeddings", int(main_token))
-    rows = np.arange(s.num_codebooks) * s.codebook_size + codes
-    for r in rows:
-        x = x + model.row("codebook_embeddings", int(r))
+    if is_semantic(s, main_token):
+        rows = np.arange(s.num_codebooks) * s.codebook_size + codes
+        for r in rows:
+            x = x + model.row("codebook_embeddings", int(r))
     return x.astype(F32)
 
 
@@ -192,6 +205,23 @@ def step(model: SlowModel, x: np.ndarray, kv: np.ndarray, n_past: int) -> StepRe
     h = _fa.rms_norm(x, model.get("norm"), s.norm_eps).astype(F32)
     logits = _fa.linear(h, model.get("embeddings")).astype(F32)
     return StepResult(h, logits, kv_new)
+
+
+def prefill(model: SlowModel, tokens, kv: np.ndarray, n_past0: int):
+    """The prompt's positions n_past0 .. n_past0 + T - 1 (tokens [T, 1 +
+    num_codebooks]: row-0 token, then the codebook codes) through the cached
+    step in order; `kv` receives every new entry.  Returns the last
+    position's StepResult ("Overall architecture & Dual-AR data flow",
+    section 4: prefill in chunks, one token per chunk on CUDA; main-loop
+    page, section 5: the first main token is drawn from the prefill
+    logits)."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    st = None
+    for t in range(tokens.shape[0]):
+        x = combine(model, tokens[t, 0], tokens[t, 1:])
+        st = step(model, x, kv, n_past0 + t)
+        kv[:, :, n_past0 + t] = st.kv_new
+    return st
 
 
 # --------------------------------------------------------------------------

@@ -47,7 +47,7 @@ def test_combine_closed_form():
     m = sa.SlowModel(s, w)
     rng = np.random.default_rng(0)
     for _ in range(5):
-        main = int(rng.integers(0, s.vocab))
+        main = int(rng.integers(s.sem_begin, s.sem_end + 1))   # a position that carries codes
         codes = rng.integers(0, s.codebook_size, size=s.num_codebooks)
         x = sa.combine(m, main, codes)
         want = main / math.sqrt(11.0) + sum(j * s.codebook_size + int(c) for j, c in enumerate(codes))
@@ -214,3 +214,44 @@ def test_decode_frame_tiny(tiny):
     want = fa.decode_frame(fast, r.hidden[None], np.array([r.sem_code]), inp["u_fast"][:1],
                            np.array([0.8], F32), np.array([0.8], F32), np.array([30]))
     np.testing.assert_array_equal(r.codes, want.codes[0])
+
+
+def test_combine_text_position_has_no_codebook_terms():
+    """A row-0 token outside the semantic ids (text, markers, the end id)
+    takes its scaled embedding only."""
+    s = ssi.SLOW_TINY
+    w = {"embeddings": np.repeat(np.arange(s.vocab, dtype=F32)[:, None], s.dim, 1),
+         "codebook_embeddings": np.repeat(np.arange(s.num_codebooks * s.codebook_size, dtype=F32)[:, None], s.dim, 1)}
+    m = sa.SlowModel(s, w)
+    codes = np.arange(s.num_codebooks) + 5
+    for tok in (0, 17, s.sem_begin - 1, s.end_id, s.sem_end + 1, s.vocab - 1):
+        np.testing.assert_allclose(sa.combine(m, tok, codes), np.full(s.dim, tok / math.sqrt(11.0)), rtol=2e-7)
+    assert sa.is_semantic(s, s.sem_begin) and sa.is_semantic(s, s.sem_end)
+    assert not sa.is_semantic(s, s.end_id)
+
+
+def test_prefill_equals_full_causal_forward(tiny):
+    """Prefill of a mixed prompt (text tokens, then semantic positions with
+    codes) from an empty cache gives, at its last position, the final state
+    of one causal forward over the combined inputs."""
+    s = tiny.shape
+    rng = np.random.default_rng(8)
+    T = 7
+    toks = np.zeros((T, 1 + s.num_codebooks), np.int64)
+    toks[:3, 0] = rng.integers(0, s.sem_begin, size=3)                     # text
+    toks[3:, 0] = rng.integers(s.sem_begin, s.sem_end + 1, size=T - 3)     # reference audio
+    toks[3:, 1:] = rng.integers(0, s.codebook_size, size=(T - 3, s.num_codebooks))
+    kv = np.zeros((s.n_layer, s.n_head_kv, T, 2, s.head_dim), F32)
+    st = sa.prefill(tiny, toks, kv, 0)
+    xs = np.stack([sa.combine(tiny, toks[t, 0], toks[t, 1:]) for t in range(T)])[None]
+    cos, sin = fa.rope_table(s.head_dim, T, s.rope_base)
+    for i in range(s.n_layer):
+        xs = fa.block(tiny, i, xs, cos, sin)
+    h = fa.rms_norm(xs[0, -1], tiny.get("norm"), s.norm_eps)
+    np.testing.assert_allclose(st.hidden, h, rtol=1e-4, atol=1e-5)
+    assert np.all(kv[:, :, T - 1] == st.kv_new)
+    # the same prompt in two parts gives the same state
+    kv2 = np.zeros_like(kv)
+    sa.prefill(tiny, toks[:4], kv2, 0)
+    st2 = sa.prefill(tiny, toks[4:], kv2, 4)
+    np.testing.assert_array_equal(st2.hidden, st.hidden)
