@@ -104,6 +104,8 @@ def library() -> ctypes.CDLL:
         lib.s2fast_slow_destroy.restype = None
         lib.s2fast_slow_step.argtypes = [P, P, I, P, P, P, P, P, P, P, P, P, P, P, V]
         lib.s2fast_slow_step.restype = ctypes.c_int
+        lib.s2fast_slow_prefill.argtypes = [P, P, I, I, P, P, P, P, P, P, P, P, P, P, V]
+        lib.s2fast_slow_prefill.restype = ctypes.c_int
         lib.s2fast_full_frame.argtypes = [P, P, P, I, P, P, P, P, P, P, P, P, P, P, P, V]
         lib.s2fast_full_frame.restype = ctypes.c_int
         lib.s2fast_slow_syncs.argtypes = [P]
@@ -119,7 +121,7 @@ def library() -> ctypes.CDLL:
 EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_frame",
            "s2fast_forward_logits", "s2fast_test_rope_table", "s2fast_test_sample",
            "s2fast_syncs_per_frame", "s2fast_test_timeline", "s2fast_slow_create", "s2fast_slow_destroy",
-           "s2fast_slow_step", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed",
+           "s2fast_slow_step", "s2fast_slow_prefill", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed",
            "s2fast_test_slow_timeline")
 
 
@@ -357,6 +359,32 @@ class SlowAR:
                                         _ptr(main_out), _ptr(sem_out), _ptr(hidden_out), _ptr(logits_out),
                                         _stream(stream))
         _check(rc, "s2fast_slow_step")
+        return main_out, sem_out, hidden_out
+
+    def prefill(self, kv, n_past0: int, tokens, window, u, temperature, top_p, top_k, main_out=None,
+                sem_out=None, hidden_out=None, logits_out=None, stream=None):
+        """Positions n_past0 .. n_past0 + T - 1 of a prompt (tokens [T, 1 +
+        num_codebooks] int32: row-0 token, then codes), then the first main
+        token from the last position's logits."""
+        s = self.shape
+        T = tokens.shape[0]
+        _dev(tokens, torch.int32, (T, 1 + s.num_codebooks), "tokens")
+        _dev(kv, self.kv_dtype(), (s.n_layer, s.n_head_kv, s.max_ctx, 2, s.head_dim), "kv_cache")
+        _dev(window, torch.int32, (1 + RAS_WINDOW,), "window")
+        _dev(u, torch.float32, (2,), "u")
+        dev = kv.device
+        if main_out is None:
+            main_out = torch.empty(1, dtype=torch.int32, device=dev)
+        if sem_out is None:
+            sem_out = torch.empty(1, dtype=torch.int32, device=dev)
+        if hidden_out is None:
+            hidden_out = torch.empty(s.dim, dtype=torch.float32, device=dev)
+        if logits_out is not None:
+            _dev(logits_out, torch.float32, (self.n_allowed,), "logits_out")
+        rc = library().s2fast_slow_prefill(self._ctx, _ptr(kv), int(n_past0), int(T), _ptr(tokens), _ptr(window),
+                                           _ptr(u), _ptr(temperature), _ptr(top_p), _ptr(top_k), _ptr(main_out),
+                                           _ptr(sem_out), _ptr(hidden_out), _ptr(logits_out), _stream(stream))
+        _check(rc, "s2fast_slow_prefill")
         return main_out, sem_out, hidden_out
 
     def full_frame(self, fast: "FastAR", kv, n_past: int, prev_main, prev_codes, window, u_slow, u_fast,

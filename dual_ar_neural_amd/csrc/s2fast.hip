@@ -1931,17 +1931,17 @@ int s2fast_slow_syncs(const s2fast_slow_ctx* ctx) { return ctx ? 5 * ctx->cfg.n_
 
 int s2fast_slow_allowed(const s2fast_slow_ctx* ctx) { return ctx ? ctx->n_allowed : -1; }
 
-int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const int32_t* prev_main,
-                     const int32_t* prev_codes, int32_t* window, const float* u, const float* temperature,
-                     const float* top_p, const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out,
-                     float* hidden_out, float* logits_out, void* stream) {
-  if (!ctx || !kv_cache || !prev_main || !prev_codes || !window || !u || !temperature || !top_p || !top_k ||
-      !main_out || !sem_code_out || !hidden_out)
-    return S2FAST_ERR_ARG;
+}  // extern "C"
+
+namespace {
+
+// One launch of the Slow-AR step kernel at position n_past (arguments
+// already validated); do_head = 0 stops after the last layer.
+int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const int32_t* prev_main,
+                const int32_t* prev_codes, int do_head, int32_t* window, const float* u, const float* temperature,
+                const float* top_p, const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out,
+                float* hidden_out, float* logits_out, hipStream_t st) {
   const s2fast_slow_config& k = ctx->cfg;
-  if (n_past < 0 || n_past >= k.max_context) return S2FAST_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(kv_cache) & 15u) || (reinterpret_cast<uintptr_t>(hidden_out) & 15u))
-    return S2FAST_ERR_ARG;
   SlowArgs a;
   std::memset(&a, 0, sizeof(a));
   a.dim = k.dim; a.n_layer = k.n_layer; a.n_head = k.n_head; a.n_kv = k.n_head_kv; a.hd = k.head_dim;
@@ -1956,7 +1956,7 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
   a.gheads = k.n_head / k.n_head_kv;
   a.gw = a.gheads * k.head_dim;
   a.kmax = ctx->kmax; a.rmax = ctx->rmax;
-  a.max_ctx = k.max_context; a.n_past = n_past; a.nchunk = ctx->nchunk;
+  a.max_ctx = k.max_context; a.n_past = n_past; a.nchunk = ctx->nchunk; a.do_head = do_head;
   a.emb = ctx->w.embeddings; a.cemb = ctx->w.codebook_embeddings; a.norm = ctx->w.norm;
   a.L = ctx->layers; a.rope = ctx->rope; a.kv = kv_cache;
   a.prev_main = prev_main; a.prev_codes = prev_codes; a.window = window; a.u = u;
@@ -1967,7 +1967,6 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
   a.x_slot = ctx->x_slot; a.qkv_slot = ctx->qkv_slot; a.acc_slot = ctx->acc_slot; a.g_slot = ctx->g_slot;
   a.po_slot = ctx->po_slot; a.pml_slot = ctx->pml_slot;
   a.flags = ctx->flags; a.err = ctx->err; a.tlog = ctx->tlog_on ? ctx->tlog : nullptr;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (ctx->epoch > 0xF0000000u) {
     if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
     ctx->epoch = 0;
@@ -1977,7 +1976,48 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
   if (hipLaunchCooperativeKernel(slow_kernel_fn(k.weight_dtype), dim3(ctx->ncu), dim3(NTHREADS), args,
                                  ctx->lds_bytes, st) != hipSuccess)
     return S2FAST_ERR_HIP;
-  ctx->epoch += (u32)s2fast_slow_syncs(ctx);
+  ctx->epoch += (u32)(5 * k.n_layer + (do_head ? 1 : 0));
+  return S2FAST_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const int32_t* prev_main,
+                     const int32_t* prev_codes, int32_t* window, const float* u, const float* temperature,
+                     const float* top_p, const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out,
+                     float* hidden_out, float* logits_out, void* stream) {
+  if (!ctx || !kv_cache || !prev_main || !prev_codes || !window || !u || !temperature || !top_p || !top_k ||
+      !main_out || !sem_code_out || !hidden_out)
+    return S2FAST_ERR_ARG;
+  const s2fast_slow_config& k = ctx->cfg;
+  if (n_past < 0 || n_past >= k.max_context) return S2FAST_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(kv_cache) & 15u) || (reinterpret_cast<uintptr_t>(hidden_out) & 15u))
+    return S2FAST_ERR_ARG;
+  return slow_launch(ctx, kv_cache, n_past, prev_main, prev_codes, 1, window, u, temperature, top_p, top_k,
+                     main_out, sem_code_out, hidden_out, logits_out, reinterpret_cast<hipStream_t>(stream));
+}
+
+int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int32_t T, const int32_t* tokens,
+                        int32_t* window, const float* u, const float* temperature, const float* top_p,
+                        const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out, float* hidden_out,
+                        float* logits_out, void* stream) {
+  if (!ctx || !kv_cache || !tokens || !window || !u || !temperature || !top_p || !top_k || !main_out ||
+      !sem_code_out || !hidden_out)
+    return S2FAST_ERR_ARG;
+  const s2fast_slow_config& k = ctx->cfg;
+  if (T < 1 || n_past0 < 0 || (long long)n_past0 + T > k.max_context) return S2FAST_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(kv_cache) & 15u) || (reinterpret_cast<uintptr_t>(hidden_out) & 15u))
+    return S2FAST_ERR_ARG;
+  const int row = 1 + k.num_codebooks;
+  for (int t = 0; t < T; ++t) {
+    const int32_t* tk = tokens + (size_t)t * row;
+    const int rc = slow_launch(ctx, kv_cache, n_past0 + t, tk, tk + 1, t == T - 1 ? 1 : 0, window, u, temperature,
+                               top_p, top_k, main_out, sem_code_out, hidden_out, logits_out,
+                               reinterpret_cast<hipStream_t>(stream));
+    if (rc != S2FAST_OK) return rc;
+  }
   return S2FAST_OK;
 }
 

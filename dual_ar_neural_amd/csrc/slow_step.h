@@ -43,6 +43,7 @@ struct SlowArgs {
   float eps, sem_scale;
   int has_qkn, qkv_dim, attn_dim, gheads, gw, kmax, rmax;
   int max_ctx, n_past, nchunk;
+  int do_head;        // 0: a prefill position before the last (no head, no draw)
   const void* emb;    // [vocab][dim]
   const void* cemb;   // [ncb * cbs][dim]
   const void* norm;   // [dim]
@@ -92,7 +93,7 @@ struct SlowLds {
   int* cidx;
   u32* mark;
   int* flag;
-  int* tok;      // [32]: previous main token, its codes; then the draw
+  int* tok;      // [32]: previous main token, its codes; [16..17] the draw; [20] codes count
 };
 
 __host__ __device__ inline size_t slow_lds_floats(int kmax, int rmax, int gheads, int hd) {
@@ -258,12 +259,14 @@ __device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, 
       const int c = min(cu, nq - 1);
       float v[4];
       if (MODE == 0) {
-        // sem_scale * e_main, then the codebook rows added in codebook order
+        // sem_scale * e_main, then, if the position carries codes (its
+        // row-0 token is a semantic id), the codebook rows in codebook order
+        const int nadd = s.tok[20] ? a.ncb : 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = a.sem_scale * WQuad<WT>::get(ev[j][0], e);
 #pragma unroll
         for (int t = 1; t < NT; ++t) {
-          if (t > a.ncb) break;
+          if (t > nadd) break;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] += WQuad<WT>::get(ev[j][t], e);
         }
@@ -768,6 +771,7 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs a) {
   if (tidx() <= a.ncb) {
     const int t = tidx();
     s.tok[t] = t == 0 ? min(max(a.prev_main[0], 0), a.vocab - 1) : min(max(a.prev_codes[t - 1], 0), a.cbs - 1);
+    if (t == 0) s.tok[20] = (s.tok[0] >= a.sem_begin && s.tok[0] < a.sem_begin + a.nsem) ? 1 : 0;
   }
   // cos and sin of position n_past (the same for every layer)
   for (int i = tidx(); i < a.hd; i += NTHREADS) {
@@ -775,7 +779,7 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs a) {
     s.rope1[i] = a.rope[((size_t)half * a.max_ctx + a.n_past) * h2 + (i - half * h2)];
   }
   __syncthreads();
-  const int nph = 5 * a.n_layer + 1;
+  const int nph = 5 * a.n_layer + (a.do_head ? 1 : 0);
   // A phase's plan (plain integers) is computed before the barrier that
   // precedes the phase.
   Plan pl = slow_plan<WT>(a, 0, SP_QKV);
@@ -799,5 +803,5 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs a) {
     }
     if (!grid_sync(a, epoch, s.flag)) return;
   }
-  if (blockIdx.x == 0) slow_draw(a, s);
+  if (a.do_head && blockIdx.x == 0) slow_draw(a, s);
 }

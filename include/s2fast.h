@@ -181,7 +181,9 @@ int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const
  * c_0..c_9) give the input
  *     x = (1/sqrt(num_codebooks+1)) * embeddings[m]
  *         + sum_j codebook_embeddings[j * codebook_size + c_j],
- * which runs through n_layer pre-norm layers (RMSNorm, fused wqkv, per-head
+ * (the codebook terms count only when m is a semantic id: the prompt's
+ * mask; a generated frame's main token is one), which runs through n_layer
+ * pre-norm layers (RMSNorm, fused wqkv, per-head
  * q/k RMSNorm, pair RoPE at position n_past, GQA attention over the KV cache
  * positions 0..n_past, wo, SwiGLU) as position n_past; the layer's new key
  * and value are written into the cache at n_past.  hidden = RMSNorm(x, norm);
@@ -265,6 +267,23 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
                      const int32_t* prev_codes, int32_t* window, const float* u, const float* temperature,
                      const float* top_p, const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out,
                      float* hidden_out, float* logits_out, void* stream);
+
+/* Prefill ("Overall architecture & Dual-AR data flow", sections 3.1 and 4):
+ * the prompt's positions n_past0 .. n_past0 + T - 1 run through the step
+ * above in order, one position per launch (the pages' engine takes one
+ * token per chunk on CUDA), writing their keys and values into the cache;
+ * the last position's logits give the first main token, drawn and checked
+ * against the window exactly as s2fast_slow_step does.
+ *   tokens [T, 1 + num_codebooks] i32: per position the row-0 token (text,
+ *          marker or semantic id), then the codebook codes; the codes count
+ *          only where the row-0 token is a semantic id (the prompt's mask)
+ * Other arguments as s2fast_slow_step.  Errors: S2FAST_ERR_ARG for NULL
+ * pointers (other than logits_out), misaligned kv_cache / hidden_out, T < 1
+ * or positions outside [0, max_context). */
+int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int32_t T, const int32_t* tokens,
+                        int32_t* window, const float* u, const float* temperature, const float* top_p,
+                        const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out, float* hidden_out,
+                        float* logits_out, void* stream);
 
 /* One full frame ("Fast-AR codebook decoding ...", section 5.1): the Slow-AR
  * step above, then s2fast_decode_frame of one request on its hidden state

@@ -187,6 +187,8 @@ def test_slow_null_arguments():
                                 None) == 1
     assert lib.s2fast_full_frame(None, None, None, 0, None, None, None, None, None, None, None, None, None, None,
                                  None, None) == 1
+    assert lib.s2fast_slow_prefill(None, None, 0, 1, None, None, None, None, None, None, None, None, None, None,
+                                   None) == 1
     assert lib.s2fast_slow_syncs(None) == -1 and lib.s2fast_slow_allowed(None) == -1
     assert lib.s2fast_test_slow_timeline(None, 1, None, 0) == 1
     lib.s2fast_slow_destroy(None)

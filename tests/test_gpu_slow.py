@@ -257,18 +257,109 @@ def test_full_frame_ragged(slow_ragged):
     assert exact >= 10 and fragile <= 1
 
 
+@pytest.fixture(scope="module")
+def slow_s2pro():
+    w = ssi.SLOW_WORKLOADS["full_s2pro"]
+    _announce("slow s2pro weights (7.3 GB bf16)")
+    p = SlowPair(w.shape, w.seed(0))
+    yield p
+    p.gpu.close()
+
+
 @pytest.mark.timeout(600)
-def test_slow_step_s2pro_full_size():
+def test_slow_step_s2pro_full_size(slow_s2pro):
     """The measured shape: 36 layers, 2048 cached positions (N(0,1) bf16),
     vocabulary 155776; steps at positions 2048 and 2559 (the last) against
     the full oracle step (positions past n_past hold NaN)."""
     w = ssi.SLOW_WORKLOADS["full_s2pro"]
     s = w.shape
-    _announce("slow s2pro weights (7.3 GB bf16)")
-    p = SlowPair(s, w.seed(0))
+    p = slow_s2pro
     inp = ssi.make_step_inputs(w, 2)
     _check_step(p, w.n_fill, inp["main"][0], inp["codes"][0], [], inp["u_slow"][0], seed=w.seed(5))
     # the cache's last position (chunks of 80 positions)
     _check_step(p, s.max_ctx - 1, inp["main"][1], inp["codes"][1], [int(inp["main"][0])], inp["u_slow"][1],
                 seed=w.seed(6))
-    p.gpu.close()
+
+
+# ------------------------------------------------------------------ prefill
+
+def _prompt(s, T, seed, n_text):
+    """T prompt positions: n_text text tokens (ids below the semantic range,
+    codes present but masked), then semantic ids with codes, one of them the
+    end id's row turned into a text-like position."""
+    rng = np.random.default_rng(seed)
+    toks = np.zeros((T, 1 + s.num_codebooks), np.int32)
+    toks[:, 1:] = rng.integers(0, s.codebook_size, size=(T, s.num_codebooks))
+    toks[:n_text, 0] = rng.integers(0, min(s.sem_begin, s.vocab), size=n_text)
+    toks[n_text:, 0] = rng.integers(s.sem_begin, s.sem_end + 1, size=T - n_text)
+    if T - n_text >= 3:
+        toks[n_text + 1, 0] = s.end_id
+    return toks
+
+
+def _check_prefill(p, n_past0, toks, win, u, T_=0.8, top_p=0.8, top_k=30, seed=55):
+    s = p.shape
+    T = toks.shape[0]
+    kv_host, kv_f = _host_kv(s, n_past0, seed)
+    kv = _dev_kv(kv_host)
+    logits = torch.empty(p.gpu.n_allowed, dtype=torch.float32, device="cuda")
+    window = _window_dev(win)
+    _announce(f"prefill {s.name} n_past0={n_past0} T={T}")
+    m_out, sem_out, h_out = p.gpu.prefill(kv, n_past0, torch.from_numpy(toks).cuda(), window, _f32(u), _f32([T_]),
+                                          _f32([top_p]), _i32([top_k]), logits_out=logits)
+    torch.cuda.synchronize()
+    kv_before = kv_f.copy()
+    st = sa.prefill(p.oracle, toks, kv_f, n_past0)
+    ref = st.logits[sa.allowed_ids(s)]
+    got = logits.cpu().numpy()
+    assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max() + 1e-3
+    h = h_out.cpu().numpy()
+    assert np.abs(h - st.hidden).max() <= 1e-3 * np.abs(st.hidden).max() + 1e-4
+    kv_after = _kv_f32(kv)
+    new = slice(n_past0, n_past0 + T)
+    np.testing.assert_allclose(kv_after[:, :, new], kv_f[:, :, new], rtol=1e-2, atol=2e-3)
+    keep = np.r_[0:n_past0, n_past0 + T:s.max_ctx]
+    assert np.array_equal(kv_after[:, :, keep], kv_before[:, :, keep], equal_nan=True)
+    md = sa.draw_main(s, st.logits, list(win), T_, top_p, top_k, u[0], u[1])
+    tok = int(m_out.item())
+    if not md.fragile:
+        assert tok == md.token, (tok, md)
+    assert tok in set(sa.allowed_ids(s).tolist())
+    assert int(sem_out.item()) == sa.sem_code(s, tok)
+    w = window.cpu().numpy()
+    want = sa.push_window(list(win), tok)
+    assert w[0] == len(want) and list(w[1:1 + w[0]]) == want
+
+
+@pytest.mark.parametrize("n_past0,T,n_text", [(0, 1, 1), (0, 9, 4), (30, 5, 0), (70, 10, 3)])
+def test_prefill_tiny(slow_tiny, n_past0, T, n_text):
+    _check_prefill(slow_tiny, n_past0, _prompt(slow_tiny.shape, T, 100 + T, n_text), [], [0.3, 0.7])
+
+
+@pytest.mark.parametrize("n_past0,T,n_text", [(0, 6, 2), (90, 8, 3)])
+def test_prefill_mid(slow_mid, n_past0, T, n_text):
+    _check_prefill(slow_mid, n_past0, _prompt(slow_mid.shape, T, 200 + T, n_text), [], [0.6, 0.2])
+
+
+def test_prefill_ragged(slow_ragged):
+    s = slow_ragged.shape
+    _check_prefill(slow_ragged, 100, _prompt(s, 7, 300, 2), [s.sem_begin + 9], [0.45, 0.55], T_=0.9, top_p=0.85)
+
+
+def test_prefill_rejects_bad_arguments(slow_tiny):
+    s = slow_tiny.shape
+    kv = torch.zeros((s.n_layer, s.n_head_kv, s.max_ctx, 2, s.head_dim), dtype=torch.float32, device="cuda")
+    args = (_window_dev([]), _f32([0.5, 0.5]), _f32([0.8]), _f32([0.8]), _i32([30]))
+    toks = torch.zeros((3, 1 + s.num_codebooks), dtype=torch.int32, device="cuda")
+    for n0 in (-1, s.max_ctx - 2):
+        with pytest.raises(bd.S2FastError) as e:
+            slow_tiny.gpu.prefill(kv, n0, toks, *args)
+        assert e.value.code == 1
+
+
+@pytest.mark.timeout(600)
+def test_prefill_s2pro_full_size(slow_s2pro):
+    """Three prompt positions (a text token, then two semantic positions)
+    over the 2048-position cache at the measured shape."""
+    w = ssi.SLOW_WORKLOADS["full_s2pro"]
+    _check_prefill(slow_s2pro, w.n_fill - 1, _prompt(w.shape, 3, 400, 1), [], [0.25, 0.75], seed=w.seed(7))
