@@ -54,7 +54,7 @@ def algorithmic_bytes_per_frame(shape, batch: int, qkv0_table: bool) -> int:
     return per_frame + io
 
 
-def slow_step_bytes(shape, n_past: int) -> int:
+def slow_step_bytes(shape, n_past: int, head: bool = True) -> int:
     """Bytes one Slow-AR step must move at minimum at position n_past: every
     layer matrix and norm vector once, the input rows (one embedding row and
     one codebook row per codebook), the cache keys/values of positions
@@ -67,9 +67,9 @@ def slow_step_bytes(shape, n_past: int) -> int:
     kv_pos = s.n_head_kv * 2 * s.head_dim * wb
     kv = s.n_layer * (n_past + 1) * kv_pos
     n_allowed = s.codebook_size + (0 if s.sem_begin <= s.end_id <= s.sem_end else 1)
-    head = (n_allowed + 1) * s.dim * wb
+    head_b = (n_allowed + 1) * s.dim * wb + s.dim * 4 if head else 0
     inputs = (1 + s.num_codebooks) * s.dim * wb
-    return s.n_layer * per_layer + kv + head + inputs + s.dim * 4
+    return s.n_layer * per_layer + kv + head_b + inputs
 
 
 def slow_traffic():
@@ -186,6 +186,33 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
                            "bytes_per_launch": int(slow_b), "achieved_gbs": round(slow_b / slow_s / 1e9, 1),
                            "frac": round(slow_b / slow_s / 1e9 / PEAK_HBM_GBS, 4), "syncs": slow.syncs(),
                            "launches": n_slow}}
+    # prefill: a prompt of 64 text tokens and 192 reference-audio positions
+    # (semantic ids with codes) from position 0, one launch per position
+    P, n_text = 256, 64
+    rng = np.random.default_rng(w.seed(6))
+    toks = np.zeros((P, 1 + s.num_codebooks), np.int32)
+    toks[:, 1:] = rng.integers(0, s.codebook_size, size=(P, s.num_codebooks))
+    toks[:n_text, 0] = rng.integers(0, s.sem_begin, size=n_text)
+    toks[n_text:, 0] = rng.integers(s.sem_begin, s.sem_end + 1, size=P - n_text)
+    toks_d = torch.from_numpy(toks).cuda()
+    window.zero_()
+    slow.prefill(kv, 0, toks_d, window, u_slow[0], temp, tp, tk, main_out=main, sem_out=sem, hidden_out=hidden,
+                 stream=stream)
+    torch.cuda.synchronize()
+    print(f"[bench] timing a {P}-position prefill", file=sys.stderr, flush=True)
+    e0.record(stream)
+    slow.prefill(kv, 0, toks_d, window, u_slow[0], temp, tp, tk, main_out=main, sem_out=sem, hidden_out=hidden,
+                 stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    psec = e0.elapsed_time(e1) / 1e3
+    pb = sum(slow_step_bytes(s, p, head=(p == P - 1)) for p in range(P))
+    out["prefill"] = {"workload": f"S2 Pro-shaped Slow-AR prefill of {P} prompt positions ({n_text} text tokens, "
+                                  f"{P - n_text} reference-audio positions with codes) from an empty cache, one "
+                                  "step launch per position, then the first main-token draw",
+                      "positions": P, "positions_per_s": round(P / psec, 1), "ms": round(psec * 1e3, 2),
+                      "bytes": int(pb), "hbm_gbs": round(pb / psec / 1e9, 1),
+                      "frac": round(pb / psec / 1e9 / PEAK_HBM_GBS, 4)}
     slow.close()
     del dev, kv
     torch.cuda.empty_cache()
