@@ -77,8 +77,8 @@ def slow_traffic():
     was taken on the current kernel code (else None)."""
     csrc = os.path.join(ROOT, "dual_ar_neural_amd", "csrc")
     rec = traffic_from_profile(os.path.join(ROOT, "profiles", "slow_kernel_s2pro_full_frame_hbm_traffic.md"),
-                               [os.path.join(csrc, f) for f in ("s2fast.hip", "slow_step.h", "device_common.h",
-                                                                "sampler.h")])
+                               [os.path.join(csrc, f) for f in ("s2fast.hip", "slow_step.h", "slow_host.h",
+                                                                "device_common.h", "sampler.h")])
     return rec["hbm_bytes_per_launch"] if rec else None
 
 

@@ -1768,287 +1768,4 @@ int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* t
 }  // extern "C"
 
 // ======================================================= Slow-AR host side
-
-struct s2fast_slow_ctx {
-  s2fast_slow_config cfg;
-  s2fast_slow_weights w;
-  int device = 0, ncu = 0;
-  size_t lds_bytes = 0;
-  int kmax = 0, rmax = 0, nchunk = 0, nsem = 0, n_allowed = 0, end_first = 0;
-  long long x_slot = 0, qkv_slot = 0, acc_slot = 0, g_slot = 0, po_slot = 0, pml_slot = 0;
-  LayerPtr* layers = nullptr;   // device copy of the layer pointers
-  float* rope = nullptr;
-  float* x0 = nullptr;
-  float* x = nullptr;
-  float* qkv = nullptr;
-  long long* acc = nullptr;
-  float* g = nullptr;
-  float* po = nullptr;
-  float* pml = nullptr;
-  float* logits = nullptr;
-  int* sem = nullptr;          // the full frame's semantic code, handed to Fast-AR
-  u32* flags = nullptr;
-  u32* err = nullptr;
-  u32* tlog = nullptr;     // allocated on first s2fast_test_slow_timeline call
-  bool tlog_on = false;
-  u32 epoch = 0;
-};
-
-namespace {
-
-void free_slow(s2fast_slow_ctx* c) {
-  if (!c) return;
-  void* ptrs[] = {c->layers, c->rope, c->x0, c->x, c->qkv, c->acc, c->g, c->po, c->pml, c->logits, c->sem,
-                  c->flags, c->err, c->tlog};
-  for (void* p : ptrs)
-    if (p) (void)hipFree(p);
-  delete c;
-}
-
-const void* slow_kernel_fn(int dtype) {
-  return dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&slow_kernel<uint16_t>)
-                              : reinterpret_cast<const void*>(&slow_kernel<float>);
-}
-
-}  // namespace
-
-extern "C" {
-
-int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights* w, s2fast_slow_ctx** out) {
-  if (!cfg || !w || !out) return S2FAST_ERR_ARG;
-  *out = nullptr;
-  const s2fast_slow_config& k = *cfg;
-  if (k.weight_dtype != S2FAST_BF16 && k.weight_dtype != S2FAST_F32) return S2FAST_ERR_ARG;
-  const int epl = k.weight_dtype == S2FAST_BF16 ? 8 : 4;
-  if (k.n_layer < 1 || k.n_layer > S2FAST_SLOW_MAX_LAYERS) return S2FAST_ERR_ARG;
-  if (k.n_head < 1 || k.n_head_kv < 1 || k.n_head % k.n_head_kv != 0 || k.n_head / k.n_head_kv > GH_MAX)
-    return S2FAST_ERR_ARG;
-  if (k.head_dim < 8 || k.head_dim > 128 || (k.head_dim % 8)) return S2FAST_ERR_ARG;
-  if (k.dim < epl || k.ffn_dim < epl || k.dim > 16384 || k.ffn_dim > 16384 || k.dim % epl || k.ffn_dim % epl)
-    return S2FAST_ERR_ARG;
-  if (((k.n_head / k.n_head_kv) * k.head_dim) % epl) return S2FAST_ERR_ARG;
-  if (k.num_codebooks < 1 || k.num_codebooks > 10) return S2FAST_ERR_ARG;
-  if (k.codebook_size < 1 || k.codebook_size > 8191 || k.vocab < 2) return S2FAST_ERR_ARG;
-  if (k.semantic_begin < 0 || (long long)k.semantic_begin + k.codebook_size > k.vocab) return S2FAST_ERR_ARG;
-  if (k.end_id < 0 || k.end_id >= k.vocab) return S2FAST_ERR_ARG;
-  if (k.max_context < 1 || k.max_context > (1 << 20)) return S2FAST_ERR_ARG;
-  if (!(k.norm_eps >= 0.0f) || !(k.rope_base > 0.0f)) return S2FAST_ERR_ARG;
-  if (!w->embeddings || !w->codebook_embeddings || !w->norm) return S2FAST_ERR_NO_FAST_DECODER;
-  auto misaligned = [](const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); };
-  if (misaligned(w->embeddings) || misaligned(w->codebook_embeddings) || misaligned(w->norm)) return S2FAST_ERR_ARG;
-  for (int l = 0; l < k.n_layer; ++l) {
-    const s2fast_layer_weights& L = w->layers[l];
-    if (!L.attention_norm || !L.wqkv || !L.wo || !L.ffn_norm || !L.w1 || !L.w3 || !L.w2)
-      return S2FAST_ERR_NO_FAST_DECODER;
-    if (k.has_qk_norm && (!L.q_norm || !L.k_norm)) return S2FAST_ERR_NO_FAST_DECODER;
-    for (const void* p : {L.attention_norm, L.wqkv, L.q_norm, L.k_norm, L.wo, L.ffn_norm, L.w1, L.w3, L.w2})
-      if (misaligned(p)) return S2FAST_ERR_ARG;
-  }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return S2FAST_ERR_HIP;
-  if (!is_gfx950(dev)) return S2FAST_ERR_DEVICE;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return S2FAST_ERR_HIP;
-  if (!prop.cooperativeLaunch) return S2FAST_ERR_DEVICE;
-
-  s2fast_slow_ctx* c = new (std::nothrow) s2fast_slow_ctx();
-  if (!c) return S2FAST_ERR_NOMEM;
-  c->cfg = k;
-  c->w = *w;
-  c->device = dev;
-  c->ncu = prop.multiProcessorCount;
-  const int P = c->ncu, G = k.n_head_kv;
-  if (P < G || P > 1024) { free_slow(c); return S2FAST_ERR_DEVICE; }
-  const int gheads = k.n_head / G, gw = gheads * k.head_dim;
-  const int qkv_dim = (k.n_head + 2 * G) * k.head_dim;
-  c->nsem = k.codebook_size;
-  const bool end_inside = k.end_id >= k.semantic_begin && k.end_id < k.semantic_begin + k.codebook_size;
-  c->n_allowed = c->nsem + (end_inside ? 0 : 1);
-  c->end_first = (!end_inside && k.end_id < k.semantic_begin) ? 1 : 0;
-  c->nchunk = P / G;
-  c->kmax = (std::max(std::max(k.dim, k.ffn_dim), gw) + 3) & ~3;
-  int rmax = 0;
-  for (int n : {qkv_dim, k.dim, c->n_allowed}) rmax = std::max(rmax, (n + P - 1) / P);
-  rmax = std::max(rmax, 2 * ((k.ffn_dim + P - 1) / P));
-  rmax = std::max(rmax, (k.dim + c->nchunk - 1) / c->nchunk);   // wo rows of one block of a group
-  c->rmax = rmax + 1;
-  size_t lds = slow_lds_floats(c->kmax, c->rmax, gheads, k.head_dim) * sizeof(float);
-  const size_t one_per_cu = 84 * 1024;   // more than half the CU's LDS: one block per CU
-  if (lds < one_per_cu) lds = one_per_cu;
-  if (lds > (size_t)prop.sharedMemPerBlock) { free_slow(c); return S2FAST_ERR_ARG; }
-  c->lds_bytes = lds;
-  const void* fn = slow_kernel_fn(k.weight_dtype);
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-    free_slow(c); return S2FAST_ERR_HIP;
-  }
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, NTHREADS, lds) != hipSuccess) { free_slow(c); return S2FAST_ERR_HIP; }
-  if (nb < 1) { free_slow(c); return S2FAST_ERR_DEVICE; }
-
-  const int half = k.head_dim / 2;
-  std::vector<float> rope((size_t)2 * k.max_context * half);
-  rope_table_host(k.head_dim, k.max_context, k.rope_base, rope.data(), rope.data() + (size_t)k.max_context * half);
-  std::vector<LayerPtr> lp(k.n_layer);
-  for (int l = 0; l < k.n_layer; ++l) {
-    const s2fast_layer_weights& L = w->layers[l];
-    lp[l] = LayerPtr{L.attention_norm, L.wqkv, L.q_norm, L.k_norm, L.wo, L.ffn_norm, L.w1, L.w3, L.w2};
-  }
-  auto rup = [](long long n, long long q) { return (n + q - 1) / q * q; };
-  const long long Ln = k.n_layer;
-  c->x_slot = rup(k.dim, 64);
-  c->qkv_slot = rup(qkv_dim, 64);
-  c->acc_slot = rup(k.dim, 32);
-  c->g_slot = rup(k.ffn_dim, 64);
-  c->po_slot = rup((long long)G * c->nchunk * gw, 64);
-  c->pml_slot = rup((long long)G * c->nchunk * gheads * 2, 64);
-  bool ok = dalloc(&c->layers, (size_t)k.n_layer) == hipSuccess && dalloc(&c->rope, rope.size()) == hipSuccess &&
-            dalloc(&c->x0, (size_t)c->x_slot) == hipSuccess && dalloc(&c->x, (size_t)(Ln * c->x_slot)) == hipSuccess &&
-            dalloc(&c->qkv, (size_t)(Ln * c->qkv_slot)) == hipSuccess &&
-            dalloc(&c->acc, (size_t)(Ln * c->acc_slot)) == hipSuccess &&
-            dalloc(&c->g, (size_t)(Ln * c->g_slot)) == hipSuccess &&
-            dalloc(&c->po, (size_t)(Ln * c->po_slot)) == hipSuccess &&
-            dalloc(&c->pml, (size_t)(Ln * c->pml_slot)) == hipSuccess &&
-            dalloc(&c->logits, (size_t)rup(c->n_allowed, 64)) == hipSuccess && dalloc(&c->sem, 64) == hipSuccess &&
-            dalloc(&c->flags, (size_t)P * 64) == hipSuccess && dalloc(&c->err, 64) == hipSuccess;
-  if (!ok) { free_slow(c); return S2FAST_ERR_NOMEM; }
-  ok = hipMemcpy(c->layers, lp.data(), lp.size() * sizeof(LayerPtr), hipMemcpyHostToDevice) == hipSuccess &&
-       hipMemcpy(c->rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice) == hipSuccess &&
-       hipMemset(c->acc, 0, (size_t)(Ln * c->acc_slot) * sizeof(long long)) == hipSuccess &&
-       hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
-       hipMemset(c->err, 0, 64 * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
-  if (!ok) { free_slow(c); return S2FAST_ERR_HIP; }
-  *out = c;
-  return S2FAST_OK;
-}
-
-void s2fast_slow_destroy(s2fast_slow_ctx* ctx) {
-  if (!ctx) return;
-  (void)hipDeviceSynchronize();
-  free_slow(ctx);
-}
-
-int s2fast_slow_syncs(const s2fast_slow_ctx* ctx) { return ctx ? 5 * ctx->cfg.n_layer + 1 : -1; }
-
-int s2fast_slow_allowed(const s2fast_slow_ctx* ctx) { return ctx ? ctx->n_allowed : -1; }
-
-}  // extern "C"
-
-namespace {
-
-// One launch of the Slow-AR step kernel at position n_past (arguments
-// already validated); do_head = 0 stops after the last layer.
-int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const int32_t* prev_main,
-                const int32_t* prev_codes, int do_head, int32_t* window, const float* u, const float* temperature,
-                const float* top_p, const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out,
-                float* hidden_out, float* logits_out, hipStream_t st) {
-  const s2fast_slow_config& k = ctx->cfg;
-  SlowArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.dim = k.dim; a.n_layer = k.n_layer; a.n_head = k.n_head; a.n_kv = k.n_head_kv; a.hd = k.head_dim;
-  a.ffn = k.ffn_dim; a.vocab = k.vocab; a.ncb = k.num_codebooks; a.cbs = k.codebook_size;
-  a.sem_begin = k.semantic_begin; a.end_id = k.end_id; a.nsem = ctx->nsem; a.n_allowed = ctx->n_allowed;
-  a.end_first = ctx->end_first;
-  a.eps = k.norm_eps;
-  a.sem_scale = (float)(1.0 / std::sqrt((double)(k.num_codebooks + 1)));
-  a.has_qkn = k.has_qk_norm ? 1 : 0;
-  a.qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim;
-  a.attn_dim = k.n_head * k.head_dim;
-  a.gheads = k.n_head / k.n_head_kv;
-  a.gw = a.gheads * k.head_dim;
-  a.kmax = ctx->kmax; a.rmax = ctx->rmax;
-  a.max_ctx = k.max_context; a.n_past = n_past; a.nchunk = ctx->nchunk; a.do_head = do_head;
-  a.emb = ctx->w.embeddings; a.cemb = ctx->w.codebook_embeddings; a.norm = ctx->w.norm;
-  a.L = ctx->layers; a.rope = ctx->rope; a.kv = kv_cache;
-  a.prev_main = prev_main; a.prev_codes = prev_codes; a.window = window; a.u = u;
-  a.temp = temperature; a.top_p = top_p; a.top_k = top_k;
-  a.main_out = main_out; a.sem_out = sem_code_out; a.hidden_out = hidden_out; a.logits_out = logits_out;
-  a.x0 = ctx->x0; a.x = ctx->x; a.qkv = ctx->qkv; a.acc = ctx->acc; a.g = ctx->g; a.po = ctx->po;
-  a.pml = ctx->pml; a.logits = ctx->logits;
-  a.x_slot = ctx->x_slot; a.qkv_slot = ctx->qkv_slot; a.acc_slot = ctx->acc_slot; a.g_slot = ctx->g_slot;
-  a.po_slot = ctx->po_slot; a.pml_slot = ctx->pml_slot;
-  a.flags = ctx->flags; a.err = ctx->err; a.tlog = ctx->tlog_on ? ctx->tlog : nullptr;
-  if (ctx->epoch > 0xF0000000u) {
-    if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
-    ctx->epoch = 0;
-  }
-  a.epoch0 = ctx->epoch;
-  void* args[] = {&a};
-  if (hipLaunchCooperativeKernel(slow_kernel_fn(k.weight_dtype), dim3(ctx->ncu), dim3(NTHREADS), args,
-                                 ctx->lds_bytes, st) != hipSuccess)
-    return S2FAST_ERR_HIP;
-  ctx->epoch += (u32)(5 * k.n_layer + (do_head ? 1 : 0));
-  return S2FAST_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const int32_t* prev_main,
-                     const int32_t* prev_codes, int32_t* window, const float* u, const float* temperature,
-                     const float* top_p, const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out,
-                     float* hidden_out, float* logits_out, void* stream) {
-  if (!ctx || !kv_cache || !prev_main || !prev_codes || !window || !u || !temperature || !top_p || !top_k ||
-      !main_out || !sem_code_out || !hidden_out)
-    return S2FAST_ERR_ARG;
-  const s2fast_slow_config& k = ctx->cfg;
-  if (n_past < 0 || n_past >= k.max_context) return S2FAST_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(kv_cache) & 15u) || (reinterpret_cast<uintptr_t>(hidden_out) & 15u))
-    return S2FAST_ERR_ARG;
-  return slow_launch(ctx, kv_cache, n_past, prev_main, prev_codes, 1, window, u, temperature, top_p, top_k,
-                     main_out, sem_code_out, hidden_out, logits_out, reinterpret_cast<hipStream_t>(stream));
-}
-
-int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int32_t T, const int32_t* tokens,
-                        int32_t* window, const float* u, const float* temperature, const float* top_p,
-                        const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out, float* hidden_out,
-                        float* logits_out, void* stream) {
-  if (!ctx || !kv_cache || !tokens || !window || !u || !temperature || !top_p || !top_k || !main_out ||
-      !sem_code_out || !hidden_out)
-    return S2FAST_ERR_ARG;
-  const s2fast_slow_config& k = ctx->cfg;
-  if (T < 1 || n_past0 < 0 || (long long)n_past0 + T > k.max_context) return S2FAST_ERR_ARG;
-  if ((reinterpret_cast<uintptr_t>(kv_cache) & 15u) || (reinterpret_cast<uintptr_t>(hidden_out) & 15u))
-    return S2FAST_ERR_ARG;
-  const int row = 1 + k.num_codebooks;
-  for (int t = 0; t < T; ++t) {
-    const int32_t* tk = tokens + (size_t)t * row;
-    const int rc = slow_launch(ctx, kv_cache, n_past0 + t, tk, tk + 1, t == T - 1 ? 1 : 0, window, u, temperature,
-                               top_p, top_k, main_out, sem_code_out, hidden_out, logits_out,
-                               reinterpret_cast<hipStream_t>(stream));
-    if (rc != S2FAST_OK) return rc;
-  }
-  return S2FAST_OK;
-}
-
-int s2fast_test_slow_timeline(s2fast_slow_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity) {
-  if (!ctx) return S2FAST_ERR_ARG;
-  const size_t n = (size_t)ctx->ncu * TLOG_MAX * TLOG_W;
-  if (!ctx->tlog) {
-    if (hipMalloc(reinterpret_cast<void**>(&ctx->tlog), n * sizeof(u32)) != hipSuccess) return S2FAST_ERR_NOMEM;
-    if (hipMemset(ctx->tlog, 0, n * sizeof(u32)) != hipSuccess) return S2FAST_ERR_HIP;
-  }
-  ctx->tlog_on = enable != 0;
-  if (host_out) {
-    if (capacity < (int64_t)n) return S2FAST_ERR_ARG;
-    if (hipDeviceSynchronize() != hipSuccess) return S2FAST_ERR_HIP;
-    if (hipMemcpy(host_out, ctx->tlog, n * sizeof(u32), hipMemcpyDeviceToHost) != hipSuccess) return S2FAST_ERR_HIP;
-  }
-  return S2FAST_OK;
-}
-
-int s2fast_full_frame(s2fast_slow_ctx* slow, s2fast_ctx* fast, void* kv_cache, int32_t n_past,
-                      const int32_t* prev_main, const int32_t* prev_codes, int32_t* window, const float* u_slow,
-                      const float* u_fast, const float* temperature, const float* top_p, const int32_t* top_k,
-                      int32_t* main_out, float* hidden_out, int32_t* codes_out, void* stream) {
-  if (!slow || !fast || !codes_out || !u_fast) return S2FAST_ERR_ARG;
-  if (fast->cfg.in_dim != slow->cfg.dim || fast->cfg.codebook_size != slow->cfg.codebook_size ||
-      fast->cfg.num_codebooks != slow->cfg.num_codebooks)
-    return S2FAST_ERR_ARG;
-  int rc = s2fast_slow_step(slow, kv_cache, n_past, prev_main, prev_codes, window, u_slow, temperature, top_p,
-                            top_k, main_out, slow->sem, hidden_out, nullptr, stream);
-  if (rc != S2FAST_OK) return rc;
-  return s2fast_decode_frame(fast, 1, hidden_out, slow->sem, u_fast, temperature, top_p, top_k, codes_out, stream);
-}
-
-}  // extern "C"
+#include "slow_host.h"

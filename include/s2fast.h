@@ -293,7 +293,10 @@ int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, i
  *   hidden_out [dim] f32 OUT (16-byte aligned); codes_out [num_codebooks]
  *   i32 OUT [sem_code, c_1, ..., c_9].
  * A following frame passes main_out and codes_out as prev_main and
- * prev_codes and n_past + 1; the caller stops at end_id. */
+ * prev_codes and n_past + 1; the caller stops at end_id.  If the Slow-AR
+ * launch fails, S2FAST_ERR_HIP is returned and no output is written; a
+ * failure of the Fast-AR part follows s2fast_decode_frame (codes_out[1:]
+ * zero-filled). */
 int s2fast_full_frame(s2fast_slow_ctx* slow, s2fast_ctx* fast, void* kv_cache, int32_t n_past,
                       const int32_t* prev_main, const int32_t* prev_codes, int32_t* window, const float* u_slow,
                       const float* u_fast, const float* temperature, const float* top_p, const int32_t* top_k,

@@ -363,3 +363,17 @@ def test_prefill_s2pro_full_size(slow_s2pro):
     over the 2048-position cache at the measured shape."""
     w = ssi.SLOW_WORKLOADS["full_s2pro"]
     _check_prefill(slow_s2pro, w.n_fill - 1, _prompt(w.shape, 3, 400, 1), [], [0.25, 0.75], seed=w.seed(7))
+
+
+@pytest.mark.timeout(600)
+def test_full_frame_s2pro_full_size(slow_s2pro):
+    """Two chained full frames at the measured shapes (36-layer Slow-AR over
+    the 2048-position cache, then the S2 Pro Fast-AR), as bench.py runs
+    them."""
+    fast = FastPair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0))
+    w = ssi.SLOW_WORKLOADS["full_s2pro"]
+    inp = ssi.make_step_inputs(w, 2)
+    exact, fragile = _full_frames(slow_s2pro, fast, 2, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
+                                  inp["codes"][0], 0.8, 0.8)
+    assert exact >= 10 and fragile <= 1
+    fast.gpu.close()
