@@ -30,7 +30,9 @@
 //   UP    RMSNorm(x + attn) -> w1, w3 rows -> silu(a1) * a3
 //   DOWN  w2 rows; x = x + attn + ffn
 // then the head (only the rows sem_mask leaves finite: every other logit is
-// -inf and can never be drawn) and, in block 0, the draw.
+// -inf and can never be drawn) and, in block 0, the draw.  A prefill
+// position before the prompt's last stops after the last layer (do_head 0):
+// it only writes its keys and values into the cache.
 
 constexpr int SLOW_MAX_LAYERS = S2FAST_SLOW_MAX_LAYERS;
 constexpr int RAS_WIN = 10;     // repetition window (main-loop page, section 6)

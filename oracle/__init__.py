@@ -1,4 +1,4 @@
-"""Oracle for the Fast-AR codebook decoder — TEST INFRASTRUCTURE ONLY.
+"""Oracle for the Dual-AR decoder (Fast-AR frame, Slow-AR step) — TEST INFRASTRUCTURE ONLY.
 
 A plain, slow, literal CPU implementation of what the Fast-AR decoder
 computes, written from the s2.cpp analysis pages ("Fast-AR codebook decoding
@@ -19,6 +19,11 @@ Modules:
              exponential race with SplitMix64 per-candidate uniforms).
   brute    - an independent float64 scalar-loop forward for small shapes,
              used only to pin ``fast_ar``.
+  slow_ar  - the Slow-AR side ("Overall architecture & Dual-AR data flow",
+             sections 3-4; main-loop page, sections 5-6): the input combine,
+             the cached decode step, prefill, the masked tied head, the
+             main-token draw with the repetition check, and the full frame
+             (Slow-AR step, then the Fast-AR frame).
 
 Parity status of each function is listed in the module headers.  Nothing
 here is "parity unpinned" except the end-to-end logits at the 2560-wide
