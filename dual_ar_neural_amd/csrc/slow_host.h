@@ -129,12 +129,14 @@ int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights*
   }
   auto rup = [](long long n, long long q) { return (n + q - 1) / q * q; };
   const long long Ln = k.n_layer;
-  c->x_slot = rup(k.dim, 64);
-  c->qkv_slot = rup(qkv_dim, 64);
-  c->acc_slot = rup(k.dim, 32);
-  c->g_slot = rup(k.ffn_dim, 64);
-  c->po_slot = rup((long long)G * c->nchunk * gw, 64);
-  c->pml_slot = rup((long long)G * c->nchunk * gheads * 2, 64);
+  // every per-layer region holds MMAX position rows (prefill takes two
+  // positions per launch)
+  c->x_slot = rup((long long)MMAX * k.dim, 64);
+  c->qkv_slot = rup((long long)MMAX * qkv_dim, 64);
+  c->acc_slot = rup((long long)MMAX * k.dim, 32);
+  c->g_slot = rup((long long)MMAX * k.ffn_dim, 64);
+  c->po_slot = rup((long long)G * c->nchunk * MMAX * gw, 64);
+  c->pml_slot = rup((long long)G * c->nchunk * MMAX * gheads * 2, 64);
   bool ok = dalloc(&c->layers, (size_t)k.n_layer) == hipSuccess && dalloc(&c->rope, rope.size()) == hipSuccess &&
             dalloc(&c->x0, (size_t)c->x_slot) == hipSuccess && dalloc(&c->x, (size_t)(Ln * c->x_slot)) == hipSuccess &&
             dalloc(&c->qkv, (size_t)(Ln * c->qkv_slot)) == hipSuccess &&
@@ -169,12 +171,13 @@ int s2fast_slow_allowed(const s2fast_slow_ctx* ctx) { return ctx ? ctx->n_allowe
 
 namespace {
 
-// One launch of the Slow-AR step kernel at position n_past (arguments
-// already validated); do_head = 0 stops after the last layer.
-int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const int32_t* prev_main,
-                const int32_t* prev_codes, int do_head, int32_t* window, const float* u, const float* temperature,
-                const float* top_p, const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out,
-                float* hidden_out, float* logits_out, hipStream_t st) {
+// Arguments are already validated; do_head = 0 stops after the last layer.
+// One launch of the Slow-AR step kernel at positions n_past .. n_past + M - 1
+// (M <= MMAX; the second position's tokens are main1 / codes1).
+int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, const int32_t* prev_main,
+                const int32_t* prev_codes, const int32_t* main1, const int32_t* codes1, int do_head, int32_t* window,
+                const float* u, const float* temperature, const float* top_p, const int32_t* top_k,
+                int32_t* main_out, int32_t* sem_code_out, float* hidden_out, float* logits_out, hipStream_t st) {
   const s2fast_slow_config& k = ctx->cfg;
   SlowArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -191,9 +194,11 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const int3
   a.gw = a.gheads * k.head_dim;
   a.kmax = ctx->kmax; a.rmax = ctx->rmax;
   a.max_ctx = k.max_context; a.n_past = n_past; a.nchunk = ctx->nchunk; a.do_head = do_head;
+  a.M = M;
   a.emb = ctx->w.embeddings; a.cemb = ctx->w.codebook_embeddings; a.norm = ctx->w.norm;
   a.L = ctx->layers; a.rope = ctx->rope; a.kv = kv_cache;
   a.prev_main = prev_main; a.prev_codes = prev_codes; a.window = window; a.u = u;
+  a.main1 = main1 ? main1 : prev_main; a.codes1 = codes1 ? codes1 : prev_codes;
   a.temp = temperature; a.top_p = top_p; a.top_k = top_k;
   a.main_out = main_out; a.sem_out = sem_code_out; a.hidden_out = hidden_out; a.logits_out = logits_out;
   a.x0 = ctx->x0; a.x = ctx->x; a.qkv = ctx->qkv; a.acc = ctx->acc; a.g = ctx->g; a.po = ctx->po;
@@ -229,8 +234,9 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
   if (n_past < 0 || n_past >= k.max_context) return S2FAST_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(kv_cache) & 15u) || (reinterpret_cast<uintptr_t>(hidden_out) & 15u))
     return S2FAST_ERR_ARG;
-  return slow_launch(ctx, kv_cache, n_past, prev_main, prev_codes, 1, window, u, temperature, top_p, top_k,
-                     main_out, sem_code_out, hidden_out, logits_out, reinterpret_cast<hipStream_t>(stream));
+  return slow_launch(ctx, kv_cache, n_past, 1, prev_main, prev_codes, nullptr, nullptr, 1, window, u, temperature,
+                     top_p, top_k, main_out, sem_code_out, hidden_out, logits_out,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int32_t T, const int32_t* tokens,
@@ -244,11 +250,14 @@ int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, i
   if (T < 1 || n_past0 < 0 || (long long)n_past0 + T > k.max_context) return S2FAST_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(kv_cache) & 15u) || (reinterpret_cast<uintptr_t>(hidden_out) & 15u))
     return S2FAST_ERR_ARG;
+  // two positions a launch (one weight pass for both)
   const int row = 1 + k.num_codebooks;
-  for (int t = 0; t < T; ++t) {
+  for (int t = 0; t < T; t += MMAX) {
+    const int M = std::min(MMAX, T - t);
     const int32_t* tk = tokens + (size_t)t * row;
-    const int rc = slow_launch(ctx, kv_cache, n_past0 + t, tk, tk + 1, t == T - 1 ? 1 : 0, window, u, temperature,
-                               top_p, top_k, main_out, sem_code_out, hidden_out, logits_out,
+    const int32_t* tk1 = tk + (size_t)(M - 1) * row;
+    const int rc = slow_launch(ctx, kv_cache, n_past0 + t, M, tk, tk + 1, tk1, tk1 + 1, t + M == T ? 1 : 0, window,
+                               u, temperature, top_p, top_k, main_out, sem_code_out, hidden_out, logits_out,
                                reinterpret_cast<hipStream_t>(stream));
     if (rc != S2FAST_OK) return rc;
   }

@@ -45,7 +45,8 @@ struct SlowArgs {
   float eps, sem_scale;
   int has_qkn, qkv_dim, attn_dim, gheads, gw, kmax, rmax;
   int max_ctx, n_past, nchunk;
-  int do_head;        // 0: a prefill position before the last (no head, no draw)
+  int do_head;        // 0: prefill positions before the prompt's last (no head, no draw)
+  int M;              // positions this launch: n_past .. n_past + M - 1 (M <= MMAX)
   const void* emb;    // [vocab][dim]
   const void* cemb;   // [ncb * cbs][dim]
   const void* norm;   // [dim]
@@ -55,6 +56,8 @@ struct SlowArgs {
   // the request
   const int* prev_main;     // [1] the previous frame's main token
   const int* prev_codes;    // [ncb] and its codes
+  const int* main1;         // [1], [ncb]: the second position's tokens (M = 2)
+  const int* codes1;
   int* window;              // [1 + RAS_WIN]: count, then main tokens oldest first
   const float* u;           // [2]: main draw, repetition redraw
   const float* temp;
@@ -66,13 +69,13 @@ struct SlowArgs {
   float* logits_out;        // [n_allowed] or nullptr
   // per-launch arena: every region is written once per launch and read only
   // after the barrier that follows its writes (see FrameArgs)
-  float* x0;                // [dim] the step's input vector
-  float* x;                 // [n_layer][x_slot]
-  float* qkv;               // [n_layer][qkv_slot]
-  long long* acc;           // [n_layer][acc_slot] (zero between launches)
-  float* g;                 // [n_layer][g_slot]
-  float* po;                // [n_layer][n_kv][nchunk][gheads][hd] chunk outputs
-  float* pml;               // [n_layer][n_kv][nchunk][gheads][2] chunk max and sum
+  float* x0;                // [MMAX][dim] the positions' input vectors
+  float* x;                 // [n_layer][x_slot]: [MMAX][dim] per layer
+  float* qkv;               // [n_layer][qkv_slot]: [MMAX][qkv_dim]
+  long long* acc;           // [n_layer][acc_slot]: [MMAX][dim] (zero between launches)
+  float* g;                 // [n_layer][g_slot]: [MMAX][ffn]
+  float* po;                // [n_layer][n_kv][nchunk][MMAX][gheads][hd] chunk outputs
+  float* pml;               // [n_layer][n_kv][nchunk][MMAX][gheads][2] chunk max and sum
   float* logits;            // [n_allowed]
   long long x_slot, qkv_slot, acc_slot, g_slot, po_slot, pml_slot;
   u32* flags;
@@ -83,38 +86,38 @@ struct SlowArgs {
 };
 
 struct SlowLds {
-  float* act;    // [kmax] GEMV activation row (phys() layout)
+  float* act;    // [MMAX][kmax] GEMV activation rows (phys() layout)
   float* red;    // [rmax][MMAX][NWAVE]
   float* small;  // [64]
-  float* q;      // [gheads + 2][hd]: the group's query heads, then the new key and value
+  float* q;      // [MMAX][gheads + 2][hd]: per position the group's query heads, its new key and value
   float* qkn;    // [2][hd] q_norm, k_norm
   float* ow;     // [NWAVE][gheads][hd + 2] per-wave attention partials
   float* mrg;    // [NTHREADS][6] chunk-merge partials (max, sum, 4 outputs)
-  float* rope1;  // [hd]: cos then sin at position n_past
+  float* rope1;  // [MMAX][hd]: cos then sin at positions n_past + m
   float* cval;
   int* cidx;
   u32* mark;
   int* flag;
-  int* tok;      // [32]: previous main token, its codes; [16..17] the draw; [20] codes count
+  int* tok;      // [64]: row-0 token and codes of position m at 32 m, its codes flag at 32 m + 20; the draw at [16..17]
 };
 
 __host__ __device__ inline size_t slow_lds_floats(int kmax, int rmax, int gheads, int hd) {
-  const size_t act = ((size_t)kmax + 3) & ~(size_t)3;
-  return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)(gheads + 2) * hd + 2 * (size_t)hd +
-         (size_t)NWAVE * gheads * (hd + 2) + 6 * (size_t)NTHREADS + (size_t)hd + 2 * TOPK_MAX + 256 + 4 + 32;
+  const size_t act = (size_t)MMAX * (((size_t)kmax + 3) & ~(size_t)3);
+  return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)MMAX * (gheads + 2) * hd + 2 * (size_t)hd +
+         (size_t)NWAVE * gheads * (hd + 2) + 6 * (size_t)NTHREADS + (size_t)MMAX * hd + 2 * TOPK_MAX + 256 + 4 + 64;
 }
 
 __device__ inline SlowLds slow_carve(float* base, const SlowArgs& a) {
   SlowLds s;
   float* p = base;
-  s.act = p; p += ((size_t)a.kmax + 3) & ~(size_t)3;
+  s.act = p; p += (size_t)MMAX * (((size_t)a.kmax + 3) & ~(size_t)3);
   s.red = p; p += (size_t)a.rmax * NWAVE * MMAX;
   s.small = p; p += 64;
-  s.q = p; p += (size_t)(a.gheads + 2) * a.hd;
+  s.q = p; p += (size_t)MMAX * (a.gheads + 2) * a.hd;
   s.qkn = p; p += 2 * (size_t)a.hd;
   s.ow = p; p += (size_t)NWAVE * a.gheads * (a.hd + 2);
   s.mrg = p; p += 6 * (size_t)NTHREADS;
-  s.rope1 = p; p += a.hd;
+  s.rope1 = p; p += (size_t)MMAX * a.hd;
   s.cval = p; p += TOPK_MAX;
   s.cidx = reinterpret_cast<int*>(p); p += TOPK_MAX;
   s.mark = reinterpret_cast<u32*>(p); p += 256;
@@ -219,34 +222,37 @@ __device__ __forceinline__ Plan slow_plan(const SlowArgs& a, int l, int kind) {
 // it to the arena for the later phases of layer 0); 1: the previous layer's
 // output; 2: layer input + the attention accumulator (x_mid).
 template <typename WT, int MODE, typename Hook>
-__device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, int l, const WT* normw,
+__device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, int l, int m0, int Mr, const WT* normw,
                                            const Hook& hook) {
   constexpr int NS = MODE == 0 ? 2 : 3;
   constexpr int NT = 11;                    // main token + at most 10 codebook rows per batch step
-  const int nq = a.dim >> 2;
+  const int hq = a.dim >> 2;
+  const int nq = Mr * hq;                   // rows m0 .. m0 + Mr - 1 (Mr <= 2), row by row
   const float* src = slow_lin(a, l);
   const WT* emb = reinterpret_cast<const WT*>(a.emb);
   const WT* cemb = reinterpret_cast<const WT*>(a.cemb);
-  float ss = 0.0f;
+  float ss0 = 0.0f, ss1 = 0.0f;
   auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
     v4f xv[NS];
     v2ll a0[NS], a1[NS];
     typename WQuad<WT>::type wv[NS], ev[NS][NT];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const int c = quad_of(base, j, nq);
+      const int q = quad_of(base, j, nq);
+      const int r = q >= hq ? 1 : 0, c = q - r * hq, m = m0 + r;
       wv[j] = WQuad<WT>::load(normw, c);
       if (MODE == 0) {
-        ev[j][0] = WQuad<WT>::load(emb + (size_t)s.tok[0] * a.dim, c);
+        const int* tk = s.tok + 32 * m;
+        ev[j][0] = WQuad<WT>::load(emb + (size_t)tk[0] * a.dim, c);
 #pragma unroll
         for (int t = 1; t < NT; ++t) {
           const int jj = min(t - 1, a.ncb - 1);
-          ev[j][t] = WQuad<WT>::load(cemb + ((size_t)jj * a.cbs + s.tok[1 + jj]) * a.dim, c);
+          ev[j][t] = WQuad<WT>::load(cemb + ((size_t)jj * a.cbs + tk[1 + jj]) * a.dim, c);
         }
       } else {
-        xv[j] = *reinterpret_cast<const v4f*>(src + 4 * c);
+        xv[j] = *reinterpret_cast<const v4f*>(src + (size_t)m * a.dim + 4 * c);
         if (MODE == 2) {
-          const long long* ac = a.acc + (size_t)l * a.acc_slot + 4 * c;
+          const long long* ac = a.acc + (size_t)l * a.acc_slot + (size_t)m * a.dim + 4 * c;
           a0[j] = *reinterpret_cast<const v2ll*>(ac);
           a1[j] = *reinterpret_cast<const v2ll*>(ac + 2);
         }
@@ -258,19 +264,22 @@ __device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, 
     for (int j = 0; j < NS; ++j) {
       if (j >= nj) break;
       const int cu = base + j * NTHREADS + tidx();
-      const int c = min(cu, nq - 1);
+      const int q = min(cu, nq - 1);
+      const int r = q >= hq ? 1 : 0, c = q - r * hq, m = m0 + r;
       float v[4];
       if (MODE == 0) {
         // sem_scale * e_main, then, if the position carries codes (its
         // row-0 token is a semantic id), the codebook rows in codebook order
-        const int nadd = s.tok[20] ? a.ncb : 0;
+        const int nadd = s.tok[32 * m + 20] ? a.ncb : 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = a.sem_scale * WQuad<WT>::get(ev[j][0], e);
+        // (a masked row adds exactly 0; the mask differs between the rows of
+        // a batch, so no lane-dependent loop bound)
 #pragma unroll
         for (int t = 1; t < NT; ++t) {
-          if (t > nadd) break;
+          const bool add = t <= nadd;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += WQuad<WT>::get(ev[j][t], e);
+          for (int e = 0; e < 4; ++e) v[e] += add ? WQuad<WT>::get(ev[j][t], e) : 0.0f;
         }
       } else {
 #pragma unroll
@@ -281,21 +290,23 @@ __device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, 
         }
       }
       if (cu < nq) {
+        float t = r ? ss1 : ss0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss = fmaf(v[e], v[e], ss);
+        for (int e = 0; e < 4; ++e) t = fmaf(v[e], v[e], t);
+        if (r) ss1 = t; else ss0 = t;
         if (MODE == 0 && blockIdx.x == 0)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) st_coh(a.x0 + 4 * c + e, v[e]);
+          for (int e = 0; e < 4; ++e) st_coh(a.x0 + (size_t)m * a.dim + 4 * c + e, v[e]);
         v4f o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = v[e] * WQuad<WT>::get(wv[j], e);
-        *reinterpret_cast<v4f*>(s.act + phys<WT>(4 * c, a.dim)) = o;
+        *reinterpret_cast<v4f*>(s.act + (size_t)r * a.kmax + phys<WT>(4 * c, a.dim)) = o;
       }
     }
   };
   batch(0, hook);
   for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
-  store_ss(s.small, 1, ss, 0.0f);
+  store_ss(s.small, Mr, ss0, ss1);
 }
 
 template <typename WT>
@@ -304,37 +315,40 @@ __device__ __forceinline__ void slow_qkv(const SlowArgs& a, const SlowLds& s, in
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   const WT* nw = reinterpret_cast<const WT*>(a.L[l].attn_norm);
-  if (l == 0) slow_stage<WT, 0>(a, s, l, nw, pro);
-  else slow_stage<WT, 1>(a, s, l, nw, pro);
+  const int M = a.M;
+  if (l == 0) slow_stage<WT, 0>(a, s, l, 0, M, nw, pro);
+  else slow_stage<WT, 1>(a, s, l, 0, M, nw, pro);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
-  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  const float den = norm_den(s.small, 0, a.dim, a.eps);
   float* out = a.qkv + (size_t)l * a.qkv_slot;
-  for (int r = tidx(); r < r1 - r0; r += NTHREADS) st_coh(out + r0 + r, red_sum(s.red, r, 0) / den);
+  for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
+    const int r = i / M, m = i - r * M;
+    st_coh(out + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m) / norm_den(s.small, m, a.dim, a.eps));
+  }
 }
 
 // Attention of one block over positions [p0, p1) of its KV group, any
 // head_dim / cache type: lane pairs of head dims, one wave reduction per
 // (position, head).  Leaves each wave's (output, max, sum) per head in s.ow.
 template <typename WT>
-__device__ __forceinline__ void attn_lanes(const SlowArgs& a, const SlowLds& s, const WT* kvg, int p0, int p1) {
+__device__ __forceinline__ void attn_lanes(const SlowArgs& a, const SlowLds& s, const WT* kvg, int p0, int p1,
+                                           int mq) {
   using KV = KVElem<WT>;
-  const int gh = a.gheads, hd = a.hd;
+  const int gh = a.gheads, hd = a.hd, rs = (gh + 2) * hd;
   const int wave = tidx() >> 6, lane = tidx() & 63;
-  const float* kn = s.q + (size_t)gh * hd;
-  const float* vn = kn + hd;
+  const float* qrow = s.q + (size_t)mq * rs;     // query position n_past + mq
   const bool own = 2 * lane < hd;
   const int lp = own ? lane : 0;
   float qx[GH_MAX][2], m[GH_MAX], ls[GH_MAX], o0[GH_MAX], o1[GH_MAX];
 #pragma unroll
   for (int hh = 0; hh < GH_MAX; ++hh) {
     const int h = min(hh, gh - 1);
-    qx[hh][0] = own ? s.q[h * hd + 2 * lp] : 0.0f;
-    qx[hh][1] = own ? s.q[h * hd + 2 * lp + 1] : 0.0f;
+    qx[hh][0] = own ? qrow[h * hd + 2 * lp] : 0.0f;
+    qx[hh][1] = own ? qrow[h * hd + 2 * lp + 1] : 0.0f;
     m[hh] = -INFINITY;
     ls[hh] = 0.0f;
     o0[hh] = 0.0f;
@@ -354,14 +368,17 @@ __device__ __forceinline__ void attn_lanes(const SlowArgs& a, const SlowLds& s, 
     float kx[SPPW][2], vx[SPPW][2];
 #pragma unroll
     for (int i = 0; i < SPPW; ++i) {
-      // the new position comes from LDS; a position past the chunk reads as
-      // zeros, so whatever the cache holds past n_past never enters the sums
-      const int j = base + NWAVE * i;
-      const bool nw = j == a.n_past, live = j < p1;
-      kx[i][0] = nw ? kn[2 * lp] : (live ? KV::lo(kr[i]) : 0.0f);
-      kx[i][1] = nw ? kn[2 * lp + 1] : (live ? KV::hi(kr[i]) : 0.0f);
-      vx[i][0] = nw ? vn[2 * lp] : (live ? KV::lo(vr[i]) : 0.0f);
-      vx[i][1] = nw ? vn[2 * lp + 1] : (live ? KV::hi(vr[i]) : 0.0f);
+      // the launch's new positions come from LDS; a position past the chunk
+      // or after the query reads as zeros, so whatever the cache holds past
+      // n_past never enters the sums
+      const int j = base + NWAVE * i, mm = j - a.n_past;
+      const bool nw = mm >= 0 && mm < a.M, live = j < p1 && j <= a.n_past + mq;
+      const float* kn = s.q + (size_t)min(max(mm, 0), a.M - 1) * rs + (size_t)gh * hd;
+      const float* vn = kn + hd;
+      kx[i][0] = !live ? 0.0f : nw ? kn[2 * lp] : KV::lo(kr[i]);
+      kx[i][1] = !live ? 0.0f : nw ? kn[2 * lp + 1] : KV::hi(kr[i]);
+      vx[i][0] = !live ? 0.0f : nw ? vn[2 * lp] : KV::lo(vr[i]);
+      vx[i][1] = !live ? 0.0f : nw ? vn[2 * lp + 1] : KV::hi(vr[i]);
     }
 #pragma unroll
     for (int hh = 0; hh < GH_MAX; ++hh) {
@@ -372,7 +389,8 @@ __device__ __forceinline__ void attn_lanes(const SlowArgs& a, const SlowLds& s, 
       for (int i = 0; i < SPPW; ++i) {
         float part = fmaf(qx[hh][0], kx[i][0], qx[hh][1] * kx[i][1]);
         part = wave_sum(own ? part : 0.0f);
-        sc[i] = (base + NWAVE * i < p1) ? part * scale : -INFINITY;
+        const int j = base + NWAVE * i;
+        sc[i] = (j < p1 && j <= a.n_past + mq) ? part * scale : -INFINITY;
         mb = fmaxf(mb, sc[i]);
       }
       const float mn = fmaxf(m[hh], mb);
@@ -410,18 +428,19 @@ __device__ __forceinline__ void attn_lanes(const SlowArgs& a, const SlowLds& s, 
 // positions for its 8 head dims; the four rows of a wave are added at the
 // end.  Leaves each wave's (output, max, sum) per head in s.ow.
 template <typename WT>
-__device__ __forceinline__ void attn_rows16(const SlowArgs& a, const SlowLds& s, const WT* kvg, int p0, int p1) {
+__device__ __forceinline__ void attn_rows16(const SlowArgs& a, const SlowLds& s, const WT* kvg, int p0, int p1,
+                                            int mq) {
   constexpr int NI = 3;      // load instructions (4 positions each) per wave per batch
-  constexpr int GH = 4, HD = 128;
+  constexpr int GH = 4, HD = 128, RS = (GH + 2) * HD;
   const int wave = tidx() >> 6, lane = tidx() & 63;
   const int r = lane >> 4, sg = lane & 15;     // position row of the instruction, dims 8sg..8sg+7
-  const float* kn = s.q + GH * HD;
-  const float* vn = kn + HD;
+  const float* qrow = s.q + (size_t)mq * RS;   // query position n_past + mq
+  const int jq = a.n_past + mq;
   float qv[GH][8], m[GH], ls[GH], o[GH][8];
 #pragma unroll
   for (int hh = 0; hh < GH; ++hh) {
-    const float4 q0 = *reinterpret_cast<const float4*>(s.q + hh * HD + 8 * sg);
-    const float4 q1 = *reinterpret_cast<const float4*>(s.q + hh * HD + 8 * sg + 4);
+    const float4 q0 = *reinterpret_cast<const float4*>(qrow + hh * HD + 8 * sg);
+    const float4 q1 = *reinterpret_cast<const float4*>(qrow + hh * HD + 8 * sg + 4);
     qv[hh][0] = q0.x; qv[hh][1] = q0.y; qv[hh][2] = q0.z; qv[hh][3] = q0.w;
     qv[hh][4] = q1.x; qv[hh][5] = q1.y; qv[hh][6] = q1.z; qv[hh][7] = q1.w;
     m[hh] = -INFINITY;
@@ -443,16 +462,19 @@ __device__ __forceinline__ void attn_rows16(const SlowArgs& a, const SlowLds& s,
     float kx[NI][8], vx[NI][8], sc[NI][GH];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      // the new position from LDS; positions past the chunk read as zeros
-      const int j = b0 + (i * NWAVE + wave) * 4 + r;
-      const bool nw = j == a.n_past, live = j < p1;
+      // the launch's new positions from LDS; positions past the chunk or
+      // after the query read as zeros
+      const int j = b0 + (i * NWAVE + wave) * 4 + r, mm = j - a.n_past;
+      const bool nw = mm >= 0 && mm < a.M, live = j < p1 && j <= jq;
+      const float* kn = s.q + (size_t)min(max(mm, 0), a.M - 1) * RS + GH * HD;
+      const float* vn = kn + HD;
       float kf[8], vf[8];
       WTraits<WT>::unpack(make_uint4(kr[i].x, kr[i].y, kr[i].z, kr[i].w), kf);
       WTraits<WT>::unpack(make_uint4(vr[i].x, vr[i].y, vr[i].z, vr[i].w), vf);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        kx[i][k] = nw ? kn[8 * sg + k] : (live ? kf[k] : 0.0f);
-        vx[i][k] = nw ? vn[8 * sg + k] : (live ? vf[k] : 0.0f);
+        kx[i][k] = !live ? 0.0f : nw ? kn[8 * sg + k] : kf[k];
+        vx[i][k] = !live ? 0.0f : nw ? vn[8 * sg + k] : vf[k];
       }
 #pragma unroll
       for (int hh = 0; hh < GH; ++hh) {
@@ -515,59 +537,75 @@ __device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, i
   const int g = blockIdx.x % G, c = blockIdx.x / G;
   if (c >= a.nchunk) return;
   const int wave = tidx() >> 6, lane = tidx() & 63;
-  const int N = a.n_past + 1;
+  const int M = a.M;
+  const int N = a.n_past + M;                     // positions 0 .. n_past + M - 1
   const int p0 = (int)(((long long)N * c) / a.nchunk), p1 = (int)(((long long)N * (c + 1)) / a.nchunk);
   const float* qkv = a.qkv + (size_t)l * a.qkv_slot;
-  // the group's query heads, then the new key and value, and the q/k norm weights
-  for (int i = tidx(); i < (gh + 2) * hd; i += NTHREADS) {
-    const int v = i / hd, d = i - v * hd;
+  const int rs = (gh + 2) * hd;
+  // per new position: the group's query heads, its new key and value; and
+  // the q/k norm weights
+  for (int i = tidx(); i < M * rs; i += NTHREADS) {
+    const int m = i / rs, v = (i - m * rs) / hd, d = i - m * rs - v * hd;
     const int src = v < gh ? (g * gh + v) * hd : (v == gh ? (H + g) * hd : (H + G + g) * hd);
-    s.q[i] = qkv[src + d];
+    s.q[i] = qkv[(size_t)m * a.qkv_dim + src + d];
   }
   if (a.has_qkn)
     for (int i = tidx(); i < 2 * hd; i += NTHREADS)
       s.qkn[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(i < hd ? a.L[l].q_norm : a.L[l].k_norm), i % hd);
   __syncthreads();
-  for (int v = wave; v < gh + 1; v += NWAVE)
-    head_norm_rope(s.q + (size_t)v * hd, hd, v < gh ? s.qkn : s.qkn + hd, a.has_qkn, a.eps, s.rope1, 1, 0);
+  for (int v = wave; v < M * (gh + 1); v += NWAVE) {
+    const int m = v / (gh + 1), vv = v - m * (gh + 1);
+    head_norm_rope(s.q + (size_t)m * rs + (size_t)vv * hd, hd, vv < gh ? s.qkn : s.qkn + hd, a.has_qkn, a.eps,
+                   s.rope1 + (size_t)m * hd, 1, 0);
+  }
   __syncthreads();
   mark(a, s.flag[1], 6);
-  float* kn = s.q + (size_t)gh * hd;
-  float* vn = kn + hd;
-  for (int d = tidx(); d < 2 * hd; d += NTHREADS) kn[d] = KV::round(kn[d]);   // the cache's precision
+  for (int d = tidx(); d < M * 2 * hd; d += NTHREADS) {   // new keys and values in the cache's precision
+    const int m = d / (2 * hd);
+    float* kv2 = s.q + (size_t)m * rs + (size_t)gh * hd;
+    kv2[d - m * 2 * hd] = KV::round(kv2[d - m * 2 * hd]);
+  }
   __syncthreads();
 
   const WT* kvg = reinterpret_cast<const WT*>(a.kv) + (size_t)(l * G + g) * a.max_ctx * 2 * hd;
   const int ws = hd + 2;
-  if (sizeof(WT) == 2 && hd == 128 && gh == 4) attn_rows16<WT>(a, s, kvg, p0, p1);
-  else attn_lanes<WT>(a, s, kvg, p0, p1);
-  mark(a, s.flag[1], 7);
-  __syncthreads();
-  float* po = a.po + (size_t)l * a.po_slot + ((size_t)g * a.nchunk + c) * gh * hd;
-  float* pml = a.pml + (size_t)l * a.pml_slot + ((size_t)g * a.nchunk + c) * gh * 2;
-  for (int t = tidx(); t < gh * hd; t += NTHREADS) {
-    const int hh = t / hd, d = t - hh * hd;
-    float M = -INFINITY;
-    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s.ow[((size_t)w * gh + hh) * ws + hd]);
-    float O = 0.0f, Ls = 0.0f;
-    if (M != -INFINITY) {
-      for (int w = 0; w < NWAVE; ++w) {
-        const float* ww = s.ow + ((size_t)w * gh + hh) * ws;
-        const float f = expf(ww[hd] - M);   // 0 for a wave without positions
-        O = fmaf(f, ww[d], O);
-        Ls = fmaf(f, ww[hd + 1], Ls);
+  for (int mq = 0; mq < M; ++mq) {
+    if (sizeof(WT) == 2 && hd == 128 && gh == 4) attn_rows16<WT>(a, s, kvg, p0, p1, mq);
+    else attn_lanes<WT>(a, s, kvg, p0, p1, mq);
+    mark(a, s.flag[1], 7);
+    __syncthreads();
+    const size_t pc = ((size_t)g * a.nchunk + c) * MMAX + mq;   // this chunk's partial of query mq
+    float* po = a.po + (size_t)l * a.po_slot + pc * gh * hd;
+    float* pml = a.pml + (size_t)l * a.pml_slot + pc * gh * 2;
+    for (int t = tidx(); t < gh * hd; t += NTHREADS) {
+      const int hh = t / hd, d = t - hh * hd;
+      float Mx = -INFINITY;
+      for (int w = 0; w < NWAVE; ++w) Mx = fmaxf(Mx, s.ow[((size_t)w * gh + hh) * ws + hd]);
+      float O = 0.0f, Ls = 0.0f;
+      if (Mx != -INFINITY) {
+        for (int w = 0; w < NWAVE; ++w) {
+          const float* ww = s.ow + ((size_t)w * gh + hh) * ws;
+          const float f = expf(ww[hd] - Mx);   // 0 for a wave without positions
+          O = fmaf(f, ww[d], O);
+          Ls = fmaf(f, ww[hd + 1], Ls);
+        }
+      }
+      st_coh(po + t, O);
+      if (d == 0) {
+        st_coh(pml + 2 * hh, Mx);
+        st_coh(pml + 2 * hh + 1, Ls);
       }
     }
-    st_coh(po + t, O);
-    if (d == 0) {
-      st_coh(pml + 2 * hh, M);
-      st_coh(pml + 2 * hh + 1, Ls);
-    }
+    __syncthreads();   // s.ow is rewritten by the next query's pass
   }
-  // the new key and value into the cache (the block whose chunk holds n_past)
-  if (c == a.nchunk - 1) {
-    WT* row = reinterpret_cast<WT*>(a.kv) + ((size_t)(l * G + g) * a.max_ctx + a.n_past) * 2 * hd;
-    for (int d = tidx(); d < 2 * hd; d += NTHREADS) row[d] = KV::enc(kn[d]);
+  // the new keys and values into the cache, each by the block whose chunk
+  // holds its position
+  for (int mm = 0; mm < M; ++mm) {
+    const int pos = a.n_past + mm;
+    if (pos < p0 || pos >= p1) continue;
+    WT* row = reinterpret_cast<WT*>(a.kv) + ((size_t)(l * G + g) * a.max_ctx + pos) * 2 * hd;
+    const float* src = s.q + (size_t)mm * rs + (size_t)gh * hd;
+    for (int d = tidx(); d < 2 * hd; d += NTHREADS) row[d] = KV::enc(src[d]);
   }
 }
 
@@ -577,8 +615,9 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
   const int gh = a.gheads, hd = a.hd, nc = a.nchunk, n = gh * hd;
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   u32x4 slot[RING];
-  const float* pml = a.pml + (size_t)l * a.pml_slot + (size_t)g * nc * gh * 2;
-  const float* po = a.po + (size_t)l * a.po_slot + (size_t)g * nc * gh * hd;
+  const int M = a.M;
+  const float* pml0 = a.pml + (size_t)l * a.pml_slot + (size_t)g * nc * MMAX * gh * 2;
+  const float* po0 = a.po + (size_t)l * a.po_slot + (size_t)g * nc * MMAX * gh * hd;
   // Merge the chunk partials of every head of the group (log-sum-exp
   // weights).  A thread takes 4 consecutive output elements (one 16-byte
   // load per chunk) of the chunks cs, cs + S, ...; the S subsets of a quad
@@ -587,6 +626,12 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
   const int S = max(1, NTHREADS / nq);
   const int iters = S > 1 ? 1 : (nq + NTHREADS - 1) / NTHREADS;
   constexpr int CB = 8;
+  for (int mq = 0; mq < M; ++mq) {
+  // chunk cc's partial of query mq: pml0 + (cc * MMAX + mq) * gh * 2, po0 + (cc * MMAX + mq) * n
+  const float* pml = pml0 + (size_t)mq * gh * 2;
+  const float* po = po0 + (size_t)mq * n;
+  float* actm = s.act + (size_t)mq * a.kmax;
+  if (mq > 0) __syncthreads();   // s.mrg of the previous query is read
   for (int it = 0; it < iters; ++it) {
     const int t = tidx();
     const int q = S > 1 ? t % nq : it * NTHREADS + t;
@@ -602,10 +647,10 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int cc = min(c0 + j * S, nc - 1);
-        ml[j] = ld64(pml + ((size_t)cc * gh + hh) * 2);
-        ov[j] = *reinterpret_cast<const v4f*>(po + (size_t)cc * n + 4 * qq);
+        ml[j] = ld64(pml + ((size_t)cc * MMAX * gh + hh) * 2);
+        ov[j] = *reinterpret_cast<const v4f*>(po + (size_t)cc * MMAX * n + 4 * qq);
       }
-      if (it == 0 && c0 == cs) gemv_prologue(pl, slot);
+      if (mq == 0 && it == 0 && c0 == cs) gemv_prologue(pl, slot);
       float mb = -INFINITY;
 #pragma unroll
       for (int j = 0; j < CB; ++j)
@@ -632,7 +677,7 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
       }
     } else if (live) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s.act[phys<WT>(4 * qq + e, a.gw)] = O[e] / Ls;
+      for (int e = 0; e < 4; ++e) actm[phys<WT>(4 * qq + e, a.gw)] = O[e] / Ls;
     }
   }
   if (S > 1) {
@@ -649,16 +694,20 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
         for (int e = 0; e < 4; ++e) O[e] = fmaf(f, w[2 + e], O[e]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s.act[phys<WT>(4 * q + e, a.gw)] = O[e] / Ls;
+      for (int e = 0; e < 4; ++e) actm[phys<WT>(4 * q + e, a.gw)] = O[e] / Ls;
     }
+  }
   }
   __syncthreads();
   mark(a, s.flag[1], 2);
-  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
   long long* acc = a.acc + (size_t)l * a.acc_slot;
-  for (int r = tidx(); r < r1 - r0; r += NTHREADS) atomic_add_coh(acc + r0 + r, to_fx(red_sum(s.red, r, 0)));
+  for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
+    const int r = i / M, m = i - r * M;
+    atomic_add_coh(acc + (size_t)m * a.dim + r0 + r, to_fx(red_sum(s.red, r, m)));
+  }
 }
 
 template <typename WT>
@@ -666,17 +715,20 @@ __device__ __forceinline__ void slow_up(const SlowArgs& a, const SlowLds& s, int
   const int r0 = pl.r0, r1 = pl.r1, nr = r1 - r0;
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
-  slow_stage<WT, 2>(a, s, l, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
+  const int M = a.M;
+  slow_stage<WT, 2>(a, s, l, 0, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
   zero_lds(s.red, 2 * nr * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
-  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);   // rows [0, nr): w1, [nr, 2nr): w3
+  gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);   // rows [0, nr): w1, [nr, 2nr): w3
   __syncthreads();
   mark(a, s.flag[1], 3);
-  const float den = norm_den(s.small, 0, a.dim, a.eps);
   float* out = a.g + (size_t)l * a.g_slot;
-  for (int r = tidx(); r < nr; r += NTHREADS)
-    st_coh(out + r0 + r, silu(red_sum(s.red, r, 0) / den) * (red_sum(s.red, nr + r, 0) / den));
+  for (int i = tidx(); i < nr * M; i += NTHREADS) {
+    const int r = i / M, m = i - r * M;
+    const float den = norm_den(s.small, m, a.dim, a.eps);
+    st_coh(out + (size_t)m * a.ffn + r0 + r, silu(red_sum(s.red, r, m) / den) * (red_sum(s.red, nr + r, m) / den));
+  }
 }
 
 template <typename WT>
@@ -684,20 +736,25 @@ __device__ __forceinline__ void slow_down(const SlowArgs& a, const SlowLds& s, i
   const int r0 = pl.r0, r1 = pl.r1;
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  const int M = a.M;
   stage_arena<WT, true, 5>(s.act, a.g + (size_t)l * a.g_slot, a.ffn, pro);
+  for (int m = 1; m < M; ++m)
+    stage_arena<WT, true, 5>(s.act + (size_t)m * a.kmax, a.g + (size_t)l * a.g_slot + (size_t)m * a.ffn, a.ffn,
+                             NoHook{});
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
-  gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
+  gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
   const float* xin = slow_lin(a, l);
   float* xo = a.x + (size_t)l * a.x_slot;
   long long* acc = a.acc + (size_t)l * a.acc_slot;
-  for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
-    const int k = r0 + r;
+  for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
+    const int r = i / M, m = i - r * M;
+    const size_t k = (size_t)m * a.dim + r0 + r;
     const float xm = xin[k] + from_fx(acc[k]);
-    st_coh(xo + k, xm + red_sum(s.red, r, 0));
+    st_coh(xo + k, xm + red_sum(s.red, r, m));
     st_coh(acc + k, 0ll);   // ready for the next launch
   }
 }
@@ -709,7 +766,7 @@ __device__ __forceinline__ void slow_head(const SlowArgs& a, const SlowLds& s, P
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   // the final norm reads the last layer's output: the same staging as a
   // layer input one past the last layer
-  slow_stage<WT, 1>(a, s, a.n_layer, reinterpret_cast<const WT*>(a.norm), pro);
+  slow_stage<WT, 1>(a, s, a.n_layer, a.M - 1, 1, reinterpret_cast<const WT*>(a.norm), pro);   // the last position
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
@@ -770,15 +827,21 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs a) {
   const SlowLds s = slow_carve(lds_base, a);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   u32 epoch = a.epoch0;
-  if (tidx() <= a.ncb) {
-    const int t = tidx();
-    s.tok[t] = t == 0 ? min(max(a.prev_main[0], 0), a.vocab - 1) : min(max(a.prev_codes[t - 1], 0), a.cbs - 1);
-    if (t == 0) s.tok[20] = (s.tok[0] >= a.sem_begin && s.tok[0] < a.sem_begin + a.nsem) ? 1 : 0;
+  {
+    const int m = tidx() >> 5, t = tidx() & 31;   // position m's row-0 token (t = 0) and codes
+    if (m < a.M && t <= a.ncb) {
+      const int* mt = m ? a.main1 : a.prev_main;
+      const int* ct = m ? a.codes1 : a.prev_codes;
+      const int v = t == 0 ? min(max(mt[0], 0), a.vocab - 1) : min(max(ct[t - 1], 0), a.cbs - 1);
+      s.tok[32 * m + t] = v;
+      if (t == 0) s.tok[32 * m + 20] = (v >= a.sem_begin && v < a.sem_begin + a.nsem) ? 1 : 0;
+    }
   }
-  // cos and sin of position n_past (the same for every layer)
-  for (int i = tidx(); i < a.hd; i += NTHREADS) {
-    const int h2 = a.hd >> 1, half = i >= h2 ? 1 : 0;
-    s.rope1[i] = a.rope[((size_t)half * a.max_ctx + a.n_past) * h2 + (i - half * h2)];
+  // cos and sin of positions n_past + m (the same for every layer)
+  for (int i = tidx(); i < a.M * a.hd; i += NTHREADS) {
+    const int m = i / a.hd, d = i - m * a.hd;
+    const int h2 = a.hd >> 1, half = d >= h2 ? 1 : 0;
+    s.rope1[i] = a.rope[((size_t)half * a.max_ctx + a.n_past + m) * h2 + (d - half * h2)];
   }
   __syncthreads();
   const int nph = 5 * a.n_layer + (a.do_head ? 1 : 0);
