@@ -54,21 +54,22 @@ def algorithmic_bytes_per_frame(shape, batch: int, qkv0_table: bool) -> int:
     return per_frame + io
 
 
-def slow_step_bytes(shape, n_past: int, head: bool = True) -> int:
-    """Bytes one Slow-AR step must move at minimum at position n_past: every
-    layer matrix and norm vector once, the input rows (one embedding row and
-    one codebook row per codebook), the cache keys/values of positions
-    0..n_past-1 read and the new position's written, and the head rows the
-    mask leaves open (semantic ids and the end id) plus the final norm."""
+def slow_step_bytes(shape, n_past: int, head: bool = True, M: int = 1) -> int:
+    """Bytes one Slow-AR launch must move at minimum for the M positions
+    n_past .. n_past + M - 1: every layer matrix and norm vector once, the
+    input rows (one embedding row and one codebook row per codebook, per
+    position), the cache keys/values of positions 0..n_past-1 read and the
+    M new positions' written, and the head rows the mask leaves open
+    (semantic ids and the end id) plus the final norm."""
     s = shape
     wb = 2 if s.weight_dtype == "bf16" else 4
     per_layer = (s.qkv_dim * s.dim + s.dim * s.attn_dim + 3 * s.ffn_dim * s.dim + 2 * s.dim
                  + (2 * s.head_dim if s.has_qk_norm else 0)) * wb
     kv_pos = s.n_head_kv * 2 * s.head_dim * wb
-    kv = s.n_layer * (n_past + 1) * kv_pos
+    kv = s.n_layer * (n_past + M) * kv_pos
     n_allowed = s.codebook_size + (0 if s.sem_begin <= s.end_id <= s.sem_end else 1)
     head_b = (n_allowed + 1) * s.dim * wb + s.dim * 4 if head else 0
-    inputs = (1 + s.num_codebooks) * s.dim * wb
+    inputs = M * (1 + s.num_codebooks) * s.dim * wb
     return s.n_layer * per_layer + kv + head_b + inputs
 
 
@@ -187,7 +188,7 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
                            "frac": round(slow_b / slow_s / 1e9 / PEAK_HBM_GBS, 4), "syncs": slow.syncs(),
                            "launches": n_slow}}
     # prefill: a prompt of 64 text tokens and 192 reference-audio positions
-    # (semantic ids with codes) from position 0, one launch per position
+    # (semantic ids with codes) from position 0, two positions per launch
     P, n_text = 256, 64
     rng = np.random.default_rng(w.seed(6))
     toks = np.zeros((P, 1 + s.num_codebooks), np.int32)
@@ -206,10 +207,10 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
     e1.record(stream)
     torch.cuda.synchronize()
     psec = e0.elapsed_time(e1) / 1e3
-    pb = sum(slow_step_bytes(s, p, head=(p == P - 1)) for p in range(P))
+    pb = sum(slow_step_bytes(s, p, head=(p + 2 >= P), M=min(2, P - p)) for p in range(0, P, 2))
     out["prefill"] = {"workload": f"S2 Pro-shaped Slow-AR prefill of {P} prompt positions ({n_text} text tokens, "
-                                  f"{P - n_text} reference-audio positions with codes) from an empty cache, one "
-                                  "step launch per position, then the first main-token draw",
+                                  f"{P - n_text} reference-audio positions with codes) from an empty cache, two "
+                                  "positions per step launch, then the first main-token draw",
                       "positions": P, "positions_per_s": round(P / psec, 1), "ms": round(psec * 1e3, 2),
                       "bytes": int(pb), "hbm_gbs": round(pb / psec / 1e9, 1),
                       "frac": round(pb / psec / 1e9 / PEAK_HBM_GBS, 4)}
