@@ -596,7 +596,7 @@ __device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, i
         st_coh(pml + 2 * hh + 1, Ls);
       }
     }
-    __syncthreads();   // s.ow is rewritten by the next query's pass
+    if (mq + 1 < M) __syncthreads();   // s.ow is rewritten by the next query's pass
   }
   // the new keys and values into the cache, each by the block whose chunk
   // holds its position
