@@ -39,9 +39,12 @@ void free_slow(s2fast_slow_ctx* c) {
   delete c;
 }
 
-const void* slow_kernel_fn(int dtype) {
-  return dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&slow_kernel<uint16_t>)
-                              : reinterpret_cast<const void*>(&slow_kernel<float>);
+const void* slow_kernel_fn(int dtype, int M) {
+  if (dtype == S2FAST_BF16)
+    return M == 2 ? reinterpret_cast<const void*>(&slow_kernel<uint16_t, 2>)
+                  : reinterpret_cast<const void*>(&slow_kernel<uint16_t, 1>);
+  return M == 2 ? reinterpret_cast<const void*>(&slow_kernel<float, 2>)
+                : reinterpret_cast<const void*>(&slow_kernel<float, 1>);
 }
 
 }  // namespace
@@ -111,13 +114,15 @@ int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights*
   if (lds < one_per_cu) lds = one_per_cu;
   if (lds > (size_t)prop.sharedMemPerBlock) { free_slow(c); return S2FAST_ERR_ARG; }
   c->lds_bytes = lds;
-  const void* fn = slow_kernel_fn(k.weight_dtype);
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-    free_slow(c); return S2FAST_ERR_HIP;
+  for (int M = 1; M <= MMAX; ++M) {
+    const void* fn = slow_kernel_fn(k.weight_dtype, M);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+      free_slow(c); return S2FAST_ERR_HIP;
+    }
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, NTHREADS, lds) != hipSuccess) { free_slow(c); return S2FAST_ERR_HIP; }
+    if (nb < 1) { free_slow(c); return S2FAST_ERR_DEVICE; }
   }
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, NTHREADS, lds) != hipSuccess) { free_slow(c); return S2FAST_ERR_HIP; }
-  if (nb < 1) { free_slow(c); return S2FAST_ERR_DEVICE; }
 
   const int half = k.head_dim / 2;
   std::vector<float> rope((size_t)2 * k.max_context * half);
@@ -212,7 +217,7 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
   }
   a.epoch0 = ctx->epoch;
   void* args[] = {&a};
-  if (hipLaunchCooperativeKernel(slow_kernel_fn(k.weight_dtype), dim3(ctx->ncu), dim3(NTHREADS), args,
+  if (hipLaunchCooperativeKernel(slow_kernel_fn(k.weight_dtype, M), dim3(ctx->ncu), dim3(NTHREADS), args,
                                  ctx->lds_bytes, st) != hipSuccess)
     return S2FAST_ERR_HIP;
   ctx->epoch += (u32)(5 * k.n_layer + (do_head ? 1 : 0));

@@ -821,8 +821,12 @@ __device__ __forceinline__ void slow_draw(const SlowArgs& a, const SlowLds& s) {
   }
 }
 
-template <typename WT>
-__global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs a) {
+// MM: positions per launch (1 for decode, 2 for prefill pairs), fixed at
+// compile time so that the one-position kernel carries no per-row loops.
+template <typename WT, int MM>
+__global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
+  SlowArgs a = args;
+  a.M = MM;
   extern __shared__ float lds_base[];
   const SlowLds s = slow_carve(lds_base, a);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
