@@ -182,7 +182,7 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
            "frames": frames, "frames_per_s": round(frames / sec, 2), "ms_per_frame": round(sec * 1e3 / frames, 3),
            "frame_bytes": int(frame_b), "frame_hbm_gbs": round(frame_b * frames / sec / 1e9, 1),
            "frame_frac": round(frame_b * frames / sec / 1e9 / PEAK_HBM_GBS, 4),
-           "slow_kernel": {"kernel": "slow_kernel<bf16>", "avg_launch_us": round(slow_s * 1e6, 2),
+           "slow_kernel": {"kernel": "slow_kernel<bf16, 1>", "avg_launch_us": round(slow_s * 1e6, 2),
                            "traffic": slow_traffic(),
                            "bytes_per_launch": int(slow_b), "achieved_gbs": round(slow_b / slow_s / 1e9, 1),
                            "frac": round(slow_b / slow_s / 1e9 / PEAK_HBM_GBS, 4), "syncs": slow.syncs(),
