@@ -1,0 +1,46 @@
+"""The algorithmic byte counts bench.py divides by kernel time, recomputed
+from the tensor shapes of the synthetic models (CPU only)."""
+import numpy as np
+
+import bench
+from oracle import slow_ar as sa
+from synth import inputs as si
+from synth import slow_inputs as ssi
+
+
+def _tensor_bytes(shape_fn, names, wb):
+    return sum(int(np.prod(shape_fn(n))) * wb for n in names)
+
+
+def test_slow_step_bytes_from_shapes():
+    s = ssi.SLOW_S2PRO
+    wb = 2
+    layer_names = [n for n in ssi.weight_names(s) if n.startswith("layers.")]
+    weights = _tensor_bytes(lambda n: ssi.weight_shape(s, n), layer_names, wb)
+    head_rows = sa.allowed_ids(s).size
+    for n_past in (0, 2048, 2559):
+        want = (weights
+                + s.n_layer * s.n_head_kv * 2 * s.head_dim * wb * (n_past + 1)    # cache read + the new row
+                + (1 + s.num_codebooks) * s.dim * wb                              # input rows
+                + head_rows * s.dim * wb + s.dim * wb + s.dim * 4)               # open head rows, norm, hidden
+        assert bench.slow_step_bytes(s, n_past) == want
+    # a two-position prefill launch: one weight pass, two input rows sets
+    want2 = (weights + s.n_layer * s.n_head_kv * 2 * s.head_dim * wb * (100 + 2)
+             + 2 * (1 + s.num_codebooks) * s.dim * wb)
+    assert bench.slow_step_bytes(s, 100, head=False, M=2) == want2
+
+
+def test_fast_frame_bytes_from_shapes():
+    s = si.S2PRO
+    wb = 2
+    names = si.weight_names(s)
+    layer = [n for n in names if n.startswith("fast_layers.")]
+    per_step = (_tensor_bytes(lambda n: si.weight_shape(s, n), layer, wb)
+                + _tensor_bytes(lambda n: si.weight_shape(s, n), ["fast_output", "fast_norm"], wb)
+                + s.dim * wb)                                                    # one embedding row
+    l0 = _tensor_bytes(lambda n: si.weight_shape(s, n), ["fast_layers.0.attention.wqkv",
+                                                         "fast_layers.0.attention_norm"], wb)
+    io = s.in_dim * 4 + 4 + s.n_steps * 4 + 3 * 4 + s.num_codebooks * 4
+    # steps 2..9 take their layer-0 q/k/v from the table (one float32 row)
+    want = s.n_steps * per_step - (s.n_steps - 1) * (l0 - s.qkv_dim * 4) + io
+    assert bench.algorithmic_bytes_per_frame(s, 1, True) == want

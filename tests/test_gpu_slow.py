@@ -3,9 +3,15 @@ with the oracle, on the GPU.
 
 Tolerances (float32 accumulation in another order than the oracle's):
   logits: |delta| <= 1e-2 * max|logit| + 1e-3 (the Fast-AR logit bound);
-  hidden: |delta| <= 1e-3 * max|hidden| + 1e-4;
-  new cache entries: rtol 1e-2, atol 1e-3 (a float32 value a few ulps away
-  from the oracle's can round to the neighbouring bf16 value, 2^-8 apart);
+  hidden: |delta| <= 1e-2 * max|hidden| + 1e-3, the logit bound: new cache
+    entries are rounded to bf16, and where the two sides' float32 keys or
+    values differ in the last bits the rounding can land one bf16 ulp
+    (2^-8 relative) apart; with few cached positions the attention output is
+    those rounded values themselves, and 36 layers compound the flips
+    (at the measured shape and position 0 the hidden state differs by up to
+    0.2 % of its largest element);
+  new cache entries: the same bound relative to their largest magnitude
+    (they carry the same rounding flips, one bf16 ulp each);
   main token and codes: equal unless the oracle reports a knife-edge draw,
   and then inside the allowed set."""
 import numpy as np
@@ -20,6 +26,7 @@ from synth import slow_inputs as ssi
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
+HIDDEN_RTOL, HIDDEN_ATOL = 1e-2, 1e-3
 
 
 def _announce(msg):
@@ -101,9 +108,10 @@ def _check_step(p, n_past, main, codes, win, u, T=0.8, top_p=0.8, top_k=30, seed
     tol = 1e-2 * np.abs(ref).max() + 1e-3
     assert np.abs(got - ref).max() <= tol, (np.abs(got - ref).max(), tol)
     h = h_out.cpu().numpy()
-    assert np.abs(h - st.hidden).max() <= 1e-3 * np.abs(st.hidden).max() + 1e-4
+    assert np.abs(h - st.hidden).max() <= HIDDEN_RTOL * np.abs(st.hidden).max() + HIDDEN_ATOL
     kv_after = _kv_f32(kv)
-    np.testing.assert_allclose(kv_after[:, :, n_past], st.kv_new, rtol=1e-2, atol=1e-3)
+    dkv = np.abs(kv_after[:, :, n_past] - st.kv_new).max()
+    assert dkv <= HIDDEN_RTOL * np.abs(st.kv_new).max() + HIDDEN_ATOL, dkv
     # every other position is untouched
     assert np.array_equal(np.delete(kv_after, n_past, axis=2), np.delete(kv_f, n_past, axis=2), equal_nan=True)
     md = sa.draw_main(s, st.logits, list(win), T, top_p, top_k, u[0], u[1])
@@ -215,7 +223,7 @@ def _full_frames(p, fast_pair, n_frames, n_fill, u_slow, u_fast, main0, codes0, 
                             u_fast[f], T, top_p, top_k)
         tok, codes = int(m_new.item()), c_new.cpu().numpy()
         h = hid.cpu().numpy()
-        assert np.abs(h - r.hidden).max() <= 1e-3 * np.abs(r.hidden).max() + 1e-4
+        assert np.abs(h - r.hidden).max() <= HIDDEN_RTOL * np.abs(r.hidden).max() + HIDDEN_ATOL
         assert tok in allowed and codes.min() >= 0 and codes.max() < s.codebook_size
         if r.main.fragile:
             fragile += 1              # a knife-edge main draw: the GPU's token is followed below
@@ -314,10 +322,11 @@ def _check_prefill(p, n_past0, toks, win, u, T_=0.8, top_p=0.8, top_k=30, seed=5
     got = logits.cpu().numpy()
     assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max() + 1e-3
     h = h_out.cpu().numpy()
-    assert np.abs(h - st.hidden).max() <= 1e-3 * np.abs(st.hidden).max() + 1e-4
+    assert np.abs(h - st.hidden).max() <= HIDDEN_RTOL * np.abs(st.hidden).max() + HIDDEN_ATOL
     kv_after = _kv_f32(kv)
     new = slice(n_past0, n_past0 + T)
-    np.testing.assert_allclose(kv_after[:, :, new], kv_f[:, :, new], rtol=1e-2, atol=2e-3)
+    dkv = np.abs(kv_after[:, :, new] - kv_f[:, :, new]).max()
+    assert dkv <= HIDDEN_RTOL * np.abs(kv_f[:, :, new]).max() + HIDDEN_ATOL, dkv
     keep = np.r_[0:n_past0, n_past0 + T:s.max_ctx]
     assert np.array_equal(kv_after[:, :, keep], kv_before[:, :, keep], equal_nan=True)
     md = sa.draw_main(s, st.logits, list(win), T_, top_p, top_k, u[0], u[1])
@@ -377,3 +386,14 @@ def test_full_frame_s2pro_full_size(slow_s2pro):
                                   inp["codes"][0], 0.8, 0.8)
     assert exact >= 10 and fragile <= 1
     fast.gpu.close()
+
+
+@pytest.mark.timeout(600)
+def test_slow_edges_s2pro_full_size(slow_s2pro):
+    """The measured shape at the cache's first position (every attention
+    chunk but the last is empty) and an odd prefill from position 0 (two
+    pairs, then a one-position launch)."""
+    w = ssi.SLOW_WORKLOADS["full_s2pro"]
+    inp = ssi.make_step_inputs(w, 1)
+    _check_step(slow_s2pro, 0, inp["main"][0], inp["codes"][0], [], inp["u_slow"][0], seed=w.seed(8))
+    _check_prefill(slow_s2pro, 0, _prompt(w.shape, 5, 500, 2), [], [0.35, 0.65], seed=w.seed(9))
