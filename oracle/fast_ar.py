@@ -143,8 +143,13 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """x [..., in] times a row-major [out, in] weight: x @ w.T in float32."""
-    return np.matmul(x, w.T)
+    """x [..., in] times a row-major [out, in] weight: x @ w.T in float32.
+    The leading axes are flattened first, so a batch of windows is one
+    matrix product over all of its rows (each output is still the dot
+    product of one input row with one weight row)."""
+    x = np.asarray(x)
+    y = np.matmul(x.reshape(-1, x.shape[-1]), w.T)
+    return y.reshape(x.shape[:-1] + (w.shape[0],))
 
 
 # --------------------------------------------------------------------------
@@ -248,6 +253,7 @@ class FrameResult:
     codes: np.ndarray      # [B, num_codebooks] int32
     logits: np.ndarray     # [B, n_steps, V] float32, logits of each step
     fragile: np.ndarray    # [B, n_steps] bool, knife-edge decisions
+    alts: list = None      # [B][n_steps] tuples: every defensible code of each draw
 
 
 def decode_frame(model: Model, hidden, sem_code, uniforms, temperature, top_p, top_k,
@@ -269,6 +275,7 @@ def decode_frame(model: Model, hidden, sem_code, uniforms, temperature, top_p, t
         prefix_src[:, 0] = codes[:, 0]
     logits = np.zeros((B, s.n_steps, s.codebook_size), dtype=F32)
     fragile = np.zeros((B, s.n_steps), dtype=bool)
+    alts = [[None] * s.n_steps for _ in range(B)]
     for k in range(1, s.num_codebooks):
         lg = fast_forward(model, hidden, prefix_src[:, :k])
         logits[:, k - 1] = lg
@@ -276,4 +283,5 @@ def decode_frame(model: Model, hidden, sem_code, uniforms, temperature, top_p, t
             d = _sampler.sample(lg[b], temperature[b], top_p[b], top_k[b], uniforms[b][k - 1])
             codes[b, k] = d.code
             fragile[b, k - 1] = d.fragile
-    return FrameResult(codes.astype(np.int32), logits, fragile)
+            alts[b][k - 1] = d.alts
+    return FrameResult(codes.astype(np.int32), logits, fragile, alts)

@@ -24,13 +24,20 @@ oracle's stated reading:
      lowest rank on ties.  With independent Exp(1) variables E_j this picks
      candidate j with probability p_j / sum(kept p) (the exponential race).
 
+Besides the code, a draw reports every code another implementation may
+defensibly return when its logits differ from these in the last bits (the
+margins below): the parity tests accept exactly those.
+
 Pins (tests/test_oracle_sampler.py): SplitMix64 against the published
 reference sequence; greedy/T->0+/top_k=1/top_p->0+ all reduce to argmax;
 the code is always inside the top-k set; the kept set is the minimal prefix;
-draw frequencies match p_j (chi-square).
+draw frequencies match p_j (chi-square); draws on slightly perturbed logits
+always land in the reported set, which is the code alone away from the
+margins.
 """
 from __future__ import annotations
 
+import itertools
 from dataclasses import dataclass
 
 import numpy as np
@@ -39,13 +46,15 @@ F32 = np.float32
 MASK64 = (1 << 64) - 1
 TOPK_MAX = 64
 
-# Margins below which a decision is reported as a knife-edge: a legitimately
-# different code may come out of an implementation whose logits differ from
-# these in the last bits.
-GREEDY_GAP = 1.0e-3      # absolute logit gap between the top two (greedy)
-TOPK_GAP = 1.0e-3        # absolute logit gap at the top-k boundary
-TOPP_GAP = 1.0e-4        # |c_j - top_p| at the nucleus boundary
-RACE_GAP = 1.0e-4        # relative gap between the two best race keys
+# Margins below which a decision is reported as a knife-edge: an
+# implementation whose logits differ from these in the last bits may take the
+# other side of such a decision.  Each margin names the alternative it
+# allows (see `sample`).
+GREEDY_GAP = 1.0e-3      # any logit within this of the maximum may be the argmax
+ORDER_GAP = 1.0e-3       # two logits closer than this may rank either way
+                         # (this covers the top-k boundary: rank n-1 against rank n)
+TOPP_GAP = 1.0e-4        # |c_j - top_p| at the nucleus boundary: rank j kept or dropped
+RACE_GAP = 1.0e-4        # relative gap between the two best race keys: either wins
 
 
 def splitmix64(x: int) -> int:
@@ -77,14 +86,18 @@ class Draw:
     fragile: bool          # knife-edge: another code is also defensible
     kept: int = 0          # number of kept candidates (m + 1); 0 for greedy
     ranks: np.ndarray = None  # candidate indices in rank order (sampled only)
+    alts: tuple = ()       # every defensible code (sorted; always holds `code`)
 
 
 def greedy(logits: np.ndarray) -> Draw:
+    """argmax, lowest index on ties; every index whose logit is within
+    GREEDY_GAP of the maximum is a defensible alternative."""
     l = np.asarray(logits, dtype=F32)
     code = int(np.argmax(l))              # first occurrence = lowest index
-    top2 = np.sort(l)[-2:] if l.size > 1 else np.array([l[0], -np.inf], F32)
-    fragile = bool(l.size > 1 and float(top2[1]) - float(top2[0]) < GREEDY_GAP)
-    return Draw(code, fragile)
+    alts = tuple(int(i) for i in np.flatnonzero(l.astype(np.float64) >= float(l[code]) - GREEDY_GAP))
+    if code not in alts:                  # NaN-free inputs always hold it; keep the invariant regardless
+        alts = tuple(sorted(set(alts) | {code}))
+    return Draw(code, len(alts) > 1, alts=alts)
 
 
 def rank_order(l: np.ndarray) -> np.ndarray:
@@ -92,17 +105,10 @@ def rank_order(l: np.ndarray) -> np.ndarray:
     return np.argsort(-l, kind="stable")
 
 
-def sample(logits, temperature, top_p, top_k, u) -> Draw:
-    """Draw one code from a request's logits (steps 1-6 of the header)."""
-    l = np.asarray(logits, dtype=F32)
-    V = l.size
-    T = F32(temperature)
-    if not (T > 0):
-        return greedy(l)
-    n = int(min(max(int(top_k), 1), min(V, TOPK_MAX)))
-    order = rank_order(l)
-    ranks = order[:n]
-    lv = l[ranks]
+def _nucleus(lv: np.ndarray, T, top_p):
+    """Steps 3-4 on candidate logits lv given in rank order: float32
+    probabilities p, running sums cum and the last kept rank m."""
+    n = lv.size
     z = (lv / T).astype(F32)
     d = (z - z[0]).astype(F32)
     e = np.exp(d.astype(np.float64)).astype(F32)
@@ -113,33 +119,104 @@ def sample(logits, temperature, top_p, top_k, u) -> Draw:
     tp = F32(top_p)
     c = F32(0.0)
     cum = np.empty(n, F32)
-    m = n - 1
     for j in range(n):
         c = F32(c + p[j])
         cum[j] = c
+    m = n - 1
     for j in range(n):
         if cum[j] >= tp:
             m = j
             break
-    E = np.array([candidate_exponential(u, j) for j in range(m + 1)], dtype=F32)
-    key = (p[: m + 1] / E).astype(F32)
+    return p, cum, m
+
+
+def _race(p: np.ndarray, E: np.ndarray, m: int):
+    """Step 6 over ranks 0..m: the winning rank, and the runner-up rank when
+    its key is within RACE_GAP (relative) of the winner's, else None."""
+    key = (p[: m + 1] / E[: m + 1]).astype(F32)
     best = int(np.argmax(key))            # first occurrence = lowest rank
-
-    # knife-edge report
-    fragile = False
-    if n < V:
-        nxt = l[order[n]]
-        fragile |= float(lv[-1]) - float(nxt) < TOPK_GAP
-    fragile |= abs(float(cum[m]) - float(tp)) < TOPP_GAP
+    runner = None
     if m > 0:
-        fragile |= abs(float(cum[m - 1]) - float(tp)) < TOPP_GAP
-    if m > 0:
-        srt = np.sort(key)
-        fragile |= (float(srt[-1]) - float(srt[-2])) <= RACE_GAP * float(srt[-1])
-    return Draw(int(ranks[best]), bool(fragile), m + 1, ranks)
+        k2 = key.astype(np.float64).copy()
+        k2[best] = -np.inf
+        r = int(np.argmax(k2))
+        if float(key[best]) - float(key[r]) <= RACE_GAP * float(key[best]):
+            runner = r
+    return best, runner
 
 
-def sample_batch(logits, temperature, top_p, top_k, u):
-    """Row-wise `sample` over a batch: logits [B,V], settings [B], u [B]."""
-    return [sample(logits[b], temperature[b], top_p[b], top_k[b], u[b])
-            for b in range(len(logits))]
+def _order_variants(l: np.ndarray, order: np.ndarray, n: int):
+    """Rank orders an implementation with slightly different logits may
+    see: in every run of consecutive ranked logits whose neighbours differ by
+    less than ORDER_GAP and that reaches into the first n ranks (or across
+    the boundary at rank n), each permutation of the run (runs of up to four
+    logits; longer runs: each swap of two of its members).  Only one run is
+    disturbed at a time.  Yields the first n indices of each variant."""
+    V = l.size
+    lim = min(V, n + TOPK_MAX + 1)
+    lv = l[order[:lim]].astype(np.float64)
+    j = 0
+    while j < min(n, lim - 1):
+        a = j
+        while j + 1 < lim and lv[j] - lv[j + 1] < ORDER_GAP:
+            j += 1
+        b = j                                  # run [a, b]
+        j += 1
+        if b == a:
+            continue
+        run = list(order[a:b + 1])
+        if len(run) <= 4:
+            perms = [list(q) for q in itertools.permutations(run) if list(q) != run]
+        else:
+            # pairs of members (adjacent pairs only in runs longer than 16)
+            perms = []
+            for x in range(len(run)):
+                for y in range(x + 1, len(run) if len(run) <= 16 else min(x + 2, len(run))):
+                    q = list(run)
+                    q[x], q[y] = q[y], q[x]
+                    perms.append(q)
+        for q in perms:
+            var = np.array(order[:lim])
+            var[a:b + 1] = q
+            yield var[:n]
+
+
+def sample(logits, temperature, top_p, top_k, u) -> Draw:
+    """Draw one code from a request's logits (steps 1-6 of the header).
+
+    The draw also reports every code that is defensible for logits which
+    differ from these by less than the margins above: the draws under each
+    rank order of near-equal logits (`_order_variants`; the top-k boundary
+    is the pair at ranks n-1 and n), each with the nucleus cut one rank
+    earlier or later where a running sum lies within TOPP_GAP of top_p, and
+    the race's runner-up where its key is within RACE_GAP of the winner's."""
+    l = np.asarray(logits, dtype=F32)
+    V = l.size
+    T = F32(temperature)
+    if not (T > 0):
+        return greedy(l)
+    n = int(min(max(int(top_k), 1), min(V, TOPK_MAX)))
+    order = rank_order(l)
+    ranks = order[:n]
+    tp = F32(top_p)
+    E = np.array([candidate_exponential(u, j) for j in range(n)], dtype=F32)
+    p, cum, m = _nucleus(l[ranks], T, tp)
+    best, _ = _race(p, E, m)
+    code = int(ranks[best])
+
+    alts = set()
+    for cand in [ranks] + list(_order_variants(l, order, n)):
+        pv, cv, mv = _nucleus(l[cand], T, tp)
+        cuts = {mv}
+        if mv + 1 < n and abs(float(cv[mv]) - float(tp)) < TOPP_GAP:
+            cuts.add(mv + 1)
+        if mv > 0 and abs(float(cv[mv - 1]) - float(tp)) < TOPP_GAP:
+            cuts.add(mv - 1)
+        for mm in cuts:
+            b, r = _race(pv, E, mm)
+            alts.add(int(cand[b]))
+            if r is not None:
+                alts.add(int(cand[r]))
+    alts.add(code)
+    alts = tuple(sorted(alts))
+    return Draw(code, len(alts) > 1, m + 1, ranks, alts)

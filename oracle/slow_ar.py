@@ -101,6 +101,47 @@ def cache_round(shape, x: np.ndarray) -> np.ndarray:
     return bf16_round_f32(x) if shape.weight_dtype == "bf16" else np.asarray(x, dtype=F32)
 
 
+# A float32 key or value within this relative distance of the midpoint
+# between its two bfloat16 neighbours may round to either of them in an
+# implementation whose float32 value differs from this one in the last bits
+# (float32 sums taken in another order differ by about 1e-6 relative).
+ROUND_BAND = 1.0e-4
+
+
+class CacheFollowError(AssertionError):
+    """A followed cache entry is not a defensible rounding of the oracle's
+    value."""
+
+
+def follow_rounding(shape, exact: np.ndarray, theirs: np.ndarray):
+    """The cache entries to continue with when another implementation wrote
+    `theirs` for the float32 values `exact`: its entries, provided each one
+    is the oracle's rounding of `exact` or, for a value within ROUND_BAND of
+    a rounding midpoint, the other bfloat16 neighbour.  float32 caches are
+    not rounded, so their entries are compared, not followed (the oracle's
+    values are returned).  Returns (entries, number of other-neighbour
+    choices); raises CacheFollowError otherwise."""
+    exact = np.asarray(exact, dtype=F32)
+    mine = cache_round(shape, exact)
+    if shape.weight_dtype != "bf16":
+        return mine, 0
+    theirs = np.asarray(theirs, dtype=F32)
+    same = theirs.view(np.uint32) == mine.view(np.uint32)
+    # bfloat16 neighbours below and above the exact value (truncation and the next bf16 up in magnitude)
+    b = exact.view(np.uint32)
+    lo = (b & np.uint32(0xFFFF0000)).view(F32)
+    hi = ((b & np.uint32(0xFFFF0000)) + np.uint32(0x10000)).view(F32)
+    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2.0
+    near = np.abs(exact.astype(np.float64) - mid) <= ROUND_BAND * np.abs(exact.astype(np.float64))
+    other = ((theirs.view(np.uint32) == lo.view(np.uint32)) | (theirs.view(np.uint32) == hi.view(np.uint32))) & near
+    ok = same | other
+    if not ok.all():
+        i = np.flatnonzero(~ok.reshape(-1))[0]
+        raise CacheFollowError(f"entry {i}: exact {exact.reshape(-1)[i]!r}, theirs {theirs.reshape(-1)[i]!r}, "
+                               f"oracle {mine.reshape(-1)[i]!r}")
+    return np.where(same, mine, theirs).astype(F32), int((~same).sum())
+
+
 # --------------------------------------------------------------------------
 # input, mask, head
 # --------------------------------------------------------------------------
@@ -170,18 +211,25 @@ class StepResult:
     hidden: np.ndarray       # [dim] RMSNorm(x_last, norm): the tied head's input
     logits: np.ndarray       # [vocab] unmasked tied logits
     kv_new: np.ndarray       # [n_layer, n_head_kv, 2, head_dim] entries written at position n_past
+    flips: int = 0           # followed entries that took the other bf16 neighbour
 
 
-def step(model: SlowModel, x: np.ndarray, kv: np.ndarray, n_past: int) -> StepResult:
+def step(model: SlowModel, x: np.ndarray, kv: np.ndarray, n_past: int,
+         follow: Optional[np.ndarray] = None) -> StepResult:
     """One Slow-AR position at index n_past over a cache holding positions
     0..n_past-1.  kv: [n_layer, n_head_kv, >= n_past, 2, head_dim] float32
-    (key then value); it is not modified."""
+    (key then value); it is not modified.  With `follow` ([n_layer,
+    n_head_kv, 2, head_dim], the entries another implementation wrote at
+    n_past) the step continues with those entries wherever they are a
+    defensible rounding of this step's values (follow_rounding), so that a
+    comparison tracks that implementation's rounding decisions."""
     s = model.shape
     H, G, hd = s.n_head, s.n_head_kv, s.head_dim
     cos, sin = _fa.rope_table(hd, n_past + 1, s.rope_base)
     cos, sin = cos[n_past:n_past + 1], sin[n_past:n_past + 1]
     x = np.asarray(x, dtype=F32)
     kv_new = np.zeros((s.n_layer, G, 2, hd), dtype=F32)
+    flips = 0
     for i in range(s.n_layer):
         a = _fa.rms_norm(x, model.layer(i, "attention_norm"), s.norm_eps)
         qkv = _fa.linear(a, model.layer(i, "attention.wqkv"))
@@ -193,8 +241,13 @@ def step(model: SlowModel, x: np.ndarray, kv: np.ndarray, n_past: int) -> StepRe
             k = _fa.rms_norm(k, model.layer(i, "attention.k_norm"), s.norm_eps)
         q = _fa.apply_rope(q, cos, sin)[0]
         k = _fa.apply_rope(k, cos, sin)[0]
-        kv_new[i, :, 0] = cache_round(s, k)
-        kv_new[i, :, 1] = cache_round(s, v)
+        if follow is None:
+            kv_new[i, :, 0] = cache_round(s, k)
+            kv_new[i, :, 1] = cache_round(s, v)
+        else:
+            kv_new[i, :, 0], f0 = follow_rounding(s, k, follow[i, :, 0])
+            kv_new[i, :, 1], f1 = follow_rounding(s, v, follow[i, :, 1])
+            flips += f0 + f1
         K = np.concatenate([kv[i, :, :n_past, 0], kv_new[i, :, None, 0]], axis=1)
         V = np.concatenate([kv[i, :, :n_past, 1], kv_new[i, :, None, 1]], axis=1)
         o = attend(q, K, V)
@@ -204,10 +257,10 @@ def step(model: SlowModel, x: np.ndarray, kv: np.ndarray, n_past: int) -> StepRe
         x = (x + _fa.linear(g, model.layer(i, "feed_forward.w2"))).astype(F32)
     h = _fa.rms_norm(x, model.get("norm"), s.norm_eps).astype(F32)
     logits = _fa.linear(h, model.get("embeddings")).astype(F32)
-    return StepResult(h, logits, kv_new)
+    return StepResult(h, logits, kv_new, flips)
 
 
-def prefill(model: SlowModel, tokens, kv: np.ndarray, n_past0: int):
+def prefill(model: SlowModel, tokens, kv: np.ndarray, n_past0: int, follow: Optional[np.ndarray] = None):
     """The prompt's positions n_past0 .. n_past0 + T - 1 (tokens [T, 1 +
     num_codebooks]: row-0 token, then the codebook codes) through the cached
     step in order; `kv` receives every new entry.  Returns the last
@@ -217,10 +270,13 @@ def prefill(model: SlowModel, tokens, kv: np.ndarray, n_past0: int):
     logits)."""
     tokens = np.asarray(tokens, dtype=np.int64)
     st = None
+    flips = 0
     for t in range(tokens.shape[0]):
         x = combine(model, tokens[t, 0], tokens[t, 1:])
-        st = step(model, x, kv, n_past0 + t)
+        st = step(model, x, kv, n_past0 + t, None if follow is None else follow[:, :, t])
         kv[:, :, n_past0 + t] = st.kv_new
+        flips += st.flips
+    st.flips = flips
     return st
 
 
@@ -234,21 +290,30 @@ class MainDraw:
     first: int               # the draw before any repetition resample
     resampled: bool
     fragile: bool
+    alts: tuple = ()         # every defensible main token (see sampler.sample)
 
 
 def draw_main(shape, logits: np.ndarray, window: List[int], temperature, top_p, top_k,
               u_main, u_ras) -> MainDraw:
     """Main token from logits + sem_mask; a semantic token already in
     `window` is redrawn at temperature 1.0 / top_p 0.9 (main-loop page,
-    sections 5 and 6).  `window` is not modified."""
+    sections 5 and 6).  `window` is not modified.  The defensible tokens
+    follow each defensible first draw through the repetition check."""
     masked = (np.asarray(logits, dtype=F32) + sem_mask(shape)).astype(F32)
     d = _sampler.sample(masked, temperature, top_p, top_k, u_main)
-    first, fragile = d.code, d.fragile
-    tok, resampled = first, False
-    if shape.sem_begin <= first <= shape.sem_end and first in window:
+    repeats = lambda t: shape.sem_begin <= t <= shape.sem_end and t in window
+    d2 = None
+    if any(repeats(a) for a in d.alts):
         d2 = _sampler.sample(masked, F32(RAS_TEMPERATURE), F32(RAS_TOP_P), top_k, u_ras)
-        tok, resampled, fragile = d2.code, True, fragile or d2.fragile
-    return MainDraw(int(tok), int(first), resampled, bool(fragile))
+    first = d.code
+    tok, resampled = first, False
+    if repeats(first):
+        tok, resampled = d2.code, True
+    alts = set()
+    for a in d.alts:
+        alts |= set(d2.alts) if repeats(a) else {a}
+    alts = tuple(sorted(alts))
+    return MainDraw(int(tok), int(first), resampled, len(alts) > 1, alts)
 
 
 def push_window(window: List[int], token: int) -> List[int]:
@@ -271,19 +336,34 @@ class FrameResult:
     kv_new: np.ndarray
     window: List[int]
     logits: np.ndarray       # [vocab] unmasked
+    fast_alts: list = None   # [n_steps] tuples: every defensible code of each Fast-AR draw
 
 
 def decode_frame(slow: SlowModel, fast: "_fa.Model", kv: np.ndarray, n_past: int, prev_main: int, prev_codes,
-                 window: List[int], u_slow, u_fast, temperature, top_p, top_k) -> FrameResult:
+                 window: List[int], u_slow, u_fast, temperature, top_p, top_k,
+                 follow: Optional[np.ndarray] = None, main_token: Optional[int] = None,
+                 fast_codes=None) -> FrameResult:
     """One Dual-AR frame: the Slow-AR step on the previous frame's 11 values,
     the main-token draw with repetition check, then the nine Fast-AR draws
-    (main-loop page, section 5.1)."""
+    (main-loop page, section 5.1).
+
+    To compare another implementation's frame along its own path: `follow`
+    takes its new cache entries (see step), `main_token` its main token
+    (which must be one of the draw's defensible tokens) and `fast_codes` its
+    Fast-AR codes, which then form the prefixes of the Fast-AR draws
+    (teacher forcing; the draws and their defensible codes are reported)."""
     x = combine(slow, prev_main, prev_codes)
-    st = step(slow, x, kv, n_past)
+    st = step(slow, x, kv, n_past, follow)
     md = draw_main(slow.shape, st.logits, window, temperature, top_p, top_k, u_slow[0], u_slow[1])
-    sc = sem_code(slow.shape, md.token)
+    tok = md.token
+    if main_token is not None:
+        tok = int(main_token)
+        if tok not in md.alts:
+            raise AssertionError(f"main token {tok} is not defensible (oracle {md.token}, defensible {md.alts})")
+    sc = sem_code(slow.shape, tok)
     one = lambda v, dt: np.asarray([v], dtype=dt)
+    forced = None if fast_codes is None else np.asarray(fast_codes, dtype=np.int64).reshape(1, -1)
     fr = _fa.decode_frame(fast, st.hidden[None, :], one(sc, np.int64), np.asarray(u_fast, F32)[None, :],
-                          one(temperature, F32), one(top_p, F32), one(top_k, np.int64))
+                          one(temperature, F32), one(top_p, F32), one(top_k, np.int64), forced=forced)
     return FrameResult(md, sc, st.hidden, fr.codes[0], fr.fragile[0], st.kv_new,
-                       push_window(window, md.token), st.logits)
+                       push_window(window, tok), st.logits, fr.alts[0])

@@ -62,32 +62,83 @@ def check_logits(p: Pair, hidden: np.ndarray, codes: np.ndarray):
     ref = fa.decode_frame(p.oracle, hidden, codes[:, 0], np.full((len(codes), p.shape.n_steps), 0.5, np.float32),
                           np.zeros(len(codes), np.float32), np.ones(len(codes), np.float32),
                           np.full(len(codes), 30, np.int32), forced=codes).logits
-    worst, worst_rel = 0.0, 0.0
-    for b in range(len(codes)):
-        for k in range(p.shape.n_steps):
-            d = float(np.max(np.abs(got[b, k] - ref[b, k])))
-            worst = max(worst, d / logit_tolerance(ref[b, k]))
-            worst_rel = max(worst_rel, d / float(np.max(np.abs(ref[b, k]))))
+    worst, worst_rel = logit_errors(got, ref)
     return worst, worst_rel, got, ref
 
 
-def check_codes(p: Pair, hidden, sem, uniforms, temperature, top_p, top_k, gpu_codes):
-    """Walk the oracle along the GPU's codes.  A step must match exactly
-    unless the oracle reports that decision as a knife-edge; after an excused
-    difference the walk continues on the GPU's code.  Returns the number of
-    excused steps; raises AssertionError on a real mismatch."""
+def logit_errors(got: np.ndarray, ref: np.ndarray):
+    """Worst |delta| / tolerance and worst |delta| / max|logit| over calls."""
+    worst, worst_rel = 0.0, 0.0
+    for b in range(ref.shape[0]):
+        for k in range(ref.shape[1]):
+            d = float(np.max(np.abs(got[b, k] - ref[b, k])))
+            worst = max(worst, d / logit_tolerance(ref[b, k]))
+            worst_rel = max(worst_rel, d / float(np.max(np.abs(ref[b, k]))))
+    return worst, worst_rel
+
+
+# At most this share of draws may come out as the oracle's alternative
+# rather than its own code (plus one).  The GPU's logits differ from the
+# oracle's by about 1e-6 of their largest magnitude, a hundred times less
+# than the smallest margin, so a legitimate flip is rare even among the
+# draws the oracle marks.
+EXCUSED_SHARE = 0.02
+
+
+@dataclass
+class FrameReport:
+    draws: int = 0         # decode steps compared
+    marked: int = 0        # draws with more than one defensible code
+    excused: int = 0       # draws where the GPU took a defensible alternative
+    worst: float = 0.0     # worst |delta logit| / tolerance
+    worst_rel: float = 0.0  # worst |delta logit| / max|logit|
+
+    def add(self, o: "FrameReport") -> "FrameReport":
+        return FrameReport(self.draws + o.draws, self.marked + o.marked, self.excused + o.excused,
+                           max(self.worst, o.worst), max(self.worst_rel, o.worst_rel))
+
+    def assert_ok(self, rel_bound: float):
+        assert self.excused <= self.marked, self
+        assert self.excused <= EXCUSED_SHARE * self.draws + 1, self
+        assert self.worst <= 1.0 and self.worst_rel < rel_bound, self
+
+
+def check_frame(p: Pair, hidden, sem, uniforms, temperature, top_p, top_k, gpu_codes,
+                logits: bool = True, one_by_one: bool = False) -> FrameReport:
+    """One frame of B requests decoded on the GPU, against one oracle pass
+    teacher-forced along the GPU's own codes: at every step the oracle
+    computes the logits of the GPU's prefix and the draw from them, and the
+    GPU's code must be one of that draw's defensible codes (the oracle's own
+    code unless a decision sits within a margin).  With `logits`, the GPU's
+    teacher-forced logits of the same prefixes are compared with the
+    oracle's; `one_by_one` runs them one request per call (the batch-1
+    kernel) instead of as one batch.  Raises AssertionError on a code
+    outside the set."""
     V = p.shape.codebook_size
-    excused = 0
-    for b in range(len(gpu_codes)):
-        c0 = int(np.clip(sem[b], 0, V - 1))
-        assert gpu_codes[b, 0] == c0, (b, gpu_codes[b, 0], c0)
-        prefix = [c0]
+    gpu_codes = np.asarray(gpu_codes)
+    B = len(gpu_codes)
+    c0 = np.clip(np.asarray(sem, np.int64), 0, V - 1)
+    assert np.array_equal(gpu_codes[:, 0], c0), (gpu_codes[:, 0], c0)
+    ref = fa.decode_frame(p.oracle, hidden, sem, uniforms, temperature, top_p, top_k, forced=gpu_codes)
+    rep = FrameReport()
+    for b in range(B):
         for k in range(1, p.shape.num_codebooks):
-            lg = fa.fast_forward(p.oracle, hidden[b:b + 1], np.array([prefix]))[0]
-            d = sm.sample(lg, temperature[b], top_p[b], top_k[b], uniforms[b][k - 1])
             g = int(gpu_codes[b, k])
-            if g != d.code:
-                assert d.fragile, f"request {b} step {k}: gpu {g} oracle {d.code} (not a knife-edge)"
-                excused += 1
-            prefix.append(g)
-    return excused
+            alts = ref.alts[b][k - 1]
+            assert g in alts, f"request {b} step {k}: gpu {g}, oracle {ref.codes[b, k]}, defensible {alts}"
+            rep.draws += 1
+            rep.marked += len(alts) > 1
+            rep.excused += g != int(ref.codes[b, k])
+    if logits:
+        gc = gpu_codes.astype(np.int32)
+        if one_by_one:
+            got = np.concatenate([gpu_forward_logits(p, hidden[b:b + 1], gc[b:b + 1]) for b in range(B)])
+        else:
+            got = gpu_forward_logits(p, hidden, gc)
+        rep.worst, rep.worst_rel = logit_errors(got, ref.logits)
+    return rep
+
+
+def check_codes(p: Pair, hidden, sem, uniforms, temperature, top_p, top_k, gpu_codes):
+    """Codes only (see check_frame); returns the number of excused draws."""
+    return check_frame(p, hidden, sem, uniforms, temperature, top_p, top_k, gpu_codes, logits=False).excused

@@ -3,17 +3,19 @@ with the oracle, on the GPU.
 
 Tolerances (float32 accumulation in another order than the oracle's):
   logits: |delta| <= 1e-2 * max|logit| + 1e-3 (the Fast-AR logit bound);
-  hidden: |delta| <= 1e-2 * max|hidden| + 1e-3, the logit bound: new cache
-    entries are rounded to bf16, and where the two sides' float32 keys or
-    values differ in the last bits the rounding can land one bf16 ulp
-    (2^-8 relative) apart; with few cached positions the attention output is
-    those rounded values themselves, and 36 layers compound the flips
-    (at the measured shape and position 0 the hidden state differs by up to
-    0.2 % of its largest element);
-  new cache entries: the same bound relative to their largest magnitude
-    (they carry the same rounding flips, one bf16 ulp each);
-  main token and codes: equal unless the oracle reports a knife-edge draw,
-  and then inside the allowed set."""
+  hidden: |delta| <= 1e-3 * max|hidden| + 1e-4;
+  new cache entries: bf16 caches round each float32 key and value, and where
+    the two sides' float32 values differ in the last bits a value next to a
+    rounding midpoint may round either way (one bf16 ulp, 2^-8 relative).
+    The oracle checks every GPU entry element by element (it must be the
+    oracle's rounding, or the other neighbour of a value within 1e-4 of a
+    midpoint) and then continues with the GPU's entries, so one such flip
+    is not compounded over 36 layers (a CPU test shows those flips alone
+    move the hidden state by about 1e-3 of its largest element at position
+    0); float32 caches are compared within the hidden-state bound;
+  main token and codes: the oracle's, or one of the draw's defensible
+  alternatives (then the comparison follows the GPU's draw), with the
+  excused count bounded."""
 import numpy as np
 import pytest
 import torch
@@ -26,7 +28,8 @@ from synth import slow_inputs as ssi
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
-HIDDEN_RTOL, HIDDEN_ATOL = 1e-2, 1e-3
+HIDDEN_RTOL, HIDDEN_ATOL = 1e-3, 1e-4
+EXCUSED_SHARE = 0.02    # excused draws at most this share of all draws, plus one
 
 
 def _announce(msg):
@@ -90,6 +93,14 @@ def _window_dev(win):
     return _i32(w)
 
 
+def _check_new_entries(s, gpu_new, oracle_new):
+    """float32 caches: the GPU's new entries within the hidden-state bound
+    (bf16 caches were checked entry by entry while the oracle followed them)."""
+    if s.weight_dtype != "bf16":
+        d = np.abs(gpu_new - oracle_new).max()
+        assert d <= HIDDEN_RTOL * np.abs(oracle_new).max() + HIDDEN_ATOL, d
+
+
 def _check_step(p, n_past, main, codes, win, u, T=0.8, top_p=0.8, top_k=30, seed=77):
     s = p.shape
     kv_host, kv_f = _host_kv(s, n_past, seed)
@@ -100,7 +111,9 @@ def _check_step(p, n_past, main, codes, win, u, T=0.8, top_p=0.8, top_k=30, seed
     m_out, sem_out, h_out = p.gpu.step(kv, n_past, _i32([main]), _i32(codes), window, _f32(u), _f32([T]),
                                        _f32([top_p]), _i32([top_k]), logits_out=logits)
     torch.cuda.synchronize()
-    st = sa.step(p.oracle, sa.combine(p.oracle, main, codes), kv_f, n_past)
+    kv_after = _kv_f32(kv)
+    st = sa.step(p.oracle, sa.combine(p.oracle, main, codes), kv_f, n_past, follow=kv_after[:, :, n_past])
+    _check_new_entries(s, kv_after[:, :, n_past], st.kv_new)
     ids = sa.allowed_ids(s)
     assert ids.size == p.gpu.n_allowed
     ref = st.logits[ids]
@@ -108,21 +121,20 @@ def _check_step(p, n_past, main, codes, win, u, T=0.8, top_p=0.8, top_k=30, seed
     tol = 1e-2 * np.abs(ref).max() + 1e-3
     assert np.abs(got - ref).max() <= tol, (np.abs(got - ref).max(), tol)
     h = h_out.cpu().numpy()
-    assert np.abs(h - st.hidden).max() <= HIDDEN_RTOL * np.abs(st.hidden).max() + HIDDEN_ATOL
-    kv_after = _kv_f32(kv)
-    dkv = np.abs(kv_after[:, :, n_past] - st.kv_new).max()
-    assert dkv <= HIDDEN_RTOL * np.abs(st.kv_new).max() + HIDDEN_ATOL, dkv
+    dh = np.abs(h - st.hidden).max()
+    assert dh <= HIDDEN_RTOL * np.abs(st.hidden).max() + HIDDEN_ATOL, (dh, st.flips)
     # every other position is untouched
     assert np.array_equal(np.delete(kv_after, n_past, axis=2), np.delete(kv_f, n_past, axis=2), equal_nan=True)
     md = sa.draw_main(s, st.logits, list(win), T, top_p, top_k, u[0], u[1])
     tok = int(m_out.item())
-    if not md.fragile:
-        assert tok == md.token, (tok, md)
+    assert tok in md.alts, (tok, md)
     assert tok in set(ids.tolist())
     assert int(sem_out.item()) == sa.sem_code(s, tok)
     w = window.cpu().numpy()
     want = sa.push_window(list(win), tok)
     assert w[0] == len(want) and list(w[1:1 + w[0]]) == want
+    _announce(f"  rounding flips followed {st.flips}, |dh|/max {dh / np.abs(st.hidden).max():.1e}, "
+              f"main {'excused' if tok != md.token else 'exact'}")
     return md, tok
 
 
@@ -200,7 +212,11 @@ def test_slow_step_rejects_bad_arguments(slow_tiny):
 
 def _full_frames(p, fast_pair, n_frames, n_fill, u_slow, u_fast, main0, codes0, T, top_p, top_k=30):
     """Chained frames on the device (each frame's outputs feed the next)
-    against the oracle's frame loop."""
+    against the oracle's frame loop, which follows the GPU's path: its new
+    cache entries (checked entry by entry), its main token (one of the
+    draw's defensible tokens) and its Fast-AR codes (each one of its draw's
+    defensible codes, teacher-forced as the next prefix).  Returns (draws,
+    excused)."""
     s = p.shape
     kv_host, kv_f = _host_kv(s, n_fill + n_frames, 91)
     kv_host[:, :, n_fill:] = 0x7FC0 if s.weight_dtype == "bf16" else np.nan
@@ -211,34 +227,35 @@ def _full_frames(p, fast_pair, n_frames, n_fill, u_slow, u_fast, main0, codes0, 
     hid = torch.empty(s.dim, dtype=torch.float32, device="cuda")
     o_main, o_codes, o_win = int(main0), np.asarray(codes0), []
     allowed = set(sa.allowed_ids(s).tolist())
-    exact = fragile = 0
+    draws = excused = 0
     for f in range(n_frames):
         _announce(f"full frame {s.name} frame {f}")
+        pos = n_fill + f
         m_new = torch.empty(1, dtype=torch.int32, device="cuda")
         c_new = torch.empty(s.num_codebooks, dtype=torch.int32, device="cuda")
-        p.gpu.full_frame(fast_pair.gpu, kv, n_fill + f, main_d, codes_d, window, _f32(u_slow[f]), _f32(u_fast[f]),
+        p.gpu.full_frame(fast_pair.gpu, kv, pos, main_d, codes_d, window, _f32(u_slow[f]), _f32(u_fast[f]),
                          _f32([T]), _f32([top_p]), _i32([top_k]), main_out=m_new, hidden_out=hid, codes_out=c_new)
         torch.cuda.synchronize()
-        r = sa.decode_frame(p.oracle, fast_pair.oracle, kv_f, n_fill + f, o_main, o_codes, o_win, u_slow[f],
-                            u_fast[f], T, top_p, top_k)
         tok, codes = int(m_new.item()), c_new.cpu().numpy()
+        assert tok in allowed and codes.min() >= 0 and codes.max() < s.codebook_size
+        gpu_new = _kv_f32(kv)[:, :, pos]
+        r = sa.decode_frame(p.oracle, fast_pair.oracle, kv_f, pos, o_main, o_codes, o_win, u_slow[f], u_fast[f],
+                            T, top_p, top_k, follow=gpu_new, main_token=tok, fast_codes=codes)
+        _check_new_entries(s, gpu_new, r.kv_new)
         h = hid.cpu().numpy()
         assert np.abs(h - r.hidden).max() <= HIDDEN_RTOL * np.abs(r.hidden).max() + HIDDEN_ATOL
-        assert tok in allowed and codes.min() >= 0 and codes.max() < s.codebook_size
-        if r.main.fragile:
-            fragile += 1              # a knife-edge main draw: the GPU's token is followed below
-        else:
-            assert tok == r.main.token, (f, tok, r.main)
-            # codes up to the first knife-edge Fast-AR draw are exact
-            k = 1 + int(np.argmax(r.fast_fragile)) if r.fast_fragile.any() else s.num_codebooks
-            assert np.array_equal(codes[:k], r.codes[:k]), (f, codes, r.codes, r.fast_fragile)
-            exact += k
-        kv_f[:, :, n_fill + f] = r.kv_new
+        assert codes[0] == r.sem_code
+        for k in range(1, s.num_codebooks):
+            assert codes[k] in r.fast_alts[k - 1], (f, k, codes, r.codes, r.fast_alts[k - 1])
+            excused += int(codes[k] != r.codes[k])
+        draws += s.num_codebooks
+        excused += int(tok != r.main.token)
+        kv_f[:, :, pos] = r.kv_new
         # the next frame starts from the GPU's draws on both sides
         o_main, o_codes, o_win = tok, codes, sa.push_window(o_win, tok)
         main_d, codes_d = m_new, c_new
-    assert _kv_f32(kv)[:, :, n_fill:n_fill + n_frames].shape[2] == n_frames
-    return exact, fragile
+    assert excused <= EXCUSED_SHARE * draws + 1, (excused, draws)
+    return draws, excused
 
 
 class FastPair:
@@ -251,18 +268,18 @@ def test_full_frame_tiny(slow_tiny):
     fast = FastPair(si.TINY, si.WORKLOADS["tiny"].seed(0))
     w = ssi.SLOW_WORKLOADS["slow_tiny"]
     inp = ssi.make_step_inputs(w, 4)
-    exact, fragile = _full_frames(slow_tiny, fast, 4, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
+    draws, excused = _full_frames(slow_tiny, fast, 4, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
                                   inp["codes"][0], 0.8, 0.8)
-    assert exact >= 10 and fragile <= 1
+    _announce(f"full frames tiny: {draws} draws, {excused} excused")
 
 
 def test_full_frame_ragged(slow_ragged):
     fast = FastPair(si.RAGGED, si.WORKLOADS["ragged"].seed(0))
     w = ssi.SLOW_WORKLOADS["slow_ragged"]
     inp = ssi.make_step_inputs(w, 3)
-    exact, fragile = _full_frames(slow_ragged, fast, 3, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
+    draws, excused = _full_frames(slow_ragged, fast, 3, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
                                   inp["codes"][0], 0.9, 0.85)
-    assert exact >= 10 and fragile <= 1
+    _announce(f"full frames {w.name}: {draws} draws, {excused} excused")
 
 
 @pytest.fixture(scope="module")
@@ -317,22 +334,22 @@ def _check_prefill(p, n_past0, toks, win, u, T_=0.8, top_p=0.8, top_k=30, seed=5
                                           _f32([top_p]), _i32([top_k]), logits_out=logits)
     torch.cuda.synchronize()
     kv_before = kv_f.copy()
-    st = sa.prefill(p.oracle, toks, kv_f, n_past0)
+    kv_after = _kv_f32(kv)
+    new = slice(n_past0, n_past0 + T)
+    st = sa.prefill(p.oracle, toks, kv_f, n_past0, follow=kv_after[:, :, new])
+    _check_new_entries(s, kv_after[:, :, new], kv_f[:, :, new])
     ref = st.logits[sa.allowed_ids(s)]
     got = logits.cpu().numpy()
     assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max() + 1e-3
     h = h_out.cpu().numpy()
-    assert np.abs(h - st.hidden).max() <= HIDDEN_RTOL * np.abs(st.hidden).max() + HIDDEN_ATOL
-    kv_after = _kv_f32(kv)
-    new = slice(n_past0, n_past0 + T)
-    dkv = np.abs(kv_after[:, :, new] - kv_f[:, :, new]).max()
-    assert dkv <= HIDDEN_RTOL * np.abs(kv_f[:, :, new]).max() + HIDDEN_ATOL, dkv
+    dh = np.abs(h - st.hidden).max()
+    assert dh <= HIDDEN_RTOL * np.abs(st.hidden).max() + HIDDEN_ATOL, (dh, st.flips)
     keep = np.r_[0:n_past0, n_past0 + T:s.max_ctx]
     assert np.array_equal(kv_after[:, :, keep], kv_before[:, :, keep], equal_nan=True)
     md = sa.draw_main(s, st.logits, list(win), T_, top_p, top_k, u[0], u[1])
     tok = int(m_out.item())
-    if not md.fragile:
-        assert tok == md.token, (tok, md)
+    assert tok in md.alts, (tok, md)
+    _announce(f"  rounding flips followed {st.flips}, |dh|/max {dh / np.abs(st.hidden).max():.1e}")
     assert tok in set(sa.allowed_ids(s).tolist())
     assert int(sem_out.item()) == sa.sem_code(s, tok)
     w = window.cpu().numpy()
@@ -382,9 +399,9 @@ def test_full_frame_s2pro_full_size(slow_s2pro):
     fast = FastPair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0))
     w = ssi.SLOW_WORKLOADS["full_s2pro"]
     inp = ssi.make_step_inputs(w, 2)
-    exact, fragile = _full_frames(slow_s2pro, fast, 2, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
+    draws, excused = _full_frames(slow_s2pro, fast, 2, w.n_fill, inp["u_slow"], inp["u_fast"], inp["main"][0],
                                   inp["codes"][0], 0.8, 0.8)
-    assert exact >= 10 and fragile <= 1
+    _announce(f"full frames {w.name}: {draws} draws, {excused} excused")
     fast.gpu.close()
 
 

@@ -111,3 +111,86 @@ def test_deterministic():
     a = [sm.sample(l, 0.8, 0.8, 30, np.float32(u)).code for u in (0.1, 0.5, 0.9)]
     b = [sm.sample(l, 0.8, 0.8, 30, np.float32(u)).code for u in (0.1, 0.5, 0.9)]
     assert a == b
+
+
+# ------------------------------------------------------------ knife-edges
+# The parity tests accept a GPU code that differs from the oracle's only if
+# it is in the draw's reported set of defensible codes.  These pins check
+# that set against its meaning: a draw on logits that differ by far less
+# than the margins (1e-3 / 1e-4) always lands in it, and it is the code
+# alone where no decision is near a margin.
+
+def _perturb(l, rng, eps):
+    return (l.astype(np.float64) + rng.uniform(-eps, eps, l.size)).astype(np.float32)
+
+
+def _knife_edge_logits(rng, kind, T, n):
+    """Logits with one decision placed a few 1e-6 from its margin."""
+    V = int(rng.integers(n + 5, 600))
+    l = (rng.standard_normal(V) * rng.uniform(0.5, 3.0)).astype(np.float32)
+    order = np.argsort(-l, kind="stable")
+    if kind == "greedy":
+        l[order[1]] = l[order[0]] - np.float32(3e-6)
+    elif kind == "boundary":                     # ranks n-1 and n nearly equal
+        l[order[n]] = l[order[n - 1]] - np.float32(3e-6)
+    elif kind == "order":                        # two candidates inside the set nearly equal
+        j = int(rng.integers(0, n - 1))
+        l[order[j + 1]] = l[order[j]] - np.float32(3e-6)
+    return l
+
+
+def test_defensible_set_covers_perturbed_draws():
+    rng = np.random.default_rng(2024)
+    changed = fragile = 0
+    for it in range(360):
+        kind = ("random", "greedy", "boundary", "order", "topp", "race")[it % 6]
+        T = np.float32(0.0 if kind == "greedy" else rng.uniform(0.5, 1.2))
+        n = int(rng.integers(2, 40))
+        u = np.float32((rng.integers(0, 1 << 23) + 0.5) * 2.0 ** -23)
+        l = _knife_edge_logits(rng, kind, T, n)
+        tp = np.float32(rng.uniform(0.3, 0.99))
+        if kind == "topp":
+            # top_p a hair above a running sum: the cut sits on the margin
+            d0 = sm.sample(l, T, np.float32(1.0), n, u)
+            z = (l[d0.ranks] / T).astype(np.float32)
+            e = np.exp((z - z[0]).astype(np.float64)).astype(np.float32)
+            c = np.cumsum((e / np.float32(e.sum(dtype=np.float32))).astype(np.float64))
+            j = int(rng.integers(0, max(1, len(c) - 1)))
+            tp = np.float32(c[j] + 2e-6)
+        if kind == "race":
+            # two race keys equal: ranks 0 and 1 with l1 = l0 + T log(E1 / E0)
+            order = np.argsort(-l, kind="stable")
+            E0, E1 = sm.candidate_exponential(u, 0), sm.candidate_exponential(u, 1)
+            if E1 < E0:
+                l[order[1]] = np.float32(float(l[order[0]]) + float(T) * np.log(float(E1) / float(E0)))
+            tp = np.float32(1.0)
+        d = sm.sample(l, T, tp, n, u)
+        assert d.code in d.alts and d.fragile == (len(d.alts) > 1)
+        fragile += d.fragile
+        for _ in range(6):
+            got = sm.sample(_perturb(l, rng, 2e-5), T, tp, n, u).code
+            assert got in d.alts, (it, kind, got, d.code, d.alts)
+            changed += got != d.code
+    # the cases do reach the knife-edges: many draws are fragile and the
+    # perturbations do move some of them
+    assert fragile > 80 and changed > 20, (fragile, changed)
+
+
+def test_defensible_set_is_the_code_alone_away_from_margins():
+    # linearly spaced logits (gaps 0.05), whole nucleus: only a race tie could add a code
+    l = np.linspace(3.0, -3.0, 121).astype(np.float32)
+    rng = np.random.default_rng(4)
+    alone = 0
+    for it in range(200):
+        u = np.float32((rng.integers(0, 1 << 23) + 0.5) * 2.0 ** -23)
+        d = sm.sample(l, np.float32(0.9), np.float32(1.0), 30, u)
+        alone += d.alts == (d.code,)
+    assert alone >= 195
+    g = sm.sample(l, 0.0, 0.8, 30, 0.5)
+    assert g.alts == (0,) and not g.fragile
+
+
+def test_greedy_defensible_set():
+    l = np.array([0.0, 1.0, 0.9995, 0.998, 1.0, -2.0], np.float32)
+    d = sm.sample(l, 0.0, 0.8, 30, 0.5)
+    assert d.code == 1 and d.alts == (1, 2, 4)   # within 1e-3 of the maximum, not 0.998

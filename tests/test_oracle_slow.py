@@ -255,3 +255,70 @@ def test_prefill_equals_full_causal_forward(tiny):
     sa.prefill(tiny, toks[:4], kv2, 0)
     st2 = sa.prefill(tiny, toks[4:], kv2, 4)
     np.testing.assert_array_equal(st2.hidden, st.hidden)
+
+
+# ------------------------------------------------------------ rounding follow
+# A bf16 cache rounds every new key and value.  Two implementations whose
+# float32 values differ in the last bits can round a value that sits next to
+# a rounding midpoint to different neighbours; the oracle then follows the
+# other implementation's entry, after checking it is such a rounding.
+
+def _deep_mid_shape():
+    from dataclasses import replace
+    return replace(ssi.SLOW_MID, name="deep_mid", n_layer=36)
+
+
+def test_rounding_flips_compound_over_36_layers_and_following_removes_them():
+    """At position 0 the attention output is the rounded value itself, so
+    flips feed straight into the residual stream.  Emulate an implementation
+    whose float32 keys/values differ by ~1e-6 relative before rounding: a few
+    entries round the other way, the hidden state moves by about 1e-3 of its
+    largest element (more than a 1e-3 * max + 1e-4 bound allows room for),
+    and following its entries reproduces its hidden state exactly."""
+    shp = _deep_mid_shape()
+    m = sa.SlowModel.from_weights(shp, ssi.make_weights(shp, 7))
+    kv = np.zeros((shp.n_layer, shp.n_head_kv, 1, 2, shp.head_dim), np.float32)
+    x = sa.combine(m, shp.sem_begin + 3, np.arange(shp.num_codebooks))
+    own = sa.step(m, x, kv, 0)
+    rng = np.random.default_rng(1)
+    exact_round = sa.cache_round
+
+    def other(s, v):
+        v = np.asarray(v, np.float32)
+        return exact_round(s, (v.astype(np.float64) * (1 + rng.standard_normal(v.shape) * 1e-6)).astype(np.float32))
+
+    sa.cache_round = other
+    try:
+        theirs = sa.step(m, x, kv, 0)
+    finally:
+        sa.cache_round = exact_round
+    followed = sa.step(m, x, kv, 0, follow=theirs.kv_new)
+    M = float(np.abs(theirs.hidden).max())
+    assert followed.flips >= 1
+    assert float(np.abs(own.hidden - theirs.hidden).max()) > 5e-4 * M
+    assert np.array_equal(followed.hidden, theirs.hidden)
+    assert np.array_equal(followed.kv_new, theirs.kv_new)
+
+
+def test_follow_rounding_accepts_only_defensible_entries():
+    s = ssi.SLOW_MID                                   # bf16 cache
+    lo = np.float32(1.0)                               # bf16 neighbours 1.0 and 1.0078125
+    hi = np.float32(1.0078125)
+    mid = (np.float64(lo) + np.float64(hi)) / 2
+    near = np.float32(mid * (1 + 3e-5))                # rounds to hi; within the band of the midpoint
+    far = np.float32(1.002)                            # rounds to lo; far from the midpoint
+    exact = np.array([near, far, -near], np.float32)
+    mine = sa.cache_round(s, exact)
+    assert list(mine) == [hi, lo, -hi]
+    got, flips = sa.follow_rounding(s, exact, mine)
+    assert flips == 0 and np.array_equal(got, mine)
+    got, flips = sa.follow_rounding(s, exact, np.array([lo, lo, -lo], np.float32))   # near-midpoint flips
+    assert flips == 2 and list(got) == [lo, lo, -lo]
+    for bad in ([lo, hi, -hi],                         # a flip away from any midpoint
+                [np.float32(1.015625), lo, -hi],       # two ulps off
+                [hi, lo, np.float32(1.0078125)]):      # wrong sign
+        with pytest.raises(sa.CacheFollowError):
+            sa.follow_rounding(s, exact, np.array(bad, np.float32))
+    # float32 caches are not rounded: the oracle keeps its own values
+    got, flips = sa.follow_rounding(ssi.SLOW_TINY, exact, exact + 1)
+    assert flips == 0 and np.array_equal(got, exact)
