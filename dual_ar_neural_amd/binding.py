@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from typing import Dict, Optional, Sequence
 
 import torch
@@ -114,6 +115,20 @@ def library() -> ctypes.CDLL:
         lib.s2fast_slow_allowed.restype = ctypes.c_int
         lib.s2fast_test_slow_timeline.argtypes = [P, I, P, I]
         lib.s2fast_test_slow_timeline.restype = ctypes.c_int
+        lib.s2fast_fast_decode.argtypes = [P, I, P, I, P, I, P, V]
+        lib.s2fast_fast_decode.restype = ctypes.c_int
+        lib.s2fast_status.argtypes = [P, V]
+        lib.s2fast_status.restype = ctypes.c_int
+        lib.s2fast_slow_status.argtypes = [P, V]
+        lib.s2fast_slow_status.restype = ctypes.c_int
+        lib.s2fast_test_watchdog.argtypes = [P, I]
+        lib.s2fast_test_watchdog.restype = ctypes.c_int
+        lib.s2fast_test_slow_watchdog.argtypes = [P, I]
+        lib.s2fast_test_slow_watchdog.restype = ctypes.c_int
+        lib.s2fast_test_gemv.argtypes = [I, I, I, I, P, P, P, F, P, P, V]
+        lib.s2fast_test_gemv.restype = ctypes.c_int
+        lib.s2fast_test_norm_rope_attn.argtypes = [I, I, I, I, I, F, F, P, P, P, P, V]
+        lib.s2fast_test_norm_rope_attn.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -122,7 +137,8 @@ EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_
            "s2fast_forward_logits", "s2fast_test_rope_table", "s2fast_test_sample",
            "s2fast_syncs_per_frame", "s2fast_test_timeline", "s2fast_slow_create", "s2fast_slow_destroy",
            "s2fast_slow_step", "s2fast_slow_prefill", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed",
-           "s2fast_test_slow_timeline")
+           "s2fast_test_slow_timeline", "s2fast_fast_decode", "s2fast_status", "s2fast_slow_status",
+           "s2fast_test_watchdog", "s2fast_test_slow_watchdog", "s2fast_test_gemv", "s2fast_test_norm_rope_attn")
 
 
 def _strerror(code: int) -> str:
@@ -214,6 +230,11 @@ class FastAR:
             self._ctx = None
 
     def __del__(self):
+        # Never touch the device while the interpreter shuts down: the HIP
+        # runtime (or a profiler attached to it) may already be torn down.
+        # Close contexts explicitly; at exit the process releases them.
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
@@ -253,6 +274,32 @@ class FastAR:
                                            _stream(stream))
         _check(rc, "s2fast_decode_frame")
         return codes
+
+    def status(self, stream=None) -> int:
+        """S2FAST_OK, or S2FAST_ERR_HIP if a launch on this context gave up
+        a grid-wide wait since the last call (waits for the stream)."""
+        return library().s2fast_status(self._ctx, _stream(stream))
+
+    def test_watchdog(self, give_up: bool) -> None:
+        _check(library().s2fast_test_watchdog(self._ctx, int(give_up)), "s2fast_test_watchdog")
+
+    def fast_decode(self, hidden, prefix, logits=None, hidden_dim=None, stream=None):
+        """One Fast-AR call: logits [B, V] after `prefix` [B, k] (int32)."""
+        s = self.shape
+        B = hidden.shape[0]
+        if not (hidden.is_cuda and hidden.dtype == torch.float32 and hidden.is_contiguous() and hidden.dim() == 2):
+            raise ValueError("hidden: expected a contiguous float32 CUDA tensor [B, width]")
+        if not (prefix.is_cuda and prefix.dtype == torch.int32 and prefix.is_contiguous() and prefix.dim() == 2
+                and prefix.shape[0] == B):
+            raise ValueError("prefix: expected a contiguous int32 CUDA tensor [B, k]")
+        if logits is None:
+            logits = torch.empty((B, s.codebook_size), dtype=torch.float32, device=hidden.device)
+        _dev(logits, torch.float32, (B, s.codebook_size), "logits")
+        hd = hidden.shape[1] if hidden_dim is None else hidden_dim
+        rc = library().s2fast_fast_decode(self._ctx, B, _ptr(hidden), int(hd), _ptr(prefix), int(prefix.shape[1]),
+                                          _ptr(logits), _stream(stream))
+        _check(rc, "s2fast_fast_decode")
+        return logits
 
     def forward_logits(self, hidden, codes, logits=None, stream=None):
         s = self.shape
@@ -307,6 +354,11 @@ class SlowAR:
             self._ctx = None
 
     def __del__(self):
+        # Never touch the device while the interpreter shuts down: the HIP
+        # runtime (or a profiler attached to it) may already be torn down.
+        # Close contexts explicitly; at exit the process releases them.
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
@@ -314,6 +366,12 @@ class SlowAR:
 
     def syncs(self) -> int:
         return library().s2fast_slow_syncs(self._ctx)
+
+    def status(self, stream=None) -> int:
+        return library().s2fast_slow_status(self._ctx, _stream(stream))
+
+    def test_watchdog(self, give_up: bool) -> None:
+        _check(library().s2fast_test_slow_watchdog(self._ctx, int(give_up)), "s2fast_test_slow_watchdog")
 
     def timeline(self, enable: bool = True, fetch: bool = False):
         """Per-block phase timing of later steps (see FastAR.timeline)."""
@@ -432,3 +490,38 @@ def sample(logits, temperature, top_p, top_k, u, stream=None):
     _check(library().s2fast_test_sample(B, V, _ptr(logits), _ptr(temperature), _ptr(top_p), _ptr(top_k),
                                         _ptr(u), _ptr(codes), _stream(stream)), "s2fast_test_sample")
     return codes
+
+
+def gemv(W, x, W3=None, norm_w=None, eps: float = 1e-6, stream=None):
+    """The frame kernel's GEMV on its own (test export): y [M, N] = W . n
+    with n = x * norm_w / rms(x) if norm_w is given, or the SwiGLU pair
+    silu(W . n) * (W3 . n) if W3 is given."""
+    N, K = W.shape
+    M = x.shape[0]
+    dt = {torch.bfloat16: BF16, torch.float32: F32}[W.dtype]
+    _dev(W, W.dtype, (N, K), "W")
+    if W3 is not None:
+        _dev(W3, W.dtype, (N, K), "W3")
+    if norm_w is not None:
+        _dev(norm_w, W.dtype, (K,), "norm_w")
+    _dev(x, torch.float32, (M, K), "x")
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(library().s2fast_test_gemv(dt, N, K, M, _ptr(W), _ptr(W3), _ptr(norm_w), float(eps), _ptr(x), _ptr(y),
+                                      _stream(stream)), "s2fast_test_gemv")
+    return y
+
+
+def norm_rope_attn(qkv, n_head: int, n_head_kv: int, head_dim: int, context: int, rope_base: float, eps: float,
+                   q_norm=None, k_norm=None, stream=None):
+    """q/k RMSNorm + pair RoPE + causal attention of the frame kernel on its
+    own (test export): qkv [T, (H + 2 G) hd] raw wqkv outputs -> [T, H hd]."""
+    T = qkv.shape[0]
+    _dev(qkv, torch.float32, (T, (n_head + 2 * n_head_kv) * head_dim), "qkv")
+    for t, n in ((q_norm, "q_norm"), (k_norm, "k_norm")):
+        if t is not None:
+            _dev(t, torch.float32, (head_dim,), n)
+    out = torch.empty((T, n_head * head_dim), dtype=torch.float32, device=qkv.device)
+    _check(library().s2fast_test_norm_rope_attn(n_head, n_head_kv, head_dim, T, context, float(rope_base), float(eps),
+                                                _ptr(qkv), _ptr(q_norm), _ptr(k_norm), _ptr(out), _stream(stream)),
+           "s2fast_test_norm_rope_attn")
+    return out

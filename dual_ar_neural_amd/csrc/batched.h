@@ -72,9 +72,12 @@ struct BatchArgs {
   const float* temp;        // [Bq]
   const float* top_p;       // [Bq]
   const int* top_k;         // [Bq]
-  const int* forced;        // [Bq][ncb] or nullptr
+  const int* forced;        // [Bq][forced_ld] or nullptr
   int* codes_out;           // [Bq][ncb] or nullptr
-  float* logits_out;        // [Bq][ncb-1][V] or nullptr
+  float* logits_out;        // [Bq][lo_rows][V] or nullptr
+  int nsteps;               // decode steps this launch runs (ncb-1 for a whole frame)
+  int forced_ld;            // codes per request in `forced`
+  int lo_first, lo_rows;    // logits_out row of step s >= lo_first is s - lo_first
   // arena: every (step, layer) region written once per frame (see FrameArgs)
   float* xin0;              // [BQ_MAX][dim]
   float* x;                 // [slot][MP_MAX][dim] residual after the layer
@@ -88,7 +91,8 @@ struct BatchArgs {
   long long x_slot, qkv_slot, att_slot, g_slot, logits_slot;
   u32* flags;
   u32 epoch0;
-  u32* err;
+  u32* err;                 // watchdog words (see Watch)
+  Watch watch;
   u32* tlog;
 };
 
@@ -157,7 +161,7 @@ __device__ __forceinline__ float* bkv(const BatchArgs& a, int b, int l, int pos,
 // teacher-forced input or the code sampled at step j
 __device__ __forceinline__ int b_code(const BatchArgs& a, int b, int j) {
   int c;
-  if (a.forced) c = a.forced[(size_t)b * a.ncb + j];
+  if (a.forced) c = a.forced[(size_t)b * a.forced_ld + j];
   else if (j == 0) c = a.sem_code[b];
   else c = ld_coh(a.codes + b * 16 + j);   // one line holds codes written at different steps
   return min(max(c, 0), a.V - 1);
@@ -613,7 +617,8 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
           } else {
             const float y = d / s.rms[mp];
             st_coh(blogits(a, step) + (size_t)m * a.V + r0 + v, y);
-            if (a.logits_out) a.logits_out[((size_t)m * (a.ncb - 1) + (step - 1)) * a.V + r0 + v] = y;
+            if (a.logits_out && step >= a.lo_first)
+              a.logits_out[((size_t)m * a.lo_rows + (step - a.lo_first)) * a.V + r0 + v] = y;
           }
           break;
         }
@@ -820,7 +825,7 @@ __device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s
       for (int q = 1; q < S; ++q) v += bkpart(a, BK_HEAD, step, 0, q)[(size_t)b * a.V + i];
       v /= rd;
       lg[i] = v;
-      if (a.logits_out) a.logits_out[((size_t)b * (a.ncb - 1) + (step - 1)) * a.V + i] = v;
+      if (a.logits_out && step >= a.lo_first) a.logits_out[((size_t)b * a.lo_rows + (step - a.lo_first)) * a.V + i] = v;
     }
     __syncthreads();
     L = lg;
@@ -840,15 +845,13 @@ __device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s
 // a teacher-forced prefix a step ends at the head, unless the head is split
 // over K and the caller wants the logits (head_logits): then one sync lets
 // the sample phase assemble them.
-__host__ __device__ inline int b_syncs(int has_proj, int ncb, int n_layer, bool forced, bool head_logits) {
-  return (has_proj ? 1 : 0) + (ncb - 1) * (5 * n_layer + (forced ? (head_logits ? 1 : 0) : 2)) - (ncb - 2);
+__host__ __device__ inline int b_syncs(int has_proj, int nsteps, int n_layer, bool forced, bool head_logits) {
+  return (has_proj ? 1 : 0) + nsteps * (5 * n_layer + (forced ? (head_logits ? 1 : 0) : 2)) - (nsteps - 1);
 }
 
+// The phases of one launch; false if a barrier wait gave up.
 template <typename WT>
-__global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
-  extern __shared__ float lds_base[];
-  const BLds s = b_carve(reinterpret_cast<char*>(lds_base), a);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+__device__ __forceinline__ bool b_frame(const BatchArgs& a, const BLds& s) {
   u32 epoch = a.epoch0;
   if (a.has_qkn) {
     for (int i = tidx(); i < a.n_layer * 2 * a.hd; i += NTHREADS) {
@@ -863,9 +866,9 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
   __syncthreads();
   if (a.has_proj) {
     b_phase_gemm<WT>(a, s, BK_PROJ, 0, 0);
-    if (!grid_sync(a, epoch, s.flag)) return;
+    if (!grid_sync(a, epoch, s.flag)) return false;
   }
-  for (int step = 1; step < a.ncb; ++step) {
+  for (int step = 1; step <= a.nsteps; ++step) {
     const int M = b_rows(a, step);
     if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     for (int l = 0; l < a.n_layer; ++l) {
@@ -880,29 +883,52 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
       }
       if (l > 0 || step == 1) {   // layer 0 of later steps reads the qkv0 table in the attention phase
         b_phase_gemm<WT>(a, s, BK_QKV, step, l);
-        if (!grid_sync(a, epoch, s.flag)) return;
+        if (!grid_sync(a, epoch, s.flag)) return false;
         if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       }
       b_phase_attn<WT>(a, s, step, l);
-      if (!grid_sync(a, epoch, s.flag)) return;
+      if (!grid_sync(a, epoch, s.flag)) return false;
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       b_phase_gemm<WT>(a, s, BK_WO, step, l);
-      if (!grid_sync(a, epoch, s.flag)) return;
+      if (!grid_sync(a, epoch, s.flag)) return false;
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       b_phase_gemm<WT>(a, s, BK_UP, step, l);
-      if (!grid_sync(a, epoch, s.flag)) return;
+      if (!grid_sync(a, epoch, s.flag)) return false;
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       b_phase_gemm<WT>(a, s, BK_DOWN, step, l);
-      if (!grid_sync(a, epoch, s.flag)) return;
+      if (!grid_sync(a, epoch, s.flag)) return false;
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     }
     b_phase_gemm<WT>(a, s, BK_HEAD, step, 0);
     // teacher forcing: the next prefix is known (the sample phase then only
     // assembles a split head's logits for the caller)
     if (a.forced && !(a.ks[BK_HEAD] > 1 && a.logits_out)) continue;
-    if (!grid_sync(a, epoch, s.flag)) return;
+    if (!grid_sync(a, epoch, s.flag)) return false;
     b_phase_sample(a, s, step);
     if (a.forced) continue;
-    if (!grid_sync(a, epoch, s.flag)) return;
+    if (!grid_sync(a, epoch, s.flag)) return false;
   }
+  return true;
+}
+
+template <typename WT>
+__global__ void __launch_bounds__(NTHREADS) frame_kernel_b(BatchArgs a) {
+  extern __shared__ float lds_base[];
+  const BLds s = b_carve(reinterpret_cast<char*>(lds_base), a);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  b_frame<WT>(a, s);
+  // a barrier wait gave up: the K-split counts are cleared (the next frame
+  // counts from zero) and every request of the launch keeps its semantic
+  // code with codebooks 1.. at 0 ("Fast-AR codebook decoding ...", section
+  // 5.2)
+  launch_exit(a, s.flag, [&]() __attribute__((always_inline)) {
+    const size_t slots = (size_t)(a.ncb - 1) * a.n_layer;
+    for (int kd = 0; kd < 6; ++kd)
+      if (a.ks[kd] > 1 && a.kcnt[kd]) zero_words32(a.kcnt[kd], slots * (gridDim.x / a.ks[kd]) * KCNT_STRIDE);
+    if (a.codes_out)
+      for (int i = tidx(); i < a.Bq * a.ncb; i += NTHREADS) {
+        const int b = i / a.ncb, j = i - b * a.ncb;
+        st_coh(a.codes_out + i, j == 0 ? b_code(a, b, 0) : 0);
+      }
+  });
 }

@@ -23,6 +23,19 @@ constexpr int MMAX = 2;              // activation rows one launch processes per
 constexpr int TOPK_MAX = 64;         // sampler candidate limit (one per lane)
 constexpr u32 SPIN_LIMIT = 1u << 22; // bounded waits: far longer than any phase
 
+// A context's watchdog words (u32 offsets into one 256-word buffer, each
+// pair on separate cache lines): a barrier wait that gave up during the
+// current launch, the blocks that have left the current launch, and the
+// sticky status the host reads back.
+constexpr int W_ERR = 0, W_EXITS = 64, W_STATUS = 128, W_WORDS = 256;
+
+// Test hook carried by every launch: with give_up set, every block's first
+// barrier waits for an epoch no block publishes and gives up after one poll,
+// so the failure path runs while every block still exits normally.
+struct Watch {
+  u32 give_up;
+};
+
 __device__ __forceinline__ float ld_coh(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

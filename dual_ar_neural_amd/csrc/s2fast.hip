@@ -69,9 +69,12 @@ struct FrameArgs {
   const float* temp;       // [1]
   const float* top_p;      // [1]
   const int* top_k;        // [1]
-  const int* forced;       // [ncb] teacher-forced codes, or nullptr
+  const int* forced;       // teacher-forced codes (forced_ld of them), or nullptr
   int* codes_out;          // [ncb] or nullptr
-  float* logits_out;       // [ncb-1][V] or nullptr
+  float* logits_out;       // [lo_rows][V] or nullptr
+  int nsteps;              // decode steps this launch runs (ncb-1 for a whole frame)
+  int forced_ld;           // codes per request in `forced`
+  int lo_first, lo_rows;   // logits_out row of step s >= lo_first is s - lo_first
   // Per-frame arena.  Every (step, layer) output has its own 256-byte
   // aligned region, written once per frame (write-through sc1 stores or
   // device atomics) and read only after the grid sync that follows its
@@ -90,7 +93,8 @@ struct FrameArgs {
   long long x_slot, qkv_slot, acc_slot, g_slot, logits_slot;  // region strides (elements)
   u32* flags;              // [P][64] per-block barrier epochs
   u32 epoch0;              // epoch reached before this launch
-  u32* err;                // watchdog word
+  u32* err;                // watchdog words (see Watch)
+  Watch watch;
   u32* tlog;               // optional [P][TLOG_MAX][TLOG_W] wall-clock marks
   u32 tlog_epoch;          // scratch for the marks: epoch at the phase start
 };
@@ -208,6 +212,9 @@ __device__ __forceinline__ bool grid_sync(const Args& a, u32& epoch, int* lds_fl
     const int lane = tidx();
     const int P = gridDim.x;
     if (lane == 0) st_coh(a.flags + 64 * blockIdx.x, epoch);
+    // the epoch to wait for; the test hook waits for one no block publishes
+    const u32 want = a.watch.give_up ? epoch + 0x40000000u : epoch;
+    const u32 limit = a.watch.give_up ? 1u : SPIN_LIMIT;
     u32 spins = 0;
     bool ok = true;
     while (true) {
@@ -217,13 +224,13 @@ __device__ __forceinline__ bool grid_sync(const Args& a, u32& epoch, int* lds_fl
       u32 f[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) f[q] = ld_coh(a.flags + 64 * min(lane + 64 * q, P - 1));
-      bool done = (f[0] >= epoch) & (f[1] >= epoch) & (f[2] >= epoch) & (f[3] >= epoch);
-      for (int b = lane + 256; b < P; b += 64) done &= ld_coh(a.flags + 64 * b) >= epoch;
+      bool done = (f[0] >= want) & (f[1] >= want) & (f[2] >= want) & (f[3] >= want);
+      for (int b = lane + 256; b < P; b += 64) done &= ld_coh(a.flags + 64 * b) >= want;
       if (__ballot(done) == ~0ull) break;
-      if (++spins > SPIN_LIMIT) { ok = false; break; }
+      if (++spins > limit) { ok = false; break; }
     }
     if (lane == 0) {
-      if (!ok) atomicOr(a.err, 1u);
+      if (!ok) atomicOr(a.err + W_ERR, 1u);
       lds_flag[0] = ok ? 0 : 1;
       if (a.tlog && idx < TLOG_MAX) a.tlog[((size_t)blockIdx.x * TLOG_MAX + idx) * TLOG_W + 1] = (u32)wall_clock64();
     }
@@ -232,6 +239,44 @@ __device__ __forceinline__ bool grid_sync(const Args& a, u32& epoch, int* lds_fl
   return lds_flag[0] == 0;
 }
 
+
+// End of a launch.  Every block counts itself out; the last one out finds
+// whether any barrier wait of the launch gave up (the watchdog word).  If so
+// it runs `recover` with all of its threads (restore the state the next
+// launch relies on, and write the outputs the failure convention asks for),
+// raises the context's sticky status, which s2fast_status reports, and
+// clears the watchdog word.  It also resets the exit count for the next
+// launch.  Every block reaches this point: each barrier wait is bounded.
+template <typename Args, typename Recover>
+__device__ __forceinline__ void launch_exit(const Args& a, int* lds_flag, const Recover& recover) {
+  wait_vmem();
+  __syncthreads();
+  if (tidx() == 0) {
+    const u32 n = __hip_atomic_fetch_add(a.err + W_EXITS, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    lds_flag[2] = (n + 1 == gridDim.x) ? 1 : 0;
+    lds_flag[3] = lds_flag[2] ? (int)ld_coh(a.err + W_ERR) : 0;
+  }
+  __syncthreads();
+  if (!lds_flag[2]) return;
+  if (lds_flag[3]) {
+    recover();
+    wait_vmem();
+    __syncthreads();
+    if (tidx() == 0) {
+      atomicOr(a.err + W_STATUS, 1u);
+      st_coh(a.err + W_ERR, 0u);
+    }
+  }
+  if (tidx() == 0) st_coh(a.err + W_EXITS, 0u);
+}
+
+// Zero n 8-byte words with every thread of the block (recovery only).
+__device__ __forceinline__ void zero_words64(long long* p, size_t n) {
+  for (size_t i = tidx(); i < n; i += NTHREADS) st_coh(p + i, 0ll);
+}
+__device__ __forceinline__ void zero_words32(int* p, size_t n) {
+  for (size_t i = tidx(); i < n; i += NTHREADS) st_coh(p + i, 0);
+}
 
 // in-phase timeline mark (instrumented runs only): word w of the current
 // phase's record, by thread 0
@@ -625,6 +670,74 @@ __device__ __forceinline__ float x_mid_of(const FrameArgs& a, const Lds& s, int 
   return xin + from_fx(accb(a, step, l)[(size_t)m * a.dim + k]);
 }
 
+// Scaled dot-product attention of one KV group, causal with offset 0: new
+// row m sits at window position first_new + m and sees positions 0..that
+// ("Fast-AR codebook decoding ...", section 3).  In LDS: q [M][gh][hd]
+// (after q-norm and RoPE), kc / vc [positions][hd] (keys after k-norm and
+// RoPE, values).  One wave per (row, head); row m's output of head hh goes
+// to out + m * out_ld at the wo GEMV layout position of column hh * hd + d
+// of the group's gw columns.
+// Straight-line code: every LDS read is unconditional (clamped addresses)
+// and masking is done on values, so the reads issue back to back; guarded
+// reads would each become a branch with its own wait.  Positions: at most 16.
+template <typename WT>
+__device__ __forceinline__ void attend_rows(const float* q, const float* kc, const float* vc, int M, int first_new,
+                                            int gh, int hd, float* out, int out_ld, int gw) {
+  const int wave = tidx() >> 6, lane = tidx() & 63;
+  const float scale = 1.0f / sqrtf((float)hd);
+  const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane row of the wave, lane in it
+  const int d8 = min(8 * l16, hd - 8);          // lane's 8 head dims in the score pass (hd % 8 == 0)
+  const bool dlive = 8 * l16 < hd;
+  for (int pr = wave; pr < M * gh; pr += NWAVE) {
+    const int m = pr / gh, hh = pr % gh;
+    const int pos = first_new + m;
+    const float* qv = q + (size_t)pr * hd;
+    const float4 qa = *reinterpret_cast<const float4*>(qv + d8);
+    const float4 qb = *reinterpret_cast<const float4*>(qv + d8 + 4);
+    // scores: row g16 of the wave takes positions g16, g16+4, g16+8, g16+12
+    float sc4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 4 * r + g16;
+      const float* kr = kc + (size_t)min(j, pos) * hd + d8;
+      const float4 ka = *reinterpret_cast<const float4*>(kr);
+      const float4 kb = *reinterpret_cast<const float4*>(kr + 4);
+      float part = qa.x * ka.x;
+      part = fmaf(qa.y, ka.y, part); part = fmaf(qa.z, ka.z, part); part = fmaf(qa.w, ka.w, part);
+      part = fmaf(qb.x, kb.x, part); part = fmaf(qb.y, kb.y, part);
+      part = fmaf(qb.z, kb.z, part); part = fmaf(qb.w, kb.w, part);
+      part = row16_sum(dlive ? part : 0.0f);
+      sc4[r] = (j <= pos) ? part * scale : -INFINITY;
+    }
+    // softmax over positions 0..pos: exp(s - max) / sum
+    float mx = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
+    mx = fmaxf(fmaxf(readlane_f(mx, 0), readlane_f(mx, 16)), fmaxf(readlane_f(mx, 32), readlane_f(mx, 48)));
+    float e4[4], es = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      e4[r] = expf(sc4[r] - mx);    // exp(-inf) = 0 for masked positions
+      es += e4[r];
+    }
+    const float den = (readlane_f(es, 0) + readlane_f(es, 16)) + (readlane_f(es, 32) + readlane_f(es, 48));
+    // output: lanes over head dims; all 16 positions are read, masked ones
+    // with weight 0 (the weights' normalisation is applied once to the output)
+    const int c0 = min(lane, hd - 1), c1 = min(lane + 64, hd - 1);
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float* vr = vc + (size_t)min(j, pos) * hd;
+      const float ej = readlane_f(e4[j >> 2], (j & 3) * 16);   // 0 past pos
+      o0 = fmaf(ej, vr[c0], o0);
+      o1 = fmaf(ej, vr[c1], o1);
+    }
+    o0 /= den;
+    o1 /= den;
+    float* o = out + (size_t)m * out_ld;
+    if (lane < hd) o[phys<WT>(hh * hd + lane, gw)] = o0;
+    if (lane + 64 < hd) o[phys<WT>(hh * hd + lane + 64, gw)] = o1;
+  }
+}
+
 // --------------------------------------------------------------- phases
 enum PhaseKind { PH_PROJ = 0, PH_QKV, PH_WO, PH_FFN_UP, PH_FFN_DOWN, PH_HEAD };
 
@@ -658,7 +771,7 @@ __device__ __forceinline__ PhaseId next_phase(const FrameArgs& a, PhaseId id) {
 }
 
 __device__ __forceinline__ int phase_count(const FrameArgs& a) {
-  return (a.has_proj ? 1 : 0) + (a.ncb - 1) * (4 * a.n_layer + 1) - (a.ncb - 2);
+  return (a.has_proj ? 1 : 0) + a.nsteps * (4 * a.n_layer + 1) - (a.nsteps - 1);
 }
 
 // rows of the wo phase: KV group g of this block and its share of the rows
@@ -833,67 +946,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
         }
       }
     }
-    // scaled dot-product attention, causal with offset 0: the row at
-    // position p sees positions 0..p ("Fast-AR codebook decoding ...",
-    // section 3).  One wave per (row, head); the output goes to LDS in the
-    // wo GEMV layout (columns of this KV group).
-    // Straight-line code: every LDS read is unconditional (clamped
-    // addresses) and masking is done on values, so the reads issue back to
-    // back; guarded reads would each become a branch with its own wait.
-    const float scale = 1.0f / sqrtf((float)hd);
-    const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane row of the wave, lane in it
-    const int d8 = min(8 * l16, hd - 8);          // lane's 8 head dims in the score pass (hd % 8 == 0)
-    const bool dlive = 8 * l16 < hd;
-    for (int pr = wave; pr < M * gh; pr += NWAVE) {
-      const int m = pr / gh, hh = pr % gh;
-      const int pos = row_pos(step, m);
-      const float* qv = s.q + (size_t)pr * hd;
-      const float4 qa = *reinterpret_cast<const float4*>(qv + d8);
-      const float4 qb = *reinterpret_cast<const float4*>(qv + d8 + 4);
-      // scores: row g16 of the wave takes positions g16, g16+4, g16+8,
-      // g16+12 (context <= 16)
-      float sc4[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 4 * r + g16;
-        const float* kr = s.kc + (size_t)min(j, pos) * hd + d8;
-        const float4 ka = *reinterpret_cast<const float4*>(kr);
-        const float4 kb = *reinterpret_cast<const float4*>(kr + 4);
-        float part = qa.x * ka.x;
-        part = fmaf(qa.y, ka.y, part); part = fmaf(qa.z, ka.z, part); part = fmaf(qa.w, ka.w, part);
-        part = fmaf(qb.x, kb.x, part); part = fmaf(qb.y, kb.y, part);
-        part = fmaf(qb.z, kb.z, part); part = fmaf(qb.w, kb.w, part);
-        part = row16_sum(dlive ? part : 0.0f);
-        sc4[r] = (j <= pos) ? part * scale : -INFINITY;
-      }
-      // softmax over positions 0..pos: exp(s - max) / sum
-      float mx = fmaxf(fmaxf(sc4[0], sc4[1]), fmaxf(sc4[2], sc4[3]));
-      mx = fmaxf(fmaxf(readlane_f(mx, 0), readlane_f(mx, 16)), fmaxf(readlane_f(mx, 32), readlane_f(mx, 48)));
-      float e4[4], es = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        e4[r] = expf(sc4[r] - mx);    // exp(-inf) = 0 for masked positions
-        es += e4[r];
-      }
-      const float den = (readlane_f(es, 0) + readlane_f(es, 16)) + (readlane_f(es, 32) + readlane_f(es, 48));
-      // output: lanes over head dims; all 16 positions are read, masked
-      // ones with weight 0
-      // (the weights' normalisation is applied once to the output)
-      const int c0 = min(lane, hd - 1), c1 = min(lane + 64, hd - 1);
-      float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float* vr = s.vc + (size_t)min(j, pos) * hd;
-        const float ej = readlane_f(e4[j >> 2], (j & 3) * 16);   // 0 past pos
-        o0 = fmaf(ej, vr[c0], o0);
-        o1 = fmaf(ej, vr[c1], o1);
-      }
-      o0 /= den;
-      o1 /= den;
-      float* o = s.act + (size_t)m * a.kmax;
-      if (lane < hd) o[phys<WT>(hh * hd + lane, a.gw)] = o0;
-      if (lane + 64 < hd) o[phys<WT>(hh * hd + lane + 64, a.gw)] = o1;
-    }
+    attend_rows<WT>(s.q, s.kc, s.vc, M, first_new, gh, hd, s.act, a.kmax, a.gw);
     mark(a, s.flag[1], 7);
   }
   __syncthreads();
@@ -998,7 +1051,7 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
   for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
     const float v = red_sum(s.red, r, 0) / hden;
     st_coh(logitsb(a, step) + r0 + r, v);
-    if (a.logits_out) a.logits_out[(size_t)(step - 1) * a.V + r0 + r] = v;
+    if (a.logits_out && step >= a.lo_first) a.logits_out[(size_t)(step - a.lo_first) * a.V + r0 + r] = v;
   }
 }
 
@@ -1029,7 +1082,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
     const int c0 = a.forced ? a.forced[0] : a.sem_code[0];
     s.codes[0] = min(max(c0, 0), V - 1);     // clamp both ways (main loop, section 5.2)
     if (a.forced)
-      for (int j = 1; j < a.ncb; ++j) s.codes[j] = min(max(a.forced[j], 0), V - 1);
+      for (int j = 1; j < a.nsteps; ++j) s.codes[j] = min(max(a.forced[j], 0), V - 1);
   }
   // per-frame constants into LDS: q/k norm weights of every layer, RoPE table
   if (a.has_qkn) {
@@ -1048,6 +1101,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
   // issued only inside the phase.
   PhaseId id = first_phase(a);
   Plan pl = plan_for<WT>(a, id);
+  bool ok = true;
   for (int ph = 0; ph < nph; ++ph) {
     const int step = id.step, l = id.layer;
     const int M = (step == 1) ? 2 : 1;
@@ -1068,7 +1122,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
       __syncthreads();   // the head's epilogue still reads red and small
       continue;
     }
-    if (!grid_sync(a, epoch, s.flag)) return;
+    if (!grid_sync(a, epoch, s.flag)) { ok = false; break; }
     if (done.kind == PH_HEAD) {
       const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
       const int code = sample_request(logitsb(a, step), V, a.temp[0], a.top_p[0], a.top_k[0],
@@ -1077,7 +1131,15 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
       __syncthreads();
     }
   }
-  if (blockIdx.x == 0 && a.codes_out && tidx() < a.ncb) a.codes_out[tidx()] = s.codes[tidx()];
+  if (ok && blockIdx.x == 0 && a.codes_out && tidx() < a.ncb) a.codes_out[tidx()] = s.codes[tidx()];
+  // a barrier wait gave up: the frame failed.  The attention accumulators
+  // are cleared (the next frame adds into them) and the request's codebooks
+  // 1.. are 0, the main loop's convention for a failed fast_decode
+  // ("Fast-AR codebook decoding ...", section 5.2).
+  launch_exit(a, s.flag, [&]() __attribute__((always_inline)) {
+    zero_words64(a.acc, (size_t)(a.ncb - 1) * a.n_layer * a.acc_slot);
+    if (a.codes_out && tidx() < a.ncb) st_coh(a.codes_out + tidx(), tidx() == 0 ? s.codes[0] : 0);
+  });
 }
 
 __global__ void __launch_bounds__(NTHREADS) sample_kernel(int V, const float* logits, const float* temp,
@@ -1090,6 +1152,105 @@ __global__ void __launch_bounds__(NTHREADS) sample_kernel(int V, const float* lo
   const SampScratch sc{cval, cidx, red};
   const int c = sample_request(logits + (size_t)b * V, V, temp[b], top_p[b], top_k[b], u[b], sc);
   if (tidx() == 0) codes[b] = c;
+}
+
+// ------------------------------------------------------ test kernels
+// The GEMV of the frame kernel on its own: y = W x, with the phase options
+// the frame kernel uses (RMSNorm fused into staging and the RMS dividing the
+// outputs; w1 / w3 rows run as one GEMV with the SwiGLU epilogue).  Rows of
+// W split over the blocks as in a phase; the plan, the weight ring, the
+// activation layout and the wave reduction are the frame kernel's own.
+struct GemvTestArgs {
+  int N, K, M, kmax, rmax;
+  const void* W;
+  const void* W3;        // second matrix of a SwiGLU pair, or nullptr
+  const void* normw;     // RMSNorm weight [K], or nullptr
+  float eps;
+  const float* x;        // [M][K]
+  float* y;              // [M][N]
+};
+
+template <typename WT>
+__global__ void __launch_bounds__(NTHREADS) gemv_test_kernel(GemvTestArgs a) {
+  extern __shared__ float lds_base[];
+  float* act = lds_base;                                             // [MMAX][kmax]
+  float* red = act + (((size_t)MMAX * a.kmax + 3) & ~(size_t)3);    // [rmax][MMAX][NWAVE]
+  float* small = red + (size_t)a.rmax * NWAVE * MMAX;                // [64]
+  int r0, r1;
+  split_rows(a.N, blockIdx.x, gridDim.x, r0, r1);
+  const int nr = r1 - r0;
+  const WT* W3 = reinterpret_cast<const WT*>(a.W3);
+  Plan pl = make_plan<WT>(reinterpret_cast<const WT*>(a.W), W3, a.K, 0, a.K, r0, nr, W3 ? 2 * nr : nr);
+  u32x4 slot[RING];
+  gemv_prologue(pl, slot);
+  float ss0 = 0.0f, ss1 = 0.0f;
+  const int nq = a.K >> 2;
+  for (int i = tidx(); i < a.M * nq; i += NTHREADS) {
+    const int m = i / nq, c = i - m * nq;
+    const float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)m * a.K + 4 * c);
+    float e[4] = {v.x, v.y, v.z, v.w};
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t = fmaf(e[j], e[j], t);
+      if (a.normw) e[j] *= WTraits<WT>::one(reinterpret_cast<const WT*>(a.normw), 4 * c + j);
+    }
+    if (m == 0) ss0 += t; else ss1 += t;
+    *reinterpret_cast<float4*>(act + (size_t)m * a.kmax + phys<WT>(4 * c, a.K)) = make_float4(e[0], e[1], e[2], e[3]);
+  }
+  store_ss(small, a.M, ss0, ss1);
+  zero_lds(red, (W3 ? 2 : 1) * nr * NWAVE * MMAX);
+  __syncthreads();
+  gemv_body<WT>(pl, slot, act, a.kmax, a.M, red);
+  __syncthreads();
+  for (int i = tidx(); i < nr * a.M; i += NTHREADS) {
+    const int r = i / a.M, m = i % a.M;
+    const float den = a.normw ? norm_den(small, m, a.K, a.eps) : 1.0f;
+    const float d = red_sum(red, r, m) / den;
+    a.y[(size_t)m * a.N + r0 + r] = W3 ? silu(d) * (red_sum(red, nr + r, m) / den) : d;
+  }
+}
+
+// q/k RMSNorm + pair RoPE + causal attention of one KV group for the row at
+// window position t (block (g, t)) over the raw wqkv outputs of positions
+// 0..t, with the frame kernel's device functions (head_norm_rope,
+// attend_rows).  out[t][g * gw ..] receives the group's heads.
+struct AttnTestArgs {
+  int H, G, hd, T, ctx, has_qkn;
+  float eps;
+  const float* qkv;      // [T][(H + 2G) hd]
+  const float* qn;       // [hd] (or any valid pointer without q/k norm)
+  const float* kn;
+  const float* rope;     // [2][ctx][hd/2]
+  float* out;            // [T][H hd]
+};
+
+__global__ void __launch_bounds__(NTHREADS) attn_test_kernel(AttnTestArgs a) {
+  extern __shared__ float lds_base[];
+  const int g = blockIdx.x, t = blockIdx.y;
+  const int hd = a.hd, gh = a.H / a.G, gw = gh * hd, qkv_dim = (a.H + 2 * a.G) * hd;
+  float* q = lds_base;                        // [gh][hd]
+  float* kc = q + (size_t)gh * hd;            // [ctx][hd]
+  float* vc = kc + (size_t)a.ctx * hd;        // [ctx][hd]
+  float* rope = vc + (size_t)a.ctx * hd;      // [2][ctx][hd/2]
+  float* o = rope + (size_t)a.ctx * hd;       // [gw]
+  for (int i = tidx(); i < a.ctx * hd; i += NTHREADS) rope[i] = a.rope[i];
+  for (int i = tidx(); i < gh * hd; i += NTHREADS) q[i] = a.qkv[(size_t)t * qkv_dim + (size_t)g * gh * hd + i];
+  for (int i = tidx(); i < (t + 1) * hd; i += NTHREADS) {
+    const int p = i / hd, d = i - p * hd;
+    kc[i] = a.qkv[(size_t)p * qkv_dim + (size_t)(a.H + g) * hd + d];
+    vc[i] = a.qkv[(size_t)p * qkv_dim + (size_t)(a.H + a.G + g) * hd + d];
+  }
+  __syncthreads();
+  const int wave = tidx() >> 6;
+  for (int v = wave; v < gh + t + 1; v += NWAVE) {
+    if (v < gh) head_norm_rope(q + (size_t)v * hd, hd, a.qn, a.has_qkn, a.eps, rope, a.ctx, t);
+    else head_norm_rope(kc + (size_t)(v - gh) * hd, hd, a.kn, a.has_qkn, a.eps, rope, a.ctx, v - gh);
+  }
+  __syncthreads();
+  attend_rows<float>(q, kc, vc, 1, t, gh, hd, o, 0, gw);
+  __syncthreads();
+  for (int i = tidx(); i < gw; i += NTHREADS) a.out[(size_t)t * a.H * hd + (size_t)g * gw + i] = o[i];
 }
 
 // ------------------------------------------------------ qkv0 table build
@@ -1193,6 +1354,7 @@ struct s2fast_ctx {
   u32* err = nullptr;
   u32* tlog = nullptr;     // allocated on first s2fast_test_timeline call
   bool tlog_on = false;
+  u32 give_up = 0;         // test hook (s2fast_test_watchdog)
   u32 epoch = 0;
   // batched decoding (batch >= 2): requests per launch (0: every request is
   // decoded by its own launch) and the batched arena
@@ -1241,11 +1403,12 @@ void rope_table_host(int hd, int ctx, float base, float* c, float* s) {
     }
 }
 
-// grid syncs of one launch: one per phase (the frame kernel's phase_count),
-// less the head's when the prefix is teacher-forced
-int syncs_for(const s2fast_config& c, bool forced) {
+// grid syncs of one launch of `nsteps` decode steps: one per phase (the
+// frame kernel's phase_count), less the head's when the prefix is
+// teacher-forced
+int syncs_for(const s2fast_config& c, int nsteps, bool forced) {
   const int per_step = 4 * c.n_layer + (forced ? 0 : 1);
-  return (c.has_project_in ? 1 : 0) + (c.num_codebooks - 1) * per_step - (c.num_codebooks - 2);
+  return (c.has_project_in ? 1 : 0) + nsteps * per_step - (nsteps - 1);
 }
 
 void free_ctx(s2fast_ctx* c) {
@@ -1335,7 +1498,7 @@ int build_qkv0(s2fast_ctx* c) {
 
 int launch_frame(s2fast_ctx* c, const FrameArgs& fa_in, hipStream_t stream) {
   FrameArgs fa = fa_in;
-  const u32 n = (u32)syncs_for(c->cfg, fa.forced != nullptr);
+  const u32 n = (u32)syncs_for(c->cfg, fa.nsteps, fa.forced != nullptr);
   if (c->epoch > 0xF0000000u) {
     if (hipMemsetAsync(c->flags, 0, (size_t)c->ncu * 64 * sizeof(u32), stream) != hipSuccess) return S2FAST_ERR_HIP;
     c->epoch = 0;
@@ -1352,7 +1515,7 @@ int launch_frame(s2fast_ctx* c, const FrameArgs& fa_in, hipStream_t stream) {
 
 int launch_batched(s2fast_ctx* c, const BatchArgs& ba_in, hipStream_t stream) {
   BatchArgs ba = ba_in;
-  const u32 n = (u32)b_syncs(c->cfg.has_project_in, c->cfg.num_codebooks, c->cfg.n_layer, ba.forced != nullptr,
+  const u32 n = (u32)b_syncs(c->cfg.has_project_in, ba.nsteps, c->cfg.n_layer, ba.forced != nullptr,
                             c->b_ks[BK_HEAD] > 1 && ba.logits_out != nullptr);
   if (c->epoch > 0xF0000000u) {
     if (hipMemsetAsync(c->flags, 0, (size_t)c->ncu * 64 * sizeof(u32), stream) != hipSuccess) return S2FAST_ERR_HIP;
@@ -1374,6 +1537,7 @@ void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
   ba.in_dim = k.in_dim; ba.dim = k.dim; ba.n_layer = k.n_layer; ba.n_head = k.n_head; ba.n_kv = k.n_head_kv;
   ba.hd = k.head_dim; ba.ffn = k.ffn_dim; ba.V = k.codebook_size; ba.ncb = k.num_codebooks; ba.ctx_len = k.context;
   ba.eps = k.norm_eps; ba.has_proj = k.has_project_in; ba.has_qkn = k.has_qk_norm;
+  ba.nsteps = k.num_codebooks - 1; ba.forced_ld = k.num_codebooks; ba.lo_first = 1; ba.lo_rows = k.num_codebooks - 1;
   ba.qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim;
   ba.attn_dim = k.n_head * k.head_dim;
   ba.gheads = k.n_head / k.n_head_kv;
@@ -1395,6 +1559,7 @@ void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
   ba.x_slot = c->bx_slot; ba.qkv_slot = c->bqkv_slot; ba.att_slot = c->batt_slot; ba.g_slot = c->bg_slot;
   ba.logits_slot = c->blogits_slot;
   ba.flags = c->flags; ba.err = c->err;
+  ba.watch.give_up = c->give_up;
   ba.tlog = c->tlog_on ? c->tlog : nullptr;
 }
 
@@ -1412,12 +1577,27 @@ int batched_group(const s2fast_config& k, int P) {
   return bq >= 2 ? bq : 0;
 }
 
+// The sticky status of a context's watchdog words, read (and cleared) after
+// the work enqueued on `st` has finished: S2FAST_ERR_HIP if a launch gave up
+// a barrier wait since the last read.
+int read_status(u32* err, hipStream_t st) {
+  u32 v = 0;
+  if (hipMemcpyAsync(&v, err + W_STATUS, sizeof(u32), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return S2FAST_ERR_HIP;
+  if (v == 0) return S2FAST_OK;
+  if (hipMemsetAsync(err + W_STATUS, 0, sizeof(u32), st) != hipSuccess || hipStreamSynchronize(st) != hipSuccess)
+    return S2FAST_ERR_HIP;
+  return S2FAST_ERR_HIP;
+}
+
 void fill_shape(const s2fast_ctx* c, FrameArgs& fa) {
   const s2fast_config& k = c->cfg;
   std::memset(&fa, 0, sizeof(fa));
   fa.in_dim = k.in_dim; fa.dim = k.dim; fa.n_layer = k.n_layer; fa.n_head = k.n_head; fa.n_kv = k.n_head_kv;
   fa.hd = k.head_dim; fa.ffn = k.ffn_dim; fa.V = k.codebook_size; fa.ncb = k.num_codebooks; fa.ctx_len = k.context;
   fa.eps = k.norm_eps; fa.has_proj = k.has_project_in; fa.has_qkn = k.has_qk_norm;
+  fa.nsteps = k.num_codebooks - 1; fa.forced_ld = k.num_codebooks; fa.lo_first = 1; fa.lo_rows = k.num_codebooks - 1;
   fa.qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim;
   fa.attn_dim = k.n_head * k.head_dim;
   fa.gheads = k.n_head / k.n_head_kv;
@@ -1435,7 +1615,46 @@ void fill_shape(const s2fast_ctx* c, FrameArgs& fa) {
   fa.x_slot = c->x_slot; fa.qkv_slot = c->qkv_slot; fa.acc_slot = c->acc_slot; fa.g_slot = c->g_slot;
   fa.logits_slot = c->logits_slot;
   fa.logits = c->logits; fa.flags = c->flags; fa.err = c->err;
+  fa.watch.give_up = c->give_up;
   fa.tlog = c->tlog_on ? c->tlog : nullptr;
+}
+
+// Teacher-forced launches: B requests with the codes `codes` [B][ld] as
+// their prefixes, `nsteps` decode steps, logits of step s >= lo_first into
+// row s - lo_first of `logits` [B][lo_rows][V].  Arguments are validated.
+int launch_forced(s2fast_ctx* ctx, int B, const float* hidden, const int32_t* codes, int ld, int nsteps,
+                  float* logits, int lo_first, int lo_rows, hipStream_t st) {
+  const s2fast_config& k = ctx->cfg;
+  const size_t lo_req = (size_t)lo_rows * k.codebook_size;
+  if (B >= 2 && ctx->bq > 0) {
+    BatchArgs ba;
+    fill_batch_shape(ctx, ba);
+    ba.nsteps = nsteps; ba.forced_ld = ld; ba.lo_first = lo_first; ba.lo_rows = lo_rows;
+    for (int b0 = 0; b0 < B; b0 += ctx->bq) {
+      ba.Bq = std::min(ctx->bq, B - b0);
+      ba.hidden = hidden + (size_t)b0 * k.in_dim;
+      ba.sem_code = codes + (size_t)b0 * ld;
+      ba.forced = codes + (size_t)b0 * ld;
+      ba.codes_out = nullptr;
+      ba.logits_out = logits + (size_t)b0 * lo_req;
+      const int rc = launch_batched(ctx, ba, st);
+      if (rc != S2FAST_OK) return rc;
+    }
+    return S2FAST_OK;
+  }
+  FrameArgs fa;
+  fill_shape(ctx, fa);
+  fa.nsteps = nsteps; fa.forced_ld = ld; fa.lo_first = lo_first; fa.lo_rows = lo_rows;
+  for (int b = 0; b < B; ++b) {
+    fa.hidden = hidden + (size_t)b * k.in_dim;
+    fa.sem_code = codes + (size_t)b * ld;
+    fa.forced = codes + (size_t)b * ld;
+    fa.codes_out = nullptr;
+    fa.logits_out = logits + (size_t)b * lo_req;
+    const int rc = launch_frame(ctx, fa, st);
+    if (rc != S2FAST_OK) return rc;
+  }
+  return S2FAST_OK;
 }
 
 }  // namespace
@@ -1558,12 +1777,12 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
             dalloc(&c->g, (size_t)(slots * c->g_slot)) == hipSuccess &&
             dalloc(&c->kv, (size_t)(k.n_layer * k.context * c->kv_pos)) == hipSuccess &&
             dalloc(&c->logits, (size_t)((k.num_codebooks - 1) * c->logits_slot)) == hipSuccess &&
-            dalloc(&c->flags, (size_t)P * 64) == hipSuccess && dalloc(&c->err, 64) == hipSuccess;
+            dalloc(&c->flags, (size_t)P * 64) == hipSuccess && dalloc(&c->err, W_WORDS) == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
   ok = hipMemcpy(c->rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemset(c->acc, 0, (size_t)(slots * c->acc_slot) * sizeof(long long)) == hipSuccess &&
        hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
-       hipMemset(c->err, 0, 64 * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+       hipMemset(c->err, 0, W_WORDS * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_HIP; }
   if (build_qkv0(c) != S2FAST_OK) { free_ctx(c); return S2FAST_ERR_HIP; }
   if (k.max_batch >= 2) {
@@ -1640,9 +1859,10 @@ void s2fast_destroy(s2fast_ctx* ctx) {
 
 int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B) {
   if (!ctx || B < 1) return -1;
-  if (B == 1 || ctx->bq == 0) return B * syncs_for(ctx->cfg, false);
+  const int nsteps = ctx->cfg.num_codebooks - 1;
+  if (B == 1 || ctx->bq == 0) return B * syncs_for(ctx->cfg, nsteps, false);
   const int groups = (B + ctx->bq - 1) / ctx->bq;
-  return groups * b_syncs(ctx->cfg.has_project_in, ctx->cfg.num_codebooks, ctx->cfg.n_layer, false, false);
+  return groups * b_syncs(ctx->cfg.has_project_in, nsteps, ctx->cfg.n_layer, false, false);
 }
 
 int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
@@ -1655,6 +1875,7 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const s2fast_config& k = ctx->cfg;
   int rc = S2FAST_OK;
+  int done = 0;   // requests whose launch was enqueued
   if (B >= 2 && ctx->bq > 0) {
     BatchArgs ba;
     fill_batch_shape(ctx, ba);
@@ -1670,6 +1891,7 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
       ba.codes_out = codes + (size_t)b0 * k.num_codebooks;
       ba.logits_out = nullptr;
       rc = launch_batched(ctx, ba, st);
+      if (rc == S2FAST_OK) done = b0 + ba.Bq;
     }
   }
   FrameArgs fa;
@@ -1685,11 +1907,14 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
     fa.codes_out = codes + (size_t)b * k.num_codebooks;
     fa.logits_out = nullptr;
     rc = launch_frame(ctx, fa, st);
+    if (rc == S2FAST_OK) done = b + 1;
   }
   if (rc != S2FAST_OK) {
-    // a failed frame leaves codebooks 1.. at 0 ("Fast-AR codebook decoding ...", section 5.2)
-    (void)hipMemset2DAsync(codes + 1, (size_t)k.num_codebooks * sizeof(int32_t), 0,
-                           (size_t)(k.num_codebooks - 1) * sizeof(int32_t), (size_t)B, st);
+    // the requests whose launch could not be enqueued leave codebooks 1.. at
+    // 0 ("Fast-AR codebook decoding ...", section 5.2); earlier launches
+    // keep their codes
+    (void)hipMemset2DAsync(codes + (size_t)done * k.num_codebooks + 1, (size_t)k.num_codebooks * sizeof(int32_t), 0,
+                           (size_t)(k.num_codebooks - 1) * sizeof(int32_t), (size_t)(B - done), st);
   }
   return rc;
 }
@@ -1700,34 +1925,30 @@ int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const
   if (B < 1 || B > ctx->cfg.max_batch) return S2FAST_ERR_BATCH;
   if (!hidden || !codes || !logits) return S2FAST_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(hidden) & 15u) return S2FAST_ERR_ARG;   // read in 16-byte quads
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const s2fast_config& k = ctx->cfg;
-  if (B >= 2 && ctx->bq > 0) {
-    BatchArgs ba;
-    fill_batch_shape(ctx, ba);
-    for (int b0 = 0; b0 < B; b0 += ctx->bq) {
-      ba.Bq = std::min(ctx->bq, B - b0);
-      ba.hidden = hidden + (size_t)b0 * k.in_dim;
-      ba.sem_code = codes + (size_t)b0 * k.num_codebooks;
-      ba.forced = codes + (size_t)b0 * k.num_codebooks;
-      ba.codes_out = nullptr;
-      ba.logits_out = logits + (size_t)b0 * (k.num_codebooks - 1) * k.codebook_size;
-      const int rc = launch_batched(ctx, ba, st);
-      if (rc != S2FAST_OK) return rc;
-    }
-    return S2FAST_OK;
-  }
-  FrameArgs fa;
-  fill_shape(ctx, fa);
-  for (int b = 0; b < B; ++b) {
-    fa.hidden = hidden + (size_t)b * k.in_dim;
-    fa.sem_code = codes + (size_t)b * k.num_codebooks;
-    fa.forced = codes + (size_t)b * k.num_codebooks;
-    fa.codes_out = nullptr;
-    fa.logits_out = logits + (size_t)b * (k.num_codebooks - 1) * k.codebook_size;
-    const int rc = launch_frame(ctx, fa, st);
-    if (rc != S2FAST_OK) return rc;
-  }
+  const int n = ctx->cfg.num_codebooks;
+  return launch_forced(ctx, B, hidden, codes, n, n - 1, logits, 1, n - 1, reinterpret_cast<hipStream_t>(stream));
+}
+
+int s2fast_fast_decode(s2fast_ctx* ctx, int32_t B, const float* hidden, int32_t hidden_dim, const int32_t* prefix,
+                       int32_t prefix_len, float* logits, void* stream) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  if (hidden_dim != ctx->cfg.in_dim) return S2FAST_ERR_HIDDEN_DIM;
+  if (prefix_len < 1 || prefix_len >= ctx->cfg.num_codebooks) return S2FAST_ERR_PREFIX_LEN;
+  if (B < 1 || B > ctx->cfg.max_batch) return S2FAST_ERR_BATCH;
+  if (!hidden || !prefix || !logits) return S2FAST_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(hidden) & 15u) return S2FAST_ERR_ARG;
+  return launch_forced(ctx, B, hidden, prefix, prefix_len, prefix_len, logits, prefix_len, 1,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int s2fast_status(s2fast_ctx* ctx, void* stream) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  return read_status(ctx->err, reinterpret_cast<hipStream_t>(stream));
+}
+
+int s2fast_test_watchdog(s2fast_ctx* ctx, int32_t give_up) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  ctx->give_up = give_up ? 1u : 0u;
   return S2FAST_OK;
 }
 
@@ -1752,6 +1973,64 @@ int s2fast_test_rope_table(int32_t head_dim, int32_t context, float rope_base, f
     return S2FAST_ERR_ARG;
   rope_table_host(head_dim, context, rope_base, cos_out, sin_out);
   return S2FAST_OK;
+}
+
+int s2fast_test_gemv(int32_t weight_dtype, int32_t N, int32_t K, int32_t M, const void* W, const void* W3,
+                     const void* norm_w, float eps, const float* x, float* y, void* stream) {
+  const int epl = weight_dtype == S2FAST_BF16 ? 8 : 4;
+  if (weight_dtype != S2FAST_BF16 && weight_dtype != S2FAST_F32) return S2FAST_ERR_ARG;
+  if (N < 1 || K < epl || K > 16384 || (K % epl) || M < 1 || M > MMAX || !W || !x || !y) return S2FAST_ERR_ARG;
+  auto mis = [](const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); };
+  if (mis(W) || mis(W3) || mis(norm_w) || mis(x)) return S2FAST_ERR_ARG;
+  int dev = 0, P = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return S2FAST_ERR_HIP;
+  if (!is_gfx950(dev)) return S2FAST_ERR_DEVICE;
+  if (hipDeviceGetAttribute(&P, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return S2FAST_ERR_HIP;
+  GemvTestArgs a;
+  a.N = N; a.K = K; a.M = M; a.kmax = (K + 3) & ~3; a.rmax = (W3 ? 2 : 1) * ((N + P - 1) / P) + 1;
+  a.W = W; a.W3 = W3; a.normw = norm_w; a.eps = eps; a.x = x; a.y = y;
+  const size_t lds = ((((size_t)MMAX * a.kmax + 3) & ~(size_t)3) + (size_t)a.rmax * NWAVE * MMAX + 64) * sizeof(float);
+  const void* fn = weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&gemv_test_kernel<uint16_t>)
+                                                : reinterpret_cast<const void*>(&gemv_test_kernel<float>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return S2FAST_ERR_ARG;
+  void* args[] = {&a};
+  if (hipLaunchKernel(fn, dim3(P), dim3(NTHREADS), args, lds, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return S2FAST_ERR_HIP;
+  return S2FAST_OK;
+}
+
+int s2fast_test_norm_rope_attn(int32_t n_head, int32_t n_head_kv, int32_t head_dim, int32_t T, int32_t context,
+                               float rope_base, float eps, const float* qkv, const float* q_norm, const float* k_norm,
+                               float* out, void* stream) {
+  if (n_head < 1 || n_head_kv < 1 || n_head % n_head_kv || head_dim < 8 || head_dim > 128 || (head_dim % 8) ||
+      context < 1 || context > 16 || T < 1 || T > context || !(rope_base > 0.0f) || !qkv || !out ||
+      (!q_norm) != (!k_norm))
+    return S2FAST_ERR_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return S2FAST_ERR_HIP;
+  if (!is_gfx950(dev)) return S2FAST_ERR_DEVICE;
+  const int half = head_dim / 2;
+  std::vector<float> rope((size_t)2 * context * half);
+  rope_table_host(head_dim, context, rope_base, rope.data(), rope.data() + (size_t)context * half);
+  float* drope = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&drope), rope.size() * sizeof(float)) != hipSuccess) return S2FAST_ERR_NOMEM;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  AttnTestArgs a;
+  a.H = n_head; a.G = n_head_kv; a.hd = head_dim; a.T = T; a.ctx = context; a.has_qkn = q_norm ? 1 : 0;
+  a.eps = eps; a.qkv = qkv; a.qn = q_norm ? q_norm : drope; a.kn = k_norm ? k_norm : drope; a.rope = drope;
+  a.out = out;
+  const int gh = n_head / n_head_kv;
+  const size_t lds = ((size_t)gh * head_dim + 3 * (size_t)context * head_dim + (size_t)gh * head_dim) * sizeof(float);
+  int rc = S2FAST_OK;
+  void* args[] = {&a};
+  if (hipMemcpyAsync(drope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipLaunchKernel(reinterpret_cast<const void*>(&attn_test_kernel), dim3(n_head_kv, T), dim3(NTHREADS), args,
+                      lds, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    rc = S2FAST_ERR_HIP;
+  (void)hipFree(drope);
+  return rc;
 }
 
 int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* temperature, const float* top_p,

@@ -25,6 +25,7 @@ struct s2fast_slow_ctx {
   u32* err = nullptr;
   u32* tlog = nullptr;     // allocated on first s2fast_test_slow_timeline call
   bool tlog_on = false;
+  u32 give_up = 0;         // test hook (s2fast_test_slow_watchdog)
   u32 epoch = 0;
 };
 
@@ -150,13 +151,13 @@ int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights*
             dalloc(&c->po, (size_t)(Ln * c->po_slot)) == hipSuccess &&
             dalloc(&c->pml, (size_t)(Ln * c->pml_slot)) == hipSuccess &&
             dalloc(&c->logits, (size_t)rup(c->n_allowed, 64)) == hipSuccess && dalloc(&c->sem, 64) == hipSuccess &&
-            dalloc(&c->flags, (size_t)P * 64) == hipSuccess && dalloc(&c->err, 64) == hipSuccess;
+            dalloc(&c->flags, (size_t)P * 64) == hipSuccess && dalloc(&c->err, W_WORDS) == hipSuccess;
   if (!ok) { free_slow(c); return S2FAST_ERR_NOMEM; }
   ok = hipMemcpy(c->layers, lp.data(), lp.size() * sizeof(LayerPtr), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(c->rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemset(c->acc, 0, (size_t)(Ln * c->acc_slot) * sizeof(long long)) == hipSuccess &&
        hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
-       hipMemset(c->err, 0, 64 * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+       hipMemset(c->err, 0, W_WORDS * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) { free_slow(c); return S2FAST_ERR_HIP; }
   *out = c;
   return S2FAST_OK;
@@ -169,6 +170,17 @@ void s2fast_slow_destroy(s2fast_slow_ctx* ctx) {
 }
 
 int s2fast_slow_syncs(const s2fast_slow_ctx* ctx) { return ctx ? 5 * ctx->cfg.n_layer + 1 : -1; }
+
+int s2fast_slow_status(s2fast_slow_ctx* ctx, void* stream) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  return read_status(ctx->err, reinterpret_cast<hipStream_t>(stream));
+}
+
+int s2fast_test_slow_watchdog(s2fast_slow_ctx* ctx, int32_t give_up) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  ctx->give_up = give_up ? 1u : 0u;
+  return S2FAST_OK;
+}
 
 int s2fast_slow_allowed(const s2fast_slow_ctx* ctx) { return ctx ? ctx->n_allowed : -1; }
 
@@ -211,6 +223,7 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
   a.x_slot = ctx->x_slot; a.qkv_slot = ctx->qkv_slot; a.acc_slot = ctx->acc_slot; a.g_slot = ctx->g_slot;
   a.po_slot = ctx->po_slot; a.pml_slot = ctx->pml_slot;
   a.flags = ctx->flags; a.err = ctx->err; a.tlog = ctx->tlog_on ? ctx->tlog : nullptr;
+  a.watch.give_up = ctx->give_up;
   if (ctx->epoch > 0xF0000000u) {
     if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
     ctx->epoch = 0;
@@ -290,8 +303,10 @@ int s2fast_full_frame(s2fast_slow_ctx* slow, s2fast_ctx* fast, void* kv_cache, i
                       const float* u_fast, const float* temperature, const float* top_p, const int32_t* top_k,
                       int32_t* main_out, float* hidden_out, int32_t* codes_out, void* stream) {
   if (!slow || !fast || !codes_out || !u_fast) return S2FAST_ERR_ARG;
-  if (fast->cfg.in_dim != slow->cfg.dim || fast->cfg.codebook_size != slow->cfg.codebook_size ||
-      fast->cfg.num_codebooks != slow->cfg.num_codebooks)
+  // the hidden state handed over must have the Fast-AR's input width
+  // ("Fast-AR codebook decoding ...", section 1)
+  if (fast->cfg.in_dim != slow->cfg.dim) return S2FAST_ERR_HIDDEN_DIM;
+  if (fast->cfg.codebook_size != slow->cfg.codebook_size || fast->cfg.num_codebooks != slow->cfg.num_codebooks)
     return S2FAST_ERR_ARG;
   int rc = s2fast_slow_step(slow, kv_cache, n_past, prev_main, prev_codes, window, u_slow, temperature, top_p,
                             top_k, main_out, slow->sem, hidden_out, nullptr, stream);

@@ -80,7 +80,8 @@ struct SlowArgs {
   long long x_slot, qkv_slot, acc_slot, g_slot, po_slot, pml_slot;
   u32* flags;
   u32 epoch0;
-  u32* err;
+  u32* err;                 // watchdog words (see Watch)
+  Watch watch;
   u32* tlog;
   u32 tlog_epoch;
 };
@@ -852,6 +853,7 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
   // A phase's plan (plain integers) is computed before the barrier that
   // precedes the phase.
   Plan pl = slow_plan<WT>(a, 0, SP_QKV);
+  bool ok = true;
   for (int ph = 0; ph < nph; ++ph) {
     const int l = ph / 5;
     const int kind = ph < 5 * a.n_layer ? ph - 5 * l : (int)SP_HEAD;
@@ -870,7 +872,13 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
       const int kn = ph + 1 < 5 * a.n_layer ? ph + 1 - 5 * ln : (int)SP_HEAD;
       pl = slow_plan<WT>(a, min(ln, a.n_layer - 1), kn);   // past the last phase: never used
     }
-    if (!grid_sync(a, epoch, s.flag)) return;
+    if (!grid_sync(a, epoch, s.flag)) { ok = false; break; }
   }
-  if (a.do_head && blockIdx.x == 0) slow_draw(a, s);
+  if (ok && a.do_head && blockIdx.x == 0) slow_draw(a, s);
+  // a barrier wait gave up: the step failed (no main token is drawn and the
+  // window is left as it was); the attention accumulators are cleared for
+  // the next launch
+  launch_exit(a, s.flag, [&]() __attribute__((always_inline)) {
+    zero_words64(a.acc, (size_t)a.n_layer * a.acc_slot);
+  });
 }

@@ -110,7 +110,11 @@ typedef struct s2fast_weights {
 
 typedef struct s2fast_ctx s2fast_ctx;
 
-/* Validate the shape and the weight pointers, allocate the context's device
+/* Create a decoder over the caller's Fast-AR weights: the device side of
+ * the pages' model load for the fast decoder ("Model loading and GGUF",
+ * sections 3 and 4: the fast_* tensors are bound by name and kept on the
+ * GPU, where the Fast-AR runs every frame).
+ * Validate the shape and the weight pointers, allocate the context's device
  * scratch for max_batch requests, build the bf16-rounded RoPE table and the
  * layer-0 q/k/v table above (one GEMM on the current stream's device,
  * synchronised before returning).  With max_batch >= 2 the context also
@@ -127,9 +131,24 @@ typedef struct s2fast_ctx s2fast_ctx;
  * Missing required weight pointers give S2FAST_ERR_NO_FAST_DECODER. */
 int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx** out);
 
+/* Wait for the device, then free everything the context owns (not the
+ * caller's weights).  NULL is ignored. */
 void s2fast_destroy(s2fast_ctx* ctx);
 
+/* Static description of an S2FAST_* code (never NULL). */
 const char* s2fast_strerror(int code);
+
+/* Device-side failure report.  Every grid-wide wait inside a launch is
+ * bounded; if one gives up, the launch ends early and its last block
+ * restores the context's state for the next launch and applies the main
+ * loop's convention for a failed Fast-AR call ("Fast-AR codebook decoding
+ * ...", section 5.2): every request of that launch keeps codes[:, 0] (its
+ * clamped semantic code) and gets codes[:, 1:] = 0; logits of a
+ * teacher-forced launch are then undefined.  This call waits for the work
+ * enqueued on `stream`, returns S2FAST_ERR_HIP if any launch on this context
+ * failed that way since the previous call (and clears the report), else
+ * S2FAST_OK.  Blocking. */
+int s2fast_status(s2fast_ctx* ctx, void* stream);
 
 /* Decode one frame for B requests ("Fast-AR codebook decoding ...", section
  * 5.1, step 3).
@@ -154,15 +173,20 @@ const char* s2fast_strerror(int code);
  *   u_j = (floor(splitmix64(bits(u) * 2^32 + j) / 2^40) + 0.5) * 2^-24;
  *   code = kept candidate maximising p_j / f32(-log(f64(u_j))).
  * Errors: S2FAST_ERR_BATCH for B outside [1, max_batch]; S2FAST_ERR_ARG for
- * NULL pointers or a hidden pointer that is not 16-byte aligned.  If a launch fails after validation, codes[:, 1:] are
- * zero-filled on `stream` (the main loop's "failed fast_decode fills the rest
- * of the frame with 0" convention, section 5.2) and S2FAST_ERR_HIP is
- * returned. */
+ * NULL pointers or a hidden pointer that is not 16-byte aligned.  Batches
+ * run as launches of up to 32 requests (the context's group size); if a
+ * launch cannot be enqueued, codes[:, 1:] of its requests and of every
+ * later one are zero-filled on `stream` (the main loop's "failed
+ * fast_decode fills the rest of the frame with 0" convention, section 5.2)
+ * and S2FAST_ERR_HIP is returned; earlier launches keep their codes.  A
+ * failure inside a launch is reported by s2fast_status. */
 int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
                         const float* uniforms, const float* temperature, const float* top_p,
                         const int32_t* top_k, int32_t* codes, void* stream);
 
-/* Teacher-forced logits: for k = 1..num_codebooks-1 the prefix is
+/* Teacher-forced logits of a whole frame (the per-step logits the main
+ * loop hands to the sampler, "Fast-AR codebook decoding ...", section 4):
+ * for k = 1..num_codebooks-1 the prefix is
  * codes[:, 0..k-1] (codes[:, 0] is clamped like sem_code; the last column
  * is not read) and logits[:, k-1, :] receives the codebook_size logits of
  * that call.
@@ -172,6 +196,20 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
  * Out-of-range prefix codes are clamped to [0, V-1] on the device. */
 int s2fast_forward_logits(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* codes,
                           float* logits, void* stream);
+
+/* One Fast-AR call as the pages define it ("Fast-AR codebook decoding ...",
+ * sections 1-4): the codebook_size logits that follow `prefix` for each of
+ * B requests, the window being [hidden, fast_embeddings[prefix[0]], ...].
+ *   hidden     [B, hidden_dim] f32, 16-byte aligned
+ *   hidden_dim must equal the model's in_dim, else S2FAST_ERR_HIDDEN_DIM
+ *   prefix     [B, prefix_len] i32 codes (prefix[:, 0] is the semantic code;
+ *              every code is clamped on the device into [0, codebook_size))
+ *   prefix_len 1 <= prefix_len < num_codebooks, else S2FAST_ERR_PREFIX_LEN
+ *   logits     [B, codebook_size] f32 OUT
+ * Checks run in the pages' order (hidden width, then prefix length), then
+ * S2FAST_ERR_BATCH and S2FAST_ERR_ARG; nothing is enqueued on an error. */
+int s2fast_fast_decode(s2fast_ctx* ctx, int32_t B, const float* hidden, int32_t hidden_dim, const int32_t* prefix,
+                       int32_t prefix_len, float* logits, void* stream);
 
 /* ---- Slow-AR decode step and the full Dual-AR frame ----
  *
@@ -231,7 +269,10 @@ typedef struct s2fast_slow_weights {
 
 typedef struct s2fast_slow_ctx s2fast_slow_ctx;
 
-/* Validate, allocate the step's device scratch (one launch's arena, about
+/* Create a Slow-AR step over the caller's weights ("Model loading and
+ * GGUF", section 3: the Slow-AR tensors; "Overall architecture ...", section
+ * 2: the 36-layer shape).
+ * Validate, allocate the step's device scratch (one launch's arena, about
  * n_layer * 0.7 MB at the S2 Pro shape) and the RoPE table for max_context
  * positions.  Shape limits (else S2FAST_ERR_ARG): dim, ffn_dim and the
  * per-KV-group width multiples of 8 (bf16) or 4 (f32) elements and <= 16384;
@@ -240,7 +281,14 @@ typedef struct s2fast_slow_ctx s2fast_slow_ctx;
  * Release with s2fast_slow_destroy. */
 int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights* w, s2fast_slow_ctx** out);
 
+/* Wait for the device, then free the context (not the caller's weights). */
 void s2fast_slow_destroy(s2fast_slow_ctx* ctx);
+
+/* As s2fast_status, for Slow-AR launches: a step or prefill launch whose
+ * bounded grid-wide wait gave up draws no main token and leaves the window
+ * unchanged; hidden_out, the cache entry at its position and logits_out are
+ * then undefined.  Blocking. */
+int s2fast_slow_status(s2fast_slow_ctx* ctx, void* stream);
 
 /* One Slow-AR decode step of one request.
  *   kv_cache    [n_layer, n_head_kv, max_context, 2, head_dim] weight_dtype,
@@ -270,8 +318,10 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
 
 /* Prefill ("Overall architecture & Dual-AR data flow", sections 3.1 and 4):
  * the prompt's positions n_past0 .. n_past0 + T - 1 run through the step
- * above in order, one position per launch (the pages' engine takes one
- * token per chunk on CUDA), writing their keys and values into the cache;
+ * above in order, two positions per launch (one pass over the weights for
+ * both, the second attending to the first; an odd last position takes a
+ * launch of its own; the pages' engine takes one token per chunk on CUDA),
+ * writing their keys and values into the cache;
  * the last position's logits give the first main token, drawn and checked
  * against the window exactly as s2fast_slow_step does.
  *   tokens [T, 1 + num_codebooks] i32: per position the row-0 token (text,
@@ -287,8 +337,9 @@ int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, i
 
 /* One full frame ("Fast-AR codebook decoding ...", section 5.1): the Slow-AR
  * step above, then s2fast_decode_frame of one request on its hidden state
- * and semantic code.  The fast context must have in_dim == dim,
- * the same codebook_size and num_codebooks.
+ * and semantic code.  The fast context must have in_dim == dim (else
+ * S2FAST_ERR_HIDDEN_DIM, the pages' hidden-width check, section 1) and the
+ * same codebook_size and num_codebooks (else S2FAST_ERR_ARG).
  *   u_slow [2], u_fast [num_codebooks-1] f32; main_out [1] i32 OUT;
  *   hidden_out [dim] f32 OUT (16-byte aligned); codes_out [num_codebooks]
  *   i32 OUT [sem_code, c_1, ..., c_9].
@@ -321,6 +372,42 @@ int s2fast_test_rope_table(int32_t head_dim, int32_t context, float rope_base,
 int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* temperature,
                        const float* top_p, const int32_t* top_k, const float* u, int32_t* codes,
                        void* stream);
+
+/* The frame kernel's GEMV on its own (weight-streaming, 16-byte weight
+ * loads, rows split over one block per CU), for per-kernel parity:
+ *   y[m, :] = W . n_m  for m < M (M = 1 or 2),  n_m = x[m, :] * norm_w / rms(x[m, :])
+ *   when norm_w is not NULL (RMSNorm, "Model loading and GGUF", section 2.2),
+ *   else n_m = x[m, :]; with W3 not NULL the output is the SwiGLU pair
+ *   silu(W . n_m) * (W3 . n_m) ("Fast-AR codebook decoding ...", section 3).
+ *   W, W3 [N, K] and norm_w [K] of weight_dtype; x [M, K] f32; y [M, N] f32
+ *   OUT; device pointers, W / W3 / x 16-byte aligned; K a multiple of 8
+ *   (bf16) or 4 (f32), K <= 16384.  Enqueued on `stream`.
+ * Errors: S2FAST_ERR_ARG for bad sizes or pointers, S2FAST_ERR_DEVICE off
+ * gfx950. */
+int s2fast_test_gemv(int32_t weight_dtype, int32_t N, int32_t K, int32_t M, const void* W, const void* W3,
+                     const void* norm_w, float eps, const float* x, float* y, void* stream);
+
+/* The frame kernel's q/k RMSNorm + pair RoPE + causal attention (mask
+ * offset 0) on its own ("Fast-AR codebook decoding ...", section 3; Mizuoto
+ * page, "What matches upstream": bf16-rounded RoPE table): for every window
+ * position t < T, the attention output of position t over positions 0..t.
+ *   qkv    [T, (n_head + 2 n_head_kv) head_dim] f32: raw wqkv outputs
+ *          (Q heads, K heads, V heads) of positions 0..T-1
+ *   q_norm, k_norm [head_dim] f32, both NULL for no q/k norm
+ *   out    [T, n_head head_dim] f32 OUT, heads in order
+ * head_dim a multiple of 8 and <= 128; T <= context <= 16.  Device
+ * pointers.  Blocking (it builds and uploads the RoPE table). */
+int s2fast_test_norm_rope_attn(int32_t n_head, int32_t n_head_kv, int32_t head_dim, int32_t T, int32_t context,
+                               float rope_base, float eps, const float* qkv, const float* q_norm,
+                               const float* k_norm, float* out, void* stream);
+
+/* Failure-path test hook: with give_up != 0, later launches on this
+ * context make every block's first grid-wide wait target an epoch that no
+ * block publishes and give up after its first polls, so every block leaves
+ * the kernel normally and the failure path of s2fast_status runs; 0
+ * restores normal launches. */
+int s2fast_test_watchdog(s2fast_ctx* ctx, int32_t give_up);
+int s2fast_test_slow_watchdog(s2fast_slow_ctx* ctx, int32_t give_up);
 
 /* Timeline instrumentation (blocking; for measurement only).  enable != 0
  * makes later launches on this context record, for every block and every

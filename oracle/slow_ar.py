@@ -101,11 +101,13 @@ def cache_round(shape, x: np.ndarray) -> np.ndarray:
     return bf16_round_f32(x) if shape.weight_dtype == "bf16" else np.asarray(x, dtype=F32)
 
 
-# A float32 key or value within this relative distance of the midpoint
-# between its two bfloat16 neighbours may round to either of them in an
-# implementation whose float32 value differs from this one in the last bits
-# (float32 sums taken in another order differ by about 1e-6 relative).
-ROUND_BAND = 1.0e-4
+# Two implementations whose float32 sums run in different orders compute
+# keys and values that differ by about 1e-6 of the vector's largest
+# magnitude (the error of a dot product scales with its terms, not with its
+# result).  A cache entry is a defensible rounding when it is the bfloat16
+# rounding of some float32 value within ROUND_BAND times that magnitude of
+# the oracle's value.
+ROUND_BAND = 1.0e-5
 
 
 class CacheFollowError(AssertionError):
@@ -115,31 +117,32 @@ class CacheFollowError(AssertionError):
 
 def follow_rounding(shape, exact: np.ndarray, theirs: np.ndarray):
     """The cache entries to continue with when another implementation wrote
-    `theirs` for the float32 values `exact`: its entries, provided each one
-    is the oracle's rounding of `exact` or, for a value within ROUND_BAND of
-    a rounding midpoint, the other bfloat16 neighbour.  float32 caches are
-    not rounded, so their entries are compared, not followed (the oracle's
-    values are returned).  Returns (entries, number of other-neighbour
-    choices); raises CacheFollowError otherwise."""
+    `theirs` for the float32 values `exact` (one layer's keys or values): its
+    entries, provided each one lies between the bfloat16 roundings of
+    exact - band and exact + band, band = ROUND_BAND * max|exact| (rounding
+    is monotone, so those are exactly the roundings of values within the
+    band).  float32 caches are not rounded, so their entries are compared,
+    not followed (the oracle's values are returned).  Returns (entries,
+    number of entries that differ from the oracle's rounding); raises
+    CacheFollowError otherwise."""
     exact = np.asarray(exact, dtype=F32)
     mine = cache_round(shape, exact)
     if shape.weight_dtype != "bf16":
         return mine, 0
     theirs = np.asarray(theirs, dtype=F32)
-    same = theirs.view(np.uint32) == mine.view(np.uint32)
-    # bfloat16 neighbours below and above the exact value (truncation and the next bf16 up in magnitude)
-    b = exact.view(np.uint32)
-    lo = (b & np.uint32(0xFFFF0000)).view(F32)
-    hi = ((b & np.uint32(0xFFFF0000)) + np.uint32(0x10000)).view(F32)
-    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2.0
-    near = np.abs(exact.astype(np.float64) - mid) <= ROUND_BAND * np.abs(exact.astype(np.float64))
-    other = ((theirs.view(np.uint32) == lo.view(np.uint32)) | (theirs.view(np.uint32) == hi.view(np.uint32))) & near
-    ok = same | other
+    band = ROUND_BAND * float(np.max(np.abs(exact))) if exact.size else 0.0
+    e64 = exact.astype(np.float64)
+    lo = bf16_round_f32((e64 - band).astype(F32)).astype(np.float64)
+    hi = bf16_round_f32((e64 + band).astype(F32)).astype(np.float64)
+    t64 = theirs.astype(np.float64)
+    is_bf16 = (theirs.view(np.uint32) & np.uint32(0xFFFF)) == 0
+    ok = is_bf16 & (t64 >= lo) & (t64 <= hi)
     if not ok.all():
         i = np.flatnonzero(~ok.reshape(-1))[0]
         raise CacheFollowError(f"entry {i}: exact {exact.reshape(-1)[i]!r}, theirs {theirs.reshape(-1)[i]!r}, "
-                               f"oracle {mine.reshape(-1)[i]!r}")
-    return np.where(same, mine, theirs).astype(F32), int((~same).sum())
+                               f"oracle {mine.reshape(-1)[i]!r}, band {band:.3g}")
+    same = theirs.view(np.uint32) == mine.view(np.uint32)
+    return theirs.copy(), int((~same).sum())
 
 
 # --------------------------------------------------------------------------

@@ -112,7 +112,28 @@ def test_null_arguments():
     assert lib.s2fast_forward_logits(None, 1, None, None, None, None) == 1
     assert lib.s2fast_test_sample(0, 10, None, None, None, None, None, None, None) == 1
     assert lib.s2fast_syncs_per_frame(None, 1) == -1
+    assert lib.s2fast_fast_decode(None, 1, None, 256, None, 1, None, None) == 1
+    assert lib.s2fast_status(None, None) == 1
+    assert lib.s2fast_test_watchdog(None, 1) == 1
     lib.s2fast_destroy(None)
+
+
+def test_kernel_test_exports_reject_bad_arguments():
+    """Checked on the host before any device call."""
+    lib = bd.library()
+    fake = 0x7F0000000000
+    # weight dtype, K not a multiple of the weight vector, M outside 1..2, NULL / misaligned pointers
+    assert lib.s2fast_test_gemv(5, 16, 64, 1, fake, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 16, 60, 1, fake, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 16, 64, 3, fake, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 16, 64, 1, None, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 16, 64, 1, fake + 4, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 0, 64, 1, fake, None, None, 1e-6, fake, fake, None) == 1
+    # heads that do not divide, head_dim not a multiple of 8, T past the context, one norm weight only
+    assert lib.s2fast_test_norm_rope_attn(6, 4, 64, 4, 11, 1e6, 1e-6, fake, None, None, fake, None) == 1
+    assert lib.s2fast_test_norm_rope_attn(4, 2, 60, 4, 11, 1e6, 1e-6, fake, None, None, fake, None) == 1
+    assert lib.s2fast_test_norm_rope_attn(4, 2, 64, 12, 11, 1e6, 1e-6, fake, None, None, fake, None) == 1
+    assert lib.s2fast_test_norm_rope_attn(4, 2, 64, 4, 11, 1e6, 1e-6, fake, fake, None, fake, None) == 1
 
 
 # ---------------------------------------------------------------- Slow-AR
@@ -191,4 +212,5 @@ def test_slow_null_arguments():
                                    None) == 1
     assert lib.s2fast_slow_syncs(None) == -1 and lib.s2fast_slow_allowed(None) == -1
     assert lib.s2fast_test_slow_timeline(None, 1, None, 0) == 1
+    assert lib.s2fast_slow_status(None, None) == 1 and lib.s2fast_test_slow_watchdog(None, 0) == 1
     lib.s2fast_slow_destroy(None)

@@ -305,18 +305,22 @@ def test_follow_rounding_accepts_only_defensible_entries():
     lo = np.float32(1.0)                               # bf16 neighbours 1.0 and 1.0078125
     hi = np.float32(1.0078125)
     mid = (np.float64(lo) + np.float64(hi)) / 2
-    near = np.float32(mid * (1 + 3e-5))                # rounds to hi; within the band of the midpoint
+    near = np.float32(mid * (1 + 3e-6))                # rounds to hi; within the band of the midpoint
     far = np.float32(1.002)                            # rounds to lo; far from the midpoint
-    exact = np.array([near, far, -near], np.float32)
+    tiny = np.float32(-1.5057623e-05)                  # far below the band: several roundings are defensible
+    exact = np.array([near, far, -near, tiny], np.float32)
     mine = sa.cache_round(s, exact)
-    assert list(mine) == [hi, lo, -hi]
+    assert list(mine[:3]) == [hi, lo, -hi]
     got, flips = sa.follow_rounding(s, exact, mine)
     assert flips == 0 and np.array_equal(got, mine)
-    got, flips = sa.follow_rounding(s, exact, np.array([lo, lo, -lo], np.float32))   # near-midpoint flips
-    assert flips == 2 and list(got) == [lo, lo, -lo]
-    for bad in ([lo, hi, -hi],                         # a flip away from any midpoint
-                [np.float32(1.015625), lo, -hi],       # two ulps off
-                [hi, lo, np.float32(1.0078125)]):      # wrong sign
+    other_tiny = np.float32(-1.50203705e-05)           # a bf16 value one ulp from the oracle's rounding
+    got, flips = sa.follow_rounding(s, exact, np.array([lo, lo, -lo, other_tiny], np.float32))
+    assert flips == 3 and list(got) == [lo, lo, -lo, other_tiny]
+    for bad in ([lo, hi, -hi, mine[3]],                # a flip away from any midpoint
+                [np.float32(1.015625), lo, -hi, mine[3]],   # two ulps off
+                [hi, lo, np.float32(1.0078125), mine[3]],   # wrong sign
+                [hi, lo, -hi, np.float32(-1.0e-3)],    # a small value far outside the band
+                [hi, np.float32(1.0000001), -hi, mine[3]]):  # not a bf16 value
         with pytest.raises(sa.CacheFollowError):
             sa.follow_rounding(s, exact, np.array(bad, np.float32))
     # float32 caches are not rounded: the oracle keeps its own values
