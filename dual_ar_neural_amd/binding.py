@@ -20,7 +20,7 @@ BF16, F32 = 0, 1
 
 ERRORS = {
     0: "OK", 1: "ERR_ARG", 2: "ERR_NO_FAST_DECODER", 3: "ERR_HIDDEN_DIM", 4: "ERR_PREFIX_LEN",
-    5: "ERR_BATCH", 6: "ERR_HIP", 7: "ERR_NOMEM", 8: "ERR_DEVICE",
+    5: "ERR_BATCH", 6: "ERR_HIP", 7: "ERR_NOMEM", 8: "ERR_DEVICE", 9: "ERR_SCRATCH",
 }
 
 
@@ -115,6 +115,8 @@ def library() -> ctypes.CDLL:
         lib.s2fast_slow_allowed.restype = ctypes.c_int
         lib.s2fast_test_slow_timeline.argtypes = [P, I, P, I]
         lib.s2fast_test_slow_timeline.restype = ctypes.c_int
+        lib.s2fast_decode_frame_static.argtypes = [P, I, P, P, P, P, P, P, P, V]
+        lib.s2fast_decode_frame_static.restype = ctypes.c_int
         lib.s2fast_fast_decode.argtypes = [P, I, P, I, P, I, P, V]
         lib.s2fast_fast_decode.restype = ctypes.c_int
         lib.s2fast_status.argtypes = [P, V]
@@ -138,7 +140,8 @@ EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_
            "s2fast_syncs_per_frame", "s2fast_test_timeline", "s2fast_slow_create", "s2fast_slow_destroy",
            "s2fast_slow_step", "s2fast_slow_prefill", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed",
            "s2fast_test_slow_timeline", "s2fast_fast_decode", "s2fast_status", "s2fast_slow_status",
-           "s2fast_test_watchdog", "s2fast_test_slow_watchdog", "s2fast_test_gemv", "s2fast_test_norm_rope_attn")
+           "s2fast_test_watchdog", "s2fast_test_slow_watchdog", "s2fast_test_gemv", "s2fast_test_norm_rope_attn",
+           "s2fast_decode_frame_static")
 
 
 def _strerror(code: int) -> str:
@@ -257,7 +260,11 @@ class FastAR:
     def syncs_per_frame(self, B: int) -> int:
         return library().s2fast_syncs_per_frame(self._ctx, B)
 
-    def decode_frame(self, hidden, sem_code, uniforms, temperature, top_p, top_k, codes=None, stream=None):
+    def decode_frame(self, hidden, sem_code, uniforms, temperature, top_p, top_k, codes=None, stream=None,
+                     static_scratch: bool = False):
+        """One frame for B requests; with static_scratch, through
+        s2fast_decode_frame_static (no allocation: the library's static
+        per-GPU scratch, the batch-1 kernel per request)."""
         s = self.shape
         B = hidden.shape[0]
         _dev(hidden, torch.float32, (B, s.in_dim), "hidden")
@@ -269,10 +276,10 @@ class FastAR:
         if codes is None:
             codes = torch.empty((B, s.num_codebooks), dtype=torch.int32, device=hidden.device)
         _dev(codes, torch.int32, (B, s.num_codebooks), "codes")
-        rc = library().s2fast_decode_frame(self._ctx, B, _ptr(hidden), _ptr(sem_code), _ptr(uniforms),
-                                           _ptr(temperature), _ptr(top_p), _ptr(top_k), _ptr(codes),
-                                           _stream(stream))
-        _check(rc, "s2fast_decode_frame")
+        fn = library().s2fast_decode_frame_static if static_scratch else library().s2fast_decode_frame
+        rc = fn(self._ctx, B, _ptr(hidden), _ptr(sem_code), _ptr(uniforms), _ptr(temperature), _ptr(top_p),
+                _ptr(top_k), _ptr(codes), _stream(stream))
+        _check(rc, "s2fast_decode_frame_static" if static_scratch else "s2fast_decode_frame")
         return codes
 
     def status(self, stream=None) -> int:

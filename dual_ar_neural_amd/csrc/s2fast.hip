@@ -31,6 +31,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -1321,6 +1322,18 @@ __global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const WT* e
   }
 }
 
+// ------------------------------------------------- static frame scratch
+// Scratch of s2fast_decode_frame_static, for callers that cannot allocate:
+// the batch-1 frame arena and barrier flags of one launch, in one array per
+// GPU that lives until the process ends.  Host code reaches it only through
+// the device address hipGetSymbolAddress returns (StaticScratch::ptr).
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(u32* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
 #include "batched.h"
 #include "slow_step.h"
 
@@ -1619,6 +1632,49 @@ void fill_shape(const s2fast_ctx* c, FrameArgs& fa) {
   fa.tlog = c->tlog_on ? c->tlog : nullptr;
 }
 
+// Per-device state of the static scratch: its device address (from
+// hipGetSymbolAddress, taken once per device with that device current), the
+// barrier epoch its flags have reached, and whether it was cleared.
+struct StaticScratch {
+  char* ptr = nullptr;
+  u32 epoch = 0;
+  bool cleared = false;
+  size_t layout[3] = {0, 0, 0};   // the arena layout the array was last left in (acc, flags, end)
+};
+constexpr int STATIC_MAX_DEVICES = 64;
+StaticScratch g_static[STATIC_MAX_DEVICES];
+std::mutex g_static_mu;
+
+// Byte offsets of the batch-1 frame arena inside the static scratch (the
+// layout of the context arena: one 256-byte aligned region per (step,
+// layer) output, then the barrier flags); total bytes in `end`.
+struct StaticLayout {
+  size_t xin0, x, qkv, acc, g, kv, logits, flags, end;
+};
+
+StaticLayout static_layout(const s2fast_ctx* c) {
+  const s2fast_config& k = c->cfg;
+  const size_t slots = (size_t)(k.num_codebooks - 1) * k.n_layer;
+  auto r = [](size_t n) { return (n + 255) / 256 * 256; };
+  StaticLayout L;
+  size_t o = 0;
+  L.xin0 = o; o += r(((size_t)k.dim + 63) / 64 * 64 * sizeof(float));
+  L.x = o; o += r(slots * c->x_slot * sizeof(float));
+  L.qkv = o; o += r(slots * c->qkv_slot * sizeof(float));
+  L.acc = o; o += r(slots * c->acc_slot * sizeof(long long));
+  L.g = o; o += r(slots * c->g_slot * sizeof(float));
+  L.kv = o; o += r((size_t)k.n_layer * k.context * c->kv_pos * sizeof(float));
+  L.logits = o; o += r((size_t)(k.num_codebooks - 1) * c->logits_slot * sizeof(float));
+  L.flags = o; o += r((size_t)c->ncu * 64 * sizeof(u32));
+  L.end = o;
+  return L;
+}
+
+int zero_device(void* p, size_t bytes, hipStream_t st) {
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, st, static_cast<u32*>(p), bytes / sizeof(u32));
+  return hipGetLastError() == hipSuccess ? S2FAST_OK : S2FAST_ERR_HIP;
+}
+
 // Teacher-forced launches: B requests with the codes `codes` [B][ld] as
 // their prefixes, `nsteps` decode steps, logits of step s >= lo_first into
 // row s - lo_first of `logits` [B][lo_rows][V].  Arguments are validated.
@@ -1672,6 +1728,7 @@ const char* s2fast_strerror(int code) {
     case S2FAST_ERR_HIP: return "HIP runtime error";
     case S2FAST_ERR_NOMEM: return "out of memory";
     case S2FAST_ERR_DEVICE: return "unsupported device (needs gfx950 with co-resident cooperative blocks)";
+    case S2FAST_ERR_SCRATCH: return "the shape's frame arena is larger than the library's static scratch";
     default: return "unknown error";
   }
 }
@@ -1939,6 +1996,81 @@ int s2fast_fast_decode(s2fast_ctx* ctx, int32_t B, const float* hidden, int32_t 
   if (reinterpret_cast<uintptr_t>(hidden) & 15u) return S2FAST_ERR_ARG;
   return launch_forced(ctx, B, hidden, prefix, prefix_len, prefix_len, logits, prefix_len, 1,
                        reinterpret_cast<hipStream_t>(stream));
+}
+
+int s2fast_decode_frame_static(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
+                               const float* uniforms, const float* temperature, const float* top_p,
+                               const int32_t* top_k, int32_t* codes, void* stream) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  if (B < 1 || B > ctx->cfg.max_batch) return S2FAST_ERR_BATCH;
+  if (!hidden || !sem_code || !uniforms || !temperature || !top_p || !top_k || !codes) return S2FAST_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(hidden) & 15u) return S2FAST_ERR_ARG;
+  const StaticLayout L = static_layout(ctx);
+  if (L.end > STATIC_SCRATCH_BYTES) return S2FAST_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return S2FAST_ERR_HIP;
+  if (dev != ctx->device || dev < 0 || dev >= STATIC_MAX_DEVICES) return S2FAST_ERR_DEVICE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const s2fast_config& k = ctx->cfg;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticScratch& S = g_static[dev];
+  if (!S.ptr) {
+    // once per device, with that device current: the array's device address
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return S2FAST_ERR_HIP;
+    S.ptr = static_cast<char*>(p);
+  }
+  // The accumulators must start at zero and the flags below the first
+  // epoch.  Every launch leaves its own layout so (a failed one through its
+  // recovery), but a context of another shape lays the arena out
+  // differently (its accumulators may sit where the last one kept
+  // activations): the array is cleared on the first call, when the layout
+  // changes, and when the epoch counter would wrap.
+  const size_t key[3] = {L.acc, L.flags, L.end};
+  if (!S.cleared || S.epoch > 0xF0000000u || std::memcmp(key, S.layout, sizeof(key)) != 0) {
+    if (zero_device(S.ptr, STATIC_SCRATCH_BYTES, st) != S2FAST_OK) return S2FAST_ERR_HIP;
+    S.cleared = true;
+    S.epoch = 0;
+    std::memcpy(S.layout, key, sizeof(key));
+  }
+  FrameArgs fa;
+  fill_shape(ctx, fa);
+  fa.xin0 = reinterpret_cast<float*>(S.ptr + L.xin0);
+  fa.x = reinterpret_cast<float*>(S.ptr + L.x);
+  fa.qkv = reinterpret_cast<float*>(S.ptr + L.qkv);
+  fa.acc = reinterpret_cast<long long*>(S.ptr + L.acc);
+  fa.g = reinterpret_cast<float*>(S.ptr + L.g);
+  fa.kv = reinterpret_cast<float*>(S.ptr + L.kv);
+  fa.logits = reinterpret_cast<float*>(S.ptr + L.logits);
+  fa.flags = reinterpret_cast<u32*>(S.ptr + L.flags);
+  fa.tlog = nullptr;
+  const void* fn = k.weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&frame_kernel<uint16_t>)
+                                                 : reinterpret_cast<const void*>(&frame_kernel<float>);
+  const u32 n = (u32)syncs_for(k, fa.nsteps, false);
+  int done = 0, rc = S2FAST_OK;
+  for (int b = 0; b < B; ++b) {
+    fa.hidden = hidden + (size_t)b * k.in_dim;
+    fa.sem_code = sem_code + b;
+    fa.uniforms = uniforms + (size_t)b * (k.num_codebooks - 1);
+    fa.temp = temperature + b;
+    fa.top_p = top_p + b;
+    fa.top_k = top_k + b;
+    fa.forced = nullptr;
+    fa.codes_out = codes + (size_t)b * k.num_codebooks;
+    fa.logits_out = nullptr;
+    fa.epoch0 = S.epoch;
+    void* args[] = {&fa};
+    if (hipLaunchCooperativeKernel(fn, dim3(ctx->ncu), dim3(NTHREADS), args, ctx->lds_bytes, st) != hipSuccess) {
+      rc = S2FAST_ERR_HIP;
+      break;
+    }
+    S.epoch += n;
+    done = b + 1;
+  }
+  if (rc != S2FAST_OK)
+    (void)hipMemset2DAsync(codes + (size_t)done * k.num_codebooks + 1, (size_t)k.num_codebooks * sizeof(int32_t), 0,
+                           (size_t)(k.num_codebooks - 1) * sizeof(int32_t), (size_t)(B - done), st);
+  return rc;
 }
 
 int s2fast_status(s2fast_ctx* ctx, void* stream) {

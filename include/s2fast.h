@@ -46,8 +46,10 @@ enum {
   S2FAST_ERR_BATCH = 5,            /* B < 1 or B > max_batch */
   S2FAST_ERR_HIP = 6,              /* a HIP runtime call failed */
   S2FAST_ERR_NOMEM = 7,            /* device or host allocation failed */
-  S2FAST_ERR_DEVICE = 8            /* device not supported (not gfx950, or the
+  S2FAST_ERR_DEVICE = 8,           /* device not supported (not gfx950, or the
                                       grid cannot be co-resident) */
+  S2FAST_ERR_SCRATCH = 9           /* the shape needs more scratch than the
+                                      static buffer of s2fast_decode_frame_static */
 };
 
 enum { S2FAST_BF16 = 0, S2FAST_F32 = 1 };
@@ -183,6 +185,28 @@ int s2fast_status(s2fast_ctx* ctx, void* stream);
 int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
                         const float* uniforms, const float* temperature, const float* top_p,
                         const int32_t* top_k, int32_t* codes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * s2fast_decode_frame with the same arguments and results for every request
+ * as a batch-1 call of s2fast_decode_frame (each request runs the batch-1
+ * kernel, one launch after another), whose per-frame scratch (activations,
+ * attention accumulators, the frame's keys and values, logits, barrier
+ * flags) lives in one static 16 MiB device array per GPU instead of the
+ * context's arena.  It calls no allocating routine: the first call on a
+ * device takes the array's device address and clears it with a kernel on
+ * `stream` (the array then stays with the process), and so does the first
+ * call after one with a context of another shape.  The context must have
+ * been created on the current device (else S2FAST_ERR_DEVICE); a shape
+ * whose batch-1 arena exceeds 16 MiB gives S2FAST_ERR_SCRATCH (the S2 Pro
+ * shape needs 7.4 MiB).  Every call on one GPU shares the array: calls that
+ * overlap on one GPU, from any context or thread, race, and must be
+ * serialised by the caller (one stream).  Each call leaves the array ready
+ * for the next, also after a failure reported by s2fast_status.  Other
+ * errors as s2fast_decode_frame. */
+int s2fast_decode_frame_static(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
+                               const float* uniforms, const float* temperature, const float* top_p,
+                               const int32_t* top_k, int32_t* codes, void* stream);
 
 /* Teacher-forced logits of a whole frame (the per-step logits the main
  * loop hands to the sampler, "Fast-AR codebook decoding ...", section 4):
