@@ -54,6 +54,22 @@ def algorithmic_bytes_per_frame(shape, batch: int, qkv0_table: bool) -> int:
     return per_frame + io
 
 
+def survey_bytes_per_frame(shape, batch: int) -> int:
+    """The roofline's algorithmic bytes of one frame of `batch` requests:
+    every weight matrix (wqkv, wo, w1, w3, w2 of each layer and the untied
+    head) once per decode step, fast_project_in once per frame, plus each
+    request's inputs and codes (hidden state, semantic code, nine uniforms,
+    three sampling settings, ten codes).  7,455,375,360 + 10,332 bytes at
+    the S2 Pro shape and batch 1."""
+    s = shape
+    wb = 2 if s.weight_dtype == "bf16" else 4
+    per_step = (s.n_layer * (s.qkv_dim * s.dim + s.dim * s.attn_dim + 3 * s.ffn_dim * s.dim)
+                + s.codebook_size * s.dim) * wb
+    proj = s.dim * s.in_dim * wb if s.has_project_in else 0
+    io = batch * (s.in_dim * 4 + 4 + s.n_steps * 4 + 3 * 4 + s.num_codebooks * 4)
+    return s.n_steps * per_step + proj + io
+
+
 def slow_step_bytes(shape, n_past: int, head: bool = True, M: int = 1) -> int:
     """Bytes one Slow-AR launch must move at minimum for the M positions
     n_past .. n_past + M - 1: every layer matrix and norm vector once, the
@@ -288,28 +304,67 @@ def traffic_from_profile(path: str, source_files) -> dict | None:
     return rec
 
 
-def cpu_baseline(workload, frames: int, host_weights):
-    """The oracle as it stands, on this host: literal recompute of every
-    window, float32 numpy, BLAS on all the cores the process may use."""
+def oracle_leg(workload, frames: int, host_weights, gpu_codes, gpu_logits, batched=()):
+    """The oracle on this host: the literal-recompute float32 numpy decoder
+    as it stands, BLAS on every core the process may use.  It decodes the
+    first `frames` frames of the batch-1 workload teacher-forced along the
+    GPU's codes of the timed run (the same windows a free decode computes),
+    timed after one warm-up frame; the same run supplies the parity of
+    those frames: each GPU code must be one of the oracle draw's defensible
+    codes, and the GPU's teacher-forced logits of the same prefixes must lie
+    within 1e-2 * max|logit| + 1e-3.  `batched` adds one frame of each batch
+    line (workload, host weights, GPU codes, GPU logits), checked the same
+    way but not timed."""
     from oracle import fast_ar as fa
     from synth import inputs as si
     w = workload
     model = fa.Model.from_weights(w.shape, host_weights)
     fr = si.make_frames(w, n_frames=frames + 1)
-    fa.decode_frame(model, fr["hidden"][0], fr["sem_code"][0], fr["uniforms"][0], fr["temperature"],
-                    fr["top_p"], fr["top_k"])
+
+    def one(m, fr_, f, codes):
+        return fa.decode_frame(m, fr_["hidden"][f], fr_["sem_code"][f], fr_["uniforms"][f], fr_["temperature"],
+                               fr_["top_p"], fr_["top_k"], forced=codes)
+
+    one(model, fr, 0, gpu_codes[0])
     t0 = time.perf_counter()
-    for f in range(1, frames + 1):
-        fa.decode_frame(model, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], fr["temperature"],
-                        fr["top_p"], fr["top_k"])
+    refs = [one(model, fr, f, gpu_codes[f]) for f in range(1, frames + 1)]
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
     threads = os.environ.get("OMP_NUM_THREADS")
     if threads and threads.isdigit():
         cores = min(cores, int(threads))
-    return {"value": round(w.batch * frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
-            "sample": f"{frames} frames of {w.name} (batch {w.batch}) after one warm-up frame, "
-                      f"{dt:.1f} s wall clock"}
+    base = {"value": round(w.batch * frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
+            "sample": f"{frames} frames of {w.name} (batch {w.batch}) after one warm-up frame, teacher-forced "
+                      f"along the GPU's codes, {dt:.1f} s wall clock"}
+
+    def check(refs_, codes_, logits_):
+        draws = marked = excused = 0
+        worst = 0.0
+        for r, c, lg in zip(refs_, codes_, logits_):
+            for b in range(c.shape[0]):
+                for k in range(1, c.shape[1]):
+                    alts = r.alts[b][k - 1]
+                    draws += 1
+                    marked += len(alts) > 1
+                    excused += int(c[b, k]) != int(r.codes[b, k])
+                    if int(c[b, k]) not in alts:
+                        raise AssertionError(f"parity: request {b} step {k}: GPU code {int(c[b, k])} is not "
+                                             f"defensible (oracle {int(r.codes[b, k])}, {alts})")
+                for k in range(lg.shape[1]):
+                    ref = r.logits[b, k]
+                    d = float(np.max(np.abs(lg[b, k] - ref)))
+                    worst = max(worst, d / (1e-2 * float(np.max(np.abs(ref))) + 1e-3))
+        if worst > 1.0:
+            raise AssertionError(f"parity: logits {worst:.3g} x the tolerance")
+        return {"frames": len(refs_), "draws": draws, "marked": marked, "excused": excused,
+                "worst_logit_err_over_tol": float(f"{worst:.3g}")}
+
+    parity = {"b1": check(refs, gpu_codes[1:frames + 1], gpu_logits[1:frames + 1])}
+    for name, wb, hw, codes_b, logits_b in batched:
+        mb = fa.Model.from_weights(wb.shape, hw)
+        frb = si.make_frames(wb, n_frames=1)
+        parity[name] = check([one(mb, frb, 0, codes_b)], [codes_b], [logits_b])
+    return base, parity
 
 
 def main():
@@ -319,6 +374,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch 16/64 lines")
+    ap.add_argument("--sweep-frames", type=int, default=16, help="timed frames of each batch line")
     ap.add_argument("--cpu-frames", type=int, default=96)
     ap.add_argument("--no-full-frame", action="store_true", help="skip the full-frame (Slow-AR + Fast-AR) line")
     ap.add_argument("--full-frames", type=int, default=512)
@@ -342,7 +398,8 @@ def main():
     if args.no_cpu_baseline:
         del host
     ctx = bd.FastAR(shape, dev, max_batch=64)
-    fr = si.make_frames(w, n_frames=min(w.frames, max(args.steps, 1)))
+    n_in = max(args.steps, args.cpu_frames + 1 if not args.no_cpu_baseline else 1)
+    fr = si.make_frames(w, n_frames=min(w.frames, n_in))
     dev_in = upload(torch, fr)
 
     # one elementwise kernel of known traffic (reads 256 MiB, writes 256 MiB),
@@ -358,7 +415,8 @@ def main():
     B = 1
     frames_per_s = B * args.steps / secs
     ms = secs * 1e3 / args.steps
-    bytes_frame = algorithmic_bytes_per_frame(shape, B, True)   # one launch is one frame at batch 1
+    bytes_frame = survey_bytes_per_frame(shape, B)                # one launch is one frame at batch 1
+    path_bytes = algorithmic_bytes_per_frame(shape, B, True)
     achieved = bytes_frame / kern_s / 1e9
     csrc = os.path.join(ROOT, "dual_ar_neural_amd", "csrc")
     prof = traffic_from_profile(os.path.join(ROOT, "profiles", "frame_kernel_s2pro_b1_hbm_traffic.md"),
@@ -378,49 +436,73 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "S2 Pro-shaped Fast-AR frame decode, batch 1, independent frames",
-                   "batch": 1, "weights": "bf16", "dim": shape.dim, "layers": shape.n_layer,
+                   "batch": 1, "weights": "bf16 (float32 arithmetic)", "dim": shape.dim, "layers": shape.n_layer,
                    "heads": f"{shape.n_head}/{shape.n_head_kv}", "head_dim": shape.head_dim,
                    "ffn": shape.ffn_dim, "codebook": shape.codebook_size, "codebooks": shape.num_codebooks,
                    "sampling": "T 0.8, top_p 0.8, top_k 30"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "frame_kernel<bf16>", "bytes_per_launch": bytes_frame,
-                     "avg_launch_us": round(kern_s * 1e6, 2)},
+                     "avg_launch_us": round(kern_s * 1e6, 2),
+                     "path_bytes_per_launch": path_bytes,
+                     "path_frac": round(path_bytes / kern_s / 1e9 / PEAK_HBM_GBS, 4)},
         "syncs_per_frame": ctx.syncs_per_frame(1),
     }
+    n_chk = 0 if args.no_cpu_baseline else min(args.cpu_frames + 1, dev_in[0].shape[0])
+    if n_chk:
+        # the codes of the frames the oracle leg checks (decoded again after
+        # the timed region: the decoder is deterministic, so a frame the
+        # timed run decoded gets the same codes), and the batch-1 kernel's
+        # teacher-forced logits of the same prefixes
+        for f in range(n_chk):
+            ctx.decode_frame(dev_in[0][f], dev_in[1][f], dev_in[2][f], dev_in[3], dev_in[4], dev_in[5],
+                             codes=dev_in[6][f])
+        gpu_codes = dev_in[6][:n_chk].cpu().numpy()
+        gpu_logits = np.stack([ctx.forward_logits(dev_in[0][f], dev_in[6][f]).cpu().numpy() for f in range(n_chk)])
+    batched_chk = []
     if not args.no_sweep:
         sweep = {}
-        for Bs, wname, nf in ((16, "s2pro_b16", 4), (64, "s2pro_b64", 2)):
+        for Bs, wname in ((16, "s2pro_b16"), (64, "s2pro_b64")):
             ws = si.WORKLOADS[wname]
+            hs = None
             if ws.shape is not shape:
                 hs = si.make_weights(ws.shape, ws.seed(0))
                 ds = bd.device_weights(ws.shape, hs)
-                del hs
                 cs = bd.FastAR(ws.shape, ds, max_batch=Bs)
             else:
                 ds, cs = None, ctx
+            nf = args.sweep_frames
             frs = si.make_frames(ws, n_frames=nf)
             di = upload(torch, frs)
             print(f"[bench] timing {nf} frames at batch {Bs}", file=sys.stderr, flush=True)
-            sec, _ = time_frames(torch, cs, di, Bs, nf, 1)
-            fb = algorithmic_bytes_per_frame(ws.shape, Bs, True)
+            sec, per_call = time_frames(torch, cs, di, Bs, nf, 2)
+            fb = survey_bytes_per_frame(ws.shape, Bs)
             sweep[f"b{Bs}"] = {"frames_per_s": round(Bs * nf / sec, 2), "ms_per_frame": round(sec * 1e3 / nf, 3),
                                "hbm_gbs": round(fb * nf / sec / 1e9, 1),
                                "frac": round(fb * nf / sec / 1e9 / PEAK_HBM_GBS, 4), "frames": nf,
-                               "workload": ws.name}
+                               "bytes_per_frame": fb, "kernel_ms_per_frame": round(per_call * 1e3, 3),
+                               "launches_per_frame": (Bs + 31) // 32, "workload": ws.name}
+            if n_chk:
+                c0 = di[6][0].cpu().numpy()
+                l0 = cs.forward_logits(di[0][0], di[6][0]).cpu().numpy()
+                batched_chk.append((f"b{Bs}", ws, hs if hs is not None else host, c0, l0))
             if cs is not ctx:
                 cs.close()
                 del ds
+            del di
             torch.cuda.empty_cache()
         result["batch_sweep"] = sweep
     if not args.no_full_frame:
         result["full_frame"] = full_frame_bench(torch, bd, ctx, shape, args.full_frames, 4,
                                                 None if args.no_cpu_baseline else host, args.cpu_full_frames)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_frames, host)
-    print(json.dumps(result), flush=True)
     ctx.close()
+    del dev, dev_in
+    torch.cuda.synchronize()
+    if n_chk:
+        print("[bench] the oracle on the host: timing and parity of the timed frames", file=sys.stderr, flush=True)
+        result["cpu_baseline"], result["parity"] = oracle_leg(w, n_chk - 1, host, gpu_codes, gpu_logits,
+                                                               batched_chk)
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

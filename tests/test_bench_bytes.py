@@ -44,3 +44,17 @@ def test_fast_frame_bytes_from_shapes():
     # steps 2..9 take their layer-0 q/k/v from the table (one float32 row)
     want = s.n_steps * per_step - (s.n_steps - 1) * (l0 - s.qkv_dim * 4) + io
     assert bench.algorithmic_bytes_per_frame(s, 1, True) == want
+
+
+def test_survey_bytes_are_the_scope_tables_figure():
+    """The roofline's bytes: every weight matrix once per decode step
+    (7,455,375,360 B a frame at the S2 Pro shape, 828,375,040 a step) plus
+    10,332 B of each request's inputs and codes; fast_project_in once per
+    frame for the batch-64 workload."""
+    s = si.S2PRO
+    mats = [n for n in si.weight_names(s) if not n.endswith("norm") and n != "fast_embeddings"]
+    per_step = _tensor_bytes(lambda n: si.weight_shape(s, n), mats, 2)
+    assert per_step == 828_375_040
+    assert bench.survey_bytes_per_frame(s, 1) == 7_455_375_360 + 10_332
+    assert bench.survey_bytes_per_frame(s, 16) == 7_455_375_360 + 16 * 10_332
+    assert bench.survey_bytes_per_frame(si.S2PRO_PROJ, 64) == 7_455_375_360 + 13_107_200 + 64 * 10_332
