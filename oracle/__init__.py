@@ -14,7 +14,8 @@ route through it.
 
 Modules:
   fast_ar  - float32 numpy forward (full recompute of every window, no KV
-             cache) and the frame decode loop.
+             cache) and the frame decode loop; weight-only int8 matrices
+             (one float32 scale per output row) are dequantized first.
   sampler  - the per-request sampler (temperature, top-k, softmax, top-p,
              exponential race with SplitMix64 per-candidate uniforms).
   brute    - an independent float64 scalar-loop forward for small shapes,

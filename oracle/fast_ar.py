@@ -48,6 +48,22 @@ def as_f32_weight(w: np.ndarray) -> np.ndarray:
     return w.astype(F32, copy=False)
 
 
+SCALE_SUFFIX = ".scale"
+
+
+def dequantize_rows(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Weight-only int8 matrices with one float32 scale per output row:
+    W[r, k] = scale[r] * q[r, k], rounded to float32.  (The pages name GGUF
+    quantised tensors, "Overall architecture & Dual-AR data flow", section 5
+    and "Model loading and GGUF", section 4, but no Fast-AR format; per-row
+    symmetric int8 is this build's reading.)"""
+    q = np.asarray(q)
+    assert q.dtype == np.int8 and q.ndim == 2
+    scale = np.asarray(scale, dtype=F32).reshape(-1)
+    assert scale.shape[0] == q.shape[0]
+    return (scale.astype(np.float64)[:, None] * q.astype(np.float64)).astype(F32)
+
+
 @dataclass
 class Model:
     """Shape hyper-parameters plus float32 weights keyed by GGUF-style name."""
@@ -56,7 +72,17 @@ class Model:
 
     @classmethod
     def from_weights(cls, shape, weights: Dict[str, np.ndarray]) -> "Model":
-        return cls(shape, {k: as_f32_weight(v) for k, v in weights.items()})
+        """Weights as float32 or bf16 bits; an int8 matrix comes with its
+        per-row scales under name + ".scale" and is dequantized."""
+        out = {}
+        for k, v in weights.items():
+            if k.endswith(SCALE_SUFFIX):
+                continue
+            if np.asarray(v).dtype == np.int8:
+                out[k] = dequantize_rows(v, weights[k + SCALE_SUFFIX])
+            else:
+                out[k] = as_f32_weight(v)
+        return cls(shape, out)
 
     def layer(self, i: int, name: str) -> np.ndarray:
         return self.w[f"fast_layers.{i}.{name}"]

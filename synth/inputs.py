@@ -45,7 +45,7 @@ class ModelShape:
     norm_eps: float = 1.0e-6
     has_project_in: bool = False
     has_qk_norm: bool = True
-    weight_dtype: str = "bf16"   # "bf16" or "f32"
+    weight_dtype: str = "bf16"   # "bf16", "f32" or "q8" (int8 matrices, bf16 vectors)
 
     @property
     def qkv_dim(self) -> int:
@@ -69,6 +69,13 @@ S2PRO_PROJ = replace(S2PRO, name="s2pro_proj", has_project_in=True)
 # the projection is rectangular and head_dim is not a power of two.
 RAGGED = ModelShape("ragged", in_dim=176, dim=200, n_layer=2, n_head=6, n_head_kv=2,
                     head_dim=40, ffn_dim=520, codebook_size=300, has_project_in=True)
+# Weight-only int8: every weight matrix int8 with one float32 scale per
+# output row; norm weights and fast_embeddings stay bf16.  Widths are
+# multiples of 16 (one 16-byte load holds 16 weights).
+S2PRO_Q8 = replace(S2PRO, name="s2pro_q8", weight_dtype="q8")
+TINY_Q8 = replace(TINY, name="tiny_q8", weight_dtype="q8")
+RAGGED_Q8 = ModelShape("ragged_q8", in_dim=176, dim=208, n_layer=2, n_head=6, n_head_kv=2,
+                       head_dim=48, ffn_dim=528, codebook_size=300, has_project_in=True, weight_dtype="q8")
 
 
 def weight_names(shape: ModelShape) -> List[str]:
@@ -137,10 +144,32 @@ def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def quantize_rows(w: np.ndarray):
+    """Symmetric per-row int8 of a float matrix [N, K]: scale[r] =
+    max_k |w[r, k]| / 127 (float64, then float32), q = round-half-even of
+    w / scale clipped to [-127, 127]; an all-zero row gets scale 0 and
+    q = 0.  Returns (q int8, scale float32)."""
+    w64 = np.asarray(w, dtype=np.float64)
+    amax = np.max(np.abs(w64), axis=1)
+    scale = (amax / 127.0).astype(np.float32)
+    s64 = scale.astype(np.float64)
+    safe = np.where(s64 > 0, s64, 1.0)
+    q = np.clip(np.rint(w64 / safe[:, None]), -127, 127)
+    q[s64 == 0] = 0
+    return q.astype(np.int8), scale
+
+
+def is_matrix(name: str) -> bool:
+    return not is_norm(name) and name != "fast_embeddings"
+
+
 def make_weights(shape: ModelShape, seed: int) -> Dict[str, np.ndarray]:
     """Draw every weight tensor in `weight_names` order from one PCG64 stream.
 
-    bf16 shapes return uint16 bit arrays, f32 shapes float32 arrays.
+    bf16 shapes return uint16 bit arrays, f32 shapes float32 arrays.  q8
+    shapes draw the same bf16 model and store each weight matrix as int8
+    (quantize_rows of its bf16 values) with its float32 row scales under
+    name + ".scale"; norm weights and fast_embeddings stay bf16.
     """
     rng = np.random.default_rng(seed)
     out: Dict[str, np.ndarray] = {}
@@ -152,7 +181,14 @@ def make_weights(shape: ModelShape, seed: int) -> Dict[str, np.ndarray]:
             w += np.float32(1.0)
         else:                        # 0.02 z, float32
             w *= np.float32(0.02)
-        out[name] = bf16_bits_from_f32(w, inplace=True) if shape.weight_dtype == "bf16" else w
+        if shape.weight_dtype == "f32":
+            out[name] = w
+            continue
+        bits = bf16_bits_from_f32(w, inplace=True)
+        if shape.weight_dtype == "q8" and is_matrix(name):
+            out[name], out[name + ".scale"] = quantize_rows(f32_from_bf16_bits(bits))
+        else:
+            out[name] = bits
     return out
 
 
@@ -184,6 +220,12 @@ WORKLOADS: Dict[str, Workload] = {
     # not one of the measured workloads: awkward sizes for the parity tests
     "ragged": Workload(9, "ragged", RAGGED, batch=3, frames=4, sampling="mixed",
                        temperature=0.9, top_p=0.85),
+    # weight-only int8 (the next row after the measured bf16 workloads): the
+    # batch-1 workload's settings on the int8 model
+    "s2pro_q8": Workload(6, "s2pro_q8", S2PRO_Q8, batch=1, frames=256),
+    "tiny_q8": Workload(7, "tiny_q8", TINY_Q8, batch=1, frames=1),
+    "ragged_q8": Workload(8, "ragged_q8", RAGGED_Q8, batch=3, frames=4, sampling="mixed",
+                          temperature=0.9, top_p=0.85),
 }
 
 
