@@ -62,10 +62,13 @@ def survey_bytes_per_frame(shape, batch: int) -> int:
     three sampling settings, ten codes).  7,455,375,360 + 10,332 bytes at
     the S2 Pro shape and batch 1."""
     s = shape
-    wb = 2 if s.weight_dtype == "bf16" else 4
+    wb = {"bf16": 2, "f32": 4, "q8": 1}[s.weight_dtype]
     per_step = (s.n_layer * (s.qkv_dim * s.dim + s.dim * s.attn_dim + 3 * s.ffn_dim * s.dim)
                 + s.codebook_size * s.dim) * wb
     proj = s.dim * s.in_dim * wb if s.has_project_in else 0
+    if s.weight_dtype == "q8":   # plus one float32 scale per matrix row
+        per_step += (s.n_layer * (s.qkv_dim + 2 * s.dim + 2 * s.ffn_dim) + s.codebook_size) * 4
+        proj += s.dim * 4 if s.has_project_in else 0
     io = batch * (s.in_dim * 4 + 4 + s.n_steps * 4 + 3 * 4 + s.num_codebooks * 4)
     return s.n_steps * per_step + proj + io
 
@@ -376,6 +379,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch 16/64 lines")
     ap.add_argument("--sweep-frames", type=int, default=16, help="timed frames of each batch line")
     ap.add_argument("--cpu-frames", type=int, default=96)
+    ap.add_argument("--no-q8", action="store_true", help="skip the weight-only int8 line")
+    ap.add_argument("--q8-frames", type=int, default=64)
     ap.add_argument("--no-full-frame", action="store_true", help="skip the full-frame (Slow-AR + Fast-AR) line")
     ap.add_argument("--full-frames", type=int, default=512)
     ap.add_argument("--cpu-full-frames", type=int, default=3)
@@ -492,6 +497,32 @@ def main():
             del di
             torch.cuda.empty_cache()
         result["batch_sweep"] = sweep
+    if not args.no_q8:
+        # weight-only int8 model (int8 matrices with per-row scales), batch 1
+        wq = si.WORKLOADS["s2pro_q8"]
+        print(f"[bench] generating {wq.name} weights", file=sys.stderr, flush=True)
+        hq = si.make_weights(wq.shape, wq.seed(0))
+        dq = bd.device_weights(wq.shape, hq)
+        cq = bd.FastAR(wq.shape, dq, max_batch=1)
+        nq = args.q8_frames
+        frq = si.make_frames(wq, n_frames=nq)
+        diq = upload(torch, frq)
+        print(f"[bench] timing {nq} frames of the int8 model at batch 1", file=sys.stderr, flush=True)
+        sec, per_call = time_frames(torch, cq, diq, 1, nq, 4)
+        fbq = survey_bytes_per_frame(wq.shape, 1)
+        result["q8"] = {"workload": "S2 Pro-shaped Fast-AR with weight-only int8 matrices (one float32 scale per "
+                                    "row; bf16 norms and embeddings), batch 1, independent frames",
+                        "frames_per_s": round(nq / sec, 2), "ms_per_frame": round(sec * 1e3 / nq, 4),
+                        "frames": nq, "kernel": "frame_kernel<int8>", "bytes_per_launch": fbq,
+                        "avg_launch_us": round(per_call * 1e6, 2),
+                        "achieved_gbs": round(fbq / per_call / 1e9, 1),
+                        "frac": round(fbq / per_call / 1e9 / PEAK_HBM_GBS, 4)}
+        if n_chk:
+            batched_chk.append(("q8", wq, hq, diq[6][0].cpu().numpy(),
+                                cq.forward_logits(diq[0][0], diq[6][0]).cpu().numpy()))
+        cq.close()
+        del dq, diq
+        torch.cuda.empty_cache()
     if not args.no_full_frame:
         result["full_frame"] = full_frame_bench(torch, bd, ctx, shape, args.full_frames, 4,
                                                 None if args.no_cpu_baseline else host, args.cpu_full_frames)

@@ -16,7 +16,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libs2fast.so")
 MAX_LAYERS = 8
-BF16, F32 = 0, 1
+BF16, F32, Q8 = 0, 1, 2
+DTYPES = {"bf16": BF16, "f32": F32, "q8": Q8}
 
 ERRORS = {
     0: "OK", 1: "ERR_ARG", 2: "ERR_NO_FAST_DECODER", 3: "ERR_HIDDEN_DIM", 4: "ERR_PREFIX_LEN",
@@ -46,10 +47,23 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
 
 
+Q8_FIELDS = (("wqkv", "attention.wqkv"), ("wo", "attention.wo"), ("w1", "feed_forward.w1"),
+             ("w3", "feed_forward.w3"), ("w2", "feed_forward.w2"))
+
+
+class Q8LayerScales(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n, _ in Q8_FIELDS]
+
+
+class Q8Scales(ctypes.Structure):
+    _fields_ = [("project_in", ctypes.c_void_p), ("output", ctypes.c_void_p),
+                ("layers", Q8LayerScales * MAX_LAYERS)]
+
+
 class Weights(ctypes.Structure):
     _fields_ = [("project_in", ctypes.c_void_p), ("embeddings", ctypes.c_void_p),
                 ("norm", ctypes.c_void_p), ("output", ctypes.c_void_p),
-                ("layers", LayerWeights * MAX_LAYERS)]
+                ("layers", LayerWeights * MAX_LAYERS), ("q8_scales", ctypes.POINTER(Q8Scales))]
 
 
 SLOW_MAX_LAYERS = 64
@@ -127,7 +141,7 @@ def library() -> ctypes.CDLL:
         lib.s2fast_test_watchdog.restype = ctypes.c_int
         lib.s2fast_test_slow_watchdog.argtypes = [P, I]
         lib.s2fast_test_slow_watchdog.restype = ctypes.c_int
-        lib.s2fast_test_gemv.argtypes = [I, I, I, I, P, P, P, F, P, P, V]
+        lib.s2fast_test_gemv.argtypes = [I, I, I, I, P, P, P, P, P, F, P, P, V]
         lib.s2fast_test_gemv.restype = ctypes.c_int
         lib.s2fast_test_norm_rope_attn.argtypes = [I, I, I, I, I, F, F, P, P, P, P, V]
         lib.s2fast_test_norm_rope_attn.restype = ctypes.c_int
@@ -179,11 +193,12 @@ def make_config(shape, max_batch: int) -> Config:
                   codebook_size=shape.codebook_size, num_codebooks=shape.num_codebooks,
                   context=shape.context, rope_base=shape.rope_base, norm_eps=shape.norm_eps,
                   has_project_in=int(shape.has_project_in), has_qk_norm=int(shape.has_qk_norm),
-                  weight_dtype=BF16 if shape.weight_dtype == "bf16" else F32, max_batch=max_batch)
+                  weight_dtype=DTYPES[shape.weight_dtype], max_batch=max_batch)
 
 
 def device_weights(shape, weights: Dict[str, "object"], device="cuda") -> Dict[str, torch.Tensor]:
-    """Copy host weights (numpy: uint16 bf16 bits or float32) to device tensors."""
+    """Copy host weights (numpy: uint16 bf16 bits, int8 matrices with their
+    float32 row scales, or float32) to device tensors."""
     import numpy as np
     out = {}
     for k, v in weights.items():
@@ -191,6 +206,8 @@ def device_weights(shape, weights: Dict[str, "object"], device="cuda") -> Dict[s
             out[k] = v.to(device).contiguous()
         elif v.dtype == np.uint16:
             out[k] = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(device).contiguous()
+        elif v.dtype == np.int8:
+            out[k] = torch.from_numpy(np.ascontiguousarray(v)).to(device)
         else:
             out[k] = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(device)
     return out
@@ -223,6 +240,15 @@ class FastAR:
             L.w1 = g(p + "feed_forward.w1")
             L.w3 = g(p + "feed_forward.w3")
             L.w2 = g(p + "feed_forward.w2")
+        if shape.weight_dtype == "q8":
+            q = Q8Scales()
+            q.project_in = g("fast_project_in.scale")
+            q.output = g("fast_output.scale")
+            for i in range(shape.n_layer):
+                for f, n in Q8_FIELDS:
+                    setattr(q.layers[i], f, g(f"fast_layers.{i}.{n}.scale"))
+            self._q8 = q
+            w.q8_scales = ctypes.pointer(q)
         ctx = ctypes.c_void_p()
         _check(lib.s2fast_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ctx)), "s2fast_create")
         self._ctx = ctx
@@ -499,22 +525,26 @@ def sample(logits, temperature, top_p, top_k, u, stream=None):
     return codes
 
 
-def gemv(W, x, W3=None, norm_w=None, eps: float = 1e-6, stream=None):
+def gemv(W, x, W3=None, norm_w=None, eps: float = 1e-6, scale=None, scale3=None, stream=None):
     """The frame kernel's GEMV on its own (test export): y [M, N] = W . n
     with n = x * norm_w / rms(x) if norm_w is given, or the SwiGLU pair
-    silu(W . n) * (W3 . n) if W3 is given."""
+    silu(W . n) * (W3 . n) if W3 is given.  int8 W (and W3) take their
+    float32 row scales."""
     N, K = W.shape
     M = x.shape[0]
-    dt = {torch.bfloat16: BF16, torch.float32: F32}[W.dtype]
+    dt = {torch.bfloat16: BF16, torch.float32: F32, torch.int8: Q8}[W.dtype]
     _dev(W, W.dtype, (N, K), "W")
     if W3 is not None:
         _dev(W3, W.dtype, (N, K), "W3")
     if norm_w is not None:
-        _dev(norm_w, W.dtype, (K,), "norm_w")
+        _dev(norm_w, torch.bfloat16 if dt == Q8 else W.dtype, (K,), "norm_w")
+    for t, n in ((scale, "scale"), (scale3, "scale3")):
+        if t is not None:
+            _dev(t, torch.float32, (N,), n)
     _dev(x, torch.float32, (M, K), "x")
     y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _check(library().s2fast_test_gemv(dt, N, K, M, _ptr(W), _ptr(W3), _ptr(norm_w), float(eps), _ptr(x), _ptr(y),
-                                      _stream(stream)), "s2fast_test_gemv")
+    _check(library().s2fast_test_gemv(dt, N, K, M, _ptr(W), _ptr(W3), _ptr(scale), _ptr(scale3), _ptr(norm_w),
+                                      float(eps), _ptr(x), _ptr(y), _stream(stream)), "s2fast_test_gemv")
     return y
 
 

@@ -105,6 +105,29 @@ template <> struct WTraits<float> {
   __device__ __forceinline__ static float one(const float* p, int i) { return gbl(p)[i]; }
 };
 
+// Weight-only int8 matrices: 16 signed weights per 16-byte load; each output
+// row's float32 scale is applied to the row's dot product by the caller.
+// The vectors of an int8 model (norm weights, embedding rows) are bf16
+// (VecOf).
+struct q8_t {
+  int8_t v;
+};
+template <> struct WTraits<q8_t> {
+  static constexpr int EPL = 16;
+  __device__ __forceinline__ static void unpack(const uint4& q, float* f) {
+    const u32 d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[4 * i + j] = (float)(int)(signed char)(d[i] >> (8 * j));
+  }
+  __device__ __forceinline__ static float one(const q8_t* p, int i) { return (float)gbl(p)[i].v; }
+};
+
+// Element type of a model's vectors (norm weights, embedding rows).
+template <typename WT> struct VecOf { using type = WT; };
+template <> struct VecOf<q8_t> { using type = uint16_t; };
+
 // Weights are read exactly once per decode step and never reused inside it:
 // stream them with the non-temporal hint.
 __device__ __forceinline__ uint4 ld_stream(const void* p) {

@@ -41,6 +41,8 @@ namespace {
 
 struct LayerPtr {
   const void *attn_norm, *wqkv, *q_norm, *k_norm, *wo, *ffn_norm, *w1, *w3, *w2;
+  // per-row float32 scales of int8 matrices (nullptr: the matrices carry their values)
+  const float *s_qkv, *s_wo, *s_w1, *s_w3, *s_w2;
 };
 
 struct FrameArgs {
@@ -56,6 +58,8 @@ struct FrameArgs {
   const void* emb;
   const void* fnorm;
   const void* outw;
+  const float* proj_scale;   // row scales of int8 fast_project_in / fast_output, or nullptr
+  const float* out_scale;
   LayerPtr L[S2FAST_MAX_LAYERS];
   const float* rope;  // [2][ctx_len][hd/2]: cos then sin
   // Layer-0 q/k/v of every embedding row, [V][qkv_dim]:
@@ -120,6 +124,7 @@ struct Lds {
   float* fnw;    // [dim] fast_norm weight (loaded once per frame)
   float* qkn;    // [n_layer][2][hd] q_norm and k_norm weights (loaded once per frame)
   float* rope;   // [2][ctx][hd/2] cos and sin (loaded once per frame)
+  float* rsc;    // [rmax] the phase's row scales (int8 matrices; 1 otherwise)
 };
 
 __host__ __device__ inline size_t lds_floats(int kmax, int rmax, int gheads, int hd, int ctx, int V, int dim,
@@ -127,7 +132,7 @@ __host__ __device__ inline size_t lds_floats(int kmax, int rmax, int gheads, int
   const size_t act = ((size_t)MMAX * kmax + 3) & ~(size_t)3;   // keeps the regions after it 16-byte aligned
   return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)MMAX * gheads * hd + 2 * (size_t)ctx * hd +
          2 * TOPK_MAX + 256 + 16 + 4 + (size_t)dim + (size_t)n_layer * 2 * hd +
-         (size_t)ctx * hd;
+         (size_t)ctx * hd + (size_t)rmax;
 }
 
 __device__ inline Lds carve(float* base, const FrameArgs& a) {
@@ -147,7 +152,8 @@ __device__ inline Lds carve(float* base, const FrameArgs& a) {
   s.flag = reinterpret_cast<int*>(p); p += 4;
   s.fnw = p; p += a.dim;
   s.qkn = p; p += (size_t)a.n_layer * 2 * a.hd;
-  s.rope = p;
+  s.rope = p; p += (size_t)a.ctx_len * a.hd;
+  s.rsc = p;
   return s;
 }
 
@@ -295,12 +301,16 @@ __device__ __forceinline__ void mark(const Args& a, u32 phase, int w) {
 // For bf16 weights a lane consumes 8 columns (16 bytes of weights) per load;
 // its 8 activation floats are kept as two 16-byte halves in two separate
 // half-rows, so each half is one conflict-free ds_read_b128 across the wave
-// (lane-consecutive 16-byte addresses).  f32 weights consume 4 columns, which
-// is already one lane-consecutive 16-byte read: identity.
+// (lane-consecutive 16-byte addresses); int8 weights (16 columns a load) use
+// four quarter-rows the same way.  f32 weights consume 4 columns, which is
+// already one lane-consecutive 16-byte read: identity.
 template <typename WT>
 __device__ __forceinline__ int phys(int k, int K) {
-  if (WTraits<WT>::EPL == 8) return ((k >> 3) << 2) + (k & 3) + ((k & 4) ? (K >> 1) : 0);
-  return k;
+  // G = EPL / 4 groups of four columns per lane load; group g of segment sg
+  // sits at sg * 4 in the g-th of G equal parts of the row
+  constexpr int EPL = WTraits<WT>::EPL, G = EPL / 4;
+  if (G == 1) return k;
+  return ((k / EPL) << 2) + (k & 3) + ((k >> 2) % G) * (K / G);
 }
 
 typedef float v4f __attribute__((ext_vector_type(4)));         // native vectors stay in registers
@@ -391,7 +401,8 @@ __device__ __forceinline__ float norm_den(const float* small, int m, int K, floa
 // sums of squares are left as per-wave partials in small[m * NWAVE + wave].
 template <typename WT, bool ADD_ACC, typename Hook>
 __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds& s, int l, int step, int M,
-                                                  const WT* normw, const Hook& hook) {
+                                                  const typename VecOf<WT>::type* normw, const Hook& hook) {
+  using VT = typename VecOf<WT>::type;
   constexpr int NS = 3;
   const int hq = a.dim >> 2;
   const int nq = M * hq;
@@ -405,18 +416,18 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
   auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
     v4f xv[NS];
     v2ll a0[NS], a1[NS];
-    typename WQuad<WT>::type wv[NS], ev[NS];
+    typename WQuad<VT>::type wv[NS], ev[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int q = quad_of(base, j, nq);
       const int m = q >= hq ? 1 : 0, c = q - m * hq;   // M <= 2
       const int pos = row_pos(step, m);
-      wv[j] = WQuad<WT>::load(normw, c);   // the RMSNorm weight, same round trip
+      wv[j] = WQuad<VT>::load(normw, c);   // the RMSNorm weight, same round trip
       xv[j] = *reinterpret_cast<const v4f*>(fsrc + (size_t)m * fstride + 4 * c);
       // layer 0, position >= 1: the embedding row of the previous code
       // (otherwise row 0, loaded and not used, so that the load needs no branch)
       const int code = (l == 0 && pos > 0) ? s.codes[max(pos - 1, 0)] : 0;
-      ev[j] = WQuad<WT>::load(reinterpret_cast<const WT*>(a.emb) + (size_t)code * a.dim, c);
+      ev[j] = WQuad<VT>::load(reinterpret_cast<const VT*>(a.emb) + (size_t)code * a.dim, c);
       if (ADD_ACC) {
         const long long* ac = accb(a, step, l) + (size_t)m * a.dim + 4 * c;
         a0[j] = *reinterpret_cast<const v2ll*>(ac);
@@ -434,7 +445,7 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
       const bool emb = (l == 0 && row_pos(step, m) > 0);
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = emb ? WQuad<WT>::get(ev[j], e) : xv[j][e];
+      for (int e = 0; e < 4; ++e) v[e] = emb ? WQuad<VT>::get(ev[j], e) : xv[j][e];
       if (ADD_ACC) {
         v[0] += from_fx(a0[j][0]); v[1] += from_fx(a0[j][1]);
         v[2] += from_fx(a1[j][0]); v[3] += from_fx(a1[j][1]);
@@ -446,7 +457,7 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
         if (m == 0) ss0 = t; else ss1 = t;
         v4f o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = v[e] * WQuad<WT>::get(wv[j], e);
+        for (int e = 0; e < 4; ++e) o[e] = v[e] * WQuad<VT>::get(wv[j], e);
         *reinterpret_cast<v4f*>(s.act + (size_t)m * a.kmax + phys<WT>(4 * c, a.dim)) = o;
       }
     }
@@ -558,7 +569,7 @@ __device__ __forceinline__ void gemv_rows(Plan& p, u32x4 (&slot)[R], const float
   const int wave = __builtin_amdgcn_readfirstlane(tidx() >> 6), lane = tidx() & 63;
   const int t0 = p.t0, t1 = p.t1;
   if (t0 >= t1) return;
-  const int C = p.C, S = p.S, Kh = p.K >> 1;
+  const int C = p.C, S = p.S;
   int cr = t0 / C, cc = t0 - cr * C;
   float acc[MM];
 #pragma unroll
@@ -571,6 +582,8 @@ __device__ __forceinline__ void gemv_rows(Plan& p, u32x4 (&slot)[R], const float
       acc[m] = 0.0f;
     }
   };
+  constexpr int G = EPL / 4;   // four-column groups a load covers (phys places group g in part g of G)
+  const int Kg = p.K / G;
   auto consume = [&](const u32x4& q) __attribute__((always_inline)) {
     const int seg = cc * 64 + lane;
     const bool live = seg < S;
@@ -582,14 +595,12 @@ __device__ __forceinline__ void gemv_rows(Plan& p, u32x4 (&slot)[R], const float
 #pragma unroll
     for (int m = 0; m < MM; ++m) {
       const float* row = act + (size_t)m * act_ld;
-      const float4 x0 = *reinterpret_cast<const float4*>(row + (size_t)sg * 4);
       float s0 = acc[m];
-      s0 = fmaf(w[0], x0.x, s0); s0 = fmaf(w[1], x0.y, s0);
-      s0 = fmaf(w[2], x0.z, s0); s0 = fmaf(w[3], x0.w, s0);
-      if (EPL == 8) {
-        const float4 x1 = *reinterpret_cast<const float4*>(row + Kh + (size_t)sg * 4);
-        s0 = fmaf(w[4 % EPL], x1.x, s0); s0 = fmaf(w[5 % EPL], x1.y, s0);
-        s0 = fmaf(w[6 % EPL], x1.z, s0); s0 = fmaf(w[7 % EPL], x1.w, s0);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float4 x = *reinterpret_cast<const float4*>(row + (size_t)g * Kg + (size_t)sg * 4);
+        s0 = fmaf(w[4 * g + 0], x.x, s0); s0 = fmaf(w[4 * g + 1], x.y, s0);
+        s0 = fmaf(w[4 * g + 2], x.z, s0); s0 = fmaf(w[4 * g + 3], x.w, s0);
       }
       acc[m] = s0;
     }
@@ -633,9 +644,10 @@ __device__ __forceinline__ float red_sum(const float* red, int r, int m) {
 // the few rows a block owns in the w2 phase).
 template <typename WT>
 __device__ __forceinline__ float layer0_input(const FrameArgs& a, const Lds& s, int pos, int k) {
+  using VT = typename VecOf<WT>::type;
   if (pos == 0) return a.has_proj ? a.xin0[k] : a.hidden[k];
-  const WT* e = reinterpret_cast<const WT*>(a.emb) + (size_t)s.codes[pos - 1] * a.dim;
-  return WTraits<WT>::one(e, k);
+  const VT* e = reinterpret_cast<const VT*>(a.emb) + (size_t)s.codes[pos - 1] * a.dim;
+  return WTraits<VT>::one(e, k);
 }
 
 // One head vector per wave: RMSNorm with weight w (optional), then pair RoPE
@@ -739,6 +751,23 @@ __device__ __forceinline__ void attend_rows(const float* q, const float* kc, con
   }
 }
 
+// Row scales of a phase's int8 matrices: the block's rows [0, nr_a) are
+// rows r0.. of matrix a, rows [nr_a, nrows) rows r0.. of matrix b (w1 and
+// w3).  row_scale_issue loads thread t's value at the phase start (its
+// latency overlaps the activation staging); row_scale_store puts the values
+// into LDS before the GEMV.  Without scales (bf16 and f32 models) every row
+// scale is 1, which leaves the outputs unchanged.
+__device__ __forceinline__ float row_scale_issue(const float* sa, const float* sb, int r0, int nr_a, int nrows) {
+  if (!sa || nrows <= 0) return 1.0f;
+  const int i = min(tidx(), nrows - 1);
+  return i < nr_a ? sa[r0 + i] : sb[r0 + i - nr_a];
+}
+__device__ __forceinline__ void row_scale_store(float* rsc, float v, const float* sa, const float* sb, int r0,
+                                                int nr_a, int nrows) {
+  if (tidx() < nrows) rsc[tidx()] = v;
+  for (int i = tidx() + NTHREADS; i < nrows; i += NTHREADS) rsc[i] = i < nr_a ? sa[r0 + i] : sb[r0 + i - nr_a];
+}
+
 // --------------------------------------------------------------- phases
 enum PhaseKind { PH_PROJ = 0, PH_QKV, PH_WO, PH_FFN_UP, PH_FFN_DOWN, PH_HEAD };
 
@@ -824,11 +853,15 @@ __device__ __forceinline__ Plan plan_for(const FrameArgs& a, PhaseId id) {
 
 template <typename WT>
 __device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
+  using VT = typename VecOf<WT>::type;
   const int D = a.dim;
   const int r0 = pl.r0, r1 = pl.r1;
+  const float* sq = a.L[l].s_qkv;
+  const float scv = row_scale_issue(sq, nullptr, r0, r1 - r0, r1 - r0);
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
-  stage_layer_input<WT, false>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].attn_norm), pro);
+  stage_layer_input<WT, false>(a, s, l, step, M, reinterpret_cast<const VT*>(a.L[l].attn_norm), pro);
+  row_scale_store(s.rsc, scv, sq, nullptr, r0, r1 - r0, r1 - r0);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 4);
@@ -838,7 +871,8 @@ __device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int 
   mark(a, s.flag[1], 3);
   for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
-    st_coh(qkvb(a, step, l) + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m) / norm_den(s.small, m, D, a.eps));
+    st_coh(qkvb(a, step, l) + (size_t)m * a.qkv_dim + r0 + r,
+           s.rsc[r] * red_sum(s.red, r, m) / norm_den(s.small, m, D, a.eps));
   }
 }
 
@@ -853,6 +887,8 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
   const float* kn = qn + hd;
   float* kvl = a.kv + (size_t)l * a.ctx_len * a.kv_pos;   // [ctx][kv_pos]
   const bool need_attn = (r1 > r0) || rg == 0;
+  const float* so = a.L[l].s_wo;
+  const float scv = row_scale_issue(so, nullptr, r0, r1 - r0, r1 - r0);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);   // the GEMV's partial sums (read after the barriers below)
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
@@ -950,6 +986,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
     attend_rows<WT>(s.q, s.kc, s.vc, M, first_new, gh, hd, s.act, a.kmax, a.gw);
     mark(a, s.flag[1], 7);
   }
+  row_scale_store(s.rsc, scv, so, nullptr, r0, r1 - r0, r1 - r0);
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
@@ -957,18 +994,22 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
   mark(a, s.flag[1], 3);
   for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
-    atomic_add_coh(accb(a, step, l) + (size_t)m * a.dim + r0 + r, to_fx(red_sum(s.red, r, m)));
+    atomic_add_coh(accb(a, step, l) + (size_t)m * a.dim + r0 + r, to_fx(s.rsc[r] * red_sum(s.red, r, m)));
   }
 }
 
 template <typename WT>
 __device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
+  using VT = typename VecOf<WT>::type;
   const int D = a.dim;
   const int r0 = pl.r0, r1 = pl.r1;
   const int nr = r1 - r0;
+  const LayerPtr& L = a.L[l];
+  const float scv = row_scale_issue(L.s_w1, L.s_w3, r0, nr, 2 * nr);
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
-  stage_layer_input<WT, true>(a, s, l, step, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
+  stage_layer_input<WT, true>(a, s, l, step, M, reinterpret_cast<const VT*>(L.ffn_norm), pro);
+  row_scale_store(s.rsc, scv, L.s_w1, L.s_w3, r0, nr, 2 * nr);
   zero_lds(s.red, 2 * nr * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
@@ -978,18 +1019,22 @@ __device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, i
   for (int i = tidx(); i < nr * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
     const float den = norm_den(s.small, m, D, a.eps);
-    st_coh(gb(a, step, l) + (size_t)m * a.ffn + r0 + r, silu(red_sum(s.red, r, m) / den) * (red_sum(s.red, nr + r, m) / den));
+    st_coh(gb(a, step, l) + (size_t)m * a.ffn + r0 + r,
+           silu(s.rsc[r] * red_sum(s.red, r, m) / den) * (s.rsc[nr + r] * red_sum(s.red, nr + r, m) / den));
   }
 }
 
 template <typename WT>
 __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s, int l, int step, int M, Plan& pl) {
   const int r0 = pl.r0, r1 = pl.r1;
+  const float* s2 = a.L[l].s_w2;
+  const float scv = row_scale_issue(s2, nullptr, r0, r1 - r0, r1 - r0);
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   stage_arena<WT, true, 5>(s.act, gb(a, step, l), a.ffn, pro);
   for (int m = 1; m < M; ++m)
     stage_arena<WT, true, 5>(s.act + (size_t)m * a.kmax, gb(a, step, l) + (size_t)m * a.ffn, a.ffn, NoHook{});
+  row_scale_store(s.rsc, scv, s2, nullptr, r0, r1 - r0, r1 - r0);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
@@ -1000,7 +1045,7 @@ __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s,
     const int r = i / M, m = i % M;
     const int k = r0 + r;
     const float xm = x_mid_of<WT>(a, s, l, step, m, k);
-    st_coh(xb(a, step, l) + (size_t)m * a.dim + k, xm + red_sum(s.red, r, m));
+    st_coh(xb(a, step, l) + (size_t)m * a.dim + k, xm + s.rsc[r] * red_sum(s.red, r, m));
     st_coh(accb(a, step, l) + (size_t)m * a.dim + k, 0ll);   // ready for the next frame
   }
 }
@@ -1009,6 +1054,7 @@ template <typename WT>
 __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int step, int M, Plan& pl) {
   const int D = a.dim;
   const int r0 = pl.r0, r1 = pl.r1;
+  const float scv = row_scale_issue(a.out_scale, nullptr, r0, r1 - r0, r1 - r0);
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   {
@@ -1042,6 +1088,7 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
     for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
     store_ss(s.small, 1, ss, 0.0f);
   }
+  row_scale_store(s.rsc, scv, a.out_scale, nullptr, r0, r1 - r0, r1 - r0);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
@@ -1050,7 +1097,7 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
   mark(a, s.flag[1], 3);
   const float hden = norm_den(s.small, 0, D, a.eps);
   for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
-    const float v = red_sum(s.red, r, 0) / hden;
+    const float v = s.rsc[r] * red_sum(s.red, r, 0) / hden;
     st_coh(logitsb(a, step) + r0 + r, v);
     if (a.logits_out && step >= a.lo_first) a.logits_out[(size_t)(step - a.lo_first) * a.V + r0 + r] = v;
   }
@@ -1059,16 +1106,18 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
 template <typename WT>
 __device__ __forceinline__ void phase_project_in(const FrameArgs& a, const Lds& s, Plan& pl) {
   const int r0 = pl.r0, r1 = pl.r1;
+  const float scv = row_scale_issue(a.proj_scale, nullptr, r0, r1 - r0, r1 - r0);
   u32x4 slot[RING];
   gemv_prologue(pl, slot);
   for (int k = tidx(); k < a.in_dim; k += NTHREADS) s.act[phys<WT>(k, a.in_dim)] = a.hidden[k];
+  row_scale_store(s.rsc, scv, a.proj_scale, nullptr, r0, r1 - r0, r1 - r0);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, 1, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  for (int r = tidx(); r < r1 - r0; r += NTHREADS) st_coh(a.xin0 + r0 + r, red_sum(s.red, r, 0));
+  for (int r = tidx(); r < r1 - r0; r += NTHREADS) st_coh(a.xin0 + r0 + r, s.rsc[r] * red_sum(s.red, r, 0));
 }
 
 template <typename WT>
@@ -1086,15 +1135,16 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
       for (int j = 1; j < a.nsteps; ++j) s.codes[j] = min(max(a.forced[j], 0), V - 1);
   }
   // per-frame constants into LDS: q/k norm weights of every layer, RoPE table
+  using VT = typename VecOf<WT>::type;
   if (a.has_qkn) {
     for (int i = tidx(); i < a.n_layer * 2 * a.hd; i += NTHREADS) {
       const int l = i / (2 * a.hd), r = i - l * 2 * a.hd;
-      const WT* w = reinterpret_cast<const WT*>(r < a.hd ? a.L[l].q_norm : a.L[l].k_norm);
-      s.qkn[i] = WTraits<WT>::one(w, r < a.hd ? r : r - a.hd);
+      const VT* w = reinterpret_cast<const VT*>(r < a.hd ? a.L[l].q_norm : a.L[l].k_norm);
+      s.qkn[i] = WTraits<VT>::one(w, r < a.hd ? r : r - a.hd);
     }
   }
   for (int i = tidx(); i < a.ctx_len * a.hd; i += NTHREADS) s.rope[i] = a.rope[i];
-  for (int i = tidx(); i < a.dim; i += NTHREADS) s.fnw[i] = WTraits<WT>::one(reinterpret_cast<const WT*>(a.fnorm), i);
+  for (int i = tidx(); i < a.dim; i += NTHREADS) s.fnw[i] = WTraits<VT>::one(reinterpret_cast<const VT*>(a.fnorm), i);
   __syncthreads();
   const int nph = phase_count(a);
   // A phase's plan (row range and chunk split) is plain integers and is
@@ -1165,6 +1215,8 @@ struct GemvTestArgs {
   int N, K, M, kmax, rmax;
   const void* W;
   const void* W3;        // second matrix of a SwiGLU pair, or nullptr
+  const float* sc;       // row scales of int8 W and W3, or nullptr
+  const float* sc3;
   const void* normw;     // RMSNorm weight [K], or nullptr
   float eps;
   const float* x;        // [M][K]
@@ -1177,11 +1229,15 @@ __global__ void __launch_bounds__(NTHREADS) gemv_test_kernel(GemvTestArgs a) {
   float* act = lds_base;                                             // [MMAX][kmax]
   float* red = act + (((size_t)MMAX * a.kmax + 3) & ~(size_t)3);    // [rmax][MMAX][NWAVE]
   float* small = red + (size_t)a.rmax * NWAVE * MMAX;                // [64]
+  float* rsc = small + 64;                                            // [rmax]
+  using VT = typename VecOf<WT>::type;
   int r0, r1;
   split_rows(a.N, blockIdx.x, gridDim.x, r0, r1);
   const int nr = r1 - r0;
   const WT* W3 = reinterpret_cast<const WT*>(a.W3);
-  Plan pl = make_plan<WT>(reinterpret_cast<const WT*>(a.W), W3, a.K, 0, a.K, r0, nr, W3 ? 2 * nr : nr);
+  const int nrows = W3 ? 2 * nr : nr;
+  const float scv = row_scale_issue(a.sc, a.sc3, r0, nr, nrows);
+  Plan pl = make_plan<WT>(reinterpret_cast<const WT*>(a.W), W3, a.K, 0, a.K, r0, nr, nrows);
   u32x4 slot[RING];
   gemv_prologue(pl, slot);
   float ss0 = 0.0f, ss1 = 0.0f;
@@ -1194,21 +1250,22 @@ __global__ void __launch_bounds__(NTHREADS) gemv_test_kernel(GemvTestArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       t = fmaf(e[j], e[j], t);
-      if (a.normw) e[j] *= WTraits<WT>::one(reinterpret_cast<const WT*>(a.normw), 4 * c + j);
+      if (a.normw) e[j] *= WTraits<VT>::one(reinterpret_cast<const VT*>(a.normw), 4 * c + j);
     }
     if (m == 0) ss0 += t; else ss1 += t;
     *reinterpret_cast<float4*>(act + (size_t)m * a.kmax + phys<WT>(4 * c, a.K)) = make_float4(e[0], e[1], e[2], e[3]);
   }
   store_ss(small, a.M, ss0, ss1);
-  zero_lds(red, (W3 ? 2 : 1) * nr * NWAVE * MMAX);
+  row_scale_store(rsc, scv, a.sc, a.sc3, r0, nr, nrows);
+  zero_lds(red, nrows * NWAVE * MMAX);
   __syncthreads();
   gemv_body<WT>(pl, slot, act, a.kmax, a.M, red);
   __syncthreads();
   for (int i = tidx(); i < nr * a.M; i += NTHREADS) {
     const int r = i / a.M, m = i % a.M;
     const float den = a.normw ? norm_den(small, m, a.K, a.eps) : 1.0f;
-    const float d = red_sum(red, r, m) / den;
-    a.y[(size_t)m * a.N + r0 + r] = W3 ? silu(d) * (red_sum(red, nr + r, m) / den) : d;
+    const float d = rsc[r] * red_sum(red, r, m) / den;
+    a.y[(size_t)m * a.N + r0 + r] = W3 ? silu(d) * (rsc[nr + r] * red_sum(red, nr + r, m) / den) : d;
   }
 }
 
@@ -1258,13 +1315,13 @@ __global__ void __launch_bounds__(NTHREADS) attn_test_kernel(AttnTestArgs a) {
 // Run once when a context is created.  den[c] = sqrt(mean_k e_c[k]^2 + eps)
 // of every embedding row (the layer-0 attention_norm RMS, "Model loading and
 // GGUF", section 2.2).
-template <typename WT>
-__global__ void __launch_bounds__(256) qkv0_den_kernel(const WT* emb, int D, float eps, float* den) {
+template <typename VT>
+__global__ void __launch_bounds__(256) qkv0_den_kernel(const VT* emb, int D, float eps, float* den) {
   __shared__ float red[4];
-  const WT* e = emb + (size_t)blockIdx.x * D;
+  const VT* e = emb + (size_t)blockIdx.x * D;
   float ss = 0.0f;
   for (int k = threadIdx.x; k < D; k += 256) {
-    const float v = WTraits<WT>::one(e, k);
+    const float v = WTraits<VT>::one(e, k);
     ss = fmaf(v, v, ss);
   }
   ss = wave_sum(ss);
@@ -1275,10 +1332,13 @@ __global__ void __launch_bounds__(256) qkv0_den_kernel(const WT* emb, int D, flo
 
 // out[c][r] = (sum_k W[r][k] * (g[k] * e_c[k])) / den[c]: the layer-0 wqkv
 // output of embedding row c, a float32 GEMM in 64 x 64 tiles (16 outputs a
-// thread).
+// thread).  An int8 W carries row scales: out = scale[r] * sum / den.
 template <typename WT>
-__global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const WT* emb, const WT* g, const float* den,
+__global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const float* wscale,
+                                                        const typename VecOf<WT>::type* emb,
+                                                        const typename VecOf<WT>::type* g, const float* den,
                                                         int V, int R, int D, float* out) {
+  using VT = typename VecOf<WT>::type;
   constexpr int TK = 32;
   __shared__ float Es[TK][65];   // [k][c]: g * e
   __shared__ float Ws[TK][65];   // [k][r]
@@ -1293,7 +1353,7 @@ __global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const WT* e
     for (int i = threadIdx.x; i < 64 * TK; i += 256) {
       const int row = i / TK, k = i % TK, kk = k0 + k;
       const int c = c0 + row, r = r0 + row;
-      Es[k][row] = (c < V && kk < D) ? WTraits<WT>::one(g, kk) * WTraits<WT>::one(emb + (size_t)c * D, kk) : 0.0f;
+      Es[k][row] = (c < V && kk < D) ? WTraits<VT>::one(g, kk) * WTraits<VT>::one(emb + (size_t)c * D, kk) : 0.0f;
       Ws[k][row] = (r < R && kk < D) ? WTraits<WT>::one(W + (size_t)r * D, kk) : 0.0f;
     }
     __syncthreads();
@@ -1317,7 +1377,7 @@ __global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const WT* e
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = r0 + tx * 4 + j;
-      if (c < V && r < R) out[(size_t)c * R + r] = acc[i][j] / den[c];
+      if (c < V && r < R) out[(size_t)c * R + r] = (wscale ? wscale[r] * acc[i][j] : acc[i][j]) / den[c];
     }
   }
 }
@@ -1349,6 +1409,7 @@ static_assert(KS_DOWN >= 1 && KS_DOWN <= 4, "the finalising workgroup adds at mo
 struct s2fast_ctx {
   s2fast_config cfg;
   s2fast_weights w;
+  s2fast_q8_scales q8 = {};   // row scales of an int8 model (copied at creation)
   int device = 0;
   int ncu = 0;
   size_t lds_bytes = 0;
@@ -1398,6 +1459,13 @@ bool is_gfx950(int dev) {
   hipDeviceProp_t p;
   if (hipGetDeviceProperties(&p, dev) != hipSuccess) return false;
   return std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+}
+
+// The batch-1 frame kernel instantiated for a weight type.
+const void* frame_fn(int dtype) {
+  if (dtype == S2FAST_BF16) return reinterpret_cast<const void*>(&frame_kernel<uint16_t>);
+  if (dtype == S2FAST_Q8) return reinterpret_cast<const void*>(&frame_kernel<q8_t>);
+  return reinterpret_cast<const void*>(&frame_kernel<float>);
 }
 
 // bf16 rounding straight from double: 8 significant bits, ties to even
@@ -1491,17 +1559,23 @@ int build_qkv0(s2fast_ctx* c) {
     return S2FAST_ERR_NOMEM;
   }
   const dim3 grid((R + 63) / 64, (V + 63) / 64);
-  if (k.weight_dtype == S2FAST_BF16) {
+  if (k.weight_dtype != S2FAST_F32) {   // bf16 vectors (bf16 and int8 models)
     const uint16_t* e = static_cast<const uint16_t*>(c->w.embeddings);
+    const uint16_t* g = static_cast<const uint16_t*>(c->w.layers[0].attention_norm);
     hipLaunchKernelGGL(qkv0_den_kernel<uint16_t>, dim3(V), dim3(256), 0, 0, e, D, k.norm_eps, den);
-    hipLaunchKernelGGL(qkv0_gemm_kernel<uint16_t>, grid, dim3(256), 0, 0,
-                       static_cast<const uint16_t*>(c->w.layers[0].wqkv), e,
-                       static_cast<const uint16_t*>(c->w.layers[0].attention_norm), den, V, R, D, c->qkv0);
+    if (k.weight_dtype == S2FAST_Q8)
+      hipLaunchKernelGGL(qkv0_gemm_kernel<q8_t>, grid, dim3(256), 0, 0,
+                         static_cast<const q8_t*>(c->w.layers[0].wqkv), c->q8.layers[0].wqkv, e, g, den, V, R, D,
+                         c->qkv0);
+    else
+      hipLaunchKernelGGL(qkv0_gemm_kernel<uint16_t>, grid, dim3(256), 0, 0,
+                         static_cast<const uint16_t*>(c->w.layers[0].wqkv), (const float*)nullptr, e, g, den, V, R,
+                         D, c->qkv0);
   } else {
     const float* e = static_cast<const float*>(c->w.embeddings);
     hipLaunchKernelGGL(qkv0_den_kernel<float>, dim3(V), dim3(256), 0, 0, e, D, k.norm_eps, den);
     hipLaunchKernelGGL(qkv0_gemm_kernel<float>, grid, dim3(256), 0, 0,
-                       static_cast<const float*>(c->w.layers[0].wqkv), e,
+                       static_cast<const float*>(c->w.layers[0].wqkv), (const float*)nullptr, e,
                        static_cast<const float*>(c->w.layers[0].attention_norm), den, V, R, D, c->qkv0);
   }
   const bool ok = hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess;
@@ -1518,9 +1592,8 @@ int launch_frame(s2fast_ctx* c, const FrameArgs& fa_in, hipStream_t stream) {
   }
   fa.epoch0 = c->epoch;
   void* args[] = {&fa};
-  const void* fn = c->cfg.weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&frame_kernel<uint16_t>)
-                                                       : reinterpret_cast<const void*>(&frame_kernel<float>);
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(c->ncu), dim3(NTHREADS), args, c->lds_bytes, stream);
+  hipError_t e = hipLaunchCooperativeKernel(frame_fn(c->cfg.weight_dtype), dim3(c->ncu), dim3(NTHREADS), args,
+                                            c->lds_bytes, stream);
   if (e != hipSuccess) return S2FAST_ERR_HIP;
   c->epoch += n;
   return S2FAST_OK;
@@ -1617,9 +1690,12 @@ void fill_shape(const s2fast_ctx* c, FrameArgs& fa) {
   fa.gw = fa.gheads * k.head_dim;
   fa.kmax = c->kmax; fa.rmax = c->rmax;
   fa.proj = c->w.project_in; fa.emb = c->w.embeddings; fa.fnorm = c->w.norm; fa.outw = c->w.output;
+  fa.proj_scale = c->q8.project_in; fa.out_scale = c->q8.output;
   for (int l = 0; l < k.n_layer; ++l) {
     const s2fast_layer_weights& L = c->w.layers[l];
-    fa.L[l] = LayerPtr{L.attention_norm, L.wqkv, L.q_norm, L.k_norm, L.wo, L.ffn_norm, L.w1, L.w3, L.w2};
+    const auto& Q = c->q8.layers[l];
+    fa.L[l] = LayerPtr{L.attention_norm, L.wqkv, L.q_norm, L.k_norm, L.wo, L.ffn_norm, L.w1, L.w3, L.w2,
+                       Q.wqkv, Q.wo, Q.w1, Q.w3, Q.w2};
   }
   fa.rope = c->rope;
   fa.qkv0 = c->qkv0;
@@ -1737,8 +1813,9 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   if (!cfg || !w || !out) return S2FAST_ERR_ARG;
   *out = nullptr;
   const s2fast_config& k = *cfg;
-  const int epl = k.weight_dtype == S2FAST_BF16 ? 8 : 4;
-  if (k.weight_dtype != S2FAST_BF16 && k.weight_dtype != S2FAST_F32) return S2FAST_ERR_ARG;
+  const int epl = k.weight_dtype == S2FAST_BF16 ? 8 : (k.weight_dtype == S2FAST_Q8 ? 16 : 4);
+  if (k.weight_dtype != S2FAST_BF16 && k.weight_dtype != S2FAST_F32 && k.weight_dtype != S2FAST_Q8)
+    return S2FAST_ERR_ARG;
   if (k.n_layer < 1 || k.n_layer > S2FAST_MAX_LAYERS) return S2FAST_ERR_ARG;
   if (k.n_head < 1 || k.n_head_kv < 1 || k.n_head % k.n_head_kv != 0 || k.n_head_kv > 64) return S2FAST_ERR_ARG;
   if (k.head_dim < 8 || k.head_dim > 128 || (k.head_dim % 8)) return S2FAST_ERR_ARG;
@@ -1759,6 +1836,19 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
     if (!L.attention_norm || !L.wqkv || !L.wo || !L.ffn_norm || !L.w1 || !L.w3 || !L.w2)
       return S2FAST_ERR_NO_FAST_DECODER;
     if (k.has_qk_norm && (!L.q_norm || !L.k_norm)) return S2FAST_ERR_NO_FAST_DECODER;
+  }
+  // an int8 model's row scales (one per output row of every matrix)
+  if ((k.weight_dtype == S2FAST_Q8) != (w->q8_scales != nullptr)) {
+    if (k.weight_dtype == S2FAST_Q8) return S2FAST_ERR_NO_FAST_DECODER;
+    return S2FAST_ERR_ARG;
+  }
+  if (w->q8_scales) {
+    const s2fast_q8_scales& q = *w->q8_scales;
+    if (!q.output || (k.has_project_in && !q.project_in)) return S2FAST_ERR_NO_FAST_DECODER;
+    for (int l = 0; l < k.n_layer; ++l) {
+      const s2fast_q8_layer_scales& Q = q.layers[l];
+      if (!Q.wqkv || !Q.wo || !Q.w1 || !Q.w3 || !Q.w2) return S2FAST_ERR_NO_FAST_DECODER;
+    }
   }
 
   // 16-byte weight loads need 16-byte aligned tensors
@@ -1782,6 +1872,11 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   if (!c) return S2FAST_ERR_NOMEM;
   c->cfg = k;
   c->w = *w;
+  c->w.q8_scales = nullptr;
+  if (w->q8_scales) {
+    c->q8 = *w->q8_scales;
+    if (!k.has_project_in) c->q8.project_in = nullptr;
+  }
   c->device = dev;
   c->ncu = prop.multiProcessorCount;
   if (c->ncu < k.n_head_kv || c->ncu > 1024) { free_ctx(c); return S2FAST_ERR_DEVICE; }
@@ -1806,8 +1901,7 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   if (lds < one_per_cu) lds = one_per_cu;
   if (lds > (size_t)prop.sharedMemPerBlock) { free_ctx(c); return S2FAST_ERR_ARG; }
   c->lds_bytes = lds;
-  const void* fn = k.weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&frame_kernel<uint16_t>)
-                                                 : reinterpret_cast<const void*>(&frame_kernel<float>);
+  const void* fn = frame_fn(k.weight_dtype);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
     free_ctx(c); return S2FAST_ERR_HIP;
   }
@@ -1842,7 +1936,7 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
        hipMemset(c->err, 0, W_WORDS * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_HIP; }
   if (build_qkv0(c) != S2FAST_OK) { free_ctx(c); return S2FAST_ERR_HIP; }
-  if (k.max_batch >= 2) {
+  if (k.max_batch >= 2 && k.weight_dtype != S2FAST_Q8) {   // int8 models decode with the batch-1 kernel
     c->bq = batched_group(k, P);
     if (c->bq > 0) {
       c->b_lds = b_lds_bytes(k.n_layer, k.head_dim, k.context, k.dim);
@@ -2044,8 +2138,7 @@ int s2fast_decode_frame_static(s2fast_ctx* ctx, int32_t B, const float* hidden, 
   fa.logits = reinterpret_cast<float*>(S.ptr + L.logits);
   fa.flags = reinterpret_cast<u32*>(S.ptr + L.flags);
   fa.tlog = nullptr;
-  const void* fn = k.weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&frame_kernel<uint16_t>)
-                                                 : reinterpret_cast<const void*>(&frame_kernel<float>);
+  const void* fn = frame_fn(k.weight_dtype);
   const u32 n = (u32)syncs_for(k, fa.nsteps, false);
   int done = 0, rc = S2FAST_OK;
   for (int b = 0; b < B; ++b) {
@@ -2108,10 +2201,14 @@ int s2fast_test_rope_table(int32_t head_dim, int32_t context, float rope_base, f
 }
 
 int s2fast_test_gemv(int32_t weight_dtype, int32_t N, int32_t K, int32_t M, const void* W, const void* W3,
-                     const void* norm_w, float eps, const float* x, float* y, void* stream) {
-  const int epl = weight_dtype == S2FAST_BF16 ? 8 : 4;
-  if (weight_dtype != S2FAST_BF16 && weight_dtype != S2FAST_F32) return S2FAST_ERR_ARG;
+                     const float* scale, const float* scale3, const void* norm_w, float eps, const float* x, float* y,
+                     void* stream) {
+  const int epl = weight_dtype == S2FAST_BF16 ? 8 : (weight_dtype == S2FAST_Q8 ? 16 : 4);
+  if (weight_dtype != S2FAST_BF16 && weight_dtype != S2FAST_F32 && weight_dtype != S2FAST_Q8) return S2FAST_ERR_ARG;
   if (N < 1 || K < epl || K > 16384 || (K % epl) || M < 1 || M > MMAX || !W || !x || !y) return S2FAST_ERR_ARG;
+  if ((weight_dtype == S2FAST_Q8) != (scale != nullptr) || (W3 && (scale != nullptr) != (scale3 != nullptr)) ||
+      (!W3 && scale3))
+    return S2FAST_ERR_ARG;
   auto mis = [](const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); };
   if (mis(W) || mis(W3) || mis(norm_w) || mis(x)) return S2FAST_ERR_ARG;
   int dev = 0, P = 0;
@@ -2120,10 +2217,12 @@ int s2fast_test_gemv(int32_t weight_dtype, int32_t N, int32_t K, int32_t M, cons
   if (hipDeviceGetAttribute(&P, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return S2FAST_ERR_HIP;
   GemvTestArgs a;
   a.N = N; a.K = K; a.M = M; a.kmax = (K + 3) & ~3; a.rmax = (W3 ? 2 : 1) * ((N + P - 1) / P) + 1;
-  a.W = W; a.W3 = W3; a.normw = norm_w; a.eps = eps; a.x = x; a.y = y;
-  const size_t lds = ((((size_t)MMAX * a.kmax + 3) & ~(size_t)3) + (size_t)a.rmax * NWAVE * MMAX + 64) * sizeof(float);
+  a.W = W; a.W3 = W3; a.sc = scale; a.sc3 = scale3; a.normw = norm_w; a.eps = eps; a.x = x; a.y = y;
+  const size_t lds = ((((size_t)MMAX * a.kmax + 3) & ~(size_t)3) + (size_t)a.rmax * NWAVE * MMAX + 64 +
+                      (size_t)a.rmax) * sizeof(float);
   const void* fn = weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&gemv_test_kernel<uint16_t>)
-                                                : reinterpret_cast<const void*>(&gemv_test_kernel<float>);
+                   : weight_dtype == S2FAST_Q8 ? reinterpret_cast<const void*>(&gemv_test_kernel<q8_t>)
+                                               : reinterpret_cast<const void*>(&gemv_test_kernel<float>);
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
     return S2FAST_ERR_ARG;
   void* args[] = {&a};

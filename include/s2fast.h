@@ -52,7 +52,15 @@ enum {
                                       static buffer of s2fast_decode_frame_static */
 };
 
-enum { S2FAST_BF16 = 0, S2FAST_F32 = 1 };
+/* Weight types.  S2FAST_Q8: weight-only int8 — every weight matrix (wqkv,
+ * wo, w1, w3, w2, fast_output, fast_project_in) is int8 [out, in] with one
+ * float32 scale per output row, W[r, k] = scale[r] * q[r, k] (the pages name
+ * GGUF quantised tensors, "Overall architecture & Dual-AR data flow",
+ * section 5 and "Model loading and GGUF", section 4, but no Fast-AR
+ * format; per-row symmetric int8 is this library's choice); norm weights
+ * and fast_embeddings are bf16.  Q8 contexts decode every request with the
+ * batch-1 kernel (one launch per request). */
+enum { S2FAST_BF16 = 0, S2FAST_F32 = 1, S2FAST_Q8 = 2 };
 
 /* Model shape ("Overall architecture & Dual-AR data flow", section 2;
  * "Model loading and GGUF", section 2.2).  S2 Pro: in_dim 2560, dim 2560,
@@ -73,8 +81,9 @@ typedef struct s2fast_config {
   float norm_eps;          /* 1e-6, also used by the per-head q/k norms */
   int32_t has_project_in;  /* fast_project_in [dim, in_dim] present */
   int32_t has_qk_norm;     /* per-head q_norm / k_norm present */
-  int32_t weight_dtype;    /* S2FAST_BF16 or S2FAST_F32; all matrices and norm
-                              weights share it */
+  int32_t weight_dtype;    /* S2FAST_BF16 or S2FAST_F32 (all matrices and norm
+                              weights share it), or S2FAST_Q8 (int8 matrices,
+                              bf16 vectors; widths multiples of 16) */
   int32_t max_batch;       /* largest B passed to the decode calls */
 } s2fast_config;
 
@@ -102,12 +111,31 @@ typedef struct s2fast_layer_weights {
   const void* w2;              /* [dim, ffn_dim] down */
 } s2fast_layer_weights;
 
+/* Row scales of an S2FAST_Q8 model's matrices: float32 device vectors, one
+ * value per output row of the matrix named. */
+typedef struct s2fast_q8_layer_scales {
+  const float* wqkv;           /* [(n_head + 2 n_head_kv) head_dim] */
+  const float* wo;             /* [dim] */
+  const float* w1;             /* [ffn_dim] */
+  const float* w3;             /* [ffn_dim] */
+  const float* w2;             /* [dim] */
+} s2fast_q8_layer_scales;
+
+typedef struct s2fast_q8_scales {
+  const float* project_in;     /* [dim], NULL iff !has_project_in */
+  const float* output;         /* [codebook_size] */
+  s2fast_q8_layer_scales layers[S2FAST_MAX_LAYERS];
+} s2fast_q8_scales;
+
 typedef struct s2fast_weights {
   const void* project_in;      /* fast_project_in [dim, in_dim], NULL iff !has_project_in */
   const void* embeddings;      /* fast_embeddings [codebook_size, dim] */
   const void* norm;            /* fast_norm [dim] */
   const void* output;          /* fast_output [codebook_size, dim] (untied) */
   s2fast_layer_weights layers[S2FAST_MAX_LAYERS];
+  const s2fast_q8_scales* q8_scales;   /* HOST pointer to the row scales of an
+                                          S2FAST_Q8 model (copied at creation),
+                                          NULL for the other weight types */
 } s2fast_weights;
 
 typedef struct s2fast_ctx s2fast_ctx;
@@ -130,7 +158,9 @@ typedef struct s2fast_ctx s2fast_ctx;
  * multiples of 8 (bf16) or 4 (f32) elements; dim, in_dim, ffn_dim <= 16384;
  * head_dim a multiple of 8 and <= 128; context <= 16; 2 <= num_codebooks <= context;
  * codebook_size <= 8192; n_head_kv <= 64.
- * Missing required weight pointers give S2FAST_ERR_NO_FAST_DECODER. */
+ * Missing required weight pointers (or, for S2FAST_Q8, row scales) give
+ * S2FAST_ERR_NO_FAST_DECODER; q8_scales with another weight type gives
+ * S2FAST_ERR_ARG. */
 int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx** out);
 
 /* Wait for the device, then free everything the context owns (not the
@@ -403,13 +433,16 @@ int s2fast_test_sample(int32_t B, int32_t V, const float* logits, const float* t
  *   when norm_w is not NULL (RMSNorm, "Model loading and GGUF", section 2.2),
  *   else n_m = x[m, :]; with W3 not NULL the output is the SwiGLU pair
  *   silu(W . n_m) * (W3 . n_m) ("Fast-AR codebook decoding ...", section 3).
- *   W, W3 [N, K] and norm_w [K] of weight_dtype; x [M, K] f32; y [M, N] f32
- *   OUT; device pointers, W / W3 / x 16-byte aligned; K a multiple of 8
- *   (bf16) or 4 (f32), K <= 16384.  Enqueued on `stream`.
+ *   W, W3 [N, K] of weight_dtype and norm_w [K] (bf16 for S2FAST_Q8, else
+ *   weight_dtype); with S2FAST_Q8, scale / scale3 [N] f32 are the row scales
+ *   of W / W3 (NULL otherwise); x [M, K] f32; y [M, N] f32 OUT; device
+ *   pointers, W / W3 / x 16-byte aligned; K a multiple of 8 (bf16), 16
+ *   (int8) or 4 (f32), K <= 16384.  Enqueued on `stream`.
  * Errors: S2FAST_ERR_ARG for bad sizes or pointers, S2FAST_ERR_DEVICE off
  * gfx950. */
 int s2fast_test_gemv(int32_t weight_dtype, int32_t N, int32_t K, int32_t M, const void* W, const void* W3,
-                     const void* norm_w, float eps, const float* x, float* y, void* stream);
+                     const float* scale, const float* scale3, const void* norm_w, float eps, const float* x, float* y,
+                     void* stream);
 
 /* The frame kernel's q/k RMSNorm + pair RoPE + causal attention (mask
  * offset 0) on its own ("Fast-AR codebook decoding ...", section 3; Mizuoto

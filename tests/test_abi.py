@@ -123,12 +123,12 @@ def test_kernel_test_exports_reject_bad_arguments():
     lib = bd.library()
     fake = 0x7F0000000000
     # weight dtype, K not a multiple of the weight vector, M outside 1..2, NULL / misaligned pointers
-    assert lib.s2fast_test_gemv(5, 16, 64, 1, fake, None, None, 1e-6, fake, fake, None) == 1
-    assert lib.s2fast_test_gemv(0, 16, 60, 1, fake, None, None, 1e-6, fake, fake, None) == 1
-    assert lib.s2fast_test_gemv(0, 16, 64, 3, fake, None, None, 1e-6, fake, fake, None) == 1
-    assert lib.s2fast_test_gemv(0, 16, 64, 1, None, None, None, 1e-6, fake, fake, None) == 1
-    assert lib.s2fast_test_gemv(0, 16, 64, 1, fake + 4, None, None, 1e-6, fake, fake, None) == 1
-    assert lib.s2fast_test_gemv(0, 0, 64, 1, fake, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(5, 16, 64, 1, fake, None, None, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 16, 60, 1, fake, None, None, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 16, 64, 3, fake, None, None, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 16, 64, 1, None, None, None, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 16, 64, 1, fake + 4, None, None, None, None, 1e-6, fake, fake, None) == 1
+    assert lib.s2fast_test_gemv(0, 0, 64, 1, fake, None, None, None, None, 1e-6, fake, fake, None) == 1
     # heads that do not divide, head_dim not a multiple of 8, T past the context, one norm weight only
     assert lib.s2fast_test_norm_rope_attn(6, 4, 64, 4, 11, 1e6, 1e-6, fake, None, None, fake, None) == 1
     assert lib.s2fast_test_norm_rope_attn(4, 2, 60, 4, 11, 1e6, 1e-6, fake, None, None, fake, None) == 1
@@ -214,3 +214,56 @@ def test_slow_null_arguments():
     assert lib.s2fast_test_slow_timeline(None, 1, None, 0) == 1
     assert lib.s2fast_slow_status(None, None) == 1 and lib.s2fast_test_slow_watchdog(None, 0) == 1
     lib.s2fast_slow_destroy(None)
+
+
+# ---------------------------------------------------------------- weight-only int8
+
+def _fake_q8_scales(shape):
+    q = bd.Q8Scales()
+    base = [0x7E0000000000]
+
+    def nxt():
+        base[0] += 1 << 16
+        return base[0]
+    q.output = nxt()
+    if shape.has_project_in:
+        q.project_in = nxt()
+    for i in range(shape.n_layer):
+        for f, _ in bd.Q8_FIELDS:
+            setattr(q.layers[i], f, nxt())
+    return q
+
+
+def test_create_q8_needs_every_row_scale():
+    cfg = bd.make_config(si.S2PRO_Q8, 1)
+    w = _fake_weights(si.S2PRO_Q8)
+    assert _create(cfg, w)[0] == 2                       # no scales at all
+    q = _fake_q8_scales(si.S2PRO_Q8)
+    q.layers[2].w3 = None
+    w.q8_scales = ctypes.pointer(q)
+    assert _create(cfg, w)[0] == 2
+    q = _fake_q8_scales(si.S2PRO_Q8)
+    q.output = None
+    w.q8_scales = ctypes.pointer(q)
+    assert _create(cfg, w)[0] == 2
+
+
+def test_create_rejects_scales_without_q8_and_q8_widths():
+    cfg = bd.make_config(si.S2PRO, 1)
+    w = _fake_weights(si.S2PRO)
+    w.q8_scales = ctypes.pointer(_fake_q8_scales(si.S2PRO))
+    assert _create(cfg, w)[0] == 1
+    cfg = bd.make_config(si.S2PRO_Q8, 1)
+    cfg.dim = cfg.in_dim = 2568                          # a multiple of 8, not of 16
+    w = _fake_weights(si.S2PRO_Q8)
+    w.q8_scales = ctypes.pointer(_fake_q8_scales(si.S2PRO_Q8))
+    assert _create(cfg, w)[0] == 1
+
+
+def test_test_gemv_q8_arguments():
+    lib = bd.library()
+    fake = 0x7F0000000000
+    assert lib.s2fast_test_gemv(2, 16, 64, 1, fake, None, None, None, None, 1e-6, fake, fake, None) == 1  # no scale
+    assert lib.s2fast_test_gemv(2, 16, 56, 1, fake, None, fake, None, None, 1e-6, fake, fake, None) == 1  # K % 16
+    assert lib.s2fast_test_gemv(0, 16, 64, 1, fake, None, fake, None, None, 1e-6, fake, fake, None) == 1  # scale on bf16
+    assert lib.s2fast_test_gemv(2, 16, 64, 1, fake, fake, fake, None, None, 1e-6, fake, fake, None) == 1  # W3 unscaled

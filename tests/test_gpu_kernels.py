@@ -241,3 +241,63 @@ def test_slow_device_failure_is_reported_and_recovered():
     md = sa.draw_main(s, st.logits, [], 0.8, 0.8, 30, inp["u_slow"][0][0], inp["u_slow"][0][1])
     assert int(m_out.item()) in md.alts
     slow.close()
+
+
+# ------------------------------------------------------------ weight-only int8
+
+Q8_GEMVS = [("wqkv", 6144, 2560, False, True), ("wo", 2560, 4096, False, False), ("w1w3", 9728, 2560, True, True),
+            ("w2", 2560, 9728, False, False), ("head", 4096, 2560, False, True), ("small", 400, 208, True, True),
+            ("odd_rows", 7, 64, False, False)]
+
+
+@pytest.mark.parametrize("name,N,K,swiglu,norm", Q8_GEMVS, ids=[c[0] for c in Q8_GEMVS])
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_q8_integer_exact(name, N, K, swiglu, norm, M):
+    """int8 weights, power-of-two row scales and small integer activations:
+    every product, partial sum and scaled result is exact in float32."""
+    g = torch.Generator().manual_seed(N + K + 31 * M)
+    W = torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8).cuda()
+    W3 = torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8).cuda() if swiglu else None
+    sc = (2.0 ** torch.randint(-6, 2, (N,), generator=g).float()).cuda()
+    sc3 = (2.0 ** torch.randint(-6, 2, (N,), generator=g).float()).cuda() if swiglu else None
+    x = torch.randint(-3, 4, (M, K), generator=g).float().cuda()
+    y = bd.gemv(W, x, W3=W3, scale=sc, scale3=sc3).cpu().double()
+    a1 = (x.double() @ W.double().T).cpu() * sc.double().cpu()
+    if swiglu:
+        a3 = (x.double() @ W3.double().T).cpu() * sc3.double().cpu()
+        want = (a1 / (1 + torch.exp(-a1))) * a3
+        assert torch.all((y - want).abs() <= 8 * U * want.abs() + 1e-30), name
+    else:
+        assert torch.equal(y, a1), (name, (y - a1).abs().max().item())
+    _announce(f"gemv q8 {name} M={M}: exact")
+
+
+@pytest.mark.parametrize("name,N,K,swiglu,norm", Q8_GEMVS, ids=[c[0] for c in Q8_GEMVS])
+def test_gemv_q8_random(name, N, K, swiglu, norm):
+    rng = np.random.default_rng(N * 5 + K)
+    q, s = si.quantize_rows((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    q3, s3 = si.quantize_rows((rng.standard_normal((N, K)) * 0.02).astype(np.float32)) if swiglu else (None, None)
+    wn = si.bf16_bits_from_f32((1 + 0.05 * rng.standard_normal(K)).astype(np.float32)) if norm else None
+    x = rng.standard_normal((2, K)).astype(np.float32)
+    d = lambda a: torch.from_numpy(a).cuda()
+    nw = torch.from_numpy(wn.view(np.int16)).view(torch.bfloat16).cuda() if norm else None
+    y = bd.gemv(d(q), d(x), W3=d(q3) if swiglu else None, norm_w=nw, eps=1e-6, scale=d(s),
+                scale3=d(s3) if swiglu else None).cpu().numpy().astype(np.float64)
+    Wd = q.astype(np.float64) * s.astype(np.float64)[:, None]
+    n = x.astype(np.float64)
+    if norm:
+        n = n * si.f32_from_bf16_bits(wn).astype(np.float64) / np.sqrt(np.mean(n ** 2, axis=1, keepdims=True) + 1e-6)
+    a1 = n @ Wd.T
+    b1 = 64 * U * (np.abs(n) @ np.abs(Wd).T) + 8 * U * np.abs(a1)
+    if swiglu:
+        W3d = q3.astype(np.float64) * s3.astype(np.float64)[:, None]
+        a3 = n @ W3d.T
+        b3 = 64 * U * (np.abs(n) @ np.abs(W3d).T) + 8 * U * np.abs(a3)
+        sig = 1 / (1 + np.exp(-a1))
+        want = a1 * sig * a3
+        bound = np.abs(sig * (1 + a1 * (1 - sig)) * a3) * b1 + np.abs(a1 * sig) * b3 + 8 * U * np.abs(want)
+    else:
+        want, bound = a1, b1
+    r = np.abs(y - want) / (bound + 1e-30)
+    assert np.all(r <= 1.0), (name, float(r.max()))
+    _announce(f"gemv q8 {name} random: worst |d|/bound {float(r.max()):.2e}")

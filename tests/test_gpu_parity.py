@@ -258,6 +258,44 @@ def test_tiny_f32_batched_groups():
     pair.ctx.close()
 
 
+# ------------------------------------------------------------------ weight-only int8
+# int8 matrices with per-row scales (bf16 norm weights and embeddings); the
+# oracle dequantizes them.  Every request runs the batch-1 kernel.
+
+@pytest.mark.parametrize("wname,frames,B", [("tiny_q8", 6, 1), ("ragged_q8", 3, 3)])
+def test_q8_small_shapes(wname, frames, B):
+    w = si.WORKLOADS[wname]
+    pair = pr.make_pair(w.shape, w.seed(0), max_batch=B)
+    fr = _frames(w, frames, B)
+    rep = pr.FrameReport()
+    for f in range(frames):
+        codes = pr.gpu_decode(pair, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], fr["temperature"],
+                              fr["top_p"], fr["top_k"])
+        rep = rep.add(pr.check_frame(pair, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f],
+                                     fr["temperature"], fr["top_p"], fr["top_k"], codes))
+    _announce(f"{wname}: {rep}")
+    rep.assert_ok(1e-4)
+    pair.ctx.close()
+
+
+def test_q8_s2pro_protocol():
+    """16 frames of the int8 S2 Pro model at batch 1 (the batch-1
+    workload's settings), codes and teacher-forced logits; the oracle runs
+    them as one batch of windows."""
+    w = si.WORKLOADS["s2pro_q8"]
+    pair = pr.make_pair(w.shape, w.seed(0), max_batch=1)
+    F = 16
+    fr = _frames(w, F, 1)
+    codes = np.concatenate([pr.gpu_decode(pair, fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f],
+                                          fr["temperature"], fr["top_p"], fr["top_k"]) for f in range(F)])
+    rep = pr.check_frame(pair, fr["hidden"][:, 0], fr["sem_code"][:, 0], fr["uniforms"][:, 0],
+                         np.repeat(fr["temperature"], F), np.repeat(fr["top_p"], F), np.repeat(fr["top_k"], F),
+                         codes, one_by_one=True)
+    _announce(f"s2pro q8 B=1, {F} frames: {rep}")
+    rep.assert_ok(1e-4)
+    pair.ctx.close()
+
+
 # ------------------------------------------------------------------ behaviour
 
 def test_deterministic(tiny):
