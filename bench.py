@@ -486,7 +486,7 @@ def main():
                                "hbm_gbs": round(fb * nf / sec / 1e9, 1),
                                "frac": round(fb * nf / sec / 1e9 / PEAK_HBM_GBS, 4), "frames": nf,
                                "bytes_per_frame": fb, "kernel_ms_per_frame": round(per_call * 1e3, 3),
-                               "launches_per_frame": (Bs + 31) // 32, "workload": ws.name}
+                               "launches_per_frame": (Bs + 63) // 64, "workload": ws.name}
             if n_chk:
                 c0 = di[6][0].cpu().numpy()
                 l0 = cs.forward_logits(di[0][0], di[6][0]).cpu().numpy()

@@ -262,9 +262,9 @@ class FastAR:
         # Never touch the device while the interpreter shuts down: the HIP
         # runtime (or a profiler attached to it) may already be torn down.
         # Close contexts explicitly; at exit the process releases them.
-        if sys.is_finalizing():
-            return
         try:
+            if sys.is_finalizing():
+                return
             self.close()
         except Exception:
             pass
@@ -390,9 +390,9 @@ class SlowAR:
         # Never touch the device while the interpreter shuts down: the HIP
         # runtime (or a profiler attached to it) may already be torn down.
         # Close contexts explicitly; at exit the process releases them.
-        if sys.is_finalizing():
-            return
         try:
+            if sys.is_finalizing():
+                return
             self.close()
         except Exception:
             pass

@@ -25,9 +25,10 @@
 //
 // Included by s2fast.hip inside its anonymous namespace.
 
-constexpr int BQ_MAX = 32;               // requests per batched launch
+constexpr int BQ_MAX = 64;               // requests per batched launch
 constexpr int MP_MAX = 2 * BQ_MAX;       // rows per decode step at most
-constexpr int GM_MAX = 32;               // rows of one GEMM pass (two 16-row M-tiles)
+constexpr int GROUP_ROWS = 32;           // rows of one wave group (two 16-row M-tiles)
+constexpr int GM_MAX = 4 * GROUP_ROWS;   // rows of one GEMM pass (up to four wave groups)
 constexpr int KCNT_STRIDE = 64;          // ints between K-split counts (each on its own line)
 constexpr int XF_BYTES = 128 * 1024;     // LDS for the GEMM partial sums and the attention scratch
 constexpr int TMAX = 5;                  // 16-row tiles of W per workgroup and phase
@@ -98,7 +99,7 @@ struct BatchArgs {
 
 struct BLds {
   char* xf;      // XF_BYTES: GEMM partial sums; attention scratch
-  float* ssp;    // [NTHREADS] per-wave row sums of squares ([NWAVE][MP_MAX] used)
+  float* ssp;    // [NWAVE][MP_MAX] per-wave row sums of squares
   float* rms;    // [MP_MAX]
   float* qkn;    // [n_layer][2][hd]
   float* rope;   // [2][ctx][hd/2]
@@ -111,7 +112,7 @@ struct BLds {
 };
 
 __host__ __device__ inline size_t b_lds_bytes(int n_layer, int hd, int ctx, int dim) {
-  return (size_t)XF_BYTES + sizeof(float) * ((size_t)NTHREADS + MP_MAX + (size_t)n_layer * 2 * hd + (size_t)ctx * hd +
+  return (size_t)XF_BYTES + sizeof(float) * ((size_t)NWAVE * MP_MAX + MP_MAX + (size_t)n_layer * 2 * hd + (size_t)ctx * hd +
                                              TOPK_MAX) +
          sizeof(int) * ((size_t)TOPK_MAX + 2 * NWAVE * SAMP_TAU + MP_MAX + 4) + sizeof(float) * (size_t)dim;
 }
@@ -120,7 +121,7 @@ __device__ inline BLds b_carve(char* base, const BatchArgs& a) {
   BLds s;
   char* p = base;
   s.xf = p; p += XF_BYTES;
-  s.ssp = reinterpret_cast<float*>(p); p += sizeof(float) * NTHREADS;
+  s.ssp = reinterpret_cast<float*>(p); p += sizeof(float) * NWAVE * MP_MAX;
   s.rms = reinterpret_cast<float*>(p); p += sizeof(float) * MP_MAX;
   s.qkn = reinterpret_cast<float*>(p); p += sizeof(float) * (size_t)a.n_layer * 2 * a.hd;
   s.rope = reinterpret_cast<float*>(p); p += sizeof(float) * (size_t)a.ctx_len * a.hd;
@@ -405,16 +406,17 @@ __device__ __forceinline__ void b_use(const BLds& s, const GemmDesc& gd, int st,
   }
 }
 
-// One wave's share of a GEMM phase with TT row tiles and MTT M-tiles: its
-// partial sums go to red[((wave * TT + t) * MTT + mt) * 256 + lane * 4 ..],
+// One wave's share of a GEMM phase with TT row tiles and MTT M-tiles: the
+// k-steps kw, kw + wpg, ... of its wave group's rows (gd.m0.., gd.M <= 32);
+// its partial sums go to red[((wave * TT + t) * 2 + mt) * 256 + lane * 4 ..],
 // its per-lane sums of squares of X to ssm[mt] (row 16 mt + lane % 16).
 template <typename WT, int TT, int MTT>
-__device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int wave, int lane,
-                                       float* red, float (&ssm)[2]) {
+__device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int wave, int kw,
+                                       int wpg, int lane, float* red, float (&ssm)[2]) {
   constexpr int KSZ = MF<WT>::KSZ, PD = bpd<TT, MTT>();
   const int KST = (gd.K + KSZ - 1) / KSZ;
-  const int ns = wave < KST ? (KST - wave + NWAVE - 1) / NWAVE : 0;   // this wave's k-steps
-  const auto kstep = [&](int j) __attribute__((always_inline)) { return j < ns ? wave + NWAVE * j : KST; };
+  const int ns = kw < KST ? (KST - kw + wpg - 1) / wpg : 0;   // this wave's k-steps
+  const auto kstep = [&](int j) __attribute__((always_inline)) { return j < ns ? kw + wpg * j : KST; };
   f32x4 D[TT][MTT];
   float ss[MTT];
 #pragma unroll
@@ -438,21 +440,22 @@ __device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const 
     ssm[mt] = ss[mt];
 #pragma unroll
     for (int t = 0; t < TT; ++t)
-      *reinterpret_cast<float4*>(red + (((size_t)wave * TT + t) * MTT + mt) * 256 + lane * 4) =
+      *reinterpret_cast<float4*>(red + (((size_t)wave * TT + t) * 2 + mt) * 256 + lane * 4) =
           make_float4(D[t][mt][0], D[t][mt][1], D[t][mt][2], D[t][mt][3]);
   }
 }
 
-// Per-wave partial products of one GEMM phase, summed in wave order.
+// Per-wave partial products of one GEMM phase: row m of the pass belongs to
+// wave group m / 32, whose wpg waves' partials are summed in wave order.
 struct RedView {
   const float* red;
-  int T, MT;
+  int T, wpg;
   __device__ __forceinline__ float sum(int v, int m) const {
-    // element (v = 16 t + 4 qd + r, m = 16 mt + j) sits in lane qd * 16 + j, slot r
-    const int t = v >> 4, i = v & 15, mt = m >> 4;
+    // element (v = 16 t + 4 qd + r, row 32 g + 16 mt + j) sits in lane qd * 16 + j, slot r
+    const int t = v >> 4, i = v & 15, g = m >> 5, mt = (m >> 4) & 1;
     const int ln = (i >> 2) * 16 + (m & 15), r = i & 3;
     float acc = 0.0f;
-    for (int w = 0; w < NWAVE; ++w) acc += red[(((size_t)w * T + t) * MT + mt) * 256 + ln * 4 + r];
+    for (int w = g * wpg; w < (g + 1) * wpg; ++w) acc += red[(((size_t)w * T + t) * 2 + mt) * 256 + ln * 4 + r];
     return acc;
   }
 };
@@ -460,12 +463,23 @@ struct RedView {
 // Run one GEMM phase on this workgroup.  On return (after a barrier) the
 // view holds the waves' partial sums and, with a norm weight, rms[m] holds
 // sqrt(mean(x_m^2) + eps) over the K columns.
+// The pass's rows form up to four wave groups of 32 (1, 2 or 4 groups of
+// 8, 4 or 2 waves): each group streams the workgroup's whole weight range
+// for its rows, the waves of a group splitting the k-steps.  The groups
+// read the same weight fragments at about the same time (one HBM fill
+// serves them).
 template <typename WT>
 __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, const GemmDesc& gd) {
   const int tid = tidx();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave-uniform work split
-  const int MT = gd.M <= 16 ? 1 : 2;
-  const int T = (gd.R + 15) >> 4;
+  const int ng = gd.M <= GROUP_ROWS ? 1 : (gd.M <= 2 * GROUP_ROWS ? 2 : 4);
+  const int wpg = NWAVE / ng;
+  const int grp = wave / wpg, kw = wave - grp * wpg;
+  GemmDesc gg = gd;
+  gg.m0 = gd.m0 + GROUP_ROWS * grp;
+  gg.M = max(0, min(GROUP_ROWS, gd.M - GROUP_ROWS * grp));
+  const int MT = gg.M <= 16 ? 1 : 2;
+  const int T = gg.M > 0 ? (gd.R + 15) >> 4 : 0;   // a group without rows does nothing
   if (gd.normw) {
     for (int k = tid; k < gd.K; k += NTHREADS)
       s.nw[k] = WTraits<WT>::one(reinterpret_cast<const WT*>(gd.normw), gd.k0 + k);
@@ -474,10 +488,10 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
   float* red = reinterpret_cast<float*>(s.xf);
   float ssm[2] = {0.0f, 0.0f};
   mark(a, s.flag[1], 2);
-#define B_CORE(TT_)                                                         \
-  case TT_:                                                                 \
-    if (MT == 1) b_core<WT, TT_, 1>(a, s, gd, wave, lane, red, ssm);        \
-    else b_core<WT, TT_, 2>(a, s, gd, wave, lane, red, ssm);                \
+#define B_CORE(TT_)                                                                 \
+  case TT_:                                                                         \
+    if (MT == 1) b_core<WT, TT_, 1>(a, s, gg, wave, kw, wpg, lane, red, ssm);       \
+    else b_core<WT, TT_, 2>(a, s, gg, wave, kw, wpg, lane, red, ssm);               \
     break;
   switch (T) {
     B_CORE(1)
@@ -495,22 +509,23 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
     // then the waves
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      if (mt >= MT) break;
+      if (mt >= MT || gg.M == 0) break;
       float v = ssm[mt];
       v += xor_lane_f<16>(v, lane);
       v += xor_lane_f<32>(v, lane);
-      if (lane < 16) s.ssp[wave * MP_MAX + 16 * mt + lane] = v;
+      if (lane < 16) s.ssp[wave * MP_MAX + GROUP_ROWS * grp + 16 * mt + lane] = v;
     }
   }
   __syncthreads();
   if (gd.normw && tid < gd.M) {
     float t2 = 0.0f;
-    for (int w = 0; w < NWAVE; ++w) t2 += s.ssp[w * MP_MAX + tid];
+    const int g0 = (tid / GROUP_ROWS) * wpg;
+    for (int w = g0; w < g0 + wpg; ++w) t2 += s.ssp[w * MP_MAX + tid];
     // a K slice keeps its raw sum of squares (the consumer adds the slices')
     s.rms[tid] = a.ks[gd.kind] > 1 ? t2 : sqrtf(t2 / (float)gd.K + a.eps);
   }
   __syncthreads();
-  return RedView{red, T, MT};
+  return RedView{red, (gd.R + 15) >> 4, wpg};
 }
 
 // ------------------------------------------------------------ phases
@@ -580,7 +595,9 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
     const int M = gd.M;
     const int nv = kind == BK_UP ? nr : gd.R;
     for (int o = tidx(); o < nv * M; o += NTHREADS) {
-      const int mp = o % M, v = o / M;   // row of the pass, output column
+      // output column fastest: a wave's stores cover consecutive columns of
+      // one row (a few cache lines) rather than one column of many rows
+      const int v = o % nv, mp = o / nv;   // output column, row of the pass
       const int m = m0 + mp;
       const float d = rv.sum(v, mp);
       switch (kind) {
@@ -649,7 +666,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
 #pragma unroll
         for (int j = 0; j < FB; ++j) {
           const int o = min(base + j * NTHREADS + tidx(), n - 1);
-          const int m = o % M, k = r0 + o / M;
+          const int k = r0 + o % nr, m = o / nr;   // columns fastest (coalesced)
           const size_t e = (size_t)m * a.dim + k;
 #pragma unroll
           for (int q = 0; q < SMAX; ++q) pv[j][q] = q < S ? ld_coh(bkpart(a, kind, step, l, q) + e) : 0.0f;
@@ -660,7 +677,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
         for (int j = 0; j < FB; ++j) {
           const int o = base + j * NTHREADS + tidx();
           if (o < n) {
-            const int m = o % M, k = r0 + o / M;
+            const int k = r0 + o % nr, m = o / nr;   // columns fastest (coalesced)
             float sum = pv[j][0];
 #pragma unroll
             for (int q = 1; q < SMAX; ++q)
@@ -675,15 +692,13 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   mark(a, s.flag[1], 5);
 }
 
-// One workgroup per (request b, KV group g): the request's new rows' q (the
-// group's heads), k and v from the wqkv outputs, its cached keys/values of
-// earlier positions, q/k RMSNorm + pair RoPE, then causal attention with
-// offset 0; the new keys/values are kept for the frame's later steps.
+// One (request b, KV group g) pair of the attention phase: the request's
+// new rows' q (the group's heads), k and v from the wqkv outputs, its cached
+// keys/values of earlier positions, q/k RMSNorm + pair RoPE, then causal
+// attention with offset 0; the new keys/values are kept for the frame's
+// later steps.
 template <typename WT>
-__device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, int step, int l) {
-  const int j = blockIdx.x;
-  if (j >= a.Bq * a.n_kv) return;
-  const int b = j / a.n_kv, g = j % a.n_kv;
+__device__ __forceinline__ void b_attn_pair(const BatchArgs& a, const BLds& s, int step, int l, int b, int g) {
   const int hd = a.hd, gh = a.gheads, H = a.n_head, G = a.n_kv;
   const int n_new = step == 1 ? 2 : 1;
   const int first_new = step == 1 ? 0 : step;
@@ -802,6 +817,15 @@ __device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, 
     float* o = batt(a, step, l) + (size_t)m * a.attn_dim + (size_t)g * a.gw + (size_t)hh * hd;
     if (lane < hd) st_coh(o + lane, o0);
     if (lane + 64 < hd) st_coh(o + lane + 64, o1);
+  }
+}
+
+// The attention phase: workgroup j takes the pairs j, j + gridDim.x, ...
+template <typename WT>
+__device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, int step, int l) {
+  for (int j = blockIdx.x; j < a.Bq * a.n_kv; j += gridDim.x) {
+    if (j != (int)blockIdx.x) __syncthreads();   // the previous pair's LDS scratch is read out
+    b_attn_pair<WT>(a, s, step, l, j / a.n_kv, j % a.n_kv);
   }
 }
 

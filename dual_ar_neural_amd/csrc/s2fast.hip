@@ -1659,8 +1659,7 @@ int batched_group(const s2fast_config& k, int P) {
   tmax = std::max(tmax, (2 * ((k.ffn_dim + P - 1) / P) + 15) / 16);
   if (tmax > TMAX || 2 * tmax > RED_TILES) return 0;
   if ((size_t)(2 * gh * k.head_dim + 2 * k.context * k.head_dim) * sizeof(float) > (size_t)XF_BYTES) return 0;
-  const int bq = std::min(BQ_MAX, P / k.n_head_kv);
-  return bq >= 2 ? bq : 0;
+  return BQ_MAX;   // the attention phase loops over (request, KV group) pairs
 }
 
 // The sticky status of a context's watchdog words, read (and cleared) after

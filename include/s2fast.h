@@ -150,7 +150,7 @@ typedef struct s2fast_ctx s2fast_ctx;
  * synchronised before returning).  With max_batch >= 2 the context also
  * keeps a repacked copy of every weight matrix for the batched kernel (the
  * size of the weights: 0.83 GB at the S2 Pro shape), in which each
- * workgroup's rows form one contiguous stream; batches run 32 requests to a
+ * workgroup's rows form one contiguous stream; batches run 64 requests to a
  * launch.
  * Uses the current HIP device.  On success *out owns the scratch; release
  * it with s2fast_destroy.  Shape limits (else S2FAST_ERR_ARG): dim, in_dim,
@@ -206,7 +206,7 @@ int s2fast_status(s2fast_ctx* ctx, void* stream);
  *   code = kept candidate maximising p_j / f32(-log(f64(u_j))).
  * Errors: S2FAST_ERR_BATCH for B outside [1, max_batch]; S2FAST_ERR_ARG for
  * NULL pointers or a hidden pointer that is not 16-byte aligned.  Batches
- * run as launches of up to 32 requests (the context's group size); if a
+ * run as launches of up to 64 requests (the context's group size); if a
  * launch cannot be enqueued, codes[:, 1:] of its requests and of every
  * later one are zero-filled on `stream` (the main loop's "failed
  * fast_decode fills the rest of the frame with 0" convention, section 5.2)

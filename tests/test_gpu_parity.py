@@ -167,9 +167,9 @@ def test_s2pro_greedy_b2(s2pro):
 
 
 # ------------------------------------------------------------------ batched decoding
-# Batches of 2..32 requests share one launch (skinny GEMMs on the matrix
-# cores, rows in passes of 32: step 1 of a group above 16 takes two);
-# larger batches run in groups of 32.
+# Batches of 2..64 requests share one launch (skinny GEMMs on the matrix
+# cores; a pass takes up to 128 rows in wave groups of 32, so step 1 of a
+# group of 64 is one pass); larger batches run in groups of 64.
 
 @pytest.mark.parametrize("frame", range(8))
 def test_s2pro_b16_protocol(s2pro, frame):
@@ -187,14 +187,14 @@ def test_s2pro_b16_protocol(s2pro, frame):
 
 
 def test_s2pro_batched_teacher_forced_all_rows(s2pro):
-    """Teacher-forced logits of a full group of 32 (every row of the skinny
-    GEMMs; step 1's 64 rows in two passes)."""
+    """Teacher-forced logits of a full group of 64 (every row of the skinny
+    GEMMs: four wave groups of 32; step 1's 128 rows in one pass)."""
     w = si.WORKLOADS["s2pro_b16"]
-    fr = _frames(w, 1, 32)
+    fr = _frames(w, 1, 64)
     rng = np.random.default_rng(5)
-    codes = rng.integers(0, w.shape.codebook_size, size=(32, w.shape.num_codebooks)).astype(np.int32)
+    codes = rng.integers(0, w.shape.codebook_size, size=(64, w.shape.num_codebooks)).astype(np.int32)
     worst, rel, _, _ = pr.check_logits(s2pro, fr["hidden"][0], codes)
-    _announce(f"s2pro B=32 teacher-forced: worst |d|/tol {worst:.2e}, |d|/max {rel:.2e}")
+    _announce(f"s2pro B=64 teacher-forced: worst |d|/tol {worst:.2e}, |d|/max {rel:.2e}")
     assert worst <= 1.0 and rel < 1e-3, (worst, rel)
 
 
