@@ -35,7 +35,7 @@ def ragged():
 @pytest.fixture(scope="module")
 def s2pro():
     _announce("s2pro model (bf16, 828 MB)")
-    return pr.make_pair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0), max_batch=32)
+    return pr.make_pair(si.S2PRO, si.WORKLOADS["s2pro_b1"].seed(0), max_batch=64)
 
 
 # ------------------------------------------------------------------ sampler
