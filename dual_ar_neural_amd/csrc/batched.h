@@ -296,9 +296,9 @@ __device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const
 }
 
 // ------------------------------------------------------------ GEMM core
-// Work split: wave w takes the k-steps s = w, w + NWAVE, ... (KSZ columns
-// each) for every row tile of the workgroup, so each X
-// fragment is read and converted by exactly one wave, straight into MFMA B
+// Work split: the waves of a wave group split the k-steps (KSZ columns
+// each) between them, for every row tile of the workgroup, so each X
+// fragment is read and converted by exactly one wave of the group, straight into MFMA B
 // operands: no staging in LDS and no barrier inside the phase.  Per k-step a wave loads the
 // weight fragment of each row tile (A operand: lane -> row 16 t + lane % 16,
 // columns s KSZ + GE (lane / 16) ..) and the X fragment of each M-tile (B
@@ -307,6 +307,11 @@ __device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const
 // to about 2^-16 relative) and accumulates D[t][mt] in float32.  The loads of
 // a k-step are issued PD k-steps before it is used (more when a k-step has
 // few row tiles; deeper pipelines measured slower).
+//
+// The two waves that share a SIMD do not progress alike: the first one
+// (waves 0..3 of the workgroup) is issued first, and measured 10-25 % faster
+// than the second.  A first wave therefore takes a larger share of the
+// k-steps (BShare), so the waves of a workgroup finish together.
 template <int TT, int MTT> constexpr int bpd() { return TT == 1 ? 4 : (TT == 2 ? 3 : 2); }
 
 template <typename WT, int TT, int MTT>
@@ -406,17 +411,47 @@ __device__ __forceinline__ void b_use(const BLds& s, const GemmDesc& gd, int st,
   }
 }
 
-// One wave's share of a GEMM phase with TT row tiles and MTT M-tiles: the
-// k-steps kw, kw + wpg, ... of its wave group's rows (gd.m0.., gd.M <= 32);
+// One wave's share of a GEMM phase with TT row tiles and MTT M-tiles: its
+// range of the k-steps of its wave group's rows (gd.m0.., gd.M <= 32);
 // its partial sums go to red[((wave * TT + t) * 2 + mt) * 256 + lane * 4 ..],
 // its per-lane sums of squares of X to ssm[mt] (row 16 mt + lane % 16).
+// K-steps of wave kw of a group of wpg waves, h = wpg / 2 of them first
+// waves of their SIMDs (kw < h).  The k-steps go in rounds of wpg * base +
+// h: a round's first wpg * base k-steps are dealt to the waves in turn
+// (consecutive k-steps to consecutive waves, the pattern the memory system
+// streams best), its last h k-steps one each to the first waves.  So a
+// first wave takes base + 1 k-steps a round, a second wave base.
+struct BShare {
+  int kw, wpg, base, cw, R;
+  __device__ __forceinline__ BShare(int KST, int kw_, int wpg_, int base_, int& ns)
+      : kw(kw_), wpg(wpg_), base(base_) {
+    const int h = wpg >> 1;
+    cw = base + (kw < h ? 1 : 0);
+    R = wpg * base + h;
+    const int nr = KST / R, rem = KST - nr * R;
+    int last;   // this wave's k-steps of the partial last round
+    if (rem <= wpg * base) last = kw < rem ? (rem - 1 - kw) / wpg + 1 : 0;
+    else last = base + (kw < rem - wpg * base ? 1 : 0);
+    ns = nr * cw + last;
+  }
+  // global index of the wave's j-th k-step (j < ns)
+  __device__ __forceinline__ int at(int j) const {
+    const int r = j / cw, i = j - r * cw;
+    return r * R + (i < base ? i * wpg + kw : wpg * base + kw);
+  }
+};
+
 template <typename WT, int TT, int MTT>
 __device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int wave, int kw,
                                        int wpg, int lane, float* red, float (&ssm)[2]) {
   constexpr int KSZ = MF<WT>::KSZ, PD = bpd<TT, MTT>();
   const int KST = (gd.K + KSZ - 1) / KSZ;
-  const int ns = kw < KST ? (KST - kw + wpg - 1) / wpg : 0;   // this wave's k-steps
-  const auto kstep = [&](int j) __attribute__((always_inline)) { return j < ns ? kw + wpg * j : KST; };
+  // the SwiGLU phase's first waves measured 25 % faster than the second ones
+  // (a first wave takes 5 k-steps to a second's 4), the other phases' about
+  // 10 % (9 to 8)
+  int ns;
+  const BShare sh(KST, kw, wpg, gd.kind == BK_UP ? 4 : 8, ns);
+  const auto kstep = [&](int j) __attribute__((always_inline)) { return j < ns ? sh.at(j) : KST; };
   f32x4 D[TT][MTT];
   float ss[MTT];
 #pragma unroll
@@ -446,16 +481,20 @@ __device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const 
 }
 
 // Per-wave partial products of one GEMM phase: row m of the pass belongs to
-// wave group m / 32, whose wpg waves' partials are summed in wave order.
+// wave group g = m / 32 (waves g, g + ng, ...), whose wpg waves' partials
+// are summed in wave order.
 struct RedView {
   const float* red;
-  int T, wpg;
+  int T, wpg, ng;
   __device__ __forceinline__ float sum(int v, int m) const {
     // element (v = 16 t + 4 qd + r, row 32 g + 16 mt + j) sits in lane qd * 16 + j, slot r
     const int t = v >> 4, i = v & 15, g = m >> 5, mt = (m >> 4) & 1;
     const int ln = (i >> 2) * 16 + (m & 15), r = i & 3;
     float acc = 0.0f;
-    for (int w = g * wpg; w < (g + 1) * wpg; ++w) acc += red[(((size_t)w * T + t) * 2 + mt) * 256 + ln * 4 + r];
+    for (int j = 0; j < wpg; ++j) {
+      const int w = g + j * ng;
+      acc += red[(((size_t)w * T + t) * 2 + mt) * 256 + ln * 4 + r];
+    }
     return acc;
   }
 };
@@ -474,7 +513,8 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave-uniform work split
   const int ng = gd.M <= GROUP_ROWS ? 1 : (gd.M <= 2 * GROUP_ROWS ? 2 : 4);
   const int wpg = NWAVE / ng;
-  const int grp = wave / wpg, kw = wave - grp * wpg;
+  // group grp = wave % ng: every group holds first and second waves of the SIMDs alike
+  const int grp = wave % ng, kw = wave / ng;
   GemmDesc gg = gd;
   gg.m0 = gd.m0 + GROUP_ROWS * grp;
   gg.M = max(0, min(GROUP_ROWS, gd.M - GROUP_ROWS * grp));
@@ -519,13 +559,13 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
   __syncthreads();
   if (gd.normw && tid < gd.M) {
     float t2 = 0.0f;
-    const int g0 = (tid / GROUP_ROWS) * wpg;
-    for (int w = g0; w < g0 + wpg; ++w) t2 += s.ssp[w * MP_MAX + tid];
+    const int g = tid / GROUP_ROWS;
+    for (int j = 0; j < wpg; ++j) t2 += s.ssp[(g + j * ng) * MP_MAX + tid];
     // a K slice keeps its raw sum of squares (the consumer adds the slices')
     s.rms[tid] = a.ks[gd.kind] > 1 ? t2 : sqrtf(t2 / (float)gd.K + a.eps);
   }
   __syncthreads();
-  return RedView{red, (gd.R + 15) >> 4, wpg};
+  return RedView{red, (gd.R + 15) >> 4, wpg, ng};
 }
 
 // ------------------------------------------------------------ phases
@@ -840,16 +880,41 @@ __device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s
   const float* L = blogits(a, step) + (size_t)b * a.V;
   const int S = a.ks[BK_HEAD];
   if (S > 1) {
-    float ss = bkss(a, BK_HEAD, step, 0, 0)[b];
-    for (int q = 1; q < S; ++q) ss += bkss(a, BK_HEAD, step, 0, q)[b];
-    const float rd = sqrtf(ss / (float)a.dim + a.eps);
+    // Every load of a batch (the slices' sums of squares, then SB logits a
+    // thread from each slice) is issued before any is used: one memory
+    // round trip a batch.  Slices past S read slice 0 and are not added.
+    constexpr int SB = 8, SMAX = 4;
+    float ssq[SMAX];
+#pragma unroll
+    for (int q = 0; q < SMAX; ++q) ssq[q] = bkss(a, BK_HEAD, step, 0, q < S ? q : 0)[b];
     float* lg = reinterpret_cast<float*>(s.xf);
-    for (int i = tidx(); i < a.V; i += NTHREADS) {
-      float v = bkpart(a, BK_HEAD, step, 0, 0)[(size_t)b * a.V + i];
-      for (int q = 1; q < S; ++q) v += bkpart(a, BK_HEAD, step, 0, q)[(size_t)b * a.V + i];
-      v /= rd;
-      lg[i] = v;
-      if (a.logits_out && step >= a.lo_first) a.logits_out[((size_t)b * a.lo_rows + (step - a.lo_first)) * a.V + i] = v;
+    const int V = a.V;
+    for (int base = 0; base < V; base += SB * NTHREADS) {
+      float pv[SB][SMAX];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const int i = min(base + j * NTHREADS + tidx(), V - 1);
+#pragma unroll
+        for (int q = 0; q < SMAX; ++q) pv[j][q] = bkpart(a, BK_HEAD, step, 0, q < S ? q : 0)[(size_t)b * V + i];
+      }
+      float ss = ssq[0];
+#pragma unroll
+      for (int q = 1; q < SMAX; ++q)
+        if (q < S) ss += ssq[q];
+      const float rd = sqrtf(ss / (float)a.dim + a.eps);
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const int i = base + j * NTHREADS + tidx();
+        if (i < V) {
+          float v = pv[j][0];
+#pragma unroll
+          for (int q = 1; q < SMAX; ++q)
+            if (q < S) v += pv[j][q];
+          v /= rd;
+          lg[i] = v;
+          if (a.logits_out && step >= a.lo_first) a.logits_out[((size_t)b * a.lo_rows + (step - a.lo_first)) * V + i] = v;
+        }
+      }
     }
     __syncthreads();
     L = lg;
