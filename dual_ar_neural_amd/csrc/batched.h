@@ -108,13 +108,12 @@ struct BLds {
   int* sred;     // [2 * NWAVE * SAMP_TAU]
   int* rcode;    // [MP_MAX] embedding row of each row's layer-0 input (-1: hidden state)
   int* flag;     // [4]
-  float* nw;     // [dim] the current phase's RMSNorm weight
 };
 
-__host__ __device__ inline size_t b_lds_bytes(int n_layer, int hd, int ctx, int dim) {
+__host__ __device__ inline size_t b_lds_bytes(int n_layer, int hd, int ctx) {
   return (size_t)XF_BYTES + sizeof(float) * ((size_t)NWAVE * MP_MAX + MP_MAX + (size_t)n_layer * 2 * hd + (size_t)ctx * hd +
                                              TOPK_MAX) +
-         sizeof(int) * ((size_t)TOPK_MAX + 2 * NWAVE * SAMP_TAU + MP_MAX + 4) + sizeof(float) * (size_t)dim;
+         sizeof(int) * ((size_t)TOPK_MAX + 2 * NWAVE * SAMP_TAU + MP_MAX + 4);
 }
 
 __device__ inline BLds b_carve(char* base, const BatchArgs& a) {
@@ -129,8 +128,7 @@ __device__ inline BLds b_carve(char* base, const BatchArgs& a) {
   s.cidx = reinterpret_cast<int*>(p); p += sizeof(int) * TOPK_MAX;
   s.sred = reinterpret_cast<int*>(p); p += sizeof(int) * 2 * NWAVE * SAMP_TAU;
   s.rcode = reinterpret_cast<int*>(p); p += sizeof(int) * MP_MAX;
-  s.flag = reinterpret_cast<int*>(p); p += sizeof(int) * 4;
-  s.nw = reinterpret_cast<float*>(p);
+  s.flag = reinterpret_cast<int*>(p);
   return s;
 }
 
@@ -319,6 +317,7 @@ struct BUnit {
   u32x4 w[TT];
   float x[MTT][8];
   bool ok[MTT];
+  uint4 nw;       // the RMSNorm weight of the lane's GE columns (phases with a norm)
 };
 
 // A non-temporal 16-byte load of the packed weight stream.  The stream's
@@ -353,26 +352,19 @@ __device__ __forceinline__ void b_load(const BatchArgs& a, const BLds& s, const 
     u.ok[mt] = live && colok && m < gd.M;
     b_fetch<WT>(a, s, gd, gd.m0 + (m < gd.M ? m : 0), gd.k0 + c, u.x[mt]);
   }
+  // GE norm weights are 16 bytes in either weight format
+  if (gd.normw) u.nw = *reinterpret_cast<const uint4*>(reinterpret_cast<const WT*>(gd.normw) + gd.k0 + c);
 }
 
 template <typename WT, int TT, int MTT>
 __device__ __forceinline__ void b_use(const BLds& s, const GemmDesc& gd, int st, int lane, const BUnit<WT, TT, MTT>& u,
                                       f32x4 (&D)[TT][MTT], float (&ss)[MTT]) {
-  constexpr int KSZ = MF<WT>::KSZ, GE = MF<WT>::GE;
-  const int col = st * KSZ + GE * (lane >> 4);
+  constexpr int GE = MF<WT>::GE;
+  float w[8];
+  if (gd.normw) WTraits<WT>::unpack(u.nw, w);   // uniform: the phase's RMSNorm weight
 #pragma unroll
   for (int mt = 0; mt < MTT; ++mt) {
     float x[8];
-    float w[8];
-    if (gd.normw) {                              // uniform: the phase's RMSNorm weight, from LDS
-      const int kk = u.ok[mt] ? col : 0;
-      const float4 w0 = *reinterpret_cast<const float4*>(s.nw + kk);
-      w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-      if (GE == 8) {
-        const float4 w1 = *reinterpret_cast<const float4*>(s.nw + kk + 4);
-        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
-      }
-    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x[e] = 0.0f;
@@ -520,11 +512,6 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
   gg.M = max(0, min(GROUP_ROWS, gd.M - GROUP_ROWS * grp));
   const int MT = gg.M <= 16 ? 1 : 2;
   const int T = gg.M > 0 ? (gd.R + 15) >> 4 : 0;   // a group without rows does nothing
-  if (gd.normw) {
-    for (int k = tid; k < gd.K; k += NTHREADS)
-      s.nw[k] = WTraits<WT>::one(reinterpret_cast<const WT*>(gd.normw), gd.k0 + k);
-    __syncthreads();
-  }
   float* red = reinterpret_cast<float*>(s.xf);
   float ssm[2] = {0.0f, 0.0f};
   mark(a, s.flag[1], 2);

@@ -1938,7 +1938,7 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   if (k.max_batch >= 2 && k.weight_dtype != S2FAST_Q8) {   // int8 models decode with the batch-1 kernel
     c->bq = batched_group(k, P);
     if (c->bq > 0) {
-      c->b_lds = b_lds_bytes(k.n_layer, k.head_dim, k.context, k.dim);
+      c->b_lds = b_lds_bytes(k.n_layer, k.head_dim, k.context);
       const void* fb = k.weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&frame_kernel_b<uint16_t>)
                                                      : reinterpret_cast<const void*>(&frame_kernel_b<float>);
       int nbb = 0;
