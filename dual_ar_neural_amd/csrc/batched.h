@@ -478,16 +478,26 @@ __device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const 
 struct RedView {
   const float* red;
   int T, wpg, ng;
+  // the N = wpg partials of element (t, slot ln * 4 + r, M-tile mt) of group
+  // g: all N reads issued together, then added in wave order
+  template <int N>
+  __device__ __forceinline__ float sum_n(int g, int t, int mt, int ln, int r) const {
+    float pv[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) pv[j] = red[((((size_t)(g + j * ng)) * T + t) * 2 + mt) * 256 + ln * 4 + r];
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc += pv[j];
+    return acc;
+  }
   __device__ __forceinline__ float sum(int v, int m) const {
     // element (v = 16 t + 4 qd + r, row 32 g + 16 mt + j) sits in lane qd * 16 + j, slot r
     const int t = v >> 4, i = v & 15, g = m >> 5, mt = (m >> 4) & 1;
     const int ln = (i >> 2) * 16 + (m & 15), r = i & 3;
-    float acc = 0.0f;
-    for (int j = 0; j < wpg; ++j) {
-      const int w = g + j * ng;
-      acc += red[(((size_t)w * T + t) * 2 + mt) * 256 + ln * 4 + r];
-    }
-    return acc;
+    static_assert(NWAVE == 8, "wave groups of 8, 4 or 2 waves");
+    if (wpg == 8) return sum_n<8>(g, t, mt, ln, r);
+    if (wpg == 4) return sum_n<4>(g, t, mt, ln, r);
+    return sum_n<2>(g, t, mt, ln, r);
   }
 };
 
