@@ -746,49 +746,86 @@ __device__ __forceinline__ void b_attn_pair(const BatchArgs& a, const BLds& s, i
   // gather: cached keys/values, then the new rows' raw q, k, v (layer 0 of
   // steps >= 2: the qkv0 row of the code that produced the row)
   const float* row0 = (l == 0 && step >= 2) ? a.qkv0 + (size_t)b_code(a, b, step - 1) * a.qkv_dim : nullptr;
-  // a wqkv split over K: the new rows' values are the slices' partial sums
-  // added in slice order, divided by the RMS of the whole row
+  // a wqkv split over K (two slices): the new rows' values are the slices'
+  // partial sums added in slice order, divided by the RMS of the whole row,
+  // rebuilt from the slices' sums of squares
   const int S = row0 ? 1 : a.ks[BK_QKV];
-  float rden[2] = {1.0f, 1.0f};
-  if (S > 1) {
-    for (int nr = 0; nr < n_new; ++nr) {
-      const int m = step == 1 ? nr * a.Bq + b : b;
-      float ss = bkss(a, BK_QKV, step, l, 0)[m];
-      for (int q2 = 1; q2 < S; ++q2) ss += bkss(a, BK_QKV, step, l, q2)[m];
-      rden[nr] = sqrtf(ss / (float)a.dim + a.eps);
-    }
+  // Segments of hd floats: the cached keys of positions < first_new, their
+  // values, then per new row its gh query heads, its key and its value.  A
+  // wave moves one segment per step (lane i: floats 2i, 2i + 1, one 8-byte
+  // load per K-slice); the segment arithmetic is wave-uniform, and a wave
+  // issues the loads of all its segments before storing any.
+  const int F = first_new;
+  const int nseg = 2 * F + n_new * (gh + 2);
+  constexpr int NSW = 4;   // segments a wave per batch
+  float ssq[2][2];
+#pragma unroll
+  for (int nr = 0; nr < 2; ++nr) {
+    const int m = step == 1 ? min(nr, n_new - 1) * a.Bq + b : b;
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) ssq[nr][q2] = S > 1 ? bkss(a, BK_QKV, step, l, q2)[m] : 0.0f;
   }
-  const int n_cache = first_new * 2 * hd;
-  const int n_row = (gh + 2) * hd;
-  for (int i = tid; i < n_cache + n_new * n_row; i += NTHREADS) {
-    if (i < n_cache) {
-      const int pos = i / (2 * hd), r = i - pos * 2 * hd;
-      const float v = bkv(a, b, l, pos, g)[r];
-      (r < hd ? kc : vc)[(size_t)pos * hd + (r % hd)] = v;
-    } else {
-      const int t = i - n_cache;
-      const int nr = t / n_row, r = t - nr * n_row;
-      const int m = step == 1 ? nr * a.Bq + b : b;
-      const int pos = step == 1 ? nr : step;
-      int c;          // column of the wqkv output row
-      float* dst;
-      if (r < gh * hd) { c = g * gh * hd + r; dst = q + (size_t)nr * gh * hd + r; }
-      else if (r < (gh + 1) * hd) { c = H * hd + g * hd + (r - gh * hd); dst = kc + (size_t)pos * hd + (r - gh * hd); }
-      else { c = (H + G) * hd + g * hd + (r - (gh + 1) * hd); dst = vc + (size_t)pos * hd + (r - (gh + 1) * hd); }
-      float v;
-      if (row0) {
-        v = row0[c];
-      } else if (S > 1) {
-        v = bkpart(a, BK_QKV, step, l, 0)[(size_t)m * a.qkv_dim + c];
-        for (int q2 = 1; q2 < S; ++q2) v += bkpart(a, BK_QKV, step, l, q2)[(size_t)m * a.qkv_dim + c];
-        v /= rden[nr];
-      } else {
-        v = bqkv(a, step, l)[(size_t)m * a.qkv_dim + c];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int hp = hd >> 1, lp = min(lane, hp - 1);
+  // segment sg: sources (slice 0, slice 1), LDS destination, and the new
+  // row whose RMS divides it (-1: taken as is)
+  const auto seg = [&](int sg, const float*& s0, const float*& s1, float*& dst, int& nr) __attribute__((always_inline)) {
+    nr = -1;
+    if (sg < F) {
+      s0 = s1 = bkv(a, b, l, sg, g);
+      dst = kc + (size_t)sg * hd;
+      return;
+    }
+    if (sg < 2 * F) {
+      s0 = s1 = bkv(a, b, l, sg - F, g) + hd;
+      dst = vc + (size_t)(sg - F) * hd;
+      return;
+    }
+    const int t = sg - 2 * F;
+    const int r = t >= gh + 2 ? 1 : 0, h = t - r * (gh + 2);   // n_new <= 2
+    const int m = step == 1 ? r * a.Bq + b : b;
+    const int pos = step == 1 ? r : step;
+    int c;   // first column of the segment in the wqkv output row
+    if (h < gh) { c = (g * gh + h) * hd; dst = q + (size_t)(r * gh + h) * hd; }
+    else if (h == gh) { c = (H + g) * hd; dst = kc + (size_t)pos * hd; }
+    else { c = (H + G + g) * hd; dst = vc + (size_t)pos * hd; }
+    if (row0) { s0 = s1 = row0 + c; }
+    else if (S > 1) {
+      s0 = bkpart(a, BK_QKV, step, l, 0) + (size_t)m * a.qkv_dim + c;
+      s1 = bkpart(a, BK_QKV, step, l, 1) + (size_t)m * a.qkv_dim + c;
+      nr = r;
+    } else { s0 = s1 = bqkv(a, step, l) + (size_t)m * a.qkv_dim + c; }
+  };
+  for (int base = 0; base < nseg; base += NSW * NWAVE) {
+    u64 v0[NSW], v1[NSW];
+    float* dst[NSW];
+    int nrw[NSW];
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+      const int sg = base + wv + NWAVE * j;
+      const float *s0, *s1;
+      seg(sg < nseg ? sg : 0, s0, s1, dst[j], nrw[j]);   // a step past the end re-reads segment 0
+      v0[j] = *reinterpret_cast<const u64*>(s0 + 2 * lp);
+      v1[j] = *reinterpret_cast<const u64*>(s1 + 2 * lp);
+    }
+    float rden[2];
+#pragma unroll
+    for (int nr = 0; nr < 2; ++nr) rden[nr] = sqrtf((ssq[nr][0] + ssq[nr][1]) / (float)a.dim + a.eps);
+#pragma unroll
+    for (int j = 0; j < NSW; ++j) {
+      if (base + wv + NWAVE * j < nseg && lane < hp) {
+        float x0 = __uint_as_float((u32)v0[j]), x1 = __uint_as_float((u32)(v0[j] >> 32));
+        if (nrw[j] >= 0) {
+          x0 = (x0 + __uint_as_float((u32)v1[j])) / rden[nrw[j]];
+          x1 = (x1 + __uint_as_float((u32)(v1[j] >> 32))) / rden[nrw[j]];
+        }
+        dst[j][2 * lane] = x0;
+        dst[j][2 * lane + 1] = x1;
       }
-      *dst = v;
     }
   }
   __syncthreads();
+  mark(a, s.flag[1], 2);
   const float* qn = s.qkn + (size_t)l * 2 * hd;
   const float* kn = qn + hd;
   for (int v = wave; v < n_new * gh + n_new; v += NWAVE) {
@@ -800,11 +837,13 @@ __device__ __forceinline__ void b_attn_pair(const BatchArgs& a, const BLds& s, i
     }
   }
   __syncthreads();
+  mark(a, s.flag[1], 3);
   for (int i = tid; i < n_new * 2 * hd; i += NTHREADS) {
     const int nr = i / (2 * hd), r = i - nr * 2 * hd;
     const int pos = first_new + nr;
     st_coh(bkv(a, b, l, pos, g) + r, r < hd ? kc[(size_t)pos * hd + r] : vc[(size_t)pos * hd + r - hd]);
   }
+  mark(a, s.flag[1], 4);
   // one wave per (row, head); same straight-line scheme as the batch-1 kernel
   const float scale = 1.0f / sqrtf((float)hd);
   const int g16 = lane >> 4, l16 = lane & 15;
@@ -855,6 +894,7 @@ __device__ __forceinline__ void b_attn_pair(const BatchArgs& a, const BLds& s, i
     if (lane < hd) st_coh(o + lane, o0);
     if (lane + 64 < hd) st_coh(o + lane + 64, o1);
   }
+  mark(a, s.flag[1], 5);
 }
 
 // The attention phase: workgroup j takes the pairs j, j + gridDim.x, ...

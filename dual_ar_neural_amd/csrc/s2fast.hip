@@ -1976,7 +1976,8 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
       c->b_ks[BK_WO] = (rows_fit && (k.n_head * k.head_dim) % (ks * ksz) == 0) ? ks : 1;
       // wqkv splits two ways (its row groups must also fit TMAX tiles); its
       // consumer, the attention, adds the two slices itself
-      const int kq = 2;
+      constexpr int kq = 2;
+      static_assert(kq <= 2, "the attention gather and the sample phase add at most two slices of wqkv / the head");
       c->b_ks[BK_QKV] = (P % kq == 0 && (qkv_dim + P / kq - 1) / (P / kq) <= 16 * TMAX && k.dim % (kq * ksz) == 0)
                             ? kq : 1;
       // the head too, its consumer (the sample phase) adding the slices
