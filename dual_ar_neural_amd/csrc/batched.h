@@ -735,7 +735,8 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
 // attention with offset 0; the new keys/values are kept for the frame's
 // later steps.
 template <typename WT>
-__device__ __forceinline__ void b_attn_pair(const BatchArgs& a, const BLds& s, int step, int l, int b, int g) {
+__device__ __forceinline__ void b_attn_pair(const BatchArgs& a, const BLds& s, int step, int l, int b, int g,
+                                            int prev_code) {
   const int hd = a.hd, gh = a.gheads, H = a.n_head, G = a.n_kv;
   const int n_new = step == 1 ? 2 : 1;
   const int first_new = step == 1 ? 0 : step;
@@ -745,7 +746,9 @@ __device__ __forceinline__ void b_attn_pair(const BatchArgs& a, const BLds& s, i
   float* vc = kc + (size_t)a.ctx_len * hd;                   // [ctx][hd]
   // gather: cached keys/values, then the new rows' raw q, k, v (layer 0 of
   // steps >= 2: the qkv0 row of the code that produced the row)
-  const float* row0 = (l == 0 && step >= 2) ? a.qkv0 + (size_t)b_code(a, b, step - 1) * a.qkv_dim : nullptr;
+  const float* row0 = (l == 0 && step >= 2)
+                          ? a.qkv0 + (size_t)(prev_code >= 0 ? prev_code : b_code(a, b, step - 1)) * a.qkv_dim
+                          : nullptr;
   // a wqkv split over K (two slices): the new rows' values are the slices'
   // partial sums added in slice order, divided by the RMS of the whole row,
   // rebuilt from the slices' sums of squares
@@ -897,25 +900,18 @@ __device__ __forceinline__ void b_attn_pair(const BatchArgs& a, const BLds& s, i
   mark(a, s.flag[1], 5);
 }
 
-// The attention phase: workgroup j takes the pairs j, j + gridDim.x, ...
-template <typename WT>
-__device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, int step, int l) {
-  for (int j = blockIdx.x; j < a.Bq * a.n_kv; j += gridDim.x) {
-    if (j != (int)blockIdx.x) __syncthreads();   // the previous pair's LDS scratch is read out
-    b_attn_pair<WT>(a, s, step, l, j / a.n_kv, j % a.n_kv);
-  }
-}
-
-// Workgroup b < Bq draws request b's code of step `step` from its logits.
-// With the head split over K, the workgroup first adds request b's two
-// slices of logits in slice order and divides by the RMS rebuilt from the
-// slices' sums of squares, into LDS (and the caller's logits buffer); with a
-// teacher-forced prefix that is all it does.
-__device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s, int step) {
-  const int b = blockIdx.x;
-  if (b >= a.Bq) return;
+// Request b's code of step `step`, drawn from that step's logits and
+// returned to every thread of the workgroup (with a teacher-forced prefix:
+// the prefix's code).  With the head split over K, the workgroup first adds
+// request b's two slices of logits in slice order and divides by the RMS
+// rebuilt from the slices' sums of squares, into LDS.  With `publish` the
+// workgroup also writes the logits to the caller's buffer and the code to
+// the codes arrays.
+__device__ __forceinline__ int b_draw(const BatchArgs& a, const BLds& s, int step, int b, bool publish) {
   const float* L = blogits(a, step) + (size_t)b * a.V;
   const int S = a.ks[BK_HEAD];
+  const bool want_logits = publish && a.logits_out && step >= a.lo_first;
+  if (a.forced && !(S > 1 && want_logits)) return b_code(a, b, step);
   if (S > 1) {
     // Every load of a batch (the slices' sums of squares, then SB logits a
     // thread from each slice) is issued before any is used: one memory
@@ -949,30 +945,71 @@ __device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s
             if (q < S) v += pv[j][q];
           v /= rd;
           lg[i] = v;
-          if (a.logits_out && step >= a.lo_first) a.logits_out[((size_t)b * a.lo_rows + (step - a.lo_first)) * V + i] = v;
+          if (want_logits) a.logits_out[((size_t)b * a.lo_rows + (step - a.lo_first)) * V + i] = v;
         }
       }
     }
     __syncthreads();
     L = lg;
   }
-  if (a.forced) return;
+  if (a.forced) return b_code(a, b, step);
   const SampScratch sc{s.cval, s.cidx, s.sred};
   const int code = sample_request(L, a.V, a.temp[b], a.top_p[b], a.top_k[b],
                                   a.uniforms[(size_t)b * (a.ncb - 1) + (step - 1)], sc);
   if (tidx() == 0) {
     const int c = min(max(code, 0), a.V - 1);
-    st_coh(a.codes + b * 16 + step, c);
-    if (a.codes_out) a.codes_out[(size_t)b * a.ncb + step] = c;
+    s.flag[2] = c;
+    if (publish) {
+      st_coh(a.codes + b * 16 + step, c);
+      if (a.codes_out) a.codes_out[(size_t)b * a.ncb + step] = c;
+    }
+  }
+  __syncthreads();
+  return s.flag[2];
+}
+
+// The last step's draw: workgroup b < Bq draws and publishes request b's code.
+__device__ __forceinline__ void b_phase_sample(const BatchArgs& a, const BLds& s, int step) {
+  if ((int)blockIdx.x < a.Bq) b_draw(a, s, step, blockIdx.x, true);
+}
+
+// The attention phase: workgroup j takes the pairs j, j + gridDim.x, ...
+// With `draw` (layer 0 of steps >= 2), the workgroup of pair (b, g) first
+// draws request b's code of the previous step itself (b_draw; every
+// workgroup of the request draws the same code), so no grid barrier
+// separates the draw from the attention that needs it; the workgroup of
+// KV group 0 publishes the code.
+template <typename WT>
+__device__ __forceinline__ void b_phase_attn(const BatchArgs& a, const BLds& s, int step, int l, bool draw) {
+  for (int j = blockIdx.x; j < a.Bq * a.n_kv; j += gridDim.x) {
+    if (j != (int)blockIdx.x) __syncthreads();   // the previous pair's LDS scratch is read out
+    const int b = j / a.n_kv, g = j - (j / a.n_kv) * a.n_kv;
+    int code = -1;
+    if (draw) {
+      code = b_draw(a, s, step - 1, b, g == 0);
+      __syncthreads();   // the draw's LDS scratch is the attention's
+    }
+    b_attn_pair<WT>(a, s, step, l, b, g, code);
   }
 }
 
-// grid syncs of one launch; steps >= 2 have no layer-0 wqkv phase.  With
-// a teacher-forced prefix a step ends at the head, unless the head is split
-// over K and the caller wants the logits (head_logits): then one sync lets
-// the sample phase assemble them.
-__host__ __device__ inline int b_syncs(int has_proj, int nsteps, int n_layer, bool forced, bool head_logits) {
-  return (has_proj ? 1 : 0) + nsteps * (5 * n_layer + (forced ? (head_logits ? 1 : 0) : 2)) - (nsteps - 1);
+// Whether the next step's layer-0 attention phase draws the codes itself:
+// when every (request, KV group) pair has a workgroup of its own (a
+// workgroup with two pairs of different requests would draw twice: slower
+// than a sample phase of one draw a workgroup and its barrier).
+__host__ __device__ inline bool b_merged_draw(int Bq, int n_kv, int P) { return Bq * n_kv <= P; }
+
+// grid syncs of one launch; steps >= 2 have no layer-0 wqkv phase.  A
+// step's head is followed by one sync; with merged draws the next step's
+// layer-0 attention phase then draws the codes (the last step: a sample
+// phase with no sync after it), otherwise a sample phase and a second sync
+// follow.  With a teacher-forced prefix nothing is drawn, and the head's
+// sync remains only when the head is split over K and the caller wants the
+// logits (head_logits), which the next phase assembles.
+__host__ __device__ inline int b_syncs(int has_proj, int nsteps, int n_layer, bool forced, bool head_logits,
+                                       bool merged) {
+  return (has_proj ? 1 : 0) + nsteps * (5 * n_layer + (forced ? (head_logits ? 1 : 0) : (merged ? 1 : 2))) -
+         (nsteps - 1);
 }
 
 // The phases of one launch; false if a barrier wait gave up.
@@ -994,13 +1031,18 @@ __device__ __forceinline__ bool b_frame(const BatchArgs& a, const BLds& s) {
     b_phase_gemm<WT>(a, s, BK_PROJ, 0, 0);
     if (!grid_sync(a, epoch, s.flag)) return false;
   }
+  // a step's head is followed by a sync when something reads its output:
+  // the draw, or with a teacher-forced prefix the assembly of a split head's
+  // logits for the caller
+  const bool head_sync = !a.forced || (a.ks[BK_HEAD] > 1 && a.logits_out);
+  const bool merged = b_merged_draw(a.Bq, a.n_kv, gridDim.x);
   for (int step = 1; step <= a.nsteps; ++step) {
     const int M = b_rows(a, step);
     if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     for (int l = 0; l < a.n_layer; ++l) {
-      if (l == 0) {
+      if (l == 0 && step == 1) {
         // layer-0 input of every row: the hidden state at position 0, else
-        // fast_embeddings[c_{pos-1}] ("Fast-AR codebook decoding ...", section 2)
+        // fast_embeddings[c_0] ("Fast-AR codebook decoding ...", section 2)
         for (int m = tidx(); m < M; m += NTHREADS) {
           const int pos = b_pos(a, step, m);
           s.rcode[m] = pos == 0 ? -1 : b_code(a, m % a.Bq, pos - 1);
@@ -1012,9 +1054,15 @@ __device__ __forceinline__ bool b_frame(const BatchArgs& a, const BLds& s) {
         if (!grid_sync(a, epoch, s.flag)) return false;
         if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
       }
-      b_phase_attn<WT>(a, s, step, l);
+      b_phase_attn<WT>(a, s, step, l, merged && l == 0 && step >= 2 && head_sync);
       if (!grid_sync(a, epoch, s.flag)) return false;
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
+      if (l == 0 && step >= 2) {
+        // the rows' layer-0 inputs (for wo's residual): fast_embeddings of
+        // the codes the attention phase drew
+        for (int m = tidx(); m < M; m += NTHREADS) s.rcode[m] = b_code(a, m, step - 1);
+        __syncthreads();
+      }
       b_phase_gemm<WT>(a, s, BK_WO, step, l);
       if (!grid_sync(a, epoch, s.flag)) return false;
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
@@ -1026,13 +1074,19 @@ __device__ __forceinline__ bool b_frame(const BatchArgs& a, const BLds& s) {
       if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     }
     b_phase_gemm<WT>(a, s, BK_HEAD, step, 0);
-    // teacher forcing: the next prefix is known (the sample phase then only
-    // assembles a split head's logits for the caller)
-    if (a.forced && !(a.ks[BK_HEAD] > 1 && a.logits_out)) continue;
+    if (!head_sync) continue;
     if (!grid_sync(a, epoch, s.flag)) return false;
+    if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
+    if (merged && !a.forced) {
+      if (step == a.nsteps) b_phase_sample(a, s, step);
+      continue;
+    }
+    // a sample phase of its own: workgroup b draws (or, teacher-forced,
+    // assembles the logits of) request b
     b_phase_sample(a, s, step);
     if (a.forced) continue;
     if (!grid_sync(a, epoch, s.flag)) return false;
+    if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
   }
   return true;
 }

@@ -1602,7 +1602,8 @@ int launch_frame(s2fast_ctx* c, const FrameArgs& fa_in, hipStream_t stream) {
 int launch_batched(s2fast_ctx* c, const BatchArgs& ba_in, hipStream_t stream) {
   BatchArgs ba = ba_in;
   const u32 n = (u32)b_syncs(c->cfg.has_project_in, ba.nsteps, c->cfg.n_layer, ba.forced != nullptr,
-                            c->b_ks[BK_HEAD] > 1 && ba.logits_out != nullptr);
+                            c->b_ks[BK_HEAD] > 1 && ba.logits_out != nullptr,
+                            b_merged_draw(ba.Bq, c->cfg.n_head_kv, c->ncu));
   if (c->epoch > 0xF0000000u) {
     if (hipMemsetAsync(c->flags, 0, (size_t)c->ncu * 64 * sizeof(u32), stream) != hipSuccess) return S2FAST_ERR_HIP;
     c->epoch = 0;
@@ -2012,8 +2013,13 @@ int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B) {
   if (!ctx || B < 1) return -1;
   const int nsteps = ctx->cfg.num_codebooks - 1;
   if (B == 1 || ctx->bq == 0) return B * syncs_for(ctx->cfg, nsteps, false);
-  const int groups = (B + ctx->bq - 1) / ctx->bq;
-  return groups * b_syncs(ctx->cfg.has_project_in, nsteps, ctx->cfg.n_layer, false, false);
+  int n = 0;
+  for (int b0 = 0; b0 < B; b0 += ctx->bq) {
+    const int Bg = std::min(ctx->bq, B - b0);
+    n += b_syncs(ctx->cfg.has_project_in, nsteps, ctx->cfg.n_layer, false, false,
+                 b_merged_draw(Bg, ctx->cfg.n_head_kv, ctx->ncu));
+  }
+  return n;
 }
 
 int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const int32_t* sem_code,
