@@ -121,6 +121,11 @@ __device__ __forceinline__ int sample_block(const float* L, int V, float T, floa
     const int i = tid + j * NTHREADS;
     x[j] = (i < V) ? L[i] : -INFINITY;
   }
+  // The race's exponential of rank `lane` depends only on the uniform: it
+  // is computed while the logits are in flight.
+  const u64 h = splitmix64(((u64)__float_as_uint(u) << 32) + (u64)lane);
+  const double uj = ((double)(h >> 40) + 0.5) * (1.0 / 16777216.0);
+  const float E = (float)(-log(uj));
   int buf = 0;
   if (!(T > 0.0f)) {                                   // greedy: argmax, lowest index on ties
     float bv = -INFINITY; int bi = BIG;
@@ -265,10 +270,7 @@ __device__ __forceinline__ int sample_block(const float* L, int V, float T, floa
   }
   const u64 ge = __ballot(act && my_c >= top_p);
   const int m = ge ? (__ffsll((long long)ge) - 1) : (n - 1);
-  // 5. exponential race over the kept ranks 0..m
-  const u64 h = splitmix64(((u64)__float_as_uint(u) << 32) + (u64)lane);
-  const double uj = ((double)(h >> 40) + 0.5) * (1.0 / 16777216.0);
-  const float E = (float)(-log(uj));
+  // 5. exponential race over the kept ranks 0..m (E computed at the start)
   float key = (lane <= m) ? p / E : -INFINITY;
   int kl = lane;
   wave_best(key, kl);
