@@ -243,6 +243,32 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
     return out
 
 
+def probe_hbm(torch, bd):
+    """The achievable HBM read rate: the library's streaming-read probe (the
+    frame kernel's 16-byte non-temporal load form) over a 2 GiB buffer, eight
+    times the memory-side cache, at a few grid sizes and loads in flight;
+    the best of five timed launches after one warm-up each."""
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(7)
+    sink = torch.empty(1, dtype=torch.int32, device="cuda")
+    best = None
+    for grid, inflight in ((256, 4), (256, 8), (512, 4), (1024, 4), (1024, 8)):
+        bd.stream_read(buf, grid, inflight, sink)
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bd.stream_read(buf, grid, inflight, sink)
+            e1.record()
+            e1.synchronize()
+            gbs = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, grid, inflight)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"probe_gbs": round(best[0], 1), "probe_config": f"{best[1]} workgroups x 512 threads, {best[2]} 16-byte "
+            f"non-temporal loads in flight a thread, 2 GiB read"}
+
+
 def time_frames(torch, ctx, dev_in, B, frames, warmup):
     """Decode `warmup` then `frames` frames on the current stream.  Returns
     (seconds over the timed region, mean seconds per decode call): every call
@@ -415,6 +441,8 @@ def main():
     torch.cuda.synchronize()
     del cal, cal2
 
+    print("[bench] streaming-read probe", file=sys.stderr, flush=True)
+    probe = probe_hbm(torch, bd)
     print(f"[bench] timing {args.steps} frames at batch 1", file=sys.stderr, flush=True)
     secs, kern_s = time_frames(torch, ctx, dev_in, 1, args.steps, args.warmup)
     B = 1
@@ -450,7 +478,8 @@ def main():
                      "kernel": "frame_kernel<bf16>", "bytes_per_launch": bytes_frame,
                      "avg_launch_us": round(kern_s * 1e6, 2),
                      "path_bytes_per_launch": path_bytes,
-                     "path_frac": round(path_bytes / kern_s / 1e9 / PEAK_HBM_GBS, 4)},
+                     "path_frac": round(path_bytes / kern_s / 1e9 / PEAK_HBM_GBS, 4),
+                     **probe, "frac_of_probe": round(achieved / probe["probe_gbs"], 4)},
         "syncs_per_frame": ctx.syncs_per_frame(1),
     }
     n_chk = 0 if args.no_cpu_baseline else min(args.cpu_frames + 1, dev_in[0].shape[0])

@@ -145,6 +145,8 @@ def library() -> ctypes.CDLL:
         lib.s2fast_test_gemv.restype = ctypes.c_int
         lib.s2fast_test_norm_rope_attn.argtypes = [I, I, I, I, I, F, F, P, P, P, P, V]
         lib.s2fast_test_norm_rope_attn.restype = ctypes.c_int
+        lib.s2fast_test_stream_read.argtypes = [P, ctypes.c_uint64, I, I, P, V]
+        lib.s2fast_test_stream_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -155,7 +157,7 @@ EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_
            "s2fast_slow_step", "s2fast_slow_prefill", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed",
            "s2fast_test_slow_timeline", "s2fast_fast_decode", "s2fast_status", "s2fast_slow_status",
            "s2fast_test_watchdog", "s2fast_test_slow_watchdog", "s2fast_test_gemv", "s2fast_test_norm_rope_attn",
-           "s2fast_decode_frame_static")
+           "s2fast_decode_frame_static", "s2fast_test_stream_read")
 
 
 def _strerror(code: int) -> str:
@@ -509,6 +511,18 @@ def rope_table(head_dim: int, context: int, base: float):
     _check(library().s2fast_test_rope_table(head_dim, context, base, c.ctypes.data, s.ctypes.data),
            "s2fast_test_rope_table")
     return c, s
+
+
+def stream_read(buf, grid: int = 256, in_flight: int = 4, sink=None, stream=None):
+    """The streaming-read probe over a contiguous device tensor (test
+    export); returns the int32 device tensor holding the XOR of its words."""
+    if not (isinstance(buf, torch.Tensor) and buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    _check(library().s2fast_test_stream_read(_ptr(buf), buf.numel() * buf.element_size(), grid, in_flight,
+                                             _ptr(sink), _stream(stream)), "s2fast_test_stream_read")
+    return sink
 
 
 def sample(logits, temperature, top_p, top_k, u, stream=None):

@@ -1382,6 +1382,41 @@ __global__ void __launch_bounds__(256) qkv0_gemm_kernel(const WT* W, const float
   }
 }
 
+// ------------------------------------------------- streaming-read probe
+// The achievable HBM read rate, measured with the frame kernel's load form:
+// workgroup b reads bytes [b n / G, (b + 1) n / G) of src with 16-byte
+// non-temporal loads, U in flight a thread, and folds every 32-bit word
+// into an XOR; sink[0] receives the XOR of the whole buffer (one atomic a
+// workgroup), so a test can check that every byte was read.
+template <int U>
+__global__ void __launch_bounds__(NTHREADS) stream_read_kernel(const u32x4* src, size_t n16, u32* sink) {
+  const size_t G = gridDim.x;
+  const size_t s0 = n16 * blockIdx.x / G, s1 = n16 * (blockIdx.x + 1) / G;
+  u32 acc = 0u;
+  size_t i = s0 + threadIdx.x;
+  for (; i + (size_t)(U - 1) * NTHREADS < s1; i += (size_t)U * NTHREADS) {
+    u32x4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) v[j] = __builtin_nontemporal_load(src + i + (size_t)j * NTHREADS);
+#pragma unroll
+    for (int j = 0; j < U; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  for (; i < s1; i += NTHREADS) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  __shared__ u32 part[NWAVE];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc ^= (u32)__shfl_xor((int)acc, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u32 t = 0u;
+    for (int w = 0; w < NWAVE; ++w) t ^= part[w];
+    atomicXor(sink, t);
+  }
+}
+
 // ------------------------------------------------- static frame scratch
 // Scratch of s2fast_decode_frame_static, for callers that cannot allocate:
 // the batch-1 frame arena and barrier flags of one launch, in one array per
@@ -2197,6 +2232,22 @@ int s2fast_test_timeline(s2fast_ctx* ctx, int32_t enable, uint32_t* host_out, in
     if (hipMemcpy(host_out, ctx->tlog, n * sizeof(u32), hipMemcpyDeviceToHost) != hipSuccess) return S2FAST_ERR_HIP;
   }
   return S2FAST_OK;
+}
+
+int s2fast_test_stream_read(const void* src, uint64_t bytes, int32_t grid, int32_t in_flight, uint32_t* sink,
+                            void* stream) {
+  if (!src || !sink || (reinterpret_cast<uintptr_t>(src) & 15u) || bytes == 0 || (bytes & 15u) || grid < 1 ||
+      grid > 65535 || (in_flight != 4 && in_flight != 8))
+    return S2FAST_ERR_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return S2FAST_ERR_HIP;
+  if (!is_gfx950(dev)) return S2FAST_ERR_DEVICE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemsetAsync(sink, 0, sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
+  const u32x4* p = reinterpret_cast<const u32x4*>(src);
+  if (in_flight == 4) hipLaunchKernelGGL(stream_read_kernel<4>, dim3(grid), dim3(NTHREADS), 0, st, p, bytes / 16, sink);
+  else hipLaunchKernelGGL(stream_read_kernel<8>, dim3(grid), dim3(NTHREADS), 0, st, p, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? S2FAST_OK : S2FAST_ERR_HIP;
 }
 
 int s2fast_test_rope_table(int32_t head_dim, int32_t context, float rope_base, float* cos_out, float* sin_out) {

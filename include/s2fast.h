@@ -420,6 +420,18 @@ int s2fast_slow_allowed(const s2fast_slow_ctx* ctx);
 int s2fast_test_rope_table(int32_t head_dim, int32_t context, float rope_base,
                            float* cos_out, float* sin_out);
 
+/* Streaming-read probe (the achievable HBM read rate the roofline quotes
+ * beside the 8 TB/s specification): one launch of `grid` workgroups x 512
+ * threads reads the `bytes` at `src` (device, 16-byte aligned, bytes a
+ * multiple of 16) with 16-byte non-temporal loads, `in_flight` (4 or 8) a
+ * thread, block b taking a contiguous 1/grid of the buffer, and writes the
+ * XOR of every 32-bit word of the buffer to *sink (device; cleared first).
+ * Enqueued on `stream`.  S2FAST_ERR_ARG for NULL or misaligned pointers,
+ * a size of 0 or not a multiple of 16, grid outside [1, 65535] or another
+ * in_flight; S2FAST_ERR_DEVICE off gfx950. */
+int s2fast_test_stream_read(const void* src, uint64_t bytes, int32_t grid, int32_t in_flight, uint32_t* sink,
+                            void* stream);
+
 /* Device sampler on caller-supplied logits [B, V] (device), with the same
  * settings layout as s2fast_decode_frame but one uniform per request
  * (u [B]).  Writes codes [B] (device).  V <= 8192. */

@@ -134,6 +134,14 @@ def test_kernel_test_exports_reject_bad_arguments():
     assert lib.s2fast_test_norm_rope_attn(4, 2, 60, 4, 11, 1e6, 1e-6, fake, None, None, fake, None) == 1
     assert lib.s2fast_test_norm_rope_attn(4, 2, 64, 12, 11, 1e6, 1e-6, fake, None, None, fake, None) == 1
     assert lib.s2fast_test_norm_rope_attn(4, 2, 64, 4, 11, 1e6, 1e-6, fake, fake, None, fake, None) == 1
+    # streaming probe: NULL / misaligned buffer, size 0 or not a multiple of 16, grid, loads in flight
+    assert lib.s2fast_test_stream_read(None, 1024, 256, 4, fake, None) == 1
+    assert lib.s2fast_test_stream_read(fake + 8, 1024, 256, 4, fake, None) == 1
+    assert lib.s2fast_test_stream_read(fake, 0, 256, 4, fake, None) == 1
+    assert lib.s2fast_test_stream_read(fake, 1000, 256, 4, fake, None) == 1
+    assert lib.s2fast_test_stream_read(fake, 1024, 0, 4, fake, None) == 1
+    assert lib.s2fast_test_stream_read(fake, 1024, 256, 3, fake, None) == 1
+    assert lib.s2fast_test_stream_read(fake, 1024, 256, 4, None, None) == 1
 
 
 # ---------------------------------------------------------------- Slow-AR

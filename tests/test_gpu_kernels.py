@@ -301,3 +301,23 @@ def test_gemv_q8_random(name, N, K, swiglu, norm):
     r = np.abs(y - want) / (bound + 1e-30)
     assert np.all(r <= 1.0), (name, float(r.max()))
     _announce(f"gemv q8 {name} random: worst |d|/bound {float(r.max()):.2e}")
+
+
+# ------------------------------------------------------------------ streaming-read probe
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("nbytes,grid,in_flight", [(16, 1, 4), (1 << 20, 256, 4), ((1 << 20) + 48, 7, 8),
+                                                   (64 << 20, 256, 8), ((64 << 20) + 16 * 513, 1024, 4)])
+def test_stream_read_reads_every_byte(nbytes, grid, in_flight):
+    """The probe's XOR of every 32-bit word equals numpy's over the same
+    random buffer: every byte was read exactly once (a word read twice
+    would cancel out, one skipped would be missing)."""
+    _announce(f"stream_read {nbytes} B, grid {grid}, {in_flight} in flight")
+    rng = np.random.default_rng(nbytes + grid)
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = bd.stream_read(buf, grid=grid, in_flight=in_flight)
+    torch.cuda.synchronize()
+    want = int(np.bitwise_xor.reduce(host))
+    got = int(sink.cpu().numpy().view(np.uint32)[0])
+    assert got == want, (hex(got), hex(want))
