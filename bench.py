@@ -92,6 +92,31 @@ def slow_step_bytes(shape, n_past: int, head: bool = True, M: int = 1) -> int:
     return s.n_layer * per_layer + kv + head_b + inputs
 
 
+def prefill_launches(T: int, chunks: bool, chunk: int = 64):
+    """(first position offset, positions, head) of each launch the library
+    makes for a T-position prefill whose cache positions all fit the chunked
+    attention's score buffer: the positions before the last in chunks of up
+    to `chunk`, then the last alone with the head; with chunks off, two
+    positions a launch, the last launch with the head."""
+    out, t = [], 0
+    if chunks:
+        while t < T - 1:
+            c = min(chunk, T - 1 - t)
+            out.append((t, c, False))
+            t += c
+    while t < T:
+        m = min(2, T - t)
+        out.append((t, m, t + m == T))
+        t += m
+    return out
+
+
+def prefill_bytes(shape, n_past0: int, T: int, chunks: bool) -> int:
+    """Minimum bytes of a prefill as the library splits it into launches
+    (slow_step_bytes of each launch)."""
+    return sum(slow_step_bytes(shape, n_past0 + t, head=h, M=m) for t, m, h in prefill_launches(T, chunks))
+
+
 def slow_traffic():
     """HBM bytes per Slow-AR launch from the committed counter summary, if it
     was taken on the current kernel code (else None)."""
@@ -207,7 +232,9 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
                            "frac": round(slow_b / slow_s / 1e9 / PEAK_HBM_GBS, 4), "syncs": slow.syncs(),
                            "launches": n_slow}}
     # prefill: a prompt of 64 text tokens and 192 reference-audio positions
-    # (semantic ids with codes) from position 0, two positions per launch
+    # (semantic ids with codes) from position 0; the positions before the
+    # last in chunks of up to 64 a launch, then the last with the head and
+    # the draw; and the same prompt two positions a launch for comparison
     P, n_text = 256, 64
     rng = np.random.default_rng(w.seed(6))
     toks = np.zeros((P, 1 + s.num_codebooks), np.int32)
@@ -215,24 +242,38 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
     toks[:n_text, 0] = rng.integers(0, s.sem_begin, size=n_text)
     toks[n_text:, 0] = rng.integers(s.sem_begin, s.sem_end + 1, size=P - n_text)
     toks_d = torch.from_numpy(toks).cuda()
-    window.zero_()
-    slow.prefill(kv, 0, toks_d, window, u_slow[0], temp, tp, tk, main_out=main, sem_out=sem, hidden_out=hidden,
-                 stream=stream)
-    torch.cuda.synchronize()
-    print(f"[bench] timing a {P}-position prefill", file=sys.stderr, flush=True)
-    e0.record(stream)
-    slow.prefill(kv, 0, toks_d, window, u_slow[0], temp, tp, tk, main_out=main, sem_out=sem, hidden_out=hidden,
-                 stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    psec = e0.elapsed_time(e1) / 1e3
-    pb = sum(slow_step_bytes(s, p, head=(p + 2 >= P), M=min(2, P - p)) for p in range(0, P, 2))
+
+    def time_prefill(chunks):
+        slow.prefill_chunks(chunks)
+        window.zero_()
+        slow.prefill(kv, 0, toks_d, window, u_slow[0], temp, tp, tk, main_out=main, sem_out=sem, hidden_out=hidden,
+                     stream=stream)
+        torch.cuda.synchronize()
+        print(f"[bench] timing a {P}-position prefill ({'chunks of 64' if chunks else 'two positions a launch'})",
+              file=sys.stderr, flush=True)
+        window.zero_()
+        e0.record(stream)
+        slow.prefill(kv, 0, toks_d, window, u_slow[0], temp, tp, tk, main_out=main, sem_out=sem, hidden_out=hidden,
+                     stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    psec2 = time_prefill(False)
+    psec = time_prefill(True)
+    pb = prefill_bytes(s, 0, P, True)
+    pb2 = prefill_bytes(s, 0, P, False)
     out["prefill"] = {"workload": f"S2 Pro-shaped Slow-AR prefill of {P} prompt positions ({n_text} text tokens, "
-                                  f"{P - n_text} reference-audio positions with codes) from an empty cache, two "
-                                  "positions per step launch, then the first main-token draw",
+                                  f"{P - n_text} reference-audio positions with codes) from an empty cache: the "
+                                  "positions before the last in chunks of up to 64 a launch on the matrix cores, "
+                                  "then the last position with the head and the first main-token draw",
                       "positions": P, "positions_per_s": round(P / psec, 1), "ms": round(psec * 1e3, 2),
+                      "launches": len(prefill_launches(P, True)),
                       "bytes": int(pb), "hbm_gbs": round(pb / psec / 1e9, 1),
-                      "frac": round(pb / psec / 1e9 / PEAK_HBM_GBS, 4)}
+                      "frac": round(pb / psec / 1e9 / PEAK_HBM_GBS, 4),
+                      "two_per_launch": {"positions_per_s": round(P / psec2, 1), "ms": round(psec2 * 1e3, 2),
+                                         "launches": len(prefill_launches(P, False)), "bytes": int(pb2),
+                                         "hbm_gbs": round(pb2 / psec2 / 1e9, 1)}}
     slow.close()
     del dev, kv
     torch.cuda.empty_cache()

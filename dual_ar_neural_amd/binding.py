@@ -141,6 +141,8 @@ def library() -> ctypes.CDLL:
         lib.s2fast_test_watchdog.restype = ctypes.c_int
         lib.s2fast_test_slow_watchdog.argtypes = [P, I]
         lib.s2fast_test_slow_watchdog.restype = ctypes.c_int
+        lib.s2fast_test_slow_prefill_chunks.argtypes = [P, I]
+        lib.s2fast_test_slow_prefill_chunks.restype = ctypes.c_int
         lib.s2fast_test_gemv.argtypes = [I, I, I, I, P, P, P, P, P, F, P, P, V]
         lib.s2fast_test_gemv.restype = ctypes.c_int
         lib.s2fast_test_norm_rope_attn.argtypes = [I, I, I, I, I, F, F, P, P, P, P, V]
@@ -157,7 +159,7 @@ EXPORTS = ("s2fast_create", "s2fast_destroy", "s2fast_strerror", "s2fast_decode_
            "s2fast_slow_step", "s2fast_slow_prefill", "s2fast_full_frame", "s2fast_slow_syncs", "s2fast_slow_allowed",
            "s2fast_test_slow_timeline", "s2fast_fast_decode", "s2fast_status", "s2fast_slow_status",
            "s2fast_test_watchdog", "s2fast_test_slow_watchdog", "s2fast_test_gemv", "s2fast_test_norm_rope_attn",
-           "s2fast_decode_frame_static", "s2fast_test_stream_read")
+           "s2fast_decode_frame_static", "s2fast_test_stream_read", "s2fast_test_slow_prefill_chunks")
 
 
 def _strerror(code: int) -> str:
@@ -407,6 +409,10 @@ class SlowAR:
 
     def test_watchdog(self, give_up: bool) -> None:
         _check(library().s2fast_test_slow_watchdog(self._ctx, int(give_up)), "s2fast_test_slow_watchdog")
+
+    def prefill_chunks(self, enable: bool) -> None:
+        """Chunked prefill on (default) or off (two positions a launch)."""
+        _check(library().s2fast_test_slow_prefill_chunks(self._ctx, int(enable)), "s2fast_test_slow_prefill_chunks")
 
     def timeline(self, enable: bool = True, fetch: bool = False):
         """Per-block phase timing of later steps (see FastAR.timeline)."""

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libs2fast.so")
 SOURCES = [os.path.join(HERE, "csrc", "s2fast.hip")]
-DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("device_common.h", "sampler.h", "batched.h", "slow_step.h", "slow_host.h")] + \
+DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("device_common.h", "sampler.h", "batched.h", "slow_step.h", "prefill.h", "slow_host.h")] + \
     [os.path.join(ROOT, "include", "s2fast.h")]
 
 HIPCC_FLAGS = [

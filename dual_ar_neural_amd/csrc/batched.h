@@ -8,8 +8,9 @@
 // cores: each workgroup owns a range of W's rows (all of K); W (bf16) is the
 // MFMA A operand, streamed from HBM with 16-byte loads; X, read from the
 // arena by the wave that uses it, is the B operand split into bf16 high and
-// low halves (x = hi + lo to about 2^-16 relative), so that the products keep
-// float32-level accuracy; accumulation is float32.  f32 weights use the
+// low halves (x = hi + lo to about 2^-18 relative; the Slow-AR prefill,
+// 36 layers deep, adds a third piece), so that the products keep near
+// float32 accuracy; accumulation is float32.  f32 weights use the
 // float32 MFMA with float32 X instead.
 //
 // Phases per step and layer (grid barrier after each):
@@ -95,6 +96,21 @@ struct BatchArgs {
   u32* err;                 // watchdog words (see Watch)
   Watch watch;
   u32* tlog;
+  // Slow-AR prefill launches (prefill = 1): the prompt positions n_past0 ..
+  // n_past0 + Bq - 1 are the rows of one step through up to
+  // S2FAST_SLOW_MAX_LAYERS layers, whose pointers and packed streams come
+  // from device tables
+  int prefill;
+  int lds_layers;           // layers whose q/k norm weights the LDS holds (n_layer; 1 in prefill)
+  const LayerPtr* Lt;       // [n_layer] (prefill)
+  const char* const* pkt;   // [2 + 4 n_layer] (prefill)
+  int n_past0, max_ctx;
+  void* cache;              // the caller's KV cache [n_layer][n_kv][max_ctx][2][hd], weight type
+  const int* tokens;        // [Bq][1 + ncb] row-0 token and codes of each position
+  float* x0w;               // [Bq][dim] the positions' inputs (hidden reads them)
+  const void* cemb;         // codebook embeddings [ncb * cbs][dim]
+  int cbs, sem_begin, vocab;
+  float sem_scale;
 };
 
 struct BLds {
@@ -110,8 +126,10 @@ struct BLds {
   int* flag;     // [4]
 };
 
-__host__ __device__ inline size_t b_lds_bytes(int n_layer, int hd, int ctx) {
-  return (size_t)XF_BYTES + sizeof(float) * ((size_t)NWAVE * MP_MAX + MP_MAX + (size_t)n_layer * 2 * hd + (size_t)ctx * hd +
+// dynamic LDS of a launch whose q/k norm weights of lds_layers layers and
+// RoPE table of ctx positions sit in LDS
+__host__ __device__ inline size_t b_lds_bytes(int lds_layers, int hd, int ctx) {
+  return (size_t)XF_BYTES + sizeof(float) * ((size_t)NWAVE * MP_MAX + MP_MAX + (size_t)lds_layers * 2 * hd + (size_t)ctx * hd +
                                              TOPK_MAX) +
          sizeof(int) * ((size_t)TOPK_MAX + 2 * NWAVE * SAMP_TAU + MP_MAX + 4);
 }
@@ -122,7 +140,7 @@ __device__ inline BLds b_carve(char* base, const BatchArgs& a) {
   s.xf = p; p += XF_BYTES;
   s.ssp = reinterpret_cast<float*>(p); p += sizeof(float) * NWAVE * MP_MAX;
   s.rms = reinterpret_cast<float*>(p); p += sizeof(float) * MP_MAX;
-  s.qkn = reinterpret_cast<float*>(p); p += sizeof(float) * (size_t)a.n_layer * 2 * a.hd;
+  s.qkn = reinterpret_cast<float*>(p); p += sizeof(float) * (size_t)a.lds_layers * 2 * a.hd;
   s.rope = reinterpret_cast<float*>(p); p += sizeof(float) * (size_t)a.ctx_len * a.hd;
   s.cval = reinterpret_cast<float*>(p); p += sizeof(float) * TOPK_MAX;
   s.cidx = reinterpret_cast<int*>(p); p += sizeof(int) * TOPK_MAX;
@@ -134,7 +152,12 @@ __device__ inline BLds b_carve(char* base, const BatchArgs& a) {
 
 // rows of decode step `step`: request b's positions 0 and 1 are rows b and
 // Bq + b at step 1; position `step` is row b afterwards
-__device__ __forceinline__ int b_rows(const BatchArgs& a, int step) { return step == 1 ? 2 * a.Bq : a.Bq; }
+__device__ __forceinline__ int b_rows(const BatchArgs& a, int step) {
+  return (step == 1 && !a.prefill) ? 2 * a.Bq : a.Bq;
+}
+// layer l's pointers and the packed stream idx (device tables in prefill launches)
+__device__ __forceinline__ LayerPtr b_layer(const BatchArgs& a, int l) { return a.prefill ? a.Lt[l] : a.L[l]; }
+__device__ __forceinline__ const char* b_pk(const BatchArgs& a, int idx) { return a.prefill ? a.pkt[idx] : a.pk[idx]; }
 __device__ __forceinline__ int b_pos(const BatchArgs& a, int step, int m) { return step == 1 ? m / a.Bq : step; }
 __device__ __forceinline__ int b_last_row(const BatchArgs& a, int step, int b) { return step == 1 ? a.Bq + b : b; }
 
@@ -302,7 +325,7 @@ __device__ __forceinline__ void b_fetch(const BatchArgs& a, const BLds& s, const
 // columns s KSZ + GE (lane / 16) ..) and the X fragment of each M-tile (B
 // operand: lane -> row 16 mt + lane % 16, the same columns), applies the
 // phase's RMSNorm weight, splits X into bf16 high and low halves (x = hi + lo
-// to about 2^-16 relative) and accumulates D[t][mt] in float32.  The loads of
+// to about 2^-18 relative; a third piece with XS = 3) and accumulates D[t][mt] in float32.  The loads of
 // a k-step are issued PD k-steps before it is used (more when a k-step has
 // few row tiles; deeper pipelines measured slower).
 //
@@ -356,7 +379,9 @@ __device__ __forceinline__ void b_load(const BatchArgs& a, const BLds& s, const 
   if (gd.normw) u.nw = *reinterpret_cast<const uint4*>(reinterpret_cast<const WT*>(gd.normw) + gd.k0 + c);
 }
 
-template <typename WT, int TT, int MTT>
+// XS: bf16 pieces of X for bf16 weights (2: x = hi + lo to about 2^-18
+// relative; 3: a third piece, to about 2^-27, float32-level)
+template <typename WT, int TT, int MTT, int XS>
 __device__ __forceinline__ void b_use(const BLds& s, const GemmDesc& gd, int st, int lane, const BUnit<WT, TT, MTT>& u,
                                       f32x4 (&D)[TT][MTT], float (&ss)[MTT]) {
   constexpr int GE = MF<WT>::GE;
@@ -374,21 +399,25 @@ __device__ __forceinline__ void b_use(const BLds& s, const GemmDesc& gd, int st,
       }
     }
     if (GE == 8) {
-      u32 h[4], lw[4];
+      u32 h[4], lw[4], l2[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         h[p] = bf16_pair(x[2 * p], x[2 * p + 1]);
-        lw[p] = bf16_pair(x[2 * p] - __uint_as_float(h[p] << 16), x[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u));
+        const float r0 = x[2 * p] - __uint_as_float(h[p] << 16), r1 = x[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u);
+        lw[p] = bf16_pair(r0, r1);
+        if (XS == 3) l2[p] = bf16_pair(r0 - __uint_as_float(lw[p] << 16), r1 - __uint_as_float(lw[p] & 0xFFFF0000u));
       }
-      bf16x8 hv, lv;
+      bf16x8 hv, lv, l2v;
       __builtin_memcpy(&hv, h, 16);
       __builtin_memcpy(&lv, lw, 16);
+      if (XS == 3) __builtin_memcpy(&l2v, l2, 16);
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         bf16x8 av;
         __builtin_memcpy(&av, &u.w[t], 16);
         D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, D[t][mt], 0, 0, 0);
         D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lv, D[t][mt], 0, 0, 0);
+        if (XS == 3) D[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, l2v, D[t][mt], 0, 0, 0);
       }
     } else {
 #pragma unroll
@@ -433,7 +462,7 @@ struct BShare {
   }
 };
 
-template <typename WT, int TT, int MTT>
+template <typename WT, int TT, int MTT, int XS>
 __device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const GemmDesc& gd, int wave, int kw,
                                        int wpg, int lane, float* red, float (&ssm)[2]) {
   constexpr int KSZ = MF<WT>::KSZ, PD = bpd<TT, MTT>();
@@ -459,7 +488,7 @@ __device__ __forceinline__ void b_core(const BatchArgs& a, const BLds& s, const 
 #pragma unroll
     for (int r = 0; r < PD; ++r) {
       b_load<WT, TT, MTT>(a, s, gd, kstep(i + r + PD - 1), KST, lane, u[(r + PD - 1) % PD]);
-      if (i + r < ns) b_use<WT, TT, MTT>(s, gd, kstep(i + r), lane, u[r], D, ss);
+      if (i + r < ns) b_use<WT, TT, MTT, XS>(s, gd, kstep(i + r), lane, u[r], D, ss);
     }
   }
 #pragma unroll
@@ -509,7 +538,7 @@ struct RedView {
 // for its rows, the waves of a group splitting the k-steps.  The groups
 // read the same weight fragments at about the same time (one HBM fill
 // serves them).
-template <typename WT>
+template <typename WT, int XS>
 __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, const GemmDesc& gd) {
   const int tid = tidx();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave-uniform work split
@@ -527,8 +556,8 @@ __device__ __forceinline__ RedView b_gemm(const BatchArgs& a, const BLds& s, con
   mark(a, s.flag[1], 2);
 #define B_CORE(TT_)                                                                 \
   case TT_:                                                                         \
-    if (MT == 1) b_core<WT, TT_, 1>(a, s, gg, wave, kw, wpg, lane, red, ssm);       \
-    else b_core<WT, TT_, 2>(a, s, gg, wave, kw, wpg, lane, red, ssm);               \
+    if (MT == 1) b_core<WT, TT_, 1, XS>(a, s, gg, wave, kw, wpg, lane, red, ssm);   \
+    else b_core<WT, TT_, 2, XS>(a, s, gg, wave, kw, wpg, lane, red, ssm);           \
     break;
   switch (T) {
     B_CORE(1)
@@ -573,7 +602,7 @@ __device__ __forceinline__ float b_layer0_elem(const BatchArgs& a, const BLds& s
   return WTraits<WT>::one(reinterpret_cast<const WT*>(a.emb) + (size_t)c * a.dim, k);
 }
 
-template <typename WT>
+template <typename WT, int XS = 2>
 __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, int kind, int step, int l) {
   const int P = gridDim.x, blk = blockIdx.x;
   GemmDesc gd;
@@ -583,7 +612,7 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   gd.m0 = 0;
   int r0 = 0, r1 = 0, ks = 0;
   const int S = a.ks[kind];
-  const LayerPtr& L = a.L[l];
+  const LayerPtr L = b_layer(a, l);
   switch (kind) {
     case BK_PROJ:
       split_rows(a.dim, blk, P, r0, r1);
@@ -620,14 +649,14 @@ __device__ __forceinline__ void b_phase_gemm(const BatchArgs& a, const BLds& s, 
   const int nr = r1 - r0;
   gd.R = kind == BK_UP ? 2 * nr : nr;
   gd.kp = (long long)((gd.K + MF<WT>::KSZ - 1) / MF<WT>::KSZ) * 64;
-  gd.pk = a.pk[pk_index(kind, l)] + (long long)(kind == BK_UP ? 2 * r0 : r0 * S + ks * nr) * gd.kp;
+  gd.pk = b_pk(a, pk_index(kind, l)) + (long long)(kind == BK_UP ? 2 * r0 : r0 * S + ks * nr) * gd.kp;
   // rows in passes of at most GM_MAX (the MFMA core's M-tiles): a pass
   // streams this workgroup's weights once
   const int Mt = gd.M;
   for (int m0 = 0; m0 < Mt; m0 += GM_MAX) {
     gd.m0 = m0;
     gd.M = min(GM_MAX, Mt - m0);
-    const RedView rv = b_gemm<WT>(a, s, gd);
+    const RedView rv = b_gemm<WT, XS>(a, s, gd);
     mark(a, s.flag[1], 4);
     const int M = gd.M;
     const int nv = kind == BK_UP ? nr : gd.R;

@@ -1431,6 +1431,7 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(u32* p, size_t n) {
 
 #include "batched.h"
 #include "slow_step.h"
+#include "prefill.h"
 
 #ifndef KS_DOWN
 #define KS_DOWN 4
@@ -1544,14 +1545,40 @@ hipError_t dalloc(T** p, size_t n) {
   return hipMalloc(reinterpret_cast<void**>(p), n * sizeof(T) > 0 ? n * sizeof(T) : 16);
 }
 
-// The batched GEMMs' packed weight streams (b_pack_kernel), one per GEMM
-// and layer, from the weights the context was created with.
+// One packed weight stream (b_pack_kernel) per job, all in one allocation;
+// off[idx] is job idx's byte offset in it.  The streams are cut for grids of
+// ncu workgroups.
+struct PackJob { int idx; const void* wa; const void* wb; int R, K, S; };
+
+int pack_jobs(int dtype, int ncu, const PackJob* jobs, int nj, char** out, long long* off) {
+  const int ksz = dtype == S2FAST_BF16 ? 32 : 16;
+  long long total = 0;
+  for (int j = 0; j < nj; ++j) {
+    off[jobs[j].idx] = total;
+    const long long rows = (long long)jobs[j].R * (jobs[j].wb ? 2 : 1) * jobs[j].S;
+    total += rows * ((jobs[j].K / jobs[j].S + ksz - 1) / ksz) * 64;
+    total = (total + 255) / 256 * 256;
+  }
+  if (dalloc(out, (size_t)total) != hipSuccess) return S2FAST_ERR_NOMEM;
+  for (int j = 0; j < nj; ++j) {
+    char* dst = *out + off[jobs[j].idx];
+    if (dtype == S2FAST_BF16)
+      hipLaunchKernelGGL(b_pack_kernel<uint16_t>, dim3(ncu), dim3(256), 0, 0,
+                         static_cast<const uint16_t*>(jobs[j].wa), static_cast<const uint16_t*>(jobs[j].wb),
+                         jobs[j].R, jobs[j].K, jobs[j].S, dst);
+    else
+      hipLaunchKernelGGL(b_pack_kernel<float>, dim3(ncu), dim3(256), 0, 0, static_cast<const float*>(jobs[j].wa),
+                         static_cast<const float*>(jobs[j].wb), jobs[j].R, jobs[j].K, jobs[j].S, dst);
+  }
+  return (hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess) ? S2FAST_OK : S2FAST_ERR_HIP;
+}
+
+// The batched GEMMs' packed weight streams, one per GEMM and layer, from the
+// weights the context was created with.
 int pack_batched(s2fast_ctx* c) {
   const s2fast_config& k = c->cfg;
   const int qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim, attn_dim = k.n_head * k.head_dim;
-  const int ksz = k.weight_dtype == S2FAST_BF16 ? 32 : 16;
-  struct Job { int idx; const void* wa; const void* wb; int R, K, S; };
-  Job jobs[2 + 4 * S2FAST_MAX_LAYERS];
+  PackJob jobs[2 + 4 * S2FAST_MAX_LAYERS];
   int nj = 0;
   if (k.has_project_in) jobs[nj++] = {0, c->w.project_in, nullptr, k.dim, k.in_dim, 1};
   jobs[nj++] = {1, c->w.output, nullptr, k.codebook_size, k.dim, c->b_ks[BK_HEAD]};
@@ -1562,25 +1589,7 @@ int pack_batched(s2fast_ctx* c) {
     jobs[nj++] = {2 + 4 * l + 2, L.w1, L.w3, k.ffn_dim, k.dim, 1};
     jobs[nj++] = {2 + 4 * l + 3, L.w2, nullptr, k.dim, k.ffn_dim, c->b_ks[BK_DOWN]};
   }
-  long long total = 0;
-  for (int j = 0; j < nj; ++j) {
-    c->b_pk_off[jobs[j].idx] = total;
-    const long long rows = (long long)jobs[j].R * (jobs[j].wb ? 2 : 1) * jobs[j].S;
-    total += rows * ((jobs[j].K / jobs[j].S + ksz - 1) / ksz) * 64;
-    total = (total + 255) / 256 * 256;
-  }
-  if (dalloc(&c->b_pk, (size_t)total) != hipSuccess) return S2FAST_ERR_NOMEM;
-  for (int j = 0; j < nj; ++j) {
-    char* dst = c->b_pk + c->b_pk_off[jobs[j].idx];
-    if (k.weight_dtype == S2FAST_BF16)
-      hipLaunchKernelGGL(b_pack_kernel<uint16_t>, dim3(c->ncu), dim3(256), 0, 0,
-                         static_cast<const uint16_t*>(jobs[j].wa), static_cast<const uint16_t*>(jobs[j].wb),
-                         jobs[j].R, jobs[j].K, jobs[j].S, dst);
-    else
-      hipLaunchKernelGGL(b_pack_kernel<float>, dim3(c->ncu), dim3(256), 0, 0, static_cast<const float*>(jobs[j].wa),
-                         static_cast<const float*>(jobs[j].wb), jobs[j].R, jobs[j].K, jobs[j].S, dst);
-  }
-  return (hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess) ? S2FAST_OK : S2FAST_ERR_HIP;
+  return pack_jobs(k.weight_dtype, c->ncu, jobs, nj, &c->b_pk, c->b_pk_off);
 }
 
 // The qkv0 table from the weights the context was created with (they stay
@@ -1658,7 +1667,7 @@ void fill_batch_shape(const s2fast_ctx* c, BatchArgs& ba) {
   std::memset(&ba, 0, sizeof(ba));
   ba.in_dim = k.in_dim; ba.dim = k.dim; ba.n_layer = k.n_layer; ba.n_head = k.n_head; ba.n_kv = k.n_head_kv;
   ba.hd = k.head_dim; ba.ffn = k.ffn_dim; ba.V = k.codebook_size; ba.ncb = k.num_codebooks; ba.ctx_len = k.context;
-  ba.eps = k.norm_eps; ba.has_proj = k.has_project_in; ba.has_qkn = k.has_qk_norm;
+  ba.eps = k.norm_eps; ba.has_proj = k.has_project_in; ba.has_qkn = k.has_qk_norm; ba.lds_layers = k.n_layer;
   ba.nsteps = k.num_codebooks - 1; ba.forced_ld = k.num_codebooks; ba.lo_first = 1; ba.lo_rows = k.num_codebooks - 1;
   ba.qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim;
   ba.attn_dim = k.n_head * k.head_dim;

@@ -27,6 +27,28 @@ struct s2fast_slow_ctx {
   bool tlog_on = false;
   u32 give_up = 0;         // test hook (s2fast_test_slow_watchdog)
   u32 epoch = 0;
+  // chunked prefill on the matrix cores (prefill_kernel_b), set up by the
+  // first s2fast_slow_prefill: packed weight streams, their device table and
+  // an arena of n_layer slots of BQ_MAX position rows
+  int prefill_chunks = 1;  // 0: every prefill runs two positions a launch (s2fast_test_slow_prefill_chunks)
+  int pf_state = 0;        // 0: not set up; 1: ready; -1: the shape prefills two positions a launch
+  int pf_pmax = 0;         // cache positions whose attention scores fit in LDS
+  size_t pf_lds = 0;
+  char* pf_pk = nullptr;
+  long long pf_pk_off[2 + 4 * S2FAST_SLOW_MAX_LAYERS] = {};
+  const char** pf_pkt = nullptr;
+  float* pf_x0w = nullptr;
+  float* pf_x = nullptr;
+  float* pf_xmid = nullptr;
+  float* pf_qkv = nullptr;
+  float* pf_att = nullptr;
+  float* pf_g = nullptr;
+  long long pf_x_slot = 0, pf_qkv_slot = 0, pf_att_slot = 0, pf_g_slot = 0;
+  int pf_ks[6] = {1, 1, 1, 1, 1, 1};
+  float* pf_kpart[6] = {};
+  long long pf_kslot[6] = {};
+  int* pf_kcnt[6] = {};
+  float* pf_kss[6] = {};
 };
 
 namespace {
@@ -34,9 +56,15 @@ namespace {
 void free_slow(s2fast_slow_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->layers, c->rope, c->x0, c->x, c->qkv, c->acc, c->g, c->po, c->pml, c->logits, c->sem,
-                  c->flags, c->err, c->tlog};
+                  c->flags, c->err, c->tlog, c->pf_pk, c->pf_pkt, c->pf_x0w, c->pf_x, c->pf_xmid, c->pf_qkv,
+                  c->pf_att, c->pf_g};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
+  for (int kd = 0; kd < 6; ++kd) {
+    void* kp[] = {c->pf_kpart[kd], c->pf_kcnt[kd], c->pf_kss[kd]};
+    for (void* p : kp)
+      if (p) (void)hipFree(p);
+  }
   delete c;
 }
 
@@ -184,6 +212,12 @@ int s2fast_test_slow_watchdog(s2fast_slow_ctx* ctx, int32_t give_up) {
 
 int s2fast_slow_allowed(const s2fast_slow_ctx* ctx) { return ctx ? ctx->n_allowed : -1; }
 
+int s2fast_test_slow_prefill_chunks(s2fast_slow_ctx* ctx, int32_t enable) {
+  if (!ctx) return S2FAST_ERR_ARG;
+  ctx->prefill_chunks = enable ? 1 : 0;
+  return S2FAST_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -237,6 +271,131 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
   return S2FAST_OK;
 }
 
+const void* prefill_fn(int dtype) {
+  return dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&prefill_kernel_b<uint16_t>)
+                              : reinterpret_cast<const void*>(&prefill_kernel_b<float>);
+}
+
+// First prefill: can this shape run prefill_kernel_b (the batched GEMM's
+// tile limits, the attention's LDS), and if so its packed weights, their
+// device table, the arena and the K splits (as the batched Fast-AR kernel
+// chooses them).  S2FAST_OK with pf_state -1 when the shape cannot.
+int prefill_setup(s2fast_slow_ctx* c) {
+  const s2fast_slow_config& k = c->cfg;
+  const int P = c->ncu, G = k.n_head_kv, gh = k.n_head / G, hd = k.head_dim;
+  const int qkv_dim = (k.n_head + 2 * G) * hd, attn_dim = k.n_head * hd;
+  c->pf_state = -1;
+  int tmax = 0;
+  for (int n : {qkv_dim, k.dim}) tmax = std::max(tmax, ((n + P - 1) / P + 15) / 16);
+  tmax = std::max(tmax, (2 * ((k.ffn_dim + P - 1) / P) + 15) / 16);
+  if (tmax > TMAX || 2 * tmax > RED_TILES) return S2FAST_OK;
+  c->pf_pmax = p_max_positions(gh, hd);
+  if (c->pf_pmax < 2) return S2FAST_OK;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) return S2FAST_ERR_HIP;
+  c->pf_lds = b_lds_bytes(1, hd, 0);
+  const void* fn = prefill_fn(k.weight_dtype);
+  int nb = 0;
+  if (c->pf_lds > (size_t)prop.sharedMemPerBlock ||
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c->pf_lds) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, NTHREADS, c->pf_lds) != hipSuccess || nb < 1)
+    return S2FAST_OK;
+  const int ksz = k.weight_dtype == S2FAST_BF16 ? 32 : 16;
+  const int ks = KS_DOWN;
+  const bool rows_fit = P % ks == 0 && (k.dim + P / ks - 1) / (P / ks) <= 16 * TMAX;
+  c->pf_ks[BK_DOWN] = (rows_fit && k.ffn_dim % (ks * ksz) == 0) ? ks : 1;
+  c->pf_ks[BK_WO] = (rows_fit && attn_dim % (ks * ksz) == 0) ? ks : 1;
+  constexpr int kq = 2;
+  c->pf_ks[BK_QKV] = (P % kq == 0 && (qkv_dim + P / kq - 1) / (P / kq) <= 16 * TMAX && k.dim % (kq * ksz) == 0)
+                         ? kq : 1;
+  auto rup = [](long long n, long long q) { return (n + q - 1) / q * q; };
+  const long long slots = k.n_layer;
+  c->pf_x_slot = rup((long long)BQ_MAX * k.dim, 64);
+  c->pf_qkv_slot = rup((long long)BQ_MAX * qkv_dim, 64);
+  c->pf_att_slot = rup((long long)BQ_MAX * attn_dim, 64);
+  c->pf_g_slot = rup((long long)BQ_MAX * k.ffn_dim, 64);
+  bool ok = dalloc(&c->pf_x0w, (size_t)c->pf_x_slot) == hipSuccess &&
+            dalloc(&c->pf_x, (size_t)(slots * c->pf_x_slot)) == hipSuccess &&
+            dalloc(&c->pf_xmid, (size_t)(slots * c->pf_x_slot)) == hipSuccess &&
+            dalloc(&c->pf_qkv, (size_t)(slots * c->pf_qkv_slot)) == hipSuccess &&
+            dalloc(&c->pf_att, (size_t)(slots * c->pf_att_slot)) == hipSuccess &&
+            dalloc(&c->pf_g, (size_t)(slots * c->pf_g_slot)) == hipSuccess &&
+            dalloc(&c->pf_pkt, (size_t)(2 + 4 * k.n_layer)) == hipSuccess;
+  if (!ok) return S2FAST_ERR_NOMEM;
+  c->pf_kslot[BK_QKV] = c->pf_qkv_slot;
+  c->pf_kslot[BK_WO] = c->pf_kslot[BK_DOWN] = c->pf_x_slot;
+  for (int kd : {(int)BK_QKV, (int)BK_WO, (int)BK_DOWN}) {
+    if (c->pf_ks[kd] == 1) continue;
+    ok = dalloc(&c->pf_kpart[kd], (size_t)(slots * c->pf_ks[kd] * c->pf_kslot[kd])) == hipSuccess &&
+         dalloc(&c->pf_kcnt[kd], (size_t)(slots * P * KCNT_STRIDE)) == hipSuccess &&
+         dalloc(&c->pf_kss[kd], (size_t)(slots * c->pf_ks[kd] * MP_MAX)) == hipSuccess;
+    if (!ok) return S2FAST_ERR_NOMEM;
+    if (hipMemset(c->pf_kcnt[kd], 0, (size_t)(slots * P * KCNT_STRIDE) * sizeof(int)) != hipSuccess)
+      return S2FAST_ERR_HIP;
+  }
+  std::vector<PackJob> jobs;
+  for (int l = 0; l < k.n_layer; ++l) {
+    const s2fast_layer_weights& L = c->w.layers[l];
+    jobs.push_back({pk_index(BK_QKV, l), L.wqkv, nullptr, qkv_dim, k.dim, c->pf_ks[BK_QKV]});
+    jobs.push_back({pk_index(BK_WO, l), L.wo, nullptr, k.dim, attn_dim, c->pf_ks[BK_WO]});
+    jobs.push_back({pk_index(BK_UP, l), L.w1, L.w3, k.ffn_dim, k.dim, 1});
+    jobs.push_back({pk_index(BK_DOWN, l), L.w2, nullptr, k.dim, k.ffn_dim, c->pf_ks[BK_DOWN]});
+  }
+  const int pst = pack_jobs(k.weight_dtype, P, jobs.data(), (int)jobs.size(), &c->pf_pk, c->pf_pk_off);
+  if (pst != S2FAST_OK) return pst;
+  std::vector<const char*> tbl(2 + 4 * k.n_layer, nullptr);
+  for (const PackJob& j : jobs) tbl[j.idx] = c->pf_pk + c->pf_pk_off[j.idx];
+  if (hipMemcpy(c->pf_pkt, tbl.data(), tbl.size() * sizeof(const char*), hipMemcpyHostToDevice) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess)
+    return S2FAST_ERR_HIP;
+  c->pf_state = 1;
+  return S2FAST_OK;
+}
+
+// One launch of prefill_kernel_b over positions n_past0 .. n_past0 + C - 1
+// (C <= BQ_MAX, their tokens [C][1 + num_codebooks]).
+int prefill_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int C, const int32_t* tokens,
+                   hipStream_t st) {
+  const s2fast_slow_config& k = ctx->cfg;
+  BatchArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.in_dim = k.dim; a.dim = k.dim; a.n_layer = k.n_layer; a.n_head = k.n_head; a.n_kv = k.n_head_kv;
+  a.hd = k.head_dim; a.ffn = k.ffn_dim; a.V = k.codebook_size; a.ncb = k.num_codebooks; a.ctx_len = 0;
+  a.eps = k.norm_eps; a.has_proj = 0; a.has_qkn = k.has_qk_norm ? 1 : 0;
+  a.qkv_dim = (k.n_head + 2 * k.n_head_kv) * k.head_dim;
+  a.attn_dim = k.n_head * k.head_dim;
+  a.gheads = k.n_head / k.n_head_kv;
+  a.gw = a.gheads * k.head_dim;
+  a.emb = ctx->w.embeddings; a.fnorm = ctx->w.norm;
+  a.rope = ctx->rope;
+  for (int kd = 0; kd < 6; ++kd) {
+    a.ks[kd] = ctx->pf_ks[kd]; a.kpart[kd] = ctx->pf_kpart[kd]; a.kslot[kd] = ctx->pf_kslot[kd];
+    a.kcnt[kd] = ctx->pf_kcnt[kd]; a.kss[kd] = ctx->pf_kss[kd];
+  }
+  a.Bq = C; a.nsteps = 1;
+  a.hidden = ctx->pf_x0w; a.xin0 = ctx->pf_x0w;
+  a.x = ctx->pf_x; a.xmid = ctx->pf_xmid; a.qkv = ctx->pf_qkv; a.att = ctx->pf_att; a.g = ctx->pf_g;
+  a.x_slot = ctx->pf_x_slot; a.qkv_slot = ctx->pf_qkv_slot; a.att_slot = ctx->pf_att_slot; a.g_slot = ctx->pf_g_slot;
+  a.flags = ctx->flags; a.err = ctx->err;
+  a.watch.give_up = ctx->give_up;
+  a.tlog = ctx->tlog_on ? ctx->tlog : nullptr;
+  a.prefill = 1; a.lds_layers = 1; a.Lt = ctx->layers; a.pkt = ctx->pf_pkt;
+  a.n_past0 = n_past0; a.max_ctx = k.max_context; a.cache = kv_cache; a.tokens = tokens; a.x0w = ctx->pf_x0w;
+  a.cemb = ctx->w.codebook_embeddings; a.cbs = k.codebook_size; a.sem_begin = k.semantic_begin;
+  a.vocab = k.vocab; a.sem_scale = (float)(1.0 / std::sqrt((double)(k.num_codebooks + 1)));
+  if (ctx->epoch > 0xF0000000u) {
+    if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
+    ctx->epoch = 0;
+  }
+  a.epoch0 = ctx->epoch;
+  void* args[] = {&a};
+  if (hipLaunchCooperativeKernel(prefill_fn(k.weight_dtype), dim3(ctx->ncu), dim3(NTHREADS), args, ctx->pf_lds,
+                                 st) != hipSuccess)
+    return S2FAST_ERR_HIP;
+  ctx->epoch += (u32)p_syncs(k.n_layer);
+  return S2FAST_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -268,15 +427,30 @@ int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, i
   if (T < 1 || n_past0 < 0 || (long long)n_past0 + T > k.max_context) return S2FAST_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(kv_cache) & 15u) || (reinterpret_cast<uintptr_t>(hidden_out) & 15u))
     return S2FAST_ERR_ARG;
-  // two positions a launch (one weight pass for both)
   const int row = 1 + k.num_codebooks;
-  for (int t = 0; t < T; t += MMAX) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (ctx->prefill_chunks && ctx->pf_state == 0) {
+    const int rc = prefill_setup(ctx);
+    if (rc != S2FAST_OK) return rc;
+  }
+  // the positions before the last in chunks of up to BQ_MAX a launch (one
+  // weight pass a chunk), while their attention scores fit in LDS
+  int t = 0;
+  if (ctx->prefill_chunks && ctx->pf_state == 1)
+    while (t < T - 1 && n_past0 + t + 1 <= ctx->pf_pmax) {
+      const int C = std::min(std::min(BQ_MAX, T - 1 - t), ctx->pf_pmax - (n_past0 + t));
+      const int rc = prefill_launch(ctx, kv_cache, n_past0 + t, C, tokens + (size_t)t * row, st);
+      if (rc != S2FAST_OK) return rc;
+      t += C;
+    }
+  // the rest two positions a launch (one weight pass for both), the last
+  // one with the head and the draw
+  for (; t < T; t += MMAX) {
     const int M = std::min(MMAX, T - t);
     const int32_t* tk = tokens + (size_t)t * row;
     const int32_t* tk1 = tk + (size_t)(M - 1) * row;
     const int rc = slow_launch(ctx, kv_cache, n_past0 + t, M, tk, tk + 1, tk1, tk1 + 1, t + M == T ? 1 : 0, window,
-                               u, temperature, top_p, top_k, main_out, sem_code_out, hidden_out, logits_out,
-                               reinterpret_cast<hipStream_t>(stream));
+                               u, temperature, top_p, top_k, main_out, sem_code_out, hidden_out, logits_out, st);
     if (rc != S2FAST_OK) return rc;
   }
   return S2FAST_OK;

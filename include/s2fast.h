@@ -371,13 +371,17 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
                      float* hidden_out, float* logits_out, void* stream);
 
 /* Prefill ("Overall architecture & Dual-AR data flow", sections 3.1 and 4):
- * the prompt's positions n_past0 .. n_past0 + T - 1 run through the step
- * above in order, two positions per launch (one pass over the weights for
- * both, the second attending to the first; an odd last position takes a
- * launch of its own; the pages' engine takes one token per chunk on CUDA),
- * writing their keys and values into the cache;
+ * the prompt's positions n_past0 .. n_past0 + T - 1 run through the layers
+ * of the step above causally, writing their keys and values into the cache;
  * the last position's logits give the first main token, drawn and checked
- * against the window exactly as s2fast_slow_step does.
+ * against the window exactly as s2fast_slow_step does.  The positions
+ * before the last run in chunks of up to 64 a launch on the matrix cores
+ * (one pass over the weights a chunk; each position attends to the cache
+ * up to itself), while the cache positions a chunk attends to fit the
+ * attention's on-chip score buffer (several thousand at the S2 Pro shape);
+ * the rest, and the last position with the head, run two positions a
+ * launch (one weight pass for both, the second attending to the first).
+ * The pages' engine takes one token per chunk on CUDA.
  *   tokens [T, 1 + num_codebooks] i32: per position the row-0 token (text,
  *          marker or semantic id), then the codebook codes; the codes count
  *          only where the row-0 token is a semantic id (the prompt's mask)
@@ -477,6 +481,11 @@ int s2fast_test_norm_rope_attn(int32_t n_head, int32_t n_head_kv, int32_t head_d
  * restores normal launches. */
 int s2fast_test_watchdog(s2fast_ctx* ctx, int32_t give_up);
 int s2fast_test_slow_watchdog(s2fast_slow_ctx* ctx, int32_t give_up);
+
+/* Chunked-prefill switch: enable = 0 makes later s2fast_slow_prefill calls
+ * on this context run every position two a launch (the comparison path);
+ * 1 (the default) restores the chunks. */
+int s2fast_test_slow_prefill_chunks(s2fast_slow_ctx* ctx, int32_t enable);
 
 /* Timeline instrumentation (blocking; for measurement only).  enable != 0
  * makes later launches on this context record, for every block and every

@@ -248,8 +248,11 @@ def step(model: SlowModel, x: np.ndarray, kv: np.ndarray, n_past: int,
             kv_new[i, :, 0] = cache_round(s, k)
             kv_new[i, :, 1] = cache_round(s, v)
         else:
-            kv_new[i, :, 0], f0 = follow_rounding(s, k, follow[i, :, 0])
-            kv_new[i, :, 1], f1 = follow_rounding(s, v, follow[i, :, 1])
+            try:
+                kv_new[i, :, 0], f0 = follow_rounding(s, k, follow[i, :, 0])
+                kv_new[i, :, 1], f1 = follow_rounding(s, v, follow[i, :, 1])
+            except CacheFollowError as e:
+                raise CacheFollowError(f"position {n_past}, layer {i}: {e}") from None
             flips += f0 + f1
         K = np.concatenate([kv[i, :, :n_past, 0], kv_new[i, :, None, 0]], axis=1)
         V = np.concatenate([kv[i, :, :n_past, 1], kv_new[i, :, None, 1]], axis=1)

@@ -221,6 +221,7 @@ def test_slow_null_arguments():
     assert lib.s2fast_slow_syncs(None) == -1 and lib.s2fast_slow_allowed(None) == -1
     assert lib.s2fast_test_slow_timeline(None, 1, None, 0) == 1
     assert lib.s2fast_slow_status(None, None) == 1 and lib.s2fast_test_slow_watchdog(None, 0) == 1
+    assert lib.s2fast_test_slow_prefill_chunks(None, 1) == 1
     lib.s2fast_slow_destroy(None)
 
 

@@ -70,3 +70,24 @@ def test_survey_bytes_of_the_int8_model():
     assert bench.survey_bytes_per_frame(si.TINY_Q8, 1) == 9 * per_step_tiny + io
     rows = 4 * (s.qkv_dim + 2 * s.dim + 2 * s.ffn_dim) + s.codebook_size   # wqkv, wo, w1, w3, w2, head
     assert bench.survey_bytes_per_frame(s, 1) == 7_455_375_360 // 2 + 9 * rows * 4 + 10_332
+
+
+def test_prefill_launch_split_and_bytes():
+    """The chunked prefill's launches: the positions before the last in
+    chunks of up to 64, then the last alone with the head; the comparison
+    path two a launch.  Bytes: every launch's weight pass, its cache reads
+    and writes and its input rows."""
+    assert bench.prefill_launches(1, True) == [(0, 1, True)]
+    assert bench.prefill_launches(256, True) == [(0, 64, False), (64, 64, False), (128, 64, False),
+                                                 (192, 63, False), (255, 1, True)]
+    assert bench.prefill_launches(5, False) == [(0, 2, False), (2, 2, False), (4, 1, True)]
+    s = ssi.SLOW_S2PRO
+    wb = 2
+    layer_names = [n for n in ssi.weight_names(s) if n.startswith("layers.")]
+    weights = _tensor_bytes(lambda n: ssi.weight_shape(s, n), layer_names, wb)
+    kv_pos = s.n_layer * s.n_head_kv * 2 * s.head_dim * wb
+    row = (1 + s.num_codebooks) * s.dim * wb
+    head = sa.allowed_ids(s).size * s.dim * wb + s.dim * wb + s.dim * 4
+    # 130 positions from 10: chunks at 10 (64), 74 (64), 138 (1), then 139
+    want = (4 * weights + kv_pos * ((10 + 64) + (74 + 64) + (138 + 1) + (139 + 1)) + 130 * row + head)
+    assert bench.prefill_bytes(s, 10, 130, True) == want

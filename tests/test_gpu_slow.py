@@ -383,6 +383,85 @@ def test_prefill_rejects_bad_arguments(slow_tiny):
         assert e.value.code == 1
 
 
+# Chunked prefill: the positions before the last run up to 64 a launch on
+# the matrix cores; these prompts take several chunks and a ragged last one.
+@pytest.mark.parametrize("n_past0,T,n_text", [(0, 80, 30), (5, 75, 0), (1, 66, 2)])
+def test_prefill_chunks_tiny(slow_tiny, n_past0, T, n_text):
+    _check_prefill(slow_tiny, n_past0, _prompt(slow_tiny.shape, T, 600 + T, n_text), [], [0.4, 0.6])
+
+
+def test_prefill_chunks_ragged(slow_ragged):
+    s = slow_ragged.shape
+    _check_prefill(slow_ragged, 100, _prompt(s, 150, 700, 20), [s.sem_begin + 3], [0.55, 0.45], T_=0.9, top_p=0.85)
+
+
+def test_prefill_chunks_mid(slow_mid):
+    _check_prefill(slow_mid, 3, _prompt(slow_mid.shape, 200, 800, 40), [], [0.7, 0.3])
+
+
+def test_prefill_chunks_off_matches(slow_mid):
+    """The comparison path (two positions a launch) still runs when the
+    chunks are switched off."""
+    slow_mid.gpu.prefill_chunks(False)
+    try:
+        _check_prefill(slow_mid, 10, _prompt(slow_mid.shape, 9, 900, 3), [], [0.2, 0.8])
+    finally:
+        slow_mid.gpu.prefill_chunks(True)
+
+
+def test_prefill_mid_long_crosses_score_buffer():
+    """A prompt across the cache position up to which a chunk's attention
+    scores fit on chip (7008 at 4 heads of 128 per group): the positions
+    below it run in one chunk, the rest two a launch."""
+    w = ssi.SLOW_WORKLOADS["slow_mid_long"]
+    p = SlowPair(w.shape, ssi.SLOW_WORKLOADS["slow_mid"].seed(0))
+    _check_prefill(p, 6990, _prompt(w.shape, 30, 1000, 5), [], [0.3, 0.7], seed=w.seed(3))
+    p.gpu.close()
+
+
+def _check_prefill_sampled(p, n_past0, toks, samples, u, T_=0.8, top_p=0.8, top_k=30, seed=55):
+    """A long prefill at full size, checked at sampled positions: the oracle
+    runs each sampled position's step over the cache the GPU wrote before it
+    (following its rounding) and checks the entries the GPU wrote there; the
+    last position's logits and hidden state the same way."""
+    s = p.shape
+    T = toks.shape[0]
+    kv_host, kv_f = _host_kv(s, n_past0, seed)
+    kv = _dev_kv(kv_host)
+    logits = torch.empty(p.gpu.n_allowed, dtype=torch.float32, device="cuda")
+    window = _window_dev([])
+    _announce(f"prefill {s.name} n_past0={n_past0} T={T}, sampled at {samples}")
+    m_out, _, h_out = p.gpu.prefill(kv, n_past0, torch.from_numpy(toks).cuda(), window, _f32(u), _f32([T_]),
+                                    _f32([top_p]), _i32([top_k]), logits_out=logits)
+    torch.cuda.synchronize()
+    kv_after = _kv_f32(kv)
+    keep = np.r_[0:n_past0, n_past0 + T:s.max_ctx]
+    assert np.array_equal(kv_after[:, :, keep], kv_f[:, :, keep], equal_nan=True)
+    assert np.isfinite(kv_after[:, :, n_past0:n_past0 + T]).all()
+    for t in sorted(set(samples) | {T - 1}):
+        pos = n_past0 + t
+        x = sa.combine(p.oracle, toks[t, 0], toks[t, 1:])
+        st = sa.step(p.oracle, x, kv_after, pos, follow=kv_after[:, :, pos])
+        _check_new_entries(s, kv_after[:, :, pos], st.kv_new)
+        _announce(f"  position {pos}: entries ok ({st.flips} rounding flips followed)")
+    ref = st.logits[sa.allowed_ids(s)]
+    got = logits.cpu().numpy()
+    assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max() + 1e-3
+    h = h_out.cpu().numpy()
+    assert np.abs(h - st.hidden).max() <= HIDDEN_RTOL * np.abs(st.hidden).max() + HIDDEN_ATOL
+    assert int(m_out.item()) in sa.draw_main(s, st.logits, [], T_, top_p, top_k, u[0], u[1]).alts
+
+
+@pytest.mark.timeout(900)
+def test_prefill_chunks_s2pro_full_size(slow_s2pro):
+    """130 prompt positions over the 2000 cached ones at the measured shape:
+    chunks of 64, 64 and 1, then the last position with the head; sampled
+    at each chunk's first and last position."""
+    w = ssi.SLOW_WORKLOADS["full_s2pro"]
+    _check_prefill_sampled(slow_s2pro, 2000, _prompt(w.shape, 130, 1100, 10), [0, 63, 64, 127, 128], [0.5, 0.5],
+                           seed=w.seed(10))
+
+
 @pytest.mark.timeout(600)
 def test_prefill_s2pro_full_size(slow_s2pro):
     """Three prompt positions (a text token, then two semantic positions)
