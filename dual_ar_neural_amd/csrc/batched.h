@@ -111,6 +111,13 @@ struct BatchArgs {
   const void* cemb;         // codebook embeddings [ncb * cbs][dim]
   int cbs, sem_begin, vocab;
   float sem_scale;
+  // the prefill attention on the matrix cores (bf16 caches): work items of
+  // pf_qpos positions of one KV group, the cache positions split pf_ps ways
+  // (partial results in pf_part, merged in a phase of their own when
+  // pf_ps > 1); pf_hdp = head_dim rounded up to whole 32-wide k-steps
+  int pf_qpos, pf_nb, pf_ps, pf_hdp;
+  float* pf_part;           // [n_kv][pf_nb][pf_ps][64][pf_hdp + 2]: output sums, max, sum
+  float* pf_q;              // [Bq][n_head * hd] query vectors after q RMSNorm and RoPE
 };
 
 struct BLds {

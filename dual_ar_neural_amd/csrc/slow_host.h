@@ -43,6 +43,8 @@ struct s2fast_slow_ctx {
   float* pf_qkv = nullptr;
   float* pf_att = nullptr;
   float* pf_g = nullptr;
+  float* pf_part = nullptr;  // the attention's split results (bf16 caches)
+  float* pf_q = nullptr;     // the chunk's query vectors (bf16 caches)
   long long pf_x_slot = 0, pf_qkv_slot = 0, pf_att_slot = 0, pf_g_slot = 0;
   int pf_ks[6] = {1, 1, 1, 1, 1, 1};
   float* pf_kpart[6] = {};
@@ -57,7 +59,7 @@ void free_slow(s2fast_slow_ctx* c) {
   if (!c) return;
   void* ptrs[] = {c->layers, c->rope, c->x0, c->x, c->qkv, c->acc, c->g, c->po, c->pml, c->logits, c->sem,
                   c->flags, c->err, c->tlog, c->pf_pk, c->pf_pkt, c->pf_x0w, c->pf_x, c->pf_xmid, c->pf_qkv,
-                  c->pf_att, c->pf_g};
+                  c->pf_att, c->pf_g, c->pf_part, c->pf_q};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   for (int kd = 0; kd < 6; ++kd) {
@@ -289,7 +291,9 @@ int prefill_setup(s2fast_slow_ctx* c) {
   for (int n : {qkv_dim, k.dim}) tmax = std::max(tmax, ((n + P - 1) / P + 15) / 16);
   tmax = std::max(tmax, (2 * ((k.ffn_dim + P - 1) / P) + 15) / 16);
   if (tmax > TMAX || 2 * tmax > RED_TILES) return S2FAST_OK;
-  c->pf_pmax = p_max_positions(gh, hd);
+  // bf16 caches: the attention streams the cache in tiles (no bound); f32:
+  // the scores of a position's attention are held in LDS
+  c->pf_pmax = k.weight_dtype == S2FAST_BF16 ? k.max_context : p_max_positions(gh, hd);
   if (c->pf_pmax < 2) return S2FAST_OK;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) return S2FAST_ERR_HIP;
@@ -322,6 +326,12 @@ int prefill_setup(s2fast_slow_ctx* c) {
             dalloc(&c->pf_g, (size_t)(slots * c->pf_g_slot)) == hipSuccess &&
             dalloc(&c->pf_pkt, (size_t)(2 + 4 * k.n_layer)) == hipSuccess;
   if (!ok) return S2FAST_ERR_NOMEM;
+  if (k.weight_dtype == S2FAST_BF16) {
+    const int hdp = (hd + 31) / 32 * 32, nbmax = (BQ_MAX + p_qpos(gh) - 1) / p_qpos(gh);
+    if (dalloc(&c->pf_part, (size_t)G * nbmax * PF_PSMAX * PF_NQ * (hdp + 2)) != hipSuccess ||
+        dalloc(&c->pf_q, (size_t)BQ_MAX * attn_dim) != hipSuccess)
+      return S2FAST_ERR_NOMEM;
+  }
   c->pf_kslot[BK_QKV] = c->pf_qkv_slot;
   c->pf_kslot[BK_WO] = c->pf_kslot[BK_DOWN] = c->pf_x_slot;
   for (int kd : {(int)BK_QKV, (int)BK_WO, (int)BK_DOWN}) {
@@ -383,6 +393,17 @@ int prefill_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int C,
   a.n_past0 = n_past0; a.max_ctx = k.max_context; a.cache = kv_cache; a.tokens = tokens; a.x0w = ctx->pf_x0w;
   a.cemb = ctx->w.codebook_embeddings; a.cbs = k.codebook_size; a.sem_begin = k.semantic_begin;
   a.vocab = k.vocab; a.sem_scale = (float)(1.0 / std::sqrt((double)(k.num_codebooks + 1)));
+  // attention work items (bf16): blocks of pf_qpos positions per KV group,
+  // their cache positions split so that the items fill the grid (each split
+  // at least one 64-position tile)
+  const int gh = k.n_head / k.n_head_kv;
+  a.pf_qpos = p_qpos(gh);
+  a.pf_nb = (C + a.pf_qpos - 1) / a.pf_qpos;
+  a.pf_hdp = (k.head_dim + 31) / 32 * 32;
+  const int tiles = (n_past0 + C + PF_TILE - 1) / PF_TILE;
+  a.pf_ps = std::max(1, std::min(std::min(PF_PSMAX, ctx->ncu / (k.n_head_kv * a.pf_nb)), tiles));
+  a.pf_part = ctx->pf_part; a.pf_q = ctx->pf_q;
+  const bool merge = k.weight_dtype == S2FAST_BF16 && a.pf_ps > 1;
   if (ctx->epoch > 0xF0000000u) {
     if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
     ctx->epoch = 0;
@@ -392,7 +413,7 @@ int prefill_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int C,
   if (hipLaunchCooperativeKernel(prefill_fn(k.weight_dtype), dim3(ctx->ncu), dim3(NTHREADS), args, ctx->pf_lds,
                                  st) != hipSuccess)
     return S2FAST_ERR_HIP;
-  ctx->epoch += (u32)p_syncs(k.n_layer);
+  ctx->epoch += (u32)p_syncs(k.n_layer, merge);
   return S2FAST_OK;
 }
 
