@@ -410,8 +410,9 @@ class SlowAR:
     def test_watchdog(self, give_up: bool) -> None:
         _check(library().s2fast_test_slow_watchdog(self._ctx, int(give_up)), "s2fast_test_slow_watchdog")
 
-    def prefill_chunks(self, enable: bool) -> None:
-        """Chunked prefill on (default) or off (two positions a launch)."""
+    def prefill_chunks(self, enable) -> None:
+        """Chunked prefill on (True, the default), off (False: two positions a
+        launch), or an int N > 1: chunks only below cache position N."""
         _check(library().s2fast_test_slow_prefill_chunks(self._ctx, int(enable)), "s2fast_test_slow_prefill_chunks")
 
     def timeline(self, enable: bool = True, fetch: bool = False):

@@ -31,6 +31,7 @@ struct s2fast_slow_ctx {
   // first s2fast_slow_prefill: packed weight streams, their device table and
   // an arena of n_layer slots of BQ_MAX position rows
   int prefill_chunks = 1;  // 0: every prefill runs two positions a launch (s2fast_test_slow_prefill_chunks)
+  int pf_limit = 0;        // > 0: chunks only below this cache position (the same test hook)
   int pf_state = 0;        // 0: not set up; 1: ready; -1: the shape prefills two positions a launch
   int pf_pmax = 0;         // cache positions whose attention scores fit in LDS
   size_t pf_lds = 0;
@@ -215,8 +216,9 @@ int s2fast_test_slow_watchdog(s2fast_slow_ctx* ctx, int32_t give_up) {
 int s2fast_slow_allowed(const s2fast_slow_ctx* ctx) { return ctx ? ctx->n_allowed : -1; }
 
 int s2fast_test_slow_prefill_chunks(s2fast_slow_ctx* ctx, int32_t enable) {
-  if (!ctx) return S2FAST_ERR_ARG;
+  if (!ctx || enable < 0) return S2FAST_ERR_ARG;
   ctx->prefill_chunks = enable ? 1 : 0;
+  ctx->pf_limit = enable > 1 ? enable : 0;
   return S2FAST_OK;
 }
 
@@ -457,9 +459,10 @@ int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, i
   // the positions before the last in chunks of up to BQ_MAX a launch (one
   // weight pass a chunk), while their attention scores fit in LDS
   int t = 0;
+  const int pmax = ctx->pf_limit > 0 ? std::min(ctx->pf_pmax, ctx->pf_limit) : ctx->pf_pmax;
   if (ctx->prefill_chunks && ctx->pf_state == 1)
-    while (t < T - 1 && n_past0 + t + 1 <= ctx->pf_pmax) {
-      const int C = std::min(std::min(BQ_MAX, T - 1 - t), ctx->pf_pmax - (n_past0 + t));
+    while (t < T - 1 && n_past0 + t + 1 <= pmax) {
+      const int C = std::min(std::min(BQ_MAX, T - 1 - t), pmax - (n_past0 + t));
       const int rc = prefill_launch(ctx, kv_cache, n_past0 + t, C, tokens + (size_t)t * row, st);
       if (rc != S2FAST_OK) return rc;
       t += C;

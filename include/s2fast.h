@@ -484,7 +484,10 @@ int s2fast_test_slow_watchdog(s2fast_slow_ctx* ctx, int32_t give_up);
 
 /* Chunked-prefill switch: enable = 0 makes later s2fast_slow_prefill calls
  * on this context run every position two a launch (the comparison path);
- * 1 (the default) restores the chunks. */
+ * 1 (the default) restores the chunks; enable = N > 1 keeps the chunks but
+ * only below cache position N, as if the f32 cache's on-chip score buffer
+ * ended there (the rest runs two positions a launch).  S2FAST_ERR_ARG for
+ * a NULL context or enable < 0. */
 int s2fast_test_slow_prefill_chunks(s2fast_slow_ctx* ctx, int32_t enable);
 
 /* Timeline instrumentation (blocking; for measurement only).  enable != 0

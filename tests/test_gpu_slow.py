@@ -409,14 +409,27 @@ def test_prefill_chunks_off_matches(slow_mid):
         slow_mid.gpu.prefill_chunks(True)
 
 
-def test_prefill_mid_long_crosses_score_buffer():
-    """A prompt across the cache position up to which a chunk's attention
-    scores fit on chip (7008 at 4 heads of 128 per group): the positions
-    below it run in one chunk, the rest two a launch."""
+def test_prefill_mid_long_context():
+    """A prompt at cache positions near 7000 of a 13000-position cache: the
+    attention splits each query block's cache positions over 16 workgroups
+    and merges their partial results."""
     w = ssi.SLOW_WORKLOADS["slow_mid_long"]
     p = SlowPair(w.shape, ssi.SLOW_WORKLOADS["slow_mid"].seed(0))
     _check_prefill(p, 6990, _prompt(w.shape, 30, 1000, 5), [], [0.3, 0.7], seed=w.seed(3))
     p.gpu.close()
+
+
+@pytest.mark.parametrize("which", ["tiny", "mid"])
+def test_prefill_chunk_limit(slow_tiny, slow_mid, which):
+    """Chunks only below a cache position (as where an f32 cache's on-chip
+    score buffer ends): the positions below it run chunked, the rest two a
+    launch, the last with the head."""
+    p = slow_tiny if which == "tiny" else slow_mid
+    p.gpu.prefill_chunks(40)
+    try:
+        _check_prefill(p, 5, _prompt(p.shape, 70, 1200, 10), [], [0.65, 0.35])
+    finally:
+        p.gpu.prefill_chunks(True)
 
 
 def _check_prefill_sampled(p, n_past0, toks, samples, u, T_=0.8, top_p=0.8, top_k=30, seed=55):
