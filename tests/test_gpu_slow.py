@@ -409,6 +409,29 @@ def test_prefill_chunks_off_matches(slow_mid):
         slow_mid.gpu.prefill_chunks(True)
 
 
+def test_prefill_device_failure_is_reported_and_recovered(slow_mid):
+    """Every launch's first grid-wide wait made to give up (the test hook),
+    through a chunked prefill: every block leaves normally, the status
+    reports the failure once, no token is drawn; then the same context
+    prefills correctly (the K-split counts were restored)."""
+    s = slow_mid.shape
+    kv_host, _ = _host_kv(s, 20, 61)
+    kv = _dev_kv(kv_host)
+    main_out = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    window = _window_dev([])
+    slow_mid.gpu.test_watchdog(True)
+    try:
+        slow_mid.gpu.prefill(kv, 20, torch.from_numpy(_prompt(s, 70, 1300, 10)).cuda(), window, _f32([0.5, 0.5]),
+                             _f32([0.8]), _f32([0.8]), _i32([30]), main_out=main_out)
+        torch.cuda.synchronize()
+    finally:
+        slow_mid.gpu.test_watchdog(False)
+    assert slow_mid.gpu.status() == 6 and slow_mid.gpu.status() == 0
+    assert int(main_out.item()) == -7 and int(window[0].item()) == 0
+    _check_prefill(slow_mid, 20, _prompt(s, 70, 1300, 10), [], [0.5, 0.5])
+    assert slow_mid.gpu.status() == 0
+
+
 def test_prefill_mid_long_context():
     """A prompt at cache positions near 7000 of a 13000-position cache: the
     attention splits each query block's cache positions over 16 workgroups
