@@ -92,6 +92,17 @@ def slow_step_bytes(shape, n_past: int, head: bool = True, M: int = 1) -> int:
     return s.n_layer * per_layer + kv + head_b + inputs
 
 
+def prefill_traffic():
+    """HBM bytes per chunked-prefill launch (mean over the profiled chunks)
+    from the committed counter summary, if it was taken on the current
+    kernel code (else None)."""
+    csrc = os.path.join(ROOT, "dual_ar_neural_amd", "csrc")
+    rec = traffic_from_profile(os.path.join(ROOT, "profiles", "prefill_kernel_b_s2pro_prefill_hbm_traffic.md"),
+                               [os.path.join(csrc, f) for f in ("s2fast.hip", "batched.h", "prefill.h", "slow_host.h",
+                                                                "device_common.h")])
+    return rec["hbm_bytes_per_launch"] if rec else None
+
+
 def prefill_launches(T: int, chunks: bool, chunk: int = 64):
     """(first position offset, positions, head) of each launch the library
     makes for a T-position prefill whose cache positions all fit the chunked
@@ -269,6 +280,7 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
                                   "then the last position with the head and the first main-token draw",
                       "positions": P, "positions_per_s": round(P / psec, 1), "ms": round(psec * 1e3, 2),
                       "launches": len(prefill_launches(P, True)),
+                      "chunk_traffic": prefill_traffic(),
                       "bytes": int(pb), "hbm_gbs": round(pb / psec / 1e9, 1),
                       "frac": round(pb / psec / 1e9 / PEAK_HBM_GBS, 4),
                       "two_per_launch": {"positions_per_s": round(P / psec2, 1), "ms": round(psec2 * 1e3, 2),
