@@ -452,7 +452,7 @@ int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, i
     return S2FAST_ERR_ARG;
   const int row = 1 + k.num_codebooks;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (ctx->prefill_chunks && ctx->pf_state == 0) {
+  if (ctx->prefill_chunks && ctx->pf_state == 0 && T > 1) {
     const int rc = prefill_setup(ctx);
     if (rc != S2FAST_OK) return rc;
   }

@@ -385,9 +385,15 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
  *   tokens [T, 1 + num_codebooks] i32: per position the row-0 token (text,
  *          marker or semantic id), then the codebook codes; the codes count
  *          only where the row-0 token is a semantic id (the prompt's mask)
- * Other arguments as s2fast_slow_step.  Errors: S2FAST_ERR_ARG for NULL
- * pointers (other than logits_out), misaligned kv_cache / hidden_out, T < 1
- * or positions outside [0, max_context). */
+ * Other arguments as s2fast_slow_step.  The first call on a context that
+ * runs chunks sets them up: it packs a second copy of the layer matrices
+ * for the matrix cores (7.3 GB at the S2 Pro shape) and allocates their
+ * arena, synchronising the device; later calls only enqueue.  Errors:
+ * S2FAST_ERR_ARG for NULL pointers (other than logits_out), misaligned
+ * kv_cache / hidden_out, T < 1 or positions outside [0, max_context);
+ * S2FAST_ERR_NOMEM / S2FAST_ERR_HIP if that set-up fails (nothing is
+ * enqueued, and later calls run two positions a launch).  Shapes the chunk
+ * kernel cannot take run two positions a launch without a set-up. */
 int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int32_t T, const int32_t* tokens,
                         int32_t* window, const float* u, const float* temperature, const float* top_p,
                         const int32_t* top_k, int32_t* main_out, int32_t* sem_code_out, float* hidden_out,
