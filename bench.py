@@ -165,7 +165,7 @@ def full_frame_cpu(host_slow, kvh, fast_host, fast_shape, inp, n_fill, frames: i
     threads = os.environ.get("OMP_NUM_THREADS")
     if threads and threads.isdigit():
         cores = min(cores, int(threads))
-    return {"value": round(frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
+    return {"value": round(frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle", **host_description(),
             "sample": f"{frames} chained full frames from position {n_fill + 1} after one warm-up frame, "
                       f"{dt:.1f} s wall clock"}
 
@@ -322,11 +322,16 @@ def probe_hbm(torch, bd):
             f"non-temporal loads in flight a thread, 2 GiB read"}
 
 
-def time_frames(torch, ctx, dev_in, B, frames, warmup):
-    """Decode `warmup` then `frames` frames on the current stream.  Returns
-    (seconds over the timed region, mean seconds per decode call): every call
-    is bracketed by its own pair of HIP events on that stream, so the second
-    figure excludes the host's gaps between launches."""
+RUNS = 5   # timed runs of each line; the line reports the median run
+
+
+def time_frames(torch, ctx, dev_in, B, frames, warmup, runs=1):
+    """Decode `warmup` then `frames` frames on the current stream, `runs`
+    times (the warm-up only before the first).  Returns (seconds over the
+    timed region, mean seconds per decode call) of the median run, and the
+    list of every run's (seconds, per call): every call is bracketed by its
+    own pair of HIP events on that stream, so the second figure excludes the
+    host's gaps between launches."""
     hidden, sem, uni, temp, tp, tk, out = dev_in
     F = hidden.shape[0]
     for i in range(warmup):
@@ -334,15 +339,20 @@ def time_frames(torch, ctx, dev_in, B, frames, warmup):
         ctx.decode_frame(hidden[f], sem[f], uni[f], temp, tp, tk, codes=out[f])
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(frames)]
-    for i in range(frames):
-        f = i % F
-        ev[i][0].record(stream)
-        ctx.decode_frame(hidden[f], sem[f], uni[f], temp, tp, tk, codes=out[f], stream=stream)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    total = ev[0][0].elapsed_time(ev[-1][1]) / 1e3
-    per_call = sum(a.elapsed_time(b) for a, b in ev) / 1e3 / frames
+    res = []
+    for _ in range(runs):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(frames)]
+        torch.cuda.synchronize()
+        for i in range(frames):
+            f = i % F
+            ev[i][0].record(stream)
+            ctx.decode_frame(hidden[f], sem[f], uni[f], temp, tp, tk, codes=out[f], stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        res.append((ev[0][0].elapsed_time(ev[-1][1]) / 1e3, sum(a.elapsed_time(b) for a, b in ev) / 1e3 / frames))
+    total, per_call = sorted(res)[len(res) // 2]
+    if runs > 1:
+        return total, per_call, res
     return total, per_call
 
 
@@ -386,6 +396,25 @@ def traffic_from_profile(path: str, source_files) -> dict | None:
     return rec
 
 
+def host_description() -> dict:
+    """The host the oracle runs on: CPU model and numpy's BLAS."""
+    out = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    out["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        out["blas"] = f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:
+        pass
+    return out
+
+
 def oracle_leg(workload, frames: int, host_weights, gpu_codes, gpu_logits, batched=()):
     """The oracle on this host: the literal-recompute float32 numpy decoder
     as it stands, BLAS on every core the process may use.  It decodes the
@@ -416,6 +445,7 @@ def oracle_leg(workload, frames: int, host_weights, gpu_codes, gpu_logits, batch
     if threads and threads.isdigit():
         cores = min(cores, int(threads))
     base = {"value": round(w.batch * frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
+            **host_description(),
             "sample": f"{frames} frames of {w.name} (batch {w.batch}) after one warm-up frame, teacher-forced "
                       f"along the GPU's codes, {dt:.1f} s wall clock"}
 
@@ -497,7 +527,7 @@ def main():
     print("[bench] streaming-read probe", file=sys.stderr, flush=True)
     probe = probe_hbm(torch, bd)
     print(f"[bench] timing {args.steps} frames at batch 1", file=sys.stderr, flush=True)
-    secs, kern_s = time_frames(torch, ctx, dev_in, 1, args.steps, args.warmup)
+    secs, kern_s, runs = time_frames(torch, ctx, dev_in, 1, args.steps, args.warmup, runs=RUNS)
     B = 1
     frames_per_s = B * args.steps / secs
     ms = secs * 1e3 / args.steps
@@ -534,6 +564,9 @@ def main():
                      "path_frac": round(path_bytes / kern_s / 1e9 / PEAK_HBM_GBS, 4),
                      **probe, "frac_of_probe": round(achieved / probe["probe_gbs"], 4)},
         "syncs_per_frame": ctx.syncs_per_frame(1),
+        "timing": f"median of {RUNS} timed runs of {args.steps} frames each (one warm-up of {args.warmup} frames "
+                  "before the first); every run's frames/s in runs_frames_per_s",
+        "runs_frames_per_s": [round(args.steps / t, 2) for t, _ in runs],
     }
     n_chk = 0 if args.no_cpu_baseline else min(args.cpu_frames + 1, dev_in[0].shape[0])
     if n_chk:
@@ -562,13 +595,14 @@ def main():
             frs = si.make_frames(ws, n_frames=nf)
             di = upload(torch, frs)
             print(f"[bench] timing {nf} frames at batch {Bs}", file=sys.stderr, flush=True)
-            sec, per_call = time_frames(torch, cs, di, Bs, nf, 2)
+            sec, per_call, rs = time_frames(torch, cs, di, Bs, nf, 2, runs=RUNS)
             fb = survey_bytes_per_frame(ws.shape, Bs)
             sweep[f"b{Bs}"] = {"frames_per_s": round(Bs * nf / sec, 2), "ms_per_frame": round(sec * 1e3 / nf, 3),
                                "hbm_gbs": round(fb * nf / sec / 1e9, 1),
                                "frac": round(fb * nf / sec / 1e9 / PEAK_HBM_GBS, 4), "frames": nf,
                                "bytes_per_frame": fb, "kernel_ms_per_frame": round(per_call * 1e3, 3),
-                               "launches_per_frame": (Bs + 63) // 64, "workload": ws.name}
+                               "launches_per_frame": (Bs + 63) // 64, "workload": ws.name,
+                               "runs_frames_per_s": [round(Bs * nf / t, 2) for t, _ in rs]}
             if n_chk:
                 c0 = di[6][0].cpu().numpy()
                 l0 = cs.forward_logits(di[0][0], di[6][0]).cpu().numpy()
