@@ -390,6 +390,16 @@ def test_prefill_chunks_tiny(slow_tiny, n_past0, T, n_text):
     _check_prefill(slow_tiny, n_past0, _prompt(slow_tiny.shape, T, 600 + T, n_text), [], [0.4, 0.6])
 
 
+@pytest.mark.parametrize("which,n_past0,T", [("tiny", 0, 2), ("mid", 0, 2), ("mid", 635, 65), ("ragged", 233, 67)])
+def test_prefill_chunk_edges(slow_tiny, slow_mid, slow_ragged, which, n_past0, T):
+    """A chunk of one position (T = 2), and prompts whose last position is
+    the cache's last (a full chunk of 64 ending there; 66 positions in two
+    chunks at the ragged shape)."""
+    p = {"tiny": slow_tiny, "mid": slow_mid, "ragged": slow_ragged}[which]
+    assert n_past0 + T <= p.shape.max_ctx
+    _check_prefill(p, n_past0, _prompt(p.shape, T, 1400 + T, min(T, 3)), [], [0.45, 0.55])
+
+
 def test_prefill_chunks_ragged(slow_ragged):
     s = slow_ragged.shape
     _check_prefill(slow_ragged, 100, _prompt(s, 150, 700, 20), [s.sem_begin + 3], [0.55, 0.45], T_=0.9, top_p=0.85)
