@@ -104,28 +104,51 @@ def prefill_traffic():
 
 
 def prefill_launches(T: int, chunks: bool, chunk: int = 64):
-    """(first position offset, positions, head) of each launch the library
+    """(first position offset, positions, kind) of each launch the library
     makes for a T-position prefill whose cache positions all fit the chunked
-    attention's score buffer: the positions before the last in chunks of up
-    to `chunk`, then the last alone with the head; with chunks off, two
-    positions a launch, the last launch with the head."""
+    attention: kind "chunk" (the chunk kernel), "step" (the step kernel:
+    layers, head and draw) or "head" (a head-only step launch).  With chunks
+    on, the whole prompt runs in chunks of up to `chunk`, the last chunk
+    holding the last position, then a head-only launch; when that chunk
+    would hold the last position alone ((T - 1) a multiple of `chunk`), the
+    positions before the last run in chunks and the last as a step.  With
+    chunks off, two positions a launch, the last launch with the head."""
     out, t = [], 0
+    if chunks and T >= 2 and (T - 1) % chunk != 0:
+        while t < T:
+            c = min(chunk, T - t)
+            out.append((t, c, "chunk"))
+            t += c
+        return out + [(T - 1, 1, "head")]
     if chunks:
         while t < T - 1:
             c = min(chunk, T - 1 - t)
-            out.append((t, c, False))
+            out.append((t, c, "chunk"))
             t += c
     while t < T:
         m = min(2, T - t)
-        out.append((t, m, t + m == T))
+        out.append((t, m, "step"))
         t += m
     return out
 
 
+def head_only_bytes(shape) -> int:
+    """A head-only step launch: the open head rows, the final norm, the
+    hidden state written and the last layer's output row read."""
+    return slow_step_bytes(shape, 0, head=True, M=1) - slow_step_bytes(shape, 0, head=False, M=1) + shape.dim * 4
+
+
 def prefill_bytes(shape, n_past0: int, T: int, chunks: bool) -> int:
-    """Minimum bytes of a prefill as the library splits it into launches
-    (slow_step_bytes of each launch)."""
-    return sum(slow_step_bytes(shape, n_past0 + t, head=h, M=m) for t, m, h in prefill_launches(T, chunks))
+    """Minimum bytes of a prefill as the library splits it into launches:
+    slow_step_bytes of each chunk or step launch (chunks without the head),
+    head_only_bytes of a head-only launch."""
+    total = 0
+    for t, m, kind in prefill_launches(T, chunks):
+        if kind == "head":
+            total += head_only_bytes(shape)
+        else:
+            total += slow_step_bytes(shape, n_past0 + t, head=(kind == "step" and t + m == T), M=m)
+    return total
 
 
 def slow_traffic():
@@ -276,8 +299,9 @@ def full_frame_bench(torch, bd, fast_ctx, fast_shape, frames: int, warmup: int, 
     pb2 = prefill_bytes(s, 0, P, False)
     out["prefill"] = {"workload": f"S2 Pro-shaped Slow-AR prefill of {P} prompt positions ({n_text} text tokens, "
                                   f"{P - n_text} reference-audio positions with codes) from an empty cache: the "
-                                  "positions before the last in chunks of up to 64 a launch on the matrix cores, "
-                                  "then the last position with the head and the first main-token draw",
+                                  "prompt in chunks of up to 64 positions a launch on the matrix cores (the last "
+                                  "chunk runs the last layer in full for the last position), then a head-only "
+                                  "launch with the first main-token draw",
                       "positions": P, "positions_per_s": round(P / psec, 1), "ms": round(psec * 1e3, 2),
                       "launches": len(prefill_launches(P, True)),
                       "chunk_traffic": prefill_traffic(),

@@ -118,6 +118,7 @@ struct BatchArgs {
   int pf_qpos, pf_nb, pf_ps, pf_hdp;
   float* pf_part;           // [n_kv][pf_nb][pf_ps][64][pf_hdp + 2]: output sums, max, sum
   float* pf_q;              // [Bq][n_head * hd] query vectors after q RMSNorm and RoPE
+  int pf_full_last;         // the chunk holds the prompt's last position: the last layer runs in full
 };
 
 struct BLds {

@@ -16,16 +16,22 @@
 //   the cache) | ATTN (one workgroup per position and KV group) | WO | UP |
 //   DOWN (batched GEMMs)
 // The last layer stops after KV: its attention and FFN feed only the head,
-// which a prefill position does not have.  The prompt's last position, with
-// the head and the draw, is a Slow-AR step of its own.
+// which a prefill position does not have.  When the chunk holds the
+// prompt's last position as its last row (pf_full_last), the last layer
+// runs in full and that row's output is left in the arena for a head-only
+// Slow-AR launch (the masked head and the draw); otherwise the prompt's
+// last position is a Slow-AR step of its own.
 // The GEMMs split X into three bf16 pieces (float32-level products): with
 // two, the residual stream's error after 36 layers moved keys beyond the
 // bf16 rounding band of the float32 step.
 
 // grid syncs of one prefill launch (no sync after the last layer's KV
-// phase; `merge`: the attention's split results are merged in a phase of
-// their own)
-__host__ __device__ inline int p_syncs(int n_layer, bool merge) { return 1 + (merge ? 7 : 6) * (n_layer - 1) + 1; }
+// phase unless the last layer runs in full; `merge`: the attention's split
+// results are merged in a phase of their own)
+__host__ __device__ inline int p_syncs(int n_layer, bool merge, bool full_last) {
+  const int per = merge ? 7 : 6;
+  return 1 + per * (n_layer - 1) + (full_last ? per : 1);
+}
 
 constexpr int PF_NQ = 64;       // query vectors of one attention work item (four 16-wide MFMA tiles)
 constexpr int PF_TILE = 64;     // cache positions a workgroup stages per iteration
@@ -576,7 +582,7 @@ __device__ __forceinline__ bool p_run(const BatchArgs& a, const BLds& s) {
     if (!grid_sync(a, epoch, s.flag)) return false;
     if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     p_kv<WT>(a, s, l);
-    if (l == a.n_layer - 1) break;   // the last layer's output feeds only the head
+    if (l == a.n_layer - 1 && !a.pf_full_last) break;   // the last layer's output feeds only the head
     if (!grid_sync(a, epoch, s.flag)) return false;
     if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
     if constexpr (sizeof(WT) == 2) {

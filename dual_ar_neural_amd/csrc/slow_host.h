@@ -228,11 +228,14 @@ namespace {
 
 // Arguments are already validated; do_head = 0 stops after the last layer.
 // One launch of the Slow-AR step kernel at positions n_past .. n_past + M - 1
-// (M <= MMAX; the second position's tokens are main1 / codes1).
+// (M <= MMAX; the second position's tokens are main1 / codes1).  x_head
+// (device, not null): a head-only launch whose head reads that row as the
+// last layer's output (M = 1, do_head = 1).
 int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, const int32_t* prev_main,
                 const int32_t* prev_codes, const int32_t* main1, const int32_t* codes1, int do_head, int32_t* window,
                 const float* u, const float* temperature, const float* top_p, const int32_t* top_k,
-                int32_t* main_out, int32_t* sem_code_out, float* hidden_out, float* logits_out, hipStream_t st) {
+                int32_t* main_out, int32_t* sem_code_out, float* hidden_out, float* logits_out, hipStream_t st,
+                const float* x_head = nullptr) {
   const s2fast_slow_config& k = ctx->cfg;
   SlowArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -262,6 +265,7 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
   a.po_slot = ctx->po_slot; a.pml_slot = ctx->pml_slot;
   a.flags = ctx->flags; a.err = ctx->err; a.tlog = ctx->tlog_on ? ctx->tlog : nullptr;
   a.watch.give_up = ctx->give_up;
+  a.x_head = x_head;
   if (ctx->epoch > 0xF0000000u) {
     if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
     ctx->epoch = 0;
@@ -271,7 +275,7 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
   if (hipLaunchCooperativeKernel(slow_kernel_fn(k.weight_dtype, M), dim3(ctx->ncu), dim3(NTHREADS), args,
                                  ctx->lds_bytes, st) != hipSuccess)
     return S2FAST_ERR_HIP;
-  ctx->epoch += (u32)(5 * k.n_layer + (do_head ? 1 : 0));
+  ctx->epoch += (u32)(x_head ? 1 : 5 * k.n_layer + (do_head ? 1 : 0));
   return S2FAST_OK;
 }
 
@@ -365,9 +369,10 @@ int prefill_setup(s2fast_slow_ctx* c) {
 }
 
 // One launch of prefill_kernel_b over positions n_past0 .. n_past0 + C - 1
-// (C <= BQ_MAX, their tokens [C][1 + num_codebooks]).
+// (C <= BQ_MAX, their tokens [C][1 + num_codebooks]); full_last: the last
+// of them is the prompt's last position (the last layer runs in full).
 int prefill_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int C, const int32_t* tokens,
-                   hipStream_t st) {
+                   hipStream_t st, bool full_last) {
   const s2fast_slow_config& k = ctx->cfg;
   BatchArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -405,6 +410,7 @@ int prefill_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int C,
   const int tiles = (n_past0 + C + PF_TILE - 1) / PF_TILE;
   a.pf_ps = std::max(1, std::min(std::min(PF_PSMAX, ctx->ncu / (k.n_head_kv * a.pf_nb)), tiles));
   a.pf_part = ctx->pf_part; a.pf_q = ctx->pf_q;
+  a.pf_full_last = full_last ? 1 : 0;
   const bool merge = k.weight_dtype == S2FAST_BF16 && a.pf_ps > 1;
   if (ctx->epoch > 0xF0000000u) {
     if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
@@ -415,7 +421,7 @@ int prefill_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int C,
   if (hipLaunchCooperativeKernel(prefill_fn(k.weight_dtype), dim3(ctx->ncu), dim3(NTHREADS), args, ctx->pf_lds,
                                  st) != hipSuccess)
     return S2FAST_ERR_HIP;
-  ctx->epoch += (u32)p_syncs(k.n_layer, merge);
+  ctx->epoch += (u32)p_syncs(k.n_layer, merge, full_last);
   return S2FAST_OK;
 }
 
@@ -456,14 +462,32 @@ int s2fast_slow_prefill(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, i
     const int rc = prefill_setup(ctx);
     if (rc != S2FAST_OK) return rc;
   }
-  // the positions before the last in chunks of up to BQ_MAX a launch (one
-  // weight pass a chunk), while their attention scores fit in LDS
   int t = 0;
   const int pmax = ctx->pf_limit > 0 ? std::min(ctx->pf_pmax, ctx->pf_limit) : ctx->pf_pmax;
-  if (ctx->prefill_chunks && ctx->pf_state == 1)
+  const bool chunks = ctx->prefill_chunks && ctx->pf_state == 1;
+  // the whole prompt in chunks of up to BQ_MAX, the last chunk holding the
+  // last position, then a head-only launch for the head and the draw: when
+  // every position's attention fits and the last chunk would hold more
+  // than the last position alone (else that position costs a chunk's weight
+  // pass; the step launch below is cheaper)
+  if (chunks && T >= 2 && (long long)n_past0 + T <= pmax && (T - 1) % BQ_MAX != 0) {
+    int C = 0;
+    for (; t < T; t += C) {
+      C = std::min(BQ_MAX, T - t);
+      const int rc = prefill_launch(ctx, kv_cache, n_past0 + t, C, tokens + (size_t)t * row, st, t + C == T);
+      if (rc != S2FAST_OK) return rc;
+    }
+    const float* xh = ctx->pf_x + (size_t)(k.n_layer - 1) * ctx->pf_x_slot + (size_t)(C - 1) * k.dim;
+    const int32_t* tk = tokens + (size_t)(T - 1) * row;
+    return slow_launch(ctx, kv_cache, n_past0 + T - 1, 1, tk, tk + 1, nullptr, nullptr, 1, window, u, temperature,
+                       top_p, top_k, main_out, sem_code_out, hidden_out, logits_out, st, xh);
+  }
+  // the positions before the last in chunks of up to BQ_MAX a launch (one
+  // weight pass a chunk), while their attention fits
+  if (chunks)
     while (t < T - 1 && n_past0 + t + 1 <= pmax) {
       const int C = std::min(std::min(BQ_MAX, T - 1 - t), pmax - (n_past0 + t));
-      const int rc = prefill_launch(ctx, kv_cache, n_past0 + t, C, tokens + (size_t)t * row, st);
+      const int rc = prefill_launch(ctx, kv_cache, n_past0 + t, C, tokens + (size_t)t * row, st, false);
       if (rc != S2FAST_OK) return rc;
       t += C;
     }

@@ -84,6 +84,9 @@ struct SlowArgs {
   Watch watch;
   u32* tlog;
   u32 tlog_epoch;
+  // head-only launch (not null): the layers are skipped and the head reads
+  // this row as the last layer's output (a chunked prefill wrote it)
+  const float* x_head;
 };
 
 struct SlowLds {
@@ -128,6 +131,7 @@ __device__ inline SlowLds slow_carve(float* base, const SlowArgs& a) {
 }
 
 __device__ __forceinline__ const float* slow_lin(const SlowArgs& a, int l) {
+  if (a.x_head && l == a.n_layer) return a.x_head;
   return l == 0 ? a.x0 : a.x + (size_t)(l - 1) * a.x_slot;
 }
 
@@ -852,9 +856,11 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
   const int nph = 5 * a.n_layer + (a.do_head ? 1 : 0);
   // A phase's plan (plain integers) is computed before the barrier that
   // precedes the phase.
-  Plan pl = slow_plan<WT>(a, 0, SP_QKV);
+  // a head-only launch starts at the head phase
+  const int ph0 = a.x_head ? 5 * a.n_layer : 0;
+  Plan pl = a.x_head ? slow_plan<WT>(a, a.n_layer - 1, SP_HEAD) : slow_plan<WT>(a, 0, SP_QKV);
   bool ok = true;
-  for (int ph = 0; ph < nph; ++ph) {
+  for (int ph = ph0; ph < nph; ++ph) {
     const int l = ph / 5;
     const int kind = ph < 5 * a.n_layer ? ph - 5 * l : (int)SP_HEAD;
     if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);

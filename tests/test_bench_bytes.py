@@ -73,14 +73,18 @@ def test_survey_bytes_of_the_int8_model():
 
 
 def test_prefill_launch_split_and_bytes():
-    """The chunked prefill's launches: the positions before the last in
-    chunks of up to 64, then the last alone with the head; the comparison
-    path two a launch.  Bytes: every launch's weight pass, its cache reads
-    and writes and its input rows."""
-    assert bench.prefill_launches(1, True) == [(0, 1, True)]
-    assert bench.prefill_launches(256, True) == [(0, 64, False), (64, 64, False), (128, 64, False),
-                                                 (192, 63, False), (255, 1, True)]
-    assert bench.prefill_launches(5, False) == [(0, 2, False), (2, 2, False), (4, 1, True)]
+    """The chunked prefill's launches: the whole prompt in chunks of up to
+    64 and a head-only launch, unless the last chunk would hold the last
+    position alone (then the positions before it in chunks and the last as
+    a step); the comparison path two a launch.  Bytes: every launch's weight
+    pass, its cache reads and writes and its input rows; a head-only launch
+    its head rows, the final norm and two rows of the state."""
+    assert bench.prefill_launches(1, True) == [(0, 1, "step")]
+    assert bench.prefill_launches(2, True) == [(0, 2, "chunk"), (1, 1, "head")]
+    assert bench.prefill_launches(256, True) == [(0, 64, "chunk"), (64, 64, "chunk"), (128, 64, "chunk"),
+                                                 (192, 64, "chunk"), (255, 1, "head")]
+    assert bench.prefill_launches(65, True) == [(0, 64, "chunk"), (64, 1, "step")]
+    assert bench.prefill_launches(5, False) == [(0, 2, "step"), (2, 2, "step"), (4, 1, "step")]
     s = ssi.SLOW_S2PRO
     wb = 2
     layer_names = [n for n in ssi.weight_names(s) if n.startswith("layers.")]
@@ -88,6 +92,10 @@ def test_prefill_launch_split_and_bytes():
     kv_pos = s.n_layer * s.n_head_kv * 2 * s.head_dim * wb
     row = (1 + s.num_codebooks) * s.dim * wb
     head = sa.allowed_ids(s).size * s.dim * wb + s.dim * wb + s.dim * 4
-    # 130 positions from 10: chunks at 10 (64), 74 (64), 138 (1), then 139
-    want = (4 * weights + kv_pos * ((10 + 64) + (74 + 64) + (138 + 1) + (139 + 1)) + 130 * row + head)
+    assert bench.head_only_bytes(s) == head + s.dim * 4
+    # 130 positions from 10: chunks at 10 (64), 74 (64), 138 (2), then the head
+    want = (3 * weights + kv_pos * ((10 + 64) + (74 + 64) + (138 + 2)) + 130 * row + head + s.dim * 4)
     assert bench.prefill_bytes(s, 10, 130, True) == want
+    # 129 positions from 0: chunks at 0 (64), 64 (64), then position 128 as a step
+    want = (3 * weights + kv_pos * (64 + 128 + 129) + 129 * row + head)
+    assert bench.prefill_bytes(s, 0, 129, True) == want
