@@ -374,14 +374,16 @@ int s2fast_slow_step(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, const
  * the prompt's positions n_past0 .. n_past0 + T - 1 run through the layers
  * of the step above causally, writing their keys and values into the cache;
  * the last position's logits give the first main token, drawn and checked
- * against the window exactly as s2fast_slow_step does.  The positions
- * before the last run in chunks of up to 64 a launch on the matrix cores
- * (one pass over the weights a chunk; each position attends to the cache
- * up to itself), while the cache positions a chunk attends to fit the
- * attention's on-chip score buffer (several thousand at the S2 Pro shape);
- * the rest, and the last position with the head, run two positions a
- * launch (one weight pass for both, the second attending to the first).
- * The pages' engine takes one token per chunk on CUDA.
+ * against the window exactly as s2fast_slow_step does.  The prompt runs in
+ * chunks of up to 64 positions a launch on the matrix cores (one pass over
+ * the weights a chunk; each position attends to the cache up to itself),
+ * the last chunk holding the last position, whose head and draw then take
+ * one short launch; when the last chunk would hold only the last position,
+ * that position is a step launch of its own.  With an f32 cache the chunks
+ * stop where a chunk's attention scores no longer fit on chip (several
+ * thousand positions), and the rest runs two positions a launch (one
+ * weight pass for both, the second attending to the first).  The pages'
+ * engine takes one token per chunk on CUDA.
  *   tokens [T, 1 + num_codebooks] i32: per position the row-0 token (text,
  *          marker or semantic id), then the codebook codes; the codes count
  *          only where the row-0 token is a semantic id (the prompt's mask)
