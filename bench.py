@@ -54,7 +54,7 @@ def algorithmic_bytes_per_frame(shape, batch: int, qkv0_table: bool) -> int:
     return per_frame + io
 
 
-def survey_bytes_per_frame(shape, batch: int) -> int:
+def scope_bytes_per_frame(shape, batch: int) -> int:
     """The roofline's algorithmic bytes of one frame of `batch` requests:
     every weight matrix (wqkv, wo, w1, w3, w2 of each layer and the untied
     head) once per decode step, fast_project_in once per frame, plus each
@@ -555,7 +555,7 @@ def main():
     B = 1
     frames_per_s = B * args.steps / secs
     ms = secs * 1e3 / args.steps
-    bytes_frame = survey_bytes_per_frame(shape, B)                # one launch is one frame at batch 1
+    bytes_frame = scope_bytes_per_frame(shape, B)                # one launch is one frame at batch 1
     path_bytes = algorithmic_bytes_per_frame(shape, B, True)
     achieved = bytes_frame / kern_s / 1e9
     csrc = os.path.join(ROOT, "dual_ar_neural_amd", "csrc")
@@ -620,7 +620,7 @@ def main():
             di = upload(torch, frs)
             print(f"[bench] timing {nf} frames at batch {Bs}", file=sys.stderr, flush=True)
             sec, per_call, rs = time_frames(torch, cs, di, Bs, nf, 2, runs=RUNS)
-            fb = survey_bytes_per_frame(ws.shape, Bs)
+            fb = scope_bytes_per_frame(ws.shape, Bs)
             sweep[f"b{Bs}"] = {"frames_per_s": round(Bs * nf / sec, 2), "ms_per_frame": round(sec * 1e3 / nf, 3),
                                "hbm_gbs": round(fb * nf / sec / 1e9, 1),
                                "frac": round(fb * nf / sec / 1e9 / PEAK_HBM_GBS, 4), "frames": nf,
@@ -649,7 +649,7 @@ def main():
         diq = upload(torch, frq)
         print(f"[bench] timing {nq} frames of the int8 model at batch 1", file=sys.stderr, flush=True)
         sec, per_call = time_frames(torch, cq, diq, 1, nq, 4)
-        fbq = survey_bytes_per_frame(wq.shape, 1)
+        fbq = scope_bytes_per_frame(wq.shape, 1)
         result["q8"] = {"workload": "S2 Pro-shaped Fast-AR with weight-only int8 matrices (one float32 scale per "
                                     "row; bf16 norms and embeddings), batch 1, independent frames",
                         "frames_per_s": round(nq / sec, 2), "ms_per_frame": round(sec * 1e3 / nq, 4),

@@ -8,7 +8,7 @@ generation main loop", section 1; causal mask with offset 0, section 3).
 A batch of B requests at the same step is computed as B independent windows
 of equal length; nothing is shared between requests.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * pre-norm residual blocks, x += attn(norm(x)); x += ffn(norm(x)) — the
     pages call the block "almost isomorphic" to the Qwen3-shaped Slow-AR;
   * the fused wqkv output is [Q (n_head*hd) | K (n_kv*hd) | V (n_kv*hd)],
@@ -56,7 +56,7 @@ def dequantize_rows(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     W[r, k] = scale[r] * q[r, k], rounded to float32.  (The pages name GGUF
     quantised tensors, "Overall architecture & Dual-AR data flow", section 5
     and "Model loading and GGUF", section 4, but no Fast-AR format; per-row
-    symmetric int8 is this build's reading.)"""
+    symmetric int8 is the library's reading.)"""
     q = np.asarray(q)
     assert q.dtype == np.int8 and q.ndim == 2
     scale = np.asarray(scale, dtype=F32).reshape(-1)

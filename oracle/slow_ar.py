@@ -23,7 +23,7 @@ Plain float32 numpy, one request at a time.  What it follows:
   * sem_code = main token - semantic_begin, clamped (section 5.2), then the
     nine Fast-AR draws on the Slow-AR hidden state (section 5.1).
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   * the codebook index j runs 0..num_codebooks-1 over the frame's codes
     c_0..c_9 (the shared table has num_codebooks * codebook_size rows);
   * sem_scale multiplies the semantic embedding only, as the formula on the

@@ -46,7 +46,7 @@ def test_fast_frame_bytes_from_shapes():
     assert bench.algorithmic_bytes_per_frame(s, 1, True) == want
 
 
-def test_survey_bytes_are_the_scope_tables_figure():
+def test_scope_bytes_are_the_scope_tables_figure():
     """The roofline's bytes: every weight matrix once per decode step
     (7,455,375,360 B a frame at the S2 Pro shape, 828,375,040 a step) plus
     10,332 B of each request's inputs and codes; fast_project_in once per
@@ -55,21 +55,21 @@ def test_survey_bytes_are_the_scope_tables_figure():
     mats = [n for n in si.weight_names(s) if not n.endswith("norm") and n != "fast_embeddings"]
     per_step = _tensor_bytes(lambda n: si.weight_shape(s, n), mats, 2)
     assert per_step == 828_375_040
-    assert bench.survey_bytes_per_frame(s, 1) == 7_455_375_360 + 10_332
-    assert bench.survey_bytes_per_frame(s, 16) == 7_455_375_360 + 16 * 10_332
-    assert bench.survey_bytes_per_frame(si.S2PRO_PROJ, 64) == 7_455_375_360 + 13_107_200 + 64 * 10_332
+    assert bench.scope_bytes_per_frame(s, 1) == 7_455_375_360 + 10_332
+    assert bench.scope_bytes_per_frame(s, 16) == 7_455_375_360 + 16 * 10_332
+    assert bench.scope_bytes_per_frame(si.S2PRO_PROJ, 64) == 7_455_375_360 + 13_107_200 + 64 * 10_332
 
 
-def test_survey_bytes_of_the_int8_model():
+def test_scope_bytes_of_the_int8_model():
     """int8 matrices: one byte a weight plus one float32 scale a row."""
     s = si.S2PRO_Q8
     w = si.make_weights(si.TINY_Q8, 1)           # the same tensor set at a small shape
     mats = [n for n in w if w[n].dtype == np.int8]
     per_step_tiny = sum(w[n].size + 4 * w[n].shape[0] for n in mats)
     io = si.TINY_Q8.in_dim * 4 + 4 + 9 * 4 + 12 + 40
-    assert bench.survey_bytes_per_frame(si.TINY_Q8, 1) == 9 * per_step_tiny + io
+    assert bench.scope_bytes_per_frame(si.TINY_Q8, 1) == 9 * per_step_tiny + io
     rows = 4 * (s.qkv_dim + 2 * s.dim + 2 * s.ffn_dim) + s.codebook_size   # wqkv, wo, w1, w3, w2, head
-    assert bench.survey_bytes_per_frame(s, 1) == 7_455_375_360 // 2 + 9 * rows * 4 + 10_332
+    assert bench.scope_bytes_per_frame(s, 1) == 7_455_375_360 // 2 + 9 * rows * 4 + 10_332
 
 
 def test_prefill_launch_split_and_bytes():

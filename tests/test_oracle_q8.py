@@ -1,6 +1,6 @@
 """Pins of the oracle's weight-only int8 matrices (CPU only).
 
-Format (this build's reading; the pages name GGUF quantised tensors but no
+Format (the library's reading; the pages name GGUF quantised tensors but no
 Fast-AR format): every weight matrix int8 with one float32 scale per output
 row, W[r, k] = scale[r] * q[r, k]; norm weights and fast_embeddings stay
 bf16."""
