@@ -69,6 +69,30 @@ __device__ __forceinline__ void atomic_add_coh(long long* p, long long v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Tagged values: a float in the low word of an 8-byte word whose high word
+// names the launch that wrote it.  The 8-byte atomic store is single-copy
+// atomic, so a reader that sees the tag it expects also sees that launch's
+// value; a reader can therefore wait on the data itself instead of on a
+// separate flag written after it.
+__device__ __forceinline__ void st_tagged(u64* p, float v, u32 tag) {
+  __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_is(u64 t, u32 tag) { return (u32)(t >> 32) == tag; }
+__device__ __forceinline__ float tag_val(u64 t) { return __uint_as_float((u32)t); }
+// First reads of tagged values use ordinary (L2-cacheable) loads, 16 bytes
+// (two values) a lane where the layout allows: a copy that is not current
+// (a line cached before its writer stored it) carries an older tag and is
+// loaded again with coherent loads (ld_coh64), so a value is used only once
+// its tag is current, wherever it came from.  The hardware never splits an
+// aligned 8-byte word of such a load.
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void ld_tagged2(const u64* p, u64& a, u64& b) {
+  const u64x2 v = *reinterpret_cast<const u64x2*>(p);
+  a = v.x;
+  b = v.y;
+}
+__device__ __forceinline__ u64 ld_tagged(const u64* p) { return *p; }
+
 // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): this wave's vector memory
 // operations (loads and stores) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

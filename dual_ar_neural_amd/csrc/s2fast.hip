@@ -3,19 +3,23 @@
 // One cooperative launch decodes one frame of one request: 256 blocks (one
 // per CU) walk the nine decode steps together.  Every weight matrix is split
 // by rows across the blocks and streamed once per step with non-temporal
-// 16-byte loads; the blocks meet at device-wide flag barriers between the
-// phases whose inputs depend on every block's outputs.
+// 16-byte loads.  Every phase's input depends on every block's outputs of
+// the phase before.  Where those outputs are plain values, each block writes
+// them as tagged values (the launch's tag beside each float) and the next
+// phase's loads wait on the tags ("tag"); the attention phase's int64
+// accumulator sums and its keys/values are read after a device-wide flag
+// barrier ("sync").
 //
 // Per decode step k (window [hidden, emb(c_0), ..., emb(c_{k-1})], positions
 // restart at 0; "Fast-AR codebook decoding and the generation main loop",
 // sections 2-4) and per layer:
-//   A  RMSNorm(x) -> fused wqkv rows                                  | sync
+//   A  RMSNorm(x) -> fused wqkv rows                                  | tag
 //   B  per KV group: q/k RMSNorm + pair RoPE + causal attention (mask
 //      offset 0) -> wo restricted to the group's columns; the 8 group
 //      partial sums meet in an int64 fixed-point accumulator          | sync
-//   C  x_mid = x + attn; RMSNorm -> w1, w3 rows -> silu(a1) * a3      | sync
-//   D  w2 rows; x = x_mid + ffn                                        | sync
-// then fast_norm -> untied fast_output rows -> logits | sync, and the sampler
+//   C  x_mid = x + attn; RMSNorm -> w1, w3 rows -> silu(a1) * a3      | tag
+//   D  w2 rows; x = x_mid + ffn                                        | tag
+// then fast_norm -> untied fast_output rows -> logits | tag, and the sampler
 // (every block draws the same code from the same logits).
 //
 // The method recomputes the whole window at every call (no KV cache).  The
@@ -81,23 +85,27 @@ struct FrameArgs {
   int forced_ld;           // codes per request in `forced`
   int lo_first, lo_rows;   // logits_out row of step s >= lo_first is s - lo_first
   // Per-frame arena.  Every (step, layer) output has its own 256-byte
-  // aligned region, written once per frame (write-through sc1 stores or
-  // device atomics) and read only after the grid sync that follows its
-  // writes, so readers may use ordinary L2-cacheable loads: no stale copy of
-  // a region can exist in any L2 (the kernel starts with an acquire that
-  // invalidates lines cached by earlier frames).
+  // aligned region, written once per frame.  The outputs of the wqkv, w1/w3,
+  // w2 and head phases are tagged values (the launch's tag beside each
+  // float): their readers wait on the tags with coherent loads and need no
+  // grid sync, and every read of them is such a load.  The attention
+  // accumulators (device atomics), the keys/values and fast_project_in's
+  // output are read only after the grid sync that follows their writes, so
+  // those readers may use ordinary L2-cacheable loads: no stale copy of
+  // such a region can exist in any L2 (the kernel starts with an acquire
+  // that invalidates lines cached by earlier frames).
   float* xin0;             // [dim] fast_project_in(hidden)
-  float* x;                // [slot][MMAX][dim] residual stream after each layer
-  float* qkv;              // [slot][MMAX][qkv_dim]
+  u64* x;                  // [slot][MMAX][dim] residual stream after each layer (tagged)
+  u64* qkv;                // [slot][MMAX][qkv_dim] (tagged)
   long long* acc;          // [slot][MMAX][dim] fixed-point attention output (zero between frames)
-  float* g;                // [slot][MMAX][ffn]
+  u64* g;                  // [slot][MMAX][ffn] (tagged)
   float* kv;               // [n_layer][ctx][kv_pos] this frame's keys/values ([n_kv][2][hd] per position)
   int kv_pos;              // floats per position: n_kv * 2 * hd rounded up to a 128-byte line, so
                            // positions written at different steps never share a cache line
-  float* logits;           // [step][V]
+  u64* logits;             // [step][V] (tagged)
   long long x_slot, qkv_slot, acc_slot, g_slot, logits_slot;  // region strides (elements)
   u32* flags;              // [P][64] per-block barrier epochs
-  u32 epoch0;              // epoch reached before this launch
+  u32 epoch0;              // epoch reached before this launch; epoch0 + 1 tags its outputs
   u32* err;                // watchdog words (see Watch)
   Watch watch;
   u32* tlog;               // optional [P][TLOG_MAX][TLOG_W] wall-clock marks
@@ -120,7 +128,7 @@ struct Lds {
   int* cidx;     // [64]
   u32* mark;     // [256] sampler cross-wave scratch
   int* codes;    // [16]
-  int* flag;     // [4]
+  int* flag;     // [8]: [0] grid sync result, [1] timeline record, [2..3] launch exit, [4] a tag wait gave up
   float* fnw;    // [dim] fast_norm weight (loaded once per frame)
   float* qkn;    // [n_layer][2][hd] q_norm and k_norm weights (loaded once per frame)
   float* rope;   // [2][ctx][hd/2] cos and sin (loaded once per frame)
@@ -131,7 +139,7 @@ __host__ __device__ inline size_t lds_floats(int kmax, int rmax, int gheads, int
                                              int n_layer) {
   const size_t act = ((size_t)MMAX * kmax + 3) & ~(size_t)3;   // keeps the regions after it 16-byte aligned
   return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)MMAX * gheads * hd + 2 * (size_t)ctx * hd +
-         2 * TOPK_MAX + 256 + 16 + 4 + (size_t)dim + (size_t)n_layer * 2 * hd +
+         2 * TOPK_MAX + 256 + 16 + 8 + (size_t)dim + (size_t)n_layer * 2 * hd +
          (size_t)ctx * hd + (size_t)rmax;
 }
 
@@ -149,7 +157,7 @@ __device__ inline Lds carve(float* base, const FrameArgs& a) {
   s.cidx = reinterpret_cast<int*>(p); p += TOPK_MAX;
   s.mark = reinterpret_cast<u32*>(p); p += 256;
   s.codes = reinterpret_cast<int*>(p); p += 16;
-  s.flag = reinterpret_cast<int*>(p); p += 4;
+  s.flag = reinterpret_cast<int*>(p); p += 8;
   s.fnw = p; p += a.dim;
   s.qkn = p; p += (size_t)a.n_layer * 2 * a.hd;
   s.rope = p; p += (size_t)a.ctx_len * a.hd;
@@ -162,11 +170,13 @@ __device__ __forceinline__ int row_pos(int step, int m) { return step == 1 ? m :
 
 // per-(step, layer) regions of the frame arena
 __device__ __forceinline__ size_t slot_of(const FrameArgs& a, int step, int l) { return (size_t)(step - 1) * a.n_layer + l; }
-__device__ __forceinline__ float* xb(const FrameArgs& a, int step, int l) { return a.x + slot_of(a, step, l) * a.x_slot; }
-__device__ __forceinline__ float* qkvb(const FrameArgs& a, int step, int l) { return a.qkv + slot_of(a, step, l) * a.qkv_slot; }
-__device__ __forceinline__ float* gb(const FrameArgs& a, int step, int l) { return a.g + slot_of(a, step, l) * a.g_slot; }
+__device__ __forceinline__ u64* xb(const FrameArgs& a, int step, int l) { return a.x + slot_of(a, step, l) * a.x_slot; }
+__device__ __forceinline__ u64* qkvb(const FrameArgs& a, int step, int l) { return a.qkv + slot_of(a, step, l) * a.qkv_slot; }
+__device__ __forceinline__ u64* gb(const FrameArgs& a, int step, int l) { return a.g + slot_of(a, step, l) * a.g_slot; }
 __device__ __forceinline__ long long* accb(const FrameArgs& a, int step, int l) { return a.acc + slot_of(a, step, l) * a.acc_slot; }
-__device__ __forceinline__ float* logitsb(const FrameArgs& a, int step) { return a.logits + (size_t)(step - 1) * a.logits_slot; }
+__device__ __forceinline__ u64* logitsb(const FrameArgs& a, int step) { return a.logits + (size_t)(step - 1) * a.logits_slot; }
+// tag of this launch's tagged outputs (never 0, the arena's cleared state)
+__device__ __forceinline__ u32 out_tag(const FrameArgs& a) { return a.epoch0 + 1u; }
 
 // plain (L2-cacheable) loads of arena data
 __device__ __forceinline__ u64 ld64(const void* p) { return *reinterpret_cast<const u64*>(p); }
@@ -206,13 +216,15 @@ __device__ __forceinline__ void split_rows(int n, int j, int parts, int& r0, int
 // s_barrier, then wave 0 publishes the block's epoch and polls every block's
 // flag with coherent loads.  Returns false (after raising the watchdog word)
 // if a flag does not arrive within SPIN_LIMIT polls; the caller then leaves
-// the kernel.
-template <typename Args>
+// the kernel.  With LOG, instrumented runs record the arrival and release
+// times under the sync's index (callers that number their records
+// otherwise pass false).
+template <typename Args, bool LOG = true>
 __device__ __forceinline__ bool grid_sync(const Args& a, u32& epoch, int* lds_flag) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's output stores are done
   __syncthreads();
   const u32 idx = epoch - a.epoch0;
-  if (a.tlog && tidx() == 0 && idx < TLOG_MAX)
+  if (LOG && a.tlog && tidx() == 0 && idx < TLOG_MAX)
     a.tlog[((size_t)blockIdx.x * TLOG_MAX + idx) * TLOG_W] = (u32)wall_clock64();
   ++epoch;
   if (tidx() < 64) {
@@ -239,7 +251,7 @@ __device__ __forceinline__ bool grid_sync(const Args& a, u32& epoch, int* lds_fl
     if (lane == 0) {
       if (!ok) atomicOr(a.err + W_ERR, 1u);
       lds_flag[0] = ok ? 0 : 1;
-      if (a.tlog && idx < TLOG_MAX) a.tlog[((size_t)blockIdx.x * TLOG_MAX + idx) * TLOG_W + 1] = (u32)wall_clock64();
+      if (LOG && a.tlog && idx < TLOG_MAX) a.tlog[((size_t)blockIdx.x * TLOG_MAX + idx) * TLOG_W + 1] = (u32)wall_clock64();
     }
   }
   __syncthreads();
@@ -375,6 +387,89 @@ __device__ __forceinline__ void stage_arena(float* dst, const float* src, int n,
   for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
 }
 
+// Wait until the tagged words t[0..N) all carry `tag`.  The caller has
+// issued their first loads (ordinary ones, from addr(i)) before using any of
+// them; the words still stale are loaded again with coherent loads, all
+// together, until every one is current.
+// After SPIN_LIMIT rounds the watchdog word and the block's failure flag
+// (flag[4]) are raised and the stale values stand: the block leaves the
+// kernel at the end of the phase.
+template <int N, typename Addr>
+__device__ __forceinline__ void tag_wait(const FrameArgs& a, const Lds& s, u32 tag, u64 (&t)[N], const Addr& addr) {
+  bool stale = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) stale |= !tag_is(t[i], tag);
+  u32 spins = 0;
+  while (stale) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!tag_is(t[i], tag)) t[i] = ld_coh64(addr(i));
+    stale = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) stale |= !tag_is(t[i], tag);
+    if (stale && ++spins > SPIN_LIMIT) {
+      atomicOr(a.err + W_ERR, 1u);
+      s.flag[4] = 1;
+      break;
+    }
+  }
+}
+
+// A step's logits as this launch's tagged values, for the sampler: the
+// loads wait on their tags.
+struct TaggedLogits {
+  const FrameArgs& a;
+  const Lds& s;
+  const u64* L;
+  template <int VPT>
+  __device__ __forceinline__ void load(float (&x)[VPT], int tid, int V) const {
+    u64 t[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) t[j] = ld_tagged(L + min(tid + j * NTHREADS, V - 1));
+    tag_wait(a, s, out_tag(a), t, [&](int j) __attribute__((always_inline)) {
+      return L + min(tid + j * NTHREADS, V - 1);
+    });
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) x[j] = (tid + j * NTHREADS < V) ? tag_val(t[j]) : -INFINITY;
+  }
+};
+
+// n tagged floats (n a multiple of 4) of this launch into LDS in the GEMV
+// layout over K = n columns, as stage_arena, each load waiting on its tag.
+template <typename WT, int NS, typename Hook>
+__device__ __forceinline__ void stage_tagged(const FrameArgs& a, const Lds& s, float* dst, const u64* src, int n,
+                                             const Hook& hook) {
+  const int nq = n >> 2;
+  const u32 tag = out_tag(a);
+  auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
+    u64 t[4 * NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const u64* p = src + 4 * quad_of(base, j, nq);
+      ld_tagged2(p, t[4 * j], t[4 * j + 1]);
+      ld_tagged2(p + 2, t[4 * j + 2], t[4 * j + 3]);
+    }
+    after();
+    tag_wait(a, s, tag, t, [&](int i) __attribute__((always_inline)) {
+      return src + 4 * quad_of(base, i >> 2, nq) + (i & 3);
+    });
+    const int nj = steps_opaque(nq, base);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (j >= nj) break;
+      const int q = base + j * NTHREADS + tidx();
+      if (q < nq) {
+        v4f o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = tag_val(t[4 * j + e]);
+        *reinterpret_cast<v4f*>(dst + phys<WT>(4 * q, n)) = o;
+      }
+    }
+  };
+  batch(0, hook);
+  for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
+}
+
 // Per-wave partial sums of squares of rows 0 and 1 into small[m * NWAVE + wave].
 __device__ __forceinline__ void store_ss(float* small, int M, float ss0, float ss1) {
   const int wave = tidx() >> 6, lane = tidx() & 63;
@@ -399,21 +494,24 @@ __device__ __forceinline__ float norm_den(const float* small, int m, int K, floa
 // the fixed-point attention accumulator is added first (x_mid = x + attention
 // output).  The RMS itself divides the GEMV outputs (norm_den): the row
 // sums of squares are left as per-wave partials in small[m * NWAVE + wave].
-template <typename WT, bool ADD_ACC, typename Hook>
-__device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds& s, int l, int step, int M,
-                                                  const typename VecOf<WT>::type* normw, const Hook& hook) {
+// TAGGED: layers >= 1, whose input is the previous layer's tagged output.
+template <typename WT, bool ADD_ACC, bool TAGGED, typename Hook>
+__device__ __forceinline__ void stage_rows(const FrameArgs& a, const Lds& s, int l, int step, int M,
+                                           const typename VecOf<WT>::type* normw, const Hook& hook) {
   using VT = typename VecOf<WT>::type;
-  constexpr int NS = 3;
+  constexpr int NS = TAGGED ? 2 : 3;
   const int hq = a.dim >> 2;
   const int nq = M * hq;
+  const u32 tag = out_tag(a);
   // float32 source rows: the previous layer's output, or at layer 0 the
   // hidden state (through fast_project_in when present) at window position 0;
   // layer 0 at positions j >= 1 takes fast_embeddings[c_{j-1}]
   // ("Fast-AR codebook decoding ...", section 2)
-  const float* fsrc = (l > 0) ? xb(a, step, l - 1) : (a.has_proj ? a.xin0 : a.hidden);
-  const size_t fstride = (l > 0) ? (size_t)a.dim : 0;
+  const u64* tsrc = TAGGED ? xb(a, step, l - 1) : nullptr;
+  const float* fsrc = a.has_proj ? a.xin0 : a.hidden;
   float ss0 = 0.0f, ss1 = 0.0f;
   auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
+    u64 t[TAGGED ? 4 * NS : 1];
     v4f xv[NS];
     v2ll a0[NS], a1[NS];
     typename WQuad<VT>::type wv[NS], ev[NS];
@@ -421,13 +519,19 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
     for (int j = 0; j < NS; ++j) {
       const int q = quad_of(base, j, nq);
       const int m = q >= hq ? 1 : 0, c = q - m * hq;   // M <= 2
-      const int pos = row_pos(step, m);
       wv[j] = WQuad<VT>::load(normw, c);   // the RMSNorm weight, same round trip
-      xv[j] = *reinterpret_cast<const v4f*>(fsrc + (size_t)m * fstride + 4 * c);
-      // layer 0, position >= 1: the embedding row of the previous code
-      // (otherwise row 0, loaded and not used, so that the load needs no branch)
-      const int code = (l == 0 && pos > 0) ? s.codes[max(pos - 1, 0)] : 0;
-      ev[j] = WQuad<VT>::load(reinterpret_cast<const VT*>(a.emb) + (size_t)code * a.dim, c);
+      if constexpr (TAGGED) {
+        const u64* p = tsrc + (size_t)m * a.dim + 4 * c;
+        ld_tagged2(p, t[4 * j], t[4 * j + 1]);
+        ld_tagged2(p + 2, t[4 * j + 2], t[4 * j + 3]);
+      } else {
+        xv[j] = *reinterpret_cast<const v4f*>(fsrc + 4 * c);
+        // position >= 1: the embedding row of the previous code (otherwise
+        // row 0, loaded and not used, so that the load needs no branch)
+        const int pos = row_pos(step, m);
+        const int code = pos > 0 ? s.codes[max(pos - 1, 0)] : 0;
+        ev[j] = WQuad<VT>::load(reinterpret_cast<const VT*>(a.emb) + (size_t)code * a.dim, c);
+      }
       if (ADD_ACC) {
         const long long* ac = accb(a, step, l) + (size_t)m * a.dim + 4 * c;
         a0[j] = *reinterpret_cast<const v2ll*>(ac);
@@ -435,6 +539,12 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
       }
     }
     after();
+    if constexpr (TAGGED)
+      tag_wait(a, s, tag, t, [&](int i) __attribute__((always_inline)) {
+        const int q = quad_of(base, i >> 2, nq);
+        const int m = q >= hq ? 1 : 0, c = q - m * hq;
+        return tsrc + (size_t)m * a.dim + 4 * c + (i & 3);
+      });
     const int nj = steps_opaque(nq, base);
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -442,19 +552,24 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
       const int qu = base + j * NTHREADS + tidx();
       const int q = min(qu, nq - 1);
       const int m = q >= hq ? 1 : 0, c = q - m * hq;
-      const bool emb = (l == 0 && row_pos(step, m) > 0);
       float v[4];
+      if constexpr (TAGGED) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = emb ? WQuad<VT>::get(ev[j], e) : xv[j][e];
+        for (int e = 0; e < 4; ++e) v[e] = tag_val(t[4 * j + e]);
+      } else {
+        const bool emb = row_pos(step, m) > 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = emb ? WQuad<VT>::get(ev[j], e) : xv[j][e];
+      }
       if (ADD_ACC) {
         v[0] += from_fx(a0[j][0]); v[1] += from_fx(a0[j][1]);
         v[2] += from_fx(a1[j][0]); v[3] += from_fx(a1[j][1]);
       }
       if (qu < nq) {
-        float t = (m == 0) ? ss0 : ss1;
+        float t2 = (m == 0) ? ss0 : ss1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t = fmaf(v[e], v[e], t);
-        if (m == 0) ss0 = t; else ss1 = t;
+        for (int e = 0; e < 4; ++e) t2 = fmaf(v[e], v[e], t2);
+        if (m == 0) ss0 = t2; else ss1 = t2;
         v4f o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = v[e] * WQuad<VT>::get(wv[j], e);
@@ -465,6 +580,13 @@ __device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds&
   batch(0, hook);
   for (int base = NTHREADS * NS; base < nq; base += NTHREADS * NS) batch(base, NoHook{});
   store_ss(s.small, M, ss0, ss1);
+}
+
+template <typename WT, bool ADD_ACC, typename Hook>
+__device__ __forceinline__ void stage_layer_input(const FrameArgs& a, const Lds& s, int l, int step, int M,
+                                                  const typename VecOf<WT>::type* normw, const Hook& hook) {
+  if (l > 0) stage_rows<WT, ADD_ACC, true>(a, s, l, step, M, normw, hook);
+  else stage_rows<WT, ADD_ACC, false>(a, s, l, step, M, normw, hook);
 }
 
 // --------------------------------------------------------------- GEMV
@@ -679,7 +801,8 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // x_mid of one element (the rows a block owns in the w2 phase)
 template <typename WT>
 __device__ __forceinline__ float x_mid_of(const FrameArgs& a, const Lds& s, int l, int step, int m, int k) {
-  const float xin = (l == 0) ? layer0_input<WT>(a, s, row_pos(step, m), k) : xb(a, step, l - 1)[(size_t)m * a.dim + k];
+  const float xin = (l == 0) ? layer0_input<WT>(a, s, row_pos(step, m), k)
+                             : tag_val(ld_coh64(xb(a, step, l - 1) + (size_t)m * a.dim + k));   // current since the wqkv phase
   return xin + from_fx(accb(a, step, l)[(size_t)m * a.dim + k]);
 }
 
@@ -871,8 +994,8 @@ __device__ __forceinline__ void phase_qkv(const FrameArgs& a, const Lds& s, int 
   mark(a, s.flag[1], 3);
   for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
-    st_coh(qkvb(a, step, l) + (size_t)m * a.qkv_dim + r0 + r,
-           s.rsc[r] * red_sum(s.red, r, m) / norm_den(s.small, m, D, a.eps));
+    st_tagged(qkvb(a, step, l) + (size_t)m * a.qkv_dim + r0 + r,
+              s.rsc[r] * red_sum(s.red, r, m) / norm_den(s.small, m, D, a.eps), out_tag(a));
   }
 }
 
@@ -901,13 +1024,20 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
     // wave-uniform and a lane moves one pair of floats.
     constexpr int NS = 4;
     const int F = first_new, hp = hd >> 1;
-    // new rows' q/k/v: this step's wqkv phase output, or at layer 0 of steps
-    // >= 2 the qkv0 row of the code that produced the row
-    const float* qkv_new = (l == 0 && step >= 2) ? a.qkv0 + (size_t)s.codes[step - 1] * a.qkv_dim : qkvb(a, step, l);
+    // new rows' q/k/v: this step's wqkv phase output (tagged), or at layer 0
+    // of steps >= 2 the qkv0 row of the code that produced the row
+    const bool table = (l == 0 && step >= 2);
+    const float* qkv_tab = a.qkv0 + (size_t)(table ? s.codes[step - 1] : 0) * a.qkv_dim;
+    const u64* qkv_new = qkvb(a, step, l);
+    const u32 tag = out_tag(a);
     const int nseg = need_attn ? 2 * F + M * (gh + 2) : 0;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int lp = min(lane, hp - 1);
-    auto seg = [&](int sg, const float*& src, float*& dst) __attribute__((always_inline)) {
+    // segment sg: its LDS destination, and its source as a cache row (src)
+    // or as an offset into the new rows' q/k/v (off, with src null)
+    auto seg = [&](int sg, const float*& src, long long& off, float*& dst) __attribute__((always_inline)) {
+      src = nullptr;
+      off = 0;
       if (sg < F) {
         src = kvl + (sg * a.kv_pos + (g * 2 + 0) * hd);
         dst = s.kc + (size_t)sg * hd;
@@ -917,39 +1047,52 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
       } else {
         const int t = sg - 2 * F;
         const int m = t >= gh + 2 ? 1 : 0, r = t - m * (gh + 2);   // M <= 2
-        const float* row = qkv_new + (size_t)m * a.qkv_dim;
         const int pos = row_pos(step, m);
+        off = (long long)m * a.qkv_dim;
         if (r < gh) {
-          src = row + (size_t)(g * gh + r) * hd;
+          off += (long long)(g * gh + r) * hd;
           dst = s.q + (size_t)(m * gh + r) * hd;
         } else if (r == gh) {
-          src = row + (size_t)(H + g) * hd;
+          off += (long long)(H + g) * hd;
           dst = s.kc + (size_t)pos * hd;
         } else {
-          src = row + (size_t)(H + G + g) * hd;
+          off += (long long)(H + G + g) * hd;
           dst = s.vc + (size_t)pos * hd;
         }
+        if (table) src = qkv_tab + off;
       }
     };
     auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
-      u64 v[NS];
+      // two tagged words per lane and segment; a plain pair (cache row or
+      // qkv0 row) is given this launch's tag, so only new rows are waited on
+      u64 t[2 * NS];
+      long long offs[NS];
       float* dst[NS];
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         // a step past the end re-reads segment 0 (a valid row when nseg is 0)
         const int sg = base + wv + NWAVE * j;
         const float* src;
-        seg(sg < nseg ? sg : 0, src, dst[j]);
-        v[j] = ld64(src + 2 * lp);
+        seg(sg < nseg ? sg : 0, src, offs[j], dst[j]);
+        if (src) {
+          const u64 v = ld64(src + 2 * lp);
+          t[2 * j] = ((u64)tag << 32) | (v & 0xFFFFFFFFull);
+          t[2 * j + 1] = ((u64)tag << 32) | (v >> 32);
+        } else {
+          ld_tagged2(qkv_new + offs[j] + 2 * lp, t[2 * j], t[2 * j + 1]);
+        }
       }
       after();
+      tag_wait(a, s, tag, t, [&](int i) __attribute__((always_inline)) {
+        return qkv_new + offs[i >> 1] + 2 * lp + (i & 1);
+      });
       const int nj = steps_opaque(nseg, base, NWAVE);
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         if (j >= nj) break;
         if (base + wv + NWAVE * j < nseg && lane < hp) {
-          dst[j][2 * lane] = lo_f32(v[j]);
-          dst[j][2 * lane + 1] = hi_f32(v[j]);
+          dst[j][2 * lane] = tag_val(t[2 * j]);
+          dst[j][2 * lane + 1] = tag_val(t[2 * j + 1]);
         }
       }
     };
@@ -1019,8 +1162,9 @@ __device__ __forceinline__ void phase_ffn_up(const FrameArgs& a, const Lds& s, i
   for (int i = tidx(); i < nr * M; i += NTHREADS) {
     const int r = i / M, m = i % M;
     const float den = norm_den(s.small, m, D, a.eps);
-    st_coh(gb(a, step, l) + (size_t)m * a.ffn + r0 + r,
-           silu(s.rsc[r] * red_sum(s.red, r, m) / den) * (s.rsc[nr + r] * red_sum(s.red, nr + r, m) / den));
+    st_tagged(gb(a, step, l) + (size_t)m * a.ffn + r0 + r,
+              silu(s.rsc[r] * red_sum(s.red, r, m) / den) * (s.rsc[nr + r] * red_sum(s.red, nr + r, m) / den),
+              out_tag(a));
   }
 }
 
@@ -1031,9 +1175,9 @@ __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s,
   const float scv = row_scale_issue(s2, nullptr, r0, r1 - r0, r1 - r0);
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
-  stage_arena<WT, true, 5>(s.act, gb(a, step, l), a.ffn, pro);
+  stage_tagged<WT, 5>(a, s, s.act, gb(a, step, l), a.ffn, pro);
   for (int m = 1; m < M; ++m)
-    stage_arena<WT, true, 5>(s.act + (size_t)m * a.kmax, gb(a, step, l) + (size_t)m * a.ffn, a.ffn, NoHook{});
+    stage_tagged<WT, 5>(a, s, s.act + (size_t)m * a.kmax, gb(a, step, l) + (size_t)m * a.ffn, a.ffn, NoHook{});
   row_scale_store(s.rsc, scv, s2, nullptr, r0, r1 - r0, r1 - r0);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
@@ -1045,7 +1189,7 @@ __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s,
     const int r = i / M, m = i % M;
     const int k = r0 + r;
     const float xm = x_mid_of<WT>(a, s, l, step, m, k);
-    st_coh(xb(a, step, l) + (size_t)m * a.dim + k, xm + s.rsc[r] * red_sum(s.red, r, m));
+    st_tagged(xb(a, step, l) + (size_t)m * a.dim + k, xm + s.rsc[r] * red_sum(s.red, r, m), out_tag(a));
     st_coh(accb(a, step, l) + (size_t)m * a.dim + k, 0ll);   // ready for the next frame
   }
 }
@@ -1060,14 +1204,22 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
   {
     // last row of the final layer, times fast_norm (in LDS); the RMS divides the logits
     constexpr int NS = 2;
-    const float* src = xb(a, step, a.n_layer - 1) + (size_t)(M - 1) * D;
+    const u64* src = xb(a, step, a.n_layer - 1) + (size_t)(M - 1) * D;
     const int nq = D >> 2;
+    const u32 tag = out_tag(a);
     float ss = 0.0f;
     auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
-      v4f v[NS];
+      u64 t[4 * NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) v[j] = *reinterpret_cast<const v4f*>(src + 4 * quad_of(base, j, nq));
+      for (int j = 0; j < NS; ++j) {
+        const u64* p = src + 4 * quad_of(base, j, nq);
+        ld_tagged2(p, t[4 * j], t[4 * j + 1]);
+        ld_tagged2(p + 2, t[4 * j + 2], t[4 * j + 3]);
+      }
       after();
+      tag_wait(a, s, tag, t, [&](int i) __attribute__((always_inline)) {
+        return src + 4 * quad_of(base, i >> 2, nq) + (i & 3);
+      });
       const int nj = steps_opaque(nq, base);
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
@@ -1077,8 +1229,9 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
           v4f o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            ss = fmaf(v[j][e], v[j][e], ss);
-            o[e] = v[j][e] * s.fnw[4 * q + e];
+            const float v = tag_val(t[4 * j + e]);
+            ss = fmaf(v, v, ss);
+            o[e] = v * s.fnw[4 * q + e];
           }
           *reinterpret_cast<v4f*>(s.act + phys<WT>(4 * q, D)) = o;
         }
@@ -1098,7 +1251,7 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
   const float hden = norm_den(s.small, 0, D, a.eps);
   for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
     const float v = s.rsc[r] * red_sum(s.red, r, 0) / hden;
-    st_coh(logitsb(a, step) + r0 + r, v);
+    st_tagged(logitsb(a, step) + r0 + r, v, out_tag(a));
     if (a.logits_out && step >= a.lo_first) a.logits_out[(size_t)(step - a.lo_first) * a.V + r0 + r] = v;
   }
 }
@@ -1129,6 +1282,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
   u32 epoch = a.epoch0;
   const int V = a.V;
   if (tidx() == 0) {
+    s.flag[4] = 0;
     const int c0 = a.forced ? a.forced[0] : a.sem_code[0];
     s.codes[0] = min(max(c0, 0), V - 1);     // clamp both ways (main loop, section 5.2)
     if (a.forced)
@@ -1156,8 +1310,8 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
   for (int ph = 0; ph < nph; ++ph) {
     const int step = id.step, l = id.layer;
     const int M = (step == 1) ? 2 : 1;
-    if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
-    mark(a, epoch - a.epoch0, 5);
+    if (a.tlog && tidx() == 0) s.flag[1] = ph;
+    mark(a, ph, 5);
     switch (id.kind) {
       case PH_PROJ: phase_project_in<WT>(a, s, pl); break;
       case PH_QKV: phase_qkv<WT>(a, s, l, step, M, pl); break;
@@ -1169,21 +1323,30 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
     const PhaseId done = id;
     id = next_phase(a, id);
     pl = plan_for<WT>(a, id);   // past the last phase: a plan that is never used
-    if (done.kind == PH_HEAD && a.forced) {   // teacher forcing: the next prefix is known
-      __syncthreads();   // the head's epilogue still reads red and small
-      continue;
+    mark(a, ph, 0);
+    if (done.kind == PH_WO || done.kind == PH_PROJ) {
+      // the attention accumulators (device atomics), this step's keys and
+      // values and fast_project_in's output are read after a grid sync
+      if (!grid_sync<FrameArgs, false>(a, epoch, s.flag)) { ok = false; break; }
+    } else {
+      // the next phase's loads wait on this phase's tagged outputs: the
+      // block only finishes its own use of LDS (the epilogue still reads
+      // red and small)
+      __syncthreads();
     }
-    if (!grid_sync(a, epoch, s.flag)) { ok = false; break; }
-    if (done.kind == PH_HEAD) {
+    if (s.flag[4]) { ok = false; break; }
+    mark(a, ph, 1);
+    if (done.kind == PH_HEAD && !a.forced) {
       const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
-      const int code = sample_request(logitsb(a, step), V, a.temp[0], a.top_p[0], a.top_k[0],
-                                      a.uniforms[step - 1], sc);
+      const int code = sample_from(TaggedLogits{a, s, logitsb(a, step)}, V, a.temp[0], a.top_p[0], a.top_k[0],
+                                   a.uniforms[step - 1], sc);
       if (tidx() == 0) s.codes[step] = min(max(code, 0), V - 1);
       __syncthreads();
+      if (s.flag[4]) { ok = false; break; }
     }
   }
   if (ok && blockIdx.x == 0 && a.codes_out && tidx() < a.ncb) a.codes_out[tidx()] = s.codes[tidx()];
-  // a barrier wait gave up: the frame failed.  The attention accumulators
+  // a barrier or tag wait gave up: the frame failed.  The attention accumulators
   // are cleared (the next frame adds into them) and the request's codebooks
   // 1.. are 0, the main loop's convention for a failed fast_decode
   // ("Fast-AR codebook decoding ...", section 5.2).
@@ -1454,12 +1617,12 @@ struct s2fast_ctx {
   float* rope = nullptr;
   float* qkv0 = nullptr;   // [V][qkv_dim] layer-0 q/k/v of every embedding row
   float* xin0 = nullptr;
-  float* x = nullptr;
-  float* qkv = nullptr;
+  u64* x = nullptr;        // tagged outputs (x, qkv, g, logits): cleared at creation and when the
+  u64* qkv = nullptr;      // epoch counter wraps, so no stale tag can match a later launch's
   long long* acc = nullptr;
-  float* g = nullptr;
+  u64* g = nullptr;
   float* kv = nullptr;
-  float* logits = nullptr;
+  u64* logits = nullptr;
   u32* flags = nullptr;
   u32* err = nullptr;
   u32* tlog = nullptr;     // allocated on first s2fast_test_timeline call
@@ -1523,9 +1686,10 @@ void rope_table_host(int hd, int ctx, float base, float* c, float* s) {
 // grid syncs of one launch of `nsteps` decode steps: one per phase (the
 // frame kernel's phase_count), less the head's when the prefix is
 // teacher-forced
-int syncs_for(const s2fast_config& c, int nsteps, bool forced) {
-  const int per_step = 4 * c.n_layer + (forced ? 0 : 1);
-  return (c.has_project_in ? 1 : 0) + nsteps * per_step - (nsteps - 1);
+// Grid syncs of a batch-1 launch: after fast_project_in and after every
+// layer's attention + wo phase; the other phases hand over tagged values.
+int syncs_for(const s2fast_config& c, int nsteps) {
+  return (c.has_project_in ? 1 : 0) + nsteps * c.n_layer;
 }
 
 void free_ctx(s2fast_ctx* c) {
@@ -1627,13 +1791,27 @@ int build_qkv0(s2fast_ctx* c) {
   return ok ? S2FAST_OK : S2FAST_ERR_HIP;
 }
 
+int zero_device(void* p, size_t bytes, hipStream_t st);
+
+// Before the epoch counter wraps: the barrier flags and the tagged outputs
+// go back to their cleared state (tag 0, below every launch's tag) and the
+// counter restarts.
+int restart_epochs(s2fast_ctx* c, hipStream_t stream) {
+  const size_t slots = (size_t)(c->cfg.num_codebooks - 1) * c->cfg.n_layer;
+  if (zero_device(c->flags, (size_t)c->ncu * 64 * sizeof(u32), stream) != S2FAST_OK ||
+      zero_device(c->x, slots * c->x_slot * sizeof(u64), stream) != S2FAST_OK ||
+      zero_device(c->qkv, slots * c->qkv_slot * sizeof(u64), stream) != S2FAST_OK ||
+      zero_device(c->g, slots * c->g_slot * sizeof(u64), stream) != S2FAST_OK ||
+      zero_device(c->logits, (size_t)(c->cfg.num_codebooks - 1) * c->logits_slot * sizeof(u64), stream) != S2FAST_OK)
+    return S2FAST_ERR_HIP;
+  c->epoch = 0;
+  return S2FAST_OK;
+}
+
 int launch_frame(s2fast_ctx* c, const FrameArgs& fa_in, hipStream_t stream) {
   FrameArgs fa = fa_in;
-  const u32 n = (u32)syncs_for(c->cfg, fa.nsteps, fa.forced != nullptr);
-  if (c->epoch > 0xF0000000u) {
-    if (hipMemsetAsync(c->flags, 0, (size_t)c->ncu * 64 * sizeof(u32), stream) != hipSuccess) return S2FAST_ERR_HIP;
-    c->epoch = 0;
-  }
+  const u32 n = (u32)syncs_for(c->cfg, fa.nsteps);
+  if (c->epoch > 0xF0000000u && restart_epochs(c, stream) != S2FAST_OK) return S2FAST_ERR_HIP;
   fa.epoch0 = c->epoch;
   void* args[] = {&fa};
   hipError_t e = hipLaunchCooperativeKernel(frame_fn(c->cfg.weight_dtype), dim3(c->ncu), dim3(NTHREADS), args,
@@ -1648,10 +1826,7 @@ int launch_batched(s2fast_ctx* c, const BatchArgs& ba_in, hipStream_t stream) {
   const u32 n = (u32)b_syncs(c->cfg.has_project_in, ba.nsteps, c->cfg.n_layer, ba.forced != nullptr,
                             c->b_ks[BK_HEAD] > 1 && ba.logits_out != nullptr,
                             b_merged_draw(ba.Bq, c->cfg.n_head_kv, c->ncu));
-  if (c->epoch > 0xF0000000u) {
-    if (hipMemsetAsync(c->flags, 0, (size_t)c->ncu * 64 * sizeof(u32), stream) != hipSuccess) return S2FAST_ERR_HIP;
-    c->epoch = 0;
-  }
+  if (c->epoch > 0xF0000000u && restart_epochs(c, stream) != S2FAST_OK) return S2FAST_ERR_HIP;
   ba.epoch0 = c->epoch;
   void* args[] = {&ba};
   const void* fn = c->cfg.weight_dtype == S2FAST_BF16 ? reinterpret_cast<const void*>(&frame_kernel_b<uint16_t>)
@@ -1779,12 +1954,12 @@ StaticLayout static_layout(const s2fast_ctx* c) {
   StaticLayout L;
   size_t o = 0;
   L.xin0 = o; o += r(((size_t)k.dim + 63) / 64 * 64 * sizeof(float));
-  L.x = o; o += r(slots * c->x_slot * sizeof(float));
-  L.qkv = o; o += r(slots * c->qkv_slot * sizeof(float));
+  L.x = o; o += r(slots * c->x_slot * sizeof(u64));
+  L.qkv = o; o += r(slots * c->qkv_slot * sizeof(u64));
   L.acc = o; o += r(slots * c->acc_slot * sizeof(long long));
-  L.g = o; o += r(slots * c->g_slot * sizeof(float));
+  L.g = o; o += r(slots * c->g_slot * sizeof(u64));
   L.kv = o; o += r((size_t)k.n_layer * k.context * c->kv_pos * sizeof(float));
-  L.logits = o; o += r((size_t)(k.num_codebooks - 1) * c->logits_slot * sizeof(float));
+  L.logits = o; o += r((size_t)(k.num_codebooks - 1) * c->logits_slot * sizeof(u64));
   L.flags = o; o += r((size_t)c->ncu * 64 * sizeof(u32));
   L.end = o;
   return L;
@@ -1976,6 +2151,10 @@ int s2fast_create(const s2fast_config* cfg, const s2fast_weights* w, s2fast_ctx*
   if (!ok) { free_ctx(c); return S2FAST_ERR_NOMEM; }
   ok = hipMemcpy(c->rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemset(c->acc, 0, (size_t)(slots * c->acc_slot) * sizeof(long long)) == hipSuccess &&
+       hipMemset(c->x, 0, (size_t)(slots * c->x_slot) * sizeof(u64)) == hipSuccess &&
+       hipMemset(c->qkv, 0, (size_t)(slots * c->qkv_slot) * sizeof(u64)) == hipSuccess &&
+       hipMemset(c->g, 0, (size_t)(slots * c->g_slot) * sizeof(u64)) == hipSuccess &&
+       hipMemset(c->logits, 0, (size_t)((k.num_codebooks - 1) * c->logits_slot) * sizeof(u64)) == hipSuccess &&
        hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
        hipMemset(c->err, 0, W_WORDS * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) { free_ctx(c); return S2FAST_ERR_HIP; }
@@ -2056,7 +2235,7 @@ void s2fast_destroy(s2fast_ctx* ctx) {
 int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B) {
   if (!ctx || B < 1) return -1;
   const int nsteps = ctx->cfg.num_codebooks - 1;
-  if (B == 1 || ctx->bq == 0) return B * syncs_for(ctx->cfg, nsteps, false);
+  if (B == 1 || ctx->bq == 0) return B * syncs_for(ctx->cfg, nsteps);
   int n = 0;
   for (int b0 = 0; b0 < B; b0 += ctx->bq) {
     const int Bg = std::min(ctx->bq, B - b0);
@@ -2180,16 +2359,16 @@ int s2fast_decode_frame_static(s2fast_ctx* ctx, int32_t B, const float* hidden, 
   FrameArgs fa;
   fill_shape(ctx, fa);
   fa.xin0 = reinterpret_cast<float*>(S.ptr + L.xin0);
-  fa.x = reinterpret_cast<float*>(S.ptr + L.x);
-  fa.qkv = reinterpret_cast<float*>(S.ptr + L.qkv);
+  fa.x = reinterpret_cast<u64*>(S.ptr + L.x);
+  fa.qkv = reinterpret_cast<u64*>(S.ptr + L.qkv);
   fa.acc = reinterpret_cast<long long*>(S.ptr + L.acc);
-  fa.g = reinterpret_cast<float*>(S.ptr + L.g);
+  fa.g = reinterpret_cast<u64*>(S.ptr + L.g);
   fa.kv = reinterpret_cast<float*>(S.ptr + L.kv);
-  fa.logits = reinterpret_cast<float*>(S.ptr + L.logits);
+  fa.logits = reinterpret_cast<u64*>(S.ptr + L.logits);
   fa.flags = reinterpret_cast<u32*>(S.ptr + L.flags);
   fa.tlog = nullptr;
   const void* fn = frame_fn(k.weight_dtype);
-  const u32 n = (u32)syncs_for(k, fa.nsteps, false);
+  const u32 n = (u32)syncs_for(k, fa.nsteps);
   int done = 0, rc = S2FAST_OK;
   for (int b = 0; b < B; ++b) {
     fa.hidden = hidden + (size_t)b * k.in_dim;

@@ -104,10 +104,25 @@ __device__ __forceinline__ void block_best(float& v, int& i, int* buf, int tid) 
   }
 }
 
+// The request's V logits as plain floats in device memory (finite values).
+struct PlainLogits {
+  const float* L;
+  template <int VPT>
+  __device__ __forceinline__ void load(float (&x)[VPT], int tid, int V) const {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int i = tid + j * NTHREADS;
+      x[j] = (i < V) ? L[i] : -INFINITY;
+    }
+  }
+};
+
 // Returns the sampled code in every lane of wave 0 (other waves: undefined).
-// L: the request's V logits (device memory, finite values).
-template <int VPT>
-__device__ __forceinline__ int sample_block(const float* L, int V, float T, float top_p, int top_k, float u, const SampScratch& sc) {
+// src: the request's V logits (finite values); src.load gives thread t its
+// logits t, t + NTHREADS, ... (-inf past V).
+template <int VPT, typename Src>
+__device__ __forceinline__ int sample_block(const Src& src, int V, float T, float top_p, int top_k, float u,
+                                            const SampScratch& sc) {
   // The thread index goes through an opaque move so that nothing derived
   // from it (sort masks, hash offsets) is hoisted out of the caller's loops,
   // where it would stay live in registers across every other phase.
@@ -116,13 +131,9 @@ __device__ __forceinline__ int sample_block(const float* L, int V, float T, floa
   const int lane = tid & 63, w = tid >> 6;
   constexpr int BIG = 0x7FFFFFFF;
   float x[VPT];
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int i = tid + j * NTHREADS;
-    x[j] = (i < V) ? L[i] : -INFINITY;
-  }
-  // The race's exponential of rank `lane` depends only on the uniform: it
-  // is computed while the logits are in flight.
+  src.load(x, tid, V);
+  // The race's exponential of rank `lane` depends only on the uniform: for
+  // plain logits it is computed while they are in flight.
   const u64 h = splitmix64(((u64)__float_as_uint(u) << 32) + (u64)lane);
   const double uj = ((double)(h >> 40) + 0.5) * (1.0 / 16777216.0);
   const float E = (float)(-log(uj));
@@ -278,10 +289,15 @@ __device__ __forceinline__ int sample_block(const float* L, int V, float T, floa
 }
 
 // Sampler entry for any V <= 2 * 8 * NTHREADS.
+template <typename Src>
+__device__ __forceinline__ int sample_from(const Src& src, int V, float T, float top_p, int top_k, float u,
+                                           const SampScratch& sc) {
+  if (V <= 8 * NTHREADS) return sample_block<8>(src, V, T, top_p, top_k, u, sc);
+  return sample_block<16>(src, V, T, top_p, top_k, u, sc);
+}
 __device__ __forceinline__ int sample_request(const float* L, int V, float T, float top_p, int top_k, float u,
                                               const SampScratch& sc) {
-  if (V <= 8 * NTHREADS) return sample_block<8>(L, V, T, top_p, top_k, u, sc);
-  return sample_block<16>(L, V, T, top_p, top_k, u, sc);
+  return sample_from(PlainLogits{L}, V, T, top_p, top_k, u, sc);
 }
 
 }  // namespace s2f

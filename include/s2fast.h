@@ -229,7 +229,7 @@ int s2fast_decode_frame(s2fast_ctx* ctx, int32_t B, const float* hidden, const i
  * call after one with a context of another shape.  The context must have
  * been created on the current device (else S2FAST_ERR_DEVICE); a shape
  * whose batch-1 arena exceeds 16 MiB gives S2FAST_ERR_SCRATCH (the S2 Pro
- * shape needs 7.4 MiB).  Every call on one GPU shares the array: calls that
+ * shape needs 12.2 MiB).  Every call on one GPU shares the array: calls that
  * overlap on one GPU, from any context or thread, race, and must be
  * serialised by the caller (one stream).  Each call leaves the array ready
  * for the next, also after a failure reported by s2fast_status.  Other
@@ -500,9 +500,12 @@ int s2fast_test_slow_prefill_chunks(s2fast_slow_ctx* ctx, int32_t enable);
 
 /* Timeline instrumentation (blocking; for measurement only).  enable != 0
  * makes later launches on this context record, for every block and every
- * grid-wide synchronisation point i < 256 of a frame, the 100 MHz wall clock
- * when the block finished the phase before i (word 0) and when it left
- * synchronisation i (word 1); words 2..7 hold in-phase marks (2: before the
+ * record i < 256 of a frame (batch-1 launches: phase i; batched launches:
+ * grid-wide synchronisation point i), the 100 MHz wall clock when the block
+ * finished the phase (word 0) and when it left the synchronisation after it
+ * (word 1: a grid sync, or the block's own barrier after a batch-1 phase
+ * whose outputs the next phase waits on itself as tagged values); words
+ * 2..7 hold in-phase marks (2: before the
  * GEMV, 3: after it, 4: input staged, 5: phase start, 6 and 7: after the
  * q/k norms and after the attention scores in the attention phase), 0 where
  * a phase sets none.  If host_out is not NULL (HOST pointer, capacity >= n_blocks*256*8
@@ -515,7 +518,9 @@ int s2fast_test_timeline(s2fast_ctx* ctx, int32_t enable, uint32_t* host_out, in
 int s2fast_test_slow_timeline(s2fast_slow_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity);
 
 /* Number of grid-wide synchronisation points one frame of B requests
- * takes on this context, or -1 on error (for measurement reports). */
+ * takes on this context, or -1 on error (for measurement reports).  A
+ * batch-1 frame syncs after fast_project_in and after each layer's
+ * attention + wo phase only. */
 int s2fast_syncs_per_frame(const s2fast_ctx* ctx, int32_t B);
 
 #ifdef __cplusplus
