@@ -30,8 +30,9 @@ constexpr u32 SPIN_LIMIT = 1u << 22; // bounded waits: far longer than any phase
 constexpr int W_ERR = 0, W_EXITS = 64, W_STATUS = 128, W_WORDS = 256;
 
 // Test hook carried by every launch: with give_up set, every block's first
-// barrier waits for an epoch no block publishes and gives up after one poll,
-// so the failure path runs while every block still exits normally.
+// barrier waits for an epoch no block publishes and gives up after one poll
+// (and a wait on tagged values gives up at once), so the failure path runs
+// while every block still exits normally.
 struct Watch {
   u32 give_up;
 };

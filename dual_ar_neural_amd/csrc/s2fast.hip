@@ -392,10 +392,24 @@ __device__ __forceinline__ void stage_arena(float* dst, const float* src, int n,
 // them; the words still stale are loaded again with coherent loads, all
 // together, until every one is current.
 // After SPIN_LIMIT rounds the watchdog word and the block's failure flag
-// (flag[4]) are raised and the stale values stand: the block leaves the
-// kernel at the end of the phase.
+// are raised and the stale values stand: the block leaves the kernel at the
+// end of the phase.  The watchdog test hook (Watch) makes every tagged wait
+// give up at once.
+struct TagWait {
+  u32* err;      // the launch's watchdog words
+  int* fail;     // the block's failure flag (LDS)
+  u32 tag;       // the tag this launch writes
+  u32 give_up;   // test hook
+};
+
 template <int N, typename Addr>
-__device__ __forceinline__ void tag_wait(const FrameArgs& a, const Lds& s, u32 tag, u64 (&t)[N], const Addr& addr) {
+__device__ __forceinline__ void tag_wait(const TagWait& w, u64 (&t)[N], const Addr& addr) {
+  const u32 tag = w.tag;
+  if (w.give_up) {
+    atomicOr(w.err + W_ERR, 1u);
+    *w.fail = 1;
+    return;
+  }
   bool stale = false;
 #pragma unroll
   for (int i = 0; i < N; ++i) stale |= !tag_is(t[i], tag);
@@ -408,27 +422,29 @@ __device__ __forceinline__ void tag_wait(const FrameArgs& a, const Lds& s, u32 t
 #pragma unroll
     for (int i = 0; i < N; ++i) stale |= !tag_is(t[i], tag);
     if (stale && ++spins > SPIN_LIMIT) {
-      atomicOr(a.err + W_ERR, 1u);
-      s.flag[4] = 1;
+      atomicOr(w.err + W_ERR, 1u);
+      *w.fail = 1;
       break;
     }
   }
 }
 
+// the frame kernel's tagged waits: failure flag flag[4]
+__device__ __forceinline__ TagWait frame_tw(const FrameArgs& a, const Lds& s) {
+  return TagWait{a.err, s.flag + 4, out_tag(a), a.watch.give_up};
+}
+
 // A step's logits as this launch's tagged values, for the sampler: the
 // loads wait on their tags.
 struct TaggedLogits {
-  const FrameArgs& a;
-  const Lds& s;
+  TagWait w;
   const u64* L;
   template <int VPT>
   __device__ __forceinline__ void load(float (&x)[VPT], int tid, int V) const {
     u64 t[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) t[j] = ld_tagged(L + min(tid + j * NTHREADS, V - 1));
-    tag_wait(a, s, out_tag(a), t, [&](int j) __attribute__((always_inline)) {
-      return L + min(tid + j * NTHREADS, V - 1);
-    });
+    tag_wait(w, t, [&](int j) __attribute__((always_inline)) { return L + min(tid + j * NTHREADS, V - 1); });
 #pragma unroll
     for (int j = 0; j < VPT; ++j) x[j] = (tid + j * NTHREADS < V) ? tag_val(t[j]) : -INFINITY;
   }
@@ -437,10 +453,8 @@ struct TaggedLogits {
 // n tagged floats (n a multiple of 4) of this launch into LDS in the GEMV
 // layout over K = n columns, as stage_arena, each load waiting on its tag.
 template <typename WT, int NS, typename Hook>
-__device__ __forceinline__ void stage_tagged(const FrameArgs& a, const Lds& s, float* dst, const u64* src, int n,
-                                             const Hook& hook) {
+__device__ __forceinline__ void stage_tagged(const TagWait& w, float* dst, const u64* src, int n, const Hook& hook) {
   const int nq = n >> 2;
-  const u32 tag = out_tag(a);
   auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
     u64 t[4 * NS];
 #pragma unroll
@@ -450,7 +464,7 @@ __device__ __forceinline__ void stage_tagged(const FrameArgs& a, const Lds& s, f
       ld_tagged2(p + 2, t[4 * j + 2], t[4 * j + 3]);
     }
     after();
-    tag_wait(a, s, tag, t, [&](int i) __attribute__((always_inline)) {
+    tag_wait(w, t, [&](int i) __attribute__((always_inline)) {
       return src + 4 * quad_of(base, i >> 2, nq) + (i & 3);
     });
     const int nj = steps_opaque(nq, base);
@@ -502,7 +516,6 @@ __device__ __forceinline__ void stage_rows(const FrameArgs& a, const Lds& s, int
   constexpr int NS = TAGGED ? 2 : 3;
   const int hq = a.dim >> 2;
   const int nq = M * hq;
-  const u32 tag = out_tag(a);
   // float32 source rows: the previous layer's output, or at layer 0 the
   // hidden state (through fast_project_in when present) at window position 0;
   // layer 0 at positions j >= 1 takes fast_embeddings[c_{j-1}]
@@ -540,7 +553,7 @@ __device__ __forceinline__ void stage_rows(const FrameArgs& a, const Lds& s, int
     }
     after();
     if constexpr (TAGGED)
-      tag_wait(a, s, tag, t, [&](int i) __attribute__((always_inline)) {
+      tag_wait(frame_tw(a, s), t, [&](int i) __attribute__((always_inline)) {
         const int q = quad_of(base, i >> 2, nq);
         const int m = q >= hq ? 1 : 0, c = q - m * hq;
         return tsrc + (size_t)m * a.dim + 4 * c + (i & 3);
@@ -1083,7 +1096,7 @@ __device__ __forceinline__ void phase_attn_wo(const FrameArgs& a, const Lds& s, 
         }
       }
       after();
-      tag_wait(a, s, tag, t, [&](int i) __attribute__((always_inline)) {
+      tag_wait(frame_tw(a, s), t, [&](int i) __attribute__((always_inline)) {
         return qkv_new + offs[i >> 1] + 2 * lp + (i & 1);
       });
       const int nj = steps_opaque(nseg, base, NWAVE);
@@ -1175,9 +1188,9 @@ __device__ __forceinline__ void phase_ffn_down(const FrameArgs& a, const Lds& s,
   const float scv = row_scale_issue(s2, nullptr, r0, r1 - r0, r1 - r0);
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
-  stage_tagged<WT, 5>(a, s, s.act, gb(a, step, l), a.ffn, pro);
+  stage_tagged<WT, 5>(frame_tw(a, s), s.act, gb(a, step, l), a.ffn, pro);
   for (int m = 1; m < M; ++m)
-    stage_tagged<WT, 5>(a, s, s.act + (size_t)m * a.kmax, gb(a, step, l) + (size_t)m * a.ffn, a.ffn, NoHook{});
+    stage_tagged<WT, 5>(frame_tw(a, s), s.act + (size_t)m * a.kmax, gb(a, step, l) + (size_t)m * a.ffn, a.ffn, NoHook{});
   row_scale_store(s.rsc, scv, s2, nullptr, r0, r1 - r0, r1 - r0);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
@@ -1206,7 +1219,6 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
     constexpr int NS = 2;
     const u64* src = xb(a, step, a.n_layer - 1) + (size_t)(M - 1) * D;
     const int nq = D >> 2;
-    const u32 tag = out_tag(a);
     float ss = 0.0f;
     auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
       u64 t[4 * NS];
@@ -1217,7 +1229,7 @@ __device__ __forceinline__ void phase_head(const FrameArgs& a, const Lds& s, int
         ld_tagged2(p + 2, t[4 * j + 2], t[4 * j + 3]);
       }
       after();
-      tag_wait(a, s, tag, t, [&](int i) __attribute__((always_inline)) {
+      tag_wait(frame_tw(a, s), t, [&](int i) __attribute__((always_inline)) {
         return src + 4 * quad_of(base, i >> 2, nq) + (i & 3);
       });
       const int nj = steps_opaque(nq, base);
@@ -1338,7 +1350,7 @@ __global__ void __launch_bounds__(NTHREADS) frame_kernel(FrameArgs a) {
     mark(a, ph, 1);
     if (done.kind == PH_HEAD && !a.forced) {
       const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
-      const int code = sample_from(TaggedLogits{a, s, logitsb(a, step)}, V, a.temp[0], a.top_p[0], a.top_k[0],
+      const int code = sample_from(TaggedLogits{frame_tw(a, s), logitsb(a, step)}, V, a.temp[0], a.top_p[0], a.top_k[0],
                                    a.uniforms[step - 1], sc);
       if (tidx() == 0) s.codes[step] = min(max(code, 0), V - 1);
       __syncthreads();

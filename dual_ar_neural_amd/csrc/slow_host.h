@@ -13,13 +13,13 @@ struct s2fast_slow_ctx {
   LayerPtr* layers = nullptr;   // device copy of the layer pointers
   float* rope = nullptr;
   float* x0 = nullptr;
-  float* x = nullptr;
-  float* qkv = nullptr;
+  u64* x = nullptr;            // tagged outputs (x, qkv, g, logits): cleared at creation and
+  u64* qkv = nullptr;          // when the epoch counter wraps
   long long* acc = nullptr;
-  float* g = nullptr;
+  u64* g = nullptr;
   float* po = nullptr;
   float* pml = nullptr;
-  float* logits = nullptr;
+  u64* logits = nullptr;
   int* sem = nullptr;          // the full frame's semantic code, handed to Fast-AR
   u32* flags = nullptr;
   u32* err = nullptr;
@@ -187,6 +187,10 @@ int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights*
   ok = hipMemcpy(c->layers, lp.data(), lp.size() * sizeof(LayerPtr), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(c->rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemset(c->acc, 0, (size_t)(Ln * c->acc_slot) * sizeof(long long)) == hipSuccess &&
+       hipMemset(c->x, 0, (size_t)(Ln * c->x_slot) * sizeof(u64)) == hipSuccess &&
+       hipMemset(c->qkv, 0, (size_t)(Ln * c->qkv_slot) * sizeof(u64)) == hipSuccess &&
+       hipMemset(c->g, 0, (size_t)(Ln * c->g_slot) * sizeof(u64)) == hipSuccess &&
+       hipMemset(c->logits, 0, (size_t)rup(c->n_allowed, 64) * sizeof(u64)) == hipSuccess &&
        hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
        hipMemset(c->err, 0, W_WORDS * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
   if (!ok) { free_slow(c); return S2FAST_ERR_HIP; }
@@ -200,7 +204,23 @@ void s2fast_slow_destroy(s2fast_slow_ctx* ctx) {
   free_slow(ctx);
 }
 
-int s2fast_slow_syncs(const s2fast_slow_ctx* ctx) { return ctx ? 5 * ctx->cfg.n_layer + 1 : -1; }
+// Grid syncs of one step launch: after every layer's ATTN and WO phases.
+int s2fast_slow_syncs(const s2fast_slow_ctx* ctx) { return ctx ? 2 * ctx->cfg.n_layer : -1; }
+
+// Before the epoch counter wraps: the barrier flags and the tagged outputs
+// go back to their cleared state and the counter restarts.
+int slow_restart_epochs(s2fast_slow_ctx* c, hipStream_t st) {
+  auto rup = [](long long n, long long q) { return (n + q - 1) / q * q; };
+  const size_t Ln = (size_t)c->cfg.n_layer;
+  if (zero_device(c->flags, (size_t)c->ncu * 64 * sizeof(u32), st) != S2FAST_OK ||
+      zero_device(c->x, Ln * c->x_slot * sizeof(u64), st) != S2FAST_OK ||
+      zero_device(c->qkv, Ln * c->qkv_slot * sizeof(u64), st) != S2FAST_OK ||
+      zero_device(c->g, Ln * c->g_slot * sizeof(u64), st) != S2FAST_OK ||
+      zero_device(c->logits, (size_t)rup(c->n_allowed, 64) * sizeof(u64), st) != S2FAST_OK)
+    return S2FAST_ERR_HIP;
+  c->epoch = 0;
+  return S2FAST_OK;
+}
 
 int s2fast_slow_status(s2fast_slow_ctx* ctx, void* stream) {
   if (!ctx) return S2FAST_ERR_ARG;
@@ -266,16 +286,14 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
   a.flags = ctx->flags; a.err = ctx->err; a.tlog = ctx->tlog_on ? ctx->tlog : nullptr;
   a.watch.give_up = ctx->give_up;
   a.x_head = x_head;
-  if (ctx->epoch > 0xF0000000u) {
-    if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
-    ctx->epoch = 0;
-  }
+  if (ctx->epoch > 0xF0000000u && slow_restart_epochs(ctx, st) != S2FAST_OK) return S2FAST_ERR_HIP;
   a.epoch0 = ctx->epoch;
   void* args[] = {&a};
   if (hipLaunchCooperativeKernel(slow_kernel_fn(k.weight_dtype, M), dim3(ctx->ncu), dim3(NTHREADS), args,
                                  ctx->lds_bytes, st) != hipSuccess)
     return S2FAST_ERR_HIP;
-  ctx->epoch += (u32)(x_head ? 1 : 5 * k.n_layer + (do_head ? 1 : 0));
+  // its grid syncs, and at least one: the next launch's outputs need another tag
+  ctx->epoch += (u32)(x_head ? 1 : 2 * k.n_layer);
   return S2FAST_OK;
 }
 
@@ -412,10 +430,7 @@ int prefill_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past0, int C,
   a.pf_part = ctx->pf_part; a.pf_q = ctx->pf_q;
   a.pf_full_last = full_last ? 1 : 0;
   const bool merge = k.weight_dtype == S2FAST_BF16 && a.pf_ps > 1;
-  if (ctx->epoch > 0xF0000000u) {
-    if (hipMemsetAsync(ctx->flags, 0, (size_t)ctx->ncu * 64 * sizeof(u32), st) != hipSuccess) return S2FAST_ERR_HIP;
-    ctx->epoch = 0;
-  }
+  if (ctx->epoch > 0xF0000000u && slow_restart_epochs(ctx, st) != S2FAST_OK) return S2FAST_ERR_HIP;
   a.epoch0 = ctx->epoch;
   void* args[] = {&a};
   if (hipLaunchCooperativeKernel(prefill_fn(k.weight_dtype), dim3(ctx->ncu), dim3(NTHREADS), args, ctx->pf_lds,

@@ -15,7 +15,9 @@
 //   main token drawn from logits + sem_mask, redrawn at temperature 1.0 /
 //   top_p 0.9 if it is a semantic id already among the last 10 main tokens.
 //
-// Per layer the blocks run five phases, each closed by a grid barrier:
+// Per layer the blocks run five phases.  The outputs of QKV, UP and DOWN
+// (and the head's logits) are tagged values that the next phase waits on
+// itself; ATTN and WO are closed by a grid barrier:
 //   QKV   RMSNorm(x) -> rows of wqkv
 //   ATTN  block (g, c): KV group g, chunk c of the positions.  The group's
 //         query heads and the new key/value are normalised and rotated in
@@ -67,19 +69,21 @@ struct SlowArgs {
   int* sem_out;             // [1] clamp(main - sem_begin, 0, cbs - 1)
   float* hidden_out;        // [dim]
   float* logits_out;        // [n_allowed] or nullptr
-  // per-launch arena: every region is written once per launch and read only
-  // after the barrier that follows its writes (see FrameArgs)
+  // per-launch arena: every region is written once per launch.  x, qkv, g
+  // and logits are tagged values (the launch's tag beside each float) read
+  // with tagged waits; the others are read only after the barrier that
+  // follows their writes (see FrameArgs)
   float* x0;                // [MMAX][dim] the positions' input vectors
-  float* x;                 // [n_layer][x_slot]: [MMAX][dim] per layer
-  float* qkv;               // [n_layer][qkv_slot]: [MMAX][qkv_dim]
+  u64* x;                   // [n_layer][x_slot]: [MMAX][dim] per layer (tagged)
+  u64* qkv;                 // [n_layer][qkv_slot]: [MMAX][qkv_dim] (tagged)
   long long* acc;           // [n_layer][acc_slot]: [MMAX][dim] (zero between launches)
-  float* g;                 // [n_layer][g_slot]: [MMAX][ffn]
+  u64* g;                   // [n_layer][g_slot]: [MMAX][ffn] (tagged)
   float* po;                // [n_layer][n_kv][nchunk][MMAX][gheads][hd] chunk outputs
   float* pml;               // [n_layer][n_kv][nchunk][MMAX][gheads][2] chunk max and sum
-  float* logits;            // [n_allowed]
+  u64* logits;              // [n_allowed] (tagged)
   long long x_slot, qkv_slot, acc_slot, g_slot, po_slot, pml_slot;
   u32* flags;
-  u32 epoch0;
+  u32 epoch0;               // epoch0 + 1 tags this launch's outputs
   u32* err;                 // watchdog words (see Watch)
   Watch watch;
   u32* tlog;
@@ -101,14 +105,14 @@ struct SlowLds {
   float* cval;
   int* cidx;
   u32* mark;
-  int* flag;
+  int* flag;     // [8]: [0] grid sync result, [1] timeline record, [2..3] launch exit, [4] a tag wait gave up
   int* tok;      // [64]: row-0 token and codes of position m at 32 m, its codes flag at 32 m + 20; the draw at [16..17]
 };
 
 __host__ __device__ inline size_t slow_lds_floats(int kmax, int rmax, int gheads, int hd) {
   const size_t act = (size_t)MMAX * (((size_t)kmax + 3) & ~(size_t)3);
   return act + (size_t)rmax * NWAVE * MMAX + 64 + (size_t)MMAX * (gheads + 2) * hd + 2 * (size_t)hd +
-         (size_t)NWAVE * gheads * (hd + 2) + 6 * (size_t)NTHREADS + (size_t)MMAX * hd + 2 * TOPK_MAX + 256 + 4 + 64;
+         (size_t)NWAVE * gheads * (hd + 2) + 6 * (size_t)NTHREADS + (size_t)MMAX * hd + 2 * TOPK_MAX + 256 + 8 + 64;
 }
 
 __device__ inline SlowLds slow_carve(float* base, const SlowArgs& a) {
@@ -125,14 +129,23 @@ __device__ inline SlowLds slow_carve(float* base, const SlowArgs& a) {
   s.cval = p; p += TOPK_MAX;
   s.cidx = reinterpret_cast<int*>(p); p += TOPK_MAX;
   s.mark = reinterpret_cast<u32*>(p); p += 256;
-  s.flag = reinterpret_cast<int*>(p); p += 4;
+  s.flag = reinterpret_cast<int*>(p); p += 8;
   s.tok = reinterpret_cast<int*>(p);
   return s;
 }
 
-__device__ __forceinline__ const float* slow_lin(const SlowArgs& a, int l) {
-  if (a.x_head && l == a.n_layer) return a.x_head;
-  return l == 0 ? a.x0 : a.x + (size_t)(l - 1) * a.x_slot;
+// Layer l's input (l == n_layer: the head's): at layer 0 the step's input
+// vectors x0, past the last layer of a head-only launch the row the chunked
+// prefill wrote (both plain floats), otherwise the previous layer's tagged
+// output.
+__device__ __forceinline__ bool slow_in_tagged(const SlowArgs& a, int l) {
+  return l > 0 && !(a.x_head && l == a.n_layer);
+}
+__device__ __forceinline__ const float* slow_in_plain(const SlowArgs& a, int l) { return l == 0 ? a.x0 : a.x_head; }
+__device__ __forceinline__ const u64* slow_in_tag(const SlowArgs& a, int l) { return a.x + (size_t)(l - 1) * a.x_slot; }
+__device__ __forceinline__ u32 slow_tag(const SlowArgs& a) { return a.epoch0 + 1u; }
+__device__ __forceinline__ TagWait slow_tw(const SlowArgs& a, const SlowLds& s) {
+  return TagWait{a.err, s.flag + 4, slow_tag(a), a.watch.give_up};
 }
 
 // the cache's element type: bf16 (round to nearest even) or f32
@@ -225,19 +238,22 @@ __device__ __forceinline__ Plan slow_plan(const SlowArgs& a, int l, int kind) {
 // RMSNorm weight; the per-wave sums of squares go to small.  MODE 0: the
 // step's input vector built from the embedding tables (block 0 also stores
 // it to the arena for the later phases of layer 0); 1: the previous layer's
-// output; 2: layer input + the attention accumulator (x_mid).
-template <typename WT, int MODE, typename Hook>
+// output; 2: layer input + the attention accumulator (x_mid).  TAGGED: the
+// layer input is tagged (slow_in_tagged).
+template <typename WT, int MODE, bool TAGGED, typename Hook>
 __device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, int l, int m0, int Mr, const WT* normw,
                                            const Hook& hook) {
-  constexpr int NS = MODE == 0 ? 2 : 3;
+  constexpr int NS = MODE == 0 ? 2 : (TAGGED ? 2 : 3);
   constexpr int NT = 11;                    // main token + at most 10 codebook rows per batch step
   const int hq = a.dim >> 2;
   const int nq = Mr * hq;                   // rows m0 .. m0 + Mr - 1 (Mr <= 2), row by row
-  const float* src = slow_lin(a, l);
+  const float* src = TAGGED ? nullptr : slow_in_plain(a, l);
+  const u64* tsrc = TAGGED ? slow_in_tag(a, l) : nullptr;
   const WT* emb = reinterpret_cast<const WT*>(a.emb);
   const WT* cemb = reinterpret_cast<const WT*>(a.cemb);
   float ss0 = 0.0f, ss1 = 0.0f;
   auto batch = [&](int base, const auto& after) __attribute__((always_inline)) {
+    u64 t[TAGGED ? 4 * NS : 1];
     v4f xv[NS];
     v2ll a0[NS], a1[NS];
     typename WQuad<WT>::type wv[NS], ev[NS][NT];
@@ -255,7 +271,13 @@ __device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, 
           ev[j][t] = WQuad<WT>::load(cemb + ((size_t)jj * a.cbs + tk[1 + jj]) * a.dim, c);
         }
       } else {
-        xv[j] = *reinterpret_cast<const v4f*>(src + (size_t)m * a.dim + 4 * c);
+        if constexpr (TAGGED) {
+          const u64* p = tsrc + (size_t)m * a.dim + 4 * c;
+          ld_tagged2(p, t[4 * j], t[4 * j + 1]);
+          ld_tagged2(p + 2, t[4 * j + 2], t[4 * j + 3]);
+        } else {
+          xv[j] = *reinterpret_cast<const v4f*>(src + (size_t)m * a.dim + 4 * c);
+        }
         if (MODE == 2) {
           const long long* ac = a.acc + (size_t)l * a.acc_slot + (size_t)m * a.dim + 4 * c;
           a0[j] = *reinterpret_cast<const v2ll*>(ac);
@@ -264,6 +286,12 @@ __device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, 
       }
     }
     after();
+    if constexpr (MODE != 0 && TAGGED)
+      tag_wait(slow_tw(a, s), t, [&](int i) __attribute__((always_inline)) {
+        const int q = quad_of(base, i >> 2, nq);
+        const int r = q >= hq ? 1 : 0, c = q - r * hq;
+        return tsrc + (size_t)(m0 + r) * a.dim + 4 * c + (i & 3);
+      });
     const int nj = steps_opaque(nq, base);
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -288,7 +316,7 @@ __device__ __forceinline__ void slow_stage(const SlowArgs& a, const SlowLds& s, 
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = xv[j][e];
+        for (int e = 0; e < 4; ++e) v[e] = TAGGED ? tag_val(t[4 * j + e]) : xv[j][e];
         if (MODE == 2) {
           v[0] += from_fx(a0[j][0]); v[1] += from_fx(a0[j][1]);
           v[2] += from_fx(a1[j][0]); v[3] += from_fx(a1[j][1]);
@@ -321,18 +349,19 @@ __device__ __forceinline__ void slow_qkv(const SlowArgs& a, const SlowLds& s, in
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   const WT* nw = reinterpret_cast<const WT*>(a.L[l].attn_norm);
   const int M = a.M;
-  if (l == 0) slow_stage<WT, 0>(a, s, l, 0, M, nw, pro);
-  else slow_stage<WT, 1>(a, s, l, 0, M, nw, pro);
+  if (l == 0) slow_stage<WT, 0, false>(a, s, l, 0, M, nw, pro);
+  else slow_stage<WT, 1, true>(a, s, l, 0, M, nw, pro);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  float* out = a.qkv + (size_t)l * a.qkv_slot;
+  u64* out = a.qkv + (size_t)l * a.qkv_slot;
   for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i - r * M;
-    st_coh(out + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m) / norm_den(s.small, m, a.dim, a.eps));
+    st_tagged(out + (size_t)m * a.qkv_dim + r0 + r, red_sum(s.red, r, m) / norm_den(s.small, m, a.dim, a.eps),
+              slow_tag(a));
   }
 }
 
@@ -545,14 +574,31 @@ __device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, i
   const int M = a.M;
   const int N = a.n_past + M;                     // positions 0 .. n_past + M - 1
   const int p0 = (int)(((long long)N * c) / a.nchunk), p1 = (int)(((long long)N * (c + 1)) / a.nchunk);
-  const float* qkv = a.qkv + (size_t)l * a.qkv_slot;
+  const u64* qkv = a.qkv + (size_t)l * a.qkv_slot;
   const int rs = (gh + 2) * hd;
-  // per new position: the group's query heads, its new key and value; and
-  // the q/k norm weights
-  for (int i = tidx(); i < M * rs; i += NTHREADS) {
-    const int m = i / rs, v = (i - m * rs) / hd, d = i - m * rs - v * hd;
-    const int src = v < gh ? (g * gh + v) * hd : (v == gh ? (H + g) * hd : (H + G + g) * hd);
-    s.q[i] = qkv[(size_t)m * a.qkv_dim + src + d];
+  // per new position: the group's query heads, its new key and value (the
+  // QKV phase's tagged outputs, loaded together and waited on); and the q/k
+  // norm weights
+  {
+    constexpr int NI = 3;
+    const int n = M * rs;
+    auto at = [&](int i) __attribute__((always_inline)) {
+      i = min(i, n - 1);
+      const int m = i / rs, v = (i - m * rs) / hd, d = i - m * rs - v * hd;
+      const int src = v < gh ? (g * gh + v) * hd : (v == gh ? (H + g) * hd : (H + G + g) * hd);
+      return qkv + (size_t)m * a.qkv_dim + src + d;
+    };
+    for (int base = 0; base < n; base += NI * NTHREADS) {
+      u64 t[NI];
+#pragma unroll
+      for (int j = 0; j < NI; ++j) t[j] = ld_tagged(at(base + j * NTHREADS + tidx()));
+      tag_wait(slow_tw(a, s), t, [&](int j) __attribute__((always_inline)) { return at(base + j * NTHREADS + tidx()); });
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int i = base + j * NTHREADS + tidx();
+        if (i < n) s.q[i] = tag_val(t[j]);
+      }
+    }
   }
   if (a.has_qkn)
     for (int i = tidx(); i < 2 * hd; i += NTHREADS)
@@ -721,18 +767,20 @@ __device__ __forceinline__ void slow_up(const SlowArgs& a, const SlowLds& s, int
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   const int M = a.M;
-  slow_stage<WT, 2>(a, s, l, 0, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
+  if (l == 0) slow_stage<WT, 2, false>(a, s, l, 0, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
+  else slow_stage<WT, 2, true>(a, s, l, 0, M, reinterpret_cast<const WT*>(a.L[l].ffn_norm), pro);
   zero_lds(s.red, 2 * nr * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);   // rows [0, nr): w1, [nr, 2nr): w3
   __syncthreads();
   mark(a, s.flag[1], 3);
-  float* out = a.g + (size_t)l * a.g_slot;
+  u64* out = a.g + (size_t)l * a.g_slot;
   for (int i = tidx(); i < nr * M; i += NTHREADS) {
     const int r = i / M, m = i - r * M;
     const float den = norm_den(s.small, m, a.dim, a.eps);
-    st_coh(out + (size_t)m * a.ffn + r0 + r, silu(red_sum(s.red, r, m) / den) * (red_sum(s.red, nr + r, m) / den));
+    st_tagged(out + (size_t)m * a.ffn + r0 + r, silu(red_sum(s.red, r, m) / den) * (red_sum(s.red, nr + r, m) / den),
+              slow_tag(a));
   }
 }
 
@@ -742,24 +790,25 @@ __device__ __forceinline__ void slow_down(const SlowArgs& a, const SlowLds& s, i
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   const int M = a.M;
-  stage_arena<WT, true, 5>(s.act, a.g + (size_t)l * a.g_slot, a.ffn, pro);
+  stage_tagged<WT, 5>(slow_tw(a, s), s.act, a.g + (size_t)l * a.g_slot, a.ffn, pro);
   for (int m = 1; m < M; ++m)
-    stage_arena<WT, true, 5>(s.act + (size_t)m * a.kmax, a.g + (size_t)l * a.g_slot + (size_t)m * a.ffn, a.ffn,
-                             NoHook{});
+    stage_tagged<WT, 5>(slow_tw(a, s), s.act + (size_t)m * a.kmax, a.g + (size_t)l * a.g_slot + (size_t)m * a.ffn,
+                        a.ffn, NoHook{});
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
   __syncthreads();
   mark(a, s.flag[1], 3);
-  const float* xin = slow_lin(a, l);
-  float* xo = a.x + (size_t)l * a.x_slot;
+  u64* xo = a.x + (size_t)l * a.x_slot;
   long long* acc = a.acc + (size_t)l * a.acc_slot;
   for (int i = tidx(); i < (r1 - r0) * M; i += NTHREADS) {
     const int r = i / M, m = i - r * M;
     const size_t k = (size_t)m * a.dim + r0 + r;
-    const float xm = xin[k] + from_fx(acc[k]);
-    st_coh(xo + k, xm + red_sum(s.red, r, m));
+    // the layer input (its tagged value is current since this layer's QKV phase)
+    const float xin = l == 0 ? a.x0[k] : tag_val(ld_coh64(slow_in_tag(a, l) + k));
+    const float xm = xin + from_fx(acc[k]);
+    st_tagged(xo + k, xm + red_sum(s.red, r, m), slow_tag(a));
     st_coh(acc + k, 0ll);   // ready for the next launch
   }
 }
@@ -771,7 +820,10 @@ __device__ __forceinline__ void slow_head(const SlowArgs& a, const SlowLds& s, P
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   // the final norm reads the last layer's output: the same staging as a
   // layer input one past the last layer
-  slow_stage<WT, 1>(a, s, a.n_layer, a.M - 1, 1, reinterpret_cast<const WT*>(a.norm), pro);   // the last position
+  if (slow_in_tagged(a, a.n_layer))   // the last position
+    slow_stage<WT, 1, true>(a, s, a.n_layer, a.M - 1, 1, reinterpret_cast<const WT*>(a.norm), pro);
+  else
+    slow_stage<WT, 1, false>(a, s, a.n_layer, a.M - 1, 1, reinterpret_cast<const WT*>(a.norm), pro);
   zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
   __syncthreads();
   mark(a, s.flag[1], 2);
@@ -781,7 +833,7 @@ __device__ __forceinline__ void slow_head(const SlowArgs& a, const SlowLds& s, P
   const float den = norm_den(s.small, 0, a.dim, a.eps);
   for (int r = tidx(); r < r1 - r0; r += NTHREADS) {
     const float v = red_sum(s.red, r, 0) / den;
-    st_coh(a.logits + r0 + r, v);
+    st_tagged(a.logits + r0 + r, v, slow_tag(a));
     if (a.logits_out) a.logits_out[r0 + r] = v;
   }
   // hidden = RMSNorm(x, norm): the normalised state handed to Fast-AR
@@ -789,12 +841,14 @@ __device__ __forceinline__ void slow_head(const SlowArgs& a, const SlowLds& s, P
     for (int k = tidx(); k < a.dim; k += NTHREADS) a.hidden_out[k] = s.act[phys<WT>(k, a.dim)] / den;
 }
 
-// Block 0, after the head's barrier: the main-token draw, the repetition
-// check against the window, the window update (main-loop page, sections 5
-// and 6).
+// Block 0, after the head: the main-token draw (its loads wait on the
+// logits' tags), the repetition check against the window, the window update
+// (main-loop page, sections 5 and 6).  Nothing is written if a tag wait gave
+// up.
 __device__ __forceinline__ void slow_draw(const SlowArgs& a, const SlowLds& s) {
   const SampScratch sc{s.cval, s.cidx, reinterpret_cast<int*>(s.mark)};
-  const int i1 = sample_request(a.logits, a.n_allowed, a.temp[0], a.top_p[0], a.top_k[0], a.u[0], sc);
+  const TaggedLogits lg{slow_tw(a, s), a.logits};
+  const int i1 = sample_from(lg, a.n_allowed, a.temp[0], a.top_p[0], a.top_k[0], a.u[0], sc);
   if (tidx() == 0) {
     const int tok = slow_token(a, min(max(i1, 0), a.n_allowed - 1));
     const int cnt = min(max(a.window[0], 0), RAS_WIN);
@@ -804,11 +858,13 @@ __device__ __forceinline__ void slow_draw(const SlowArgs& a, const SlowLds& s) {
     s.tok[17] = (rep && tok >= a.sem_begin && tok < a.sem_begin + a.nsem) ? 1 : 0;
   }
   __syncthreads();
+  if (s.flag[4]) return;
   int tok = s.tok[16];
   if (s.tok[17]) {
-    const int i2 = sample_request(a.logits, a.n_allowed, 1.0f, 0.9f, a.top_k[0], a.u[1], sc);
+    const int i2 = sample_from(lg, a.n_allowed, 1.0f, 0.9f, a.top_k[0], a.u[1], sc);
     if (tidx() == 0) s.tok[16] = slow_token(a, min(max(i2, 0), a.n_allowed - 1));
     __syncthreads();
+    if (s.flag[4]) return;
     tok = s.tok[16];
   }
   if (tidx() == 0) {
@@ -836,6 +892,7 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
   const SlowLds s = slow_carve(lds_base, a);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   u32 epoch = a.epoch0;
+  if (tidx() == 0) s.flag[4] = 0;
   {
     const int m = tidx() >> 5, t = tidx() & 31;   // position m's row-0 token (t = 0) and codes
     if (m < a.M && t <= a.ncb) {
@@ -863,8 +920,8 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
   for (int ph = ph0; ph < nph; ++ph) {
     const int l = ph / 5;
     const int kind = ph < 5 * a.n_layer ? ph - 5 * l : (int)SP_HEAD;
-    if (a.tlog && tidx() == 0) s.flag[1] = (int)(epoch - a.epoch0);
-    mark(a, epoch - a.epoch0, 5);
+    if (a.tlog && tidx() == 0) s.flag[1] = ph;
+    mark(a, ph, 5);
     switch (kind) {
       case SP_QKV: slow_qkv<WT>(a, s, l, pl); break;
       case SP_ATTN: slow_attn<WT>(a, s, l); break;
@@ -878,10 +935,19 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
       const int kn = ph + 1 < 5 * a.n_layer ? ph + 1 - 5 * ln : (int)SP_HEAD;
       pl = slow_plan<WT>(a, min(ln, a.n_layer - 1), kn);   // past the last phase: never used
     }
-    if (!grid_sync(a, epoch, s.flag)) { ok = false; break; }
+    mark(a, ph, 0);
+    if (kind == SP_ATTN || kind == SP_WO) {
+      // the chunk partials and the attention accumulators are read after a grid sync
+      if (!grid_sync<SlowArgs, false>(a, epoch, s.flag)) { ok = false; break; }
+    } else {
+      // the next phase's loads wait on this phase's tagged outputs
+      __syncthreads();
+    }
+    if (s.flag[4]) { ok = false; break; }
+    mark(a, ph, 1);
   }
   if (ok && a.do_head && blockIdx.x == 0) slow_draw(a, s);
-  // a barrier wait gave up: the step failed (no main token is drawn and the
+  // a barrier or tag wait gave up: the step failed (no main token is drawn and the
   // window is left as it was); the attention accumulators are cleared for
   // the next launch
   launch_exit(a, s.flag, [&]() __attribute__((always_inline)) {

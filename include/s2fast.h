@@ -484,9 +484,10 @@ int s2fast_test_norm_rope_attn(int32_t n_head, int32_t n_head_kv, int32_t head_d
 
 /* Failure-path test hook: with give_up != 0, later launches on this
  * context make every block's first grid-wide wait target an epoch that no
- * block publishes and give up after its first polls, so every block leaves
- * the kernel normally and the failure path of s2fast_status runs; 0
- * restores normal launches. */
+ * block publishes and give up after its first polls, and every wait on
+ * another block's tagged outputs (batch-1 frames, Slow-AR steps) give up at
+ * once, so every block leaves the kernel normally and the failure path of
+ * s2fast_status runs; 0 restores normal launches. */
 int s2fast_test_watchdog(s2fast_ctx* ctx, int32_t give_up);
 int s2fast_test_slow_watchdog(s2fast_slow_ctx* ctx, int32_t give_up);
 
