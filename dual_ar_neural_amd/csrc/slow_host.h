@@ -9,7 +9,7 @@ struct s2fast_slow_ctx {
   int device = 0, ncu = 0;
   size_t lds_bytes = 0;
   int kmax = 0, rmax = 0, nchunk = 0, nsem = 0, n_allowed = 0, end_first = 0;
-  long long x_slot = 0, qkv_slot = 0, acc_slot = 0, g_slot = 0, po_slot = 0, pml_slot = 0;
+  long long x_slot = 0, qkv_slot = 0, acc_slot = 0, g_slot = 0, po_slot = 0, pml_slot = 0, att_slot = 0;
   LayerPtr* layers = nullptr;   // device copy of the layer pointers
   float* rope = nullptr;
   float* x0 = nullptr;
@@ -19,6 +19,8 @@ struct s2fast_slow_ctx {
   u64* g = nullptr;
   float* po = nullptr;
   float* pml = nullptr;
+  u64* att = nullptr;          // merged attention outputs (tagged)
+  int* acnt = nullptr;         // chunk counts of the attention phase
   u64* logits = nullptr;
   int* sem = nullptr;          // the full frame's semantic code, handed to Fast-AR
   u32* flags = nullptr;
@@ -58,7 +60,7 @@ namespace {
 
 void free_slow(s2fast_slow_ctx* c) {
   if (!c) return;
-  void* ptrs[] = {c->layers, c->rope, c->x0, c->x, c->qkv, c->acc, c->g, c->po, c->pml, c->logits, c->sem,
+  void* ptrs[] = {c->layers, c->rope, c->x0, c->x, c->qkv, c->acc, c->g, c->po, c->pml, c->att, c->acnt, c->logits, c->sem,
                   c->flags, c->err, c->tlog, c->pf_pk, c->pf_pkt, c->pf_x0w, c->pf_x, c->pf_xmid, c->pf_qkv,
                   c->pf_att, c->pf_g, c->pf_part, c->pf_q};
   for (void* p : ptrs)
@@ -174,6 +176,7 @@ int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights*
   c->g_slot = rup((long long)MMAX * k.ffn_dim, 64);
   c->po_slot = rup((long long)G * c->nchunk * MMAX * gw, 64);
   c->pml_slot = rup((long long)G * c->nchunk * MMAX * gheads * 2, 64);
+  c->att_slot = rup((long long)MMAX * k.n_head * k.head_dim, 32);
   bool ok = dalloc(&c->layers, (size_t)k.n_layer) == hipSuccess && dalloc(&c->rope, rope.size()) == hipSuccess &&
             dalloc(&c->x0, (size_t)c->x_slot) == hipSuccess && dalloc(&c->x, (size_t)(Ln * c->x_slot)) == hipSuccess &&
             dalloc(&c->qkv, (size_t)(Ln * c->qkv_slot)) == hipSuccess &&
@@ -181,6 +184,8 @@ int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights*
             dalloc(&c->g, (size_t)(Ln * c->g_slot)) == hipSuccess &&
             dalloc(&c->po, (size_t)(Ln * c->po_slot)) == hipSuccess &&
             dalloc(&c->pml, (size_t)(Ln * c->pml_slot)) == hipSuccess &&
+            dalloc(&c->att, (size_t)(Ln * c->att_slot)) == hipSuccess &&
+            dalloc(&c->acnt, (size_t)(Ln * G * 64)) == hipSuccess &&
             dalloc(&c->logits, (size_t)rup(c->n_allowed, 64)) == hipSuccess && dalloc(&c->sem, 64) == hipSuccess &&
             dalloc(&c->flags, (size_t)P * 64) == hipSuccess && dalloc(&c->err, W_WORDS) == hipSuccess;
   if (!ok) { free_slow(c); return S2FAST_ERR_NOMEM; }
@@ -190,6 +195,8 @@ int s2fast_slow_create(const s2fast_slow_config* cfg, const s2fast_slow_weights*
        hipMemset(c->x, 0, (size_t)(Ln * c->x_slot) * sizeof(u64)) == hipSuccess &&
        hipMemset(c->qkv, 0, (size_t)(Ln * c->qkv_slot) * sizeof(u64)) == hipSuccess &&
        hipMemset(c->g, 0, (size_t)(Ln * c->g_slot) * sizeof(u64)) == hipSuccess &&
+       hipMemset(c->att, 0, (size_t)(Ln * c->att_slot) * sizeof(u64)) == hipSuccess &&
+       hipMemset(c->acnt, 0, (size_t)(Ln * G * 64) * sizeof(int)) == hipSuccess &&
        hipMemset(c->logits, 0, (size_t)rup(c->n_allowed, 64) * sizeof(u64)) == hipSuccess &&
        hipMemset(c->flags, 0, (size_t)P * 64 * sizeof(u32)) == hipSuccess &&
        hipMemset(c->err, 0, W_WORDS * sizeof(u32)) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
@@ -204,8 +211,8 @@ void s2fast_slow_destroy(s2fast_slow_ctx* ctx) {
   free_slow(ctx);
 }
 
-// Grid syncs of one step launch: after every layer's ATTN and WO phases.
-int s2fast_slow_syncs(const s2fast_slow_ctx* ctx) { return ctx ? 2 * ctx->cfg.n_layer : -1; }
+// Grid syncs of one step launch: after every layer's WO phase.
+int s2fast_slow_syncs(const s2fast_slow_ctx* ctx) { return ctx ? ctx->cfg.n_layer : -1; }
 
 // Before the epoch counter wraps: the barrier flags and the tagged outputs
 // go back to their cleared state and the counter restarts.
@@ -216,6 +223,7 @@ int slow_restart_epochs(s2fast_slow_ctx* c, hipStream_t st) {
       zero_device(c->x, Ln * c->x_slot * sizeof(u64), st) != S2FAST_OK ||
       zero_device(c->qkv, Ln * c->qkv_slot * sizeof(u64), st) != S2FAST_OK ||
       zero_device(c->g, Ln * c->g_slot * sizeof(u64), st) != S2FAST_OK ||
+      zero_device(c->att, Ln * c->att_slot * sizeof(u64), st) != S2FAST_OK ||
       zero_device(c->logits, (size_t)rup(c->n_allowed, 64) * sizeof(u64), st) != S2FAST_OK)
     return S2FAST_ERR_HIP;
   c->epoch = 0;
@@ -283,6 +291,7 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
   a.pml = ctx->pml; a.logits = ctx->logits;
   a.x_slot = ctx->x_slot; a.qkv_slot = ctx->qkv_slot; a.acc_slot = ctx->acc_slot; a.g_slot = ctx->g_slot;
   a.po_slot = ctx->po_slot; a.pml_slot = ctx->pml_slot;
+  a.att = ctx->att; a.acnt = ctx->acnt; a.att_slot = ctx->att_slot;
   a.flags = ctx->flags; a.err = ctx->err; a.tlog = ctx->tlog_on ? ctx->tlog : nullptr;
   a.watch.give_up = ctx->give_up;
   a.x_head = x_head;
@@ -293,7 +302,7 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
                                  ctx->lds_bytes, st) != hipSuccess)
     return S2FAST_ERR_HIP;
   // its grid syncs, and at least one: the next launch's outputs need another tag
-  ctx->epoch += (u32)(x_head ? 1 : 2 * k.n_layer);
+  ctx->epoch += (u32)(x_head ? 1 : k.n_layer);
   return S2FAST_OK;
 }
 

@@ -15,19 +15,20 @@
 //   main token drawn from logits + sem_mask, redrawn at temperature 1.0 /
 //   top_p 0.9 if it is a semantic id already among the last 10 main tokens.
 //
-// Per layer the blocks run five phases.  The outputs of QKV, UP and DOWN
-// (and the head's logits) are tagged values that the next phase waits on
-// itself; ATTN and WO are closed by a grid barrier:
+// Per layer the blocks run five phases.  The outputs of QKV, ATTN, UP and
+// DOWN (and the head's logits) are tagged values that the next phase waits
+// on itself; WO is closed by a grid barrier:
 //   QKV   RMSNorm(x) -> rows of wqkv
 //   ATTN  block (g, c): KV group g, chunk c of the positions.  The group's
 //         query heads and the new key/value are normalised and rotated in
 //         LDS; the chunk's keys/values stream from the cache once for all
 //         the group's query heads; each wave keeps an online softmax over
 //         its positions; the block leaves one (max, sum, output) partial per
-//         head
-//   WO    block (g, row group): merges group g's chunk partials (log-sum-exp
-//         weights) into the group's attention output, then wo rows over the
-//         group's columns, added across groups in an int64 fixed-point
+//         head, and the group's last chunk to finish (a count per group)
+//         merges the partials (log-sum-exp weights) into the group's
+//         attention output
+//   WO    block (g, row group): wo rows over the group's columns of the
+//         attention output, added across groups in an int64 fixed-point
 //         accumulator
 //   UP    RMSNorm(x + attn) -> w1, w3 rows -> silu(a1) * a3
 //   DOWN  w2 rows; x = x + attn + ffn
@@ -80,8 +81,10 @@ struct SlowArgs {
   u64* g;                   // [n_layer][g_slot]: [MMAX][ffn] (tagged)
   float* po;                // [n_layer][n_kv][nchunk][MMAX][gheads][hd] chunk outputs
   float* pml;               // [n_layer][n_kv][nchunk][MMAX][gheads][2] chunk max and sum
+  u64* att;                 // [n_layer][att_slot]: [MMAX][attn_dim] merged attention output (tagged)
+  int* acnt;                // [n_layer][n_kv][64] chunks of a group done (zero between launches)
   u64* logits;              // [n_allowed] (tagged)
-  long long x_slot, qkv_slot, acc_slot, g_slot, po_slot, pml_slot;
+  long long x_slot, qkv_slot, acc_slot, g_slot, po_slot, pml_slot, att_slot;
   u32* flags;
   u32 epoch0;               // epoch0 + 1 tags this launch's outputs
   u32* err;                 // watchdog words (see Watch)
@@ -105,7 +108,8 @@ struct SlowLds {
   float* cval;
   int* cidx;
   u32* mark;
-  int* flag;     // [8]: [0] grid sync result, [1] timeline record, [2..3] launch exit, [4] a tag wait gave up
+  int* flag;     // [8]: [0] grid sync result, [1] timeline record, [2..3] launch exit, [4] a tag wait gave up,
+                 // [5] this block merges its group's chunks
   int* tok;      // [64]: row-0 token and codes of position m at 32 m, its codes flag at 32 m + 20; the draw at [16..17]
 };
 
@@ -658,21 +662,34 @@ __device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, i
     const float* src = s.q + (size_t)mm * rs + (size_t)gh * hd;
     for (int d = tidx(); d < 2 * hd; d += NTHREADS) row[d] = KV::enc(src[d]);
   }
+  // the group's last chunk to finish (its partials and every other chunk's
+  // stored before the count says so) merges them; the count is cleared for
+  // the next launch
+  int* cnt = a.acnt + ((size_t)l * G + g) * 64;
+  wait_vmem();
+  __syncthreads();
+  if (tidx() == 0)
+    s.flag[5] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.nchunk - 1;
+  __syncthreads();
+  if (s.flag[5]) {
+    slow_merge<WT>(a, s, l, g);
+    if (tidx() == 0) st_coh(cnt, 0);
+  }
 }
 
+// The group's last chunk to finish: merge the group's chunk partials of
+// every head (log-sum-exp weights) into its attention output, written as
+// tagged values.  A thread takes 4 consecutive output elements (one 16-byte
+// load per chunk, as two coherent 8-byte loads: other blocks wrote them) of
+// the chunks cs, cs + S, ...; the S subsets of a quad then meet in LDS.
 template <typename WT>
-__device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int l, Plan& pl) {
-  const int g = pl.g, r0 = pl.r0, r1 = pl.r1;
+__device__ __forceinline__ void slow_merge(const SlowArgs& a, const SlowLds& s, int l, int g) {
   const int gh = a.gheads, hd = a.hd, nc = a.nchunk, n = gh * hd;
-  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
-  u32x4 slot[RING];
   const int M = a.M;
+  const u32 tag = slow_tag(a);
   const float* pml0 = a.pml + (size_t)l * a.pml_slot + (size_t)g * nc * MMAX * gh * 2;
   const float* po0 = a.po + (size_t)l * a.po_slot + (size_t)g * nc * MMAX * gh * hd;
-  // Merge the chunk partials of every head of the group (log-sum-exp
-  // weights).  A thread takes 4 consecutive output elements (one 16-byte
-  // load per chunk) of the chunks cs, cs + S, ...; the S subsets of a quad
-  // then meet in LDS.
+  u64* att = a.att + (size_t)l * a.att_slot + (size_t)g * a.gw;
   const int nq = n >> 2;                          // hd % 8 == 0
   const int S = max(1, NTHREADS / nq);
   const int iters = S > 1 ? 1 : (nq + NTHREADS - 1) / NTHREADS;
@@ -681,7 +698,7 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
   // chunk cc's partial of query mq: pml0 + (cc * MMAX + mq) * gh * 2, po0 + (cc * MMAX + mq) * n
   const float* pml = pml0 + (size_t)mq * gh * 2;
   const float* po = po0 + (size_t)mq * n;
-  float* actm = s.act + (size_t)mq * a.kmax;
+  u64* attm = att + (size_t)mq * a.attn_dim;
   if (mq > 0) __syncthreads();   // s.mrg of the previous query is read
   for (int it = 0; it < iters; ++it) {
     const int t = tidx();
@@ -693,15 +710,15 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
     v4f O = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int c0 = cs; c0 < nc + S * CB; c0 += S * CB) {
       if (c0 >= nc && !(it == 0 && c0 == cs)) break;
-      u64 ml[CB];
-      v4f ov[CB];
+      u64 ml[CB], o01[CB], o23[CB];
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int cc = min(c0 + j * S, nc - 1);
-        ml[j] = ld64(pml + ((size_t)cc * MMAX * gh + hh) * 2);
-        ov[j] = *reinterpret_cast<const v4f*>(po + (size_t)cc * MMAX * n + 4 * qq);
+        ml[j] = ld_coh64(pml + ((size_t)cc * MMAX * gh + hh) * 2);
+        const float* op = po + (size_t)cc * MMAX * n + 4 * qq;
+        o01[j] = ld_coh64(op);
+        o23[j] = ld_coh64(op + 2);
       }
-      if (mq == 0 && it == 0 && c0 == cs) gemv_prologue(pl, slot);
       float mb = -INFINITY;
 #pragma unroll
       for (int j = 0; j < CB; ++j)
@@ -716,7 +733,8 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
         if (c0 + j * S < nc) {
           const float f = expf(lo_f32(ml[j]) - mn);   // 0 for an empty chunk
           Ls = fmaf(f, hi_f32(ml[j]), Ls);
-          O += f * ov[j];
+          const v4f ov = {lo_f32(o01[j]), hi_f32(o01[j]), lo_f32(o23[j]), hi_f32(o23[j])};
+          O += f * ov;
         }
       }
       M = mn;
@@ -728,7 +746,7 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
       }
     } else if (live) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) actm[phys<WT>(4 * qq + e, a.gw)] = O[e] / Ls;
+      for (int e = 0; e < 4; ++e) st_tagged(attm + 4 * qq + e, O[e] / Ls, tag);
     }
   }
   if (S > 1) {
@@ -745,10 +763,24 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
         for (int e = 0; e < 4; ++e) O[e] = fmaf(f, w[2 + e], O[e]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) actm[phys<WT>(4 * q + e, a.gw)] = O[e] / Ls;
+      for (int e = 0; e < 4; ++e) st_tagged(attm + 4 * q + e, O[e] / Ls, tag);
     }
   }
   }
+}
+
+template <typename WT>
+__device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int l, Plan& pl) {
+  const int g = pl.g, r0 = pl.r0, r1 = pl.r1;
+  zero_lds(s.red, (r1 - r0) * NWAVE * MMAX);
+  u32x4 slot[RING];
+  const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
+  const int M = a.M;
+  // the group's merged attention output (tagged) into LDS, GEMV layout over its gw columns
+  const u64* att = a.att + (size_t)l * a.att_slot + (size_t)g * a.gw;
+  stage_tagged<WT, 1>(slow_tw(a, s), s.act, att, a.gw, pro);
+  for (int m = 1; m < M; ++m)
+    stage_tagged<WT, 1>(slow_tw(a, s), s.act + (size_t)m * a.kmax, att + (size_t)m * a.attn_dim, a.gw, NoHook{});
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
@@ -936,8 +968,8 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
       pl = slow_plan<WT>(a, min(ln, a.n_layer - 1), kn);   // past the last phase: never used
     }
     mark(a, ph, 0);
-    if (kind == SP_ATTN || kind == SP_WO) {
-      // the chunk partials and the attention accumulators are read after a grid sync
+    if (kind == SP_WO) {
+      // the attention accumulators are read after a grid sync
       if (!grid_sync<SlowArgs, false>(a, epoch, s.flag)) { ok = false; break; }
     } else {
       // the next phase's loads wait on this phase's tagged outputs
@@ -948,9 +980,10 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
   }
   if (ok && a.do_head && blockIdx.x == 0) slow_draw(a, s);
   // a barrier or tag wait gave up: the step failed (no main token is drawn and the
-  // window is left as it was); the attention accumulators are cleared for
-  // the next launch
+  // window is left as it was); the attention accumulators and the chunk
+  // counts are cleared for the next launch
   launch_exit(a, s.flag, [&]() __attribute__((always_inline)) {
     zero_words64(a.acc, (size_t)a.n_layer * a.acc_slot);
+    zero_words32(a.acnt, (size_t)a.n_layer * a.n_kv * 64);
   });
 }
