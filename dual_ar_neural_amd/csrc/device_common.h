@@ -1,13 +1,18 @@
 // Device helpers shared by the frame kernel and the sampler kernel.
 //
-// Cross-block communication inside one kernel launch uses only device-scope
-// relaxed atomics: on gfx950 they compile to global loads/stores with the
-// sc1 cache-policy bit, which are coherent across the eight XCDs without the
-// L2 write-back/invalidate that device-scope fences cost.  Ordering between a
-// block's data stores and its arrival flag comes from s_waitcnt vmcnt(0)
-// (stores are counted by vmcnt on gfx9-family parts) plus a workgroup
-// barrier; readers only touch the data after observing every flag, and read
-// it with sc1 loads, so no stale L2/L1 line can be returned.
+// Cross-block communication inside one kernel launch uses device-scope
+// relaxed atomics for its writes: on gfx950 they compile to global
+// loads/stores with the sc1 cache-policy bit, which are coherent across the
+// eight XCDs without the L2 write-back/invalidate that device-scope fences
+// cost.  Two forms of hand-over:
+// - flag barriers: ordering between a block's data stores and its arrival
+//   flag comes from s_waitcnt vmcnt(0) (stores are counted by vmcnt on
+//   gfx9-family parts) plus a workgroup barrier; readers only touch the data
+//   after observing every flag;
+// - tagged values (st_tagged): each value carries its launch's tag in the
+//   same 8-byte atomic store, so a reader checks the tag of every value it
+//   loaded and reloads the stale ones with sc1 loads; no flag is needed and
+//   no stale copy is ever used, wherever it came from.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
