@@ -211,7 +211,8 @@ void s2fast_slow_destroy(s2fast_slow_ctx* ctx) {
   free_slow(ctx);
 }
 
-// Grid syncs of one step launch: after every layer's WO phase.
+// Grid syncs of one step launch: after every layer's WO phase (a
+// two-position launch also after its attention phases).
 int s2fast_slow_syncs(const s2fast_slow_ctx* ctx) { return ctx ? ctx->cfg.n_layer : -1; }
 
 // Before the epoch counter wraps: the barrier flags and the tagged outputs
@@ -302,7 +303,7 @@ int slow_launch(s2fast_slow_ctx* ctx, void* kv_cache, int32_t n_past, int M, con
                                  ctx->lds_bytes, st) != hipSuccess)
     return S2FAST_ERR_HIP;
   // its grid syncs, and at least one: the next launch's outputs need another tag
-  ctx->epoch += (u32)(x_head ? 1 : k.n_layer);
+  ctx->epoch += (u32)(x_head ? 1 : (M == 1 ? 1 : 2) * k.n_layer);
   return S2FAST_OK;
 }
 

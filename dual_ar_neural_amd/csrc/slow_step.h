@@ -26,7 +26,8 @@
 //         its positions; the block leaves one (max, sum, output) partial per
 //         head, and the group's last chunk to finish (a count per group)
 //         merges the partials (log-sum-exp weights) into the group's
-//         attention output
+//         attention output (a two-position launch: a grid barrier, then
+//         every WO block merges them itself)
 //   WO    block (g, row group): wo rows over the group's columns of the
 //         attention output, added across groups in an int64 fixed-point
 //         accumulator
@@ -662,34 +663,44 @@ __device__ __forceinline__ void slow_attn(const SlowArgs& a, const SlowLds& s, i
     const float* src = s.q + (size_t)mm * rs + (size_t)gh * hd;
     for (int d = tidx(); d < 2 * hd; d += NTHREADS) row[d] = KV::enc(src[d]);
   }
-  // the group's last chunk to finish (its partials and every other chunk's
-  // stored before the count says so) merges them; the count is cleared for
-  // the next launch
-  int* cnt = a.acnt + ((size_t)l * G + g) * 64;
-  wait_vmem();
-  __syncthreads();
-  if (tidx() == 0)
-    s.flag[5] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.nchunk - 1;
-  __syncthreads();
-  if (s.flag[5]) {
-    slow_merge<WT>(a, s, l, g);
-    if (tidx() == 0) st_coh(cnt, 0);
+  // One position: the group's last chunk to finish (its partials and every
+  // other chunk's stored before the count says so) merges them into the
+  // group's tagged attention output; the count is cleared for the next
+  // launch.  Two positions: every wo block merges them itself, after a grid
+  // sync (one block merging both positions in turn took longer).
+  if (M == 1) {
+    int* cnt = a.acnt + ((size_t)l * G + g) * 64;
+    wait_vmem();
+    __syncthreads();
+    if (tidx() == 0)
+      s.flag[5] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.nchunk - 1;
+    __syncthreads();
+    if (s.flag[5]) {
+      const u32 tag = slow_tag(a);
+      u64* att = a.att + (size_t)l * a.att_slot + (size_t)g * a.gw;
+      slow_merge<WT, true>(a, s, l, g, [&](int mq, int col, float v) __attribute__((always_inline)) {
+        st_tagged(att + (size_t)mq * a.attn_dim + col, v, tag);
+      }, NoHook{});
+      if (tidx() == 0) st_coh(cnt, 0);
+    }
   }
 }
 
-// The group's last chunk to finish: merge the group's chunk partials of
-// every head (log-sum-exp weights) into its attention output, written as
-// tagged values.  A thread takes 4 consecutive output elements (one 16-byte
-// load per chunk, as two coherent 8-byte loads: other blocks wrote them) of
-// the chunks cs, cs + S, ...; the S subsets of a quad then meet in LDS.
-template <typename WT>
-__device__ __forceinline__ void slow_merge(const SlowArgs& a, const SlowLds& s, int l, int g) {
+// Merge KV group g's chunk partials of every head (log-sum-exp weights)
+// into its attention output: put(mq, column, value) for each of the group's
+// gw columns and each position.  A thread takes 4 consecutive output
+// elements (two 8-byte loads per chunk) of the chunks cs, cs + S, ...; the S
+// subsets of a quad then meet in LDS.  COH: coherent loads (the partials'
+// writers are known done only through the group's count); otherwise a grid
+// sync came between, and ordinary loads may hit the L2.  hook() runs once,
+// right after the first batch of loads is issued.
+template <typename WT, bool COH, typename Put, typename Hook>
+__device__ __forceinline__ void slow_merge(const SlowArgs& a, const SlowLds& s, int l, int g, const Put& put,
+                                           const Hook& hook) {
   const int gh = a.gheads, hd = a.hd, nc = a.nchunk, n = gh * hd;
   const int M = a.M;
-  const u32 tag = slow_tag(a);
   const float* pml0 = a.pml + (size_t)l * a.pml_slot + (size_t)g * nc * MMAX * gh * 2;
   const float* po0 = a.po + (size_t)l * a.po_slot + (size_t)g * nc * MMAX * gh * hd;
-  u64* att = a.att + (size_t)l * a.att_slot + (size_t)g * a.gw;
   const int nq = n >> 2;                          // hd % 8 == 0
   const int S = max(1, NTHREADS / nq);
   const int iters = S > 1 ? 1 : (nq + NTHREADS - 1) / NTHREADS;
@@ -698,7 +709,6 @@ __device__ __forceinline__ void slow_merge(const SlowArgs& a, const SlowLds& s, 
   // chunk cc's partial of query mq: pml0 + (cc * MMAX + mq) * gh * 2, po0 + (cc * MMAX + mq) * n
   const float* pml = pml0 + (size_t)mq * gh * 2;
   const float* po = po0 + (size_t)mq * n;
-  u64* attm = att + (size_t)mq * a.attn_dim;
   if (mq > 0) __syncthreads();   // s.mrg of the previous query is read
   for (int it = 0; it < iters; ++it) {
     const int t = tidx();
@@ -714,11 +724,13 @@ __device__ __forceinline__ void slow_merge(const SlowArgs& a, const SlowLds& s, 
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int cc = min(c0 + j * S, nc - 1);
-        ml[j] = ld_coh64(pml + ((size_t)cc * MMAX * gh + hh) * 2);
+        const float* mp = pml + ((size_t)cc * MMAX * gh + hh) * 2;
         const float* op = po + (size_t)cc * MMAX * n + 4 * qq;
-        o01[j] = ld_coh64(op);
-        o23[j] = ld_coh64(op + 2);
+        ml[j] = COH ? ld_coh64(mp) : ld64(mp);
+        o01[j] = COH ? ld_coh64(op) : ld64(op);
+        o23[j] = COH ? ld_coh64(op + 2) : ld64(op + 2);
       }
+      if (mq == 0 && it == 0 && c0 == cs) hook();
       float mb = -INFINITY;
 #pragma unroll
       for (int j = 0; j < CB; ++j)
@@ -746,7 +758,7 @@ __device__ __forceinline__ void slow_merge(const SlowArgs& a, const SlowLds& s, 
       }
     } else if (live) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st_tagged(attm + 4 * qq + e, O[e] / Ls, tag);
+      for (int e = 0; e < 4; ++e) put(mq, 4 * qq + e, O[e] / Ls);
     }
   }
   if (S > 1) {
@@ -763,7 +775,7 @@ __device__ __forceinline__ void slow_merge(const SlowArgs& a, const SlowLds& s, 
         for (int e = 0; e < 4; ++e) O[e] = fmaf(f, w[2 + e], O[e]);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st_tagged(attm + 4 * q + e, O[e] / Ls, tag);
+      for (int e = 0; e < 4; ++e) put(mq, 4 * q + e, O[e] / Ls);
     }
   }
   }
@@ -776,11 +788,17 @@ __device__ __forceinline__ void slow_wo(const SlowArgs& a, const SlowLds& s, int
   u32x4 slot[RING];
   const auto pro = [&]() __attribute__((always_inline)) { gemv_prologue(pl, slot); };
   const int M = a.M;
-  // the group's merged attention output (tagged) into LDS, GEMV layout over its gw columns
-  const u64* att = a.att + (size_t)l * a.att_slot + (size_t)g * a.gw;
-  stage_tagged<WT, 1>(slow_tw(a, s), s.act, att, a.gw, pro);
-  for (int m = 1; m < M; ++m)
-    stage_tagged<WT, 1>(slow_tw(a, s), s.act + (size_t)m * a.kmax, att + (size_t)m * a.attn_dim, a.gw, NoHook{});
+  // the group's attention output into LDS, GEMV layout over its gw columns:
+  // one position waits on the merged output (tagged); two merge the
+  // partials here
+  if (M == 1) {
+    const u64* att = a.att + (size_t)l * a.att_slot + (size_t)g * a.gw;
+    stage_tagged<WT, 1>(slow_tw(a, s), s.act, att, a.gw, pro);
+  } else {
+    slow_merge<WT, false>(a, s, l, g, [&](int mq, int col, float v) __attribute__((always_inline)) {
+      s.act[(size_t)mq * a.kmax + phys<WT>(col, a.gw)] = v;
+    }, pro);
+  }
   __syncthreads();
   mark(a, s.flag[1], 2);
   gemv_body<WT>(pl, slot, s.act, a.kmax, M, s.red);
@@ -968,8 +986,9 @@ __global__ void __launch_bounds__(NTHREADS) slow_kernel(SlowArgs args) {
       pl = slow_plan<WT>(a, min(ln, a.n_layer - 1), kn);   // past the last phase: never used
     }
     mark(a, ph, 0);
-    if (kind == SP_WO) {
-      // the attention accumulators are read after a grid sync
+    if (kind == SP_WO || (kind == SP_ATTN && MM == 2)) {
+      // the attention accumulators (and, at two positions, the chunk
+      // partials) are read after a grid sync
       if (!grid_sync<SlowArgs, false>(a, epoch, s.flag)) { ok = false; break; }
     } else {
       // the next phase's loads wait on this phase's tagged outputs
