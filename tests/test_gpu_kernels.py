@@ -177,6 +177,47 @@ def test_fast_decode_entry_checks():
     p.ctx.close()
 
 
+def test_mixed_launches_on_one_context():
+    """Batch-1 frames, one-call decodes of falling prefix lengths (launches of
+    9 steps down to 1), a batched frame and the allocation-free path, in turn
+    on one context.  Every launch writes its hand-over values with a tag no
+    earlier launch used (the epoch advances by at least one a launch), so
+    each result matches the oracle whatever earlier launches, of any length
+    or kernel, left in the arena."""
+    w = si.WORKLOADS["tiny"]
+    p = pr.make_pair(w.shape, w.seed(0), max_batch=3)
+    f1 = si.make_frames(w, n_frames=3, batch=1)
+    f3 = si.make_frames(w, n_frames=1, batch=3)
+    rng = np.random.default_rng(11)
+
+    def frame(fr, f, static=False):
+        args = (fr["hidden"][f], fr["sem_code"][f], fr["uniforms"][f], fr["temperature"], fr["top_p"], fr["top_k"])
+        if static:
+            d = pr.to_dev
+            codes = p.ctx.decode_frame(d(args[0], torch.float32), d(np.asarray(args[1], np.int32)),
+                                       d(args[2], torch.float32), d(args[3], torch.float32), d(args[4], torch.float32),
+                                       d(np.asarray(args[5], np.int32)), static_scratch=True)
+            torch.cuda.synchronize()
+            codes = codes.cpu().numpy()
+        else:
+            codes = pr.gpu_decode(p, *args)
+        pr.check_frame(p, *args, codes).assert_ok(1e-3)
+
+    frame(f1, 0)
+    hidden = f1["hidden"][1]
+    for k in range(w.shape.num_codebooks - 1, 0, -1):
+        prefix = rng.integers(0, w.shape.codebook_size, size=(1, k)).astype(np.int32)
+        got = p.ctx.fast_decode(pr.to_dev(hidden), pr.to_dev(prefix)).cpu().numpy()
+        want = fa.fast_forward(p.oracle, hidden, prefix)
+        assert float(np.abs(got[0] - want[0]).max()) <= pr.logit_tolerance(want[0]), k
+    frame(f3, 0)
+    frame(f1, 1, static=True)
+    frame(f1, 2)
+    assert p.ctx.status() == 0
+    _announce("mixed launches on one context: every result matches the oracle")
+    p.ctx.close()
+
+
 # ------------------------------------------------------------ failure report
 
 @pytest.mark.parametrize("B", [1, 3])
