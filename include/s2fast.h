@@ -419,8 +419,9 @@ int s2fast_full_frame(s2fast_slow_ctx* slow, s2fast_ctx* fast, void* kv_cache, i
                       const float* u_fast, const float* temperature, const float* top_p, const int32_t* top_k,
                       int32_t* main_out, float* hidden_out, int32_t* codes_out, void* stream);
 
-/* Grid-wide synchronisation points of one Slow-AR step (5 per layer + 1),
- * and the number of head rows (n_allowed); -1 on error. */
+/* Grid-wide synchronisation points of one Slow-AR step (one per layer,
+ * after its wo phase; the other phases hand over tagged values), and the
+ * number of head rows (n_allowed); -1 on error. */
 int s2fast_slow_syncs(const s2fast_slow_ctx* ctx);
 int s2fast_slow_allowed(const s2fast_slow_ctx* ctx);
 
