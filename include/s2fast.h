@@ -515,8 +515,8 @@ int s2fast_test_slow_prefill_chunks(s2fast_slow_ctx* ctx, int32_t enable);
  * out as [block][i][8].  The buffer is allocated on the first call. */
 int s2fast_test_timeline(s2fast_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity);
 
-/* The same instrumentation for Slow-AR step launches (sync point i < 256 of
- * a step; in-phase words are 0). */
+/* The same instrumentation for Slow-AR step launches (record i: phase i < 256
+ * of a step, five a layer, then the head). */
 int s2fast_test_slow_timeline(s2fast_slow_ctx* ctx, int32_t enable, uint32_t* host_out, int32_t capacity);
 
 /* Number of grid-wide synchronisation points one frame of B requests
